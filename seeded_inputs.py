@@ -1,0 +1,122 @@
+"""Seeded synthetic inputs shared by the oracle checks and the GPU path.
+
+This module holds no attention arithmetic: it only draws random numbers and
+rounds them to the storage dtype.  Both sides (the float64 oracle and the HIP
+library) are fed the *same* rounded values, so any difference between them is
+the method's own rounding, never the inputs'.
+
+Recipe (identical for every workload):
+  * numpy ``default_rng(seed)`` (PCG64);
+  * draw Q, K, V and then (for a backward workload) dO, in that order, each as
+    float32 ``standard_normal`` of shape [B, H, N, d], multiplied by sigma;
+  * round to the storage dtype with round-to-nearest-even (bf16 by bit
+    arithmetic on the float32 pattern, fp16 by numpy's IEEE conversion,
+    fp32 unchanged).
+
+The named workloads are the five configurations the attention library is
+measured on; variants reuse their parent's seed.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str  # "f32" | "f16" | "bf16"
+    causal: bool
+    sigma: float
+    seed: int
+    backward: bool = False
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+    def fwd_flop(self) -> float:
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flop(self) -> float:
+        f = 10.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    # tiny forward case: fp32, non-causal
+    "C1": Workload("C1", 1, 2, 256, 64, "f32", False, 1.0, 1001),
+    # forward bf16 non-causal
+    "C2": Workload("C2", 4, 16, 2048, 128, "bf16", False, 1.0, 1002),
+    # forward bf16 causal, decoder-pretraining shape (and its d=64 variant)
+    "C3": Workload("C3", 2, 32, 8192, 128, "bf16", True, 1.0, 1003),
+    "C3d64": Workload("C3d64", 2, 32, 8192, 64, "bf16", True, 1.0, 1003),
+    # long-context forward fp16 causal, sigma 0.5
+    "C4": Workload("C4", 1, 32, 32768, 128, "f16", True, 0.5, 1004),
+    # backward bf16 causal with recompute (and its d=128 variant)
+    "C5": Workload("C5", 8, 16, 4096, 64, "bf16", True, 1.0, 1005, backward=True),
+    "C5d128": Workload("C5d128", 8, 16, 4096, 128, "bf16", True, 1.0, 1005, backward=True),
+}
+
+
+def round_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = np.isnan(x)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    if nan.any():
+        r[nan] = np.uint16(0x7FC0)
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def round_to(x: np.ndarray, dtype: str):
+    """Round float32 values to ``dtype``.
+
+    Returns (values as float32 holding exactly the rounded numbers,
+             storage array: uint16 bit patterns for bf16, float16 for f16,
+             float32 for f32).
+    """
+    if dtype == "f32":
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        return x, x
+    if dtype == "f16":
+        h = np.ascontiguousarray(x, dtype=np.float32).astype(np.float16)
+        return h.astype(np.float32), h
+    if dtype == "bf16":
+        b = round_bf16_bits(x)
+        return bf16_bits_to_f32(b), b
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_inputs(B: int, H: int, N: int, d: int, dtype: str, sigma: float, seed: int,
+                backward: bool = False):
+    """Draw the seeded inputs. Returns a dict name -> (float32 values, storage array)."""
+    rng = np.random.default_rng(seed)
+    names = ["q", "k", "v"] + (["do"] if backward else [])
+    out = {}
+    for nm in names:
+        x = rng.standard_normal((B, H, N, d), dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        out[nm] = round_to(x, dtype)
+    return out
+
+
+def make_workload_inputs(w: Workload, backward: bool | None = None):
+    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.sigma, w.seed,
+                       w.backward if backward is None else backward)
