@@ -1,0 +1,206 @@
+"""Python binding of libfa_mi355x.so, the gfx950 exact-attention library.
+
+Argument marshalling only: every step of attention runs in the library's HIP
+kernels.  PyTorch provides device memory and the current HIP stream.  If the
+shared library is missing this module raises instead of computing anything
+another way.
+
+Raw entry points (same names and argument order as include/fa.h, tensors in
+place of pointers):
+    fa_fwd(q, k, v, o, lse, scale, causal)
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, causal)
+    fa_bwd_workspace_bytes(B, H, N, d, dtype)
+Conveniences that allocate their outputs with torch:
+    fwd(q, k, v, causal=False, scale=None) -> (o, lse)
+    bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
+    FlashAttention (torch.autograd.Function) and attention(q, k, v, causal, scale)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+LIB_NAME = "libfa_mi355x.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_DTYPE",
+    5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_WORKSPACE", 8: "FA_ERR_HIP",
+}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the shared library (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{LIB_NAME} is not built ({path}); run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    vp, i64, f32, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    L.fa_abi_version.restype = i32
+    L.fa_abi_version.argtypes = []
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_status_string.argtypes = [i32]
+    L.fa_fwd.restype = i32
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
+    L.fa_bwd_workspace_bytes.restype = sz
+    L.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    L.fa_bwd.restype = i32
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                         i64, i64, i64, i64, f32, i32, i32, vp]
+    _lib = L
+    return L
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _check(code: int):
+    if code != 0:
+        msg = load_library().fa_status_string(code).decode()
+        raise FAError(code, msg)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _bhnd(q):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    return tuple(int(x) for x in q.shape)
+
+
+def _check_tensors(*ts):
+    ref = ts[0]
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if t.device != ref.device:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool) -> None:
+    """Enqueue the forward on the current stream of q's device (see include/fa.h)."""
+    L = load_library()
+    _check_tensors(q, k, v, o, lse)
+    B, H, N, d = _bhnd(q)
+    for t in (k, v, o):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o must share shape and dtype")
+    torch = _torch()
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, N]")
+    _check(L.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                    float(scale), int(bool(causal)), dtype_code(q), _stream(q)))
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype: int) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N, d, dtype))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale: float, causal: bool) -> None:
+    """Enqueue the backward on the current stream of q's device (see include/fa.h)."""
+    L = load_library()
+    _check_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    B, H, N, d = _bhnd(q)
+    for t in (k, v, o, dout, dq, dk, dv):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dout, dq, dk, dv must share shape and dtype")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(L.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
+                    B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), _stream(q)))
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None):
+    """Allocate O and LSE and run the forward. Returns (o, lse)."""
+    torch = _torch()
+    B, H, N, d = _bhnd(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, default_scale(d) if scale is None else scale, causal)
+    return o, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, workspace=None):
+    """Allocate dQ, dK, dV (and the workspace unless given) and run the backward."""
+    torch = _torch()
+    B, H, N, d = _bhnd(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        nb = fa_bwd_workspace_bytes(B, H, N, d, dtype_code(q))
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace,
+           default_scale(d) if scale is None else scale, causal)
+    return dq, dk, dv
+
+
+def _autograd_fn():
+    torch = _torch()
+
+    class FlashAttention(torch.autograd.Function):
+        """softmax(scale Q K^T [causal]) V with the library's forward and backward."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, causal=False, scale=None):
+            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            s = default_scale(q.shape[-1]) if scale is None else scale
+            o, lse = fwd(q, k, v, causal, s)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.causal, ctx.scale = causal, s
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale)
+            return dq, dk, dv, None, None
+
+    return FlashAttention
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None):
+    """Differentiable attention through the library (torch.autograd)."""
+    return _autograd_fn().apply(q, k, v, causal, scale)
+
+
+__all__ = [
+    "load_library", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fwd", "bwd", "attention",
+    "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH",
+]

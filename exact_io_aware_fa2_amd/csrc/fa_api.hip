@@ -1,0 +1,126 @@
+// C-ABI entry points of libfa_mi355x.so: argument checks, then dispatch to the
+// kernel launchers.  Declarations and the contract are in include/fa.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 30;
+constexpr int64_t kMaxWorkgroups = (int64_t(1) << 24) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by both passes.  Workgroup counts are bounded for the
+// smallest query tile any kernel uses (32 rows).
+int check_shape(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (N > kMaxN) return FA_ERR_SHAPE;
+  if (B > INT32_MAX / H) return FA_ERR_SHAPE;
+  const int64_t bh = B * H;
+  if (bh * ((N + 31) / 32) > kMaxWorkgroups) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  return FA_OK;
+}
+
+int check_scale(float scale) {
+  if (!isfinite(scale) || scale < 0.0f) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer argument";
+    case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and within limits)";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
+    case FA_ERR_DTYPE: return "unsupported dtype";
+    case FA_ERR_ALIGN: return "data pointer not 16-byte aligned";
+    case FA_ERR_SCALE: return "scale must be finite and >= 0";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+           int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = (int)(B * H);
+  a.N = (int)N;
+  a.d = (int)d;
+  a.c = scale * fa::kLog2eHost;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.stream = (hipStream_t)stream;
+  return fa::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  if (dtype != FA_F16 && dtype != FA_BF16) return 0;
+  return (size_t)(B * H * N) * sizeof(float);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+           int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d, dtype))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dvec = (float*)workspace;
+  a.BH = (int)(B * H);
+  a.N = (int)N;
+  a.d = (int)d;
+  a.scale = scale;
+  a.c = scale * fa::kLog2eHost;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.stream = (hipStream_t)stream;
+  return fa::launch_bwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,476 @@
+// Backward attention kernels for gfx950.
+//
+// The pages fix only the principle ("FlashAttention" lexicon, "Methodische
+// Grundlagen", paragraph "Neuberechnung statt Speicherung"): the score matrix
+// is not kept from the forward pass but rebuilt, trading compute for memory
+// traffic.  The gradient itself is the chain rule through the softmax:
+//
+//   P_ij  = exp(scale q_i.k_j - LSE_i)           (rebuilt from Q, K and LSE)
+//   dV_j  = sum_i P_ij dO_i
+//   dP_ij = dO_i . v_j
+//   dS_ij = P_ij (dP_ij - D_i),   D_i = dO_i . O_i   (= sum_j P_ij dP_ij)
+//   dQ_i  = scale sum_j dS_ij k_j
+//   dK_j  = scale sum_i dS_ij q_i
+//
+// Three launches on the caller's stream, none of which writes an N x N array:
+//   1. bwd_pre:  D_i = dO_i . O_i                       (HBM-bound, fp32 out)
+//   2. bwd_dkdv: one workgroup per (64-key... 128-key tile, batch*head); each
+//                wavefront owns 32 keys and keeps K, V, dK, dV in registers
+//                while the query tiles stream through LDS.
+//   3. bwd_dq:   one workgroup per (query tile, batch*head); each wavefront
+//                owns 32 query rows and keeps Q, dO, dQ in registers while the
+//                key tiles stream through LDS.
+// Splitting dQ from dK/dV recomputes S and dP once more but needs no atomic
+// accumulation, so every gradient is bitwise reproducible run to run
+// ("FlashAttention-2 (DE)", "Leistung und Effizienz": exact and
+// deterministic).
+//
+// All products use v_mfma_f32_32x32x16 (bf16/fp16 in, fp32 accumulate).  P and
+// dS are rounded to the input type (nearest even) before they enter a product.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+// ------------------------------------------------------------------ D_i
+
+template <class TR, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
+                                                      const uint16_t* __restrict__ dO,
+                                                      float* __restrict__ Dv, int rows) {
+  constexpr int KCH = D / 8;            // lanes per row
+  constexpr int RPB = 256 / KCH;        // rows per workgroup
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x * RPB + tid / KCH;
+  const int ch = tid % KCH;
+  float acc = 0.0f;
+  if (row < rows) {
+    const u32x4_t a = *(const u32x4_t*)(O + (size_t)row * D + ch * 8);
+    const u32x4_t b = *(const u32x4_t*)(dO + (size_t)row * D + ch * 8);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc = TR::dot2(a[p], b[p], acc);
+  }
+#pragma unroll
+  for (int off = KCH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && ch == 0) Dv[row] = acc;
+}
+
+// ------------------------------------------------------------------ dK, dV
+
+template <class TR, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                     const float* __restrict__ LSE, const float* __restrict__ Dvec,
+                     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_ktiles,
+                     uint32_t total, float c, float scale) {
+  constexpr int BKV = 128;          // keys per workgroup (4 wavefronts x 32)
+  constexpr int BQ = 64;            // query rows per step
+  constexpr int KCH = D / 8;
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int UNITS = (BQ / 4) * KCH;       // 4-row x 1-chunk staging units
+  constexpr int ULOADS = (UNITS + 255) / 256;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sQt[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sdOt[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sD[2][BQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const uint32_t lid = xcd_remap(blockIdx.x, total);
+  const int bh = lid / n_ktiles;
+  const int kt = lid % n_ktiles;
+  const int k0 = kt * BKV;
+  const int kw = k0 + 32 * w;  // first key of this wavefront
+  const size_t head_off = (size_t)bh * N * D;
+  const uint16_t* Qh = Q + head_off;
+  const uint16_t* dOh = dO + head_off;
+  const float* Lh = LSE + (size_t)bh * N;
+  const float* Dh = Dvec + (size_t)bh * N;
+
+  // K and V rows of this wavefront as B operands (column = key = lane % 32)
+  u32x4_t kf[NKS], vf[NKS];
+  {
+    const int key = kw + l32;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (key < N) {
+        kf[ks] = *(const u32x4_t*)(K + head_off + (size_t)key * D + 16 * ks + 8 * h);
+        vf[ks] = *(const u32x4_t*)(V + head_off + (size_t)key * D + 16 * ks + 8 * h);
+      } else {
+        kf[ks] = u32x4_t{0, 0, 0, 0};
+        vf[ks] = u32x4_t{0, 0, 0, 0};
+      }
+    }
+  }
+  f32x16_t acc_dk[NDB], acc_dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    acc_dk[db] = zero16();
+    acc_dv[db] = zero16();
+  }
+
+  const int i_begin = CAUSAL ? (k0 / BQ) * BQ : 0;
+  const int n_steps = (N - i_begin + BQ - 1) / BQ;
+
+  u32x4_t qreg[ULOADS][4], oreg[ULOADS][4];
+  float lreg = 0.0f, dreg = 0.0f;
+
+  auto load_step = [&](int i0) {
+#pragma unroll
+    for (int r = 0; r < ULOADS; ++r) {
+      const int u = tid + 256 * r;
+      const int g = u / KCH, ch = u % KCH;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = i0 + 4 * g + rr;
+        if (u < UNITS && row < N) {
+          qreg[r][rr] = *(const u32x4_t*)(Qh + (size_t)row * D + ch * 8);
+          oreg[r][rr] = *(const u32x4_t*)(dOh + (size_t)row * D + ch * 8);
+        } else {
+          qreg[r][rr] = u32x4_t{0, 0, 0, 0};
+          oreg[r][rr] = u32x4_t{0, 0, 0, 0};
+        }
+      }
+    }
+    if (tid < BQ) {
+      const int row = i0 + tid;
+      // rows past the end: P = exp2(-inf) = 0 and D = 0, so they add nothing
+      lreg = row < N ? Lh[row] * kLog2e : INFINITY;
+      dreg = row < N ? Dh[row] : 0.0f;
+    }
+  };
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < ULOADS; ++r) {
+      const int u = tid + 256 * r;
+      if (u < UNITS) {
+        const int g = u / KCH, ch = u % KCH;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          *(u32x4_t*)(&sQ[buf][swz_off<D>(4 * g + rr, ch)]) = qreg[r][rr];
+          *(u32x4_t*)(&sdO[buf][swz_off<D>(4 * g + rr, ch)]) = oreg[r][rr];
+        }
+        store_interleaved(&sQt[buf][il_off<D>(g, 8 * ch)], qreg[r]);
+        store_interleaved(&sdOt[buf][il_off<D>(g, 8 * ch)], oreg[r]);
+      }
+    }
+    if (tid < BQ) {
+      sL[buf][tid] = lreg;
+      sD[buf][tid] = dreg;
+    }
+  };
+
+  if (n_steps > 0) {
+    load_step(i_begin);
+    store_step(0);
+  }
+  __syncthreads();
+
+  for (int st = 0; st < n_steps; ++st) {
+    const int buf = st & 1;
+    const int i0 = i_begin + st * BQ;
+    const bool has_next = st + 1 < n_steps;
+    if (has_next) load_step(i0 + BQ);
+
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qlo = i0 + 32 * qb;
+      // causal: the whole 32-row block sees none of this wavefront's keys
+      if (CAUSAL && qlo + 31 < kw) continue;
+
+      // S = Q K^T and dP = dO V^T (rows = queries in registers, column = key)
+      f32x16_t s = zero16(), dp = zero16();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int row = 32 * qb + l32;
+        const u32x4_t qa = *(const u32x4_t*)(&sQ[buf][swz_off<D>(row, 2 * ks + h)]);
+        const u32x4_t oa = *(const u32x4_t*)(&sdO[buf][swz_off<D>(row, 2 * ks + h)]);
+        s = TR::mfma(qa, kf[ks], s);
+        dp = TR::mfma(oa, vf[ks], dp);
+      }
+
+      const int key = kw + l32;
+      uint32_t pk[8], dsk[8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 lv = *(const float4*)(&sL[buf][32 * qb + 8 * g + 4 * h]);
+        const float4 dv = *(const float4*)(&sD[buf][32 * qb + 8 * g + 4 * h]);
+        const float lq[4] = {lv.x, lv.y, lv.z, lv.w};
+        const float dq[4] = {dv.x, dv.y, dv.z, dv.w};
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const int qrow = qlo + 8 * g + 4 * h + e;
+          float pv = fast_exp2(fmaf(s[r], c, -lq[e]));
+          if (CAUSAL && key > qrow) pv = 0.0f;
+          p[e] = pv;
+          ds[e] = pv * (dp[r] - dq[e]);
+        }
+        pk[2 * g + 0] = TR::pack2(p[0], p[1]);
+        pk[2 * g + 1] = TR::pack2(p[2], p[3]);
+        dsk[2 * g + 0] = TR::pack2(ds[0], ds[1]);
+        dsk[2 * g + 1] = TR::pack2(ds[2], ds[3]);
+      }
+
+      // dV^T += dO^T P and dK^T += Q^T dS: contraction over the 32 query rows,
+      // in two steps of 16; step t pairs accumulator values 8t..8t+7, i.e.
+      // rows {16t + 4h + 0..3} and {16t + 8 + 4h + 0..3} of the block.
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4_t pb = u32x4_t{pk[4 * t + 0], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
+        const u32x4_t db_ = u32x4_t{dsk[4 * t + 0], dsk[4 * t + 1], dsk[4 * t + 2], dsk[4 * t + 3]};
+        const int ga = 8 * qb + 4 * t + h, gb = ga + 2;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int col = 32 * db + l32;
+          const u32x2_t oa0 = *(const u32x2_t*)(&sdOt[buf][il_off<D>(ga, col)]);
+          const u32x2_t oa1 = *(const u32x2_t*)(&sdOt[buf][il_off<D>(gb, col)]);
+          acc_dv[db] = TR::mfma(u32x4_t{oa0[0], oa0[1], oa1[0], oa1[1]}, pb, acc_dv[db]);
+          const u32x2_t qa0 = *(const u32x2_t*)(&sQt[buf][il_off<D>(ga, col)]);
+          const u32x2_t qa1 = *(const u32x2_t*)(&sQt[buf][il_off<D>(gb, col)]);
+          acc_dk[db] = TR::mfma(u32x4_t{qa0[0], qa0[1], qa1[0], qa1[1]}, db_, acc_dk[db]);
+        }
+      }
+    }
+
+    if (has_next) store_step(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds key kw + lane%32 and columns 32db + 8g + 4h + 0..3
+  const int key = kw + l32;
+  if (key < N) {
+    uint16_t* dkrow = dK + head_off + (size_t)key * D;
+    uint16_t* dvrow = dV + head_off + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * h;
+        *(u32x2_t*)(dkrow + col) =
+            u32x2_t{TR::pack2(acc_dk[db][4 * g + 0] * scale, acc_dk[db][4 * g + 1] * scale),
+                    TR::pack2(acc_dk[db][4 * g + 2] * scale, acc_dk[db][4 * g + 3] * scale)};
+        *(u32x2_t*)(dvrow + col) =
+            u32x2_t{TR::pack2(acc_dv[db][4 * g + 0], acc_dv[db][4 * g + 1]),
+                    TR::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3])};
+      }
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+
+template <class TR, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                   const float* __restrict__ LSE, const float* __restrict__ Dvec,
+                   uint16_t* __restrict__ dQ, int N, int n_qtiles, uint32_t total, float c,
+                   float scale) {
+  constexpr int BR = 128;           // query rows per workgroup (4 wavefronts x 32)
+  constexpr int BC = 64;            // keys per tile
+  constexpr int KCH = D / 8;
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int UNITS = (BC / 4) * KCH;
+  constexpr int ULOADS = (UNITS + 255) / 256;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sKt[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const uint32_t lid = xcd_remap(blockIdx.x, total);
+  const int bh = lid / n_qtiles;
+  int qt = lid % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  const int q0 = qt * BR;
+  const int qw = q0 + 32 * w;
+  const int qrow = qw + l32;
+  const size_t head_off = (size_t)bh * N * D;
+  const uint16_t* Kh = K + head_off;
+  const uint16_t* Vh = V + head_off;
+
+  u32x4_t qf[NKS], of[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (qrow < N) {
+      qf[ks] = *(const u32x4_t*)(Q + head_off + (size_t)qrow * D + 16 * ks + 8 * h);
+      of[ks] = *(const u32x4_t*)(dO + head_off + (size_t)qrow * D + 16 * ks + 8 * h);
+    } else {
+      qf[ks] = u32x4_t{0, 0, 0, 0};
+      of[ks] = u32x4_t{0, 0, 0, 0};
+    }
+  }
+  const float lq = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
+  const float dq_ = qrow < N ? Dvec[(size_t)bh * N + qrow] : 0.0f;
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+  const int wave_last = CAUSAL ? min(N, qw + 32) : N;
+  const int wave_tiles = (wave_last + BC - 1) / BC;
+
+  u32x4_t kreg[ULOADS][4], vreg[ULOADS][4];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < ULOADS; ++r) {
+      const int u = tid + 256 * r;
+      const int g = u / KCH, ch = u % KCH;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = j0 + 4 * g + rr;
+        if (u < UNITS && key < N) {
+          kreg[r][rr] = *(const u32x4_t*)(Kh + (size_t)key * D + ch * 8);
+          vreg[r][rr] = *(const u32x4_t*)(Vh + (size_t)key * D + ch * 8);
+        } else {
+          kreg[r][rr] = u32x4_t{0, 0, 0, 0};
+          vreg[r][rr] = u32x4_t{0, 0, 0, 0};
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < ULOADS; ++r) {
+      const int u = tid + 256 * r;
+      if (u < UNITS) {
+        const int g = u / KCH, ch = u % KCH;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          *(u32x4_t*)(&sK[buf][swz_off<D>(4 * g + rr, ch)]) = kreg[r][rr];
+          *(u32x4_t*)(&sV[buf][swz_off<D>(4 * g + rr, ch)]) = vreg[r][rr];
+        }
+        store_interleaved(&sKt[buf][il_off<D>(g, 8 * ch)], kreg[r]);
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int jt = 0; jt < n_tiles; ++jt) {
+    const int buf = jt & 1;
+    const int j0 = jt * BC;
+    const bool has_next = jt + 1 < n_tiles;
+    if (has_next) load_tile(j0 + BC);
+
+    if (jt < wave_tiles) {
+      const bool need_mask = (CAUSAL && (j0 + BC - 1 > qw)) || (j0 + BC > N);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // S^T = K Q^T and dP^T = V dO^T (column = query = lane % 32)
+        f32x16_t s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int row = 32 * kb + l32;
+          const u32x4_t ka = *(const u32x4_t*)(&sK[buf][swz_off<D>(row, 2 * ks + h)]);
+          const u32x4_t va = *(const u32x4_t*)(&sV[buf][swz_off<D>(row, 2 * ks + h)]);
+          s = TR::mfma(ka, qf[ks], s);
+          dp = TR::mfma(va, of[ks], dp);
+        }
+        uint32_t dsk[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float ds2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int key = j0 + 32 * kb + 8 * ((r + e) / 4) + 4 * h + ((r + e) % 4);
+            float pv = fast_exp2(fmaf(s[r + e], c, -lq));
+            if (need_mask && (key >= N || (CAUSAL && key > qrow))) pv = 0.0f;
+            ds2[e] = pv * (dp[r + e] - dq_);
+          }
+          dsk[r / 2] = TR::pack2(ds2[0], ds2[1]);
+        }
+        // dQ^T += K^T dS^T over the 32 keys of the block, two steps of 16
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u32x4_t b = u32x4_t{dsk[4 * t + 0], dsk[4 * t + 1], dsk[4 * t + 2], dsk[4 * t + 3]};
+          const int ga = 8 * kb + 4 * t + h, gb = ga + 2;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int col = 32 * db + l32;
+            const u32x2_t a0 = *(const u32x2_t*)(&sKt[buf][il_off<D>(ga, col)]);
+            const u32x2_t a1 = *(const u32x2_t*)(&sKt[buf][il_off<D>(gb, col)]);
+            acc[db] = TR::mfma(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, b, acc[db]);
+          }
+        }
+      }
+    }
+
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qrow < N) {
+    uint16_t* drow = dQ + head_off + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * h;
+        *(u32x2_t*)(drow + col) =
+            u32x2_t{TR::pack2(acc[db][4 * g + 0] * scale, acc[db][4 * g + 1] * scale),
+                    TR::pack2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale)};
+      }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+template <class TR, int D, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdArgs& a) {
+  const int rows = a.BH * a.N;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_pre_kernel<TR, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0,
+                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dvec, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int n_ktiles = (a.N + 127) / 128;
+  const uint32_t tk = (uint32_t)(n_ktiles * a.BH);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<TR, D, CAUSAL>), dim3(tk), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                     a.N, n_ktiles, tk, a.c, a.scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int n_qtiles = (a.N + 127) / 128;
+  const uint32_t tq = (uint32_t)(n_qtiles * a.BH);
+  hipLaunchKernelGGL((bwd_dq_kernel<TR, D, CAUSAL>), dim3(tq), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.N, n_qtiles, tq,
+                     a.c, a.scale);
+  return hipGetLastError();
+}
+
+template <class TR>
+static hipError_t dispatch_bwd(const BwdArgs& a) {
+  if (a.d == 128) return a.causal ? launch_bwd_t<TR, 128, true>(a) : launch_bwd_t<TR, 128, false>(a);
+  return a.causal ? launch_bwd_t<TR, 64, true>(a) : launch_bwd_t<TR, 64, false>(a);
+}
+
+hipError_t launch_bwd(const BwdArgs& a) {
+  return a.dtype == DT_BF16 ? dispatch_bwd<BF16>(a) : dispatch_bwd<F16>(a);
+}
+
+}  // namespace fa

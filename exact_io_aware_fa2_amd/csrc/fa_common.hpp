@@ -1,0 +1,152 @@
+// Shared device helpers for the gfx950 (CDNA4) attention kernels.
+//
+// Everything here is written for one target: 64-lane wavefronts, the
+// v_mfma_f32_32x32x16_{bf16,f16} and v_mfma_f32_32x32x2_f32 matrix
+// instructions, and 16-byte LDS/global accesses.
+//
+// MFMA 32x32 register layouts used throughout (lane l = 0..63, h = l / 32):
+//   A operand (M x K):  lane l holds row m = l % 32 and a set of K elements
+//                       that depends only on h (8 for bf16/f16, 1 for f32).
+//   B operand (K x N):  lane l holds column n = l % 32 and the K elements of
+//                       the same set as the A operand of the same lane.
+//   C/D (M x N), 16 fp32 values per lane, value r:
+//                       row m = 8 * (r / 4) + 4 * h + (r % 4), column n = l % 32.
+// Only the output layout is relied on exactly.  For the operands the kernels
+// only rely on "the same (h, element index) names the same K position in A
+// and in B", so the order of the contraction index inside an instruction is a
+// free relabelling (a permutation of the summation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16-bit element traits: bf16 and fp16 share every kernel; they differ only in
+// the MFMA opcode, the fp32 -> 16-bit packing and the 2-wide dot product.
+struct BF16 {
+  __device__ static inline f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  // Two fp32 values -> packed pair, round to nearest even (v_cvt_pk_bf16_f32).
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    bf16x2_t r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  // acc + x.lo + x.hi for a packed pair (v_dot2c_f32_bf16 against (1, 1)).
+  __device__ static inline float sum2(uint32_t x, float acc) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), one, acc, false);
+  }
+  // acc + a.lo*b.lo + a.hi*b.hi
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+  }
+};
+
+struct F16 {
+  __device__ static inline f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    f16x2_t r;
+    r[0] = (_Float16)lo;
+    r[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  __device__ static inline float sum2(uint32_t x, float acc) {
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, x), one, acc, false);
+  }
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  acc, false);
+  }
+};
+
+__device__ inline f32x16_t mfma_f32(float a, float b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ inline f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by lane (l ^ 32): the other half-wave.
+__device__ inline float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// Workgroup index -> logical tile index, so that the workgroups the hardware
+// places on one XCD (consecutive dispatch ids go round-robin over the 8 XCDs)
+// receive one contiguous range of logical tiles.  Tiles of the same head then
+// run on the same XCD and share its L2 for the K/V stream.  A bijection on
+// [0, total) for any total.
+__device__ inline uint32_t xcd_remap(uint32_t pid, uint32_t total) {
+  const uint32_t nx = 8;
+  const uint32_t x = pid % nx, slot = pid / nx;
+  const uint32_t base = total / nx, rem = total % nx;
+  return x * base + (x < rem ? x : rem) + slot;
+}
+
+// The two 16-bit halves of a dword.
+__device__ inline uint32_t lo16(uint32_t x) { return x & 0xffffu; }
+__device__ inline uint32_t hi16(uint32_t x) { return x >> 16; }
+__device__ inline uint32_t pair16(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
+
+// Row-major tile of 16-bit elements in LDS, `D` columns per row, with the
+// 16-byte chunks of each row XOR-swizzled by the row index so that 32 lanes
+// reading one chunk column of 32 consecutive rows hit distinct banks.
+template <int D>
+__device__ inline int swz_off(int row, int chunk) {
+  constexpr int KCH = D / 8;
+  constexpr int SWZ = (KCH < 16 ? KCH : 16) - 1;
+  return row * D + ((chunk ^ (row & SWZ)) * 8);
+}
+
+// "Interleaved" tile: groups of 4 consecutive rows stored column by column,
+// [row / 4][D][4], so one 8-byte read returns 4 consecutive rows of one column
+// (the layout the second operand of a contraction over rows needs).
+template <int D>
+__device__ inline int il_off(int row_group, int col) {
+  return (row_group * D + col) * 4;
+}
+
+// 4 rows x 8 columns (each row one 16-byte chunk) -> 8 interleaved units of
+// 4 rows at one column, written as four 16-byte LDS stores at `dst`, which is
+// the address of unit (row_group, 8 * chunk).
+__device__ inline void store_interleaved(uint16_t* dst, const u32x4_t r[4]) {
+  uint32_t o[16];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t a = r[0][p], b = r[1][p], c = r[2][p], d = r[3][p];
+    o[4 * p + 0] = pair16(lo16(a), lo16(b));  // column 2p, rows 0,1
+    o[4 * p + 1] = pair16(lo16(c), lo16(d));  // column 2p, rows 2,3
+    o[4 * p + 2] = pair16(hi16(a), hi16(b));  // column 2p+1, rows 0,1
+    o[4 * p + 3] = pair16(hi16(c), hi16(d));  // column 2p+1, rows 2,3
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    *(u32x4_t*)(dst + 8 * x) = u32x4_t{o[4 * x + 0], o[4 * x + 1], o[4 * x + 2], o[4 * x + 3]};
+}
+
+}  // namespace fa

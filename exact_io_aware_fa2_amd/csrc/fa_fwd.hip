@@ -1,0 +1,457 @@
+// Forward attention kernels for gfx950: O = softmax(scale * Q K^T [causal]) V,
+// plus the per-row log-sum-exp, computed tiled and fused in one pass.
+//
+// The method ("FlashAttention" lexicon, "Methodische Grundlagen"): Q, K, V are
+// cut into blocks that fit on-chip memory; similarity, normalisation and
+// weighting run in one pass with no intermediate in HBM; the row normaliser
+// is accumulated as the keys stream by and earlier partial results are
+// corrected when a larger score appears; only the log-sum-exp per row is kept
+// for the backward pass.  The work split follows "FlashAttention-2 (DE)",
+// "Technische Architektur", items 1-3: few non-matmul operations, one head
+// spread over many compute units (one workgroup per query tile and head), and
+// query rows split across wavefronts so each wavefront normalises its own
+// rows without exchanging partial results through shared memory.
+//
+// gfx950 mapping (16-bit inputs):
+//   * workgroup = 4 wavefronts x QB blocks of 32 query rows; grid = query
+//     tiles x (batch * heads), XCD-grouped, heaviest causal tiles first.
+//   * each wavefront computes S^T = K Q^T with v_mfma_f32_32x32x16: the
+//     accumulator then holds, per lane, one query row (lane % 32) and 16 keys,
+//     so row max / row sum are in-lane plus one exchange between half-waves,
+//     and the probabilities are already in the B-operand layout of
+//     O^T += V^T P^T (they never leave registers).
+//   * K and V tiles of 64 keys are staged HBM -> registers -> LDS with 16-byte
+//     coalesced loads, double buffered (the next tile is in flight while the
+//     current one is consumed).  K is stored row-major with an XOR swizzle of
+//     its 16-byte chunks; V is stored as groups of 4 keys per column
+//     ([key/4][d][4]) so the V^T operand is two 8-byte LDS reads per lane.
+//   * softmax in the exp2 domain with scale*log2(e) folded into one FMA; the
+//     output is rescaled only when a row maximum grows by more than kTau (in
+//     log2 units), and normalised once at the end (deferred rescaling).
+//   * causal: key tiles above the diagonal are never loaded or multiplied;
+//     only tiles crossing the diagonal are masked.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+// A row maximum is only re-based when it grows by more than kTau (log2 units).
+// Between re-bases probabilities are bounded by 2^kTau, which bf16/fp16 and
+// the fp32 accumulators hold without loss of relative precision; the final
+// normalisation uses the same reference maximum for numerator and
+// denominator, so the result is unchanged mathematically.
+constexpr float kTau = 8.0f;
+
+template <class TR, int D, int QB, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                  const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                  float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c) {
+  constexpr int BC = 64;               // keys per tile
+  constexpr int NW = 4;                // wavefronts per workgroup
+  constexpr int BR = 32 * QB * NW;     // query rows per workgroup
+  constexpr int KCH = D / 8;           // 16-byte chunks per row
+  constexpr int SWZ = (KCH < 16 ? KCH : 16) - 1;
+  constexpr int KLOADS = BC * KCH / 256;            // 16-byte K chunks per thread
+  constexpr int VUNITS = (BC / 4) * KCH;            // 4-key x 8-column V units
+  constexpr int VLOADS = (VUNITS + 255) / 256;      // units per thread
+  constexpr int NKB = BC / 32;                      // 32-key blocks per tile
+  constexpr int NDB = D / 32;                       // 32-column blocks of the output
+  constexpr int NKS = D / 16;                       // MFMA k-steps over d
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const uint32_t lid = xcd_remap(blockIdx.x, total);
+  const int bh = lid / n_qtiles;
+  int qt = lid % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest tiles first
+  const int q0 = qt * BR;
+
+  const size_t head_off = (size_t)bh * N * D;
+  const uint16_t* Qh = Q + head_off;
+  const uint16_t* Kh = K + head_off;
+  const uint16_t* Vh = V + head_off;
+
+  const int qw = q0 + w * 32 * QB;  // first query row of this wavefront
+
+  // ---- Q fragments (B operand of S^T = K Q^T), loaded once.
+  u32x4_t qf[QB][NKS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw + 32 * qb + l32;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (row < N)
+        qf[qb][ks] = *(const u32x4_t*)(Qh + (size_t)row * D + 16 * ks + 8 * h);
+      else
+        qf[qb][ks] = u32x4_t{0, 0, 0, 0};
+    }
+  }
+
+  // ---- running state: one query row per lane and query block
+  f32x16_t acc_o[NDB][QB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) acc_o[db][qb] = zero16();
+  float m_run[QB], l_run[QB], lt_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.0f;
+    lt_run[qb] = 0.0f;
+  }
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+  const int wave_last = CAUSAL ? min(N, qw + 32 * QB) : N;  // exclusive key bound for this wave
+  const int wave_tiles = (wave_last + BC - 1) / BC;
+
+  // ---- staging registers for the next tile
+  u32x4_t kreg[KLOADS];
+  u32x4_t vreg[VLOADS][4];
+
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < KLOADS; ++r) {
+      const int cidx = tid + 256 * r;
+      const int row = cidx / KCH, col = cidx % KCH;
+      if (j0 + row < N)
+        kreg[r] = *(const u32x4_t*)(Kh + (size_t)(j0 + row) * D + col * 8);
+      else
+        kreg[r] = u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < VLOADS; ++r) {
+      const int u = tid + 256 * r;
+      const int kg = u / KCH, dc = u % KCH;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = j0 + 4 * kg + rr;
+        if (u < VUNITS && key < N)
+          vreg[r][rr] = *(const u32x4_t*)(Vh + (size_t)key * D + dc * 8);
+        else
+          vreg[r][rr] = u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < KLOADS; ++r) {
+      const int cidx = tid + 256 * r;
+      const int row = cidx / KCH, col = cidx % KCH;
+      *(u32x4_t*)(&sK[buf][row * D + ((col ^ (row & SWZ)) * 8)]) = kreg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VLOADS; ++r) {
+      const int u = tid + 256 * r;
+      if (u < VUNITS) {
+        const int kg = u / KCH, dc = u % KCH;
+        // 4 rows x 8 columns -> 8 units of (4 keys at one column)
+        uint32_t outw[16];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t a = vreg[r][0][p], b = vreg[r][1][p], cc = vreg[r][2][p], d = vreg[r][3][p];
+          // column 2p: low halves; column 2p+1: high halves
+          outw[4 * p + 0] = pair16(lo16(a), lo16(b));
+          outw[4 * p + 1] = pair16(lo16(cc), lo16(d));
+          outw[4 * p + 2] = pair16(hi16(a), hi16(b));
+          outw[4 * p + 3] = pair16(hi16(cc), hi16(d));
+        }
+        uint16_t* dst = &sV[buf][(kg * D + dc * 8) * 4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          *(u32x4_t*)(dst + 8 * x) =
+              u32x4_t{outw[4 * x + 0], outw[4 * x + 1], outw[4 * x + 2], outw[4 * x + 3]};
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int jt = 0; jt < n_tiles; ++jt) {
+    const int buf = jt & 1;
+    const int j0 = jt * BC;
+    const bool has_next = jt + 1 < n_tiles;
+    if (has_next) load_tile(j0 + BC);
+
+    if (jt < wave_tiles) {
+      // ---- S^T = K Q^T for this tile
+      f32x16_t s[NKB][QB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int row = 32 * kb + l32;
+          const int ch = 2 * ks + h;
+          const u32x4_t kf = *(const u32x4_t*)(&sK[buf][row * D + ((ch ^ (row & SWZ)) * 8)]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = TR::mfma(kf, qf[qb][ks], s[kb][qb]);
+        }
+      }
+
+      // ---- mask (only tiles that cross the diagonal or the sequence end)
+      const bool need_mask = (CAUSAL && (j0 + BC - 1 > qw)) || (j0 + BC > N);
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int qrow = qw + 32 * qb + l32;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = j0 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
+              const bool bad = (key >= N) || (CAUSAL && key > qrow);
+              if (bad) s[kb][qb][r] = -INFINITY;
+            }
+        }
+      }
+
+      // ---- online softmax (exp2 domain), per query row = per lane
+      uint32_t pt[NKB][QB][8];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const float mnew = mx * c;
+        if (mnew > m_run[qb] + kTau) {
+          const float alpha = fast_exp2(m_run[qb] - mnew);
+          m_run[qb] = mnew;
+          l_run[qb] *= alpha;
+          lt_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_o[db][qb][r] *= alpha;
+        }
+        const float mneg = -m_run[qb];
+        float lsum = 0.0f, ltsum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(fmaf(s[kb][qb][r], c, mneg));
+            const float p1 = fast_exp2(fmaf(s[kb][qb][r + 1], c, mneg));
+            lsum += p0;
+            lsum += p1;
+            const uint32_t pk = TR::pack2(p0, p1);
+            ltsum = TR::sum2(pk, ltsum);
+            pt[kb][qb][r / 2] = pk;
+          }
+        l_run[qb] += lsum;
+        lt_run[qb] += ltsum;
+      }
+
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int col = 32 * db + l32;
+            const u32x2_t va = *(const u32x2_t*)(&sV[buf][((8 * kb + 4 * t + h) * D + col) * 4]);
+            const u32x2_t vb = *(const u32x2_t*)(&sV[buf][((8 * kb + 4 * t + 2 + h) * D + col) * 4]);
+            const u32x4_t vf = u32x4_t{va[0], va[1], vb[0], vb[1]};
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+              const u32x4_t pf = u32x4_t{pt[kb][qb][4 * t + 0], pt[kb][qb][4 * t + 1],
+                                         pt[kb][qb][4 * t + 2], pt[kb][qb][4 * t + 3]};
+              acc_o[db][qb] = TR::mfma(vf, pf, acc_o[db][qb]);
+            }
+          }
+        }
+      }
+    }
+
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise once, store O and LSE
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw + 32 * qb + l32;
+    const float lt = lt_run[qb] + swap_halves(lt_run[qb]);
+    const float l = l_run[qb] + swap_halves(l_run[qb]);
+    const float inv = 1.0f / lt;
+    if (row < N) {
+      uint16_t* orow = O + head_off + (size_t)row * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = 32 * db + 8 * g + 4 * h;
+          const uint32_t w0 = TR::pack2(acc_o[db][qb][4 * g + 0] * inv, acc_o[db][qb][4 * g + 1] * inv);
+          const uint32_t w1 = TR::pack2(acc_o[db][qb][4 * g + 2] * inv, acc_o[db][qb][4 * g + 3] * inv);
+          *(u32x2_t*)(orow + col) = u32x2_t{w0, w1};
+        }
+      if (h == 0) LSE[(size_t)bh * N + row] = (m_run[qb] + __log2f(l)) * kLn2;
+    }
+  }
+}
+
+// fp32 inputs: same scheme with v_mfma_f32_32x32x2_f32 and unrounded fp32
+// probabilities; one block of 32 query rows per wavefront, 32-key tiles.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd32_kernel(const float* __restrict__ Q,
+                                                    const float* __restrict__ K,
+                                                    const float* __restrict__ V,
+                                                    float* __restrict__ O, float* __restrict__ LSE,
+                                                    int N, int n_qtiles, uint32_t total, float c) {
+  constexpr int BC = 32;
+  constexpr int BR = 128;
+  constexpr int KP = D + 1;  // padded K row (conflict-free column reads)
+  constexpr int NDB = D / 32;
+  __shared__ float sK[BC * KP];
+  __shared__ float sV[BC * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const uint32_t lid = xcd_remap(blockIdx.x, total);
+  const int bh = lid / n_qtiles;
+  int qt = lid % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  const int q0 = qt * BR;
+  const size_t head_off = (size_t)bh * N * D;
+  const int qw = q0 + 32 * w;
+  const int qrow = qw + l32;
+
+  float qf[D / 2];
+#pragma unroll
+  for (int ks = 0; ks < D / 2; ++ks)
+    qf[ks] = (qrow < N) ? Q[head_off + (size_t)qrow * D + 2 * ks + h] : 0.0f;
+
+  f32x16_t acc_o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc_o[db] = zero16();
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+  const int wave_last = CAUSAL ? min(N, qw + 32) : N;
+  const int wave_tiles = (wave_last + BC - 1) / BC;
+
+  for (int jt = 0; jt < n_tiles; ++jt) {
+    const int j0 = jt * BC;
+    __syncthreads();
+    for (int x = tid; x < BC * D; x += 256) {
+      const int row = x / D, col = x % D;
+      const bool ok = j0 + row < N;
+      sK[row * KP + col] = ok ? K[head_off + (size_t)(j0 + row) * D + col] : 0.0f;
+      sV[row * D + col] = ok ? V[head_off + (size_t)(j0 + row) * D + col] : 0.0f;
+    }
+    __syncthreads();
+    if (jt >= wave_tiles) continue;
+
+    f32x16_t s = zero16();
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks) s = mfma_f32(sK[l32 * KP + 2 * ks + h], qf[ks], s);
+
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = j0 + 8 * (r / 4) + 4 * h + (r % 4);
+      if (key >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float mnew = fmaxf(m_run, mx * c);
+    const float alpha = fast_exp2(m_run - mnew);
+    m_run = mnew;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = fast_exp2(fmaf(s[r], c, -mnew));
+      l_run += p[r];
+    }
+    // O^T += V^T P^T: k-step r pairs key 8(r/4)+(r%4) (h = 0) with key 8(r/4)+4+(r%4) (h = 1)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r / 4) + 4 * h + (r % 4);
+        acc_o[db] = mfma_f32(sV[key * D + 32 * db + l32], p[r], acc_o[db]);
+      }
+  }
+
+  const float l = l_run + swap_halves(l_run);
+  const float inv = 1.0f / l;
+  if (qrow < N) {
+    float* orow = O + head_off + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) orow[32 * db + 8 * (r / 4) + 4 * h + (r % 4)] = acc_o[db][r] * inv;
+    if (h == 0) LSE[(size_t)bh * N + qrow] = (m_run + __log2f(l)) * kLn2;
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+template <class TR, int D, int QB, bool CAUSAL>
+static hipError_t launch16(const FwdArgs& a) {
+  constexpr int BR = 32 * QB * 4;
+  const int n_qtiles = (a.N + BR - 1) / BR;
+  const uint32_t total = (uint32_t)(n_qtiles * a.BH);
+  hipLaunchKernelGGL((fwd16_kernel<TR, D, QB, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch32(const FwdArgs& a) {
+  const int n_qtiles = (a.N + 127) / 128;
+  const uint32_t total = (uint32_t)(n_qtiles * a.BH);
+  hipLaunchKernelGGL((fwd32_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
+                     a.N, n_qtiles, total, a.c);
+  return hipGetLastError();
+}
+
+template <class TR>
+static hipError_t dispatch16(const FwdArgs& a) {
+  if (a.d == 128) return a.causal ? launch16<TR, 128, 1, true>(a) : launch16<TR, 128, 1, false>(a);
+  return a.causal ? launch16<TR, 64, 2, true>(a) : launch16<TR, 64, 2, false>(a);
+}
+
+hipError_t launch_fwd(const FwdArgs& a) {
+  switch (a.dtype) {
+    case DT_BF16: return dispatch16<BF16>(a);
+    case DT_F16: return dispatch16<F16>(a);
+    default:
+      if (a.d == 128) return a.causal ? launch32<128, true>(a) : launch32<128, false>(a);
+      return a.causal ? launch32<64, true>(a) : launch32<64, false>(a);
+  }
+}
+
+}  // namespace fa

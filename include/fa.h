@@ -1,0 +1,111 @@
+/* fa.h - C ABI of the MI355X (gfx950) exact attention library, libfa_mi355x.so.
+ *
+ * The library computes exact scaled-dot-product attention
+ *
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,   LSE_i = ln sum_j exp(scale * q_i . k_j)
+ *
+ * in the tiled, fused, IO-aware way the pages describe: the N x N score and
+ * probability matrices are never written to device memory, the row
+ * normalisation is accumulated on the fly, only the per-row log-sum-exp is
+ * stored, and the backward pass recomputes the scores instead of loading them.
+ *   - Exactness (same result as the usual computation up to rounding):
+ *     "FlashAttention" lexicon, "Methodische Grundlagen", paragraph
+ *     "Exaktheit"; "FlashAttention" glossary, "Wo es verwechselt wird".
+ *   - Tiling, fusion, running normalisation, recomputation: "FlashAttention"
+ *     lexicon, "Methodische Grundlagen".
+ *   - Work split (one head over many compute units; rows split across
+ *     wavefronts; few non-matmul operations): "FlashAttention-2 (DE)",
+ *     "Technische Architektur und Funktionsprinzipien", items 1-3.
+ *   - The mask and the gradient formulas are not on the pages; causal means
+ *     key j is visible to query i iff j <= i (top-left aligned, equal query and
+ *     key lengths), and the gradient is the chain rule through the softmax.
+ *
+ * Conventions shared by every entry point
+ *   Layout     q, k, v, o, dout, dq, dk, dv: contiguous row-major [B, H, N, d]
+ *              arrays of the element type `dtype`.  lse: contiguous [B, H, N]
+ *              float32.  Head dimension d must be 64 or 128.
+ *   Memory     All data pointers are DEVICE pointers owned by the caller.  The
+ *              library allocates no device memory and keeps no pointer after a
+ *              call returns.  Every data pointer must be 16-byte aligned.
+ *   Streams    `stream` is a hipStream_t (NULL = the default stream).  Calls
+ *              only enqueue work on it and return; they never synchronise and
+ *              never copy to the host.  Concurrent calls on different streams
+ *              are safe (the library has no mutable global state).
+ *   Numerics   Matrix products multiply in the input precision and accumulate
+ *              in float32; outputs have the input type (LSE: float32).  The
+ *              probabilities that multiply V are rounded to the input type
+ *              (round to nearest even); the float32 path keeps them in float32.
+ *   Errors     Return FA_OK (0) or a positive fa_status.  Arguments are checked
+ *              before any device call; on an argument error nothing is
+ *              enqueued.  FA_ERR_HIP means the HIP runtime refused the launch
+ *              (no device, invalid stream, ...); hipGetLastError() then holds
+ *              the runtime's code.  The library never aborts or prints.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,     /* B, H or N < 1, or an index would not fit in 32 bits */
+  FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
+  FA_ERR_DTYPE = 4,     /* unknown dtype, or a dtype this entry point does not take */
+  FA_ERR_ALIGN = 5,     /* a data pointer is not 16-byte aligned */
+  FA_ERR_SCALE = 6,     /* scale is negative, NaN or infinite */
+  FA_ERR_WORKSPACE = 7, /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
+  FA_ERR_HIP = 8        /* the HIP runtime rejected a launch */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+/* Returns FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* fa_status_string(int status);
+
+/* Forward attention.
+ *   q, k, v  [B,H,N,d] inputs of type dtype (FA_F32, FA_F16 or FA_BF16).
+ *   o        [B,H,N,d] output, same type.  Fully overwritten.
+ *   lse      [B,H,N] float32 output: natural-log log-sum-exp of the scaled
+ *            scores of each row over its visible keys.  Fully overwritten.
+ *   scale    multiplier of q.k (normally 1/sqrt(d)); finite and >= 0.
+ *   causal   0: every key is visible; nonzero: key j visible to query i iff j <= i.
+ * The output buffers must not overlap the inputs. */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+           int dtype, void* stream);
+
+/* Bytes of device workspace fa_bwd needs for these sizes (4 * B * H * N:
+ * one float32 per query row, D_i = dO_i . O_i).  0 for invalid sizes. */
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
+
+/* Backward attention: gradients of O with respect to Q, K and V, given the
+ * upstream gradient dout = dL/dO and the forward's own outputs o and lse.
+ * The scores and probabilities are recomputed from q, k and lse.
+ *   q, k, v, o, dout  [B,H,N,d] inputs of type dtype (FA_F16 or FA_BF16).
+ *   lse               [B,H,N] float32 from fa_fwd on the same q, k, v.
+ *   dq, dk, dv        [B,H,N,d] outputs, same type.  Fully overwritten.
+ *   workspace         device scratch of at least fa_bwd_workspace_bytes(),
+ *                     owned by the caller, contents need not be initialised.
+ * dq/dk/dv are deterministic: repeated calls give bitwise-identical results. */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes,
+           int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+           int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,72 @@
+"""Helpers for the GPU parity tests: device upload of the seeded inputs, the
+library calls, and the error metrics with their bounds.
+
+Tolerances (the attention library's stated parity bounds):
+  float32 inputs:      O max-abs <= 1e-5, LSE max-abs <= 1e-5
+  bf16 / fp16 inputs:  O max-abs <= 1e-2 and mean-abs <= 1e-3, LSE max-abs <= 1e-3
+  backward:            dQ, dK, dV relative L2 (||gpu - oracle|| / ||oracle||) <= 1e-2
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+TOL = {
+    "f32": dict(o_max=1e-5, o_mean=1e-5, lse_max=1e-5),
+    "bf16": dict(o_max=1e-2, o_mean=1e-3, lse_max=1e-3),
+    "f16": dict(o_max=1e-2, o_mean=1e-3, lse_max=1e-3),
+}
+BWD_REL_L2 = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(store: np.ndarray, dtype: str):
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(store).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(np.ascontiguousarray(store))
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(store, dtype=np.float32))
+    return t.cuda()
+
+
+def lib():
+    import exact_io_aware_fa2_amd as fa
+    fa.load_library()
+    return fa
+
+
+def gpu_fwd(inputs: dict, dtype: str, causal: bool, scale: float):
+    """Upload q, k, v, run the library forward, return device tensors (q, k, v, o, lse)."""
+    import torch
+    fa = lib()
+    q, k, v = (to_device(inputs[n][1], dtype) for n in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, causal, scale)
+    torch.cuda.synchronize()
+    return q, k, v, o, lse
+
+
+def fwd_errors(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray):
+    do = np.abs(o_gpu.astype(np.float64) - o_ref)
+    dl = np.abs(lse_gpu.astype(np.float64) - lse_ref)
+    return dict(o_max=float(do.max()), o_mean=float(do.mean()), lse_max=float(dl.max()))
+
+
+def assert_fwd_ok(err: dict, dtype: str, label: str):
+    tol = TOL[dtype]
+    say(f"  {label}: O max {err['o_max']:.3e} mean {err['o_mean']:.3e}  LSE max {err['lse_max']:.3e}")
+    assert np.isfinite(err["o_max"]) and np.isfinite(err["lse_max"]), label
+    assert err["o_max"] <= tol["o_max"], (label, err)
+    assert err["o_mean"] <= tol["o_mean"], (label, err)
+    assert err["lse_max"] <= tol["lse_max"], (label, err)
+
+
+def rel_l2(x: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.linalg.norm(x.astype(np.float64) - ref) / np.linalg.norm(ref))

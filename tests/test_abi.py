@@ -1,0 +1,115 @@
+"""The C ABI on the host: the library loads, exports every function include/fa.h
+declares, and rejects bad arguments with status codes before touching a device.
+No compute call is made here (no GPU is needed)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE = 0, 1, 2, 3, 4
+FA_ERR_ALIGN, FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_HIP = 5, 6, 7, 8
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import exact_io_aware_fa2_amd as fa
+    if not os.path.exists(fa.LIB_PATH):
+        from exact_io_aware_fa2_amd._build import build_library
+        build_library()
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(
+        ["fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.fa_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        s = lib.fa_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.fa_status_string(99).decode() == "unknown status"
+
+
+# fake, 16-byte aligned addresses: never dereferenced, every call below fails validation
+P = [0x10000 * (i + 1) for i in range(12)]
+
+
+def fwd(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, N=64, d=64, scale=0.125,
+        causal=0, dtype=2):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+def bwd(lib, ws=P[10], wsb=1 << 20, B=1, H=2, N=64, d=64, scale=0.125, dtype=2, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], do=P[5], dq=P[6], dk=P[7], dv=P[8])
+    a.update(kw)
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                      ws, wsb, B, H, N, d, scale, 0, dtype, None)
+
+
+def test_fwd_argument_errors(lib):
+    assert fwd(lib, q=None) == FA_ERR_NULL
+    assert fwd(lib, lse=None) == FA_ERR_NULL
+    assert fwd(lib, B=0) == FA_ERR_SHAPE
+    assert fwd(lib, H=-1) == FA_ERR_SHAPE
+    assert fwd(lib, N=0) == FA_ERR_SHAPE
+    assert fwd(lib, N=(1 << 30) + 1) == FA_ERR_SHAPE
+    assert fwd(lib, B=1 << 20, H=1 << 12) == FA_ERR_SHAPE
+    assert fwd(lib, d=96) == FA_ERR_HEADDIM
+    assert fwd(lib, d=256) == FA_ERR_HEADDIM
+    assert fwd(lib, dtype=3) == FA_ERR_DTYPE
+    assert fwd(lib, dtype=-1) == FA_ERR_DTYPE
+    assert fwd(lib, v=P[2] + 8) == FA_ERR_ALIGN
+    assert fwd(lib, lse=P[4] + 4) == FA_ERR_ALIGN
+    assert fwd(lib, scale=float("nan")) == FA_ERR_SCALE
+    assert fwd(lib, scale=math.inf) == FA_ERR_SCALE
+    assert fwd(lib, scale=-0.5) == FA_ERR_SCALE
+
+
+def test_bwd_argument_errors(lib):
+    assert bwd(lib, do=None) == FA_ERR_NULL
+    assert bwd(lib, dv=None) == FA_ERR_NULL
+    assert bwd(lib, N=0) == FA_ERR_SHAPE
+    assert bwd(lib, d=32) == FA_ERR_HEADDIM
+    assert bwd(lib, dtype=0) == FA_ERR_DTYPE  # the backward takes 16-bit inputs only
+    assert bwd(lib, dq=P[6] + 2) == FA_ERR_ALIGN
+    assert bwd(lib, scale=float("-inf")) == FA_ERR_SCALE
+    assert bwd(lib, ws=None) == FA_ERR_WORKSPACE
+    assert bwd(lib, wsb=4 * 2 * 64 - 1) == FA_ERR_WORKSPACE
+    assert bwd(lib, ws=P[10] + 4) == FA_ERR_ALIGN
+
+
+def test_workspace_bytes(lib):
+    assert lib.fa_bwd_workspace_bytes(2, 3, 100, 64, 2) == 4 * 2 * 3 * 100
+    assert lib.fa_bwd_workspace_bytes(1, 1, 1, 128, 1) == 4
+    assert lib.fa_bwd_workspace_bytes(1, 1, 1, 96, 2) == 0
+    assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64, 2) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 8, 64, 0) == 0
+
+
+def test_binding_rejects_host_tensors_and_bad_shapes(lib):
+    torch = pytest.importorskip("torch")
+    import exact_io_aware_fa2_amd as fa
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q)
+    with pytest.raises(TypeError):
+        fa.dtype_code(torch.zeros(1, dtype=torch.int32))

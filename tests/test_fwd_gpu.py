@@ -1,0 +1,149 @@
+"""Forward parity on the GPU: the library's fa_fwd against the float64 oracle on
+the same seeded inputs.
+
+Small shapes (several tiles and ragged tails, every dtype, d, mask) are compared
+element by element on every output.  The full-size workloads run in the same
+launch configuration the benchmark times and are compared on sampled outputs
+(whole heads, or sampled rows of sampled heads) that the oracle computes one by
+one.
+"""
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from oracle import attention_fwd, attention_fwd_head
+from parity import TOL, assert_fwd_ok, fwd_errors, gpu_fwd, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(B, H, N, d, dtype, causal, seed, sigma=1.0):
+    inp = si.make_inputs(B, H, N, d, dtype, sigma, seed)
+    scale = 1.0 / np.sqrt(d)
+    say(f"fwd small B{B} H{H} N{N} d{d} {dtype} causal={causal} seed={seed}")
+    q, k, v, o, lse = gpu_fwd(inp, dtype, causal, scale)
+    o_ref, lse_ref = attention_fwd(inp["q"][0], inp["k"][0], inp["v"][0], scale, causal)
+    err = fwd_errors(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    assert_fwd_ok(err, dtype, f"N{N} d{d} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 255, 257, 1000])
+def test_small_shapes_and_tails(N, causal, d, dtype):
+    _small(1, 2, N, d, dtype, causal, seed=7000 + N + d)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_several_heads_and_batches(dtype):
+    _small(3, 5, 700, 128, dtype, True, seed=77)
+    _small(2, 3, 640, 64, dtype, False, seed=78)
+
+
+def test_c1_tiny_fp32_full():
+    w = si.WORKLOADS["C1"]
+    inp = si.make_workload_inputs(w)
+    say(f"C1 {w}")
+    q, k, v, o, lse = gpu_fwd(inp, w.dtype, w.causal, w.scale)
+    o_ref, lse_ref = attention_fwd(inp["q"][0], inp["k"][0], inp["v"][0], w.scale, w.causal)
+    err = fwd_errors(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    assert_fwd_ok(err, "f32", "C1")
+
+
+def _sampled(w, heads, rows_fn):
+    inp = si.make_workload_inputs(w)
+    say(f"{w.name} full size on GPU: {w}")
+    q, k, v, o, lse = gpu_fwd(inp, w.dtype, w.causal, w.scale)
+    og = o.float().cpu().numpy()
+    lg = lse.cpu().numpy()
+    errs = []
+    for (b, hh) in heads:
+        rows = rows_fn(w.N)
+        o_ref, l_ref = attention_fwd_head(inp["q"][0][b, hh], inp["k"][0][b, hh], inp["v"][0][b, hh],
+                                          w.scale, w.causal, rows=rows)
+        e = fwd_errors(og[b, hh][rows], lg[b, hh][rows], o_ref, l_ref)
+        say(f"  head ({b},{hh}) {len(rows)} rows: {e}")
+        errs.append(e)
+    agg = dict(o_max=max(e["o_max"] for e in errs), lse_max=max(e["lse_max"] for e in errs),
+               o_mean=float(np.mean([e["o_mean"] for e in errs])))
+    assert_fwd_ok(agg, w.dtype, w.name)
+    assert np.all(np.isfinite(lg)) and np.isfinite(og).all()
+
+
+def _rows_early_random_late(n, early=512, rand=256, late=64, seed=5):
+    rng = np.random.default_rng(seed)
+    r = set(range(min(n, early))) | set(rng.integers(0, n, rand).tolist()) | set(range(max(0, n - late), n))
+    return np.array(sorted(r))
+
+
+def test_c2_bf16_noncausal_sampled_heads():
+    w = si.WORKLOADS["C2"]
+    _sampled(w, [(0, 0), (1, 7), (2, 13), (3, 15)], lambda n: np.arange(n))
+
+
+def test_c3_bf16_causal_sampled():
+    w = si.WORKLOADS["C3"]
+    _sampled(w, [(0, 0), (1, 31), (0, 17)], _rows_early_random_late)
+
+
+def test_c3_d64_bf16_causal_sampled():
+    w = si.WORKLOADS["C3d64"]
+    _sampled(w, [(0, 3), (1, 30)], _rows_early_random_late)
+
+
+def test_c4_fp16_causal_long_context_sampled():
+    w = si.WORKLOADS["C4"]
+    _sampled(w, [(0, 0), (0, 31)], lambda n: _rows_early_random_late(n, early=256, rand=128, late=32))
+
+
+# ------------------------------------------------------------ properties on the GPU
+
+def test_values_all_one_give_exactly_one():
+    import torch
+    inp = si.make_inputs(1, 2, 333, 128, "bf16", 1.0, 11)
+    inp["v"] = si.round_to(np.ones((1, 2, 333, 128), np.float32), "bf16")
+    for causal in (False, True):
+        q, k, v, o, lse = gpu_fwd(inp, "bf16", causal, 1 / np.sqrt(128))
+        assert torch.all(o.float() == 1.0)
+
+
+def test_deterministic_bitwise():
+    import torch
+    inp = si.make_inputs(2, 4, 1500, 128, "bf16", 1.0, 12)
+    _, _, _, o1, l1 = gpu_fwd(inp, "bf16", True, 1 / np.sqrt(128))
+    _, _, _, o2, l2 = gpu_fwd(inp, "bf16", True, 1 / np.sqrt(128))
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_large_scores_stay_finite_and_pick_the_max_key():
+    """Queries scaled x30: weights collapse onto the best key; nothing overflows."""
+    d = 64
+    inp = si.make_inputs(1, 2, 300, d, "bf16", 1.0, 13)
+    qv = inp["q"][0] * 30
+    inp["q"] = si.round_to(qv, "bf16")
+    scale = 1 / np.sqrt(d)
+    _, _, _, o, lse = gpu_fwd(inp, "bf16", True, scale)
+    og = o.float().cpu().numpy()
+    assert np.isfinite(og).all() and np.isfinite(lse.cpu().numpy()).all()
+    o_ref, l_ref = attention_fwd(inp["q"][0], inp["k"][0], inp["v"][0], scale, True)
+    err = fwd_errors(og, lse.cpu().numpy(), o_ref, l_ref)
+    assert_fwd_ok(err, "bf16", "x30 queries")
+
+
+def test_key_shift_invariance_on_gpu():
+    """Adding one vector to every key leaves O unchanged (within rounding) and
+    shifts LSE_i by scale * q_i . c."""
+    d = 64
+    inp = si.make_inputs(1, 2, 400, d, "f32", 1.0, 14)
+    c = np.linspace(-1, 1, d).astype(np.float32)
+    inp2 = dict(inp)
+    inp2["k"] = si.round_to(inp["k"][0] + c, "f32")
+    scale = 1 / np.sqrt(d)
+    _, _, _, o1, l1 = gpu_fwd(inp, "f32", False, scale)
+    _, _, _, o2, l2 = gpu_fwd(inp2, "f32", False, scale)
+    np.testing.assert_allclose(o2.cpu().numpy(), o1.cpu().numpy(), atol=2e-5)
+    shift = scale * (inp["q"][0].astype(np.float64) @ c.astype(np.float64))
+    np.testing.assert_allclose(l2.cpu().numpy(), l1.cpu().numpy() + shift, atol=2e-4)
