@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the attention library on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: fa_fwd, then
+the three backward stages (fa_bwd_prep, fa_bwd_dkdv, fa_bwd_dq), all through
+the C ABI on the current HIP stream.  The default workload is the
+fwd+bwd configuration B=8 H=16 N=4096 d=64, bf16, causal, with Q, K, V, dO
+drawn as seeded N(0, 1) values (numpy PCG64, seed 1005) rounded to bf16.
+
+Prints ONE JSON line: throughput in TFLOP/s (forward 4*B*H*N^2*d plus
+backward 10*B*H*N^2*d, halved for causal), the dominant kernel against the
+dense bf16 MFMA peak, and the float64 CPU oracle timed on a bounded sample of
+the same workload.
+
+Modes
+  (default)             the benchmark above
+  --profile             a few steps and no CPU baseline, for rocprofv3 runs;
+                        also runs a plain 1 GiB device copy (the calibration
+                        kernel for FETCH_SIZE / WRITE_SIZE counters)
+  --ingest-pmc F W      turn two rocprofv3 --pmc csv files (FETCH_SIZE, then
+                        WRITE_SIZE) into profiles/traffic_<workload>.json
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s (bf16, causal/non-causal) and % of MFMA peak, 1 GPU"
+PEAK_MFMA_16BIT = 2516.6  # TFLOP/s, MI355X dense bf16/fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM = 8000.0  # GB/s
+COPY_BYTES = 1 << 30  # calibration copy: reads and writes 1 GiB
+
+KERNEL_SOURCES = {
+    "fwd": ["fa_fwd.hip", "fa_common.hpp"],
+    "prep": ["fa_bwd.hip", "fa_common.hpp"],
+    "dkdv": ["fa_bwd.hip", "fa_common.hpp"],
+    "dq": ["fa_bwd.hip", "fa_common.hpp"],
+}
+# substrings of the mangled kernel names, as rocprofv3 reports them
+KERNEL_SYMBOLS = {"fwd": "fwd16_kernel", "prep": "bwd_pre_kernel", "dkdv": "bwd_dkdv_kernel",
+                  "dq": "bwd_dq_kernel"}
+
+
+def src_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "exact_io_aware_fa2_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w) -> dict:
+    """Algorithmic work per launch of each kernel (FLOP, or bytes for prep).
+
+    fwd:  S = Q K^T and O = P V: 4*B*H*N^2*d FLOP (halved when causal).
+    dkdv: S, dP = dO V^T, dV = P^T dO, dK = dS^T Q: 8*B*H*N^2*d (halved).
+    dq:   dQ = dS K: 2*B*H*N^2*d (halved).  Its recomputation of S and dP is
+          not algorithmic work (the backward's five products are counted once,
+          in dkdv and here).
+    prep: reads O and dO, writes D: 2*B*H*N*d*s + 4*B*H*N bytes.
+    """
+    f = w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    s = {"bf16": 2, "f16": 2, "f32": 4}[w.dtype]
+    return {"fwd": 4 * f, "dkdv": 8 * f, "dq": 2 * f,
+            "prep": 2 * w.B * w.H * w.N * w.d * s + 4 * w.B * w.H * w.N}
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None if the
+    kernel's sources changed since the counters were taken."""
+    p = traffic_file(workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    k = t.get("kernels", {}).get(kernel)
+    if not k or k.get("src_sha") != src_hash(kernel):
+        return None
+    return k["bytes_per_launch"]
+
+
+def cpu_baseline(w, target_s: float):
+    """The float64 oracle, as it stands, on whole heads of the same workload."""
+    import numpy as np
+    import seeded_inputs as si
+    from oracle import attention_bwd_head, attention_fwd_head
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    inp = si.make_inputs(1, 1, w.N, w.d, w.dtype, w.sigma, w.seed, backward=True)
+    q, k, v, do = (inp[n][0][0, 0] for n in ("q", "k", "v", "do"))
+    heads, t_total = 0, 0.0
+    while t_total < target_s and heads < w.B * w.H:
+        t0 = time.perf_counter()
+        attention_fwd_head(q, k, v, w.scale, w.causal)
+        attention_bwd_head(q, k, v, do, w.scale, w.causal)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    flop = (4 + 10) * w.N * w.N * w.d * (0.5 if w.causal else 1.0) * heads
+    return {"value": round(flop / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads (N={w.N}, d={w.d}), float64 numpy forward "
+                      f"+ backward, {t_total:.1f} s; BLAS threads {threads}, host cpus {os.cpu_count()}"}
+
+
+def ingest_pmc(fetch_csv: str, write_csv: str, workload: str):
+    """Counter summary -> profiles/traffic_<workload>.json.
+
+    Each csv holds one counter per dispatch (KiB).  The plain copy kernel of
+    COPY_BYTES in the same run calibrates the counter: factor = true bytes /
+    counted bytes (read side from FETCH_SIZE, write side from WRITE_SIZE)."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = list(csv.DictReader(open(path)))
+        vals = {}
+        for r in rows:
+            if r.get("Counter_Name") != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def find(vals, sym):
+        ks = [k for k in vals if sym in k]
+        if not ks:
+            return None
+        xs = [x for k in ks for x in vals[k]]
+        return sum(xs) / len(xs)
+
+    copy_sym = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    if not copy_sym:
+        raise SystemExit("no copy kernel in the counter file; run bench.py --profile")
+    copy_f = max(sum(fetch[k]) / len(fetch[k]) for k in copy_sym) * 1024
+    copy_w = max(sum(write[k]) / len(write[k]) for k in write if k in copy_sym) * 1024
+    f_fac, w_fac = COPY_BYTES / copy_f, COPY_BYTES / copy_w
+    out = {"workload": workload, "copy_calibration": {"true_bytes": COPY_BYTES,
+                                                      "fetch_counted": copy_f,
+                                                      "write_counted": copy_w,
+                                                      "fetch_factor": f_fac, "write_factor": w_fac},
+           "kernels": {}}
+    for kern, sym in KERNEL_SYMBOLS.items():
+        fv, wv = find(fetch, sym), find(write, sym)
+        if fv is None or wv is None:
+            continue
+        out["kernels"][kern] = {"src_sha": src_hash(kern),
+                                "fetch_bytes": fv * 1024 * f_fac, "write_bytes": wv * 1024 * w_fac,
+                                "bytes_per_launch": fv * 1024 * f_fac + wv * 1024 * w_fac}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(traffic_file(workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C5")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    args = ap.parse_args()
+
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1 "
+                                   "(heads shard across GPUs with no communication: see DESIGN.md)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_io_aware_fa2_amd as fa
+    import seeded_inputs as si
+
+    fa.load_library()
+    w = si.WORKLOADS[args.workload]
+    if w.dtype == "f32":
+        raise SystemExit("the fwd+bwd step needs a 16-bit workload")
+    if args.profile:
+        args.steps, args.warmup = min(args.steps, 5), min(args.warmup, 2)
+    dev = torch.device("cuda:0")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+    inp = si.make_workload_inputs(w, backward=True)
+
+    def up(name):
+        a = inp[name][1]
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v, do = up("q"), up("k"), up("v"), up("do")
+    del inp
+    shape = (w.B, w.H, w.N, w.d)
+    o = torch.empty(shape, dtype=tdt, device=dev)
+    lse = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty(shape, dtype=tdt, device=dev) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(*shape, fa.dtype_code(q)), dtype=torch.uint8, device=dev)
+    names = ["fwd", "prep", "dkdv", "dq"]
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+        if evs is not None:
+            evs[1].record()
+        fa.fa_bwd_prep(o, do, ws)
+        if evs is not None:
+            evs[2].record()
+        fa.fa_bwd_dkdv(q, k, v, do, lse, ws, dk, dv, w.scale, w.causal)
+        if evs is not None:
+            evs[3].record()
+        fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, w.scale, w.causal)
+        if evs is not None:
+            evs[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    flop_step = w.fwd_flop() + w.bwd_flop()
+    value = flop_step / (ms_step * 1e-3) / 1e12
+    alg = algorithmic(w)
+    per_kernel = {}
+    for n in names:
+        if n == "prep":
+            per_kernel[n] = {"ms": round(kern_ms[n], 4), "GB/s": round(alg[n] / kern_ms[n] / 1e6, 1)}
+        else:
+            tf = alg[n] / (kern_ms[n] * 1e-3) / 1e12
+            per_kernel[n] = {"ms": round(kern_ms[n], 4), "TFLOP/s": round(tf, 1),
+                             "frac": round(tf / PEAK_MFMA_16BIT, 4)}
+    dom = max(["fwd", "dkdv", "dq"], key=lambda n: kern_ms[n])
+    achieved = alg[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_MFMA_16BIT,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_16BIT, 4),
+            "traffic": load_traffic(w.name, dom)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": f"synthetic: seeded N(0,{w.sigma:g}) Q, K, V, dO (numpy PCG64 seed {w.seed}) rounded to {w.dtype}",
+        "config": {"workload": f"{w.name}: fwd+bwd B={w.B} H={w.H} N={w.N} d={w.d} "
+                               f"{w.dtype} {'causal' if w.causal else 'non-causal'}",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "parallelism": "single GPU"},
+        "frac_of_peak": round(value / PEAK_MFMA_16BIT, 4),
+        "fwd_tflops": round(w.fwd_flop() / (kern_ms["fwd"] * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(w.bwd_flop() / ((kern_ms["prep"] + kern_ms["dkdv"] + kern_ms["dq"]) * 1e-3) / 1e12, 1),
+        "kernels": per_kernel,
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline and not args.profile:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if args.profile:
+        a = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

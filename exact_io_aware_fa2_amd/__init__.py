@@ -10,6 +10,7 @@ place of pointers):
     fa_fwd(q, k, v, o, lse, scale, causal)
     fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, causal)
     fa_bwd_workspace_bytes(B, H, N, d, dtype)
+    fa_bwd_prep(o, dout, workspace); fa_bwd_dkdv(...); fa_bwd_dq(...)  (fa_bwd's stages)
 Conveniences that allocate their outputs with torch:
     fwd(q, k, v, causal=False, scale=None) -> (o, lse)
     bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
@@ -60,6 +61,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fa_bwd.restype = i32
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                          i64, i64, i64, i64, f32, i32, i32, vp]
+    L.fa_bwd_prep.restype = i32
+    L.fa_bwd_prep.argtypes = [vp, vp, vp, sz, i64, i64, i64, i64, i32, vp]
+    L.fa_bwd_dkdv.restype = i32
+    L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
+    L.fa_bwd_dq.restype = i32
+    L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, i64, i64, i64, i64, f32, i32, i32, vp]
     _lib = L
     return L
 
@@ -144,6 +151,36 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale: float, causal: b
                     B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), _stream(q)))
 
 
+def fa_bwd_prep(o, dout, workspace) -> None:
+    """Stage 1 of the backward: workspace[i] = dout_i . o_i (float32)."""
+    L = load_library()
+    _check_tensors(o, dout, workspace)
+    B, H, N, d = _bhnd(o)
+    _check(L.fa_bwd_prep(_ptr(o), _ptr(dout), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), B, H, N, d,
+                         dtype_code(o), _stream(o)))
+
+
+def fa_bwd_dkdv(q, k, v, dout, lse, workspace, dk, dv, scale: float, causal: bool) -> None:
+    """Stage 2 of the backward: dK and dV (needs the prepared workspace)."""
+    L = load_library()
+    _check_tensors(q, k, v, dout, lse, workspace, dk, dv)
+    B, H, N, d = _bhnd(q)
+    _check(L.fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _ptr(dk), _ptr(dv),
+                         B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), _stream(q)))
+
+
+def fa_bwd_dq(q, k, v, dout, lse, workspace, dq, scale: float, causal: bool) -> None:
+    """Stage 3 of the backward: dQ (needs the prepared workspace)."""
+    L = load_library()
+    _check_tensors(q, k, v, dout, lse, workspace, dq)
+    B, H, N, d = _bhnd(q)
+    _check(L.fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(workspace),
+                       workspace.numel() * workspace.element_size(), _ptr(dq),
+                       B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), _stream(q)))
+
+
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
@@ -201,6 +238,7 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None):
 
 
 __all__ = [
-    "load_library", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fwd", "bwd", "attention",
+    "load_library", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_prep", "fa_bwd_dkdv",
+    "fa_bwd_dq", "fwd", "bwd", "attention",
     "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH",
 ]

@@ -84,33 +84,28 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dt
   return (size_t)(B * H * N) * sizeof(float);
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-           const void* dout, void* dq, void* dk, void* dv, void* workspace,
-           size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-           int causal, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the backward entry points; fills `a` on success.  `ptrs`
+// lists the data pointers the entry point takes (all required, 16-byte aligned).
+int bwd_common(fa::BwdArgs& a, const void* const* ptrs, int nptrs, const void* workspace,
+               size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+               int causal, int dtype, void* stream) {
+  for (int i = 0; i < nptrs; ++i)
+    if (!ptrs[i]) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
-  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return FA_ERR_ALIGN;
+  for (int i = 0; i < nptrs; ++i)
+    if (!aligned16(ptrs[i])) return FA_ERR_ALIGN;
   st = check_scale(scale);
   if (st != FA_OK) return st;
   if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d, dtype))
     return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
-
-  fa::BwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.dout = dout;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
+  a = fa::BwdArgs{};
   a.dvec = (float*)workspace;
   a.BH = (int)(B * H);
   a.N = (int)N;
@@ -120,7 +115,82 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   a.causal = causal != 0;
   a.dtype = dtype;
   a.stream = (hipStream_t)stream;
-  return fa::launch_bwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return FA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+           int causal, int dtype, void* stream) {
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  fa::BwdArgs a;
+  const int st = bwd_common(a, ptrs, 9, workspace, workspace_bytes, B, H, N, d, scale, causal,
+                            dtype, stream);
+  if (st != FA_OK) return st;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  return status_of(fa::launch_bwd(a));
+}
+
+int fa_bwd_prep(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
+                int64_t B, int64_t H, int64_t N, int64_t d, int dtype, void* stream) {
+  const void* ptrs[] = {o, dout};
+  fa::BwdArgs a;
+  const int st = bwd_common(a, ptrs, 2, workspace, workspace_bytes, B, H, N, d, 0.0f, 0, dtype,
+                            stream);
+  if (st != FA_OK) return st;
+  a.o = o;
+  a.dout = dout;
+  return status_of(fa::launch_bwd_stage(a, fa::BWD_PREP));
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                const void* workspace, size_t workspace_bytes, void* dk, void* dv, int64_t B,
+                int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
+                void* stream) {
+  const void* ptrs[] = {q, k, v, dout, lse, dk, dv};
+  fa::BwdArgs a;
+  const int st = bwd_common(a, ptrs, 7, workspace, workspace_bytes, B, H, N, d, scale, causal,
+                            dtype, stream);
+  if (st != FA_OK) return st;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dk = dk;
+  a.dv = dv;
+  return status_of(fa::launch_bwd_stage(a, fa::BWD_DKDV));
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+              const void* workspace, size_t workspace_bytes, void* dq, int64_t B, int64_t H,
+              int64_t N, int64_t d, float scale, int causal, int dtype, void* stream) {
+  const void* ptrs[] = {q, k, v, dout, lse, dq};
+  fa::BwdArgs a;
+  const int st = bwd_common(a, ptrs, 6, workspace, workspace_bytes, B, H, N, d, scale, causal,
+                            dtype, stream);
+  if (st != FA_OK) return st;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  return status_of(fa::launch_bwd_stage(a, fa::BWD_DQ));
 }
 
 }  // extern "C"

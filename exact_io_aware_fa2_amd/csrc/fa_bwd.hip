@@ -14,7 +14,7 @@
 //
 // Three launches on the caller's stream, none of which writes an N x N array:
 //   1. bwd_pre:  D_i = dO_i . O_i                       (HBM-bound, fp32 out)
-//   2. bwd_dkdv: one workgroup per (64-key... 128-key tile, batch*head); each
+//   2. bwd_dkdv: one workgroup per (128-key tile, batch*head); each
 //                wavefront owns 32 keys and keeps K, V, dK, dV in registers
 //                while the query tiles stream through LDS.
 //   3. bwd_dq:   one workgroup per (query tile, batch*head); each wavefront
@@ -436,41 +436,61 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
 // ------------------------------------------------------------------ launch
 
-template <class TR, int D, bool CAUSAL>
-static hipError_t launch_bwd_t(const BwdArgs& a) {
+template <class TR, int D>
+static hipError_t prep_t(const BwdArgs& a) {
   const int rows = a.BH * a.N;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<TR, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0,
                      a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dvec, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
 
+template <class TR, int D, bool CAUSAL>
+static hipError_t dkdv_t(const BwdArgs& a) {
   const int n_ktiles = (a.N + 127) / 128;
-  const uint32_t tk = (uint32_t)(n_ktiles * a.BH);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<TR, D, CAUSAL>), dim3(tk), dim3(256), 0, a.stream,
+  const uint32_t total = (uint32_t)(n_ktiles * a.BH);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<TR, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     a.N, n_ktiles, tk, a.c, a.scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                     a.N, n_ktiles, total, a.c, a.scale);
+  return hipGetLastError();
+}
 
+template <class TR, int D, bool CAUSAL>
+static hipError_t dq_t(const BwdArgs& a) {
   const int n_qtiles = (a.N + 127) / 128;
-  const uint32_t tq = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((bwd_dq_kernel<TR, D, CAUSAL>), dim3(tq), dim3(256), 0, a.stream,
+  const uint32_t total = (uint32_t)(n_qtiles * a.BH);
+  hipLaunchKernelGGL((bwd_dq_kernel<TR, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.N, n_qtiles, tq,
+                     (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.N, n_qtiles, total,
                      a.c, a.scale);
   return hipGetLastError();
 }
 
 template <class TR>
-static hipError_t dispatch_bwd(const BwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_bwd_t<TR, 128, true>(a) : launch_bwd_t<TR, 128, false>(a);
-  return a.causal ? launch_bwd_t<TR, 64, true>(a) : launch_bwd_t<TR, 64, false>(a);
+static hipError_t stage_t(const BwdArgs& a, int stage) {
+  const bool d128 = a.d == 128;
+  switch (stage) {
+    case BWD_PREP: return d128 ? prep_t<TR, 128>(a) : prep_t<TR, 64>(a);
+    case BWD_DKDV:
+      if (d128) return a.causal ? dkdv_t<TR, 128, true>(a) : dkdv_t<TR, 128, false>(a);
+      return a.causal ? dkdv_t<TR, 64, true>(a) : dkdv_t<TR, 64, false>(a);
+    default:
+      if (d128) return a.causal ? dq_t<TR, 128, true>(a) : dq_t<TR, 128, false>(a);
+      return a.causal ? dq_t<TR, 64, true>(a) : dq_t<TR, 64, false>(a);
+  }
+}
+
+hipError_t launch_bwd_stage(const BwdArgs& a, int stage) {
+  return a.dtype == DT_BF16 ? stage_t<BF16>(a, stage) : stage_t<F16>(a, stage);
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {
-  return a.dtype == DT_BF16 ? dispatch_bwd<BF16>(a) : dispatch_bwd<F16>(a);
+  for (int st : {BWD_PREP, BWD_DKDV, BWD_DQ}) {
+    const hipError_t e = launch_bwd_stage(a, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace fa

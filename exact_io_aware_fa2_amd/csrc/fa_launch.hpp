@@ -50,7 +50,10 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+enum BwdStage { BWD_PREP = 0, BWD_DKDV = 1, BWD_DQ = 2 };
+
 hipError_t launch_fwd(const FwdArgs& a);
-hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);                 // all three stages in order
+hipError_t launch_bwd_stage(const BwdArgs& a, int stage);  // one stage
 
 }  // namespace fa

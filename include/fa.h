@@ -104,6 +104,27 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
            int dtype, void* stream);
 
+/* The three stages fa_bwd runs, in this order, for callers that schedule or
+ * time them separately (same arguments, contract and errors as fa_bwd; each
+ * takes only the arrays it reads or writes).
+ *   fa_bwd_prep  workspace[b,h,i] = sum_c dout[b,h,i,c] * o[b,h,i,c]   (float32)
+ *   fa_bwd_dkdv  dk, dv from q, k, v, dout, lse and the prepared workspace
+ *   fa_bwd_dq    dq     from q, k, v, dout, lse and the prepared workspace
+ * fa_bwd_dkdv and fa_bwd_dq read the workspace written by fa_bwd_prep and are
+ * independent of each other. */
+int fa_bwd_prep(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
+                int64_t B, int64_t H, int64_t N, int64_t d, int dtype, void* stream);
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                const void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                int dtype, void* stream);
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+              const void* workspace, size_t workspace_bytes, void* dq,
+              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+              int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

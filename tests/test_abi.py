@@ -33,7 +33,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd"])
+        ["fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
+         "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -95,6 +96,23 @@ def test_bwd_argument_errors(lib):
     assert bwd(lib, ws=None) == FA_ERR_WORKSPACE
     assert bwd(lib, wsb=4 * 2 * 64 - 1) == FA_ERR_WORKSPACE
     assert bwd(lib, ws=P[10] + 4) == FA_ERR_ALIGN
+
+
+def test_stage_argument_errors(lib):
+    a = dict(B=1, H=2, N=64, d=64)
+    ws, wsb = P[10], 1 << 20
+    assert lib.fa_bwd_prep(None, P[1], ws, wsb, 1, 2, 64, 64, 2, None) == FA_ERR_NULL
+    assert lib.fa_bwd_prep(P[0], P[1], ws, 8, 1, 2, 64, 64, 2, None) == FA_ERR_WORKSPACE
+    assert lib.fa_bwd_prep(P[0], P[1], ws, wsb, 1, 2, 64, 80, 2, None) == FA_ERR_HEADDIM
+    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], ws, wsb, P[5], None,
+                           1, 2, 64, 64, 0.1, 1, 2, None) == FA_ERR_NULL
+    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], ws, wsb, P[5], P[6],
+                           1, 2, 64, 64, 0.1, 1, 0, None) == FA_ERR_DTYPE
+    assert lib.fa_bwd_dq(P[0], P[1], P[2], P[3], P[4], ws, wsb, P[5] + 2,
+                         1, 2, 64, 64, 0.1, 1, 2, None) == FA_ERR_ALIGN
+    assert lib.fa_bwd_dq(P[0], P[1], P[2], P[3], P[4], ws, wsb, P[5],
+                         1, 2, 64, 64, -1.0, 1, 2, None) == FA_ERR_SCALE
+    assert a
 
 
 def test_workspace_bytes(lib):

@@ -30,9 +30,13 @@ def _check_heads(inp, grads, heads, scale, causal, label):
         ref = attention_bwd_head(inp["q"][0][b, h], inp["k"][0][b, h], inp["v"][0][b, h],
                                  inp["do"][0][b, h], scale, causal)
         for name, g, r in zip(("dq", "dk", "dv"), grads, ref):
+            assert np.isfinite(g[b, h]).all(), (label, name, b, h)
+            if np.linalg.norm(r) == 0.0:
+                # e.g. one key: dQ = dK = 0 exactly; only rounding noise may remain
+                assert np.abs(g[b, h]).max() <= 1e-5, (label, name, b, h)
+                continue
             e = rel_l2(g[b, h], r)
             worst[name] = max(worst[name], e)
-            assert np.isfinite(g[b, h]).all(), (label, name, b, h)
     say(f"  {label}: rel-L2 {worst}")
     for name, e in worst.items():
         assert e <= BWD_REL_L2, (label, name, e)
