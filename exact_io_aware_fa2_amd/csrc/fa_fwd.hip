@@ -42,22 +42,38 @@ namespace fa {
 // denominator, so the result is unchanged mathematically.
 constexpr float kTau = 8.0f;
 
-template <class TR, int D, int QB, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Barrier for LDS hand-off between wavefronts: waits for this wave's LDS
+// accesses only, so global loads issued for the next tile stay in flight.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// 16-bit forward.  8 wavefronts, two per SIMD, each owning 32 query rows.
+// Every wavefront alternates two phases per key tile j:
+//   M-phase j: S_j = K_j Q^T  and  O += V_{j-1}^T P_{j-1}   (matrix cores)
+//   V-phase j: online softmax of S_j -> P_j                (vector ALU)
+// Waves 4..7 run one phase behind waves 0..3, so on every SIMD one wave is in
+// its M-phase while the other is in its V-phase, and the two kinds of work
+// overlap.  A workgroup barrier separates phases ("slots").  Staging is split
+// the same way: waves 0..3 load K tiles (issue in their M-phase, write LDS in
+// their V-phase), waves 4..7 load and transpose V tiles.
+template <class TR, int D, int BC, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                   float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c) {
-  constexpr int BC = 64;               // keys per tile
-  constexpr int NW = 4;                // wavefronts per workgroup
-  constexpr int BR = 32 * QB * NW;     // query rows per workgroup
-  constexpr int KCH = D / 8;           // 16-byte chunks per row
-  constexpr int SWZ = (KCH < 16 ? KCH : 16) - 1;
-  constexpr int KLOADS = BC * KCH / 256;            // 16-byte K chunks per thread
-  constexpr int VUNITS = (BC / 4) * KCH;            // 4-key x 8-column V units
-  constexpr int VLOADS = (VUNITS + 255) / 256;      // units per thread
-  constexpr int NKB = BC / 32;                      // 32-key blocks per tile
-  constexpr int NDB = D / 32;                       // 32-column blocks of the output
-  constexpr int NKS = D / 16;                       // MFMA k-steps over d
+  constexpr int NW = 8;                     // wavefronts per workgroup
+  constexpr int BR = 32 * NW;               // query rows per workgroup
+  constexpr int KCH = D / 8;                // 16-byte chunks per row
+  constexpr int NKB = BC / 32;              // 32-key blocks per tile
+  constexpr int NDB = D / 32;               // 32-column blocks of the output
+  constexpr int NKS = D / 16;               // MFMA k-steps over d
+  constexpr int KLD = BC * KCH / 256;       // K chunks per staging thread (waves 0..3)
+  constexpr int VUNITS = (BC / 4) * KCH;    // 4-key x 8-column V units
+  constexpr int VLD = VUNITS / 256;         // V units per staging thread (waves 4..7)
+  static_assert(KLD * 256 == BC * KCH && VLD * 256 == VUNITS, "tile not divisible");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * D];
@@ -65,6 +81,8 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int grp = w >> 2;          // 0: leading group, 1: trailing group
+  const int st = tid & 255;        // staging index within the group
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -73,239 +91,189 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   int qt = lid % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest tiles first
   const int q0 = qt * BR;
-
   const size_t head_off = (size_t)bh * N * D;
-  const uint16_t* Qh = Q + head_off;
   const uint16_t* Kh = K + head_off;
   const uint16_t* Vh = V + head_off;
+  const int qw = q0 + 32 * w;      // first query row of this wavefront
+  const int qrow = qw + l32;
 
-  const int qw = q0 + w * 32 * QB;  // first query row of this wavefront
+  // Q rows as the B operand of S^T = K Q^T, loaded once
+  u32x4_t qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = qrow < N ? *(const u32x4_t*)(Q + head_off + (size_t)qrow * D + 16 * ks + 8 * h)
+                      : u32x4_t{0, 0, 0, 0};
 
-  // ---- Q fragments (B operand of S^T = K Q^T), loaded once.
-  u32x4_t qf[QB][NKS];
+  f32x16_t acc_o[NDB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw + 32 * qb + l32;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (row < N)
-        qf[qb][ks] = *(const u32x4_t*)(Qh + (size_t)row * D + 16 * ks + 8 * h);
-      else
-        qf[qb][ks] = u32x4_t{0, 0, 0, 0};
-    }
-  }
-
-  // ---- running state: one query row per lane and query block
-  f32x16_t acc_o[NDB][QB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) acc_o[db][qb] = zero16();
-  float m_run[QB], l_run[QB], lt_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.0f;
-    lt_run[qb] = 0.0f;
-  }
+  for (int db = 0; db < NDB; ++db) acc_o[db] = zero16();
+  f32x16_t s[NKB];
+  uint32_t pt[NKB][8];
+  float m_run = -INFINITY, l_run = 0.0f, lt_run = 0.0f;
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
-  const int wave_last = CAUSAL ? min(N, qw + 32 * QB) : N;  // exclusive key bound for this wave
-  const int wave_tiles = (wave_last + BC - 1) / BC;
+  const int wave_end = CAUSAL ? min(N, qw + 32) : N;
+  const int wave_tiles = (wave_end + BC - 1) / BC;
 
-  // ---- staging registers for the next tile
-  u32x4_t kreg[KLOADS];
-  u32x4_t vreg[VLOADS][4];
-
-  auto load_tile = [&](int j0) {
+  u32x4_t kreg[KLD];
+  u32x4_t vreg[VLD][4];
+  auto load_k = [&](int j0) {
 #pragma unroll
-    for (int r = 0; r < KLOADS; ++r) {
-      const int cidx = tid + 256 * r;
-      const int row = cidx / KCH, col = cidx % KCH;
-      if (j0 + row < N)
-        kreg[r] = *(const u32x4_t*)(Kh + (size_t)(j0 + row) * D + col * 8);
-      else
-        kreg[r] = u32x4_t{0, 0, 0, 0};
+    for (int r = 0; r < KLD; ++r) {
+      const int ci = st + 256 * r;
+      const int row = ci / KCH, col = ci % KCH;
+      kreg[r] = j0 + row < N ? *(const u32x4_t*)(Kh + (size_t)(j0 + row) * D + col * 8)
+                             : u32x4_t{0, 0, 0, 0};
     }
+  };
+  auto store_k = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < VLOADS; ++r) {
-      const int u = tid + 256 * r;
-      const int kg = u / KCH, dc = u % KCH;
+    for (int r = 0; r < KLD; ++r) {
+      const int ci = st + 256 * r;
+      *(u32x4_t*)(&sK[buf][swz_off<D>(ci / KCH, ci % KCH)]) = kreg[r];
+    }
+  };
+  auto load_v = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < VLD; ++r) {
+      const int u = st + 256 * r;
+      const int g = u / KCH, ch = u % KCH;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int key = j0 + 4 * kg + rr;
-        if (u < VUNITS && key < N)
-          vreg[r][rr] = *(const u32x4_t*)(Vh + (size_t)key * D + dc * 8);
-        else
-          vreg[r][rr] = u32x4_t{0, 0, 0, 0};
+        const int key = j0 + 4 * g + rr;
+        vreg[r][rr] = key < N ? *(const u32x4_t*)(Vh + (size_t)key * D + ch * 8)
+                              : u32x4_t{0, 0, 0, 0};
       }
     }
   };
-
-  auto store_tile = [&](int buf) {
+  auto store_v = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < KLOADS; ++r) {
-      const int cidx = tid + 256 * r;
-      const int row = cidx / KCH, col = cidx % KCH;
-      *(u32x4_t*)(&sK[buf][row * D + ((col ^ (row & SWZ)) * 8)]) = kreg[r];
-    }
-#pragma unroll
-    for (int r = 0; r < VLOADS; ++r) {
-      const int u = tid + 256 * r;
-      if (u < VUNITS) {
-        const int kg = u / KCH, dc = u % KCH;
-        // 4 rows x 8 columns -> 8 units of (4 keys at one column)
-        uint32_t outw[16];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t a = vreg[r][0][p], b = vreg[r][1][p], cc = vreg[r][2][p], d = vreg[r][3][p];
-          // column 2p: low halves; column 2p+1: high halves
-          outw[4 * p + 0] = pair16(lo16(a), lo16(b));
-          outw[4 * p + 1] = pair16(lo16(cc), lo16(d));
-          outw[4 * p + 2] = pair16(hi16(a), hi16(b));
-          outw[4 * p + 3] = pair16(hi16(cc), hi16(d));
-        }
-        uint16_t* dst = &sV[buf][(kg * D + dc * 8) * 4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          *(u32x4_t*)(dst + 8 * x) =
-              u32x4_t{outw[4 * x + 0], outw[4 * x + 1], outw[4 * x + 2], outw[4 * x + 3]};
-      }
+    for (int r = 0; r < VLD; ++r) {
+      const int u = st + 256 * r;
+      store_interleaved(&sV[buf][il_off<D>(u / KCH, 8 * (u % KCH))], vreg[r]);
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // prologue: K_0 staged by the leading group, V_0 requested by the trailing one
+  if (grp == 0) {
+    load_k(0);
+    store_k(0);
+  } else {
+    load_v(0);
+  }
+  lds_barrier();
 
-  for (int jt = 0; jt < n_tiles; ++jt) {
-    const int buf = jt & 1;
-    const int j0 = jt * BC;
-    const bool has_next = jt + 1 < n_tiles;
-    if (has_next) load_tile(j0 + BC);
-
-    if (jt < wave_tiles) {
-      // ---- S^T = K Q^T for this tile
-      f32x16_t s[NKB][QB];
+  const int n_slots = 2 * n_tiles + 2;
+  for (int slot = 0; slot < n_slots; ++slot) {
+    const int ph = slot - grp;  // this wave's own phase counter
+    if (ph >= 0 && (ph & 1) == 0) {
+      // ---------------- M-phase j
+      const int j = ph >> 1;
+      if (grp == 0 && j + 1 < n_tiles) load_k((j + 1) * BC);
+      if (grp == 1 && j + 1 < n_tiles) load_v((j + 1) * BC);
+      if (j < n_tiles && j < wave_tiles) {
+        const uint16_t* kb_ = sK[j & 1];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = zero16();
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int row = 32 * kb + l32;
-          const int ch = 2 * ks + h;
-          const u32x4_t kf = *(const u32x4_t*)(&sK[buf][row * D + ((ch ^ (row & SWZ)) * 8)]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = TR::mfma(kf, qf[qb][ks], s[kb][qb]);
-        }
+          for (int kb = 0; kb < NKB; ++kb) {
+            const u32x4_t kf = *(const u32x4_t*)(&kb_[swz_off<D>(32 * kb + l32, 2 * ks + h)]);
+            s[kb] = TR::mfma(kf, qf[ks], s[kb]);
+          }
       }
-
-      // ---- mask (only tiles that cross the diagonal or the sequence end)
-      const bool need_mask = (CAUSAL && (j0 + BC - 1 > qw)) || (j0 + BC > N);
-      if (need_mask) {
+      if (j >= 1 && j - 1 < wave_tiles) {
+        const uint16_t* vb_ = sV[(j - 1) & 1];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int qrow = qw + 32 * qb + l32;
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const u32x4_t pf = u32x4_t{pt[kb][4 * t + 0], pt[kb][4 * t + 1], pt[kb][4 * t + 2],
+                                       pt[kb][4 * t + 3]};
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const int col = 32 * db + l32;
+              const u32x2_t va = *(const u32x2_t*)(&vb_[il_off<D>(8 * kb + 4 * t + h, col)]);
+              const u32x2_t vb = *(const u32x2_t*)(&vb_[il_off<D>(8 * kb + 4 * t + 2 + h, col)]);
+              acc_o[db] = TR::mfma(u32x4_t{va[0], va[1], vb[0], vb[1]}, pf, acc_o[db]);
+            }
+          }
+      }
+    } else if (ph >= 0) {
+      // ---------------- V-phase j
+      const int j = (ph - 1) >> 1;
+      if (grp == 0 && j + 1 < n_tiles) store_k((j + 1) & 1);
+      if (j < wave_tiles) {
+        const int j0 = j * BC;
+        if ((CAUSAL && j0 + BC - 1 > qw) || j0 + BC > N) {
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = j0 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
-              const bool bad = (key >= N) || (CAUSAL && key > qrow);
-              if (bad) s[kb][qb][r] = -INFINITY;
+              if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
             }
         }
-      }
-
-      // ---- online softmax (exp2 domain), per query row = per lane
-      uint32_t pt[NKB][QB][8];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         mx = fmaxf(mx, swap_halves(mx));
         const float mnew = mx * c;
-        if (mnew > m_run[qb] + kTau) {
-          const float alpha = fast_exp2(m_run[qb] - mnew);
-          m_run[qb] = mnew;
-          l_run[qb] *= alpha;
-          lt_run[qb] *= alpha;
+        if (mnew > m_run + kTau) {
+          const float alpha = fast_exp2(m_run - mnew);
+          m_run = mnew;
+          l_run *= alpha;
+          lt_run *= alpha;
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc_o[db][qb][r] *= alpha;
+            for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
         }
-        const float mneg = -m_run[qb];
+        const float mneg = -m_run;
         float lsum = 0.0f, ltsum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(fmaf(s[kb][qb][r], c, mneg));
-            const float p1 = fast_exp2(fmaf(s[kb][qb][r + 1], c, mneg));
-            lsum += p0;
-            lsum += p1;
+            const float p0 = fast_exp2(fmaf(s[kb][r], c, mneg));
+            const float p1 = fast_exp2(fmaf(s[kb][r + 1], c, mneg));
+            lsum += p0 + p1;
             const uint32_t pk = TR::pack2(p0, p1);
             ltsum = TR::sum2(pk, ltsum);
-            pt[kb][qb][r / 2] = pk;
+            pt[kb][r / 2] = pk;
           }
-        l_run[qb] += lsum;
-        lt_run[qb] += ltsum;
-      }
-
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int col = 32 * db + l32;
-            const u32x2_t va = *(const u32x2_t*)(&sV[buf][((8 * kb + 4 * t + h) * D + col) * 4]);
-            const u32x2_t vb = *(const u32x2_t*)(&sV[buf][((8 * kb + 4 * t + 2 + h) * D + col) * 4]);
-            const u32x4_t vf = u32x4_t{va[0], va[1], vb[0], vb[1]};
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-              const u32x4_t pf = u32x4_t{pt[kb][qb][4 * t + 0], pt[kb][qb][4 * t + 1],
-                                         pt[kb][qb][4 * t + 2], pt[kb][qb][4 * t + 3]};
-              acc_o[db][qb] = TR::mfma(vf, pf, acc_o[db][qb]);
-            }
-          }
-        }
+        l_run += lsum;
+        lt_run += ltsum;
       }
     }
-
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    // trailing group: write V_{j+1} during its V-phase j (slot 2j+2); V_0 at slot 0
+    if (grp == 1 && (slot & 1) == 0) {
+      const int jn = slot >> 1;  // tile being written
+      if (jn < n_tiles) store_v(jn & 1);
+    }
+    lds_barrier();
   }
 
-  // ---- epilogue: normalise once, store O and LSE
+  // epilogue: normalise once, store O and LSE
+  const float lt = lt_run + swap_halves(lt_run);
+  const float l = l_run + swap_halves(l_run);
+  const float inv = 1.0f / lt;
+  if (qrow < N) {
+    uint16_t* orow = O + head_off + (size_t)qrow * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw + 32 * qb + l32;
-    const float lt = lt_run[qb] + swap_halves(lt_run[qb]);
-    const float l = l_run[qb] + swap_halves(l_run[qb]);
-    const float inv = 1.0f / lt;
-    if (row < N) {
-      uint16_t* orow = O + head_off + (size_t)row * D;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = 32 * db + 8 * g + 4 * h;
-          const uint32_t w0 = TR::pack2(acc_o[db][qb][4 * g + 0] * inv, acc_o[db][qb][4 * g + 1] * inv);
-          const uint32_t w1 = TR::pack2(acc_o[db][qb][4 * g + 2] * inv, acc_o[db][qb][4 * g + 3] * inv);
-          *(u32x2_t*)(orow + col) = u32x2_t{w0, w1};
-        }
-      if (h == 0) LSE[(size_t)bh * N + row] = (m_run[qb] + __log2f(l)) * kLn2;
-    }
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * h;
+        const uint32_t w0 = TR::pack2(acc_o[db][4 * g + 0] * inv, acc_o[db][4 * g + 1] * inv);
+        const uint32_t w1 = TR::pack2(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv);
+        *(u32x2_t*)(orow + col) = u32x2_t{w0, w1};
+      }
+    if (h == 0) LSE[(size_t)bh * N + qrow] = (m_run + __log2f(l)) * kLn2;
   }
 }
 
@@ -417,12 +385,12 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float* __restrict__ Q,
 
 // ------------------------------------------------------------------ launch
 
-template <class TR, int D, int QB, bool CAUSAL>
+template <class TR, int D, int BC, bool CAUSAL>
 static hipError_t launch16(const FwdArgs& a) {
-  constexpr int BR = 32 * QB * 4;
+  constexpr int BR = 256;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((fwd16_kernel<TR, D, QB, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((fwd16_kernel<TR, D, BC, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c);
   return hipGetLastError();
@@ -440,8 +408,8 @@ static hipError_t launch32(const FwdArgs& a) {
 
 template <class TR>
 static hipError_t dispatch16(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch16<TR, 128, 1, true>(a) : launch16<TR, 128, 1, false>(a);
-  return a.causal ? launch16<TR, 64, 2, true>(a) : launch16<TR, 64, 2, false>(a);
+  if (a.d == 128) return a.causal ? launch16<TR, 128, 64, true>(a) : launch16<TR, 128, 64, false>(a);
+  return a.causal ? launch16<TR, 64, 128, true>(a) : launch16<TR, 64, 128, false>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
