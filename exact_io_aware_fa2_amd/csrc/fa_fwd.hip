@@ -59,6 +59,14 @@ __device__ inline void lds_barrier() {
 // overlap.  A workgroup barrier separates phases ("slots").  Staging is split
 // the same way: waves 0..3 load K tiles (issue in their M-phase, write LDS in
 // their V-phase), waves 4..7 load and transpose V tiles.
+//
+// LDS layouts (per buffer):
+//   K: row-major, rows padded to D + 8 elements, so 16 consecutive rows read
+//      at one 16-byte column fall in distinct banks and every fragment address
+//      is a fixed offset from one base.
+//   V: [key/16][h][d][8]: the 16-byte unit (s, h, c) holds column c of keys
+//      16s + 4h + {0,1,2,3} and 16s + 8 + 4h + {0,1,2,3}, exactly the eight
+//      values lane (c % 32, h) needs for one O^T += V^T P^T instruction.
 template <class TR, int D, int BC, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -67,15 +75,16 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   constexpr int NW = 8;                     // wavefronts per workgroup
   constexpr int BR = 32 * NW;               // query rows per workgroup
   constexpr int KCH = D / 8;                // 16-byte chunks per row
+  constexpr int KS = D + 8;                 // padded K row (elements)
   constexpr int NKB = BC / 32;              // 32-key blocks per tile
   constexpr int NDB = D / 32;               // 32-column blocks of the output
   constexpr int NKS = D / 16;               // MFMA k-steps over d
   constexpr int KLD = BC * KCH / 256;       // K chunks per staging thread (waves 0..3)
-  constexpr int VUNITS = (BC / 4) * KCH;    // 4-key x 8-column V units
-  constexpr int VLD = VUNITS / 256;         // V units per staging thread (waves 4..7)
-  static_assert(KLD * 256 == BC * KCH && VLD * 256 == VUNITS, "tile not divisible");
+  constexpr int VU = (BC / 16) * 2 * (D / 4);  // V staging units (8 keys x 4 columns)
+  static_assert(KLD * 256 == BC * KCH && VU == 256, "tile shape must give one unit per thread");
+  static_assert(KLD == 4, "staging registers are shared by the K and V roles");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KS];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * D];
 
   const int tid = threadIdx.x;
@@ -97,12 +106,14 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   const int qw = q0 + 32 * w;      // first query row of this wavefront
   const int qrow = qw + l32;
 
-  // Q rows as the B operand of S^T = K Q^T, loaded once
+  // Q rows as the B operand of S^T = K Q^T, loaded once.  Rows past the end
+  // read the last row instead (their results are never stored).
   u32x4_t qf[NKS];
+  {
+    const uint16_t* qp = Q + head_off + (size_t)min(qrow, N - 1) * D + 8 * h;
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    qf[ks] = qrow < N ? *(const u32x4_t*)(Q + head_off + (size_t)qrow * D + 16 * ks + 8 * h)
-                      : u32x4_t{0, 0, 0, 0};
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const u32x4_t*)(qp + 16 * ks);
+  }
 
   f32x16_t acc_o[NDB];
 #pragma unroll
@@ -116,42 +127,51 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   const int wave_end = CAUSAL ? min(N, qw + 32) : N;
   const int wave_tiles = (wave_end + BC - 1) / BC;
 
-  u32x4_t kreg[KLD];
-  u32x4_t vreg[VLD][4];
+  // Staging registers: 4 x 16 bytes per thread in both roles.  Rows past the
+  // end of the sequence are replaced by the last row (finite values whose
+  // scores are masked to -inf, so they contribute exactly zero).
+  u32x4_t stg[4];
+  // K role: chunk ci = st + 256 r -> row ci / KCH, 16-byte column ci % KCH
   auto load_k = [&](int j0) {
 #pragma unroll
-    for (int r = 0; r < KLD; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const int ci = st + 256 * r;
-      const int row = ci / KCH, col = ci % KCH;
-      kreg[r] = j0 + row < N ? *(const u32x4_t*)(Kh + (size_t)(j0 + row) * D + col * 8)
-                             : u32x4_t{0, 0, 0, 0};
+      const int row = min(j0 + ci / KCH, N - 1);
+      stg[r] = *(const u32x4_t*)(Kh + (size_t)row * D + (ci % KCH) * 8);
     }
   };
   auto store_k = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < KLD; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const int ci = st + 256 * r;
-      *(u32x4_t*)(&sK[buf][swz_off<D>(ci / KCH, ci % KCH)]) = kreg[r];
+      *(u32x4_t*)(&sK[buf][(ci / KCH) * KS + (ci % KCH) * 8]) = stg[r];
     }
   };
+  // V role: unit st -> (16-key step vs, half vh, 4-column chunk vc); 8 rows x 8 bytes
+  const int vc = st % (D / 4);
+  const int vh = (st / (D / 4)) & 1;
+  const int vs = st / (D / 2);
   auto load_v = [&](int j0) {
 #pragma unroll
-    for (int r = 0; r < VLD; ++r) {
-      const int u = st + 256 * r;
-      const int g = u / KCH, ch = u % KCH;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = j0 + 4 * g + rr;
-        vreg[r][rr] = key < N ? *(const u32x4_t*)(Vh + (size_t)key * D + ch * 8)
-                              : u32x4_t{0, 0, 0, 0};
-      }
+    for (int k = 0; k < 8; ++k) {
+      const int key = min(j0 + 16 * vs + 8 * (k / 4) + 4 * vh + (k % 4), N - 1);
+      const u32x2_t x = *(const u32x2_t*)(Vh + (size_t)key * D + 4 * vc);
+      stg[k / 2][2 * (k % 2) + 0] = x[0];
+      stg[k / 2][2 * (k % 2) + 1] = x[1];
     }
   };
   auto store_v = [&](int buf) {
+    // row k holds columns (4vc, 4vc+1) in dword 2(k%2) of stg[k/2] and (4vc+2, 4vc+3) in the next
+    uint16_t* dst = &sV[buf][((2 * vs + vh) * D + 4 * vc) * 8];
 #pragma unroll
-    for (int r = 0; r < VLD; ++r) {
-      const int u = st + 256 * r;
-      store_interleaved(&sV[buf][il_off<D>(u / KCH, 8 * (u % KCH))], vreg[r]);
+    for (int cc = 0; cc < 4; ++cc) {
+      uint32_t o[4];
+#pragma unroll
+      for (int kp = 0; kp < 4; ++kp) {
+        const uint32_t a = stg[kp][(cc / 2)], b = stg[kp][2 + (cc / 2)];  // rows 2kp, 2kp+1
+        o[kp] = (cc & 1) ? pair16(hi16(a), hi16(b)) : pair16(lo16(a), lo16(b));
+      }
+      *(u32x4_t*)(dst + 8 * cc) = u32x4_t{o[0], o[1], o[2], o[3]};
     }
   };
 
@@ -164,28 +184,33 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   }
   lds_barrier();
 
+  const int kfrag = l32 * KS + 8 * h;  // element offset of this lane's K fragment
+  const int vfrag = (h * D + l32) * 8;  // element offset of this lane's V fragment
   const int n_slots = 2 * n_tiles + 2;
   for (int slot = 0; slot < n_slots; ++slot) {
     const int ph = slot - grp;  // this wave's own phase counter
     if (ph >= 0 && (ph & 1) == 0) {
       // ---------------- M-phase j
+      __builtin_amdgcn_s_setprio(1);
       const int j = ph >> 1;
-      if (grp == 0 && j + 1 < n_tiles) load_k((j + 1) * BC);
-      if (grp == 1 && j + 1 < n_tiles) load_v((j + 1) * BC);
+      if (j + 1 < n_tiles) {
+        if (grp == 0) load_k((j + 1) * BC);
+        else load_v((j + 1) * BC);
+      }
       if (j < n_tiles && j < wave_tiles) {
-        const uint16_t* kb_ = sK[j & 1];
+        const uint16_t* kb_ = sK[j & 1] + kfrag;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
-            const u32x4_t kf = *(const u32x4_t*)(&kb_[swz_off<D>(32 * kb + l32, 2 * ks + h)]);
+            const u32x4_t kf = *(const u32x4_t*)(kb_ + 32 * kb * KS + 16 * ks);
             s[kb] = TR::mfma(kf, qf[ks], s[kb]);
           }
       }
       if (j >= 1 && j - 1 < wave_tiles) {
-        const uint16_t* vb_ = sV[(j - 1) & 1];
+        const uint16_t* vb_ = sV[(j - 1) & 1] + vfrag;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -194,13 +219,12 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                                        pt[kb][4 * t + 3]};
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-              const int col = 32 * db + l32;
-              const u32x2_t va = *(const u32x2_t*)(&vb_[il_off<D>(8 * kb + 4 * t + h, col)]);
-              const u32x2_t vb = *(const u32x2_t*)(&vb_[il_off<D>(8 * kb + 4 * t + 2 + h, col)]);
-              acc_o[db] = TR::mfma(u32x4_t{va[0], va[1], vb[0], vb[1]}, pf, acc_o[db]);
+              const u32x4_t vf = *(const u32x4_t*)(vb_ + ((2 * (2 * kb + t)) * D + 32 * db) * 8);
+              acc_o[db] = TR::mfma(vf, pf, acc_o[db]);
             }
           }
       }
+      __builtin_amdgcn_s_setprio(0);
     } else if (ph >= 0) {
       // ---------------- V-phase j
       const int j = (ph - 1) >> 1;
