@@ -8,7 +8,9 @@
 
 namespace {
 
-constexpr int64_t kMaxN = int64_t(1) << 30;
+// One head of one tensor (N x d elements of up to 4 bytes) must stay below
+// 2^31 bytes: kernels address within a head with 32-bit byte offsets.
+constexpr int64_t kMaxN = int64_t(1) << 22;
 constexpr int64_t kMaxWorkgroups = (int64_t(1) << 24) - 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -108,6 +108,24 @@ __device__ inline uint32_t xcd_remap(uint32_t pid, uint32_t total) {
   return x * base + (x < rem ? x : rem) + slot;
 }
 
+// Raw buffer access: 32-bit byte offsets from a per-head base, with the
+// hardware range check (an access at or past `bytes` reads zeros).  The whole
+// offset goes in the VGPR operand so the range check covers it.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline u32x4_t buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ inline u32x2_t buf_load8(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
+// Wait until every vector-memory load issued so far has returned.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // The two 16-bit halves of a dword.
 __device__ inline uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 __device__ inline uint32_t hi16(uint32_t x) { return x >> 16; }

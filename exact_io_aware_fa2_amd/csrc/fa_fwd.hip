@@ -101,18 +101,21 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest tiles first
   const int q0 = qt * BR;
   const size_t head_off = (size_t)bh * N * D;
-  const uint16_t* Kh = K + head_off;
-  const uint16_t* Vh = V + head_off;
+  constexpr uint32_t RB = D * 2;   // bytes per row
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
+  const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
   const int qw = q0 + 32 * w;      // first query row of this wavefront
   const int qrow = qw + l32;
 
-  // Q rows as the B operand of S^T = K Q^T, loaded once.  Rows past the end
-  // read the last row instead (their results are never stored).
+  // Q rows as the B operand of S^T = K Q^T, loaded once (rows past the end
+  // read zeros; their results are never stored).
   u32x4_t qf[NKS];
   {
-    const uint16_t* qp = Q + head_off + (size_t)min(qrow, N - 1) * D + 8 * h;
+    const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
+    const uint32_t qoff = (uint32_t)qrow * RB + 16 * h;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const u32x4_t*)(qp + 16 * ks);
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(qres, qoff + 32 * ks);
   }
 
   f32x16_t acc_o[NDB];
@@ -128,17 +131,14 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   const int wave_tiles = (wave_end + BC - 1) / BC;
 
   // Staging registers: 4 x 16 bytes per thread in both roles.  Rows past the
-  // end of the sequence are replaced by the last row (finite values whose
-  // scores are masked to -inf, so they contribute exactly zero).
+  // end of the sequence read zeros (their scores are masked to -inf, so they
+  // contribute exactly zero).
   u32x4_t stg[4];
   // K role: chunk ci = st + 256 r -> row ci / KCH, 16-byte column ci % KCH
+  const uint32_t koff = (uint32_t)(st / KCH) * RB + (st % KCH) * 16;
   auto load_k = [&](int j0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int ci = st + 256 * r;
-      const int row = min(j0 + ci / KCH, N - 1);
-      stg[r] = *(const u32x4_t*)(Kh + (size_t)row * D + (ci % KCH) * 8);
-    }
+    for (int r = 0; r < 4; ++r) stg[r] = buf_load16(kres, koff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
   };
   auto store_k = [&](int buf) {
 #pragma unroll
@@ -151,11 +151,11 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   const int vc = st % (D / 4);
   const int vh = (st / (D / 4)) & 1;
   const int vs = st / (D / 2);
+  const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * RB + vc * 8;
   auto load_v = [&](int j0) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int key = min(j0 + 16 * vs + 8 * (k / 4) + 4 * vh + (k % 4), N - 1);
-      const u32x2_t x = *(const u32x2_t*)(Vh + (size_t)key * D + 4 * vc);
+      const u32x2_t x = buf_load8(vres, voff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB);
       stg[k / 2][2 * (k % 2) + 0] = x[0];
       stg[k / 2][2 * (k % 2) + 1] = x[1];
     }
@@ -174,7 +174,6 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
       *(u32x4_t*)(dst + 8 * cc) = u32x4_t{o[0], o[1], o[2], o[3]};
     }
   };
-
   // prologue: K_0 staged by the leading group, V_0 requested by the trailing one
   if (grp == 0) {
     load_k(0);
@@ -182,6 +181,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   } else {
     load_v(0);
   }
+  wait_vmem();  // Q fragments (and V_0) resident before the loop
   lds_barrier();
 
   const int kfrag = l32 * KS + 8 * h;  // element offset of this lane's K fragment

@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,     /* B, H or N < 1, or an index would not fit in 32 bits */
+  FA_ERR_SHAPE = 2,     /* B, H or N < 1, N > 2^22, or B*H*ceil(N/32) >= 2^24 */
   FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
   FA_ERR_DTYPE = 4,     /* unknown dtype, or a dtype this entry point does not take */
   FA_ERR_ALIGN = 5,     /* a data pointer is not 16-byte aligned */

@@ -72,7 +72,7 @@ def test_fwd_argument_errors(lib):
     assert fwd(lib, B=0) == FA_ERR_SHAPE
     assert fwd(lib, H=-1) == FA_ERR_SHAPE
     assert fwd(lib, N=0) == FA_ERR_SHAPE
-    assert fwd(lib, N=(1 << 30) + 1) == FA_ERR_SHAPE
+    assert fwd(lib, N=(1 << 22) + 1) == FA_ERR_SHAPE
     assert fwd(lib, B=1 << 20, H=1 << 12) == FA_ERR_SHAPE
     assert fwd(lib, d=96) == FA_ERR_HEADDIM
     assert fwd(lib, d=256) == FA_ERR_HEADDIM
