@@ -130,6 +130,12 @@ __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ inline uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 __device__ inline uint32_t hi16(uint32_t x) { return x >> 16; }
 __device__ inline uint32_t pair16(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
+// (a.lo, b.lo) and (a.hi, b.hi) as packed pairs, one v_perm_b32 each.
+__device__ inline uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ inline uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// Scheduling hints (instruction classes for __builtin_amdgcn_sched_group_barrier).
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100, kSchedDSWrite = 0x200;
 
 // Row-major tile of 16-bit elements in LDS, `D` columns per row, with the
 // 16-byte chunks of each row XOR-swizzled by the row index so that 32 lanes
@@ -157,10 +163,10 @@ __device__ inline void store_interleaved(uint16_t* dst, const u32x4_t r[4]) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const uint32_t a = r[0][p], b = r[1][p], c = r[2][p], d = r[3][p];
-    o[4 * p + 0] = pair16(lo16(a), lo16(b));  // column 2p, rows 0,1
-    o[4 * p + 1] = pair16(lo16(c), lo16(d));  // column 2p, rows 2,3
-    o[4 * p + 2] = pair16(hi16(a), hi16(b));  // column 2p+1, rows 0,1
-    o[4 * p + 3] = pair16(hi16(c), hi16(d));  // column 2p+1, rows 2,3
+    o[4 * p + 0] = pack_lo(a, b);  // column 2p, rows 0,1
+    o[4 * p + 1] = pack_lo(c, d);  // column 2p, rows 2,3
+    o[4 * p + 2] = pack_hi(a, b);  // column 2p+1, rows 0,1
+    o[4 * p + 3] = pack_hi(c, d);  // column 2p+1, rows 2,3
   }
 #pragma unroll
   for (int x = 0; x < 4; ++x)

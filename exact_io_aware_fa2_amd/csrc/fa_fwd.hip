@@ -30,6 +30,8 @@
 //     log2 units), and normalised once at the end (deferred rescaling).
 //   * causal: key tiles above the diagonal are never loaded or multiplied;
 //     only tiles crossing the diagonal are masked.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -56,9 +58,13 @@ __device__ inline void lds_barrier() {
 //   V-phase j: online softmax of S_j -> P_j                (vector ALU)
 // Waves 4..7 run one phase behind waves 0..3, so on every SIMD one wave is in
 // its M-phase while the other is in its V-phase, and the two kinds of work
-// overlap.  A workgroup barrier separates phases ("slots").  Staging is split
-// the same way: waves 0..3 load K tiles (issue in their M-phase, write LDS in
-// their V-phase), waves 4..7 load and transpose V tiles.
+// overlap.  A workgroup barrier separates phases ("slots").
+//
+// Staging: waves 0..3 stage K tiles, waves 4..7 stage V tiles.  A wave issues
+// the global loads of tile j+2 in its V-phase j (a few instructions) and writes
+// that tile to LDS in its next M-phase, between matrix instructions, where the
+// vector ALU is otherwise idle.  K is double-buffered, V triple-buffered (the
+// trailing waves still read V_{j-1} while V_{j+1} is written).
 //
 // LDS layouts (per buffer):
 //   K: row-major, rows padded to D + 8 elements, so 16 consecutive rows read
@@ -79,18 +85,19 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   constexpr int NKB = BC / 32;              // 32-key blocks per tile
   constexpr int NDB = D / 32;               // 32-column blocks of the output
   constexpr int NKS = D / 16;               // MFMA k-steps over d
-  constexpr int KLD = BC * KCH / 256;       // K chunks per staging thread (waves 0..3)
-  constexpr int VU = (BC / 16) * 2 * (D / 4);  // V staging units (8 keys x 4 columns)
-  static_assert(KLD * 256 == BC * KCH && VU == 256, "tile shape must give one unit per thread");
-  static_assert(KLD == 4, "staging registers are shared by the K and V roles");
+  constexpr int NQK = NKS * NKB;            // S MFMAs per tile
+  constexpr int NPV = NKB * 2 * NDB;        // O MFMAs per tile
+  static_assert(BC * KCH == 1024 && (BC / 16) * 2 * (D / 4) == 256,
+                "one K chunk set and one V unit per staging thread");
+  static_assert(NQK == NPV, "matrix phase interleaves the two products one to one");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[3][BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int grp = w >> 2;          // 0: leading group, 1: trailing group
+  const int grp = w >> 2;          // 0: leading group (stages K), 1: trailing group (stages V)
   const int st = tid & 255;        // staging index within the group
   const int h = lane >> 5;
   const int l32 = lane & 31;
@@ -103,8 +110,6 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   const size_t head_off = (size_t)bh * N * D;
   constexpr uint32_t RB = D * 2;   // bytes per row
   const uint32_t head_bytes = (uint32_t)N * RB;
-  const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
-  const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
   const int qw = q0 + 32 * w;      // first query row of this wavefront
   const int qrow = qw + l32;
 
@@ -130,105 +135,167 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   const int wave_end = CAUSAL ? min(N, qw + 32) : N;
   const int wave_tiles = (wave_end + BC - 1) / BC;
 
-  // Staging registers: 4 x 16 bytes per thread in both roles.  Rows past the
-  // end of the sequence read zeros (their scores are masked to -inf, so they
-  // contribute exactly zero).
+  // ---- staging: 4 x 16 bytes per thread in both roles.  Rows past the end of
+  // the sequence read zeros (their scores are masked to -inf, so they add 0).
+  const rsrc_t tres = make_rsrc((grp == 0 ? K : V) + head_off, head_bytes);
   u32x4_t stg[4];
   // K role: chunk ci = st + 256 r -> row ci / KCH, 16-byte column ci % KCH
   const uint32_t koff = (uint32_t)(st / KCH) * RB + (st % KCH) * 16;
-  auto load_k = [&](int j0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) stg[r] = buf_load16(kres, koff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int ci = st + 256 * r;
-      *(u32x4_t*)(&sK[buf][(ci / KCH) * KS + (ci % KCH) * 8]) = stg[r];
-    }
-  };
+  const int kst = (st / KCH) * KS + (st % KCH) * 8;
   // V role: unit st -> (16-key step vs, half vh, 4-column chunk vc); 8 rows x 8 bytes
   const int vc = st % (D / 4);
   const int vh = (st / (D / 4)) & 1;
   const int vs = st / (D / 2);
   const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * RB + vc * 8;
-  auto load_v = [&](int j0) {
+  const int vst = ((2 * vs + vh) * D + 4 * vc) * 8;
+
+  auto load_tile = [&](int j0) {
+    if (grp == 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const u32x2_t x = buf_load8(vres, voff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB);
-      stg[k / 2][2 * (k % 2) + 0] = x[0];
-      stg[k / 2][2 * (k % 2) + 1] = x[1];
+      for (int r = 0; r < 4; ++r) stg[r] = buf_load16(tres, koff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const u32x2_t x = buf_load8(tres, voff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB);
+        stg[k / 2][2 * (k % 2) + 0] = x[0];
+        stg[k / 2][2 * (k % 2) + 1] = x[1];
+      }
     }
   };
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) *(u32x4_t*)(&sK[buf][kst + r * (256 / KCH) * KS]) = stg[r];
+  };
   auto store_v = [&](int buf) {
-    // row k holds columns (4vc, 4vc+1) in dword 2(k%2) of stg[k/2] and (4vc+2, 4vc+3) in the next
-    uint16_t* dst = &sV[buf][((2 * vs + vh) * D + 4 * vc) * 8];
+    // stg[kp] = {row 2kp cols (0,1), row 2kp cols (2,3), row 2kp+1 cols (0,1), row 2kp+1 cols (2,3)}
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       uint32_t o[4];
 #pragma unroll
       for (int kp = 0; kp < 4; ++kp) {
-        const uint32_t a = stg[kp][(cc / 2)], b = stg[kp][2 + (cc / 2)];  // rows 2kp, 2kp+1
-        o[kp] = (cc & 1) ? pair16(hi16(a), hi16(b)) : pair16(lo16(a), lo16(b));
+        const uint32_t a = stg[kp][cc / 2], b = stg[kp][2 + cc / 2];
+        o[kp] = (cc & 1) ? pack_hi(a, b) : pack_lo(a, b);
       }
-      *(u32x4_t*)(dst + 8 * cc) = u32x4_t{o[0], o[1], o[2], o[3]};
+      *(u32x4_t*)(&sV[buf][vst + 8 * cc]) = u32x4_t{o[0], o[1], o[2], o[3]};
     }
   };
-  // prologue: K_0 staged by the leading group, V_0 requested by the trailing one
-  if (grp == 0) {
-    load_k(0);
-    store_k(0);
-  } else {
-    load_v(0);
-  }
-  wait_vmem();  // Q fragments (and V_0) resident before the loop
-  lds_barrier();
+  auto store_tile = [&](int j) {  // tile j into its buffer
+    if (grp == 0) store_k(j & 1);
+    else store_v(j % 3);
+  };
 
+  // ---- matrix products
   const int kfrag = l32 * KS + 8 * h;  // element offset of this lane's K fragment
   const int vfrag = (h * D + l32) * 8;  // element offset of this lane's V fragment
+  auto qk_step = [&](const uint16_t* kb_, int i) {  // i-th of NQK: ks = i / NKB, kb = i % NKB
+    const int ks = i / NKB, kb = i % NKB;
+    const u32x4_t kf = *(const u32x4_t*)(kb_ + 32 * kb * KS + 16 * ks);
+    s[kb] = TR::mfma(kf, qf[ks], s[kb]);
+  };
+  auto pv_step = [&](const uint16_t* vb_, int i) {  // i-th of NPV: (kb, t) = i / NDB, db = i % NDB
+    const int kt = i / NDB, db = i % NDB;
+    const int kb = kt / 2, t = kt % 2;
+    const u32x4_t pf = u32x4_t{pt[kb][4 * t + 0], pt[kb][4 * t + 1], pt[kb][4 * t + 2], pt[kb][4 * t + 3]};
+    const u32x4_t vf = *(const u32x4_t*)(vb_ + ((2 * kt) * D + 32 * db) * 8);
+    acc_o[db] = TR::mfma(vf, pf, acc_o[db]);
+  };
+
+  // ---- prologue: tile 0 in LDS, tile 1 requested
+  load_tile(0);
+  if (grp == 0) store_k(0);
+  else store_v(0);
+  wait_vmem();  // Q fragments and tile 0 resident before the loop
+  if (n_tiles > 1) load_tile(BC);
+  lds_barrier();
+
   const int n_slots = 2 * n_tiles + 2;
   for (int slot = 0; slot < n_slots; ++slot) {
     const int ph = slot - grp;  // this wave's own phase counter
     if (ph >= 0 && (ph & 1) == 0) {
-      // ---------------- M-phase j
+      // ---------------- M-phase j: write tile j+1, S_j = K_j Q^T, O += V_{j-1}^T P_{j-1}
       __builtin_amdgcn_s_setprio(1);
       const int j = ph >> 1;
-      if (j + 1 < n_tiles) {
-        if (grp == 0) load_k((j + 1) * BC);
-        else load_v((j + 1) * BC);
-      }
-      if (j < n_tiles && j < wave_tiles) {
-        const uint16_t* kb_ = sK[j & 1] + kfrag;
+      const bool stage = j + 1 < n_tiles;
+      const bool do_qk = j < wave_tiles;
+      const bool do_pv = j >= 1 && j - 1 < wave_tiles;
+      const uint16_t* kb_ = sK[j & 1] + kfrag;
+      const uint16_t* vb_ = sV[(j + 2) % 3] + vfrag;  // V_{j-1}
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            const u32x4_t kf = *(const u32x4_t*)(kb_ + 32 * kb * KS + 16 * ks);
-            s[kb] = TR::mfma(kf, qf[ks], s[kb]);
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
+      if (do_qk && do_pv) {
+        // Steady state, written as an explicit software pipeline: the products
+        // alternate S and O steps, each operand is read from LDS kAhead steps
+        // before its product, and the staging writes (with the V packing) sit
+        // between products.  sched_barrier keeps the compiler from regrouping
+        // the reads next to their uses.  The staging write is unconditional:
+        // past the last tile it rewrites a buffer no product reads again.
+        constexpr int NST = NQK + NPV;  // steps: even = S (QK), odd = O (PV)
+        constexpr int kAhead = 4;
+        auto frag_addr = [&](int step) -> const uint16_t* {
+          const int i = step >> 1;
+          if (step & 1) {
+            const int kt = i / NDB, db = i % NDB;
+            return vb_ + ((2 * kt) * D + 32 * db) * 8;
           }
-      }
-      if (j >= 1 && j - 1 < wave_tiles) {
-        const uint16_t* vb_ = sV[(j - 1) & 1] + vfrag;
+          const int ks = i / NKB, kb = i % NKB;
+          return kb_ + 32 * kb * KS + 16 * ks;
+        };
+        auto fused = [&](auto role) {
+          constexpr int R = decltype(role)::value;
+          u32x4_t fr[kAhead];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+          for (int x = 0; x < kAhead; ++x) fr[x] = *(const u32x4_t*)frag_addr(x);
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const u32x4_t pf = u32x4_t{pt[kb][4 * t + 0], pt[kb][4 * t + 1], pt[kb][4 * t + 2],
-                                       pt[kb][4 * t + 3]};
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              const u32x4_t vf = *(const u32x4_t*)(vb_ + ((2 * (2 * kb + t)) * D + 32 * db) * 8);
-              acc_o[db] = TR::mfma(vf, pf, acc_o[db]);
+          for (int stp = 0; stp < NST; ++stp) {
+            const u32x4_t a = fr[stp % kAhead];
+            if (stp + kAhead < NST) fr[stp % kAhead] = *(const u32x4_t*)frag_addr(stp + kAhead);
+            const int i = stp >> 1;
+            if (stp & 1) {
+              const int kt = i / NDB, db = i % NDB;
+              const int kb = kt / 2, t = kt % 2;
+              const u32x4_t pf = u32x4_t{pt[kb][4 * t + 0], pt[kb][4 * t + 1], pt[kb][4 * t + 2],
+                                         pt[kb][4 * t + 3]};
+              acc_o[db] = TR::mfma(a, pf, acc_o[db]);
+            } else {
+              const int ks = i / NKB, kb = i % NKB;
+              s[kb] = TR::mfma(a, qf[ks], s[kb]);
             }
+            // staging: one 16-byte LDS write every 8 steps
+            if (stp % 8 == 3) {
+              const int cc = stp / 8;
+              if constexpr (R == 0) {
+                *(u32x4_t*)(&sK[(j + 1) & 1][kst + cc * (256 / KCH) * KS]) = stg[cc];
+              } else {
+                uint32_t o[4];
+#pragma unroll
+                for (int kp = 0; kp < 4; ++kp) {
+                  const uint32_t x0 = stg[kp][cc / 2], x1 = stg[kp][2 + cc / 2];
+                  o[kp] = (cc & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
+                }
+                *(u32x4_t*)(&sV[(j + 1) % 3][vst + 8 * cc]) = u32x4_t{o[0], o[1], o[2], o[3]};
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
+        };
+        if (grp == 0) fused(std::integral_constant<int, 0>{});
+        else fused(std::integral_constant<int, 1>{});
+      } else {
+        if (stage) store_tile(j + 1);
+        if (do_qk) {
+#pragma unroll
+          for (int i = 0; i < NQK; ++i) qk_step(kb_, i);
+        }
+        if (do_pv) {
+#pragma unroll
+          for (int i = 0; i < NPV; ++i) pv_step(vb_, i);
+        }
       }
       __builtin_amdgcn_s_setprio(0);
     } else if (ph >= 0) {
-      // ---------------- V-phase j
+      // ---------------- V-phase j: request tile j+2, softmax of S_j
       const int j = (ph - 1) >> 1;
-      if (grp == 0 && j + 1 < n_tiles) store_k((j + 1) & 1);
+      if (j + 2 < n_tiles) load_tile((j + 2) * BC);
       if (j < wave_tiles) {
         const int j0 = j * BC;
         if ((CAUSAL && j0 + BC - 1 > qw) || j0 + BC > N) {
@@ -273,11 +340,6 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         l_run += lsum;
         lt_run += ltsum;
       }
-    }
-    // trailing group: write V_{j+1} during its V-phase j (slot 2j+2); V_0 at slot 0
-    if (grp == 1 && (slot & 1) == 0) {
-      const int jn = slot >> 1;  // tile being written
-      if (jn < n_tiles) store_v(jn & 1);
     }
     lds_barrier();
   }
