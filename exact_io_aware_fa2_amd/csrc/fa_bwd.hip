@@ -27,6 +27,8 @@
 //
 // All products use v_mfma_f32_32x32x16 (bf16/fp16 in, fp32 accumulate).  P and
 // dS are rounded to the input type (nearest even) before they enter a product.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -269,28 +271,44 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
 // ------------------------------------------------------------------ dQ
 
-template <class TR, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// dQ: 8 wavefronts (two per SIMD), 32 query rows each, 256 rows per
+// workgroup, with the same two-phase schedule as the forward:
+//   M-phase j: S^T_j = K_j Q^T, dP^T_j = V_j dO^T, dQ^T += K_{j-1}^T dS^T_{j-1}
+//   V-phase j: P = exp2(S c - LSE log2 e), dS_j = P (dP - D), rounded
+// Waves 4..7 run one phase behind waves 0..3.  Waves 0..3 stage K (row-major
+// for S, key-interleaved for dQ), waves 4..7 stage V (row-major for dP).
+// K and V row tiles are double-buffered, the interleaved K tile (read one
+// phase later) triple-buffered.
+template <class TR, int D, int BC, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                    const float* __restrict__ LSE, const float* __restrict__ Dvec,
                    uint16_t* __restrict__ dQ, int N, int n_qtiles, uint32_t total, float c,
                    float scale) {
-  constexpr int BR = 128;           // query rows per workgroup (4 wavefronts x 32)
-  constexpr int BC = 64;            // keys per tile
-  constexpr int KCH = D / 8;
-  constexpr int NKS = D / 16;
+  constexpr int NW = 8;
+  constexpr int BR = 32 * NW;            // query rows per workgroup
+  constexpr int KCH = D / 8;             // 16-byte chunks per row
+  constexpr int KS = D + 8;              // padded row (elements)
+  constexpr int NKB = BC / 32;
   constexpr int NDB = D / 32;
-  constexpr int UNITS = (BC / 4) * KCH;
-  constexpr int ULOADS = (UNITS + 255) / 256;
+  constexpr int NKS = D / 16;
+  constexpr int NS = NKS * NKB;          // S (and dP) products per tile
+  constexpr int NQ = NKB * 2 * NDB;      // dQ products per tile
+  constexpr int KU = BC * D / 32;        // K staging units (8 keys x 4 columns)
+  constexpr int VLD = BC * KCH / 256;    // V staging chunks per thread
+  static_assert(KU <= 256 && VLD * 256 == BC * KCH && VLD <= 4, "staging shape");
+  static_assert(NS == NQ, "matrix phase interleaves S, dP and dQ one to one");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[2][BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sKt[3][BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int grp = w >> 2;
+  const int st = tid & 255;
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -302,122 +320,198 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int qw = q0 + 32 * w;
   const int qrow = qw + l32;
   const size_t head_off = (size_t)bh * N * D;
-  const uint16_t* Kh = K + head_off;
-  const uint16_t* Vh = V + head_off;
+  constexpr uint32_t RB = D * 2;
+  const uint32_t head_bytes = (uint32_t)N * RB;
 
+  // Q and dO rows as B operands, loaded once; LSE (log2 units) and D per row.
   u32x4_t qf[NKS], of[NKS];
+  {
+    const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
+    const rsrc_t ores = make_rsrc(dO + head_off, head_bytes);
+    const uint32_t off = (uint32_t)qrow * RB + 16 * h;
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    if (qrow < N) {
-      qf[ks] = *(const u32x4_t*)(Q + head_off + (size_t)qrow * D + 16 * ks + 8 * h);
-      of[ks] = *(const u32x4_t*)(dO + head_off + (size_t)qrow * D + 16 * ks + 8 * h);
-    } else {
-      qf[ks] = u32x4_t{0, 0, 0, 0};
-      of[ks] = u32x4_t{0, 0, 0, 0};
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = buf_load16(qres, off + 32 * ks);
+      of[ks] = buf_load16(ores, off + 32 * ks);
     }
   }
+  // rows past the end: P = exp2(-inf) = 0, so dS = 0 there
   const float lq = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dq_ = qrow < N ? Dvec[(size_t)bh * N + qrow] : 0.0f;
+  const float dd = qrow < N ? Dvec[(size_t)bh * N + qrow] : 0.0f;
 
   f32x16_t acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+  f32x16_t s[NKB], dp[NKB];
+  uint32_t dsk[NKB][8];
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
-  const int wave_last = CAUSAL ? min(N, qw + 32) : N;
-  const int wave_tiles = (wave_last + BC - 1) / BC;
+  const int wave_end = CAUSAL ? min(N, qw + 32) : N;
+  const int wave_tiles = (wave_end + BC - 1) / BC;
 
-  u32x4_t kreg[ULOADS][4], vreg[ULOADS][4];
+  // ---- staging
+  const rsrc_t tres = make_rsrc((grp == 0 ? K : V) + head_off, head_bytes);
+  u32x4_t stg[4];
+  // K role: unit st -> (16-key step us, half uh, 4-column chunk uc)
+  const bool kact = st < KU;
+  const int uc = st % (D / 4);
+  const int uh = (st / (D / 4)) & 1;
+  const int us = st / (D / 2);
+  const uint32_t koff = (uint32_t)(16 * us + 4 * uh) * RB + uc * 8;
+  const int krow0 = 16 * us + 4 * uh;  // rows krow0 + 8 (k / 4) + k % 4
+  const int kst = ((2 * us + uh) * D + 4 * uc) * 8;
+  // V role: chunk ci = st + 256 r -> row ci / KCH, column ci % KCH
+  const uint32_t voff = (uint32_t)(st / KCH) * RB + (st % KCH) * 16;
+  const int vst = (st / KCH) * KS + (st % KCH) * 8;
+
   auto load_tile = [&](int j0) {
+    if (grp == 0) {
+      if (kact) {
 #pragma unroll
-    for (int r = 0; r < ULOADS; ++r) {
-      const int u = tid + 256 * r;
-      const int g = u / KCH, ch = u % KCH;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = j0 + 4 * g + rr;
-        if (u < UNITS && key < N) {
-          kreg[r][rr] = *(const u32x4_t*)(Kh + (size_t)key * D + ch * 8);
-          vreg[r][rr] = *(const u32x4_t*)(Vh + (size_t)key * D + ch * 8);
-        } else {
-          kreg[r][rr] = u32x4_t{0, 0, 0, 0};
-          vreg[r][rr] = u32x4_t{0, 0, 0, 0};
+        for (int k = 0; k < 8; ++k) {
+          const u32x2_t x = buf_load8(tres, koff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB);
+          stg[k / 2][2 * (k % 2) + 0] = x[0];
+          stg[k / 2][2 * (k % 2) + 1] = x[1];
         }
       }
+    } else {
+#pragma unroll
+      for (int r = 0; r < VLD; ++r) stg[r] = buf_load16(tres, voff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
     }
   };
-  auto store_tile = [&](int buf) {
+  // one quarter of the staging writes (part 0..3), so they can be spread out
+  auto store_part = [&](auto role, int j, int part) {
+    if constexpr (decltype(role)::value == 0) {
+      if (kact) {
+        // row-major: rows 2 part and 2 part + 1 of the unit
 #pragma unroll
-    for (int r = 0; r < ULOADS; ++r) {
-      const int u = tid + 256 * r;
-      if (u < UNITS) {
-        const int g = u / KCH, ch = u % KCH;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          *(u32x4_t*)(&sK[buf][swz_off<D>(4 * g + rr, ch)]) = kreg[r][rr];
-          *(u32x4_t*)(&sV[buf][swz_off<D>(4 * g + rr, ch)]) = vreg[r][rr];
+        for (int e = 0; e < 2; ++e) {
+          const int k = 2 * part + e;
+          *(u32x2_t*)(&sK[j & 1][(krow0 + 8 * (k / 4) + (k % 4)) * KS + 4 * uc]) =
+              u32x2_t{stg[k / 2][2 * (k % 2) + 0], stg[k / 2][2 * (k % 2) + 1]};
         }
-        store_interleaved(&sKt[buf][il_off<D>(g, 8 * ch)], kreg[r]);
+        // interleaved: column 4 uc + part
+        const int cc = part;
+        uint32_t o[4];
+#pragma unroll
+        for (int kp = 0; kp < 4; ++kp) {
+          const uint32_t x0 = stg[kp][cc / 2], x1 = stg[kp][2 + cc / 2];
+          o[kp] = (cc & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
+        }
+        *(u32x4_t*)(&sKt[j % 3][kst + 8 * cc]) = u32x4_t{o[0], o[1], o[2], o[3]};
       }
+    } else {
+      if (part < VLD) *(u32x4_t*)(&sV[j & 1][vst + part * (256 / KCH) * KS]) = stg[part];
+    }
+  };
+  auto store_tile = [&](int j) {
+    if (grp == 0) {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) store_part(std::integral_constant<int, 0>{}, j, part);
+    } else {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) store_part(std::integral_constant<int, 1>{}, j, part);
     }
   };
 
+  // ---- products
+  const int rfrag = l32 * KS + 8 * h;   // row-major fragment of this lane
+  const int ifrag = (h * D + l32) * 8;  // interleaved fragment of this lane
+  auto s_step = [&](const uint16_t* kb_, int i) {
+    const int ks = i / NKB, kb = i % NKB;
+    s[kb] = TR::mfma(*(const u32x4_t*)(kb_ + 32 * kb * KS + 16 * ks), qf[ks], s[kb]);
+  };
+  auto dp_step = [&](const uint16_t* vb_, int i) {
+    const int ks = i / NKB, kb = i % NKB;
+    dp[kb] = TR::mfma(*(const u32x4_t*)(vb_ + 32 * kb * KS + 16 * ks), of[ks], dp[kb]);
+  };
+  auto dq_step = [&](const uint16_t* tb_, int i) {
+    const int kt = i / NDB, db = i % NDB;
+    const int kb = kt / 2, t = kt % 2;
+    const u32x4_t b = u32x4_t{dsk[kb][4 * t + 0], dsk[kb][4 * t + 1], dsk[kb][4 * t + 2], dsk[kb][4 * t + 3]};
+    acc[db] = TR::mfma(*(const u32x4_t*)(tb_ + ((2 * kt) * D + 32 * db) * 8), b, acc[db]);
+  };
+
+  // ---- prologue
   load_tile(0);
   store_tile(0);
-  __syncthreads();
+  wait_vmem();
+  if (n_tiles > 1) load_tile(BC);
+  lds_barrier();
 
-  for (int jt = 0; jt < n_tiles; ++jt) {
-    const int buf = jt & 1;
-    const int j0 = jt * BC;
-    const bool has_next = jt + 1 < n_tiles;
-    if (has_next) load_tile(j0 + BC);
-
-    if (jt < wave_tiles) {
-      const bool need_mask = (CAUSAL && (j0 + BC - 1 > qw)) || (j0 + BC > N);
+  const int n_slots = 2 * n_tiles + 2;
+  for (int slot = 0; slot < n_slots; ++slot) {
+    const int ph = slot - grp;
+    if (ph >= 0 && (ph & 1) == 0) {
+      // ---------------- M-phase j
+      __builtin_amdgcn_s_setprio(1);
+      const int j = ph >> 1;
+      const bool do_s = j < wave_tiles;
+      const bool do_q = j >= 1 && j - 1 < wave_tiles;
+      const uint16_t* kb_ = sK[j & 1] + rfrag;
+      const uint16_t* vb_ = sV[j & 1] + rfrag;
+      const uint16_t* tb_ = sKt[(j + 2) % 3] + ifrag;  // K_{j-1}, interleaved
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // S^T = K Q^T and dP^T = V dO^T (column = query = lane % 32)
-        f32x16_t s = zero16(), dp = zero16();
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = zero16();
+        dp[kb] = zero16();
+      }
+      if (do_s && do_q) {
+        // steady state: S, dP, dQ products interleaved, staging writes between
+        // them (past the last tile they rewrite a buffer no one reads again)
+        auto fused = [&](auto role) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const int row = 32 * kb + l32;
-          const u32x4_t ka = *(const u32x4_t*)(&sK[buf][swz_off<D>(row, 2 * ks + h)]);
-          const u32x4_t va = *(const u32x4_t*)(&sV[buf][swz_off<D>(row, 2 * ks + h)]);
-          s = TR::mfma(ka, qf[ks], s);
-          dp = TR::mfma(va, of[ks], dp);
-        }
-        uint32_t dsk[8];
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float ds2[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int key = j0 + 32 * kb + 8 * ((r + e) / 4) + 4 * h + ((r + e) % 4);
-            float pv = fast_exp2(fmaf(s[r + e], c, -lq));
-            if (need_mask && (key >= N || (CAUSAL && key > qrow))) pv = 0.0f;
-            ds2[e] = pv * (dp[r + e] - dq_);
+          for (int i = 0; i < NS; ++i) {
+            s_step(kb_, i);
+            dp_step(vb_, i);
+            dq_step(tb_, i);
+            if (i % (NS / 4) == NS / 8) store_part(role, j + 1, i / (NS / 4));
           }
-          dsk[r / 2] = TR::pack2(ds2[0], ds2[1]);
-        }
-        // dQ^T += K^T dS^T over the 32 keys of the block, two steps of 16
+        };
+        if (grp == 0) fused(std::integral_constant<int, 0>{});
+        else fused(std::integral_constant<int, 1>{});
+      } else {
+        if (j + 1 < n_tiles) store_tile(j + 1);
+        if (do_s) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u32x4_t b = u32x4_t{dsk[4 * t + 0], dsk[4 * t + 1], dsk[4 * t + 2], dsk[4 * t + 3]};
-          const int ga = 8 * kb + 4 * t + h, gb = ga + 2;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int col = 32 * db + l32;
-            const u32x2_t a0 = *(const u32x2_t*)(&sKt[buf][il_off<D>(ga, col)]);
-            const u32x2_t a1 = *(const u32x2_t*)(&sKt[buf][il_off<D>(gb, col)]);
-            acc[db] = TR::mfma(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, b, acc[db]);
+          for (int i = 0; i < NS; ++i) {
+            s_step(kb_, i);
+            dp_step(vb_, i);
           }
+        }
+        if (do_q) {
+#pragma unroll
+          for (int i = 0; i < NQ; ++i) dq_step(tb_, i);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
+    } else if (ph >= 0) {
+      // ---------------- V-phase j
+      const int j = (ph - 1) >> 1;
+      if (j + 2 < n_tiles) load_tile((j + 2) * BC);
+      if (j < wave_tiles) {
+        const int j0 = j * BC;
+        const bool need_mask = (CAUSAL && j0 + BC - 1 > qw) || j0 + BC > N;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            float d2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              float p = fast_exp2(fmaf(s[kb][r + e], c, -lq));
+              if (need_mask) {
+                const int key = j0 + 32 * kb + 8 * ((r + e) / 4) + 4 * h + ((r + e) % 4);
+                if (key >= N || (CAUSAL && key > qrow)) p = 0.0f;
+              }
+              d2[e] = p * (dp[kb][r + e] - dd);
+            }
+            dsk[kb][r / 2] = TR::pack2(d2[0], d2[1]);
+          }
+      }
     }
-
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    lds_barrier();
   }
 
   if (qrow < N) {
@@ -458,9 +552,10 @@ static hipError_t dkdv_t(const BwdArgs& a) {
 
 template <class TR, int D, bool CAUSAL>
 static hipError_t dq_t(const BwdArgs& a) {
-  const int n_qtiles = (a.N + 127) / 128;
+  const int n_qtiles = (a.N + 255) / 256;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((bwd_dq_kernel<TR, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+  constexpr int BC = D == 128 ? 32 : 64;  // keys per tile (register budget at two waves per SIMD)
+  hipLaunchKernelGGL((bwd_dq_kernel<TR, D, BC, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.N, n_qtiles, total,
                      a.c, a.scale);

@@ -123,6 +123,14 @@ __device__ inline u32x2_t buf_load8(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
 
+// Barrier for LDS hand-off between wavefronts: waits for this wave's LDS
+// accesses only, so global loads issued for the next tile stay in flight.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wait until every vector-memory load issued so far has returned.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

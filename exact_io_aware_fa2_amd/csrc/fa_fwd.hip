@@ -44,14 +44,6 @@ namespace fa {
 // denominator, so the result is unchanged mathematically.
 constexpr float kTau = 8.0f;
 
-// Barrier for LDS hand-off between wavefronts: waits for this wave's LDS
-// accesses only, so global loads issued for the next tile stay in flight.
-__device__ inline void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // 16-bit forward.  8 wavefronts, two per SIMD, each owning 32 query rows.
 // Every wavefront alternates two phases per key tile j:
 //   M-phase j: S_j = K_j Q^T  and  O += V_{j-1}^T P_{j-1}   (matrix cores)
