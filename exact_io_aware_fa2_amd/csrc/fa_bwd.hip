@@ -269,6 +269,275 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 }
 
+// dK, dV with two wavefronts per SIMD (d = 64): 8 wavefronts x 32 keys, 256
+// keys per workgroup; query tiles of 64 rows stream through LDS.  Same
+// two-phase schedule as the forward:
+//   M-phase i: S_i = Q_i K^T, dP_i = dO_i V^T                 (rows = queries)
+//              dV^T += dO_{i-1}^T P_{i-1}, dK^T += Q_{i-1}^T dS_{i-1}
+//   V-phase i: P_i = exp2(S c - LSE log2 e), dS_i = P_i (dP_i - D), rounded
+// Waves 0..3 stage Q (row-major, query-interleaved, LSE), waves 4..7 stage dO
+// (row-major, query-interleaved, D).  Row tiles double-, interleaved tiles and
+// row vectors triple-buffered.
+template <class TR, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                      const float* __restrict__ LSE, const float* __restrict__ Dvec,
+                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_ktiles,
+                      uint32_t total, float c, float scale) {
+  constexpr int NW = 8;
+  constexpr int BKV = 32 * NW;           // keys per workgroup
+  constexpr int BQ = 64;                 // query rows per step
+  constexpr int QB = BQ / 32;
+  constexpr int KS = D + 8;              // padded row (elements)
+  constexpr int NDB = D / 32;
+  constexpr int NKS = D / 16;
+  constexpr int NS = QB * NKS;           // S (and dP) products per step
+  constexpr int NG = QB * 2 * NDB;       // dV (and dK) products per step
+  constexpr int QU = BQ * D / 32;        // staging units (8 rows x 4 columns)
+  static_assert(NS == NG && QU <= 192, "matrix phase interleaves the four products one to one");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[2][BQ * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sQt[3][BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sOt[3][BQ * D];
+  __shared__ __attribute__((aligned(16))) float sL[3][BQ];
+  __shared__ __attribute__((aligned(16))) float sD[3][BQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int grp = w >> 2;
+  const int st = tid & 255;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const uint32_t lid = xcd_remap(blockIdx.x, total);
+  const int bh = lid / n_ktiles;
+  const int kt = lid % n_ktiles;
+  const int k0 = kt * BKV;
+  const int kw = k0 + 32 * w;            // first key of this wavefront
+  const int key = kw + l32;
+  const size_t head_off = (size_t)bh * N * D;
+  constexpr uint32_t RB = D * 2;
+  const uint32_t head_bytes = (uint32_t)N * RB;
+
+  // K and V rows of this wavefront's keys as B operands (column = key)
+  u32x4_t kf[NKS], vf[NKS];
+  {
+    const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
+    const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
+    const uint32_t off = (uint32_t)key * RB + 16 * h;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kf[ks] = buf_load16(kres, off + 32 * ks);
+      vf[ks] = buf_load16(vres, off + 32 * ks);
+    }
+  }
+  f32x16_t acc_dk[NDB], acc_dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    acc_dk[db] = zero16();
+    acc_dv[db] = zero16();
+  }
+  f32x16_t s[QB], dp[QB];
+  uint32_t pk[QB][8], dsk[QB][8];
+
+  const int i_begin = CAUSAL ? (k0 / BQ) * BQ : 0;
+  const int n_steps = (N - i_begin + BQ - 1) / BQ;
+  // causal: steps whose 64 rows all precede this wave's first key are skipped
+  const int first = CAUSAL ? max(0, (kw - i_begin - (BQ - 1) + BQ - 1) / BQ) : 0;
+
+  // ---- staging: group 0 -> Q and LSE, group 1 -> dO and D
+  const rsrc_t tres = make_rsrc((grp == 0 ? Q : dO) + head_off, head_bytes);
+  const float* vec = (grp == 0 ? LSE : Dvec) + (size_t)bh * N;
+  const bool uact = st < QU;
+  const int uc = st % (D / 4);
+  const int uh = (st / (D / 4)) & 1;
+  const int us = st / (D / 2);
+  const uint32_t uoff = (uint32_t)(16 * us + 4 * uh) * RB + uc * 8;
+  const int urow0 = 16 * us + 4 * uh;
+  const int ust = ((2 * us + uh) * D + 4 * uc) * 8;
+  const int vi = st - 192;               // threads 192..255 stage the row vector
+  u32x4_t stg[4];
+  float vreg = 0.0f;
+
+  auto load_tile = [&](int i0) {
+    if (uact) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const u32x2_t x = buf_load8(tres, uoff + (uint32_t)(i0 + 8 * (k / 4) + (k % 4)) * RB);
+        stg[k / 2][2 * (k % 2) + 0] = x[0];
+        stg[k / 2][2 * (k % 2) + 1] = x[1];
+      }
+    }
+    if (vi >= 0) {
+      const int row = i0 + vi;
+      // rows past the end: LSE = +inf makes P = 0; D = 0
+      vreg = row < N ? (grp == 0 ? vec[row] * kLog2e : vec[row]) : (grp == 0 ? INFINITY : 0.0f);
+    }
+  };
+  auto store_part = [&](int i, int part) {
+    uint16_t* rowbuf = grp == 0 ? sQ[i & 1] : sO[i & 1];
+    uint16_t* ilbuf = grp == 0 ? sQt[i % 3] : sOt[i % 3];
+    if (uact) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int k = 2 * part + e;
+        *(u32x2_t*)(&rowbuf[(urow0 + 8 * (k / 4) + (k % 4)) * KS + 4 * uc]) =
+            u32x2_t{stg[k / 2][2 * (k % 2) + 0], stg[k / 2][2 * (k % 2) + 1]};
+      }
+      const int cc = part;
+      uint32_t o[4];
+#pragma unroll
+      for (int kp = 0; kp < 4; ++kp) {
+        const uint32_t x0 = stg[kp][cc / 2], x1 = stg[kp][2 + cc / 2];
+        o[kp] = (cc & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
+      }
+      *(u32x4_t*)(&ilbuf[ust + 8 * cc]) = u32x4_t{o[0], o[1], o[2], o[3]};
+    }
+    if (part == 0 && vi >= 0) (grp == 0 ? sL : sD)[i % 3][vi] = vreg;
+  };
+  auto store_tile = [&](int i) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) store_part(i, part);
+  };
+
+  // ---- products
+  const int rfrag = l32 * KS + 8 * h;   // row-major fragment of this lane
+  const int ifrag = (h * D + l32) * 8;  // interleaved fragment of this lane
+  auto s_step = [&](const uint16_t* qb_, int i) {
+    const int qb = i / NKS, ks = i % NKS;
+    s[qb] = TR::mfma(*(const u32x4_t*)(qb_ + 32 * qb * KS + 16 * ks), kf[ks], s[qb]);
+  };
+  auto dp_step = [&](const uint16_t* ob_, int i) {
+    const int qb = i / NKS, ks = i % NKS;
+    dp[qb] = TR::mfma(*(const u32x4_t*)(ob_ + 32 * qb * KS + 16 * ks), vf[ks], dp[qb]);
+  };
+  auto dv_step = [&](const uint16_t* otb_, int i) {
+    const int qt2 = i / NDB, db = i % NDB;  // 16-row step of the tile
+    const int qb = qt2 / 2, t = qt2 % 2;
+    const u32x4_t b = u32x4_t{pk[qb][4 * t + 0], pk[qb][4 * t + 1], pk[qb][4 * t + 2], pk[qb][4 * t + 3]};
+    acc_dv[db] = TR::mfma(*(const u32x4_t*)(otb_ + ((2 * qt2) * D + 32 * db) * 8), b, acc_dv[db]);
+  };
+  auto dk_step = [&](const uint16_t* qtb_, int i) {
+    const int qt2 = i / NDB, db = i % NDB;
+    const int qb = qt2 / 2, t = qt2 % 2;
+    const u32x4_t b = u32x4_t{dsk[qb][4 * t + 0], dsk[qb][4 * t + 1], dsk[qb][4 * t + 2], dsk[qb][4 * t + 3]};
+    acc_dk[db] = TR::mfma(*(const u32x4_t*)(qtb_ + ((2 * qt2) * D + 32 * db) * 8), b, acc_dk[db]);
+  };
+
+  // ---- prologue
+  if (n_steps > 0) {
+    load_tile(i_begin);
+    store_tile(0);
+  }
+  wait_vmem();
+  if (n_steps > 1) load_tile(i_begin + BQ);
+  lds_barrier();
+
+  const int n_slots = 2 * n_steps + 2;
+  for (int slot = 0; slot < n_slots; ++slot) {
+    const int ph = slot - grp;
+    if (ph >= 0 && (ph & 1) == 0) {
+      // ---------------- M-phase i
+      __builtin_amdgcn_s_setprio(1);
+      const int i = ph >> 1;
+      const bool do_s = i >= first && i < n_steps;
+      const bool do_g = i - 1 >= first && i - 1 < n_steps;
+      const uint16_t* qb_ = sQ[i & 1] + rfrag;
+      const uint16_t* ob_ = sO[i & 1] + rfrag;
+      const uint16_t* qtb_ = sQt[(i + 2) % 3] + ifrag;  // step i-1
+      const uint16_t* otb_ = sOt[(i + 2) % 3] + ifrag;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        s[qb] = zero16();
+        dp[qb] = zero16();
+      }
+      if (do_s && do_g) {
+        // steady state; the staging write is unconditional (past the last
+        // step it rewrites buffers no one reads again)
+#pragma unroll
+        for (int x = 0; x < NS; ++x) {
+          s_step(qb_, x);
+          dv_step(otb_, x);
+          dp_step(ob_, x);
+          dk_step(qtb_, x);
+          if (x % (NS / 4) == NS / 8) store_part(i + 1, x / (NS / 4));
+        }
+      } else {
+        if (i + 1 < n_steps) store_tile(i + 1);
+        if (do_s) {
+#pragma unroll
+          for (int x = 0; x < NS; ++x) {
+            s_step(qb_, x);
+            dp_step(ob_, x);
+          }
+        }
+        if (do_g) {
+#pragma unroll
+          for (int x = 0; x < NG; ++x) {
+            dv_step(otb_, x);
+            dk_step(qtb_, x);
+          }
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    } else if (ph >= 0) {
+      // ---------------- V-phase i
+      const int i = (ph - 1) >> 1;
+      if (i + 2 < n_steps) load_tile(i_begin + (i + 2) * BQ);
+      if (i >= first && i < n_steps) {
+        const int i0 = i_begin + i * BQ;
+        const float* lv = sL[i % 3];
+        const float* dv = sD[i % 3];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const bool need_mask = CAUSAL && i0 + 32 * qb < kw + 31;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 l4 = *(const float4*)(&lv[32 * qb + 8 * g + 4 * h]);
+            const float4 d4 = *(const float4*)(&dv[32 * qb + 8 * g + 4 * h]);
+            const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+            float p[4], ds[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              float pv = fast_exp2(fmaf(s[qb][r], c, -la[e]));
+              if (need_mask && key > i0 + 32 * qb + 8 * g + 4 * h + e) pv = 0.0f;
+              p[e] = pv;
+              ds[e] = pv * (dp[qb][r] - da[e]);
+            }
+            pk[qb][2 * g + 0] = TR::pack2(p[0], p[1]);
+            pk[qb][2 * g + 1] = TR::pack2(p[2], p[3]);
+            dsk[qb][2 * g + 0] = TR::pack2(ds[0], ds[1]);
+            dsk[qb][2 * g + 1] = TR::pack2(ds[2], ds[3]);
+          }
+        }
+      }
+    }
+    lds_barrier();
+  }
+
+  if (key < N) {
+    uint16_t* dkrow = dK + head_off + (size_t)key * D;
+    uint16_t* dvrow = dV + head_off + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * h;
+        *(u32x2_t*)(dkrow + col) =
+            u32x2_t{TR::pack2(acc_dk[db][4 * g + 0] * scale, acc_dk[db][4 * g + 1] * scale),
+                    TR::pack2(acc_dk[db][4 * g + 2] * scale, acc_dk[db][4 * g + 3] * scale)};
+        *(u32x2_t*)(dvrow + col) =
+            u32x2_t{TR::pack2(acc_dv[db][4 * g + 0], acc_dv[db][4 * g + 1]),
+                    TR::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3])};
+      }
+  }
+}
+
 // ------------------------------------------------------------------ dQ
 
 // dQ: 8 wavefronts (two per SIMD), 32 query rows each, 256 rows per
@@ -541,6 +810,15 @@ static hipError_t prep_t(const BwdArgs& a) {
 
 template <class TR, int D, bool CAUSAL>
 static hipError_t dkdv_t(const BwdArgs& a) {
+  if constexpr (D == 64) {
+    const int n_ktiles = (a.N + 255) / 256;
+    const uint32_t total = (uint32_t)(n_ktiles * a.BH);
+    hipLaunchKernelGGL((bwd_dkdv2_kernel<TR, D, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                       a.N, n_ktiles, total, a.c, a.scale);
+    return hipGetLastError();
+  }
   const int n_ktiles = (a.N + 127) / 128;
   const uint32_t total = (uint32_t)(n_ktiles * a.BH);
   hipLaunchKernelGGL((bwd_dkdv_kernel<TR, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
