@@ -294,8 +294,7 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   constexpr int NKS = D / 16;
   constexpr int NS = QB * NKS;           // S (and dP) products per step
   constexpr int NG = QB * 2 * NDB;       // dV (and dK) products per step
-  constexpr int QU = BQ * D / 32;        // staging units (8 rows x 4 columns)
-  static_assert(NS == NG && QU <= 192, "matrix phase interleaves the four products one to one");
+  static_assert(NS == NG, "matrix phase interleaves the four products one to one");
 
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * KS];
   __shared__ __attribute__((aligned(16))) uint16_t sO[2][BQ * KS];
@@ -348,55 +347,53 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   // causal: steps whose 64 rows all precede this wave's first key are skipped
   const int first = CAUSAL ? max(0, (kw - i_begin - (BQ - 1) + BQ - 1) / BQ) : 0;
 
-  // ---- staging: group 0 -> Q and LSE, group 1 -> dO and D
+  // ---- staging: group 0 -> Q and LSE, group 1 -> dO and D.  Every thread of
+  // a group takes part (no divergent branches): unit st = 8 rows x 2 columns,
+  // rows 16us + 4uh + {0..3} and 16us + 8 + 4uh + {0..3}, columns 2uc, 2uc + 1;
+  // the row vector is loaded by all threads (rows st % 64, four copies).
+  static_assert(BQ * D / 16 == 256, "one staging unit per thread");
   const rsrc_t tres = make_rsrc((grp == 0 ? Q : dO) + head_off, head_bytes);
-  const float* vec = (grp == 0 ? LSE : Dvec) + (size_t)bh * N;
-  const bool uact = st < QU;
-  const int uc = st % (D / 4);
-  const int uh = (st / (D / 4)) & 1;
-  const int us = st / (D / 2);
-  const uint32_t uoff = (uint32_t)(16 * us + 4 * uh) * RB + uc * 8;
+  const rsrc_t vres = make_rsrc((grp == 0 ? LSE : Dvec) + (size_t)bh * N, (uint32_t)N * 4);
+  const int uc = st % (D / 2);
+  const int uh = (st / (D / 2)) & 1;
+  const int us = st / D;
   const int urow0 = 16 * us + 4 * uh;
-  const int ust = ((2 * us + uh) * D + 4 * uc) * 8;
-  const int vi = st - 192;               // threads 192..255 stage the row vector
-  u32x4_t stg[4];
+  const uint32_t uoff = (uint32_t)urow0 * RB + uc * 4;
+  const int ust = ((2 * us + uh) * D + 2 * uc) * 8;
+  const int vrow = st % BQ;
+  u32x4_t stg[2];
   float vreg = 0.0f;
 
   auto load_tile = [&](int i0) {
-    if (uact) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const u32x2_t x = buf_load8(tres, uoff + (uint32_t)(i0 + 8 * (k / 4) + (k % 4)) * RB);
-        stg[k / 2][2 * (k % 2) + 0] = x[0];
-        stg[k / 2][2 * (k % 2) + 1] = x[1];
-      }
-    }
-    if (vi >= 0) {
-      const int row = i0 + vi;
-      // rows past the end: LSE = +inf makes P = 0; D = 0
-      vreg = row < N ? (grp == 0 ? vec[row] * kLog2e : vec[row]) : (grp == 0 ? INFINITY : 0.0f);
-    }
+    for (int k = 0; k < 8; ++k)
+      stg[k / 4][k % 4] = __builtin_amdgcn_raw_buffer_load_b32(
+          tres, uoff + (uint32_t)(i0 + 8 * (k / 4) + (k % 4)) * RB, 0, 0);
+    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  vres, (uint32_t)(i0 + vrow) * 4, 0, 0));
+    // rows past the end: LSE = +inf makes P = 0; D = 0
+    const bool in = i0 + vrow < N;
+    vreg = grp == 0 ? (in ? x * kLog2e : INFINITY) : (in ? x : 0.0f);
   };
   auto store_part = [&](int i, int part) {
     uint16_t* rowbuf = grp == 0 ? sQ[i & 1] : sO[i & 1];
     uint16_t* ilbuf = grp == 0 ? sQt[i % 3] : sOt[i % 3];
-    if (uact) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int k = 2 * part + e;
-        *(u32x2_t*)(&rowbuf[(urow0 + 8 * (k / 4) + (k % 4)) * KS + 4 * uc]) =
-            u32x2_t{stg[k / 2][2 * (k % 2) + 0], stg[k / 2][2 * (k % 2) + 1]};
-      }
-      const int cc = part;
+    for (int e = 0; e < 2; ++e) {
+      const int k = 2 * part + e;
+      *(uint32_t*)(&rowbuf[(urow0 + 8 * (k / 4) + (k % 4)) * KS + 2 * uc]) = stg[k / 4][k % 4];
+    }
+    if (part & 1) {
+      const int cc = part >> 1;
       uint32_t o[4];
 #pragma unroll
       for (int kp = 0; kp < 4; ++kp) {
-        const uint32_t x0 = stg[kp][cc / 2], x1 = stg[kp][2 + cc / 2];
-        o[kp] = (cc & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
+        const uint32_t x0 = stg[kp / 2][2 * (kp % 2)], x1 = stg[kp / 2][2 * (kp % 2) + 1];
+        o[kp] = cc ? pack_hi(x0, x1) : pack_lo(x0, x1);
       }
       *(u32x4_t*)(&ilbuf[ust + 8 * cc]) = u32x4_t{o[0], o[1], o[2], o[3]};
     }
-    if (part == 0 && vi >= 0) (grp == 0 ? sL : sD)[i % 3][vi] = vreg;
+    if (part == 0) (grp == 0 ? sL : sD)[i % 3][vrow] = vreg;
   };
   auto store_tile = [&](int i) {
 #pragma unroll
@@ -406,25 +403,19 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   // ---- products
   const int rfrag = l32 * KS + 8 * h;   // row-major fragment of this lane
   const int ifrag = (h * D + l32) * 8;  // interleaved fragment of this lane
-  auto s_step = [&](const uint16_t* qb_, int i) {
-    const int qb = i / NKS, ks = i % NKS;
-    s[qb] = TR::mfma(*(const u32x4_t*)(qb_ + 32 * qb * KS + 16 * ks), kf[ks], s[qb]);
+  auto r_addr = [&](const uint16_t* b_, int x) { return b_ + 32 * (x / NKS) * KS + 16 * (x % NKS); };
+  auto i_addr = [&](const uint16_t* b_, int x) { return b_ + ((2 * (x / NDB)) * D + 32 * (x % NDB)) * 8; };
+  auto s_mma = [&](int x, u32x4_t a) { s[x / NKS] = TR::mfma(a, kf[x % NKS], s[x / NKS]); };
+  auto dp_mma = [&](int x, u32x4_t a) { dp[x / NKS] = TR::mfma(a, vf[x % NKS], dp[x / NKS]); };
+  auto dv_mma = [&](int x, u32x4_t a) {
+    const int qt2 = x / NDB, db = x % NDB, qb = qt2 / 2, t = qt2 % 2;
+    acc_dv[db] = TR::mfma(a, u32x4_t{pk[qb][4 * t + 0], pk[qb][4 * t + 1], pk[qb][4 * t + 2], pk[qb][4 * t + 3]},
+                          acc_dv[db]);
   };
-  auto dp_step = [&](const uint16_t* ob_, int i) {
-    const int qb = i / NKS, ks = i % NKS;
-    dp[qb] = TR::mfma(*(const u32x4_t*)(ob_ + 32 * qb * KS + 16 * ks), vf[ks], dp[qb]);
-  };
-  auto dv_step = [&](const uint16_t* otb_, int i) {
-    const int qt2 = i / NDB, db = i % NDB;  // 16-row step of the tile
-    const int qb = qt2 / 2, t = qt2 % 2;
-    const u32x4_t b = u32x4_t{pk[qb][4 * t + 0], pk[qb][4 * t + 1], pk[qb][4 * t + 2], pk[qb][4 * t + 3]};
-    acc_dv[db] = TR::mfma(*(const u32x4_t*)(otb_ + ((2 * qt2) * D + 32 * db) * 8), b, acc_dv[db]);
-  };
-  auto dk_step = [&](const uint16_t* qtb_, int i) {
-    const int qt2 = i / NDB, db = i % NDB;
-    const int qb = qt2 / 2, t = qt2 % 2;
-    const u32x4_t b = u32x4_t{dsk[qb][4 * t + 0], dsk[qb][4 * t + 1], dsk[qb][4 * t + 2], dsk[qb][4 * t + 3]};
-    acc_dk[db] = TR::mfma(*(const u32x4_t*)(qtb_ + ((2 * qt2) * D + 32 * db) * 8), b, acc_dk[db]);
+  auto dk_mma = [&](int x, u32x4_t a) {
+    const int qt2 = x / NDB, db = x % NDB, qb = qt2 / 2, t = qt2 % 2;
+    acc_dk[db] = TR::mfma(a, u32x4_t{dsk[qb][4 * t + 0], dsk[qb][4 * t + 1], dsk[qb][4 * t + 2], dsk[qb][4 * t + 3]},
+                          acc_dk[db]);
   };
 
   // ---- prologue
@@ -455,30 +446,45 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
         dp[qb] = zero16();
       }
       if (do_s && do_g) {
-        // steady state; the staging write is unconditional (past the last
-        // step it rewrites buffers no one reads again)
-#pragma unroll
-        for (int x = 0; x < NS; ++x) {
-          s_step(qb_, x);
-          dv_step(otb_, x);
-          dp_step(ob_, x);
-          dk_step(qtb_, x);
-          if (x % (NS / 4) == NS / 8) store_part(i + 1, x / (NS / 4));
-        }
+        // steady state: the four products interleaved in one pipelined run;
+        // the staging write is unconditional (past the last step it rewrites
+        // buffers no one reads again)
+        mma_pipeline<4 * NS, 3>(
+            [&](int k) {
+              const int x = k / 4;
+              switch (k % 4) {
+                case 0: return r_addr(qb_, x);
+                case 1: return i_addr(otb_, x);
+                case 2: return r_addr(ob_, x);
+                default: return i_addr(qtb_, x);
+              }
+            },
+            [&](int k, u32x4_t a) {
+              const int x = k / 4;
+              switch (k % 4) {
+                case 0: s_mma(x, a); break;
+                case 1: dv_mma(x, a); break;
+                case 2: dp_mma(x, a); break;
+                default: dk_mma(x, a); break;
+              }
+            },
+            [&](int k) {
+              if (k % NS == NS / 2) store_part(i + 1, k / NS);
+            });
       } else {
         if (i + 1 < n_steps) store_tile(i + 1);
         if (do_s) {
 #pragma unroll
           for (int x = 0; x < NS; ++x) {
-            s_step(qb_, x);
-            dp_step(ob_, x);
+            s_mma(x, *(const u32x4_t*)r_addr(qb_, x));
+            dp_mma(x, *(const u32x4_t*)r_addr(ob_, x));
           }
         }
         if (do_g) {
 #pragma unroll
           for (int x = 0; x < NG; ++x) {
-            dv_step(otb_, x);
-            dk_step(qtb_, x);
+            dv_mma(x, *(const u32x4_t*)i_addr(otb_, x));
+            dk_mma(x, *(const u32x4_t*)i_addr(qtb_, x));
           }
         }
       }
@@ -564,9 +570,6 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   constexpr int NKS = D / 16;
   constexpr int NS = NKS * NKB;          // S (and dP) products per tile
   constexpr int NQ = NKB * 2 * NDB;      // dQ products per tile
-  constexpr int KU = BC * D / 32;        // K staging units (8 keys x 4 columns)
-  constexpr int VLD = BC * KCH / 256;    // V staging chunks per thread
-  static_assert(KU <= 256 && VLD * 256 == BC * KCH && VLD <= 4, "staging shape");
   static_assert(NS == NQ, "matrix phase interleaves S, dP and dQ one to one");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KS];
@@ -619,59 +622,53 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int wave_end = CAUSAL ? min(N, qw + 32) : N;
   const int wave_tiles = (wave_end + BC - 1) / BC;
 
-  // ---- staging
+  // ---- staging (every thread of a group takes part: no divergent branches)
+  // K role: unit st = 8 keys x 2 columns: keys 16us + 4uh + {0..3} and
+  //   16us + 8 + 4uh + {0..3}, columns 2uc, 2uc + 1 (one dword per key)
+  // V role: 16-byte chunks ci = st + 256 r -> row ci / KCH, column ci % KCH
+  static_assert(BC * D / 16 == 256 && BC * KCH == 512, "two staging dwordx4 per thread");
   const rsrc_t tres = make_rsrc((grp == 0 ? K : V) + head_off, head_bytes);
-  u32x4_t stg[4];
-  // K role: unit st -> (16-key step us, half uh, 4-column chunk uc)
-  const bool kact = st < KU;
-  const int uc = st % (D / 4);
-  const int uh = (st / (D / 4)) & 1;
-  const int us = st / (D / 2);
-  const uint32_t koff = (uint32_t)(16 * us + 4 * uh) * RB + uc * 8;
-  const int krow0 = 16 * us + 4 * uh;  // rows krow0 + 8 (k / 4) + k % 4
-  const int kst = ((2 * us + uh) * D + 4 * uc) * 8;
-  // V role: chunk ci = st + 256 r -> row ci / KCH, column ci % KCH
+  u32x4_t stg[2];
+  const int uc = st % (D / 2);
+  const int uh = (st / (D / 2)) & 1;
+  const int us = st / D;
+  const int urow0 = 16 * us + 4 * uh;
+  const uint32_t uoff = (uint32_t)urow0 * RB + uc * 4;
+  const int ust = ((2 * us + uh) * D + 2 * uc) * 8;
   const uint32_t voff = (uint32_t)(st / KCH) * RB + (st % KCH) * 16;
   const int vst = (st / KCH) * KS + (st % KCH) * 8;
 
   auto load_tile = [&](int j0) {
     if (grp == 0) {
-      if (kact) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const u32x2_t x = buf_load8(tres, koff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB);
-          stg[k / 2][2 * (k % 2) + 0] = x[0];
-          stg[k / 2][2 * (k % 2) + 1] = x[1];
-        }
-      }
+      for (int k = 0; k < 8; ++k)
+        stg[k / 4][k % 4] = __builtin_amdgcn_raw_buffer_load_b32(
+            tres, uoff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB, 0, 0);
     } else {
 #pragma unroll
-      for (int r = 0; r < VLD; ++r) stg[r] = buf_load16(tres, voff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
+      for (int r = 0; r < 2; ++r) stg[r] = buf_load16(tres, voff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
     }
   };
-  // one quarter of the staging writes (part 0..3), so they can be spread out
+  // staging writes in four parts, so they can be spread between products
   auto store_part = [&](auto role, int j, int part) {
     if constexpr (decltype(role)::value == 0) {
-      if (kact) {
-        // row-major: rows 2 part and 2 part + 1 of the unit
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int k = 2 * part + e;
-          *(u32x2_t*)(&sK[j & 1][(krow0 + 8 * (k / 4) + (k % 4)) * KS + 4 * uc]) =
-              u32x2_t{stg[k / 2][2 * (k % 2) + 0], stg[k / 2][2 * (k % 2) + 1]};
-        }
-        // interleaved: column 4 uc + part
-        const int cc = part;
+      for (int e = 0; e < 2; ++e) {
+        const int k = 2 * part + e;
+        *(uint32_t*)(&sK[j & 1][(urow0 + 8 * (k / 4) + (k % 4)) * KS + 2 * uc]) = stg[k / 4][k % 4];
+      }
+      if (part & 1) {
+        const int cc = part >> 1;  // column 2uc + cc
         uint32_t o[4];
 #pragma unroll
         for (int kp = 0; kp < 4; ++kp) {
-          const uint32_t x0 = stg[kp][cc / 2], x1 = stg[kp][2 + cc / 2];
-          o[kp] = (cc & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
+          const uint32_t x0 = stg[kp / 2][2 * (kp % 2)], x1 = stg[kp / 2][2 * (kp % 2) + 1];
+          o[kp] = cc ? pack_hi(x0, x1) : pack_lo(x0, x1);
         }
-        *(u32x4_t*)(&sKt[j % 3][kst + 8 * cc]) = u32x4_t{o[0], o[1], o[2], o[3]};
+        *(u32x4_t*)(&sKt[j % 3][ust + 8 * cc]) = u32x4_t{o[0], o[1], o[2], o[3]};
       }
     } else {
-      if (part < VLD) *(u32x4_t*)(&sV[j & 1][vst + part * (256 / KCH) * KS]) = stg[part];
+      if ((part & 1) == 0) *(u32x4_t*)(&sV[j & 1][vst + (part >> 1) * (256 / KCH) * KS]) = stg[part >> 1];
     }
   };
   auto store_tile = [&](int j) {
@@ -687,19 +684,15 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // ---- products
   const int rfrag = l32 * KS + 8 * h;   // row-major fragment of this lane
   const int ifrag = (h * D + l32) * 8;  // interleaved fragment of this lane
-  auto s_step = [&](const uint16_t* kb_, int i) {
-    const int ks = i / NKB, kb = i % NKB;
-    s[kb] = TR::mfma(*(const u32x4_t*)(kb_ + 32 * kb * KS + 16 * ks), qf[ks], s[kb]);
-  };
-  auto dp_step = [&](const uint16_t* vb_, int i) {
-    const int ks = i / NKB, kb = i % NKB;
-    dp[kb] = TR::mfma(*(const u32x4_t*)(vb_ + 32 * kb * KS + 16 * ks), of[ks], dp[kb]);
-  };
-  auto dq_step = [&](const uint16_t* tb_, int i) {
+  auto s_addr = [&](const uint16_t* b_, int i) { return b_ + 32 * (i % NKB) * KS + 16 * (i / NKB); };
+  auto q_addr = [&](const uint16_t* b_, int i) { return b_ + ((2 * (i / NDB)) * D + 32 * (i % NDB)) * 8; };
+  auto s_mma = [&](int i, u32x4_t a) { s[i % NKB] = TR::mfma(a, qf[i / NKB], s[i % NKB]); };
+  auto dp_mma = [&](int i, u32x4_t a) { dp[i % NKB] = TR::mfma(a, of[i / NKB], dp[i % NKB]); };
+  auto dq_mma = [&](int i, u32x4_t a) {
     const int kt = i / NDB, db = i % NDB;
     const int kb = kt / 2, t = kt % 2;
-    const u32x4_t b = u32x4_t{dsk[kb][4 * t + 0], dsk[kb][4 * t + 1], dsk[kb][4 * t + 2], dsk[kb][4 * t + 3]};
-    acc[db] = TR::mfma(*(const u32x4_t*)(tb_ + ((2 * kt) * D + 32 * db) * 8), b, acc[db]);
+    acc[db] = TR::mfma(a, u32x4_t{dsk[kb][4 * t + 0], dsk[kb][4 * t + 1], dsk[kb][4 * t + 2], dsk[kb][4 * t + 3]},
+                       acc[db]);
   };
 
   // ---- prologue
@@ -727,16 +720,24 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         dp[kb] = zero16();
       }
       if (do_s && do_q) {
-        // steady state: S, dP, dQ products interleaved, staging writes between
-        // them (past the last tile they rewrite a buffer no one reads again)
+        // steady state: S, dP, dQ products interleaved in one pipelined run,
+        // staging writes between them (past the last tile they rewrite a
+        // buffer no one reads again)
         auto fused = [&](auto role) {
-#pragma unroll
-          for (int i = 0; i < NS; ++i) {
-            s_step(kb_, i);
-            dp_step(vb_, i);
-            dq_step(tb_, i);
-            if (i % (NS / 4) == NS / 8) store_part(role, j + 1, i / (NS / 4));
-          }
+          mma_pipeline<3 * NS, 3>(
+              [&](int k) {
+                const int i = k / 3;
+                return k % 3 == 0 ? s_addr(kb_, i) : k % 3 == 1 ? s_addr(vb_, i) : q_addr(tb_, i);
+              },
+              [&](int k, u32x4_t a) {
+                const int i = k / 3;
+                if (k % 3 == 0) s_mma(i, a);
+                else if (k % 3 == 1) dp_mma(i, a);
+                else dq_mma(i, a);
+              },
+              [&](int k) {
+                if (k % (3 * NS / 4) == 3 * NS / 8) store_part(role, j + 1, k / (3 * NS / 4));
+              });
         };
         if (grp == 0) fused(std::integral_constant<int, 0>{});
         else fused(std::integral_constant<int, 1>{});
@@ -745,13 +746,13 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         if (do_s) {
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
-            s_step(kb_, i);
-            dp_step(vb_, i);
+            s_mma(i, *(const u32x4_t*)s_addr(kb_, i));
+            dp_mma(i, *(const u32x4_t*)s_addr(vb_, i));
           }
         }
         if (do_q) {
 #pragma unroll
-          for (int i = 0; i < NQ; ++i) dq_step(tb_, i);
+          for (int i = 0; i < NQ; ++i) dq_mma(i, *(const u32x4_t*)q_addr(tb_, i));
         }
       }
       __builtin_amdgcn_s_setprio(0);

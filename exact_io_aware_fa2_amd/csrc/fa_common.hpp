@@ -131,6 +131,26 @@ __device__ inline void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// A straight-line run of NST matrix products, each taking its A operand from
+// LDS: operand k is read AHEAD products before its use, and `extra(k)` (LDS
+// staging writes and the like) runs after product k.  The scheduling barrier
+// after each product stops the compiler from regrouping the reads next to
+// their uses, so AHEAD reads stay in flight behind the matrix core.
+template <int NST, int AHEAD, class Addr, class Mma, class Extra>
+__device__ inline void mma_pipeline(Addr addr, Mma mma, Extra extra) {
+  u32x4_t fr[AHEAD];
+#pragma unroll
+  for (int x = 0; x < AHEAD; ++x) fr[x] = *(const u32x4_t*)addr(x);
+#pragma unroll
+  for (int k = 0; k < NST; ++k) {
+    const u32x4_t a = fr[k % AHEAD];
+    if (k + AHEAD < NST) fr[k % AHEAD] = *(const u32x4_t*)addr(k + AHEAD);
+    mma(k, a);
+    extra(k);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Wait until every vector-memory load issued so far has returned.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
