@@ -352,8 +352,11 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   // rows 16us + 4uh + {0..3} and 16us + 8 + 4uh + {0..3}, columns 2uc, 2uc + 1;
   // the row vector is loaded by all threads (rows st % 64, four copies).
   static_assert(BQ * D / 16 == 256, "one staging unit per thread");
-  const rsrc_t tres = make_rsrc((grp == 0 ? Q : dO) + head_off, head_bytes);
-  const rsrc_t vres = make_rsrc((grp == 0 ? LSE : Dvec) + (size_t)bh * N, (uint32_t)N * 4);
+  // one resource per tensor, uniform across the wave (see the forward)
+  const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
+  const rsrc_t ores = make_rsrc(dO + head_off, head_bytes);
+  const rsrc_t lres = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
+  const rsrc_t dres = make_rsrc(Dvec + (size_t)bh * N, (uint32_t)N * 4);
   const int uc = st % (D / 2);
   const int uh = (st / (D / 2)) & 1;
   const int us = st / D;
@@ -365,15 +368,25 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   float vreg = 0.0f;
 
   auto load_tile = [&](int i0) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      stg[k / 4][k % 4] = __builtin_amdgcn_raw_buffer_load_b32(
-          tres, uoff + (uint32_t)(i0 + 8 * (k / 4) + (k % 4)) * RB, 0, 0);
-    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                  vres, (uint32_t)(i0 + vrow) * 4, 0, 0));
     // rows past the end: LSE = +inf makes P = 0; D = 0
     const bool in = i0 + vrow < N;
-    vreg = grp == 0 ? (in ? x * kLog2e : INFINITY) : (in ? x : 0.0f);
+    if (grp == 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        stg[k / 4][k % 4] = __builtin_amdgcn_raw_buffer_load_b32(
+            qres, uoff + (uint32_t)(i0 + 8 * (k / 4) + (k % 4)) * RB, 0, 0);
+      const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                    lres, (uint32_t)(i0 + vrow) * 4, 0, 0));
+      vreg = in ? x * kLog2e : INFINITY;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        stg[k / 4][k % 4] = __builtin_amdgcn_raw_buffer_load_b32(
+            ores, uoff + (uint32_t)(i0 + 8 * (k / 4) + (k % 4)) * RB, 0, 0);
+      const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                    dres, (uint32_t)(i0 + vrow) * 4, 0, 0));
+      vreg = in ? x : 0.0f;
+    }
   };
   auto store_part = [&](int i, int part) {
     uint16_t* rowbuf = grp == 0 ? sQ[i & 1] : sO[i & 1];
@@ -627,7 +640,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   //   16us + 8 + 4uh + {0..3}, columns 2uc, 2uc + 1 (one dword per key)
   // V role: 16-byte chunks ci = st + 256 r -> row ci / KCH, column ci % KCH
   static_assert(BC * D / 16 == 256 && BC * KCH == 512, "two staging dwordx4 per thread");
-  const rsrc_t tres = make_rsrc((grp == 0 ? K : V) + head_off, head_bytes);
+  // one resource per tensor, uniform across the wave (see the forward)
+  const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
+  const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
   u32x4_t stg[2];
   const int uc = st % (D / 2);
   const int uh = (st / (D / 2)) & 1;
@@ -643,10 +658,10 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         stg[k / 4][k % 4] = __builtin_amdgcn_raw_buffer_load_b32(
-            tres, uoff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB, 0, 0);
+            kres, uoff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB, 0, 0);
     } else {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) stg[r] = buf_load16(tres, voff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
+      for (int r = 0; r < 2; ++r) stg[r] = buf_load16(vres, voff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
     }
   };
   // staging writes in four parts, so they can be spread between products

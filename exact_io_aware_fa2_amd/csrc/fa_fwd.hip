@@ -129,7 +129,10 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 
   // ---- staging: 4 x 16 bytes per thread in both roles.  Rows past the end of
   // the sequence read zeros (their scores are masked to -inf, so they add 0).
-  const rsrc_t tres = make_rsrc((grp == 0 ? K : V) + head_off, head_bytes);
+  // One resource per tensor: each is uniform across the wave (SGPRs); a
+  // resource selected by the (per-lane) group index would not be.
+  const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
+  const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
   u32x4_t stg[4];
   // K role: chunk ci = st + 256 r -> row ci / KCH, 16-byte column ci % KCH
   const uint32_t koff = (uint32_t)(st / KCH) * RB + (st % KCH) * 16;
@@ -144,11 +147,11 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   auto load_tile = [&](int j0) {
     if (grp == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) stg[r] = buf_load16(tres, koff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
+      for (int r = 0; r < 4; ++r) stg[r] = buf_load16(kres, koff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const u32x2_t x = buf_load8(tres, voff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB);
+        const u32x2_t x = buf_load8(vres, voff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB);
         stg[k / 2][2 * (k % 2) + 0] = x[0];
         stg[k / 2][2 * (k % 2) + 1] = x[1];
       }
