@@ -510,9 +510,9 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
         const int i0 = i_begin + i * BQ;
         const float* lv = sL[i % 3];
         const float* dv = sD[i % 3];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const bool need_mask = CAUSAL && i0 + 32 * qb < kw + 31;
+        // masked and unmasked variants as separate code (the mask is needed
+        // only where a query block crosses this wave's keys)
+        auto grad = [&](int qb, auto masked) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const float4 l4 = *(const float4*)(&lv[32 * qb + 8 * g + 4 * h]);
@@ -524,7 +524,8 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g + e;
               float pv = fast_exp2(fmaf(s[qb][r], c, -la[e]));
-              if (need_mask && key > i0 + 32 * qb + 8 * g + 4 * h + e) pv = 0.0f;
+              if constexpr (decltype(masked)::value)
+                if (key > i0 + 32 * qb + 8 * g + 4 * h + e) pv = 0.0f;
               p[e] = pv;
               ds[e] = pv * (dp[qb][r] - da[e]);
             }
@@ -533,6 +534,11 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
             dsk[qb][2 * g + 0] = TR::pack2(ds[0], ds[1]);
             dsk[qb][2 * g + 1] = TR::pack2(ds[2], ds[3]);
           }
+        };
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          if (wave_uniform(CAUSAL && i0 + 32 * qb < kw + 31)) grad(qb, std::true_type{});
+          else grad(qb, std::false_type{});
         }
       }
     }
@@ -777,23 +783,26 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       if (j + 2 < n_tiles) load_tile((j + 2) * BC);
       if (j < wave_tiles) {
         const int j0 = j * BC;
-        const bool need_mask = (CAUSAL && j0 + BC - 1 > qw) || j0 + BC > N;
+        auto grad = [&](auto masked) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            float d2[2];
+            for (int r = 0; r < 16; r += 2) {
+              float d2[2];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              float p = fast_exp2(fmaf(s[kb][r + e], c, -lq));
-              if (need_mask) {
-                const int key = j0 + 32 * kb + 8 * ((r + e) / 4) + 4 * h + ((r + e) % 4);
-                if (key >= N || (CAUSAL && key > qrow)) p = 0.0f;
+              for (int e = 0; e < 2; ++e) {
+                float p = fast_exp2(fmaf(s[kb][r + e], c, -lq));
+                if constexpr (decltype(masked)::value) {
+                  const int key = j0 + 32 * kb + 8 * ((r + e) / 4) + 4 * h + ((r + e) % 4);
+                  if (key >= N || (CAUSAL && key > qrow)) p = 0.0f;
+                }
+                d2[e] = p * (dp[kb][r + e] - dd);
               }
-              d2[e] = p * (dp[kb][r + e] - dd);
+              dsk[kb][r / 2] = TR::pack2(d2[0], d2[1]);
             }
-            dsk[kb][r / 2] = TR::pack2(d2[0], d2[1]);
-          }
+        };
+        if (wave_uniform((CAUSAL && j0 + BC - 1 > qw) || j0 + BC > N)) grad(std::true_type{});
+        else grad(std::false_type{});
       }
     }
     lds_barrier();

@@ -151,6 +151,10 @@ __device__ inline void mma_pipeline(Addr addr, Mma mma, Extra extra) {
   }
 }
 
+// A condition the same in every lane of the wave, made visibly uniform so the
+// compiler branches on it instead of predicating every guarded instruction.
+__device__ inline bool wave_uniform(bool x) { return __builtin_amdgcn_readfirstlane((int)x) != 0; }
+
 // Wait until every vector-memory load issued so far has returned.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -293,7 +293,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
       if (j + 2 < n_tiles) load_tile((j + 2) * BC);
       if (j < wave_tiles) {
         const int j0 = j * BC;
-        if ((CAUSAL && j0 + BC - 1 > qw) || j0 + BC > N) {
+        if (wave_uniform((CAUSAL && j0 + BC - 1 > qw) || j0 + BC > N)) {
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
