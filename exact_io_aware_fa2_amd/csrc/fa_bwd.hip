@@ -385,7 +385,7 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
             ores, uoff + (uint32_t)(i0 + 8 * (k / 4) + (k % 4)) * RB, 0, 0);
       const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                     dres, (uint32_t)(i0 + vrow) * 4, 0, 0));
-      vreg = in ? x : 0.0f;
+      vreg = in ? -x : 0.0f;  // stored negated: it initialises the dP accumulator
     }
   };
   auto store_part = [&](int i, int part) {
@@ -453,10 +453,20 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
       const uint16_t* ob_ = sO[i & 1] + rfrag;
       const uint16_t* qtb_ = sQt[(i + 2) % 3] + ifrag;  // step i-1
       const uint16_t* otb_ = sOt[(i + 2) % 3] + ifrag;
+      // dP accumulators start at -D_q, so they end as dP - D (one subtraction
+      // per element fewer in the vector phase)
+      const float* dneg = sD[i % 3];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         s[qb] = zero16();
-        dp[qb] = zero16();
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 d4 = *(const float4*)(&dneg[32 * qb + 8 * g + 4 * h]);
+          dp[qb][4 * g + 0] = d4.x;
+          dp[qb][4 * g + 1] = d4.y;
+          dp[qb][4 * g + 2] = d4.z;
+          dp[qb][4 * g + 3] = d4.w;
+        }
       }
       if (do_s && do_g) {
         // steady state: the four products interleaved in one pipelined run;
@@ -509,16 +519,13 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
       if (i >= first && i < n_steps) {
         const int i0 = i_begin + i * BQ;
         const float* lv = sL[i % 3];
-        const float* dv = sD[i % 3];
         // masked and unmasked variants as separate code (the mask is needed
         // only where a query block crosses this wave's keys)
         auto grad = [&](int qb, auto masked) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const float4 l4 = *(const float4*)(&lv[32 * qb + 8 * g + 4 * h]);
-            const float4 d4 = *(const float4*)(&dv[32 * qb + 8 * g + 4 * h]);
             const float la[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float da[4] = {d4.x, d4.y, d4.z, d4.w};
             float p[4], ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -527,7 +534,7 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
               if constexpr (decltype(masked)::value)
                 if (key > i0 + 32 * qb + 8 * g + 4 * h + e) pv = 0.0f;
               p[e] = pv;
-              ds[e] = pv * (dp[qb][r] - da[e]);
+              ds[e] = pv * dp[qb][r];  // dp already holds dP - D
             }
             pk[qb][2 * g + 0] = TR::pack2(p[0], p[1]);
             pk[qb][2 * g + 1] = TR::pack2(p[2], p[3]);
