@@ -14,7 +14,7 @@ the same workload.
 
 Modes
   (default)             the benchmark above
-  --profile             a few steps and no CPU baseline, for rocprofv3 runs;
+  --profile             3 warm-up + 20 timed steps, no CPU baseline, for rocprofv3 runs;
                         also runs a plain 1 GiB device copy (the calibration
                         kernel for FETCH_SIZE / WRITE_SIZE counters)
   --ingest-pmc F W      turn two rocprofv3 --pmc csv files (FETCH_SIZE, then
@@ -45,7 +45,7 @@ KERNEL_SOURCES = {
     "dq": ["fa_bwd.hip", "fa_common.hpp"],
 }
 # substrings of the mangled kernel names, as rocprofv3 reports them
-KERNEL_SYMBOLS = {"fwd": "fwd16_kernel", "prep": "bwd_pre_kernel", "dkdv": "bwd_dkdv_kernel",
+KERNEL_SYMBOLS = {"fwd": "fwd16_kernel", "prep": "bwd_pre_kernel", "dkdv": "bwd_dkdv",
                   "dq": "bwd_dq_kernel"}
 
 
@@ -200,7 +200,7 @@ def main():
     if w.dtype == "f32":
         raise SystemExit("the fwd+bwd step needs a 16-bit workload")
     if args.profile:
-        args.steps, args.warmup = min(args.steps, 5), min(args.warmup, 2)
+        args.steps, args.warmup = min(args.steps, 20), min(args.warmup, 3)
     dev = torch.device("cuda:0")
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
     inp = si.make_workload_inputs(w, backward=True)
