@@ -1,5 +1,6 @@
 // C-ABI entry points of libfa_mi355x.so: argument checks, then dispatch to the
 // kernel launchers.  Declarations and the contract are in include/fa.h.
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -30,6 +31,16 @@ int check_shape(int64_t B, int64_t H, int64_t N, int64_t d) {
 int check_scale(float scale) {
   if (!isfinite(scale) || scale < 0.0f) return FA_ERR_SCALE;
   return FA_OK;
+}
+
+// Factor turning a raw score into log2 units, scale * log2(e).  The kernels
+// mask a score by setting it to -inf before this multiplication, so the factor
+// must not be zero: scale = 0 uses the smallest normal float instead, which
+// leaves every finite score's contribution at 2^0 = 1 (uniform weights) and
+// keeps masked scores at -inf.
+float exp2_factor(float scale) {
+  const float c = scale * fa::kLog2eHost;
+  return c < FLT_MIN ? FLT_MIN : c;
 }
 
 }  // namespace
@@ -73,7 +84,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   a.BH = (int)(B * H);
   a.N = (int)N;
   a.d = (int)d;
-  a.c = scale * fa::kLog2eHost;
+  a.c = exp2_factor(scale);
   a.causal = causal != 0;
   a.dtype = dtype;
   a.stream = (hipStream_t)stream;
@@ -113,7 +124,7 @@ int bwd_common(fa::BwdArgs& a, const void* const* ptrs, int nptrs, const void* w
   a.N = (int)N;
   a.d = (int)d;
   a.scale = scale;
-  a.c = scale * fa::kLog2eHost;
+  a.c = exp2_factor(scale);
   a.causal = causal != 0;
   a.dtype = dtype;
   a.stream = (hipStream_t)stream;

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -57,6 +59,16 @@ struct BF16 {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), acc, false);
   }
+  // Register-class-pinned forms (see MfmaAsm below).
+  // All-VGPR forms (see MfmaAsm below): c += A B, and a fresh A B.
+  __device__ static inline void mma(f32x16_t& c, u32x4_t a, u32x4_t b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  }
+  __device__ static inline f32x16_t mma0(u32x4_t a, u32x4_t b) {
+    f32x16_t c;
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+    return c;
+  }
 };
 
 struct F16 {
@@ -78,7 +90,41 @@ struct F16 {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
                                   acc, false);
   }
+  // All-VGPR forms (see MfmaAsm below): c += A B, and a fresh A B.
+  __device__ static inline void mma(f32x16_t& c, u32x4_t a, u32x4_t b) {
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  }
+  __device__ static inline f32x16_t mma0(u32x4_t a, u32x4_t b) {
+    f32x16_t c;
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+    return c;
+  }
 };
+
+// MfmaAsm: TR::mma / TR::mma0 keep every operand and the result in VGPRs.
+// The compiler's own MFMA selection places accumulators in AGPRs whenever a
+// kernel needs many registers, which splits the register budget in halves
+// and costs copies for every vector access; with these forms a kernel can
+// use all of its registers as VGPRs (MFMA issue overlaps other waves' vector
+// work equally well with VGPR accumulators).  The compiler's hazard tracking
+// does not look inside inline assembly, so a kernel using these forms must
+// itself separate a matrix instruction's result from any vector-ALU access to
+// it by the required wait states: mfma_wait_v below, placed between the last
+// product and the first vector access of its result, with the result as
+// operands so that no access moves above the wait.  Back-to-back
+// accumulation into the same registers needs no wait states.
+#define FA_MFMA_WAIT "s_nop 7\n\ts_nop 7\n\ts_nop 4"
+__device__ __forceinline__ void mfma_wait_v(f32x16_t& a, f32x16_t& b) {
+  asm volatile(FA_MFMA_WAIT : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void mfma_wait_v(f32x16_t& a, f32x16_t& b, f32x16_t& c, f32x16_t& d) {
+  asm volatile(FA_MFMA_WAIT : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void mfma_wait_v(f32x16_t& a, f32x16_t& b, f32x16_t& c, f32x16_t& d,
+                                            f32x16_t& e, f32x16_t& f, f32x16_t& g, f32x16_t& h) {
+  asm volatile(FA_MFMA_WAIT : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
+}
+#undef FA_MFMA_WAIT
 
 __device__ inline f32x16_t mfma_f32(float a, float b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -149,6 +195,26 @@ __device__ inline void mma_pipeline(Addr addr, Mma mma, Extra extra) {
     extra(k);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, expanded at compile time (a
+// long straight-line schedule that a loop unroller might refuse to expand).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Materialise x here: an empty asm that "modifies" x keeps the computation of x
+// from being sunk past later branches towards its first use.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
+// max(a, b, c) without NaN canonicalisation of the inputs (v_maximum3_f32).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
 }
 
 // A condition the same in every lane of the wave, made visibly uniform so the

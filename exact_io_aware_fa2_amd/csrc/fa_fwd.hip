@@ -44,7 +44,496 @@ namespace fa {
 // denominator, so the result is unchanged mathematically.
 constexpr float kTau = 8.0f;
 
-// 16-bit forward.  8 wavefronts, two per SIMD, each owning 32 query rows.
+// Pipelined 16-bit forward: a row is re-based only when the sum of its
+// probabilities over one key tile exceeds this bound, so no single
+// probability (nor a packed fp16 value) can exceed it between re-bases.
+constexpr float kSumMax = 32768.0f;
+
+// 16-bit forward, software-pipelined (used for d = 128).  Two wavefronts
+// per SIMD (8 per workgroup), each owning QB = 1 block of 32 query rows.  Key
+// tiles of BC keys are processed as a software pipeline inside each
+// wavefront; iteration j issues
+//   matrix cores:  S_{j+1} = K_{j+1} Q^T   and   O += V_{j-1}^T P_{j-1}
+//   vector ALU:    softmax of S_j -> P_j
+// interleaved instruction by instruction (the two kinds of work are
+// independent within an iteration), plus the staging of later tiles.  Two
+// such wavefronts share each SIMD, so one's matrix instructions run under the
+// other's vector work.  One workgroup barrier per iteration hands the LDS
+// buffers over.
+//
+// Softmax: against a reference maximum m_run fixed by the first tile (its
+// exact row maximum), every score is read once (scale, shift, exp2, pack,
+// sum).  If a row's tile sum ever exceeds kSumMax its probabilities may be out
+// of range: the wavefront raises a flag and the workgroup redoes the whole
+// pass against exact row maxima computed directly from Q and K (every
+// probability is then at most 1).  So the steady state never re-bases O.
+//
+// Staging (all threads): iteration j writes K_{j+2} and V_j to LDS from
+// registers loaded during iteration j-1, then requests K_{j+3} and V_{j+1}.
+// Iteration j reads K_{j+1} and V_{j-1}, so two buffers of each suffice.
+//
+// LDS layouts (per buffer):
+//   K: row-major, rows padded to D + 8 elements, so 16 consecutive rows read
+//      at one 16-byte column fall in distinct banks and every fragment address
+//      is a fixed offset from one base.
+//   V: [key/16][h][d][8]: the 16-byte unit (s, h, c) holds column c of keys
+//      16s + 4h + {0,1,2,3} and 16s + 8 + 4h + {0,1,2,3}, exactly the eight
+//      values lane (c % 32, h) needs for one O^T += V^T P^T instruction.
+//      Within a row (s, h) column c sits at slot c ^ ((c >> 3) & 3), so the
+//      staging writes (lanes CW columns apart) and the fragment reads (lanes
+//      on consecutive columns) both hit distinct banks.
+//
+// All matrix operands and accumulators live in VGPRs (the MfmaAsm forms).
+template <class TR, int D, int BC, int QB, bool CAUSAL>
+__global__ __launch_bounds__(512 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB, 3 - QB)))
+void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                  const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                  float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c) {
+  // QB: 32-row query blocks per wavefront (2: one wavefront per SIMD, 1: two)
+  constexpr int NT = 512 / QB;          // threads per workgroup
+  constexpr int NW = NT / 64;           // wavefronts per workgroup
+  constexpr int BR = NW * 32 * QB;      // query rows per workgroup (256)
+  constexpr int KS = D + 8;             // padded K row (elements)
+  constexpr int NKB = BC / 32;          // 32-key blocks per tile
+  constexpr int NDB = D / 32;           // 32-column blocks of the output
+  constexpr int NKS = D / 16;           // k-steps of S over d
+  constexpr int NSS = BC / 16;          // k-steps of O over the keys of a tile
+  constexpr int NQF = NKB * NKS;        // K fragments per tile
+  constexpr int NVF = NSS * NDB;        // V fragments per tile
+  constexpr int NS = QB * (NQF + NVF);  // matrix instructions per iteration
+  constexpr int KCH = D / 8;            // 16-byte chunks per row
+  constexpr int NKC = BC * KCH / NT;    // K chunks staged per thread
+  constexpr int CW = BC * D / (8 * NT); // V columns staged per thread (8 keys each)
+  constexpr int NCG = D / CW;           // V column groups
+  constexpr uint32_t RB = D * 2;        // bytes per row
+  static_assert(NQF == NVF, "the two products alternate one to one");
+  static_assert(NKC >= 1 && (CW == 2 || CW == 4), "staging split over all threads");
+  constexpr int NBLK = QB * NKB;        // 32x32 score blocks per wavefront and tile
+  constexpr int NPAIR = NBLK * 8;       // packed probability pairs per lane and tile
+  // staging inside an iteration (step = one matrix instruction)
+  constexpr int kStg0 = 2;              // staging writes every other step from here
+  constexpr int kLoad = kStg0 + 2 * (NKC + CW);  // then the loads of later tiles
+  static_assert(kLoad < NS, "schedule fits one iteration");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const uint32_t lid = xcd_remap(blockIdx.x, total);
+  const int bh = lid / n_qtiles;
+  int qt = lid % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest tiles first
+  const int q0 = qt * BR;
+  const size_t head_off = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const int qw = q0 + 32 * QB * w;  // first query row of this wavefront
+
+  // Q rows as the B operand of S^T = K Q^T, loaded once (rows past the end
+  // read zeros; their results are never stored).
+  u32x4_t qf[QB][NKS];
+  {
+    const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        qf[qb][ks] = buf_load16(qres, (uint32_t)(qw + 32 * qb + l32) * RB + 32 * ks + 16 * h);
+  }
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+
+  // ---- staging.  Rows past the end of the sequence read zeros (their scores
+  // are masked, their values multiplied by zero probabilities).
+  const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
+  const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
+  u32x4_t stk[NKC];
+  uint32_t stv[8][CW / 2];
+  // K: chunk tid + NT r -> row (tid / KCH) + (NT / KCH) r, 16-byte column tid % KCH
+  const uint32_t koff = (uint32_t)(tid / KCH) * RB + (tid % KCH) * 16;
+  const int kst = (tid / KCH) * KS + (tid % KCH) * 8;
+  // V: unit tid -> (16-key step vs, half vh, column group vc); 8 rows x CW columns
+  const int vc = tid % NCG;
+  const int vh = (tid / NCG) & 1;
+  const int vs = tid / (2 * NCG);
+  const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * RB + vc * CW * 2;
+  const int vrow = (2 * vs + vh) * D * 8;
+  const int vsw = (CW * vc) ^ ((CW * vc >> 3) & 3);  // swizzled slot of column CW vc (+ cc: xor)
+
+  auto load_k = [&](int tile) {
+#pragma unroll
+    for (int r = 0; r < NKC; ++r)
+      stk[r] = buf_load16(kres, koff + (uint32_t)(tile * BC + (NT / KCH) * r) * RB);
+  };
+  auto load_v = [&](int tile) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t off = voff + (uint32_t)(tile * BC + 8 * (k / 4) + (k % 4)) * RB;
+      if constexpr (CW == 4) {
+        const u32x2_t x = buf_load8(vres, off);
+        stv[k][0] = x[0];
+        stv[k][1] = x[1];
+      } else {
+        stv[k][0] = __builtin_amdgcn_raw_buffer_load_b32(vres, off, 0, 0);
+      }
+    }
+  };
+  // staging write number i (0 <= i < NKC + CW) into buffer b
+  auto store_part = [&](int i, int b) __attribute__((always_inline)) {
+    if (i < NKC) {
+      *(u32x4_t*)(&sK[b][kst + i * (NT / KCH) * KS]) = stk[i];
+    } else {
+      const int cc = i - NKC;  // column within the group
+      uint32_t o[4];
+#pragma unroll
+      for (int kp = 0; kp < 4; ++kp) {
+        const uint32_t x0 = stv[2 * kp][cc / 2], x1 = stv[2 * kp + 1][cc / 2];
+        o[kp] = (cc & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
+      }
+      *(u32x4_t*)(&sV[b][vrow + 8 * (vsw ^ cc)]) = u32x4_t{o[0], o[1], o[2], o[3]};
+    }
+  };
+
+  // ---- per-lane state
+  const int kfrag = l32 * KS + 8 * h;   // element offset of this lane's K fragment
+  const int vfrag = (h * D + (l32 ^ ((l32 >> 3) & 3))) * 8;  // this lane's V fragment
+  f32x16_t acc[QB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[qb][db] = zero16();
+  f32x16_t sA[QB][NKB], sB[QB][NKB];      // scores of two consecutive tiles
+  // packed probabilities of two tiles: [qb][kb][t] is the B operand of the
+  // O product for the keys 32 kb + 16 t + ...
+  u32x4_t pA[QB][NKB][2], pB[QB][NKB][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) pB[qb][kb][0] = pB[qb][kb][1] = u32x4_t{0u, 0u, 0u, 0u};
+  float m_run[QB], lsum[QB][NKB], ltsum[QB][NKB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) lsum[qb][kb] = ltsum[qb][kb] = 0.0f;
+  }
+
+  // fragment addresses: QK fragment i -> (kb, ks); PV fragment i -> (k-step, db)
+  auto kaddr = [&](int b, int i) -> const uint16_t* {
+    return sK[b] + kfrag + 32 * (i % NKB) * KS + 16 * (i / NKB);
+  };
+  auto vaddr = [&](int b, int i) -> const uint16_t* {
+    return sV[b] + vfrag + (2 * (i / NDB) * D + 32 * (i % NDB)) * 8;
+  };
+  auto pfrag = [&](const u32x4_t (&p)[QB][NKB][2], int qb, int ss) -> u32x4_t { return p[qb][ss / 2][ss % 2]; };
+  // All score blocks of one register set, or all O accumulators, as operands
+  // of a hazard wait (matrix result -> vector access).
+  auto wait_scores = [&](f32x16_t (&sc)[QB][NKB]) __attribute__((always_inline)) {
+    f32x16_t* x = &sc[0][0];  // QB * NKB blocks
+    static_assert(QB * NKB == 2 || QB * NKB == 4, "operand list below");
+    if constexpr (QB * NKB == 2) mfma_wait_v(x[0], x[1]);
+    else mfma_wait_v(x[0], x[1], x[2], x[3]);
+  };
+  auto wait_acc = [&]() __attribute__((always_inline)) {
+    f32x16_t* x = &acc[0][0];  // QB * NDB blocks
+    static_assert(QB * NDB == 2 || QB * NDB == 4 || QB * NDB == 8, "operand list below");
+    if constexpr (QB * NDB == 2) mfma_wait_v(x[0], x[1]);
+    else if constexpr (QB * NDB == 4) mfma_wait_v(x[0], x[1], x[2], x[3]);
+    else mfma_wait_v(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+  };
+
+  bool rerun = false;
+  bool exact = false;  // second pass: m_run holds exact row maxima
+  // ---- one pipelined iteration.  PAR = j & 1 selects register sets and
+  // buffers; MASKED tiles (crossing the causal diagonal or the end of the
+  // sequence) mask scores as they are read.
+  auto iteration = [&](auto par, auto masked, int j) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    constexpr bool MASKED = decltype(masked)::value;
+    f32x16_t(&s_cur)[QB][NKB] = PAR ? sB : sA;
+    f32x16_t(&s_next)[QB][NKB] = PAR ? sA : sB;
+    u32x4_t(&p_prev)[QB][NKB][2] = PAR ? pA : pB;
+    u32x4_t(&p_cur)[QB][NKB][2] = PAR ? pB : pA;
+    constexpr int RD = 1 - PAR;  // buffers read: K_{j+1}, V_{j-1}
+    constexpr int WR = PAR;      // buffers written: K_{j+2}, V_j
+    const int j0 = j * BC;
+    wait_scores(s_cur);  // S_j was produced by matrix instructions
+
+    // score r of block (qb, kb), -inf where masked
+    auto score = [&](int qb, int kb, int r) __attribute__((always_inline)) -> float {
+      const float x = s_cur[qb][kb][r];
+      if constexpr (MASKED) {
+        const int key = j0 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
+        return (key >= N || (CAUSAL && key > qw + 32 * qb + l32)) ? -INFINITY : x;
+      }
+      return x;
+    };
+
+    // Softmax of S_j against the current reference maximum m_run, as a
+    // software pipeline over the steps: pair i of scores (two adjacent values
+    // of one block) enters at step kStart(i) and advances one stage per step,
+    //   stage 0: scale and shift (fma)    stage 1: exp2
+    //   stage 2: pack, fp32 sums          stage 3: 16-bit sums, keep P
+    // so the instructions of one step never depend on each other.  No row
+    // maximum is needed on this path: if a row's tile sum exceeds 2^kSumMax
+    // (or is not finite: the first tile), every term may be large, and the
+    // slow path below re-bases the row and redoes the tile.
+    if (j == 0 && !exact) {
+      // first tile: its exact row maximum (over both half-waves) is the
+      // reference; finite, as key 0 is visible to every row
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) mx = max3f(mx, score(qb, kb, r), score(qb, kb, r + 1));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
+                                                         __builtin_bit_cast(uint32_t, mx), false, false);
+        m_run[qb] = __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)sw[0]),
+                                                  __builtin_bit_cast(float, (uint32_t)sw[1])) * c;
+      }
+    }
+    float tl[QB][NKB], tlt[QB][NKB];
+    float mneg[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mneg[qb] = -m_run[qb];
+    float ta[NPAIR][2], te[NPAIR][2];
+    uint32_t tp[NPAIR];
+    auto stage = [&](int i, int k) __attribute__((always_inline)) {
+      const int b = i % NBLK, rp = i / NBLK;
+      const int qb = b / NKB, kb = b % NKB;
+      if (k == 0) {
+        ta[i][0] = fmaf(score(qb, kb, 2 * rp), c, mneg[qb]);
+        ta[i][1] = fmaf(score(qb, kb, 2 * rp + 1), c, mneg[qb]);
+      } else if (k == 1) {
+        te[i][0] = fast_exp2(ta[i][0]);
+        te[i][1] = fast_exp2(ta[i][1]);
+      } else if (k == 2) {
+        tp[i] = TR::pack2(te[i][0], te[i][1]);
+        tl[qb][kb] = rp == 0 ? te[i][0] + te[i][1] : tl[qb][kb] + (te[i][0] + te[i][1]);
+      } else {
+        tlt[qb][kb] = TR::sum2(tp[i], rp == 0 ? 0.0f : tlt[qb][kb]);
+        pin(tp[i]);
+        p_cur[qb][kb][rp / 4][rp % 4] = tp[i];
+        if (rp == 7) {
+          pin(tl[qb][kb]);
+          pin(tlt[qb][kb]);
+        }
+      }
+    };
+    auto valu = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NPAIR; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (i * NS / NPAIR + k == st) stage(i, k);
+      // staging: writes of K_{j+2} and V_j, then requests for K_{j+3}, V_{j+1}
+      if (st == kStg0) wait_vmem();
+      if (st >= kStg0 && st < kLoad && (st - kStg0) % 2 == 0) store_part((st - kStg0) / 2, WR);
+      if (st == kLoad) {
+        load_k(j + 3);
+        load_v(j + 1);
+      }
+    };
+
+    // matrix instructions: fragment f (even: V fragment of O += V^T P, odd:
+    // K fragment of S) feeds QB products; operand reads run kAhead fragments
+    // ahead.  Steps past NS only finish the softmax pipeline.
+    constexpr int kAhead = 3;
+    constexpr int NF = NQF + NVF;
+    auto is_pv = [](int f) { return (f & 1) == 0; };
+    auto fidx = [](int f) { return f >> 1; };
+    auto faddr = [&](int f) -> const uint16_t* {
+      return is_pv(f) ? vaddr(RD, fidx(f)) : kaddr(RD, fidx(f));
+    };
+    u32x4_t fr[kAhead];
+#pragma unroll
+    for (int x = 0; x < kAhead; ++x) fr[x] = *(const u32x4_t*)faddr(x);
+    static_for<0, NS + 3>([&](auto stc) __attribute__((always_inline)) {
+      constexpr int st = decltype(stc)::value;
+      if constexpr (st < NS) {
+        constexpr int f = st / QB, qb = st % QB;
+        const u32x4_t a = fr[f % kAhead];
+        if constexpr (qb == QB - 1 && f + kAhead < NF) fr[f % kAhead] = *(const u32x4_t*)faddr(f + kAhead);
+        constexpr int i = fidx(f);
+        if constexpr (is_pv(f)) {
+          constexpr int ss = i / NDB, db = i % NDB;
+          TR::mma(acc[qb][db], a, pfrag(p_prev, qb, ss));
+        } else {
+          constexpr int kb = i % NKB, ks = i / NKB;
+          if constexpr (ks == 0) s_next[qb][kb] = TR::mma0(a, qf[qb][ks]);
+          else TR::mma(s_next[qb][kb], a, qf[qb][ks]);
+        }
+      }
+      valu(st);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+
+    // Tile row sums over both half-waves (the swap leaves the two halves'
+    // values in the two results, in some order, in every lane).
+    bool big = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float t = tl[qb][0];
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb) t += tl[qb][kb];
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, t),
+                                                       __builtin_bit_cast(uint32_t, t), false, false);
+      t = __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
+      big |= !(t <= kSumMax);
+    }
+    rerun |= big;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        lsum[qb][kb] += tl[qb][kb];
+        ltsum[qb][kb] += tlt[qb][kb];
+      }
+    lds_barrier();
+  };
+  // ---- one pass over the keys
+  auto run_pass = [&]() __attribute__((always_inline)) {
+    // ---- prologue: K_0, K_1 in LDS, V buffer 1 zeroed (iteration 0 multiplies
+    // it by the zero probabilities pB), S_0 computed, K_2 and V_0 requested.
+  #pragma unroll
+    for (int i = 0; i < CW; ++i) *(u32x4_t*)(&sV[1][(tid + NT * i) * 8]) = u32x4_t{0u, 0u, 0u, 0u};
+    load_k(0);
+    wait_vmem();  // Q fragments and K_0
+  #pragma unroll
+    for (int i = 0; i < NKC; ++i) store_part(i, 0);
+    load_k(1);
+    wait_vmem();
+  #pragma unroll
+    for (int i = 0; i < NKC; ++i) store_part(i, 1);
+    lds_barrier();
+    mma_pipeline<NQF, 3>([&](int i) { return kaddr(0, i); },
+                         [&](int i, u32x4_t a) {
+                           const int kb = i % NKB, ks = i / NKB;
+  #pragma unroll
+                           for (int qb = 0; qb < QB; ++qb) {
+                             if (ks == 0) sA[qb][kb] = TR::mma0(a, qf[qb][ks]);
+                             else TR::mma(sA[qb][kb], a, qf[qb][ks]);
+                           }
+                         },
+                         [](int) {});
+    load_k(2);
+    load_v(0);
+    lds_barrier();  // every wave is done with K_0 before iteration 0 overwrites it
+
+    // Tiles are processed in pairs (the two register sets), over an even number
+    // of tiles: a padding tile past the last one is fully masked (its keys lie
+    // past the end of the sequence or, causally, past every row of this
+    // workgroup) and contributes nothing.  The leading tiles whose keys are all
+    // visible to every row of this wavefront run without masking; the rest
+    // (the causal diagonal, the ragged end) mask scores as they are read.
+    const int n_iter = (n_tiles + 1) & ~1;
+    int n_open = N / BC;
+    if (CAUSAL) n_open = min(n_open, (qw + 1) / BC);
+    n_open = __builtin_amdgcn_readfirstlane(min(n_open, n_tiles) & ~1);
+    int j = 0;
+    for (; j < n_open; j += 2) {
+      iteration(std::integral_constant<int, 0>{}, std::false_type{}, j);
+      iteration(std::integral_constant<int, 1>{}, std::false_type{}, j + 1);
+    }
+    for (; j < n_iter; j += 2) {
+      iteration(std::integral_constant<int, 0>{}, std::true_type{}, j);
+      iteration(std::integral_constant<int, 1>{}, std::true_type{}, j + 1);
+    }
+
+    // last tile (odd index): O += V^T P from register set B and V buffer 1
+    mma_pipeline<NVF, 3>([&](int i) { return vaddr(1, i); },
+                         [&](int i, u32x4_t a) {
+                           const int ss = i / NDB, db = i % NDB;
+  #pragma unroll
+                           for (int qb = 0; qb < QB; ++qb) TR::mma(acc[qb][db], a, pfrag(pB, qb, ss));
+                         },
+                         [](int) {});
+  };
+
+  // Did a row of this workgroup need a new reference maximum?  (Rare: only
+  // when a row maximum grows by about log2(kSumMax / BC) or more after its
+  // first tile.)  Then every wavefront computes its rows' exact maxima
+  // directly from Q and K, and the pass is redone against them.
+  __shared__ int s_rerun[NW];
+  for (;;) {
+    run_pass();
+    if (exact) break;
+    if (lane == 0) s_rerun[w] = __builtin_amdgcn_ballot_w64(rerun) != 0;
+    lds_barrier();
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) any |= s_rerun[i] != 0;
+    if (!any) break;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = qw + 32 * qb + l32;
+      const int kend = CAUSAL ? min(N, qw + 32 * qb + 32) : N;
+      float mx = -INFINITY;
+      for (int k0 = 0; k0 < kend; k0 += 32) {
+        const uint32_t ko = (uint32_t)(k0 + l32) * RB + 16 * h;
+        f32x16_t sc = TR::mma0(buf_load16(kres, ko), qf[qb][0]);
+#pragma unroll
+        for (int ks = 1; ks < NKS; ++ks) TR::mma(sc, buf_load16(kres, ko + 32 * ks), qf[qb][ks]);
+        f32x16_t sc2 = sc;
+        mfma_wait_v(sc, sc2);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 8 * (r / 4) + 4 * h + (r % 4);
+          if (!(key >= N || (CAUSAL && key > row))) mx = __builtin_elementwise_maximum(mx, sc[r]);
+        }
+      }
+      mx = __builtin_elementwise_maximum(mx, swap_halves(mx));
+      m_run[qb] = mx * c;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[qb][db] = zero16();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        lsum[qb][kb] = ltsum[qb][kb] = 0.0f;
+        pB[qb][kb][0] = pB[qb][kb][1] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+    exact = true;
+  }
+  wait_acc();
+
+  // epilogue: normalise once, store O and LSE
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float l = 0.0f, lt = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      l += lsum[qb][kb];
+      lt += ltsum[qb][kb];
+    }
+    l += swap_halves(l);
+    lt += swap_halves(lt);
+    const float inv = 1.0f / lt;
+    const int qrow = qw + 32 * qb + l32;
+    if (qrow < N) {
+      uint16_t* orow = O + head_off + (size_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = 32 * db + 8 * g + 4 * h;
+          const uint32_t w0 = TR::pack2(acc[qb][db][4 * g + 0] * inv, acc[qb][db][4 * g + 1] * inv);
+          const uint32_t w1 = TR::pack2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv);
+          *(u32x2_t*)(orow + col) = u32x2_t{w0, w1};
+        }
+      if (h == 0) LSE[(size_t)bh * N + qrow] = (m_run[qb] + __log2f(l)) * kLn2;
+    }
+  }
+}
+
+// 16-bit forward, phase ping-pong (used for d = 64).  8 wavefronts, two per
+// SIMD, each owning 32 query rows.
 // Every wavefront alternates two phases per key tile j:
 //   M-phase j: S_j = K_j Q^T  and  O += V_{j-1}^T P_{j-1}   (matrix cores)
 //   V-phase j: online softmax of S_j -> P_j                (vector ALU)
@@ -65,9 +554,11 @@ constexpr float kTau = 8.0f;
 //   V: [key/16][h][d][8]: the 16-byte unit (s, h, c) holds column c of keys
 //      16s + 4h + {0,1,2,3} and 16s + 8 + 4h + {0,1,2,3}, exactly the eight
 //      values lane (c % 32, h) needs for one O^T += V^T P^T instruction.
+//      Column c sits at slot c ^ ((c >> 3) & 3) of its row (bank-conflict-
+//      free staging writes and fragment reads).
 template <class TR, int D, int BC, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                   float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c) {
   constexpr int NW = 8;                     // wavefronts per workgroup
@@ -143,6 +634,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
   const int vs = st / (D / 2);
   const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * RB + vc * 8;
   const int vst = ((2 * vs + vh) * D + 4 * vc) * 8;
+  const int vsw = (vc >> 1) & 3;  // slot swizzle of this thread's four columns
 
   auto load_tile = [&](int j0) {
     if (grp == 0) {
@@ -171,7 +663,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
         const uint32_t a = stg[kp][cc / 2], b = stg[kp][2 + cc / 2];
         o[kp] = (cc & 1) ? pack_hi(a, b) : pack_lo(a, b);
       }
-      *(u32x4_t*)(&sV[buf][vst + 8 * cc]) = u32x4_t{o[0], o[1], o[2], o[3]};
+      *(u32x4_t*)(&sV[buf][vst + 8 * (cc ^ vsw)]) = u32x4_t{o[0], o[1], o[2], o[3]};
     }
   };
   auto store_tile = [&](int j) {  // tile j into its buffer
@@ -181,7 +673,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
 
   // ---- matrix products
   const int kfrag = l32 * KS + 8 * h;  // element offset of this lane's K fragment
-  const int vfrag = (h * D + l32) * 8;  // element offset of this lane's V fragment
+  const int vfrag = (h * D + (l32 ^ ((l32 >> 3) & 3))) * 8;  // this lane's V fragment
   auto qk_step = [&](const uint16_t* kb_, int i) {  // i-th of NQK: ks = i / NKB, kb = i % NKB
     const int ks = i / NKB, kb = i % NKB;
     const u32x4_t kf = *(const u32x4_t*)(kb_ + 32 * kb * KS + 16 * ks);
@@ -267,7 +759,7 @@ void fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K
                   const uint32_t x0 = stg[kp][cc / 2], x1 = stg[kp][2 + cc / 2];
                   o[kp] = (cc & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
                 }
-                *(u32x4_t*)(&sV[(j + 1) % 3][vst + 8 * cc]) = u32x4_t{o[0], o[1], o[2], o[3]};
+                *(u32x4_t*)(&sV[(j + 1) % 3][vst + 8 * (cc ^ vsw)]) = u32x4_t{o[0], o[1], o[2], o[3]};
               }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -466,12 +958,23 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float* __restrict__ Q,
 
 // ------------------------------------------------------------------ launch
 
-template <class TR, int D, int BC, bool CAUSAL>
-static hipError_t launch16(const FwdArgs& a) {
+template <class TR, bool CAUSAL>
+static hipError_t launch_pipe(const FwdArgs& a) {  // d = 128
   constexpr int BR = 256;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((fwd16_kernel<TR, D, BC, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
+  hipLaunchKernelGGL((fwd16_pipe_kernel<TR, 128, 64, 1, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c);
+  return hipGetLastError();
+}
+
+template <class TR, bool CAUSAL>
+static hipError_t launch_pp(const FwdArgs& a) {  // d = 64
+  constexpr int BR = 256;
+  const int n_qtiles = (a.N + BR - 1) / BR;
+  const uint32_t total = (uint32_t)(n_qtiles * a.BH);
+  hipLaunchKernelGGL((fwd16_pp_kernel<TR, 64, 128, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c);
   return hipGetLastError();
@@ -489,8 +992,8 @@ static hipError_t launch32(const FwdArgs& a) {
 
 template <class TR>
 static hipError_t dispatch16(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch16<TR, 128, 64, true>(a) : launch16<TR, 128, 64, false>(a);
-  return a.causal ? launch16<TR, 64, 128, true>(a) : launch16<TR, 64, 128, false>(a);
+  if (a.d == 128) return a.causal ? launch_pipe<TR, true>(a) : launch_pipe<TR, false>(a);
+  return a.causal ? launch_pp<TR, true>(a) : launch_pp<TR, false>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {

@@ -18,10 +18,10 @@ from parity import TOL, assert_fwd_ok, fwd_errors, gpu_fwd, say
 pytestmark = pytest.mark.gpu
 
 
-def _small(B, H, N, d, dtype, causal, seed, sigma=1.0):
+def _small(B, H, N, d, dtype, causal, seed, sigma=1.0, scale=None):
     inp = si.make_inputs(B, H, N, d, dtype, sigma, seed)
-    scale = 1.0 / np.sqrt(d)
-    say(f"fwd small B{B} H{H} N{N} d{d} {dtype} causal={causal} seed={seed}")
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    say(f"fwd small B{B} H{H} N{N} d{d} {dtype} causal={causal} seed={seed} scale={scale}")
     q, k, v, o, lse = gpu_fwd(inp, dtype, causal, scale)
     o_ref, lse_ref = attention_fwd(inp["q"][0], inp["k"][0], inp["v"][0], scale, causal)
     err = fwd_errors(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
@@ -34,6 +34,14 @@ def _small(B, H, N, d, dtype, causal, seed, sigma=1.0):
 @pytest.mark.parametrize("N", [1, 17, 255, 257, 1000])
 def test_small_shapes_and_tails(N, causal, d, dtype):
     _small(1, 2, N, d, dtype, causal, seed=7000 + N + d)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale(causal, dtype):
+    # scale 0: every visible key has the same weight (O is the mean of the
+    # visible V rows, LSE the log of their count); masked keys must stay out
+    _small(1, 2, 300, 64, dtype, causal, seed=91, scale=0.0)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
