@@ -45,7 +45,7 @@ KERNEL_SOURCES = {
     "dq": ["fa_bwd.hip", "fa_common.hpp"],
 }
 # substrings of the mangled kernel names, as rocprofv3 reports them
-KERNEL_SYMBOLS = {"fwd": "fwd16_kernel", "prep": "bwd_pre_kernel", "dkdv": "bwd_dkdv",
+KERNEL_SYMBOLS = {"fwd": "fwd16_p", "prep": "bwd_pre_kernel", "dkdv": "bwd_dkdv",
                   "dq": "bwd_dq_kernel"}
 
 
