@@ -13,23 +13,24 @@
 // rows without exchanging partial results through shared memory.
 //
 // gfx950 mapping (16-bit inputs):
-//   * workgroup = 4 wavefronts x QB blocks of 32 query rows; grid = query
+//   * workgroup = 8 wavefronts (two per SIMD) x 32 query rows; grid = query
 //     tiles x (batch * heads), XCD-grouped, heaviest causal tiles first.
 //   * each wavefront computes S^T = K Q^T with v_mfma_f32_32x32x16: the
 //     accumulator then holds, per lane, one query row (lane % 32) and 16 keys,
-//     so row max / row sum are in-lane plus one exchange between half-waves,
+//     so row reductions are in-lane plus one exchange between half-waves,
 //     and the probabilities are already in the B-operand layout of
 //     O^T += V^T P^T (they never leave registers).
-//   * K and V tiles of 64 keys are staged HBM -> registers -> LDS with 16-byte
-//     coalesced loads, double buffered (the next tile is in flight while the
-//     current one is consumed).  K is stored row-major with an XOR swizzle of
-//     its 16-byte chunks; V is stored as groups of 4 keys per column
-//     ([key/4][d][4]) so the V^T operand is two 8-byte LDS reads per lane.
-//   * softmax in the exp2 domain with scale*log2(e) folded into one FMA; the
-//     output is rescaled only when a row maximum grows by more than kTau (in
-//     log2 units), and normalised once at the end (deferred rescaling).
-//   * causal: key tiles above the diagonal are never loaded or multiplied;
-//     only tiles crossing the diagonal are masked.
+//   * K and V tiles are staged HBM -> registers -> LDS with coalesced loads
+//     while earlier tiles are consumed; K row-major (padded rows), V in an
+//     interleaved, bank-swizzled layout that is one 16-byte read per product.
+//   * softmax in the exp2 domain with scale*log2(e) folded into one FMA and a
+//     single normalisation at the end.  Two kernels: fwd16_pipe_kernel (d =
+//     128) software-pipelines matrix and vector work inside each wavefront
+//     against a fixed reference maximum; fwd16_pp_kernel (d = 64) alternates
+//     whole matrix and vector phases between the two wavefronts of a SIMD
+//     with lazy re-basing of the maximum.
+//   * causal: key tiles above a workgroup's diagonal are never loaded or
+//     multiplied; only tiles crossing the diagonal are masked.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -37,16 +38,17 @@
 
 namespace fa {
 
-// A row maximum is only re-based when it grows by more than kTau (log2 units).
-// Between re-bases probabilities are bounded by 2^kTau, which bf16/fp16 and
-// the fp32 accumulators hold without loss of relative precision; the final
-// normalisation uses the same reference maximum for numerator and
-// denominator, so the result is unchanged mathematically.
+// Ping-pong kernel: a row maximum is only re-based when it grows by more than
+// kTau (log2 units).  Between re-bases probabilities are bounded by 2^kTau,
+// which bf16/fp16 and the fp32 accumulators hold without loss of relative
+// precision; the final normalisation uses the same reference maximum for
+// numerator and denominator, so the result is unchanged mathematically.
 constexpr float kTau = 8.0f;
 
-// Pipelined 16-bit forward: a row is re-based only when the sum of its
-// probabilities over one key tile exceeds this bound, so no single
-// probability (nor a packed fp16 value) can exceed it between re-bases.
+// Pipelined kernel: the reference maximum stays fixed unless the sum of a
+// row's probabilities over one key tile exceeds this bound (then the pass is
+// redone against exact row maxima); no single probability, nor a packed fp16
+// value, can exceed it.
 constexpr float kSumMax = 32768.0f;
 
 // 16-bit forward, software-pipelined (used for d = 128).  Two wavefronts
@@ -274,15 +276,14 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
       return x;
     };
 
-    // Softmax of S_j against the current reference maximum m_run, as a
-    // software pipeline over the steps: pair i of scores (two adjacent values
-    // of one block) enters at step kStart(i) and advances one stage per step,
+    // Softmax of S_j against the reference maximum m_run, as a software
+    // pipeline over the steps: pair i of scores (two adjacent values of one
+    // block) enters at step i * NS / NPAIR and advances one stage per step,
     //   stage 0: scale and shift (fma)    stage 1: exp2
     //   stage 2: pack, fp32 sums          stage 3: 16-bit sums, keep P
     // so the instructions of one step never depend on each other.  No row
-    // maximum is needed on this path: if a row's tile sum exceeds 2^kSumMax
-    // (or is not finite: the first tile), every term may be large, and the
-    // slow path below re-bases the row and redoes the tile.
+    // maximum is searched here: a row whose tile sum exceeds kSumMax (its
+    // maximum grew a lot since the first tile) raises `rerun` below.
     if (j == 0 && !exact) {
       // first tile: its exact row maximum (over both half-waves) is the
       // reference; finite, as key 0 is visible to every row
