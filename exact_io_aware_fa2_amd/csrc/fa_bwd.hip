@@ -59,216 +59,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 
 // ------------------------------------------------------------------ dK, dV
 
-template <class TR, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                     const float* __restrict__ LSE, const float* __restrict__ Dvec,
-                     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_ktiles,
-                     uint32_t total, float c, float scale) {
-  constexpr int BKV = 128;          // keys per workgroup (4 wavefronts x 32)
-  constexpr int BQ = 64;            // query rows per step
-  constexpr int KCH = D / 8;
-  constexpr int NKS = D / 16;
-  constexpr int NDB = D / 32;
-  constexpr int UNITS = (BQ / 4) * KCH;       // 4-row x 1-chunk staging units
-  constexpr int ULOADS = (UNITS + 255) / 256;
-
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sdOt[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
-  __shared__ __attribute__((aligned(16))) float sD[2][BQ];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int h = lane >> 5;
-  const int l32 = lane & 31;
-
-  const uint32_t lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / n_ktiles;
-  const int kt = lid % n_ktiles;
-  const int k0 = kt * BKV;
-  const int kw = k0 + 32 * w;  // first key of this wavefront
-  const size_t head_off = (size_t)bh * N * D;
-  const uint16_t* Qh = Q + head_off;
-  const uint16_t* dOh = dO + head_off;
-  const float* Lh = LSE + (size_t)bh * N;
-  const float* Dh = Dvec + (size_t)bh * N;
-
-  // K and V rows of this wavefront as B operands (column = key = lane % 32)
-  u32x4_t kf[NKS], vf[NKS];
-  {
-    const int key = kw + l32;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (key < N) {
-        kf[ks] = *(const u32x4_t*)(K + head_off + (size_t)key * D + 16 * ks + 8 * h);
-        vf[ks] = *(const u32x4_t*)(V + head_off + (size_t)key * D + 16 * ks + 8 * h);
-      } else {
-        kf[ks] = u32x4_t{0, 0, 0, 0};
-        vf[ks] = u32x4_t{0, 0, 0, 0};
-      }
-    }
-  }
-  f32x16_t acc_dk[NDB], acc_dv[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    acc_dk[db] = zero16();
-    acc_dv[db] = zero16();
-  }
-
-  const int i_begin = CAUSAL ? (k0 / BQ) * BQ : 0;
-  const int n_steps = (N - i_begin + BQ - 1) / BQ;
-
-  u32x4_t qreg[ULOADS][4], oreg[ULOADS][4];
-  float lreg = 0.0f, dreg = 0.0f;
-
-  auto load_step = [&](int i0) {
-#pragma unroll
-    for (int r = 0; r < ULOADS; ++r) {
-      const int u = tid + 256 * r;
-      const int g = u / KCH, ch = u % KCH;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = i0 + 4 * g + rr;
-        if (u < UNITS && row < N) {
-          qreg[r][rr] = *(const u32x4_t*)(Qh + (size_t)row * D + ch * 8);
-          oreg[r][rr] = *(const u32x4_t*)(dOh + (size_t)row * D + ch * 8);
-        } else {
-          qreg[r][rr] = u32x4_t{0, 0, 0, 0};
-          oreg[r][rr] = u32x4_t{0, 0, 0, 0};
-        }
-      }
-    }
-    if (tid < BQ) {
-      const int row = i0 + tid;
-      // rows past the end: P = exp2(-inf) = 0 and D = 0, so they add nothing
-      lreg = row < N ? Lh[row] * kLog2e : INFINITY;
-      dreg = row < N ? Dh[row] : 0.0f;
-    }
-  };
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < ULOADS; ++r) {
-      const int u = tid + 256 * r;
-      if (u < UNITS) {
-        const int g = u / KCH, ch = u % KCH;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          *(u32x4_t*)(&sQ[buf][swz_off<D>(4 * g + rr, ch)]) = qreg[r][rr];
-          *(u32x4_t*)(&sdO[buf][swz_off<D>(4 * g + rr, ch)]) = oreg[r][rr];
-        }
-        store_interleaved(&sQt[buf][il_off<D>(g, 8 * ch)], qreg[r]);
-        store_interleaved(&sdOt[buf][il_off<D>(g, 8 * ch)], oreg[r]);
-      }
-    }
-    if (tid < BQ) {
-      sL[buf][tid] = lreg;
-      sD[buf][tid] = dreg;
-    }
-  };
-
-  if (n_steps > 0) {
-    load_step(i_begin);
-    store_step(0);
-  }
-  __syncthreads();
-
-  for (int st = 0; st < n_steps; ++st) {
-    const int buf = st & 1;
-    const int i0 = i_begin + st * BQ;
-    const bool has_next = st + 1 < n_steps;
-    if (has_next) load_step(i0 + BQ);
-
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qlo = i0 + 32 * qb;
-      // causal: the whole 32-row block sees none of this wavefront's keys
-      if (CAUSAL && qlo + 31 < kw) continue;
-
-      // S = Q K^T and dP = dO V^T (rows = queries in registers, column = key)
-      f32x16_t s = zero16(), dp = zero16();
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int row = 32 * qb + l32;
-        const u32x4_t qa = *(const u32x4_t*)(&sQ[buf][swz_off<D>(row, 2 * ks + h)]);
-        const u32x4_t oa = *(const u32x4_t*)(&sdO[buf][swz_off<D>(row, 2 * ks + h)]);
-        s = TR::mfma(qa, kf[ks], s);
-        dp = TR::mfma(oa, vf[ks], dp);
-      }
-
-      const int key = kw + l32;
-      uint32_t pk[8], dsk[8];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 lv = *(const float4*)(&sL[buf][32 * qb + 8 * g + 4 * h]);
-        const float4 dv = *(const float4*)(&sD[buf][32 * qb + 8 * g + 4 * h]);
-        const float lq[4] = {lv.x, lv.y, lv.z, lv.w};
-        const float dq[4] = {dv.x, dv.y, dv.z, dv.w};
-        float p[4], ds[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          const int qrow = qlo + 8 * g + 4 * h + e;
-          float pv = fast_exp2(fmaf(s[r], c, -lq[e]));
-          if (CAUSAL && key > qrow) pv = 0.0f;
-          p[e] = pv;
-          ds[e] = pv * (dp[r] - dq[e]);
-        }
-        pk[2 * g + 0] = TR::pack2(p[0], p[1]);
-        pk[2 * g + 1] = TR::pack2(p[2], p[3]);
-        dsk[2 * g + 0] = TR::pack2(ds[0], ds[1]);
-        dsk[2 * g + 1] = TR::pack2(ds[2], ds[3]);
-      }
-
-      // dV^T += dO^T P and dK^T += Q^T dS: contraction over the 32 query rows,
-      // in two steps of 16; step t pairs accumulator values 8t..8t+7, i.e.
-      // rows {16t + 4h + 0..3} and {16t + 8 + 4h + 0..3} of the block.
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4_t pb = u32x4_t{pk[4 * t + 0], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
-        const u32x4_t db_ = u32x4_t{dsk[4 * t + 0], dsk[4 * t + 1], dsk[4 * t + 2], dsk[4 * t + 3]};
-        const int ga = 8 * qb + 4 * t + h, gb = ga + 2;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int col = 32 * db + l32;
-          const u32x2_t oa0 = *(const u32x2_t*)(&sdOt[buf][il_off<D>(ga, col)]);
-          const u32x2_t oa1 = *(const u32x2_t*)(&sdOt[buf][il_off<D>(gb, col)]);
-          acc_dv[db] = TR::mfma(u32x4_t{oa0[0], oa0[1], oa1[0], oa1[1]}, pb, acc_dv[db]);
-          const u32x2_t qa0 = *(const u32x2_t*)(&sQt[buf][il_off<D>(ga, col)]);
-          const u32x2_t qa1 = *(const u32x2_t*)(&sQt[buf][il_off<D>(gb, col)]);
-          acc_dk[db] = TR::mfma(u32x4_t{qa0[0], qa0[1], qa1[0], qa1[1]}, db_, acc_dk[db]);
-        }
-      }
-    }
-
-    if (has_next) store_step(buf ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds key kw + lane%32 and columns 32db + 8g + 4h + 0..3
-  const int key = kw + l32;
-  if (key < N) {
-    uint16_t* dkrow = dK + head_off + (size_t)key * D;
-    uint16_t* dvrow = dV + head_off + (size_t)key * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * db + 8 * g + 4 * h;
-        *(u32x2_t*)(dkrow + col) =
-            u32x2_t{TR::pack2(acc_dk[db][4 * g + 0] * scale, acc_dk[db][4 * g + 1] * scale),
-                    TR::pack2(acc_dk[db][4 * g + 2] * scale, acc_dk[db][4 * g + 3] * scale)};
-        *(u32x2_t*)(dvrow + col) =
-            u32x2_t{TR::pack2(acc_dv[db][4 * g + 0], acc_dv[db][4 * g + 1]),
-                    TR::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3])};
-      }
-  }
-}
-
 // dK, dV with two wavefronts per SIMD (d = 64): 8 wavefronts x 32 keys, 256
 // keys per workgroup; query tiles of 64 rows stream through LDS.  Same
 // two-phase schedule as the forward:
@@ -570,6 +360,314 @@ void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   }
 }
 
+// dK, dV software-pipelined inside each wavefront (d = 128: one wavefront per
+// SIMD, 4 x 32 keys per workgroup).  Query rows stream through LDS in stages
+// of 64 (two blocks of 32); iteration b of a wavefront issues
+//   matrix: S_{b+1} = Q_{b+1} K^T, dP_{b+1} = dO_{b+1} V^T - D   (VGPR results)
+//           dV^T += dO_{b-1}^T P_{b-1}, dK^T += Q_{b-1}^T dS_{b-1}  (AGPR accumulators)
+//   vector: P_b = exp2(S_b c - LSE log2 e), dS_b = P_b (dP_b - D), rounded
+// interleaved product by product, so that the matrix core and the vector unit
+// of the SIMD work at the same time within the one wavefront.  K, V (operands)
+// and dK, dV (accumulators) stay in AGPRs for the whole kernel.
+//
+// LDS stage (four in flight, stage x in slot x % 4): Q and dO tiles with rows
+// padded to d + 8 elements, the log2-scaled LSE and -D.  Within every 16 query
+// rows the S/dP products take their rows in the order perm(m) = 4 (m % 4) +
+// m / 4, so that the four rows a transposed read (lds_read_tr) gathers for
+// the dV/dK products lie 4 rows apart: with the padded rows, both the row
+// reads (S, dP) and the transposed reads (dV, dK) are free of bank conflicts,
+// and no transposed copy of Q or dO is staged.
+template <class TR, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                          const float* __restrict__ LSE, const float* __restrict__ Dvec,
+                          uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_ktiles,
+                          uint32_t total, float c, float scale) {
+  constexpr int NT = 256;
+  constexpr int BKV = 128;                  // keys per workgroup
+  constexpr int BQ = 64;                    // query rows per stage
+  constexpr int KS = D + 8;                 // padded LDS row (elements)
+  constexpr int RBL = 2 * KS;               // LDS row bytes
+  constexpr uint32_t RB = 2 * D;            // global row bytes
+  constexpr int NKS = D / 16;               // k-steps of S and dP
+  constexpr int NDB = D / 32;               // 32-column blocks of dK and dV
+  constexpr int OFF_O = BQ * RBL;           // stage layout (bytes): Q, dO, then vector w
+  constexpr int OFF_L = 2 * BQ * RBL;       // of wave w at OFF_L + 4 BQ w (0: LSE,
+  constexpr int OFF_D = OFF_L + 4 * BQ;     // 1: -D; waves 2, 3 write unread copies)
+  constexpr int STG = OFF_L + 16 * BQ;
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int ROWSTEP = NT / CPR;         // rows between a thread's staging chunks
+  constexpr int NCH = BQ / ROWSTEP;         // staging chunks per thread and tensor
+  constexpr int NSL = 4 * NKS;              // products per iteration
+  constexpr int AH = 4;                     // operand reads issued ahead of their product
+  static_assert(2 * NDB == NKS, "S, dV, dK, dP products interleave one to one");
+  static_assert(NSL == 32, "vector work: one stage of one score per product");
+  static_assert(4 * STG <= 160 * 1024, "four stages fit in LDS");
+
+  __shared__ __attribute__((aligned(16))) char smem[4 * STG];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const uint32_t lid = xcd_remap(blockIdx.x, total);
+  const int bh = lid / n_ktiles;
+  const int kt = lid % n_ktiles;
+  const int k0 = kt * BKV;
+  const int kw = k0 + 32 * w;               // first key of this wavefront
+  const int key = kw + l32;
+  const size_t head_off = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * RB;
+
+  // K and V rows of this wavefront's keys as B operands (column = key)
+  u32x4_t kf[NKS], vf[NKS];
+  {
+    const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
+    const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
+    const uint32_t off = (uint32_t)key * RB + 16 * h;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kf[ks] = buf_load16(kres, off + 32 * ks);
+      vf[ks] = buf_load16(vres, off + 32 * ks);
+    }
+  }
+  f32x16_t acc_dk[NDB], acc_dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    acc_dk[db] = zero16();
+    acc_dv[db] = zero16();
+  }
+
+  // query row (within its 32-row block) of S/dP row m
+  auto perm = [](int m) { return (m & 16) | ((m & 3) << 2) | ((m >> 2) & 3); };
+  // row-read fragment of this lane: row perm(l32), chunk h (+ 2 ks)
+  const uint32_t rbase = (uint32_t)(perm(l32) * RBL + 16 * h);
+  // transposed-read fragment: lane group G = lane / 16 covers columns
+  // 16 (G % 2) + 0..15 of rows (h + 2 sec) + 4 e, e = 0..3; lane 4e + i of the
+  // group points at columns 4i..4i+3 of row e
+  const int L16 = lane & 15, G = lane >> 4;
+  const uint32_t tbase = (uint32_t)((h + 4 * (L16 >> 2)) * RBL + (16 * (G & 1) + 4 * (L16 & 3)) * 2);
+
+  const int i_begin = CAUSAL ? k0 : 0;
+  const int n_st = (N - i_begin + BQ - 1) / BQ;
+
+  // ---- staging: chunk i of this thread is row tid / CPR + ROWSTEP i, column
+  // chunk tid % CPR, of both Q and dO.  Wave w loads vector w % 2 of the stage
+  // (0: LSE, 1: D) at positions m = lane: row 32 (m / 32) + perm(m % 32).
+  const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
+  const rsrc_t ores = make_rsrc(dO + head_off, head_bytes);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const bool is_d = (wu & 1) != 0;
+  const rsrc_t vres = make_rsrc(is_d ? (const void*)(Dvec + (size_t)bh * N) : (const void*)(LSE + (size_t)bh * N),
+                                (uint32_t)N * 4);
+  const uint32_t g_off = (uint32_t)(tid / CPR) * RB + (tid % CPR) * 16;
+  const uint32_t s_off = (uint32_t)(tid / CPR) * RBL + (tid % CPR) * 16;
+  const int vrow = (lane & 32) + perm(lane & 31);
+  const uint32_t v_off = OFF_L + 4 * BQ * wu + 4 * lane;
+  u32x4_t sq[NCH], so[NCH];
+  float vreg = 0.0f;
+  auto load_stage = [&](int i0) __attribute__((always_inline)) {
+    const uint32_t base = g_off + (uint32_t)i0 * RB;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      sq[i] = buf_load16(qres, base + ROWSTEP * i * RB);
+      so[i] = buf_load16(ores, base + ROWSTEP * i * RB);
+    }
+    // rows past the end: LSE = +inf makes P = 0; D = 0.  D is stored negated:
+    // it initialises the dP accumulators.
+    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vres, (uint32_t)(i0 + vrow) * 4, 0, 0));
+    const bool in = i0 + vrow < N;
+    vreg = is_d ? (in ? -x : 0.0f) : (in ? x * kLog2e : INFINITY);
+  };
+  auto store_chunk = [&](uint32_t sb, int i) __attribute__((always_inline)) {
+    *(u32x4_t*)(smem + sb + s_off + ROWSTEP * i * RBL) = sq[i];
+    *(u32x4_t*)(smem + sb + OFF_O + s_off + ROWSTEP * i * RBL) = so[i];
+  };
+  auto store_vec = [&](uint32_t sb) __attribute__((always_inline)) { *(float*)(smem + sb + v_off) = vreg; };
+
+  // ---- register sets of the pipeline (index: block parity)
+  f32x16_t sc[2], dp[2];
+  float lr[2][16];
+  u32x4_t pk[2][2], dsk[2][2];  // [set][k-step t]: P and dS rounded, packed in pairs
+
+  // -D into the dP accumulators, and the scaled LSE, of the block in half bb of stage sb
+  auto load_vecs = [&](uint32_t sb, int bb, f32x16_t& d, float (&l)[16]) __attribute__((always_inline)) {
+    const char* dv = smem + sb + OFF_D + 128 * bb + 16 * h;
+    const char* lv = smem + sb + OFF_L + 128 * bb + 16 * h;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 d4 = *(const float4*)(dv + 32 * g);
+      const float4 l4 = *(const float4*)(lv + 32 * g);
+      d[4 * g + 0] = d4.x; d[4 * g + 1] = d4.y; d[4 * g + 2] = d4.z; d[4 * g + 3] = d4.w;
+      l[4 * g + 0] = l4.x; l[4 * g + 1] = l4.y; l[4 * g + 2] = l4.z; l[4 * g + 3] = l4.w;
+    }
+  };
+  // A operand of S (tensor 0: Q) or dP (tensor 1: dO) for k-step ks
+  auto row_frag = [&](uint32_t sb, int bb, int tensor, int ks) __attribute__((always_inline)) -> u32x4_t {
+    return *(const u32x4_t*)(smem + sb + tensor * OFF_O + rbase + bb * 32 * RBL + 32 * ks);
+  };
+  // A operand of dK^T (tensor 0: Q^T) or dV^T (tensor 1: dO^T) for k-step t, column block db
+  auto tr_frag = [&](uint32_t sb, int bb, int tensor, int t, int db) __attribute__((always_inline)) -> u32x4_t {
+    const char* p = smem + sb + tensor * OFF_O + tbase + (32 * bb + 16 * t) * RBL + 64 * db;
+    const u32x2_t a = lds_read_tr(p), b = lds_read_tr(p + 2 * RBL);
+    return u32x4_t{a[0], a[1], b[0], b[1]};
+  };
+  // operand of product k of an iteration: (S, dV, dK, dP)[k % 4] of index k / 4;
+  // sb1: stage of block b+1, sb2: stage of block b-1, nb: their half (1 - b % 2)
+  auto frag = [&](int k, uint32_t sb1, uint32_t sb2, int nb) __attribute__((always_inline)) -> u32x4_t {
+    const int x = k / 4;
+    switch (k % 4) {
+      case 0: return row_frag(sb1, nb, 0, x);
+      case 1: return tr_frag(sb2, nb, 1, x / NDB, x % NDB);
+      case 2: return tr_frag(sb2, nb, 0, x / NDB, x % NDB);
+      default: return row_frag(sb1, nb, 1, x);
+    }
+  };
+  u32x4_t fr[AH];  // operands of the next AH products, carried across iterations
+
+  // ---- one iteration.  PAR = b % 2 selects the register sets; q0: first row
+  // of block b; (nsb1, nsb2): stages of the next iteration.  PAR 0 requests the
+  // stage after next (rows i_ld), PAR 1 writes it to slot sbw.
+  auto iteration = [&](auto par_c, auto masked_c, uint32_t sb1, uint32_t sb2, uint32_t nsb1, uint32_t nsb2,
+                       int q0, int i_ld, uint32_t sbw) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par_c)::value;
+    constexpr bool MASKED = decltype(masked_c)::value;
+    constexpr int NB = 1 - PAR;
+    // S_b, dP_b were written by matrix instructions, P and dS of block b-1 by
+    // vector instructions: all of them ordered before what reads them next
+    mfma_wait_v(sc[PAR], dp[PAR]);
+    asm volatile("" : "+v"(pk[NB][0]), "+v"(pk[NB][1]), "+v"(dsk[NB][0]), "+v"(dsk[NB][1]));
+    load_vecs(sb1, NB, dp[NB], lr[NB]);
+
+    // causal: key kw + l32 is visible to the row of score r iff thr <= qoff(r)
+    const int thr = kw - q0 + l32 - h;
+    float pe[16], dsv[16];
+    auto vwork = [&](int k) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (k == 2 * r) {
+          float x = fmaf(sc[PAR][r], c, -lr[PAR][r]);
+          if constexpr (MASKED) {
+            // score r = 4g + e is S row 8g + 4h + e: query perm(8(g%2) + 4h + e) + 16(g/2)
+            const int g = r / 4, e = r % 4;
+            const int qoff = 16 * (g / 2) + 4 * e + 2 * (g % 2);
+            x = thr <= qoff ? x : -INFINITY;
+          }
+          pe[r] = fast_exp2(x);
+        }
+        if (k == 2 * r + 1) {
+          dsv[r] = pe[r] * dp[PAR][r];  // dp holds dP - D
+          if (r & 1) {
+            pk[PAR][r / 8][(r / 2) % 4] = TR::pack2(pe[r - 1], pe[r]);
+            dsk[PAR][r / 8][(r / 2) % 4] = TR::pack2(dsv[r - 1], dsv[r]);
+          }
+        }
+      }
+      if constexpr (PAR == 0) {
+        if (k == 0) load_stage(i_ld);
+      } else {
+        if (k >= NSL / 4 && k < NSL / 4 + NCH) store_chunk(sbw, k - NSL / 4);
+        if (k == NSL / 4 + NCH) store_vec(sbw);
+      }
+    };
+    static_for<0, NSL>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int x = k / 4;
+      const u32x4_t a = fr[k % AH];
+      if constexpr (k + AH < NSL) fr[k % AH] = frag(k + AH, sb1, sb2, NB);
+      else fr[k % AH] = frag(k + AH - NSL, nsb1, nsb2, PAR);
+      if constexpr (k % 4 == 0) {
+        if constexpr (x == 0) sc[NB] = TR::mma0_vva(a, kf[0]);
+        else TR::mma_vva(sc[NB], a, kf[x]);
+      } else if constexpr (k % 4 == 1) {
+        TR::mma_avv(acc_dv[x % NDB], a, pk[NB][x / NDB]);
+      } else if constexpr (k % 4 == 2) {
+        TR::mma_avv(acc_dk[x % NDB], a, dsk[NB][x / NDB]);
+      } else {
+        TR::mma_vva(dp[NB], a, vf[x]);
+      }
+      vwork(k);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // ---- prologue: stages 0 and 1 in slots 0 and 1, slot 3 zeroed (the first
+  // iteration multiplies it by zero P and dS); S_0, dP_0; first operands
+  load_stage(i_begin);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) store_chunk(0, i);
+  store_vec(0);
+  load_stage(i_begin + BQ);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) store_chunk(STG, i);
+  store_vec(STG);
+  for (int i = tid; i < 2 * BQ * RBL / 16; i += NT) *(u32x4_t*)(smem + 3 * STG + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
+  lds_barrier();
+  load_vecs(0, 0, dp[0], lr[0]);
+  mma_pipeline<2 * NKS, 3>([&](int x) { return smem + ((x & 1) ? OFF_O : 0) + rbase + 32 * (x >> 1); },
+                           [&](int x, u32x4_t a) {
+                             const int ks = x >> 1;
+                             if (x & 1) TR::mma_vva(dp[0], a, vf[ks]);
+                             else if (ks == 0) sc[0] = TR::mma0_vva(a, kf[0]);
+                             else TR::mma_vva(sc[0], a, kf[ks]);
+                           },
+                           [](int) {});
+#pragma unroll
+  for (int t = 0; t < 2; ++t) pk[1][t] = dsk[1][t] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int x = 0; x < AH; ++x) fr[x] = frag(x, 0u, 3u * STG, 1);
+
+  // ---- pairs of iterations over the stages.  Causal: the blocks of the first
+  // two stages (each wavefront's diagonal block and those above it) are masked.
+  auto pair = [&](auto masked_c, int s) __attribute__((always_inline)) {
+    const uint32_t b0 = (uint32_t)(s & 3) * STG;
+    const uint32_t bp1 = (uint32_t)((s + 1) & 3) * STG;
+    const uint32_t bm1 = (uint32_t)((s + 3) & 3) * STG;
+    const uint32_t bp2 = (uint32_t)((s + 2) & 3) * STG;
+    const int q0 = i_begin + BQ * s;
+    iteration(std::integral_constant<int, 0>{}, masked_c, b0, bm1, bp1, b0, q0, q0 + 2 * BQ, 0u);
+    iteration(std::integral_constant<int, 1>{}, masked_c, bp1, b0, bp1, b0, q0 + 32, 0, bp2);
+    lds_barrier();
+  };
+  const int n_masked = CAUSAL ? min(2, n_st) : 0;
+  int s = 0;
+  for (; s < n_masked; ++s) pair(std::true_type{}, s);
+  for (; s < n_st; ++s) pair(std::false_type{}, s);
+
+  // ---- last block: its dV, dK products (register set 1)
+  {
+    const uint32_t sb = (uint32_t)((n_st - 1) & 3) * STG;
+    asm volatile("" : "+v"(pk[1][0]), "+v"(pk[1][1]), "+v"(dsk[1][0]), "+v"(dsk[1][1]));
+#pragma unroll
+    for (int x = 0; x < NKS; ++x) {
+      TR::mma_avv(acc_dv[x % NDB], tr_frag(sb, 1, 1, x / NDB, x % NDB), pk[1][x / NDB]);
+      TR::mma_avv(acc_dk[x % NDB], tr_frag(sb, 1, 0, x / NDB, x % NDB), dsk[1][x / NDB]);
+    }
+  }
+  static_assert(NDB == 4, "wait operand list");
+  mfma_wait_a(acc_dk[0], acc_dk[1], acc_dk[2], acc_dk[3], acc_dv[0], acc_dv[1], acc_dv[2], acc_dv[3]);
+
+  if (key < N) {
+    uint16_t* dkrow = dK + head_off + (size_t)key * D;
+    uint16_t* dvrow = dV + head_off + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * h;
+        *(u32x2_t*)(dkrow + col) =
+            u32x2_t{TR::pack2(acc_dk[db][4 * g + 0] * scale, acc_dk[db][4 * g + 1] * scale),
+                    TR::pack2(acc_dk[db][4 * g + 2] * scale, acc_dk[db][4 * g + 3] * scale)};
+        *(u32x2_t*)(dvrow + col) =
+            u32x2_t{TR::pack2(acc_dv[db][4 * g + 0], acc_dv[db][4 * g + 1]),
+                    TR::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3])};
+      }
+  }
+}
+
 // ------------------------------------------------------------------ dQ
 
 // dQ: 8 wavefronts (two per SIMD), 32 query rows each, 256 rows per
@@ -850,14 +948,15 @@ static hipError_t dkdv_t(const BwdArgs& a) {
                        (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
                        a.N, n_ktiles, total, a.c, a.scale);
     return hipGetLastError();
+  } else {
+    const int n_ktiles = (a.N + 127) / 128;
+    const uint32_t total = (uint32_t)(n_ktiles * a.BH);
+    hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                       a.N, n_ktiles, total, a.c, a.scale);
+    return hipGetLastError();
   }
-  const int n_ktiles = (a.N + 127) / 128;
-  const uint32_t total = (uint32_t)(n_ktiles * a.BH);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<TR, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     a.N, n_ktiles, total, a.c, a.scale);
-  return hipGetLastError();
 }
 
 template <class TR, int D, bool CAUSAL>

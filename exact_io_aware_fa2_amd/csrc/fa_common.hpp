@@ -59,7 +59,6 @@ struct BF16 {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), acc, false);
   }
-  // Register-class-pinned forms (see MfmaAsm below).
   // All-VGPR forms (see MfmaAsm below): c += A B, and a fresh A B.
   __device__ static inline void mma(f32x16_t& c, u32x4_t a, u32x4_t b) {
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
@@ -68,6 +67,19 @@ struct BF16 {
     f32x16_t c;
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
     return c;
+  }
+  // Mixed classes: B operand in AGPRs (VGPR accumulator), or accumulator in
+  // AGPRs (VGPR operands).
+  __device__ static inline void mma_vva(f32x16_t& c, u32x4_t a, u32x4_t b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+  }
+  __device__ static inline f32x16_t mma0_vva(u32x4_t a, u32x4_t b) {
+    f32x16_t c;
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+    return c;
+  }
+  __device__ static inline void mma_avv(f32x16_t& c, u32x4_t a, u32x4_t b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
   }
 };
 
@@ -99,6 +111,17 @@ struct F16 {
     asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
     return c;
   }
+  __device__ static inline void mma_vva(f32x16_t& c, u32x4_t a, u32x4_t b) {
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+  }
+  __device__ static inline f32x16_t mma0_vva(u32x4_t a, u32x4_t b) {
+    f32x16_t c;
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+    return c;
+  }
+  __device__ static inline void mma_avv(f32x16_t& c, u32x4_t a, u32x4_t b) {
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
 };
 
 // MfmaAsm: TR::mma / TR::mma0 keep every operand and the result in VGPRs.
@@ -124,7 +147,29 @@ __device__ __forceinline__ void mfma_wait_v(f32x16_t& a, f32x16_t& b, f32x16_t& 
                                             f32x16_t& e, f32x16_t& f, f32x16_t& g, f32x16_t& h) {
   asm volatile(FA_MFMA_WAIT : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
 }
+// The same for accumulators held in AGPRs (before v_accvgpr_read).
+__device__ __forceinline__ void mfma_wait_a(f32x16_t& a, f32x16_t& b) {
+  asm volatile(FA_MFMA_WAIT : "+a"(a), "+a"(b));
+}
+__device__ __forceinline__ void mfma_wait_a(f32x16_t& a, f32x16_t& b, f32x16_t& c, f32x16_t& d) {
+  asm volatile(FA_MFMA_WAIT : "+a"(a), "+a"(b), "+a"(c), "+a"(d));
+}
+__device__ __forceinline__ void mfma_wait_a(f32x16_t& a, f32x16_t& b, f32x16_t& c, f32x16_t& d,
+                                            f32x16_t& e, f32x16_t& f, f32x16_t& g, f32x16_t& h) {
+  asm volatile(FA_MFMA_WAIT : "+a"(a), "+a"(b), "+a"(c), "+a"(d), "+a"(e), "+a"(f), "+a"(g), "+a"(h));
+}
 #undef FA_MFMA_WAIT
+
+// Four 16-bit elements from LDS, transposed across each group of 16 lanes
+// (ds_read_b64_tr_b16): with lane j of a group pointing at 4 consecutive
+// elements E[j][0..3], lane i of the group receives E[4 * e + i / 4][i % 4]
+// for e = 0..3.  So if lanes 4e..4e+3 point at row R_e, columns C + 0..15 in
+// steps of 4, lane i receives column C + i of rows R_0..R_3.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+__device__ inline u32x2_t lds_read_tr(const void* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p));
+}
 
 __device__ inline f32x16_t mfma_f32(float a, float b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -234,41 +279,5 @@ __device__ inline uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_am
 
 // Scheduling hints (instruction classes for __builtin_amdgcn_sched_group_barrier).
 constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100, kSchedDSWrite = 0x200;
-
-// Row-major tile of 16-bit elements in LDS, `D` columns per row, with the
-// 16-byte chunks of each row XOR-swizzled by the row index so that 32 lanes
-// reading one chunk column of 32 consecutive rows hit distinct banks.
-template <int D>
-__device__ inline int swz_off(int row, int chunk) {
-  constexpr int KCH = D / 8;
-  constexpr int SWZ = (KCH < 16 ? KCH : 16) - 1;
-  return row * D + ((chunk ^ (row & SWZ)) * 8);
-}
-
-// "Interleaved" tile: groups of 4 consecutive rows stored column by column,
-// [row / 4][D][4], so one 8-byte read returns 4 consecutive rows of one column
-// (the layout the second operand of a contraction over rows needs).
-template <int D>
-__device__ inline int il_off(int row_group, int col) {
-  return (row_group * D + col) * 4;
-}
-
-// 4 rows x 8 columns (each row one 16-byte chunk) -> 8 interleaved units of
-// 4 rows at one column, written as four 16-byte LDS stores at `dst`, which is
-// the address of unit (row_group, 8 * chunk).
-__device__ inline void store_interleaved(uint16_t* dst, const u32x4_t r[4]) {
-  uint32_t o[16];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t a = r[0][p], b = r[1][p], c = r[2][p], d = r[3][p];
-    o[4 * p + 0] = pack_lo(a, b);  // column 2p, rows 0,1
-    o[4 * p + 1] = pack_lo(c, d);  // column 2p, rows 2,3
-    o[4 * p + 2] = pack_hi(a, b);  // column 2p+1, rows 0,1
-    o[4 * p + 3] = pack_hi(c, d);  // column 2p+1, rows 2,3
-  }
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-    *(u32x4_t*)(dst + 8 * x) = u32x4_t{o[4 * x + 0], o[4 * x + 1], o[4 * x + 2], o[4 * x + 3]};
-}
 
 }  // namespace fa
