@@ -59,309 +59,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 
 // ------------------------------------------------------------------ dK, dV
 
-// dK, dV with two wavefronts per SIMD (d = 64): 8 wavefronts x 32 keys, 256
-// keys per workgroup; query tiles of 64 rows stream through LDS.  Same
-// two-phase schedule as the forward:
-//   M-phase i: S_i = Q_i K^T, dP_i = dO_i V^T                 (rows = queries)
-//              dV^T += dO_{i-1}^T P_{i-1}, dK^T += Q_{i-1}^T dS_{i-1}
-//   V-phase i: P_i = exp2(S c - LSE log2 e), dS_i = P_i (dP_i - D), rounded
-// Waves 0..3 stage Q (row-major, query-interleaved, LSE), waves 4..7 stage dO
-// (row-major, query-interleaved, D).  Row tiles double-, interleaved tiles and
-// row vectors triple-buffered.
-template <class TR, int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dkdv2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                      const float* __restrict__ LSE, const float* __restrict__ Dvec,
-                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_ktiles,
-                      uint32_t total, float c, float scale) {
-  constexpr int NW = 8;
-  constexpr int BKV = 32 * NW;           // keys per workgroup
-  constexpr int BQ = 64;                 // query rows per step
-  constexpr int QB = BQ / 32;
-  constexpr int KS = D + 8;              // padded row (elements)
-  constexpr int NDB = D / 32;
-  constexpr int NKS = D / 16;
-  constexpr int NS = QB * NKS;           // S (and dP) products per step
-  constexpr int NG = QB * 2 * NDB;       // dV (and dK) products per step
-  static_assert(NS == NG, "matrix phase interleaves the four products one to one");
-
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[2][BQ * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[3][BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sOt[3][BQ * D];
-  __shared__ __attribute__((aligned(16))) float sL[3][BQ];
-  __shared__ __attribute__((aligned(16))) float sD[3][BQ];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int grp = w >> 2;
-  const int st = tid & 255;
-  const int h = lane >> 5;
-  const int l32 = lane & 31;
-
-  const uint32_t lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / n_ktiles;
-  const int kt = lid % n_ktiles;
-  const int k0 = kt * BKV;
-  const int kw = k0 + 32 * w;            // first key of this wavefront
-  const int key = kw + l32;
-  const size_t head_off = (size_t)bh * N * D;
-  constexpr uint32_t RB = D * 2;
-  const uint32_t head_bytes = (uint32_t)N * RB;
-
-  // K and V rows of this wavefront's keys as B operands (column = key)
-  u32x4_t kf[NKS], vf[NKS];
-  {
-    const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
-    const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
-    const uint32_t off = (uint32_t)key * RB + 16 * h;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = buf_load16(kres, off + 32 * ks);
-      vf[ks] = buf_load16(vres, off + 32 * ks);
-    }
-  }
-  f32x16_t acc_dk[NDB], acc_dv[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    acc_dk[db] = zero16();
-    acc_dv[db] = zero16();
-  }
-  f32x16_t s[QB], dp[QB];
-  uint32_t pk[QB][8], dsk[QB][8];
-
-  const int i_begin = CAUSAL ? (k0 / BQ) * BQ : 0;
-  const int n_steps = (N - i_begin + BQ - 1) / BQ;
-  // causal: steps whose 64 rows all precede this wave's first key are skipped
-  const int first = CAUSAL ? max(0, (kw - i_begin - (BQ - 1) + BQ - 1) / BQ) : 0;
-
-  // ---- staging: group 0 -> Q and LSE, group 1 -> dO and D.  Every thread of
-  // a group takes part (no divergent branches): unit st = 8 rows x 2 columns,
-  // rows 16us + 4uh + {0..3} and 16us + 8 + 4uh + {0..3}, columns 2uc, 2uc + 1;
-  // the row vector is loaded by all threads (rows st % 64, four copies).
-  static_assert(BQ * D / 16 == 256, "one staging unit per thread");
-  // one resource per tensor, uniform across the wave (see the forward)
-  const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
-  const rsrc_t ores = make_rsrc(dO + head_off, head_bytes);
-  const rsrc_t lres = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
-  const rsrc_t dres = make_rsrc(Dvec + (size_t)bh * N, (uint32_t)N * 4);
-  const int uc = st % (D / 2);
-  const int uh = (st / (D / 2)) & 1;
-  const int us = st / D;
-  const int urow0 = 16 * us + 4 * uh;
-  const uint32_t uoff = (uint32_t)urow0 * RB + uc * 4;
-  const int ust = ((2 * us + uh) * D + 2 * uc) * 8;
-  const int vrow = st % BQ;
-  u32x4_t stg[2];
-  float vreg = 0.0f;
-
-  auto load_tile = [&](int i0) {
-    // rows past the end: LSE = +inf makes P = 0; D = 0
-    const bool in = i0 + vrow < N;
-    if (grp == 0) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        stg[k / 4][k % 4] = __builtin_amdgcn_raw_buffer_load_b32(
-            qres, uoff + (uint32_t)(i0 + 8 * (k / 4) + (k % 4)) * RB, 0, 0);
-      const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                    lres, (uint32_t)(i0 + vrow) * 4, 0, 0));
-      vreg = in ? x * kLog2e : INFINITY;
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        stg[k / 4][k % 4] = __builtin_amdgcn_raw_buffer_load_b32(
-            ores, uoff + (uint32_t)(i0 + 8 * (k / 4) + (k % 4)) * RB, 0, 0);
-      const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                    dres, (uint32_t)(i0 + vrow) * 4, 0, 0));
-      vreg = in ? -x : 0.0f;  // stored negated: it initialises the dP accumulator
-    }
-  };
-  auto store_part = [&](int i, int part) {
-    uint16_t* rowbuf = grp == 0 ? sQ[i & 1] : sO[i & 1];
-    uint16_t* ilbuf = grp == 0 ? sQt[i % 3] : sOt[i % 3];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int k = 2 * part + e;
-      *(uint32_t*)(&rowbuf[(urow0 + 8 * (k / 4) + (k % 4)) * KS + 2 * uc]) = stg[k / 4][k % 4];
-    }
-    if (part & 1) {
-      const int cc = part >> 1;
-      uint32_t o[4];
-#pragma unroll
-      for (int kp = 0; kp < 4; ++kp) {
-        const uint32_t x0 = stg[kp / 2][2 * (kp % 2)], x1 = stg[kp / 2][2 * (kp % 2) + 1];
-        o[kp] = cc ? pack_hi(x0, x1) : pack_lo(x0, x1);
-      }
-      *(u32x4_t*)(&ilbuf[ust + 8 * cc]) = u32x4_t{o[0], o[1], o[2], o[3]};
-    }
-    if (part == 0) (grp == 0 ? sL : sD)[i % 3][vrow] = vreg;
-  };
-  auto store_tile = [&](int i) {
-#pragma unroll
-    for (int part = 0; part < 4; ++part) store_part(i, part);
-  };
-
-  // ---- products
-  const int rfrag = l32 * KS + 8 * h;   // row-major fragment of this lane
-  const int ifrag = (h * D + l32) * 8;  // interleaved fragment of this lane
-  auto r_addr = [&](const uint16_t* b_, int x) { return b_ + 32 * (x / NKS) * KS + 16 * (x % NKS); };
-  auto i_addr = [&](const uint16_t* b_, int x) { return b_ + ((2 * (x / NDB)) * D + 32 * (x % NDB)) * 8; };
-  auto s_mma = [&](int x, u32x4_t a) { s[x / NKS] = TR::mfma(a, kf[x % NKS], s[x / NKS]); };
-  auto dp_mma = [&](int x, u32x4_t a) { dp[x / NKS] = TR::mfma(a, vf[x % NKS], dp[x / NKS]); };
-  auto dv_mma = [&](int x, u32x4_t a) {
-    const int qt2 = x / NDB, db = x % NDB, qb = qt2 / 2, t = qt2 % 2;
-    acc_dv[db] = TR::mfma(a, u32x4_t{pk[qb][4 * t + 0], pk[qb][4 * t + 1], pk[qb][4 * t + 2], pk[qb][4 * t + 3]},
-                          acc_dv[db]);
-  };
-  auto dk_mma = [&](int x, u32x4_t a) {
-    const int qt2 = x / NDB, db = x % NDB, qb = qt2 / 2, t = qt2 % 2;
-    acc_dk[db] = TR::mfma(a, u32x4_t{dsk[qb][4 * t + 0], dsk[qb][4 * t + 1], dsk[qb][4 * t + 2], dsk[qb][4 * t + 3]},
-                          acc_dk[db]);
-  };
-
-  // ---- prologue
-  if (n_steps > 0) {
-    load_tile(i_begin);
-    store_tile(0);
-  }
-  wait_vmem();
-  if (n_steps > 1) load_tile(i_begin + BQ);
-  lds_barrier();
-
-  const int n_slots = 2 * n_steps + 2;
-  for (int slot = 0; slot < n_slots; ++slot) {
-    const int ph = slot - grp;
-    if (ph >= 0 && (ph & 1) == 0) {
-      // ---------------- M-phase i
-      __builtin_amdgcn_s_setprio(1);
-      const int i = ph >> 1;
-      const bool do_s = i >= first && i < n_steps;
-      const bool do_g = i - 1 >= first && i - 1 < n_steps;
-      const uint16_t* qb_ = sQ[i & 1] + rfrag;
-      const uint16_t* ob_ = sO[i & 1] + rfrag;
-      const uint16_t* qtb_ = sQt[(i + 2) % 3] + ifrag;  // step i-1
-      const uint16_t* otb_ = sOt[(i + 2) % 3] + ifrag;
-      // dP accumulators start at -D_q, so they end as dP - D (one subtraction
-      // per element fewer in the vector phase)
-      const float* dneg = sD[i % 3];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        s[qb] = zero16();
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 d4 = *(const float4*)(&dneg[32 * qb + 8 * g + 4 * h]);
-          dp[qb][4 * g + 0] = d4.x;
-          dp[qb][4 * g + 1] = d4.y;
-          dp[qb][4 * g + 2] = d4.z;
-          dp[qb][4 * g + 3] = d4.w;
-        }
-      }
-      if (do_s && do_g) {
-        // steady state: the four products interleaved in one pipelined run;
-        // the staging write is unconditional (past the last step it rewrites
-        // buffers no one reads again)
-        mma_pipeline<4 * NS, 3>(
-            [&](int k) {
-              const int x = k / 4;
-              switch (k % 4) {
-                case 0: return r_addr(qb_, x);
-                case 1: return i_addr(otb_, x);
-                case 2: return r_addr(ob_, x);
-                default: return i_addr(qtb_, x);
-              }
-            },
-            [&](int k, u32x4_t a) {
-              const int x = k / 4;
-              switch (k % 4) {
-                case 0: s_mma(x, a); break;
-                case 1: dv_mma(x, a); break;
-                case 2: dp_mma(x, a); break;
-                default: dk_mma(x, a); break;
-              }
-            },
-            [&](int k) {
-              if (k % NS == NS / 2) store_part(i + 1, k / NS);
-            });
-      } else {
-        if (i + 1 < n_steps) store_tile(i + 1);
-        if (do_s) {
-#pragma unroll
-          for (int x = 0; x < NS; ++x) {
-            s_mma(x, *(const u32x4_t*)r_addr(qb_, x));
-            dp_mma(x, *(const u32x4_t*)r_addr(ob_, x));
-          }
-        }
-        if (do_g) {
-#pragma unroll
-          for (int x = 0; x < NG; ++x) {
-            dv_mma(x, *(const u32x4_t*)i_addr(otb_, x));
-            dk_mma(x, *(const u32x4_t*)i_addr(qtb_, x));
-          }
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-    } else if (ph >= 0) {
-      // ---------------- V-phase i
-      const int i = (ph - 1) >> 1;
-      if (i + 2 < n_steps) load_tile(i_begin + (i + 2) * BQ);
-      if (i >= first && i < n_steps) {
-        const int i0 = i_begin + i * BQ;
-        const float* lv = sL[i % 3];
-        // masked and unmasked variants as separate code (the mask is needed
-        // only where a query block crosses this wave's keys)
-        auto grad = [&](int qb, auto masked) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float4 l4 = *(const float4*)(&lv[32 * qb + 8 * g + 4 * h]);
-            const float la[4] = {l4.x, l4.y, l4.z, l4.w};
-            float p[4], ds[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              float pv = fast_exp2(fmaf(s[qb][r], c, -la[e]));
-              if constexpr (decltype(masked)::value)
-                if (key > i0 + 32 * qb + 8 * g + 4 * h + e) pv = 0.0f;
-              p[e] = pv;
-              ds[e] = pv * dp[qb][r];  // dp already holds dP - D
-            }
-            pk[qb][2 * g + 0] = TR::pack2(p[0], p[1]);
-            pk[qb][2 * g + 1] = TR::pack2(p[2], p[3]);
-            dsk[qb][2 * g + 0] = TR::pack2(ds[0], ds[1]);
-            dsk[qb][2 * g + 1] = TR::pack2(ds[2], ds[3]);
-          }
-        };
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          if (wave_uniform(CAUSAL && i0 + 32 * qb < kw + 31)) grad(qb, std::true_type{});
-          else grad(qb, std::false_type{});
-        }
-      }
-    }
-    lds_barrier();
-  }
-
-  if (key < N) {
-    uint16_t* dkrow = dK + head_off + (size_t)key * D;
-    uint16_t* dvrow = dV + head_off + (size_t)key * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * db + 8 * g + 4 * h;
-        *(u32x2_t*)(dkrow + col) =
-            u32x2_t{TR::pack2(acc_dk[db][4 * g + 0] * scale, acc_dk[db][4 * g + 1] * scale),
-                    TR::pack2(acc_dk[db][4 * g + 2] * scale, acc_dk[db][4 * g + 3] * scale)};
-        *(u32x2_t*)(dvrow + col) =
-            u32x2_t{TR::pack2(acc_dv[db][4 * g + 0], acc_dv[db][4 * g + 1]),
-                    TR::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3])};
-      }
-  }
-}
-
-// dK, dV software-pipelined inside each wavefront (d = 128: one wavefront per
-// SIMD, 4 x 32 keys per workgroup).  Query rows stream through LDS in stages
+// dK, dV software-pipelined inside each wavefront: one wavefront per SIMD,
+// 4 x 32 keys per workgroup (d = 64 and 128).  Query rows stream through LDS in stages
 // of 64 (two blocks of 32); iteration b of a wavefront issues
 //   matrix: S_{b+1} = Q_{b+1} K^T, dP_{b+1} = dO_{b+1} V^T - D   (VGPR results)
 //           dV^T += dO_{b-1}^T P_{b-1}, dK^T += Q_{b-1}^T dS_{b-1}  (AGPR accumulators)
@@ -400,9 +99,9 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   constexpr int ROWSTEP = NT / CPR;         // rows between a thread's staging chunks
   constexpr int NCH = BQ / ROWSTEP;         // staging chunks per thread and tensor
   constexpr int NSL = 4 * NKS;              // products per iteration
-  constexpr int AH = 4;                     // operand reads issued ahead of their product
+  constexpr int AH = 8;                     // operand reads issued ahead of their product
   static_assert(2 * NDB == NKS, "S, dV, dK, dP products interleave one to one");
-  static_assert(NSL == 32, "vector work: one stage of one score per product");
+  static_assert(NSL == 32 || NSL == 16, "vector work schedule below");
   static_assert(4 * STG <= 160 * 1024, "four stages fit in LDS");
 
   __shared__ __attribute__((aligned(16))) char smem[4 * STG];
@@ -548,7 +247,10 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     auto vwork = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (k == 2 * r) {
+        // score r: scale, shift and exp2 at product v0(r), the rest one product later
+        constexpr int V0 = NSL / 16;
+        const int v0 = V0 * r, v1 = v0 + 1 < NSL ? v0 + 1 : v0;
+        if (k == v0) {
           float x = fmaf(sc[PAR][r], c, -lr[PAR][r]);
           if constexpr (MASKED) {
             // score r = 4g + e is S row 8g + 4h + e: query perm(8(g%2) + 4h + e) + 16(g/2)
@@ -558,7 +260,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
           }
           pe[r] = fast_exp2(x);
         }
-        if (k == 2 * r + 1) {
+        if (k == v1) {
           dsv[r] = pe[r] * dp[PAR][r];  // dp holds dP - D
           if (r & 1) {
             pk[PAR][r / 8][(r / 2) % 4] = TR::pack2(pe[r - 1], pe[r]);
@@ -647,8 +349,10 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       TR::mma_avv(acc_dk[x % NDB], tr_frag(sb, 1, 0, x / NDB, x % NDB), dsk[1][x / NDB]);
     }
   }
-  static_assert(NDB == 4, "wait operand list");
-  mfma_wait_a(acc_dk[0], acc_dk[1], acc_dk[2], acc_dk[3], acc_dv[0], acc_dv[1], acc_dv[2], acc_dv[3]);
+  if constexpr (NDB == 4)
+    mfma_wait_a(acc_dk[0], acc_dk[1], acc_dk[2], acc_dk[3], acc_dv[0], acc_dv[1], acc_dv[2], acc_dv[3]);
+  else
+    mfma_wait_a(acc_dk[0], acc_dk[1], acc_dv[0], acc_dv[1]);
 
   if (key < N) {
     uint16_t* dkrow = dK + head_off + (size_t)key * D;
@@ -940,23 +644,13 @@ static hipError_t prep_t(const BwdArgs& a) {
 
 template <class TR, int D, bool CAUSAL>
 static hipError_t dkdv_t(const BwdArgs& a) {
-  if constexpr (D == 64) {
-    const int n_ktiles = (a.N + 255) / 256;
-    const uint32_t total = (uint32_t)(n_ktiles * a.BH);
-    hipLaunchKernelGGL((bwd_dkdv2_kernel<TR, D, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                       a.N, n_ktiles, total, a.c, a.scale);
-    return hipGetLastError();
-  } else {
-    const int n_ktiles = (a.N + 127) / 128;
-    const uint32_t total = (uint32_t)(n_ktiles * a.BH);
-    hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                       a.N, n_ktiles, total, a.c, a.scale);
-    return hipGetLastError();
-  }
+  const int n_ktiles = (a.N + 127) / 128;
+  const uint32_t total = (uint32_t)(n_ktiles * a.BH);
+  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                     a.N, n_ktiles, total, a.c, a.scale);
+  return hipGetLastError();
 }
 
 template <class TR, int D, bool CAUSAL>
