@@ -100,6 +100,8 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   constexpr int NCH = BQ / ROWSTEP;         // staging chunks per thread and tensor
   constexpr int NSL = 4 * NKS;              // products per iteration
   constexpr int AH = 8;                     // operand reads issued ahead of their product
+  constexpr int kW0 = NSL / 4;              // first staging write (product index, PAR 1)
+  static_assert(kW0 + 2 * (BQ / (NT / (D / 8))) + 1 <= NSL, "staging writes fit the iteration");
   static_assert(2 * NDB == NKS, "S, dV, dK, dP products interleave one to one");
   static_assert(NSL == 32 || NSL == 16, "vector work schedule below");
   static_assert(4 * STG <= 160 * 1024, "four stages fit in LDS");
@@ -166,26 +168,44 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const uint32_t s_off = (uint32_t)(tid / CPR) * RBL + (tid % CPR) * 16;
   const int vrow = (lane & 32) + perm(lane & 31);
   const uint32_t v_off = OFF_L + 4 * BQ * wu + 4 * lane;
+  // The loaded values are only used when they are written to LDS (a whole
+  // iteration later), so no wait for the loads stalls the products.
   u32x4_t sq[NCH], so[NCH];
-  float vreg = 0.0f;
-  auto load_stage = [&](int i0) __attribute__((always_inline)) {
+  float vraw = 0.0f;
+  int vidx = 0;
+  // staging part j < NCH: Q chunk j; j < 2 NCH: dO chunk j - NCH; j = 2 NCH: the vector
+  constexpr int NPART = 2 * NCH + 1;
+  auto load_part = [&](int i0, int j) __attribute__((always_inline)) {
     const uint32_t base = g_off + (uint32_t)i0 * RB;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      sq[i] = buf_load16(qres, base + ROWSTEP * i * RB);
-      so[i] = buf_load16(ores, base + ROWSTEP * i * RB);
+    if (j < NCH) {
+      sq[j] = buf_load16(qres, base + ROWSTEP * j * RB);
+    } else if (j < 2 * NCH) {
+      so[j - NCH] = buf_load16(ores, base + ROWSTEP * (j - NCH) * RB);
+    } else {
+      vidx = i0 + vrow;
+      vraw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vres, (uint32_t)vidx * 4, 0, 0));
     }
-    // rows past the end: LSE = +inf makes P = 0; D = 0.  D is stored negated:
-    // it initialises the dP accumulators.
-    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vres, (uint32_t)(i0 + vrow) * 4, 0, 0));
-    const bool in = i0 + vrow < N;
-    vreg = is_d ? (in ? -x : 0.0f) : (in ? x * kLog2e : INFINITY);
   };
-  auto store_chunk = [&](uint32_t sb, int i) __attribute__((always_inline)) {
-    *(u32x4_t*)(smem + sb + s_off + ROWSTEP * i * RBL) = sq[i];
-    *(u32x4_t*)(smem + sb + OFF_O + s_off + ROWSTEP * i * RBL) = so[i];
+  auto store_part = [&](uint32_t sb, int j) __attribute__((always_inline)) {
+    if (j < NCH) {
+      *(u32x4_t*)(smem + sb + s_off + ROWSTEP * j * RBL) = sq[j];
+    } else if (j < 2 * NCH) {
+      *(u32x4_t*)(smem + sb + OFF_O + s_off + ROWSTEP * (j - NCH) * RBL) = so[j - NCH];
+    } else {
+      // rows past the end: LSE = +inf makes P = 0; D = 0.  D is stored
+      // negated: it initialises the dP accumulators.
+      const bool in = vidx < N;
+      *(float*)(smem + sb + v_off) = is_d ? (in ? -vraw : 0.0f) : (in ? vraw * kLog2e : INFINITY);
+    }
   };
-  auto store_vec = [&](uint32_t sb) __attribute__((always_inline)) { *(float*)(smem + sb + v_off) = vreg; };
+  auto load_stage = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NPART; ++j) load_part(i0, j);
+  };
+  auto store_stage = [&](uint32_t sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NPART; ++j) store_part(sb, j);
+  };
 
   // ---- register sets of the pipeline (index: block parity)
   f32x16_t sc[2], dp[2];
@@ -268,11 +288,12 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
           }
         }
       }
+      // staging: one load per product from the start of PAR 0, one LDS
+      // write per product from kW0 of PAR 1
       if constexpr (PAR == 0) {
-        if (k == 0) load_stage(i_ld);
+        if (k < NPART) load_part(i_ld, k);
       } else {
-        if (k >= NSL / 4 && k < NSL / 4 + NCH) store_chunk(sbw, k - NSL / 4);
-        if (k == NSL / 4 + NCH) store_vec(sbw);
+        if (k >= kW0 && k < kW0 + NPART) store_part(sbw, k - kW0);
       }
     };
     static_for<0, NSL>([&](auto kc) __attribute__((always_inline)) {
@@ -299,13 +320,9 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   // ---- prologue: stages 0 and 1 in slots 0 and 1, slot 3 zeroed (the first
   // iteration multiplies it by zero P and dS); S_0, dP_0; first operands
   load_stage(i_begin);
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) store_chunk(0, i);
-  store_vec(0);
+  store_stage(0);
   load_stage(i_begin + BQ);
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) store_chunk(STG, i);
-  store_vec(STG);
+  store_stage(STG);
   for (int i = tid; i < 2 * BQ * RBL / 16; i += NT) *(u32x4_t*)(smem + 3 * STG + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
   lds_barrier();
   load_vecs(0, 0, dp[0], lr[0]);
