@@ -460,6 +460,10 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = zero16();
   f32x16_t s[NKB], dp[NKB];
+  // dP accumulators start at -D (one constant register block), so they end as dP - D
+  f32x16_t negd;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negd[i] = -dd;
   uint32_t dsk[NKB][8];
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
@@ -534,7 +538,10 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   auto s_addr = [&](const uint16_t* b_, int i) { return b_ + 32 * (i % NKB) * KS + 16 * (i / NKB); };
   auto q_addr = [&](const uint16_t* b_, int i) { return b_ + ((2 * (i / NDB)) * D + 32 * (i % NDB)) * 8; };
   auto s_mma = [&](int i, u32x4_t a) { s[i % NKB] = TR::mfma(a, qf[i / NKB], s[i % NKB]); };
-  auto dp_mma = [&](int i, u32x4_t a) { dp[i % NKB] = TR::mfma(a, of[i / NKB], dp[i % NKB]); };
+  auto dp_mma = [&](int i, u32x4_t a) {
+    if (i < NKB) dp[i] = TR::mma_c(a, of[0], negd);  // first k-step: -D + products
+    else dp[i % NKB] = TR::mfma(a, of[i / NKB], dp[i % NKB]);
+  };
   auto dq_mma = [&](int i, u32x4_t a) {
     const int kt = i / NDB, db = i % NDB;
     const int kb = kt / 2, t = kt % 2;
@@ -564,7 +571,6 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         s[kb] = zero16();
-        dp[kb] = zero16();
       }
       if (do_s && do_q) {
         // steady state: S, dP, dQ products interleaved in one pipelined run,
@@ -622,7 +628,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                   const int key = j0 + 32 * kb + 8 * ((r + e) / 4) + 4 * h + ((r + e) % 4);
                   if (key >= N || (CAUSAL && key > qrow)) p = 0.0f;
                 }
-                d2[e] = p * (dp[kb][r + e] - dd);
+                d2[e] = p * dp[kb][r + e];
               }
               dsk[kb][r / 2] = TR::pack2(d2[0], d2[1]);
             }

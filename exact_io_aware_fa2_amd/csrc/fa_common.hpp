@@ -81,6 +81,12 @@ struct BF16 {
   __device__ static inline void mma_avv(f32x16_t& c, u32x4_t a, u32x4_t b) {
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
   }
+  // A B + c into fresh VGPRs, c (VGPRs) left unchanged
+  __device__ static inline f32x16_t mma_c(u32x4_t a, u32x4_t b, const f32x16_t& c) {
+    f32x16_t d;
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+  }
 };
 
 struct F16 {
@@ -121,6 +127,12 @@ struct F16 {
   }
   __device__ static inline void mma_avv(f32x16_t& c, u32x4_t a, u32x4_t b) {
     asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
+  // A B + c into fresh VGPRs, c (VGPRs) left unchanged
+  __device__ static inline f32x16_t mma_c(u32x4_t a, u32x4_t b, const f32x16_t& c) {
+    f32x16_t d;
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
   }
 };
 
