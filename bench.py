@@ -46,7 +46,7 @@ KERNEL_SOURCES = {
 }
 # substrings of the mangled kernel names, as rocprofv3 reports them
 KERNEL_SYMBOLS = {"fwd": "fwd16_p", "prep": "bwd_pre_kernel", "dkdv": "bwd_dkdv",
-                  "dq": "bwd_dq_kernel"}
+                  "dq": "bwd_dq"}
 
 
 def src_hash(kernel: str) -> str:

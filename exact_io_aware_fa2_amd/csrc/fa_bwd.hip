@@ -103,6 +103,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   constexpr int kW0 = NSL / 4;              // first staging write (product index, PAR 1)
   static_assert(kW0 + 2 * (BQ / (NT / (D / 8))) + 1 <= NSL, "staging writes fit the iteration");
   static_assert(2 * NDB == NKS, "S, dV, dK, dP products interleave one to one");
+  static_assert(NSL % AH == 0, "operand of product f of an iteration sits in fr[f % AH]");
   static_assert(NSL == 32 || NSL == 16, "vector work schedule below");
   static_assert(4 * STG <= 160 * 1024, "four stages fit in LDS");
 
@@ -654,7 +655,275 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
 }
 
+// dQ software-pipelined inside each wavefront: one wavefront per SIMD, 4 x 32
+// query rows per workgroup; Q, dO (B operands) and the dQ accumulators stay in
+// AGPRs.  Key rows stream through LDS in stages of 64 (two blocks of 32), with
+// the layout of bwd_dkdv_pipe_kernel (padded rows; S^T row m holds key
+// perm(m) of its 16).  Iteration b of a wavefront issues
+//   matrix: S^T_{b+1} = K_{b+1} Q^T, dP^T_{b+1} = V_{b+1} dO^T - D,
+//           dQ^T += K_{b-1}^T dS^T_{b-1}
+//   vector: P_b = exp2(S^T_b c - LSE log2 e), dS_b = P_b (dP_b - D), rounded
+// interleaved product by product.  Each lane owns one query row, so LSE and D
+// are per-lane constants (D enters as the dP accumulators' initial value).
+// Keys past the end need no mask: their K and V rows read as zeros, so their
+// dS multiplies a zero row of K.
+template <class TR, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                        const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                        const float* __restrict__ LSE, const float* __restrict__ Dvec,
+                        uint16_t* __restrict__ dQ, int N, int n_qtiles, uint32_t total, float c,
+                        float scale) {
+  constexpr int NT = 256;
+  constexpr int BR = 128;                   // query rows per workgroup
+  constexpr int BC = 64;                    // keys per stage
+  constexpr int KS = D + 8;                 // padded LDS row (elements)
+  constexpr int RBL = 2 * KS;               // LDS row bytes
+  constexpr uint32_t RB = 2 * D;            // global row bytes
+  constexpr int NKS = D / 16;               // k-steps of S and dP
+  constexpr int NDB = D / 32;               // 32-column blocks of dQ
+  constexpr int OFF_V = BC * RBL;           // stage layout (bytes): K, then V
+  constexpr int STG = 2 * BC * RBL;
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int ROWSTEP = NT / CPR;         // rows between a thread's staging chunks
+  constexpr int NCH = BC / ROWSTEP;         // staging chunks per thread and tensor
+  constexpr int NPART = 2 * NCH;
+  constexpr int NSL = 3 * NKS;              // products per iteration (S, dQ, dP)
+  constexpr int AH = NSL % 8 == 0 ? 8 : 6;  // operand reads issued ahead of their product
+  constexpr int kW0 = NSL / 4;              // first staging write (product index, PAR 1)
+  static_assert(2 * NDB == NKS, "S, dQ, dP products interleave one to one");
+  static_assert(NSL % AH == 0, "operand of product f of an iteration sits in fr[f % AH]");
+  static_assert(NPART <= NSL && kW0 + NPART <= NSL, "staging fits the iteration");
+  static_assert(4 * STG <= 160 * 1024, "four stages fit in LDS");
+
+  __shared__ __attribute__((aligned(16))) char smem[4 * STG];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const uint32_t lid = xcd_remap(blockIdx.x, total);
+  const int bh = lid / n_qtiles;
+  int qt = lid % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;       // longest rows first
+  const int q0 = qt * BR;
+  const int qw = q0 + 32 * w;               // first query row of this wavefront
+  const int qrow = qw + l32;
+  const size_t head_off = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * RB;
+
+  // Q and dO rows of this wavefront's queries as B operands (column = query)
+  u32x4_t qf[NKS], of[NKS];
+  {
+    const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
+    const rsrc_t ores = make_rsrc(dO + head_off, head_bytes);
+    const uint32_t off = (uint32_t)qrow * RB + 16 * h;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = buf_load16(qres, off + 32 * ks);
+      of[ks] = buf_load16(ores, off + 32 * ks);
+    }
+  }
+  // rows past the end: P = exp2(-inf) = 0, so dS = 0 there
+  const float lq = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
+  const float dd = qrow < N ? Dvec[(size_t)bh * N + qrow] : 0.0f;
+  f32x16_t negd;  // initial value of the dP accumulators
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negd[i] = -dd;
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+
+  // key row (within its 32-key block) of S^T row m
+  auto perm = [](int m) { return (m & 16) | ((m & 3) << 2) | ((m >> 2) & 3); };
+  const uint32_t rbase = (uint32_t)(perm(l32) * RBL + 16 * h);
+  const int L16 = lane & 15, G = lane >> 4;
+  const uint32_t tbase = (uint32_t)((h + 4 * (L16 >> 2)) * RBL + (16 * (G & 1) + 4 * (L16 & 3)) * 2);
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int n_st = (kv_end + BC - 1) / BC;
+
+  // ---- staging: chunk i of this thread is row tid / CPR + ROWSTEP i, column
+  // chunk tid % CPR, of both K and V (part j < NCH: K chunk j, else V chunk j - NCH)
+  const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
+  const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
+  const uint32_t g_off = (uint32_t)(tid / CPR) * RB + (tid % CPR) * 16;
+  const uint32_t s_off = (uint32_t)(tid / CPR) * RBL + (tid % CPR) * 16;
+  u32x4_t sk[NCH], sv[NCH];
+  auto load_part = [&](int j0, int j) __attribute__((always_inline)) {
+    const uint32_t base = g_off + (uint32_t)j0 * RB;
+    if (j < NCH) sk[j] = buf_load16(kres, base + ROWSTEP * j * RB);
+    else sv[j - NCH] = buf_load16(vres, base + ROWSTEP * (j - NCH) * RB);
+  };
+  auto store_part = [&](uint32_t sb, int j) __attribute__((always_inline)) {
+    if (j < NCH) *(u32x4_t*)(smem + sb + s_off + ROWSTEP * j * RBL) = sk[j];
+    else *(u32x4_t*)(smem + sb + OFF_V + s_off + ROWSTEP * (j - NCH) * RBL) = sv[j - NCH];
+  };
+
+  // ---- register sets of the pipeline (index: block parity)
+  f32x16_t sc[2], dp[2];
+  u32x4_t dsk[2][2];  // [set][k-step t]: dS rounded, packed in pairs
+
+  // A operand of S^T (tensor 0: K) or dP^T (tensor 1: V) for k-step ks
+  auto row_frag = [&](uint32_t sb, int bb, int tensor, int ks) __attribute__((always_inline)) -> u32x4_t {
+    return *(const u32x4_t*)(smem + sb + tensor * OFF_V + rbase + bb * 32 * RBL + 32 * ks);
+  };
+  // A operand of dQ^T (K^T) for k-step t, column block db
+  auto tr_frag = [&](uint32_t sb, int bb, int t, int db) __attribute__((always_inline)) -> u32x4_t {
+    const char* p = smem + sb + tbase + (32 * bb + 16 * t) * RBL + 64 * db;
+    const u32x2_t a = lds_read_tr(p), b = lds_read_tr(p + 2 * RBL);
+    return u32x4_t{a[0], a[1], b[0], b[1]};
+  };
+  // operand of product k of an iteration: (S, dQ, dP)[k % 3] of index k / 3;
+  // sb1: stage of block b+1, sb2: stage of block b-1, nb: their half (1 - b % 2)
+  auto frag = [&](int k, uint32_t sb1, uint32_t sb2, int nb) __attribute__((always_inline)) -> u32x4_t {
+    const int x = k / 3;
+    switch (k % 3) {
+      case 0: return row_frag(sb1, nb, 0, x);
+      case 1: return tr_frag(sb2, nb, x / NDB, x % NDB);
+      default: return row_frag(sb1, nb, 1, x);
+    }
+  };
+  u32x4_t fr[AH];  // operands of the next AH products, carried across iterations
+
+  // ---- one iteration.  PAR = b % 2 selects the register sets; j0: first key
+  // of block b; (nsb1, nsb2): stages of the next iteration.  PAR 0 requests the
+  // stage after next (keys j_ld), PAR 1 writes it to slot sbw.
+  auto iteration = [&](auto par_c, auto masked_c, uint32_t sb1, uint32_t sb2, uint32_t nsb1, uint32_t nsb2,
+                       int j0, int j_ld, uint32_t sbw) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par_c)::value;
+    constexpr bool MASKED = decltype(masked_c)::value;
+    constexpr int NB = 1 - PAR;
+    // S_b, dP_b were written by matrix instructions, dS of block b-1 by vector
+    // instructions: all of them ordered before what reads them next
+    mfma_wait_v(sc[PAR], dp[PAR]);
+    asm volatile("" : "+v"(dsk[NB][0]), "+v"(dsk[NB][1]));
+
+    // causal: key j0 + koff(r) is visible to this lane's row iff koff(r) <= thr
+    const int thr = qrow - j0 - h;
+    float pe[16], dsv[16];
+    auto vwork = [&](int k) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // score r: scale, shift and exp2 at product v0(r), the rest one later
+        const int v0 = r * NSL / 16, v1 = v0 + 1 < NSL ? v0 + 1 : v0;
+        if (k == v0) {
+          float x = fmaf(sc[PAR][r], c, -lq);
+          if constexpr (MASKED) {
+            // score r = 4g + e is S^T row 8g + 4h + e: key perm(8(g%2) + 4h + e) + 16(g/2)
+            const int g = r / 4, e = r % 4;
+            const int koff = 16 * (g / 2) + 4 * e + 2 * (g % 2);
+            x = koff <= thr ? x : -INFINITY;
+          }
+          pe[r] = fast_exp2(x);
+        }
+        if (k == v1) {
+          dsv[r] = pe[r] * dp[PAR][r];  // dp holds dP - D
+          if (r & 1) dsk[PAR][r / 8][(r / 2) % 4] = TR::pack2(dsv[r - 1], dsv[r]);
+        }
+      }
+      if constexpr (PAR == 0) {
+        if (k < NPART) load_part(j_ld, k);
+      } else {
+        if (k >= kW0 && k < kW0 + NPART) store_part(sbw, k - kW0);
+      }
+    };
+    static_for<0, NSL>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int x = k / 3;
+      const u32x4_t a = fr[k % AH];
+      if constexpr (k + AH < NSL) fr[k % AH] = frag(k + AH, sb1, sb2, NB);
+      else fr[k % AH] = frag(k + AH - NSL, nsb1, nsb2, PAR);
+      if constexpr (k % 3 == 0) {
+        if constexpr (x == 0) sc[NB] = TR::mma0_vva(a, qf[0]);
+        else TR::mma_vva(sc[NB], a, qf[x]);
+      } else if constexpr (k % 3 == 1) {
+        TR::mma_avv(acc[x % NDB], a, dsk[NB][x / NDB]);
+      } else {
+        if constexpr (x == 0) dp[NB] = TR::mma_c_vva(a, of[0], negd);
+        else TR::mma_vva(dp[NB], a, of[x]);
+      }
+      vwork(k);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // ---- prologue: stages 0 and 1 in slots 0 and 1, slot 3 zeroed (the first
+  // iteration multiplies it by zero dS); S_0, dP_0; first operands
+#pragma unroll
+  for (int j = 0; j < NPART; ++j) load_part(0, j);
+#pragma unroll
+  for (int j = 0; j < NPART; ++j) store_part(0, j);
+#pragma unroll
+  for (int j = 0; j < NPART; ++j) load_part(BC, j);
+#pragma unroll
+  for (int j = 0; j < NPART; ++j) store_part(STG, j);
+  for (int i = tid; i < STG / 16; i += NT) *(u32x4_t*)(smem + 3 * STG + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
+  lds_barrier();
+  mma_pipeline<2 * NKS, 3>([&](int x) { return smem + ((x & 1) ? OFF_V : 0) + rbase + 32 * (x >> 1); },
+                           [&](int x, u32x4_t a) {
+                             const int ks = x >> 1;
+                             if (x & 1) {
+                               if (ks == 0) dp[0] = TR::mma_c_vva(a, of[0], negd);
+                               else TR::mma_vva(dp[0], a, of[ks]);
+                             } else if (ks == 0) {
+                               sc[0] = TR::mma0_vva(a, qf[0]);
+                             } else {
+                               TR::mma_vva(sc[0], a, qf[ks]);
+                             }
+                           },
+                           [](int) {});
+#pragma unroll
+  for (int t = 0; t < 2; ++t) dsk[1][t] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int x = 0; x < AH; ++x) fr[x] = frag(x, 0u, 3u * STG, 1);
+
+  // ---- pairs of iterations over the stages.  Causal: the blocks of the last
+  // two stages (each wavefront's diagonal block and the fully masked blocks
+  // past it) are masked.
+  auto pair = [&](auto masked_c, int s) __attribute__((always_inline)) {
+    const uint32_t b0 = (uint32_t)(s & 3) * STG;
+    const uint32_t bp1 = (uint32_t)((s + 1) & 3) * STG;
+    const uint32_t bm1 = (uint32_t)((s + 3) & 3) * STG;
+    const uint32_t bp2 = (uint32_t)((s + 2) & 3) * STG;
+    const int j0 = BC * s;
+    iteration(std::integral_constant<int, 0>{}, masked_c, b0, bm1, bp1, b0, j0, j0 + 2 * BC, bp2);
+    iteration(std::integral_constant<int, 1>{}, masked_c, bp1, b0, bp1, b0, j0 + 32, 0, bp2);
+    lds_barrier();
+  };
+  const int n_open = CAUSAL ? max(0, n_st - 2) : n_st;
+  int s = 0;
+  for (; s < n_open; ++s) pair(std::false_type{}, s);
+  for (; s < n_st; ++s) pair(std::true_type{}, s);
+
+  // ---- last block: its dQ products (register set 1)
+  {
+    const uint32_t sb = (uint32_t)((n_st - 1) & 3) * STG;
+    asm volatile("" : "+v"(dsk[1][0]), "+v"(dsk[1][1]));
+#pragma unroll
+    for (int x = 0; x < NKS; ++x) TR::mma_avv(acc[x % NDB], tr_frag(sb, 1, x / NDB, x % NDB), dsk[1][x / NDB]);
+  }
+  if constexpr (NDB == 4) mfma_wait_a(acc[0], acc[1], acc[2], acc[3]);
+  else mfma_wait_a(acc[0], acc[1]);
+
+  if (qrow < N) {
+    uint16_t* drow = dQ + head_off + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * h;
+        *(u32x2_t*)(drow + col) =
+            u32x2_t{TR::pack2(acc[db][4 * g + 0] * scale, acc[db][4 * g + 1] * scale),
+                    TR::pack2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale)};
+      }
+  }
+}
+
 // ------------------------------------------------------------------ launch
+
 
 template <class TR, int D>
 static hipError_t prep_t(const BwdArgs& a) {
@@ -677,15 +946,31 @@ static hipError_t dkdv_t(const BwdArgs& a) {
 }
 
 template <class TR, int D, bool CAUSAL>
-static hipError_t dq_t(const BwdArgs& a) {
-  const int n_qtiles = (a.N + 255) / 256;
+static hipError_t dq_pipe_t(const BwdArgs& a) {
+  const int n_qtiles = (a.N + 127) / 128;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  constexpr int BC = D == 128 ? 32 : 64;  // keys per tile (register budget at two waves per SIMD)
-  hipLaunchKernelGGL((bwd_dq_kernel<TR, D, BC, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.N, n_qtiles, total,
                      a.c, a.scale);
   return hipGetLastError();
+}
+
+// dQ: the pipelined kernel at d = 128; at d = 64 (twice the vector work per
+// product) the two-wavefront ping-pong kernel is faster
+template <class TR, int D, bool CAUSAL>
+static hipError_t dq_t(const BwdArgs& a) {
+  if constexpr (D == 128) {
+    return dq_pipe_t<TR, D, CAUSAL>(a);
+  } else {
+    const int n_qtiles = (a.N + 255) / 256;
+    const uint32_t total = (uint32_t)(n_qtiles * a.BH);
+    hipLaunchKernelGGL((bwd_dq_kernel<TR, D, 64, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.N, n_qtiles, total,
+                       a.c, a.scale);
+    return hipGetLastError();
+  }
 }
 
 template <class TR>

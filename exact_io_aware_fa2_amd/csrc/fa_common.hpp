@@ -87,6 +87,11 @@ struct BF16 {
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
     return d;
   }
+  __device__ static inline f32x16_t mma_c_vva(u32x4_t a, u32x4_t b, const f32x16_t& c) {
+    f32x16_t d;
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+    return d;
+  }
 };
 
 struct F16 {
@@ -132,6 +137,11 @@ struct F16 {
   __device__ static inline f32x16_t mma_c(u32x4_t a, u32x4_t b, const f32x16_t& c) {
     f32x16_t d;
     asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+  }
+  __device__ static inline f32x16_t mma_c_vva(u32x4_t a, u32x4_t b, const f32x16_t& c) {
+    f32x16_t d;
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
     return d;
   }
 };
