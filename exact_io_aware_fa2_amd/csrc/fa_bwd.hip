@@ -170,42 +170,36 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int vrow = (lane & 32) + perm(lane & 31);
   const uint32_t v_off = OFF_L + 4 * BQ * wu + 4 * lane;
   // The loaded values are only used when they are written to LDS (a whole
-  // iteration later), so no wait for the loads stalls the products.
-  u32x4_t sq[NCH], so[NCH];
-  float vraw = 0.0f;
-  int vidx = 0;
+  // iteration later), so no wait for the loads stalls the products.  Set 1
+  // of the staging registers is used only by the prologue (two stages in
+  // flight at once).
+  u32x4_t sq[2][NCH], so[2][NCH];
+  float vraw[2] = {0.0f, 0.0f};
+  int vidx[2] = {0, 0};
   // staging part j < NCH: Q chunk j; j < 2 NCH: dO chunk j - NCH; j = 2 NCH: the vector
   constexpr int NPART = 2 * NCH + 1;
-  auto load_part = [&](int i0, int j) __attribute__((always_inline)) {
+  auto load_part = [&](int i0, int j, int t = 0) __attribute__((always_inline)) {
     const uint32_t base = g_off + (uint32_t)i0 * RB;
     if (j < NCH) {
-      sq[j] = buf_load16(qres, base + ROWSTEP * j * RB);
+      sq[t][j] = buf_load16(qres, base + ROWSTEP * j * RB);
     } else if (j < 2 * NCH) {
-      so[j - NCH] = buf_load16(ores, base + ROWSTEP * (j - NCH) * RB);
+      so[t][j - NCH] = buf_load16(ores, base + ROWSTEP * (j - NCH) * RB);
     } else {
-      vidx = i0 + vrow;
-      vraw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vres, (uint32_t)vidx * 4, 0, 0));
+      vidx[t] = i0 + vrow;
+      vraw[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vres, (uint32_t)vidx[t] * 4, 0, 0));
     }
   };
-  auto store_part = [&](uint32_t sb, int j) __attribute__((always_inline)) {
+  auto store_part = [&](uint32_t sb, int j, int t = 0) __attribute__((always_inline)) {
     if (j < NCH) {
-      *(u32x4_t*)(smem + sb + s_off + ROWSTEP * j * RBL) = sq[j];
+      *(u32x4_t*)(smem + sb + s_off + ROWSTEP * j * RBL) = sq[t][j];
     } else if (j < 2 * NCH) {
-      *(u32x4_t*)(smem + sb + OFF_O + s_off + ROWSTEP * (j - NCH) * RBL) = so[j - NCH];
+      *(u32x4_t*)(smem + sb + OFF_O + s_off + ROWSTEP * (j - NCH) * RBL) = so[t][j - NCH];
     } else {
       // rows past the end: LSE = +inf makes P = 0; D = 0.  D is stored
       // negated: it initialises the dP accumulators.
-      const bool in = vidx < N;
-      *(float*)(smem + sb + v_off) = is_d ? (in ? -vraw : 0.0f) : (in ? vraw * kLog2e : INFINITY);
+      const bool in = vidx[t] < N;
+      *(float*)(smem + sb + v_off) = is_d ? (in ? -vraw[t] : 0.0f) : (in ? vraw[t] * kLog2e : INFINITY);
     }
-  };
-  auto load_stage = [&](int i0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < NPART; ++j) load_part(i0, j);
-  };
-  auto store_stage = [&](uint32_t sb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < NPART; ++j) store_part(sb, j);
   };
 
   // ---- register sets of the pipeline (index: block parity)
@@ -320,10 +314,14 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
   // ---- prologue: stages 0 and 1 in slots 0 and 1, slot 3 zeroed (the first
   // iteration multiplies it by zero P and dS); S_0, dP_0; first operands
-  load_stage(i_begin);
-  store_stage(0);
-  load_stage(i_begin + BQ);
-  store_stage(STG);
+#pragma unroll
+  for (int j = 0; j < NPART; ++j) load_part(i_begin, j, 0);
+#pragma unroll
+  for (int j = 0; j < NPART; ++j) load_part(i_begin + BQ, j, 1);
+#pragma unroll
+  for (int j = 0; j < NPART; ++j) store_part(0, j, 0);
+#pragma unroll
+  for (int j = 0; j < NPART; ++j) store_part(STG, j, 1);
   for (int i = tid; i < 2 * BQ * RBL / 16; i += NT) *(u32x4_t*)(smem + 3 * STG + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
   lds_barrier();
   load_vecs(0, 0, dp[0], lr[0]);
@@ -751,15 +749,16 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
   const uint32_t g_off = (uint32_t)(tid / CPR) * RB + (tid % CPR) * 16;
   const uint32_t s_off = (uint32_t)(tid / CPR) * RBL + (tid % CPR) * 16;
-  u32x4_t sk[NCH], sv[NCH];
-  auto load_part = [&](int j0, int j) __attribute__((always_inline)) {
+  // (set 1 of the staging registers: prologue only, two stages in flight)
+  u32x4_t sk[2][NCH], sv[2][NCH];
+  auto load_part = [&](int j0, int j, int t = 0) __attribute__((always_inline)) {
     const uint32_t base = g_off + (uint32_t)j0 * RB;
-    if (j < NCH) sk[j] = buf_load16(kres, base + ROWSTEP * j * RB);
-    else sv[j - NCH] = buf_load16(vres, base + ROWSTEP * (j - NCH) * RB);
+    if (j < NCH) sk[t][j] = buf_load16(kres, base + ROWSTEP * j * RB);
+    else sv[t][j - NCH] = buf_load16(vres, base + ROWSTEP * (j - NCH) * RB);
   };
-  auto store_part = [&](uint32_t sb, int j) __attribute__((always_inline)) {
-    if (j < NCH) *(u32x4_t*)(smem + sb + s_off + ROWSTEP * j * RBL) = sk[j];
-    else *(u32x4_t*)(smem + sb + OFF_V + s_off + ROWSTEP * (j - NCH) * RBL) = sv[j - NCH];
+  auto store_part = [&](uint32_t sb, int j, int t = 0) __attribute__((always_inline)) {
+    if (j < NCH) *(u32x4_t*)(smem + sb + s_off + ROWSTEP * j * RBL) = sk[t][j];
+    else *(u32x4_t*)(smem + sb + OFF_V + s_off + ROWSTEP * (j - NCH) * RBL) = sv[t][j - NCH];
   };
 
   // ---- register sets of the pipeline (index: block parity)
@@ -853,13 +852,13 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   // ---- prologue: stages 0 and 1 in slots 0 and 1, slot 3 zeroed (the first
   // iteration multiplies it by zero dS); S_0, dP_0; first operands
 #pragma unroll
-  for (int j = 0; j < NPART; ++j) load_part(0, j);
+  for (int j = 0; j < NPART; ++j) load_part(0, j, 0);
 #pragma unroll
-  for (int j = 0; j < NPART; ++j) store_part(0, j);
+  for (int j = 0; j < NPART; ++j) load_part(BC, j, 1);
 #pragma unroll
-  for (int j = 0; j < NPART; ++j) load_part(BC, j);
+  for (int j = 0; j < NPART; ++j) store_part(0, j, 0);
 #pragma unroll
-  for (int j = 0; j < NPART; ++j) store_part(STG, j);
+  for (int j = 0; j < NPART; ++j) store_part(STG, j, 1);
   for (int i = tid; i < STG / 16; i += NT) *(u32x4_t*)(smem + 3 * STG + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
   lds_barrier();
   mma_pipeline<2 * NKS, 3>([&](int x) { return smem + ((x & 1) ? OFF_V : 0) + rbase + 32 * (x >> 1); },
