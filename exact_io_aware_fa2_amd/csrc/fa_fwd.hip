@@ -678,7 +678,9 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   auto qk_step = [&](const uint16_t* kb_, int i) {  // i-th of NQK: ks = i / NKB, kb = i % NKB
     const int ks = i / NKB, kb = i % NKB;
     const u32x4_t kf = *(const u32x4_t*)(kb_ + 32 * kb * KS + 16 * ks);
-    s[kb] = TR::mfma(kf, qf[ks], s[kb]);
+    // the first k-step starts from a zero accumulator (inline constant: no
+    // vector instructions to clear the score registers)
+    s[kb] = TR::mfma(kf, qf[ks], ks == 0 ? zero16() : s[kb]);
   };
   auto pv_step = [&](const uint16_t* vb_, int i) {  // i-th of NPV: (kb, t) = i / NDB, db = i % NDB
     const int kt = i / NDB, db = i % NDB;
@@ -708,8 +710,6 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       const bool do_pv = j >= 1 && j - 1 < wave_tiles;
       const uint16_t* kb_ = sK[j & 1] + kfrag;
       const uint16_t* vb_ = sV[(j + 2) % 3] + vfrag;  // V_{j-1}
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
       if (do_qk && do_pv) {
         // Steady state, written as an explicit software pipeline: the products
         // alternate S and O steps, each operand is read from LDS kAhead steps
@@ -746,7 +746,7 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
               acc_o[db] = TR::mfma(a, pf, acc_o[db]);
             } else {
               const int ks = i / NKB, kb = i % NKB;
-              s[kb] = TR::mfma(a, qf[ks], s[kb]);
+              s[kb] = TR::mfma(a, qf[ks], ks == 0 ? zero16() : s[kb]);
             }
             // staging: one 16-byte LDS write every 8 steps
             if (stp % 8 == 3) {
