@@ -536,7 +536,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int ifrag = (h * D + l32) * 8;  // interleaved fragment of this lane
   auto s_addr = [&](const uint16_t* b_, int i) { return b_ + 32 * (i % NKB) * KS + 16 * (i / NKB); };
   auto q_addr = [&](const uint16_t* b_, int i) { return b_ + ((2 * (i / NDB)) * D + 32 * (i % NDB)) * 8; };
-  auto s_mma = [&](int i, u32x4_t a) { s[i % NKB] = TR::mfma(a, qf[i / NKB], s[i % NKB]); };
+  // first k-step from a zero accumulator (inline constant, no clearing)
+  auto s_mma = [&](int i, u32x4_t a) { s[i % NKB] = TR::mfma(a, qf[i / NKB], i < NKB ? zero16() : s[i % NKB]); };
   auto dp_mma = [&](int i, u32x4_t a) {
     if (i < NKB) dp[i] = TR::mma_c(a, of[0], negd);  // first k-step: -D + products
     else dp[i % NKB] = TR::mfma(a, of[i / NKB], dp[i % NKB]);
@@ -567,10 +568,6 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       const uint16_t* kb_ = sK[j & 1] + rfrag;
       const uint16_t* vb_ = sV[j & 1] + rfrag;
       const uint16_t* tb_ = sKt[(j + 2) % 3] + ifrag;  // K_{j-1}, interleaved
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = zero16();
-      }
       if (do_s && do_q) {
         // steady state: S, dP, dQ products interleaved in one pipelined run,
         // staging writes between them (past the last tile they rewrite a
