@@ -370,22 +370,25 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   else
     mfma_wait_a(acc_dk[0], acc_dk[1], acc_dv[0], acc_dv[1]);
 
-  if (key < N) {
-    uint16_t* dkrow = dK + head_off + (size_t)key * D;
-    uint16_t* dvrow = dV + head_off + (size_t)key * D;
+  // dK, dV rounded and stored as whole rows through LDS: after the last
+  // barrier every stage slot but that of the last block is free; dK of
+  // wavefront w goes to slot n_st + 1, dV to slot n_st + 2 (32 rows each)
+  u32x2_t ok[NDB][4], ov[NDB][4];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * db + 8 * g + 4 * h;
-        *(u32x2_t*)(dkrow + col) =
-            u32x2_t{TR::pack2(acc_dk[db][4 * g + 0] * scale, acc_dk[db][4 * g + 1] * scale),
-                    TR::pack2(acc_dk[db][4 * g + 2] * scale, acc_dk[db][4 * g + 3] * scale)};
-        *(u32x2_t*)(dvrow + col) =
-            u32x2_t{TR::pack2(acc_dv[db][4 * g + 0], acc_dv[db][4 * g + 1]),
-                    TR::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3])};
-      }
-  }
+    for (int g = 0; g < 4; ++g) {
+      ok[db][g] = u32x2_t{TR::pack2(acc_dk[db][4 * g + 0] * scale, acc_dk[db][4 * g + 1] * scale),
+                          TR::pack2(acc_dk[db][4 * g + 2] * scale, acc_dk[db][4 * g + 3] * scale)};
+      ov[db][g] = u32x2_t{TR::pack2(acc_dv[db][4 * g + 0], acc_dv[db][4 * g + 1]),
+                          TR::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3])};
+    }
+  static_assert(4 * kTileRowsBytes<D> <= STG, "four wavefronts' rows fit one stage slot");
+  const int nrows = min(32, N - kw);
+  store_tile_rows<D>(smem + ((n_st + 1) & 3) * STG + w * kTileRowsBytes<D>, ok, dK + head_off + (size_t)kw * D,
+                     nrows, lane);
+  store_tile_rows<D>(smem + ((n_st + 2) & 3) * STG + w * kTileRowsBytes<D>, ov, dV + head_off + (size_t)kw * D,
+                     nrows, lane);
 }
 
 // ------------------------------------------------------------------ dQ
@@ -636,18 +639,17 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     lds_barrier();
   }
 
-  if (qrow < N) {
-    uint16_t* drow = dQ + head_off + (size_t)qrow * D;
+  u32x2_t od[NDB][4];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * db + 8 * g + 4 * h;
-        *(u32x2_t*)(drow + col) =
-            u32x2_t{TR::pack2(acc[db][4 * g + 0] * scale, acc[db][4 * g + 1] * scale),
-                    TR::pack2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale)};
-      }
-  }
+    for (int g = 0; g < 4; ++g)
+      od[db][g] = u32x2_t{TR::pack2(acc[db][4 * g + 0] * scale, acc[db][4 * g + 1] * scale),
+                          TR::pack2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale)};
+  // dQ stored as whole rows through LDS (every buffer is free after the last barrier)
+  static_assert(4 * kTileRowsBytes<D> <= (int)sizeof(sK), "four wavefronts' rows fit each buffer pair");
+  store_tile_rows<D>((grp == 0 ? (char*)sK : (char*)sV) + (w & 3) * kTileRowsBytes<D>, od,
+                     dQ + head_off + (size_t)qw * D, min(32, N - qw), lane);
 }
 
 // dQ software-pipelined inside each wavefront: one wavefront per SIMD, 4 x 32
@@ -904,18 +906,18 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   if constexpr (NDB == 4) mfma_wait_a(acc[0], acc[1], acc[2], acc[3]);
   else mfma_wait_a(acc[0], acc[1]);
 
-  if (qrow < N) {
-    uint16_t* drow = dQ + head_off + (size_t)qrow * D;
+  u32x2_t od[NDB][4];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * db + 8 * g + 4 * h;
-        *(u32x2_t*)(drow + col) =
-            u32x2_t{TR::pack2(acc[db][4 * g + 0] * scale, acc[db][4 * g + 1] * scale),
-                    TR::pack2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale)};
-      }
-  }
+    for (int g = 0; g < 4; ++g)
+      od[db][g] = u32x2_t{TR::pack2(acc[db][4 * g + 0] * scale, acc[db][4 * g + 1] * scale),
+                          TR::pack2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale)};
+  // dQ stored as whole rows through LDS: after the last barrier every stage
+  // slot but that of the last block is free
+  static_assert(4 * kTileRowsBytes<D> <= STG, "four wavefronts' rows fit one stage slot");
+  store_tile_rows<D>(smem + ((n_st + 1) & 3) * STG + w * kTileRowsBytes<D>, od, dQ + head_off + (size_t)qw * D,
+                     min(32, N - qw), lane);
 }
 
 // ------------------------------------------------------------------ launch

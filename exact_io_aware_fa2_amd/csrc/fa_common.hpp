@@ -288,6 +288,41 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // compiler branches on it instead of predicating every guarded instruction.
 __device__ inline bool wave_uniform(bool x) { return __builtin_amdgcn_readfirstlane((int)x) != 0; }
 
+// A wavefront's 32 x D output tile held in the layout of a transposed
+// product's accumulators (lane l owns row l % 32; v[db][g] holds its columns
+// 32 db + 8 g + 4 h + 0..3 as two packed pairs) is stored through LDS, so
+// that each store instruction writes whole rows (16 bytes per lane,
+// 64 / (D / 8) rows per instruction) instead of 8-byte pieces of 32 rows.
+// lds: this wavefront's scratch, 32 rows of 2 D bytes, 16-byte chunk c of
+// row r at chunk position c ^ (r % (D / 8)); rows at and past nrows are not
+// stored.
+template <int D>
+__device__ inline void store_tile_rows(char* lds, const u32x2_t (&v)[D / 32][4], uint16_t* dst, int nrows,
+                                       int lane) {
+  constexpr int RS = 2 * D;
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+  const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(u32x2_t*)(lds + l32 * RS + ((4 * db + g) ^ (l32 % CPR)) * 16 + 8 * h) = v[db][g];
+  // the rows read below were written by other lanes of this wavefront
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + lane / CPR, ch = lane % CPR;
+    const u32x4_t x = *(const u32x4_t*)(lds + r * RS + (ch ^ (r % CPR)) * 16);
+    if (r < nrows) *(u32x4_t*)(dst + (size_t)r * D + 8 * ch) = x;
+  }
+}
+// bytes of LDS scratch per wavefront for store_tile_rows
+template <int D>
+constexpr int kTileRowsBytes = 32 * 2 * D;
+
 // Wait until every vector-memory load issued so far has returned.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

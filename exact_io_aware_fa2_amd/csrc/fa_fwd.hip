@@ -517,19 +517,22 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
     lt += swap_halves(lt);
     const float inv = 1.0f / lt;
     const int qrow = qw + 32 * qb + l32;
-    if (qrow < N) {
-      uint16_t* orow = O + head_off + (size_t)qrow * D;
+    u32x2_t ov[NDB][4];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = 32 * db + 8 * g + 4 * h;
-          const uint32_t w0 = TR::pack2(acc[qb][db][4 * g + 0] * inv, acc[qb][db][4 * g + 1] * inv);
-          const uint32_t w1 = TR::pack2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv);
-          *(u32x2_t*)(orow + col) = u32x2_t{w0, w1};
-        }
-      if (h == 0) LSE[(size_t)bh * N + qrow] = (m_run[qb] + __log2f(l)) * kLn2;
-    }
+      for (int g = 0; g < 4; ++g)
+        ov[db][g] = u32x2_t{TR::pack2(acc[qb][db][4 * g + 0] * inv, acc[qb][db][4 * g + 1] * inv),
+                            TR::pack2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv)};
+    // O stored as whole rows through LDS: waves 0..NW/2-1 use the K buffers,
+    // the others the V buffers (every wavefront is past its last LDS read:
+    // barrier below, before the first write)
+    static_assert(QB == 1 && (NW / 2) * kTileRowsBytes<D> <= (int)sizeof(sK) &&
+                      (NW / 2) * kTileRowsBytes<D> <= (int)sizeof(sV), "rows fit the tile buffers");
+    if (qb == 0) lds_barrier();
+    store_tile_rows<D>((w < NW / 2 ? (char*)sK : (char*)sV) + (w % (NW / 2)) * kTileRowsBytes<D>, ov,
+                       O + head_off + (size_t)(qw + 32 * qb) * D, min(32, N - (qw + 32 * qb)), lane);
+    if (qrow < N && h == 0) LSE[(size_t)bh * N + qrow] = (m_run[qb] + __log2f(l)) * kLn2;
   }
 }
 
@@ -836,19 +839,17 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const float lt = lt_run + swap_halves(lt_run);
   const float l = l_run + swap_halves(l_run);
   const float inv = 1.0f / lt;
-  if (qrow < N) {
-    uint16_t* orow = O + head_off + (size_t)qrow * D;
+  u32x2_t ov[NDB][4];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * db + 8 * g + 4 * h;
-        const uint32_t w0 = TR::pack2(acc_o[db][4 * g + 0] * inv, acc_o[db][4 * g + 1] * inv);
-        const uint32_t w1 = TR::pack2(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv);
-        *(u32x2_t*)(orow + col) = u32x2_t{w0, w1};
-      }
-    if (h == 0) LSE[(size_t)bh * N + qrow] = (m_run + __log2f(l)) * kLn2;
-  }
+    for (int g = 0; g < 4; ++g)
+      ov[db][g] = u32x2_t{TR::pack2(acc_o[db][4 * g + 0] * inv, acc_o[db][4 * g + 1] * inv),
+                          TR::pack2(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
+  // O stored as whole rows through LDS (the K buffers; the loop ended with a barrier)
+  static_assert(8 * kTileRowsBytes<D> <= (int)sizeof(sK), "rows of all wavefronts fit the K buffers");
+  store_tile_rows<D>((char*)sK + w * kTileRowsBytes<D>, ov, O + head_off + (size_t)qw * D, min(32, N - qw), lane);
+  if (qrow < N && h == 0) LSE[(size_t)bh * N + qrow] = (m_run + __log2f(l)) * kLn2;
 }
 
 // fp32 inputs: same scheme with v_mfma_f32_32x32x2_f32 and unrounded fp32
