@@ -27,8 +27,8 @@
 //     single normalisation at the end.  Two kernels: fwd16_pipe_kernel (d =
 //     128) software-pipelines matrix and vector work inside each wavefront
 //     against a fixed reference maximum; fwd16_pp_kernel (d = 64) alternates
-//     whole matrix and vector phases between the two wavefronts of a SIMD
-//     with lazy re-basing of the maximum.
+//     whole matrix and vector phases between the two wavefronts of a SIMD;
+//     both against a reference maximum fixed by the first key tile.
 //   * causal: key tiles above a workgroup's diagonal are never loaded or
 //     multiplied; only tiles crossing the diagonal are masked.
 #include <type_traits>
@@ -38,17 +38,12 @@
 
 namespace fa {
 
-// Ping-pong kernel: a row maximum is only re-based when it grows by more than
-// kTau (log2 units).  Between re-bases probabilities are bounded by 2^kTau,
-// which bf16/fp16 and the fp32 accumulators hold without loss of relative
-// precision; the final normalisation uses the same reference maximum for
-// numerator and denominator, so the result is unchanged mathematically.
-constexpr float kTau = 8.0f;
-
-// Pipelined kernel: the reference maximum stays fixed unless the sum of a
-// row's probabilities over one key tile exceeds this bound (then the pass is
-// redone against exact row maxima); no single probability, nor a packed fp16
-// value, can exceed it.
+// Reference maximum of both 16-bit kernels: fixed by the first tile, and
+// changed only when the sum of a row's probabilities over one key tile
+// exceeds this bound (the pipelined kernel then redoes its pass against exact
+// row maxima, the ping-pong kernel re-bases that tile); no single
+// probability, nor a packed fp16 value, can exceed it.  The final
+// normalisation uses the same reference for numerator and denominator.
 constexpr float kSumMax = 32768.0f;
 
 // 16-bit forward, software-pipelined (used for d = 128).  Two wavefronts
@@ -798,15 +793,41 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
               if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
             }
         }
-        float mx = -INFINITY;
+        // probabilities against the reference maximum m_run
+        float lsum, ltsum;
+        auto softmax = [&]() __attribute__((always_inline)) {
+          const float mneg = -m_run;
+          lsum = 0.0f;
+          ltsum = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, swap_halves(mx));
-        const float mnew = mx * c;
-        if (mnew > m_run + kTau) {
-          const float alpha = fast_exp2(m_run - mnew);
+            for (int r = 0; r < 16; r += 2) {
+              const float p0 = fast_exp2(fmaf(s[kb][r], c, mneg));
+              const float p1 = fast_exp2(fmaf(s[kb][r + 1], c, mneg));
+              lsum += p0 + p1;
+              const uint32_t pk = TR::pack2(p0, p1);
+              ltsum = TR::sum2(pk, ltsum);
+              pt[kb][r / 2] = pk;
+            }
+        };
+        // The reference is the first tile's row maximum and is raised only
+        // when a tile's row sum exceeds kSumMax (a maximum grew by about
+        // log2(kSumMax / BC) or more): then, for this tile, the row maxima are
+        // searched, O and the sums re-based and the probabilities recomputed.
+        bool rebase = j == 0;
+        if (!rebase) {
+          softmax();
+          rebase = wave_uniform(__builtin_amdgcn_ballot_w64(!(lsum + swap_halves(lsum) <= kSumMax)) != 0);
+        }
+        if (rebase) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[kb][r], s[kb][r + 1]);
+          const float mnew = __builtin_elementwise_maximum(m_run, __builtin_elementwise_maximum(mx, swap_halves(mx)) * c);
+          const float alpha = fast_exp2(m_run - mnew);  // 0 on the first tile
           m_run = mnew;
           l_run *= alpha;
           lt_run *= alpha;
@@ -814,20 +835,8 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+          softmax();
         }
-        const float mneg = -m_run;
-        float lsum = 0.0f, ltsum = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(fmaf(s[kb][r], c, mneg));
-            const float p1 = fast_exp2(fmaf(s[kb][r + 1], c, mneg));
-            lsum += p0 + p1;
-            const uint32_t pk = TR::pack2(p0, p1);
-            ltsum = TR::sum2(pk, ltsum);
-            pt[kb][r / 2] = pk;
-          }
         l_run += lsum;
         lt_run += ltsum;
       }
