@@ -141,6 +141,26 @@ def test_large_scores_stay_finite_and_pick_the_max_key():
     assert_fwd_ok(err, "bf16", "x30 queries")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_scores_update_the_reference_maximum(d, causal):
+    """Keys scaled up 6x along the sequence: later key tiles hold row maxima far
+    above the first tile's (by more than the kernels' tile-sum bound allows),
+    so the reference maximum must be raised (d = 64: the tile is re-based;
+    d = 128: the pass is redone against exact maxima).  Result as the oracle."""
+    N = 600
+    inp = si.make_inputs(1, 2, N, d, "bf16", 1.0, 17 + d)
+    grow = (1.0 + 5.0 * np.arange(N) / N)[None, None, :, None]
+    inp["k"] = si.round_to(inp["k"][0] * grow, "bf16")
+    scale = 1 / np.sqrt(d)
+    _, _, _, o, lse = gpu_fwd(inp, "bf16", causal, scale)
+    og = o.float().cpu().numpy()
+    assert np.isfinite(og).all() and np.isfinite(lse.cpu().numpy()).all()
+    o_ref, l_ref = attention_fwd(inp["q"][0], inp["k"][0], inp["v"][0], scale, causal)
+    err = fwd_errors(og, lse.cpu().numpy(), o_ref, l_ref)
+    assert_fwd_ok(err, "bf16", f"growing keys d{d} causal={causal}")
+
+
 def test_key_shift_invariance_on_gpu():
     """Adding one vector to every key leaves O unchanged (within rounding) and
     shifts LSE_i by scale * q_i . c."""
