@@ -62,27 +62,30 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // dK, dV software-pipelined inside each wavefront: one wavefront per SIMD,
 // 4 x 32 keys per workgroup (d = 64 and 128).  Query rows stream through LDS in stages
 // of 64 (two blocks of 32); iteration b of a wavefront issues
-//   matrix: S_{b+1} = Q_{b+1} K^T, dP_{b+1} = dO_{b+1} V^T - D   (VGPR results)
-//           dV^T += dO_{b-1}^T P_{b-1}, dK^T += Q_{b-1}^T dS_{b-1}  (AGPR accumulators)
-//   vector: P_b = exp2(S_b c - LSE log2 e), dS_b = P_b (dP_b - D), rounded
+//   matrix: dV^T += dO_{b-1}^T P_{b-1}, dK^T += Q_{b-1}^T dS_{b-1},
+//           S'_{b+1} = Q_{b+1} K^T - LSE / scale, dP_{b+1} = dO_{b+1} V^T - D
+//   vector: P_b = exp2(S'_b c), dS_b = P_b (dP_b - D), rounded
 // interleaved product by product, so that the matrix core and the vector unit
-// of the SIMD work at the same time within the one wavefront.  K, V (operands)
-// and dK, dV (accumulators) stay in AGPRs for the whole kernel.
+// of the SIMD work at the same time within the one wavefront (c = scale log2 e;
+// -LSE / scale and -D enter as the accumulators' initial values, read from LDS
+// two products before the first product that adds to them).  At one wavefront
+// per SIMD (d = 128), K, V (operands) and dK, dV (accumulators) stay in AGPRs
+// for the whole kernel; at two (d = 64, 256 registers each) all are VGPRs.
 //
 // LDS stage (four in flight, stage x in slot x % 4): Q and dO tiles with rows
-// padded to d + 8 elements, the log2-scaled LSE and -D.  Within every 16 query
+// padded to d + 8 elements, -LSE / scale and -D.  Within every 16 query
 // rows the S/dP products take their rows in the order perm(m) = 4 (m % 4) +
 // m / 4, so that the four rows a transposed read (lds_read_tr) gathers for
 // the dV/dK products lie 4 rows apart: with the padded rows, both the row
 // reads (S, dP) and the transposed reads (dV, dK) are free of bank conflicts,
 // and no transposed copy of Q or dO is staged.
-template <class TR, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <class TR, int D, bool CAUSAL, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dvec,
                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_ktiles,
-                          uint32_t total, float c, float scale) {
+                          uint32_t total, float c, float neg_inv_scale, float scale) {
   constexpr int NT = 256;
   constexpr int BKV = 128;                  // keys per workgroup
   constexpr int BQ = 64;                    // query rows per stage
@@ -92,20 +95,21 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   constexpr int NKS = D / 16;               // k-steps of S and dP
   constexpr int NDB = D / 32;               // 32-column blocks of dK and dV
   constexpr int OFF_O = BQ * RBL;           // stage layout (bytes): Q, dO, then vector w
-  constexpr int OFF_L = 2 * BQ * RBL;       // of wave w at OFF_L + 4 BQ w (0: LSE,
+  constexpr int OFF_L = 2 * BQ * RBL;       // of wave w at OFF_L + 4 BQ w (0: -LSE/scale,
   constexpr int OFF_D = OFF_L + 4 * BQ;     // 1: -D; waves 2, 3 write unread copies)
   constexpr int STG = OFF_L + 16 * BQ;
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   constexpr int ROWSTEP = NT / CPR;         // rows between a thread's staging chunks
   constexpr int NCH = BQ / ROWSTEP;         // staging chunks per thread and tensor
   constexpr int NSL = 4 * NKS;              // products per iteration
-  constexpr int AH = 8;                     // operand reads issued ahead of their product
+  constexpr int AH = OCC == 1 ? 8 : 4;      // operand reads issued ahead of their product
   constexpr int kW0 = NSL / 4;              // first staging write (product index, PAR 1)
   static_assert(kW0 + 2 * (BQ / (NT / (D / 8))) + 1 <= NSL, "staging writes fit the iteration");
   static_assert(2 * NDB == NKS, "S, dV, dK, dP products interleave one to one");
   static_assert(NSL % AH == 0, "operand of product f of an iteration sits in fr[f % AH]");
   static_assert(NSL == 32 || NSL == 16, "vector work schedule below");
-  static_assert(4 * STG <= 160 * 1024, "four stages fit in LDS");
+  static_assert(OCC * 4 * STG <= 160 * 1024, "four stages per workgroup fit in LDS");
+  using PM = PipeMma<TR, OCC == 1>;          // K, V, dK and dV in AGPRs at one wavefront per SIMD
 
   __shared__ __attribute__((aligned(16))) char smem[4 * STG];
 
@@ -158,7 +162,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
   // ---- staging: chunk i of this thread is row tid / CPR + ROWSTEP i, column
   // chunk tid % CPR, of both Q and dO.  Wave w loads vector w % 2 of the stage
-  // (0: LSE, 1: D) at positions m = lane: row 32 (m / 32) + perm(m % 32).
+  // (0: -LSE / scale, 1: -D) at positions m = lane: row 32 (m / 32) + perm(m % 32).
   const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
   const rsrc_t ores = make_rsrc(dO + head_off, head_bytes);
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -195,20 +199,19 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     } else if (j < 2 * NCH) {
       *(u32x4_t*)(smem + sb + OFF_O + s_off + ROWSTEP * (j - NCH) * RBL) = so[t][j - NCH];
     } else {
-      // rows past the end: LSE = +inf makes P = 0; D = 0.  D is stored
-      // negated: it initialises the dP accumulators.
+      // rows past the end: -inf initialises their S, so P = 0; D = 0
       const bool in = vidx[t] < N;
-      *(float*)(smem + sb + v_off) = is_d ? (in ? -vraw[t] : 0.0f) : (in ? vraw[t] * kLog2e : INFINITY);
+      *(float*)(smem + sb + v_off) = is_d ? (in ? -vraw[t] : 0.0f) : (in ? vraw[t] * neg_inv_scale : -INFINITY);
     }
   };
 
   // ---- register sets of the pipeline (index: block parity)
   f32x16_t sc[2], dp[2];
-  float lr[2][16];
   u32x4_t pk[2][2], dsk[2][2];  // [set][k-step t]: P and dS rounded, packed in pairs
 
-  // -D into the dP accumulators, and the scaled LSE, of the block in half bb of stage sb
-  auto load_vecs = [&](uint32_t sb, int bb, f32x16_t& d, float (&l)[16]) __attribute__((always_inline)) {
+  // initial values of the S and dP accumulators (-LSE / scale, -D) of the
+  // block in half bb of stage sb
+  auto load_vecs = [&](uint32_t sb, int bb, f32x16_t& d, f32x16_t& l) __attribute__((always_inline)) {
     const char* dv = smem + sb + OFF_D + 128 * bb + 16 * h;
     const char* lv = smem + sb + OFF_L + 128 * bb + 16 * h;
 #pragma unroll
@@ -229,14 +232,14 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const u32x2_t a = lds_read_tr(p), b = lds_read_tr(p + 2 * RBL);
     return u32x4_t{a[0], a[1], b[0], b[1]};
   };
-  // operand of product k of an iteration: (S, dV, dK, dP)[k % 4] of index k / 4;
+  // operand of product k of an iteration: (dV, dK, S, dP)[k % 4] of index k / 4;
   // sb1: stage of block b+1, sb2: stage of block b-1, nb: their half (1 - b % 2)
   auto frag = [&](int k, uint32_t sb1, uint32_t sb2, int nb) __attribute__((always_inline)) -> u32x4_t {
     const int x = k / 4;
     switch (k % 4) {
-      case 0: return row_frag(sb1, nb, 0, x);
-      case 1: return tr_frag(sb2, nb, 1, x / NDB, x % NDB);
-      case 2: return tr_frag(sb2, nb, 0, x / NDB, x % NDB);
+      case 0: return tr_frag(sb2, nb, 1, x / NDB, x % NDB);
+      case 1: return tr_frag(sb2, nb, 0, x / NDB, x % NDB);
+      case 2: return row_frag(sb1, nb, 0, x);
       default: return row_frag(sb1, nb, 1, x);
     }
   };
@@ -254,7 +257,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // vector instructions: all of them ordered before what reads them next
     mfma_wait_v(sc[PAR], dp[PAR]);
     asm volatile("" : "+v"(pk[NB][0]), "+v"(pk[NB][1]), "+v"(dsk[NB][0]), "+v"(dsk[NB][1]));
-    load_vecs(sb1, NB, dp[NB], lr[NB]);
+    load_vecs(sb1, NB, dp[NB], sc[NB]);
 
     // causal: key kw + l32 is visible to the row of score r iff thr <= qoff(r)
     const int thr = kw - q0 + l32 - h;
@@ -266,7 +269,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         constexpr int V0 = NSL / 16;
         const int v0 = V0 * r, v1 = v0 + 1 < NSL ? v0 + 1 : v0;
         if (k == v0) {
-          float x = fmaf(sc[PAR][r], c, -lr[PAR][r]);
+          float x = sc[PAR][r] * c;
           if constexpr (MASKED) {
             // score r = 4g + e is S row 8g + 4h + e: query perm(8(g%2) + 4h + e) + 16(g/2)
             const int g = r / 4, e = r % 4;
@@ -298,14 +301,13 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       if constexpr (k + AH < NSL) fr[k % AH] = frag(k + AH, sb1, sb2, NB);
       else fr[k % AH] = frag(k + AH - NSL, nsb1, nsb2, PAR);
       if constexpr (k % 4 == 0) {
-        if constexpr (x == 0) sc[NB] = TR::mma0_vva(a, kf[0]);
-        else TR::mma_vva(sc[NB], a, kf[x]);
+        PM::macc(acc_dv[x % NDB], a, pk[NB][x / NDB]);
       } else if constexpr (k % 4 == 1) {
-        TR::mma_avv(acc_dv[x % NDB], a, pk[NB][x / NDB]);
+        PM::macc(acc_dk[x % NDB], a, dsk[NB][x / NDB]);
       } else if constexpr (k % 4 == 2) {
-        TR::mma_avv(acc_dk[x % NDB], a, dsk[NB][x / NDB]);
+        PM::mb(sc[NB], a, kf[x]);
       } else {
-        TR::mma_vva(dp[NB], a, vf[x]);
+        PM::mb(dp[NB], a, vf[x]);
       }
       vwork(k);
       __builtin_amdgcn_sched_barrier(0);
@@ -324,13 +326,12 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   for (int j = 0; j < NPART; ++j) store_part(STG, j, 1);
   for (int i = tid; i < 2 * BQ * RBL / 16; i += NT) *(u32x4_t*)(smem + 3 * STG + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
   lds_barrier();
-  load_vecs(0, 0, dp[0], lr[0]);
+  load_vecs(0, 0, dp[0], sc[0]);
   mma_pipeline<2 * NKS, 3>([&](int x) { return smem + ((x & 1) ? OFF_O : 0) + rbase + 32 * (x >> 1); },
                            [&](int x, u32x4_t a) {
                              const int ks = x >> 1;
-                             if (x & 1) TR::mma_vva(dp[0], a, vf[ks]);
-                             else if (ks == 0) sc[0] = TR::mma0_vva(a, kf[0]);
-                             else TR::mma_vva(sc[0], a, kf[ks]);
+                             if (x & 1) PM::mb(dp[0], a, vf[ks]);
+                             else PM::mb(sc[0], a, kf[ks]);
                            },
                            [](int) {});
 #pragma unroll
@@ -361,14 +362,14 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     asm volatile("" : "+v"(pk[1][0]), "+v"(pk[1][1]), "+v"(dsk[1][0]), "+v"(dsk[1][1]));
 #pragma unroll
     for (int x = 0; x < NKS; ++x) {
-      TR::mma_avv(acc_dv[x % NDB], tr_frag(sb, 1, 1, x / NDB, x % NDB), pk[1][x / NDB]);
-      TR::mma_avv(acc_dk[x % NDB], tr_frag(sb, 1, 0, x / NDB, x % NDB), dsk[1][x / NDB]);
+      PM::macc(acc_dv[x % NDB], tr_frag(sb, 1, 1, x / NDB, x % NDB), pk[1][x / NDB]);
+      PM::macc(acc_dk[x % NDB], tr_frag(sb, 1, 0, x / NDB, x % NDB), dsk[1][x / NDB]);
     }
   }
   if constexpr (NDB == 4)
-    mfma_wait_a(acc_dk[0], acc_dk[1], acc_dk[2], acc_dk[3], acc_dv[0], acc_dv[1], acc_dv[2], acc_dv[3]);
+    PM::wait_acc(acc_dk[0], acc_dk[1], acc_dk[2], acc_dk[3], acc_dv[0], acc_dv[1], acc_dv[2], acc_dv[3]);
   else
-    mfma_wait_a(acc_dk[0], acc_dk[1], acc_dv[0], acc_dv[1]);
+    PM::wait_acc(acc_dk[0], acc_dk[1], acc_dv[0], acc_dv[1]);
 
   // dK, dV rounded and stored as whole rows through LDS: after the last
   // barrier every stage slot but that of the last block is free; dK of
@@ -393,270 +394,13 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
 // ------------------------------------------------------------------ dQ
 
-// dQ: 8 wavefronts (two per SIMD), 32 query rows each, 256 rows per
-// workgroup, with the same two-phase schedule as the forward:
-//   M-phase j: S^T_j = K_j Q^T, dP^T_j = V_j dO^T, dQ^T += K_{j-1}^T dS^T_{j-1}
-//   V-phase j: P = exp2(S c - LSE log2 e), dS_j = P (dP - D), rounded
-// Waves 4..7 run one phase behind waves 0..3.  Waves 0..3 stage K (row-major
-// for S, key-interleaved for dQ), waves 4..7 stage V (row-major for dP).
-// K and V row tiles are double-buffered, the interleaved K tile (read one
-// phase later) triple-buffered.
-template <class TR, int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                   const float* __restrict__ LSE, const float* __restrict__ Dvec,
-                   uint16_t* __restrict__ dQ, int N, int n_qtiles, uint32_t total, float c,
-                   float scale) {
-  constexpr int NW = 8;
-  constexpr int BR = 32 * NW;            // query rows per workgroup
-  constexpr int KCH = D / 8;             // 16-byte chunks per row
-  constexpr int KS = D + 8;              // padded row (elements)
-  constexpr int NKB = BC / 32;
-  constexpr int NDB = D / 32;
-  constexpr int NKS = D / 16;
-  constexpr int NS = NKS * NKB;          // S (and dP) products per tile
-  constexpr int NQ = NKB * 2 * NDB;      // dQ products per tile
-  static_assert(NS == NQ, "matrix phase interleaves S, dP and dQ one to one");
-
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[3][BC * D];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int grp = w >> 2;
-  const int st = tid & 255;
-  const int h = lane >> 5;
-  const int l32 = lane & 31;
-
-  const uint32_t lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / n_qtiles;
-  int qt = lid % n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
-  const int q0 = qt * BR;
-  const int qw = q0 + 32 * w;
-  const int qrow = qw + l32;
-  const size_t head_off = (size_t)bh * N * D;
-  constexpr uint32_t RB = D * 2;
-  const uint32_t head_bytes = (uint32_t)N * RB;
-
-  // Q and dO rows as B operands, loaded once; LSE (log2 units) and D per row.
-  u32x4_t qf[NKS], of[NKS];
-  {
-    const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
-    const rsrc_t ores = make_rsrc(dO + head_off, head_bytes);
-    const uint32_t off = (uint32_t)qrow * RB + 16 * h;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      qf[ks] = buf_load16(qres, off + 32 * ks);
-      of[ks] = buf_load16(ores, off + 32 * ks);
-    }
-  }
-  // rows past the end: P = exp2(-inf) = 0, so dS = 0 there
-  const float lq = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dd = qrow < N ? Dvec[(size_t)bh * N + qrow] : 0.0f;
-
-  f32x16_t acc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
-  f32x16_t s[NKB], dp[NKB];
-  // dP accumulators start at -D (one constant register block), so they end as dP - D
-  f32x16_t negd;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) negd[i] = -dd;
-  uint32_t dsk[NKB][8];
-
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
-  const int n_tiles = (kv_end + BC - 1) / BC;
-  const int wave_end = CAUSAL ? min(N, qw + 32) : N;
-  const int wave_tiles = (wave_end + BC - 1) / BC;
-
-  // ---- staging (every thread of a group takes part: no divergent branches)
-  // K role: unit st = 8 keys x 2 columns: keys 16us + 4uh + {0..3} and
-  //   16us + 8 + 4uh + {0..3}, columns 2uc, 2uc + 1 (one dword per key)
-  // V role: 16-byte chunks ci = st + 256 r -> row ci / KCH, column ci % KCH
-  static_assert(BC * D / 16 == 256 && BC * KCH == 512, "two staging dwordx4 per thread");
-  // one resource per tensor, uniform across the wave (see the forward)
-  const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
-  const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
-  u32x4_t stg[2];
-  const int uc = st % (D / 2);
-  const int uh = (st / (D / 2)) & 1;
-  const int us = st / D;
-  const int urow0 = 16 * us + 4 * uh;
-  const uint32_t uoff = (uint32_t)urow0 * RB + uc * 4;
-  const int ust = ((2 * us + uh) * D + 2 * uc) * 8;
-  const uint32_t voff = (uint32_t)(st / KCH) * RB + (st % KCH) * 16;
-  const int vst = (st / KCH) * KS + (st % KCH) * 8;
-
-  auto load_tile = [&](int j0) {
-    if (grp == 0) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        stg[k / 4][k % 4] = __builtin_amdgcn_raw_buffer_load_b32(
-            kres, uoff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB, 0, 0);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 2; ++r) stg[r] = buf_load16(vres, voff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
-    }
-  };
-  // staging writes in four parts, so they can be spread between products
-  auto store_part = [&](auto role, int j, int part) {
-    if constexpr (decltype(role)::value == 0) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int k = 2 * part + e;
-        *(uint32_t*)(&sK[j & 1][(urow0 + 8 * (k / 4) + (k % 4)) * KS + 2 * uc]) = stg[k / 4][k % 4];
-      }
-      if (part & 1) {
-        const int cc = part >> 1;  // column 2uc + cc
-        uint32_t o[4];
-#pragma unroll
-        for (int kp = 0; kp < 4; ++kp) {
-          const uint32_t x0 = stg[kp / 2][2 * (kp % 2)], x1 = stg[kp / 2][2 * (kp % 2) + 1];
-          o[kp] = cc ? pack_hi(x0, x1) : pack_lo(x0, x1);
-        }
-        *(u32x4_t*)(&sKt[j % 3][ust + 8 * cc]) = u32x4_t{o[0], o[1], o[2], o[3]};
-      }
-    } else {
-      if ((part & 1) == 0) *(u32x4_t*)(&sV[j & 1][vst + (part >> 1) * (256 / KCH) * KS]) = stg[part >> 1];
-    }
-  };
-  auto store_tile = [&](int j) {
-    if (grp == 0) {
-#pragma unroll
-      for (int part = 0; part < 4; ++part) store_part(std::integral_constant<int, 0>{}, j, part);
-    } else {
-#pragma unroll
-      for (int part = 0; part < 4; ++part) store_part(std::integral_constant<int, 1>{}, j, part);
-    }
-  };
-
-  // ---- products
-  const int rfrag = l32 * KS + 8 * h;   // row-major fragment of this lane
-  const int ifrag = (h * D + l32) * 8;  // interleaved fragment of this lane
-  auto s_addr = [&](const uint16_t* b_, int i) { return b_ + 32 * (i % NKB) * KS + 16 * (i / NKB); };
-  auto q_addr = [&](const uint16_t* b_, int i) { return b_ + ((2 * (i / NDB)) * D + 32 * (i % NDB)) * 8; };
-  // first k-step from a zero accumulator (inline constant, no clearing)
-  auto s_mma = [&](int i, u32x4_t a) { s[i % NKB] = TR::mfma(a, qf[i / NKB], i < NKB ? zero16() : s[i % NKB]); };
-  auto dp_mma = [&](int i, u32x4_t a) {
-    if (i < NKB) dp[i] = TR::mma_c(a, of[0], negd);  // first k-step: -D + products
-    else dp[i % NKB] = TR::mfma(a, of[i / NKB], dp[i % NKB]);
-  };
-  auto dq_mma = [&](int i, u32x4_t a) {
-    const int kt = i / NDB, db = i % NDB;
-    const int kb = kt / 2, t = kt % 2;
-    acc[db] = TR::mfma(a, u32x4_t{dsk[kb][4 * t + 0], dsk[kb][4 * t + 1], dsk[kb][4 * t + 2], dsk[kb][4 * t + 3]},
-                       acc[db]);
-  };
-
-  // ---- prologue
-  load_tile(0);
-  store_tile(0);
-  wait_vmem();
-  if (n_tiles > 1) load_tile(BC);
-  lds_barrier();
-
-  const int n_slots = 2 * n_tiles + 2;
-  for (int slot = 0; slot < n_slots; ++slot) {
-    const int ph = slot - grp;
-    if (ph >= 0 && (ph & 1) == 0) {
-      // ---------------- M-phase j
-      __builtin_amdgcn_s_setprio(1);
-      const int j = ph >> 1;
-      const bool do_s = j < wave_tiles;
-      const bool do_q = j >= 1 && j - 1 < wave_tiles;
-      const uint16_t* kb_ = sK[j & 1] + rfrag;
-      const uint16_t* vb_ = sV[j & 1] + rfrag;
-      const uint16_t* tb_ = sKt[(j + 2) % 3] + ifrag;  // K_{j-1}, interleaved
-      if (do_s && do_q) {
-        // steady state: S, dP, dQ products interleaved in one pipelined run,
-        // staging writes between them (past the last tile they rewrite a
-        // buffer no one reads again)
-        auto fused = [&](auto role) {
-          mma_pipeline<3 * NS, 3>(
-              [&](int k) {
-                const int i = k / 3;
-                return k % 3 == 0 ? s_addr(kb_, i) : k % 3 == 1 ? s_addr(vb_, i) : q_addr(tb_, i);
-              },
-              [&](int k, u32x4_t a) {
-                const int i = k / 3;
-                if (k % 3 == 0) s_mma(i, a);
-                else if (k % 3 == 1) dp_mma(i, a);
-                else dq_mma(i, a);
-              },
-              [&](int k) {
-                if (k % (3 * NS / 4) == 3 * NS / 8) store_part(role, j + 1, k / (3 * NS / 4));
-              });
-        };
-        if (grp == 0) fused(std::integral_constant<int, 0>{});
-        else fused(std::integral_constant<int, 1>{});
-      } else {
-        if (j + 1 < n_tiles) store_tile(j + 1);
-        if (do_s) {
-#pragma unroll
-          for (int i = 0; i < NS; ++i) {
-            s_mma(i, *(const u32x4_t*)s_addr(kb_, i));
-            dp_mma(i, *(const u32x4_t*)s_addr(vb_, i));
-          }
-        }
-        if (do_q) {
-#pragma unroll
-          for (int i = 0; i < NQ; ++i) dq_mma(i, *(const u32x4_t*)q_addr(tb_, i));
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-    } else if (ph >= 0) {
-      // ---------------- V-phase j
-      const int j = (ph - 1) >> 1;
-      if (j + 2 < n_tiles) load_tile((j + 2) * BC);
-      if (j < wave_tiles) {
-        const int j0 = j * BC;
-        auto grad = [&](auto masked) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-              float d2[2];
-#pragma unroll
-              for (int e = 0; e < 2; ++e) {
-                float p = fast_exp2(fmaf(s[kb][r + e], c, -lq));
-                if constexpr (decltype(masked)::value) {
-                  const int key = j0 + 32 * kb + 8 * ((r + e) / 4) + 4 * h + ((r + e) % 4);
-                  if (key >= N || (CAUSAL && key > qrow)) p = 0.0f;
-                }
-                d2[e] = p * dp[kb][r + e];
-              }
-              dsk[kb][r / 2] = TR::pack2(d2[0], d2[1]);
-            }
-        };
-        if (wave_uniform((CAUSAL && j0 + BC - 1 > qw) || j0 + BC > N)) grad(std::true_type{});
-        else grad(std::false_type{});
-      }
-    }
-    lds_barrier();
-  }
-
-  u32x2_t od[NDB][4];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      od[db][g] = u32x2_t{TR::pack2(acc[db][4 * g + 0] * scale, acc[db][4 * g + 1] * scale),
-                          TR::pack2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale)};
-  // dQ stored as whole rows through LDS (every buffer is free after the last barrier)
-  static_assert(4 * kTileRowsBytes<D> <= (int)sizeof(sK), "four wavefronts' rows fit each buffer pair");
-  store_tile_rows<D>((grp == 0 ? (char*)sK : (char*)sV) + (w & 3) * kTileRowsBytes<D>, od,
-                     dQ + head_off + (size_t)qw * D, min(32, N - qw), lane);
-}
-
-// dQ software-pipelined inside each wavefront: one wavefront per SIMD, 4 x 32
-// query rows per workgroup; Q, dO (B operands) and the dQ accumulators stay in
-// AGPRs.  Key rows stream through LDS in stages of 64 (two blocks of 32), with
-// the layout of bwd_dkdv_pipe_kernel (padded rows; S^T row m holds key
-// perm(m) of its 16).  Iteration b of a wavefront issues
+// dQ software-pipelined inside each wavefront: 4 x 32 query rows per
+// workgroup, OCC wavefronts per SIMD.  With one (d = 128), Q, dO (B operands)
+// and the dQ accumulators stay in AGPRs; with two (d = 64), whose register
+// budget is 256 per wavefront, every operand is a VGPR.  Key rows stream
+// through LDS in stages of 64 (two blocks of 32), with the layout of
+// bwd_dkdv_pipe_kernel (padded rows; S^T row m holds key perm(m) of its 16).
+// Iteration b of a wavefront issues
 //   matrix: S^T_{b+1} = K_{b+1} Q^T, dP^T_{b+1} = V_{b+1} dO^T - D,
 //           dQ^T += K_{b-1}^T dS^T_{b-1}
 //   vector: P_b = exp2(S^T_b c - LSE log2 e), dS_b = P_b (dP_b - D), rounded
@@ -664,8 +408,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 // are per-lane constants (D enters as the dP accumulators' initial value).
 // Keys past the end need no mask: their K and V rows read as zeros, so their
 // dS multiplies a zero row of K.
-template <class TR, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <class TR, int D, bool CAUSAL, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ Dvec,
@@ -691,7 +435,8 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   static_assert(2 * NDB == NKS, "S, dQ, dP products interleave one to one");
   static_assert(NSL % AH == 0, "operand of product f of an iteration sits in fr[f % AH]");
   static_assert(NPART <= NSL && kW0 + NPART <= NSL, "staging fits the iteration");
-  static_assert(4 * STG <= 160 * 1024, "four stages fit in LDS");
+  static_assert(OCC * 4 * STG <= 160 * 1024, "four stages per workgroup fit in LDS");
+  using PM = PipeMma<TR, OCC == 1>;          // Q, dO and dQ in AGPRs at one wavefront per SIMD
 
   __shared__ __attribute__((aligned(16))) char smem[4 * STG];
 
@@ -835,13 +580,13 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       if constexpr (k + AH < NSL) fr[k % AH] = frag(k + AH, sb1, sb2, NB);
       else fr[k % AH] = frag(k + AH - NSL, nsb1, nsb2, PAR);
       if constexpr (k % 3 == 0) {
-        if constexpr (x == 0) sc[NB] = TR::mma0_vva(a, qf[0]);
-        else TR::mma_vva(sc[NB], a, qf[x]);
+        if constexpr (x == 0) sc[NB] = PM::mb0(a, qf[0]);
+        else PM::mb(sc[NB], a, qf[x]);
       } else if constexpr (k % 3 == 1) {
-        TR::mma_avv(acc[x % NDB], a, dsk[NB][x / NDB]);
+        PM::macc(acc[x % NDB], a, dsk[NB][x / NDB]);
       } else {
-        if constexpr (x == 0) dp[NB] = TR::mma_c_vva(a, of[0], negd);
-        else TR::mma_vva(dp[NB], a, of[x]);
+        if constexpr (x == 0) dp[NB] = PM::mbc(a, of[0], negd);
+        else PM::mb(dp[NB], a, of[x]);
       }
       vwork(k);
       __builtin_amdgcn_sched_barrier(0);
@@ -864,12 +609,12 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                            [&](int x, u32x4_t a) {
                              const int ks = x >> 1;
                              if (x & 1) {
-                               if (ks == 0) dp[0] = TR::mma_c_vva(a, of[0], negd);
-                               else TR::mma_vva(dp[0], a, of[ks]);
+                               if (ks == 0) dp[0] = PM::mbc(a, of[0], negd);
+                               else PM::mb(dp[0], a, of[ks]);
                              } else if (ks == 0) {
-                               sc[0] = TR::mma0_vva(a, qf[0]);
+                               sc[0] = PM::mb0(a, qf[0]);
                              } else {
-                               TR::mma_vva(sc[0], a, qf[ks]);
+                               PM::mb(sc[0], a, qf[ks]);
                              }
                            },
                            [](int) {});
@@ -901,10 +646,10 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const uint32_t sb = (uint32_t)((n_st - 1) & 3) * STG;
     asm volatile("" : "+v"(dsk[1][0]), "+v"(dsk[1][1]));
 #pragma unroll
-    for (int x = 0; x < NKS; ++x) TR::mma_avv(acc[x % NDB], tr_frag(sb, 1, x / NDB, x % NDB), dsk[1][x / NDB]);
+    for (int x = 0; x < NKS; ++x) PM::macc(acc[x % NDB], tr_frag(sb, 1, x / NDB, x % NDB), dsk[1][x / NDB]);
   }
-  if constexpr (NDB == 4) mfma_wait_a(acc[0], acc[1], acc[2], acc[3]);
-  else mfma_wait_a(acc[0], acc[1]);
+  if constexpr (NDB == 4) PM::wait_acc(acc[0], acc[1], acc[2], acc[3]);
+  else PM::wait_acc(acc[0], acc[1]);
 
   u32x2_t od[NDB][4];
 #pragma unroll
@@ -936,39 +681,29 @@ template <class TR, int D, bool CAUSAL>
 static hipError_t dkdv_t(const BwdArgs& a) {
   const int n_ktiles = (a.N + 127) / 128;
   const uint32_t total = (uint32_t)(n_ktiles * a.BH);
-  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+  // The kernel forms the exponent as (q.k - LSE / s) * s log2 e with s the
+  // scale.  Below 2^-100 (scale 0 included) it takes s = 2^-100 there, so that
+  // -1 / s stays finite: q.k then vanishes beside LSE / s in float and the
+  // exponent is -LSE log2 e, its value at scale 0 (dK is still multiplied by
+  // the true scale).
+  const float s = a.scale >= 0x1p-100f ? a.scale : 0x1p-100f;
+  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2>), dim3(total), dim3(256), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     a.N, n_ktiles, total, a.c, a.scale);
+                     a.N, n_ktiles, total, s * kLog2e, -1.0f / s, a.scale);
   return hipGetLastError();
 }
 
+// dQ: the pipelined kernel, one wavefront per SIMD at d = 128 and two at d = 64
 template <class TR, int D, bool CAUSAL>
-static hipError_t dq_pipe_t(const BwdArgs& a) {
+static hipError_t dq_t(const BwdArgs& a) {
   const int n_qtiles = (a.N + 127) / 128;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.N, n_qtiles, total,
                      a.c, a.scale);
   return hipGetLastError();
-}
-
-// dQ: the pipelined kernel at d = 128; at d = 64 (twice the vector work per
-// product) the two-wavefront ping-pong kernel is faster
-template <class TR, int D, bool CAUSAL>
-static hipError_t dq_t(const BwdArgs& a) {
-  if constexpr (D == 128) {
-    return dq_pipe_t<TR, D, CAUSAL>(a);
-  } else {
-    const int n_qtiles = (a.N + 255) / 256;
-    const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-    hipLaunchKernelGGL((bwd_dq_kernel<TR, D, 64, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.N, n_qtiles, total,
-                       a.c, a.scale);
-    return hipGetLastError();
-  }
 }
 
 template <class TR>

@@ -182,6 +182,37 @@ __device__ __forceinline__ void mfma_wait_a(f32x16_t& a, f32x16_t& b, f32x16_t& 
 }
 #undef FA_MFMA_WAIT
 
+// Products of the software-pipelined kernels.  With AG (one wavefront per
+// SIMD, 512 registers) the B operands of mb* and the accumulators of macc
+// stay in AGPRs; without (two wavefronts per SIMD, 256 registers each) every
+// operand is a VGPR.  wait_acc: the wait states before vector reads of macc
+// accumulators.
+template <class TR, bool AG>
+struct PipeMma {
+  __device__ static inline f32x16_t mb0(u32x4_t a, u32x4_t b) {
+    if constexpr (AG) return TR::mma0_vva(a, b); else return TR::mma0(a, b);
+  }
+  __device__ static inline void mb(f32x16_t& c, u32x4_t a, u32x4_t b) {
+    if constexpr (AG) TR::mma_vva(c, a, b); else TR::mma(c, a, b);
+  }
+  __device__ static inline f32x16_t mbc(u32x4_t a, u32x4_t b, const f32x16_t& c) {
+    if constexpr (AG) return TR::mma_c_vva(a, b, c); else return TR::mma_c(a, b, c);
+  }
+  __device__ static inline void macc(f32x16_t& c, u32x4_t a, u32x4_t b) {
+    if constexpr (AG) TR::mma_avv(c, a, b); else TR::mma(c, a, b);
+  }
+  __device__ static inline void wait_acc(f32x16_t& a, f32x16_t& b) {
+    if constexpr (AG) mfma_wait_a(a, b); else mfma_wait_v(a, b);
+  }
+  __device__ static inline void wait_acc(f32x16_t& a, f32x16_t& b, f32x16_t& c, f32x16_t& d) {
+    if constexpr (AG) mfma_wait_a(a, b, c, d); else mfma_wait_v(a, b, c, d);
+  }
+  __device__ static inline void wait_acc(f32x16_t& a, f32x16_t& b, f32x16_t& c, f32x16_t& d,
+                                         f32x16_t& e, f32x16_t& f, f32x16_t& g, f32x16_t& h) {
+    if constexpr (AG) mfma_wait_a(a, b, c, d, e, f, g, h); else mfma_wait_v(a, b, c, d, e, f, g, h);
+  }
+};
+
 // Four 16-bit elements from LDS, transposed across each group of 16 lanes
 // (ds_read_b64_tr_b16): with lane j of a group pointing at 4 consecutive
 // elements E[j][0..3], lane i of the group receives E[4 * e + i / 4][i % 4]
@@ -326,10 +357,6 @@ constexpr int kTileRowsBytes = 32 * 2 * D;
 // Wait until every vector-memory load issued so far has returned.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// The two 16-bit halves of a dword.
-__device__ inline uint32_t lo16(uint32_t x) { return x & 0xffffu; }
-__device__ inline uint32_t hi16(uint32_t x) { return x >> 16; }
-__device__ inline uint32_t pair16(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
 // (a.lo, b.lo) and (a.hi, b.hi) as packed pairs, one v_perm_b32 each.
 __device__ inline uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ inline uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
