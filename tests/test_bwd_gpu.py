@@ -55,6 +55,21 @@ def test_small_shapes_and_tails(N, causal, d, dtype):
     _check_heads(inp, grads, [(0, 0), (0, 1)], scale, causal, f"N{N} d{d} {dtype} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [0.0, 1e-35, 2.0])
+def test_degenerate_and_large_scales(scale, causal, d):
+    # scale 0: uniform attention over the visible keys, dQ = dK = 0 exactly;
+    # 1e-35 lies below the smallest scale the dK/dV kernel splits its exponent
+    # with (2^-100), where the exponent is -LSE log2 e up to rounding; 2: sharp
+    # softmax rows.  bf16 keeps dQ, dK ~ 1e-35 representable.
+    N, dtype = 300, "bf16"
+    say(f"bwd scale={scale} N{N} d{d} causal={causal}")
+    inp = si.make_inputs(1, 2, N, d, dtype, 1.0, 9500 + d + int(causal), backward=True)
+    grads = _run(inp, dtype, causal, scale)
+    _check_heads(inp, grads, [(0, 0), (0, 1)], scale, causal, f"scale={scale} d{d} causal={causal}")
+
+
 @pytest.mark.parametrize("name", ["C5", "C5d128"])
 def test_c5_full_size_sampled_heads(name):
     w = si.WORKLOADS[name]
