@@ -175,3 +175,56 @@ def test_key_shift_invariance_on_gpu():
     np.testing.assert_allclose(o2.cpu().numpy(), o1.cpu().numpy(), atol=2e-5)
     shift = scale * (inp["q"][0].astype(np.float64) @ c.astype(np.float64))
     np.testing.assert_allclose(l2.cpu().numpy(), l1.cpu().numpy() + shift, atol=2e-4)
+
+
+# ------------------------------------------------------------ O(N) device memory (long context)
+
+def test_c4_peak_memory_is_inputs_and_outputs_only():
+    """Long-context forward (B=1 H=32 d=128 fp16 causal): peak device memory
+    during fa_fwd is exactly Q, K, V, O plus the float32 LSE, i.e. linear in
+    N, and the library allocates nothing (free device memory is unchanged
+    across the call).  A materialised N x N score matrix would need
+    H*N^2*2 bytes (64 GiB at N = 32768)."""
+    import torch
+    fa = __import__("parity").lib()
+    B, H, d = 1, 32, 128
+    # one small call first, so that loading the kernel's code is not counted
+    x = torch.zeros((1, 1, 256, d), dtype=torch.float16, device="cuda")
+    fa.fwd(x, x, x, True)
+    torch.cuda.synchronize()
+    del x
+    peaks = {}
+    for N in (8192, 16384, 32768):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        g = torch.Generator(device="cuda").manual_seed(1004)
+        q, k, v = (torch.randn((B, H, N, d), generator=g, device="cuda", dtype=torch.float32)
+                   .mul_(0.5).to(torch.float16) for _ in range(3))
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        free0, _ = torch.cuda.mem_get_info()
+        fa.fa_fwd(q, k, v, o, lse, 1.0 / np.sqrt(d), True)
+        torch.cuda.synchronize()
+        free1, _ = torch.cuda.mem_get_info()
+        peak = torch.cuda.max_memory_allocated() - base
+        held = torch.cuda.memory_allocated() - base
+        expect = 4 * B * H * N * d * 2 + 4 * B * H * N
+        nbytes = sum(t.numel() * t.element_size() for t in (q, k, v, o, lse))
+        say(f"  N={N}: peak {peak} B, tensors {nbytes} B (Q, K, V, O + LSE = {expect}), "
+            f"free device memory before/after fa_fwd {free0}/{free1}")
+        assert nbytes == expect
+        # nothing beyond the five tensors was ever held; the caching allocator
+        # rounds a block below 2 MiB (the 1 MiB LSE at N = 8192) up to 2 MiB
+        assert peak == held and 0 <= held - expect < (2 << 20), (N, peak, held, expect)
+        assert free1 == free0, "the library allocated device memory"
+        assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+        peaks[N] = peak
+        del q, k, v, o, lse
+    assert peaks[32768] == 2 * peaks[16384]  # linear in N (both sizes are whole 2 MiB blocks)
+    assert peaks[32768] == 1_077_936_128
