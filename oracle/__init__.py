@@ -9,15 +9,19 @@ Contents
 --------
 attention.py  plain float64 numpy definition of attention forward (two-pass
               softmax, never online) and of its gradient (softmax Jacobian).
-brute.py      40-digit ``decimal`` brute force of the forward for tiny shapes,
-              used only to pin ``attention.py``.
+kvcache.py    plain float64 definition of a few new queries attending to a
+              key/value cache (fewer queries than keys, bottom-right causal
+              mask, per-batch filled lengths).
+brute.py      40-digit ``decimal`` brute force of both forwards for tiny
+              shapes, used only to pin ``attention.py`` and ``kvcache.py``.
 
 Parity status: every public function here is pinned by ``tests/test_oracle.py``
 (brute force, closed forms, invariants, finite differences, mutation checks).
 """
 
 from .attention import attention_fwd, attention_fwd_head, attention_bwd, attention_bwd_head
-from .brute import brute_fwd_decimal
+from .brute import brute_fwd_decimal, brute_kvcache_decimal
+from .kvcache import kvcache_fwd, kvcache_fwd_head
 
 __all__ = [
     "attention_fwd",
@@ -25,4 +29,7 @@ __all__ = [
     "attention_bwd",
     "attention_bwd_head",
     "brute_fwd_decimal",
+    "brute_kvcache_decimal",
+    "kvcache_fwd",
+    "kvcache_fwd_head",
 ]

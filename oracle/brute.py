@@ -51,3 +51,33 @@ def brute_fwd_decimal(q, k, v, scale, causal: bool, prec: int = 40):
             out.append(row)
             lse.append(z.ln())
         return out, lse
+
+
+def brute_kvcache_decimal(q, k, v, scale, causal: bool, seqlen: int, prec: int = 40):
+    """Nq queries against the first ``seqlen`` rows of a key/value cache, one
+    head, in 40-digit decimal: (O, LSE) as nested lists of Decimal.
+
+    Query i (0-based, of Nq) sees key j iff j < seqlen and, when ``causal``,
+    j - i <= seqlen - Nq (bottom-right aligned mask).  A query that sees no
+    key gets O = 0 and LSE = -Infinity.
+    """
+    with localcontext() as ctx:
+        ctx.prec = prec
+        sc = Decimal(float(scale))
+        nq, d, dv = len(q), len(q[0]), len(v[0])
+        out, lse = [], []
+        for i in range(nq):
+            keys = [j for j in range(seqlen) if not causal or j - i <= seqlen - nq]
+            if not keys:
+                out.append([Decimal(0)] * dv)
+                lse.append(Decimal("-Infinity"))
+                continue
+            weights = []
+            for j in keys:
+                dot = sum((Decimal(float(q[i][c])) * Decimal(float(k[j][c])) for c in range(d)), Decimal(0))
+                weights.append((j, (sc * dot).exp()))
+            z = sum((w for _, w in weights), Decimal(0))
+            out.append([sum((w * Decimal(float(v[j][c])) for j, w in weights), Decimal(0)) / z
+                        for c in range(dv)])
+            lse.append(z.ln())
+        return out, lse

@@ -1,0 +1,95 @@
+"""Plain float64 attention of a few new queries against a key/value cache.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): never imported by the
+product path.
+
+What is computed, and where the pages put it
+--------------------------------------------
+The pages name inference next to training as what the method speeds up
+("FlashAttention-2 (DE)", lead paragraph, and "Das Attention-Problem in
+Transformern": Falcon-40B inference), and place the method in model serving
+together with block-wise management of the key/value cache, which it is not
+the same thing as ("FlashAttention" glossary, sections "Der Engpass ist der
+Weg zum Speicher, nicht das Rechnen" and "Wo es verwechselt wird"; related
+terms "KV Cache", "Memory-Bound", "Model Serving").  The pages give no
+formula for it; the computation is the same scaled-dot-product attention as
+in ``attention.py``, only with fewer queries than keys.
+
+Per (batch, head), with Nq new queries, a cache of capacity Nk rows of which
+the first L (``seqlen``, 0 <= L <= Nk) are filled:
+
+    visible(i) = { j : j < L }                          (non-causal)
+               = { j : j < L and j <= i + (L - Nq) }    (causal)
+
+i.e. the causal mask is aligned at the bottom right: the last query sees every
+filled key, the query before it one key less, and so on (the queries are the
+last Nq positions of a sequence of length L).  Over visible(i):
+
+    s_ij  = scale * q_i . k_j
+    p_ij  = exp(s_ij - m_i) / sum_j' exp(s_ij' - m_i),  m_i = max_j s_ij
+    O_i   = sum_j p_ij v_j
+    LSE_i = m_i + ln sum_j exp(s_ij - m_i)
+
+A query with no visible key (L = 0, or causal with i < Nq - L) has an empty
+softmax; this file's convention for it is O_i = 0 and LSE_i = -inf (the
+logarithm of an empty sum).  Cache rows at and past L are never read.
+
+Two-pass softmax over the whole visible row, never online, never split over
+keys.  With Nq = Nk = L this is exactly ``attention.py``'s forward (the
+causal mask is then the usual top-left one).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _visible(nq: int, seqlen: int, causal: bool) -> np.ndarray:
+    """[nq, seqlen] boolean: key j visible to query i."""
+    j = np.arange(seqlen)[None, :]
+    if not causal:
+        return np.ones((nq, seqlen), dtype=bool)
+    i = np.arange(nq)[:, None]
+    return j <= i + (seqlen - nq)
+
+
+def kvcache_fwd_head(q, k, v, scale: float, causal: bool, seqlen: int | None = None):
+    """One head. q: [Nq, d]; k, v: [Nk, d] cache; seqlen: filled rows (default Nk).
+
+    Returns (O [Nq, d], LSE [Nq]) in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    nk = np.asarray(k).shape[0]
+    L = nk if seqlen is None else int(seqlen)
+    if not 0 <= L <= nk:
+        raise ValueError("seqlen must lie in [0, Nk]")
+    kk = np.asarray(k, dtype=np.float64)[:L]
+    vv = np.asarray(v, dtype=np.float64)[:L]
+    nq = q.shape[0]
+    o = np.zeros((nq, vv.shape[1]))
+    lse = np.full(nq, -np.inf)
+    if L == 0:
+        return o, lse
+    vis = _visible(nq, L, causal)
+    s = np.where(vis, scale * (q @ kk.T), -np.inf)  # s_ij over the filled keys
+    rows = vis.any(axis=1)  # queries with at least one visible key
+    m = s[rows].max(axis=1, keepdims=True)
+    e = np.exp(s[rows] - m)
+    z = e.sum(axis=1, keepdims=True)
+    o[rows] = (e / z) @ vv
+    lse[rows] = (m + np.log(z))[:, 0]
+    return o, lse
+
+
+def kvcache_fwd(q, k, v, scale: float, causal: bool, seqlens=None):
+    """[B, H, Nq, d] queries against [B, H, Nk, d] caches; seqlens: [B] filled
+    lengths (default: all Nk).  Returns (O [B,H,Nq,d], LSE [B,H,Nq]) float64."""
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+    b, h, nq, _ = q.shape
+    nk = k.shape[2]
+    lens = [nk] * b if seqlens is None else [int(x) for x in seqlens]
+    o = np.empty((b, h, nq, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((b, h, nq), dtype=np.float64)
+    for bi in range(b):
+        for hi in range(h):
+            o[bi, hi], lse[bi, hi] = kvcache_fwd_head(q[bi, hi], k[bi, hi], v[bi, hi], scale, causal, lens[bi])
+    return o, lse

@@ -1,0 +1,185 @@
+"""Pins for the float64 key/value-cache oracle (``oracle/kvcache.py``), all on
+the CPU, each checked against something other than the function itself: the
+40-digit decimal brute force, the already pinned square-attention oracle
+(``attention.py``) on the same sequence, and identities of exact attention.
+``test_kvcache_mutations_are_caught`` plants plausible mistakes in a copy of
+the source and checks that the battery catches each one.
+"""
+
+import math
+import types
+
+import numpy as np
+import pytest
+
+from oracle import attention_fwd_head, brute_kvcache_decimal, kvcache_fwd, kvcache_fwd_head
+from oracle import kvcache as okv
+
+
+def rnd(rng, *shape, s=1.0):
+    return rng.standard_normal(shape) * s
+
+
+def _dec(o, lse):
+    return (np.array([[float(x) for x in r] for r in o]).reshape(len(o), -1),
+            np.array([float(x) for x in lse]))
+
+
+CASES = [(1, 1, 1), (1, 5, 5), (1, 6, 3), (2, 4, 4), (3, 7, 5), (5, 8, 8), (4, 6, 2), (3, 3, 0), (2, 5, 1)]
+
+
+@pytest.mark.parametrize("nq,nk,L", CASES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_kvcache_matches_decimal_brute_force(nq, nk, L, causal):
+    rng = np.random.default_rng(500 + 11 * nq + 3 * nk + L)
+    d = 3
+    q, k, v = rnd(rng, nq, d, s=1.5), rnd(rng, nk, d, s=1.5), rnd(rng, nk, d)
+    o, lse = kvcache_fwd_head(q, k, v, 0.7, causal, L)
+    ob, lb = _dec(*brute_kvcache_decimal(q, k, v, 0.7, causal, L))
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lb))
+    fin = np.isfinite(lb)
+    assert np.max(np.abs(o - ob), initial=0.0) <= 1e-12
+    assert np.max(np.abs(lse[fin] - lb[fin]), initial=0.0) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_square_case_is_the_ordinary_forward(causal):
+    rng = np.random.default_rng(7)
+    n, d = 37, 8
+    q, k, v = rnd(rng, n, d), rnd(rng, n, d), rnd(rng, n, d)
+    o, lse = kvcache_fwd_head(q, k, v, 1 / math.sqrt(d), causal)
+    o2, lse2 = attention_fwd_head(q, k, v, 1 / math.sqrt(d), causal)
+    assert np.max(np.abs(o - o2)) <= 1e-13 and np.max(np.abs(lse - lse2)) <= 1e-13
+
+
+@pytest.mark.parametrize("nq,L", [(1, 40), (5, 40), (40, 40), (7, 9)])
+def test_causal_queries_are_the_last_rows_of_the_full_sequence(nq, L):
+    """Bottom-right alignment: the Nq queries are positions L-Nq .. L-1 of a
+    sequence of length L, so they equal those rows of ordinary causal attention."""
+    rng = np.random.default_rng(8 + nq)
+    d = 6
+    k, v = rnd(rng, L + 5, d), rnd(rng, L + 5, d)
+    qfull = rnd(rng, L, d)
+    o, lse = kvcache_fwd_head(qfull[L - nq:], k, v, 0.4, True, L)
+    of, lf = attention_fwd_head(qfull, k[:L], v[:L], 0.4, True)
+    assert np.max(np.abs(o - of[L - nq:])) <= 1e-13
+    assert np.max(np.abs(lse - lf[L - nq:])) <= 1e-13
+
+
+def test_single_query_sees_every_filled_key():
+    rng = np.random.default_rng(9)
+    q, k, v = rnd(rng, 1, 4), rnd(rng, 30, 4), rnd(rng, 30, 4)
+    for L in (1, 17, 30):
+        a = kvcache_fwd_head(q, k, v, 0.5, True, L)
+        b = kvcache_fwd_head(q, k, v, 0.5, False, L)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_rows_past_the_filled_length_are_never_read():
+    rng = np.random.default_rng(10)
+    q, k, v = rnd(rng, 3, 4), rnd(rng, 20, 4), rnd(rng, 20, 4)
+    k2, v2 = k.copy(), v.copy()
+    k2[12:] = np.nan
+    v2[12:] = np.inf
+    for causal in (False, True):
+        a = kvcache_fwd_head(q, k, v, 0.5, causal, 12)
+        b = kvcache_fwd_head(q, k2, v2, 0.5, causal, 12)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_empty_rows_convention():
+    rng = np.random.default_rng(11)
+    q, k, v = rnd(rng, 4, 3), rnd(rng, 6, 3), rnd(rng, 6, 3)
+    o, lse = kvcache_fwd_head(q, k, v, 0.5, False, 0)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    # causal with L = 2 < Nq = 4: queries 0 and 1 see nothing, query 2 sees key 0
+    o, lse = kvcache_fwd_head(q, k, v, 0.5, True, 2)
+    assert np.all(o[:2] == 0) and np.all(np.isneginf(lse[:2]))
+    assert np.max(np.abs(o[2] - v[0])) <= 1e-15
+    assert abs(lse[2] - 0.5 * q[2] @ k[0]) <= 1e-14
+
+
+def test_zero_queries_give_mean_of_visible_values():
+    rng = np.random.default_rng(12)
+    k, v = rnd(rng, 10, 3), rnd(rng, 10, 3)
+    q = np.zeros((3, 3))
+    o, lse = kvcache_fwd_head(q, k, v, 0.5, True, 8)
+    for i in range(3):
+        n_vis = 8 - 3 + i + 1
+        assert np.max(np.abs(o[i] - v[:n_vis].mean(axis=0))) <= 1e-14
+        assert abs(lse[i] - math.log(n_vis)) <= 1e-14
+
+
+def test_split_keys_merge_to_the_whole():
+    """The identity a split-key computation relies on: partial results over
+    disjoint key ranges combine through their log-sum-exps,
+    LSE = ln sum_s e^{LSE_s},  O = sum_s e^{LSE_s - LSE} O_s."""
+    rng = np.random.default_rng(13)
+    q, k, v = rnd(rng, 3, 5, s=2), rnd(rng, 50, 5, s=2), rnd(rng, 50, 5)
+    o, lse = kvcache_fwd_head(q, k, v, 0.6, False, 50)
+    parts = [kvcache_fwd_head(q, k[a:b], v[a:b], 0.6, False) for a, b in ((0, 7), (7, 30), (30, 50))]
+    ls = np.stack([p[1] for p in parts])
+    top = ls.max(axis=0)
+    lse_m = top + np.log(np.exp(ls - top).sum(axis=0))
+    o_m = sum(np.exp(p[1] - lse_m)[:, None] * p[0] for p in parts)
+    assert np.max(np.abs(lse_m - lse)) <= 1e-13 and np.max(np.abs(o_m - o)) <= 1e-13
+
+
+def test_batched_with_lengths_matches_per_head():
+    rng = np.random.default_rng(14)
+    q, k, v = rnd(rng, 3, 2, 4, 5), rnd(rng, 3, 2, 9, 5), rnd(rng, 3, 2, 9, 5)
+    lens = [9, 0, 4]
+    o, lse = kvcache_fwd(q, k, v, 0.3, True, lens)
+    for b in range(3):
+        for h in range(2):
+            oo, ll = kvcache_fwd_head(q[b, h], k[b, h], v[b, h], 0.3, True, lens[b])
+            assert np.array_equal(o[b, h], oo) and np.array_equal(lse[b, h], ll)
+
+
+# ---------------------------------------------------------------- mutation check
+
+def _kv_pins_pass(mod) -> bool:
+    rng = np.random.default_rng(41)
+    try:
+        for causal in (False, True):
+            for nq, nk, L in ((3, 7, 5), (4, 6, 2), (1, 4, 4), (2, 3, 0)):
+                q, k, v = rnd(rng, nq, 3, s=1.5), rnd(rng, nk, 3, s=1.5), rnd(rng, nk, 3)
+                k[L:] = np.nan
+                v[L:] = np.nan
+                o, lse = mod.kvcache_fwd_head(q, k, v, 0.7, causal, L)
+                ob, lb = _dec(*brute_kvcache_decimal(q, k, v, 0.7, causal, L))
+                if not np.array_equal(np.isneginf(lse), np.isneginf(lb)):
+                    return False
+                fin = np.isfinite(lb)
+                if not np.max(np.abs(o - ob), initial=0.0) <= 1e-12:
+                    return False
+                if not np.max(np.abs(lse[fin] - lb[fin]), initial=0.0) <= 1e-12:
+                    return False
+        return True
+    except Exception:
+        return False
+
+
+KV_MUTATIONS = [
+    ("mask aligned top-left", "return j <= i + (seqlen - nq)", "return j <= i"),
+    ("mask off by one", "return j <= i + (seqlen - nq)", "return j < i + (seqlen - nq)"),
+    ("mask offset sign", "return j <= i + (seqlen - nq)", "return j <= i - (seqlen - nq)"),
+    ("filled length ignored", "kk = np.asarray(k, dtype=np.float64)[:L]", "kk = np.asarray(k, dtype=np.float64)[:nk]"),
+    ("scale dropped", "s = np.where(vis, scale * (q @ kk.T), -np.inf)", "s = np.where(vis, (q @ kk.T), -np.inf)"),
+    ("not normalised", "o[rows] = (e / z) @ vv", "o[rows] = e @ vv"),
+    ("lse drops the max", "lse[rows] = (m + np.log(z))[:, 0]", "lse[rows] = (np.log(z))[:, 0]"),
+    ("empty rows get lse 0", "lse = np.full(nq, -np.inf)", "lse = np.zeros(nq)"),
+]
+
+
+def test_unmutated_kvcache_oracle_passes_battery():
+    assert _kv_pins_pass(okv)
+
+
+@pytest.mark.parametrize("label,old,new", KV_MUTATIONS, ids=[m[0] for m in KV_MUTATIONS])
+def test_kvcache_mutations_are_caught(label, old, new):
+    src = open(okv.__file__).read()
+    assert old in src, f"mutation anchor not found: {label}"
+    mod = types.ModuleType("kv_mutant")
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
+    assert not _kv_pins_pass(mod), f"pins did not catch mutation: {label}"
