@@ -11,9 +11,12 @@ place of pointers):
     fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, causal)
     fa_bwd_workspace_bytes(B, H, N, d, dtype)
     fa_bwd_prep(o, dout, workspace); fa_bwd_dkdv(...); fa_bwd_dq(...)  (fa_bwd's stages)
+    fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, workspace, scale, causal)
+    fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, dtype)
 Conveniences that allocate their outputs with torch:
     fwd(q, k, v, causal=False, scale=None) -> (o, lse)
     bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
+    fwd_kvcache(q, k_cache, v_cache, seqlens_k=None, causal=True, scale=None) -> (o, lse)
     FlashAttention (torch.autograd.Function) and attention(q, k, v, causal, scale)
 """
 
@@ -67,6 +70,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
     L.fa_bwd_dq.restype = i32
     L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, i64, i64, i64, i64, f32, i32, i32, vp]
+    L.fa_fwd_kvcache_workspace_bytes.restype = sz
+    L.fa_fwd_kvcache_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+    L.fa_fwd_kvcache.restype = i32
+    L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, f32, i32, i32, vp]
     _lib = L
     return L
 
@@ -181,6 +188,53 @@ def fa_bwd_dq(q, k, v, dout, lse, workspace, dq, scale: float, causal: bool) -> 
                        B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), _stream(q)))
 
 
+def fa_fwd_kvcache_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int, dtype: int) -> int:
+    return int(load_library().fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, dtype))
+
+
+def fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, workspace, scale: float, causal: bool) -> None:
+    """Enqueue queries against a key/value cache on the current stream (see include/fa.h).
+
+    q, o: [B, H, Nq, d]; k_cache, v_cache: [B, H, Nk, d]; seqlens_k: int32 [B]
+    on the device or None; lse: float32 [B, H, Nq]; workspace: device bytes or
+    None when fa_fwd_kvcache_workspace_bytes() is 0."""
+    L = load_library()
+    torch = _torch()
+    _check_tensors(q, k_cache, v_cache, seqlens_k, o, lse, workspace)
+    B, H, Nq, d = _bhnd(q)
+    Nk = int(k_cache.shape[2]) if k_cache.dim() == 4 else -1
+    if tuple(k_cache.shape) != (B, H, Nk, d) or tuple(v_cache.shape) != (B, H, Nk, d):
+        raise ValueError("k_cache and v_cache must be [B, H, Nk, d] with q's B, H and d")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or o.dtype != q.dtype:
+        raise ValueError("q, k_cache, v_cache, o must share dtype")
+    if tuple(o.shape) != (B, H, Nq, d):
+        raise ValueError("o must be [B, H, Nq, d]")
+    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, Nq]")
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or tuple(seqlens_k.shape) != (B,)):
+        raise ValueError("seqlens_k must be int32 [B]")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(L.fa_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(o), _ptr(lse),
+                            _ptr(workspace), nbytes, B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+                            dtype_code(q), _stream(q)))
+
+
+def fwd_kvcache(q, k_cache, v_cache, seqlens_k=None, causal: bool = True, scale: float | None = None,
+                workspace=None):
+    """Allocate O, LSE (and the workspace unless given) and run the queries
+    against the cache. Returns (o, lse)."""
+    torch = _torch()
+    B, H, Nq, d = _bhnd(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nb = fa_fwd_kvcache_workspace_bytes(B, H, Nq, int(k_cache.shape[2]), d, dtype_code(q))
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb > 0 else None
+    fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, workspace,
+                   default_scale(d) if scale is None else scale, causal)
+    return o, lse
+
+
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
@@ -239,6 +293,7 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None):
 
 __all__ = [
     "load_library", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_prep", "fa_bwd_dkdv",
-    "fa_bwd_dq", "fwd", "bwd", "attention",
+    "fa_bwd_dq", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fwd", "bwd", "fwd_kvcache",
+    "attention",
     "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH",
 ]

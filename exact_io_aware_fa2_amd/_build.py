@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_kvcache.hip"]
 ARCH = "gfx950"
 
 
@@ -43,7 +43,7 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build_library(verbose: bool = False, jobs: int = 3) -> str:
+def build_library(verbose: bool = False, jobs: int = 4) -> str:
     """Compile every source to an object (in parallel) and link the shared library."""
     out_dir = os.path.join(PKG_DIR, "_build")
     os.makedirs(out_dir, exist_ok=True)

@@ -207,3 +207,70 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
 }
 
 }  // extern "C"
+
+namespace {
+
+// Checks of fa_fwd_kvcache's sizes: the query and cache lengths are bounded
+// like N, and the split kernel's workgroup count (four wavefronts each) like
+// every other grid.
+int check_kv_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (Nq > kMaxN || Nk > kMaxN) return FA_ERR_SHAPE;
+  if (B > INT32_MAX / H) return FA_ERR_SHAPE;
+  const int64_t bh = B * H;
+  if (bh * Nq > INT32_MAX) return FA_ERR_SHAPE;
+  const fa::KvPlan p = fa::kv_plan(bh, Nq, Nk);
+  if ((bh * p.n_qb * p.n_splits + 3) / 4 > kMaxWorkgroups) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_fwd_kvcache_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                      int dtype) {
+  if (check_kv_shape(B, H, Nq, Nk, d) != FA_OK) return 0;
+  if (dtype != FA_F16 && dtype != FA_BF16) return 0;
+  return fa::kv_workspace_bytes(B * H, Nq, Nk, d);
+}
+
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k,
+                   void* o, float* lse, void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                   int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !lse) return FA_ERR_NULL;
+  int st = check_kv_shape(B, H, Nq, Nk, d);
+  if (st != FA_OK) return st;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0) return FA_ERR_ALIGN;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  const size_t need = fa::kv_workspace_bytes(B * H, Nq, Nk, d);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  }
+  fa::KvArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seqlens = seqlens_k;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = need > 0 ? workspace : nullptr;
+  a.H = (int)H;
+  a.BH = (int)(B * H);
+  a.Nq = (int)Nq;
+  a.Nk = (int)Nk;
+  a.d = (int)d;
+  a.c = exp2_factor(scale);
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.stream = (hipStream_t)stream;
+  return status_of(fa::launch_fwd_kvcache(a));
+}
+
+}  // extern "C"

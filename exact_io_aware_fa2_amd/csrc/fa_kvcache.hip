@@ -1,0 +1,301 @@
+// Attention of a few new queries against a key/value cache, for gfx950.
+//
+// The pages name inference beside training as what the method speeds up
+// ("FlashAttention-2 (DE)", lead paragraph; "Das Attention-Problem in
+// Transformern": Falcon-40B inference) and place it in model serving next to
+// the block-wise management of the key/value cache ("FlashAttention"
+// glossary, "Der Engpass ist der Weg zum Speicher, nicht das Rechnen" and
+// "Wo es verwechselt wird"; related terms "KV Cache", "Memory-Bound").  The
+// computation is the same exact attention with Nq new queries (usually 1) and
+// a cache of capacity Nk rows, of which the first L = seqlens[b] are filled:
+// query i sees key j iff j < L and, causal, j <= i + L - Nq (the queries are
+// the last Nq positions of the sequence: the mask is aligned bottom right).
+//
+// With few queries the work per key is tiny and the cache has to be read once
+// from HBM, so the bound is HBM bandwidth, not the matrix cores.  To spread
+// one head's cache over many compute units the keys are split into ranges
+// ("split-KV"): every wavefront takes one range of `kps` keys and one block of
+// 32 queries, runs the tiled online softmax over its range, and writes a
+// partial result (O normalised within the range, and two log-sum-exps in base
+// 2).  A second kernel merges the ranges of each query with the identity the
+// online softmax itself rests on ("FlashAttention" lexicon, "Methodische
+// Grundlagen", "Fortlaufende Normierung"):
+//     LSE = log2 sum_s 2^{LSE_s},   O = sum_s 2^{LSE_s - LSE} O_s.
+// When one range covers every key the first kernel writes O and LSE itself.
+//
+// Per 32-key tile a wavefront computes S^T = K Q^T with K straight from HBM
+// into the A operands (each lane loads 16 bytes of one key row per k-step),
+// then O^T += V^T P~^T with V staged through the wavefront's own LDS rows and
+// read back transposed (ds_read_b64_tr_b16).  No workgroup barrier is used:
+// the four wavefronts of a workgroup are independent.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+// Key (within its 32-key tile) that A-operand row m of S^T = K Q^T holds: m
+// with bits 2 and 3 exchanged.  Accumulator value r of lane half h is S^T row
+// 8 (r / 4) + 4 h + r % 4, i.e. key 16 (r / 8) + 8 h + r % 8, so the eight
+// scores r = 8 t .. 8 t + 7 a lane feeds into P~ V k-step t are eight
+// consecutive keys 16 t + 8 h + 0..7 -- the eight rows one pair of transposed
+// LDS reads returns for the V^T operand.
+__device__ inline int kv_tile_key(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+template <class TR, int D, bool CAUSAL, bool DIRECT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_split_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const int32_t* __restrict__ seqlens, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    float* __restrict__ part_o, float* __restrict__ part_l, int H, int BH, int Nq, int Nk, int n_qb,
+    int n_splits, int kps, uint32_t n_wg, uint32_t n_waves, float c) {
+  constexpr int NKS = D / 16;          // k-steps of S^T = K Q^T
+  constexpr int NDB = D / 32;          // 32-row blocks of O^T
+  constexpr uint32_t RB = 2 * D;       // global row bytes
+  constexpr int RS = 2 * D + 64;       // LDS row bytes of the V tile: a stride of 16 (mod 64)
+                                       // dwords puts the 4 rows of a transposed read in 4 bank groups
+  constexpr int VCH = D / 8;           // 16-byte chunks per V row
+  constexpr int NVL = 32 * VCH / 64;   // V chunks per lane per tile
+  static_assert(32 * RS >= kTileRowsBytes<D>, "the output tile fits the V rows");
+  __shared__ __attribute__((aligned(16))) char smem[4 * 32 * RS];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  // wavefront -> (head, key range, query block), query block fastest, so the
+  // wavefronts of one head's range sit together (same XCD via xcd_remap)
+  const uint32_t wid = 4 * xcd_remap(blockIdx.x, n_wg) + (uint32_t)w;
+  if (wid >= n_waves) return;
+  const int qb = (int)(wid % (uint32_t)n_qb);
+  const int split = (int)((wid / (uint32_t)n_qb) % (uint32_t)n_splits);
+  const int bh = (int)(wid / ((uint32_t)n_qb * (uint32_t)n_splits));
+  int L = seqlens ? seqlens[bh / H] : Nk;
+  L = min(max(L, 0), Nk);
+  char* lds = smem + w * 32 * RS;
+
+  const int q0 = 32 * qb;
+  const int qi = q0 + l32;  // this lane's query (rows past Nq read as zeros, never stored)
+  // last visible key of this lane's query, and of the block's last real query
+  const int lim = CAUSAL ? min(L - 1, qi + L - Nq) : L - 1;
+  const int lim_blk = CAUSAL ? min(L - 1, min(q0 + 31, Nq - 1) + L - Nq) : L - 1;
+  const int kb = split * kps;
+  const int ke = min(kb + kps, lim_blk + 1);
+
+  // Q rows of this block as B operands (column = query)
+  u32x4_t qf[NKS];
+  {
+    const rsrc_t qres = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * RB);
+    const uint32_t off = (uint32_t)qi * RB + 16 * h;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(qres, off + 32 * ks);
+  }
+  // the cache of this head up to the filled length: rows at and past L read as zeros
+  const rsrc_t kres = make_rsrc(K + (size_t)bh * Nk * D, (uint32_t)L * RB);
+  const rsrc_t vres = make_rsrc(V + (size_t)bh * Nk * D, (uint32_t)L * RB);
+  const uint32_t k_lane = (uint32_t)kv_tile_key(l32) * RB + 16 * h;
+  // transposed-read address of this lane: group G = lane / 16 reads columns
+  // 16 (G % 2) + 0..15 of rows 8 h + 0..3 (and + 4), lane 4 e + i of the group
+  // pointing at columns 4 i .. 4 i + 3 of row e
+  const int L16 = lane & 15, G = lane >> 4;
+  const int tr_base = (8 * h + (L16 >> 2)) * RS + (16 * (G & 1) + 4 * (L16 & 3)) * 2;
+
+  float m = -INFINITY;     // running reference maximum (base-2 units), the same in both halves
+  float l = 0.0f, lt = 0.0f;  // this lane's partial sums of P and of the rounded P~
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+
+  for (int k0 = kb; k0 < ke; k0 += 32) {
+    u32x4_t kf[NKS], vv[NVL];
+    const uint32_t kt = (uint32_t)k0 * RB;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) kf[ks] = buf_load16(kres, kt + k_lane + 32 * ks);
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int ch = 64 * i + lane;
+      vv[i] = buf_load16(vres, kt + (uint32_t)(ch / VCH) * RB + 16 * (ch % VCH));
+    }
+    f32x16_t s = zero16();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) s = TR::mfma(kf[ks], qf[ks], s);
+
+    // scores in base-2 units, masked; tile maximum of the query over both halves
+    float x[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 16 * (r / 8) + 8 * h + (r % 8);
+      x[r] = key <= lim ? s[r] * c : -INFINITY;
+      mt = fmaxf(mt, x[r]);
+    }
+    mt = fmaxf(mt, swap_halves(mt));
+    const float mn = fmaxf(m, mt);
+    const float mu = mn == -INFINITY ? 0.0f : mn;  // no visible key yet: every weight is 0
+    const float alpha = fast_exp2(m - mu);
+    if (__any(alpha != 1.0f)) {
+      l *= alpha;
+      lt *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+    m = mn;
+    u32x4_t pk[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = fast_exp2(x[8 * t + 2 * j] - mu), p1 = fast_exp2(x[8 * t + 2 * j + 1] - mu);
+        l += p0 + p1;
+        pk[t][j] = TR::pack2(p0, p1);
+        lt = TR::sum2(pk[t][j], lt);
+      }
+
+    // V tile -> this wavefront's LDS rows (after the previous tile's reads)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int ch = 64 * i + lane;
+      *(u32x4_t*)(lds + (ch / VCH) * RS + 16 * (ch % VCH)) = vv[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const char* p = lds + tr_base + 16 * t * RS + 64 * db;
+        const u32x2_t a = lds_read_tr(p), b2 = lds_read_tr(p + 4 * RS);
+        acc[db] = TR::mfma(u32x4_t{a[0], a[1], b2[0], b2[1]}, pk[t], acc[db]);
+      }
+  }
+  l += swap_halves(l);
+  lt += swap_halves(lt);
+  const bool empty = m == -INFINITY;  // no visible key for this query in this range
+  const float inv = empty ? 0.0f : 1.0f / lt;
+
+  if constexpr (DIRECT) {
+    u32x2_t ov[NDB][4];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        ov[db][g] = u32x2_t{TR::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                            TR::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    store_tile_rows<D>(lds, ov, O + ((size_t)bh * Nq + q0) * D, min(32, Nq - q0), lane);
+    if (h == 0 && qi < Nq) LSE[(size_t)bh * Nq + qi] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+  } else {
+    if (qi < Nq) {
+      const size_t rec = ((size_t)split * BH + bh) * Nq + qi;
+      float* po = part_o + rec * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(float4*)(po + 32 * db + 8 * g + 4 * h) =
+              float4{acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv, acc[db][4 * g + 2] * inv,
+                     acc[db][4 * g + 3] * inv};
+      if (h == 0)
+        *(float2*)(part_l + 2 * rec) =
+            empty ? float2{-INFINITY, -INFINITY} : float2{m + __log2f(lt), m + __log2f(l)};
+    }
+  }
+}
+
+// One wavefront per query row: combine the key ranges' partial results.
+// part_l holds per range (log2 of the range's sum of rounded weights P~, log2
+// of its sum of P), both including the range's reference maximum; part_o the
+// range's O normalised by its own sum of P~.  O is normalised by the total
+// sum of P~ (the weights that multiplied V), LSE uses the total sum of P.
+template <class TR, int D>
+__global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__ part_o,
+                                                       const float* __restrict__ part_l,
+                                                       uint16_t* __restrict__ O, float* __restrict__ LSE,
+                                                       int rows, int n_splits) {
+  constexpr int PER = D / 64;  // columns per lane
+  const int lane = threadIdx.x & 63;
+  const int row = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (row >= rows) return;
+  float mt = -INFINITY, ml = -INFINITY;
+  for (int s = lane; s < n_splits; s += 64) {
+    const float2 v = *(const float2*)(part_l + 2 * ((size_t)s * rows + row));
+    mt = fmaxf(mt, v.x);
+    ml = fmaxf(ml, v.y);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mt = fmaxf(mt, __shfl_xor(mt, off, 64));
+    ml = fmaxf(ml, __shfl_xor(ml, off, 64));
+  }
+  float acc[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) acc[p] = 0.0f;
+  float ws = 0.0f, ls = 0.0f;
+  if (mt != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const size_t rec = (size_t)s * rows + row;
+      const float2 v = *(const float2*)(part_l + 2 * rec);
+      if (v.x == -INFINITY) continue;  // empty range (the same in every lane)
+      const float wt = fast_exp2(v.x - mt);
+      ws += wt;
+      ls += fast_exp2(v.y - ml);
+      const float* po = part_o + rec * D + PER * lane;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) acc[p] += wt * po[p];
+    }
+  }
+  const float inv = mt == -INFINITY ? 0.0f : 1.0f / ws;
+  uint16_t* orow = O + (size_t)row * D + PER * lane;
+  if constexpr (PER == 2) {
+    *(uint32_t*)orow = TR::pack2(acc[0] * inv, acc[1] * inv);
+  } else {
+    *orow = (uint16_t)(TR::pack2(acc[0] * inv, 0.0f) & 0xFFFFu);
+  }
+  if (lane == 0) LSE[row] = mt == -INFINITY ? -INFINITY : (ml + __log2f(ls)) * kLn2;
+}
+
+// ------------------------------------------------------------------ launch
+
+template <class TR, int D, bool CAUSAL>
+static hipError_t launch_kv(const KvArgs& a, const KvPlan& p) {
+  const uint32_t n_waves = (uint32_t)((int64_t)a.BH * p.n_qb * p.n_splits);
+  const uint32_t n_wg = (n_waves + 3) / 4;
+  float* part_o = (float*)a.workspace;
+  float* part_l = part_o ? part_o + (size_t)p.n_splits * a.BH * a.Nq * D : nullptr;
+  if (p.n_splits == 1) {
+    hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, true>), dim3(n_wg), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.seqlens,
+                       (uint16_t*)a.o, a.lse, nullptr, nullptr, a.H, a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits,
+                       p.kps, n_wg, n_waves, a.c);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, false>), dim3(n_wg), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.seqlens, nullptr,
+                     nullptr, part_o, part_l, a.H, a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits, p.kps, n_wg, n_waves,
+                     a.c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows = a.BH * a.Nq;
+  hipLaunchKernelGGL((kv_merge_kernel<TR, D>), dim3((rows + 3) / 4), dim3(256), 0, a.stream, part_o, part_l,
+                     (uint16_t*)a.o, a.lse, rows, p.n_splits);
+  return hipGetLastError();
+}
+
+template <class TR>
+static hipError_t dispatch_kv(const KvArgs& a, const KvPlan& p) {
+  if (a.d == 128) return a.causal ? launch_kv<TR, 128, true>(a, p) : launch_kv<TR, 128, false>(a, p);
+  return a.causal ? launch_kv<TR, 64, true>(a, p) : launch_kv<TR, 64, false>(a, p);
+}
+
+hipError_t launch_fwd_kvcache(const KvArgs& a) {
+  const KvPlan p = kv_plan(a.BH, a.Nq, a.Nk);
+  return a.dtype == DT_BF16 ? dispatch_kv<BF16>(a, p) : dispatch_kv<F16>(a, p);
+}
+
+}  // namespace fa

@@ -52,6 +52,58 @@ struct BwdArgs {
 
 enum BwdStage { BWD_PREP = 0, BWD_DKDV = 1, BWD_DQ = 2 };
 
+// Queries against a key/value cache (fa_fwd_kvcache).
+struct KvArgs {
+  const void* q;           // [BH, Nq, d]
+  const void* k;           // [BH, Nk, d] cache (capacity Nk rows)
+  const void* v;
+  const int32_t* seqlens;  // [B] filled rows per batch entry, or NULL (= Nk)
+  void* o;                 // [BH, Nq, d]
+  float* lse;              // [BH, Nq]
+  void* workspace;         // kv_workspace_bytes() bytes (NULL when that is 0)
+  int H;
+  int BH;
+  int Nq;
+  int Nk;
+  int d;
+  float c;                 // scale * log2(e)
+  int causal;
+  int dtype;
+  hipStream_t stream;
+};
+
+// How the keys are split: every wavefront takes `kps` keys (a power of two,
+// >= 64) of one head for one block of 32 queries.  kps doubles from 64 until
+// the launch has at most 16384 wavefronts (64 per compute unit), so a decode
+// step over a long cache still spreads over the whole chip while each range
+// stays long enough to amortise its partial result.
+struct KvPlan {
+  int n_qb;      // 32-query blocks
+  int kps;       // keys per range
+  int n_splits;  // ranges per head
+};
+
+inline KvPlan kv_plan(int64_t BH, int64_t Nq, int64_t Nk) {
+  KvPlan p;
+  p.n_qb = (int)((Nq + 31) / 32);
+  int64_t kps = 64;
+  while (kps < Nk && BH * p.n_qb * ((Nk + kps - 1) / kps) > 16384) kps *= 2;
+  p.kps = (int)kps;
+  p.n_splits = (int)((Nk + kps - 1) / kps);
+  return p;
+}
+
+// Workspace of the split path: per range, per head and query, d floats of
+// partial O then 2 floats of base-2 log-sum-exps.  0 when one range covers
+// the cache (the kernel then writes O and LSE directly).
+inline size_t kv_workspace_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t d) {
+  const KvPlan p = kv_plan(BH, Nq, Nk);
+  if (p.n_splits == 1) return 0;
+  return (size_t)p.n_splits * (size_t)BH * (size_t)Nq * (size_t)(d + 2) * sizeof(float);
+}
+
+hipError_t launch_fwd_kvcache(const KvArgs& a);
+
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);                 // all three stages in order
 hipError_t launch_bwd_stage(const BwdArgs& a, int stage);  // one stage

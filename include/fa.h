@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
   FA_OK = 0,
@@ -124,6 +124,46 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
               const void* workspace, size_t workspace_bytes, void* dq,
               int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
               int dtype, void* stream);
+
+/* New queries against a key/value cache (inference: decoding one or a few
+ * tokens, or a chunk of a prompt, against the keys and values kept from the
+ * earlier positions).  The pages place the method in inference and serving
+ * next to the block-wise management of that cache ("FlashAttention-2 (DE)",
+ * lead paragraph; "FlashAttention" glossary, "Der Engpass ist der Weg zum
+ * Speicher, nicht das Rechnen", "Wo es verwechselt wird").  The arithmetic is
+ * the same exact attention as fa_fwd with fewer queries than keys:
+ *
+ *   query i (0 <= i < Nq) of batch entry b sees cache row j iff
+ *     j < L_b                               (causal == 0)
+ *     j < L_b and j <= i + (L_b - Nq)       (causal != 0: bottom-right aligned,
+ *                                            the queries are the last Nq
+ *                                            positions of a length-L_b sequence)
+ *   with L_b = seqlens_k[b] clamped to [0, Nk], or Nk when seqlens_k is NULL.
+ *
+ *   q          [B,H,Nq,d] queries, dtype FA_F16 or FA_BF16.
+ *   k_cache,   [B,H,Nk,d] caches of capacity Nk rows, same dtype; rows at and
+ *   v_cache    past L_b are never read (their contents do not matter).
+ *   seqlens_k  DEVICE int32 [B] filled lengths (4-byte aligned), or NULL.
+ *   o          [B,H,Nq,d] output, same dtype.  Fully overwritten.
+ *   lse        [B,H,Nq] float32 output, natural-log log-sum-exp over the
+ *              visible keys.  A query that sees no key (L_b = 0, or causal
+ *              with i < Nq - L_b) gets o = 0 and lse = -infinity.
+ *   workspace  device scratch of fa_fwd_kvcache_workspace_bytes() bytes
+ *              (16-byte aligned), owned by the caller, contents need not be
+ *              initialised; may be NULL when that size is 0.  It holds the
+ *              partial results of the key ranges the cache is split into.
+ *   scale, causal, dtype, stream: as for fa_fwd.  Nq, Nk in [1, 2^22].
+ * Errors: FA_ERR_NULL (q, k_cache, v_cache, o or lse NULL), FA_ERR_SHAPE,
+ * FA_ERR_HEADDIM, FA_ERR_DTYPE (FA_F32 is not taken), FA_ERR_ALIGN,
+ * FA_ERR_SCALE, FA_ERR_WORKSPACE (NULL or too small when the size is > 0).
+ * Results are bitwise repeatable. */
+size_t fa_fwd_kvcache_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                      int dtype);
+
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k,
+                   void* o, float* lse, void* workspace, size_t workspace_bytes,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                   int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -120,3 +120,55 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str, sigma: float, seed: 
 def make_workload_inputs(w: Workload, backward: bool | None = None):
     return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.sigma, w.seed,
                        w.backward if backward is None else backward)
+
+
+# queries against a key/value cache: a decode step of one new token per
+# sequence over a 32768-row cache (bf16, causal), filled lengths drawn per
+# batch entry between half and all of the capacity
+@dataclass(frozen=True)
+class KvWorkload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool
+    sigma: float
+    seed: int
+    min_fill: float = 0.5  # filled lengths drawn uniformly in [min_fill * Nk, Nk]
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+
+KV_WORKLOADS = {
+    "D1": KvWorkload("D1", 4, 32, 1, 32768, 128, "bf16", True, 1.0, 1006),
+    "D1d64": KvWorkload("D1d64", 4, 32, 1, 32768, 64, "bf16", True, 1.0, 1006),
+}
+
+
+def make_kvcache_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, sigma: float, seed: int,
+                        min_fill: float = 0.5):
+    """Draw queries, a key/value cache and filled lengths.
+
+    Q [B,H,Nq,d], then K and V [B,H,Nk,d], each float32 standard normal times
+    sigma rounded to ``dtype`` (as in make_inputs), then the filled lengths
+    seqlens [B] (int32) uniform in [ceil(min_fill * Nk), Nk].
+    Returns a dict name -> (float32 values, storage array), plus "seqlens"."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for nm, n in (("q", Nq), ("k", Nk), ("v", Nk)):
+        x = rng.standard_normal((B, H, n, d), dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        out[nm] = round_to(x, dtype)
+    lo = int(np.ceil(min_fill * Nk))
+    out["seqlens"] = rng.integers(lo, Nk + 1, size=B).astype(np.int32)
+    return out
+
+
+def make_kv_workload_inputs(w: KvWorkload):
+    return make_kvcache_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.sigma, w.seed, w.min_fill)

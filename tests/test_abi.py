@@ -34,13 +34,14 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
-         "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq"])
+         "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kvcache_workspace_bytes",
+         "fa_fwd_kvcache"])
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -131,3 +132,46 @@ def test_binding_rejects_host_tensors_and_bad_shapes(lib):
         fa.fwd(q, q, q)
     with pytest.raises(TypeError):
         fa.dtype_code(torch.zeros(1, dtype=torch.int32))
+
+
+def kv(lib, q=P[0], k=P[1], v=P[2], lens=None, o=P[3], lse=P[4], ws=P[10], wsb=1 << 30, B=2, H=4,
+       Nq=1, Nk=4096, d=128, scale=0.088, causal=1, dtype=2):
+    return lib.fa_fwd_kvcache(q, k, v, lens, o, lse, ws, wsb, B, H, Nq, Nk, d, scale, causal, dtype, None)
+
+
+def test_kvcache_argument_errors(lib):
+    for name in ("q", "k", "v", "o", "lse"):
+        assert kv(lib, **{name: None}) == FA_ERR_NULL, name
+    assert kv(lib, Nq=0) == FA_ERR_SHAPE
+    assert kv(lib, Nk=0) == FA_ERR_SHAPE
+    assert kv(lib, B=0) == FA_ERR_SHAPE
+    assert kv(lib, Nk=(1 << 22) + 1) == FA_ERR_SHAPE
+    assert kv(lib, Nq=(1 << 22) + 1) == FA_ERR_SHAPE
+    assert kv(lib, d=96) == FA_ERR_HEADDIM
+    assert kv(lib, dtype=0) == FA_ERR_DTYPE
+    assert kv(lib, dtype=7) == FA_ERR_DTYPE
+    assert kv(lib, q=P[0] + 8) == FA_ERR_ALIGN
+    assert kv(lib, lens=P[9] + 2) == FA_ERR_ALIGN
+    assert kv(lib, scale=-1.0) == FA_ERR_SCALE
+    assert kv(lib, scale=math.nan) == FA_ERR_SCALE
+    assert kv(lib, ws=None) == FA_ERR_WORKSPACE
+    need = lib.fa_fwd_kvcache_workspace_bytes(2, 4, 1, 4096, 128, 2)
+    assert need > 0
+    assert kv(lib, wsb=need - 1) == FA_ERR_WORKSPACE
+    assert kv(lib, ws=P[10] + 4) == FA_ERR_ALIGN
+
+
+def test_kvcache_workspace_bytes(lib):
+    ws = lib.fa_fwd_kvcache_workspace_bytes
+    # a single decode query over a 4096-row cache at B*H = 8 is split into 64 ranges of 64 keys:
+    # per range, head and query 128 floats of partial O and 2 log-sum-exps
+    assert ws(2, 4, 1, 4096, 128, 2) == 64 * 8 * 1 * 130 * 4
+    # B*H = 256 over 32768 keys: ranges double until at most 16384 wavefronts (512 keys, 64 ranges)
+    assert ws(8, 32, 1, 32768, 128, 1) == 64 * 256 * 130 * 4
+    # one range covers the cache: no workspace (O and LSE are written directly)
+    # a 4096-query chunk of one head: 128 query blocks x 64 ranges of 64 keys = 8192 wavefronts
+    assert ws(1, 1, 4096, 4096, 64, 2) == 64 * 4096 * 66 * 4
+    assert ws(64, 64, 2048, 2048, 128, 2) == 0
+    assert ws(2, 4, 1, 4096, 128, 0) == 0  # fp32 is not taken
+    assert ws(0, 4, 1, 4096, 128, 2) == 0
+    assert ws(2, 4, 1, 4096, 96, 2) == 0

@@ -1,0 +1,139 @@
+"""Parity on the GPU for queries against a key/value cache: the library's
+fa_fwd_kvcache against the float64 oracle (oracle/kvcache.py) on the same
+seeded inputs.
+
+Small shapes are compared element by element on every output; they cover one
+and several 32-query blocks with ragged ends, caches split into many key
+ranges (merge kernel) and caches one range covers (direct path), filled
+lengths below the query count (empty causal rows), empty caches and caches
+whose unfilled rows hold NaN.  The decode workload (B=4 H=32, one query, a
+32768-row cache) runs at full size in the launch configuration the benchmark
+times and is compared on sampled heads.  Tolerances are those of the
+forward: O max-abs <= 1e-2 and mean-abs <= 1e-3, LSE max-abs <= 1e-3.
+"""
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from oracle import kvcache_fwd, kvcache_fwd_head
+from parity import TOL, lib, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, dtype, causal, scale, seqlens=True, k_override=None, v_override=None):
+    import torch
+    fa = lib()
+    q = to_device(inp["q"][1], dtype)
+    k = to_device(inp["k"][1] if k_override is None else k_override, dtype)
+    v = to_device(inp["v"][1] if v_override is None else v_override, dtype)
+    lens = torch.from_numpy(inp["seqlens"]).cuda() if seqlens else None
+    o, lse = fa.fwd_kvcache(q, k, v, lens, causal, scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _check(o, lse, o_ref, lse_ref, dtype, label):
+    tol = TOL[dtype]
+    inf_ref = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), inf_ref), f"{label}: empty rows differ"
+    assert np.all(o[inf_ref] == 0), f"{label}: empty rows must be 0"
+    fin = ~inf_ref
+    do = np.abs(o.astype(np.float64) - o_ref)
+    dl = np.abs(lse[fin].astype(np.float64) - lse_ref[fin])
+    o_max, o_mean = float(do.max(initial=0.0)), float(do.mean()) if do.size else 0.0
+    l_max = float(dl.max(initial=0.0))
+    say(f"  {label}: O max {o_max:.3e} mean {o_mean:.3e}  LSE max {l_max:.3e}  empty rows {int(inf_ref.sum())}")
+    assert np.isfinite(o).all() and np.isfinite(lse[fin]).all(), label
+    assert o_max <= tol["o_max"] and o_mean <= tol["o_mean"] and l_max <= tol["lse_max"], label
+
+
+SMALL = [  # B, H, Nq, Nk, min_fill
+    (2, 3, 1, 40, 0.5),      # one range covers the cache: direct path
+    (2, 3, 1, 1000, 0.3),    # 16 ranges of 64 keys, merged
+    (3, 2, 5, 777, 0.0),     # several queries, lengths down to 0 (empty rows)
+    (2, 2, 32, 300, 0.05),   # one full query block, lengths below the query count
+    (2, 2, 33, 513, 0.5),    # two query blocks, ragged
+    (1, 3, 70, 70, 1.0),     # square, several query blocks
+    (2, 1, 100, 4097, 0.9),  # long-ish cache, ragged tiles
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Nq,Nk,fill", SMALL)
+def test_small_shapes(B, H, Nq, Nk, fill, causal, d, dtype):
+    seed = 7000 + Nq * 13 + Nk
+    inp = si.make_kvcache_inputs(B, H, Nq, Nk, d, dtype, 1.0, seed, fill)
+    scale = 1.0 / np.sqrt(d)
+    say(f"kvcache B{B} H{H} Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal} seed={seed} lens={inp['seqlens'].tolist()}")
+    o, lse = _run(inp, dtype, causal, scale)
+    o_ref, lse_ref = kvcache_fwd(inp["q"][0], inp["k"][0], inp["v"][0], scale, causal, inp["seqlens"])
+    _check(o, lse, o_ref, lse_ref, dtype, f"Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_without_lengths_square_equals_the_ordinary_forward(d):
+    """seqlens NULL and Nq = Nk: the same outputs as fa_fwd's causal attention
+    (both within tolerance of the oracle; they run different kernels)."""
+    import torch
+    fa = lib()
+    inp = si.make_kvcache_inputs(1, 2, 300, 300, d, "bf16", 1.0, 77)
+    say(f"kvcache square vs fa_fwd d{d}")
+    o, lse = _run(inp, "bf16", True, 1 / np.sqrt(d), seqlens=False)
+    q, k, v = (to_device(inp[n][1], "bf16") for n in ("q", "k", "v"))
+    o2, lse2 = fa.fwd(q, k, v, True, 1 / np.sqrt(d))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = kvcache_fwd(inp["q"][0], inp["k"][0], inp["v"][0], 1 / np.sqrt(d), True)
+    _check(o, lse, o_ref, lse_ref, "bf16", "kvcache")
+    _check(o2.float().cpu().numpy(), lse2.cpu().numpy(), o_ref, lse_ref, "bf16", "fa_fwd")
+
+
+def test_unfilled_rows_are_never_read():
+    """NaN in every cache row at and past the filled length changes nothing."""
+    inp = si.make_kvcache_inputs(3, 2, 4, 600, 128, "bf16", 1.0, 78, 0.2)
+    lens = inp["seqlens"]
+    say(f"kvcache NaN past the filled lengths {lens.tolist()}")
+    k, v = inp["k"][1].copy(), inp["v"][1].copy()
+    for b, L in enumerate(lens):
+        k[b, :, L:] = 0x7FC0  # bf16 NaN
+        v[b, :, L:] = 0x7FC0
+    for causal in (False, True):
+        a = _run(inp, "bf16", causal, 0.09)
+        b = _run(inp, "bf16", causal, 0.09, k_override=k, v_override=v)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_deterministic_bitwise():
+    inp = si.make_kvcache_inputs(2, 4, 3, 5000, 128, "f16", 1.0, 79)
+    a = _run(inp, "f16", True, 0.09)
+    b = _run(inp, "f16", True, 0.09)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_large_scores_stay_finite():
+    """Queries scaled x30: the running maximum is raised across tiles and
+    ranges without overflow."""
+    inp = si.make_kvcache_inputs(1, 2, 8, 3000, 64, "bf16", 1.0, 80)
+    inp["q"] = si.round_to(inp["q"][0] * 30.0, "bf16")
+    o, lse = _run(inp, "bf16", True, 0.125)
+    o_ref, lse_ref = kvcache_fwd(inp["q"][0], inp["k"][0], inp["v"][0], 0.125, True, inp["seqlens"])
+    _check(o, lse, o_ref, lse_ref, "bf16", "x30 queries")
+
+
+@pytest.mark.parametrize("name", ["D1", "D1d64"])
+def test_decode_workload_full_size_sampled_heads(name):
+    """The benchmarked decode step at full size, launch configuration as timed."""
+    w = si.KV_WORKLOADS[name]
+    say(f"{name} full size on GPU: {w}")
+    inp = si.make_kv_workload_inputs(w)
+    o, lse = _run(inp, w.dtype, w.causal, w.scale)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    errs = []
+    for (b, h) in [(0, 0), (1, 17), (2, 5), (3, 31)]:
+        L = int(inp["seqlens"][b])
+        o_ref, l_ref = kvcache_fwd_head(inp["q"][0][b, h], inp["k"][0][b, h], inp["v"][0][b, h], w.scale,
+                                        w.causal, L)
+        _check(o[b, h], lse[b, h], o_ref, l_ref, w.dtype, f"{name} head ({b},{h}) L={L}")
