@@ -14,6 +14,8 @@ the same workload.
 
 Modes
   (default)             the benchmark above
+  --workload D1         a decode step against a key/value cache instead (fa_fwd_kvcache,
+                        B=4 H=32, one query, 32768-row cache, d=128): HBM GB/s
   --profile             3 warm-up + 20 timed steps, no CPU baseline, for rocprofv3 runs;
                         also runs a plain 1 GiB device copy (the calibration
                         kernel for FETCH_SIZE / WRITE_SIZE counters)
@@ -39,6 +41,7 @@ PEAK_HBM = 8000.0  # GB/s
 COPY_BYTES = 1 << 30  # calibration copy: reads and writes 1 GiB
 
 KERNEL_SOURCES = {
+    "kv": ["fa_kvcache.hip", "fa_common.hpp"],
     "fwd": ["fa_fwd.hip", "fa_common.hpp"],
     "prep": ["fa_bwd.hip", "fa_common.hpp"],
     "dkdv": ["fa_bwd.hip", "fa_common.hpp"],
@@ -46,7 +49,7 @@ KERNEL_SOURCES = {
 }
 # substrings of the mangled kernel names, as rocprofv3 reports them
 KERNEL_SYMBOLS = {"fwd": "fwd16_p", "prep": "bwd_pre_kernel", "dkdv": "bwd_dkdv",
-                  "dq": "bwd_dq"}
+                  "dq": "bwd_dq", "kv": "kv_split"}
 
 
 def src_hash(kernel: str) -> str:
@@ -118,6 +121,121 @@ def cpu_baseline(w, target_s: float):
                       f"+ backward, {t_total:.1f} s; BLAS threads {threads}, host cpus {os.cpu_count()}"}
 
 
+def kv_bytes(w, seqlens) -> float:
+    """Compulsory HBM bytes of one call of fa_fwd_kvcache: read Q and the filled
+    cache rows of K and V once, write O and LSE."""
+    s = {"bf16": 2, "f16": 2}[w.dtype]
+    qo = 2 * w.B * w.H * w.Nq * w.d * s + 4 * w.B * w.H * w.Nq
+    kv = 2 * w.H * w.d * s * float(sum(int(x) for x in seqlens))
+    return qo + kv
+
+
+def cpu_baseline_kv(w, inp, target_s: float):
+    """The float64 oracle, as it stands, on whole heads of the same decode step."""
+    from oracle import kvcache_fwd_head
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    heads, t_total, nbytes = 0, 0.0, 0.0
+    s = 2
+    while t_total < target_s and heads < w.B * w.H:
+        b, h = heads % w.B, heads // w.B
+        L = int(inp["seqlens"][b])
+        t0 = time.perf_counter()
+        kvcache_fwd_head(inp["q"][0][b, h], inp["k"][0][b, h], inp["v"][0][b, h], w.scale, w.causal, L)
+        t_total += time.perf_counter() - t0
+        nbytes += 2 * L * w.d * s + 2 * w.Nq * w.d * s + 4 * w.Nq
+        heads += 1
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads (Nq={w.Nq}, filled lengths of the workload, d={w.d}), "
+                      f"float64 numpy, {t_total:.1f} s; BLAS threads {threads}, host cpus {os.cpu_count()}"}
+
+
+def bench_kvcache(args, w):
+    """Decode step against a key/value cache: one fa_fwd_kvcache call (the
+    split-key kernel and the merge kernel) per step, HBM-bound."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_fa2_amd as fa
+    import seeded_inputs as si
+
+    dev = torch.device("cuda:0")
+    inp = si.make_kv_workload_inputs(w)
+
+    def up(name):
+        a = inp[name][1]
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = up("q"), up("k"), up("v")
+    lens = torch.from_numpy(inp["seqlens"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    nb = fa.fa_fwd_kvcache_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, fa.dtype_code(q))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+
+    def step():
+        fa.fa_fwd_kvcache(q, k, v, lens, o, lse, ws, w.scale, w.causal)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for e0, e1 in evs:
+        e0.record()
+        step()
+        e1.record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_call = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = kv_bytes(w, inp["seqlens"])
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    achieved = nbytes / (ms_call * 1e-3) / 1e9
+    out = {
+        "metric": "attention decode against a KV cache, HBM GB/s (compulsory bytes), 1 GPU",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": f"synthetic: seeded N(0,{w.sigma:g}) Q, K, V (numpy PCG64 seed {w.seed}) rounded to {w.dtype}, "
+                f"filled lengths uniform in [{w.min_fill:g} Nk, Nk]",
+        "config": {"workload": f"{w.name}: decode B={w.B} H={w.H} Nq={w.Nq} cache Nk={w.Nk} d={w.d} "
+                               f"{w.dtype} {'causal' if w.causal else 'non-causal'}",
+                   "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "seqlens": [int(x) for x in inp["seqlens"]], "parallelism": "single GPU"},
+        "workspace_bytes": nb,
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "hbm", "kernel": "kv_split + kv_merge (one call)", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM, "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
+                     "traffic": load_traffic(w.name, "kv")},
+    }
+    if not args.no_cpu_baseline and not args.profile:
+        out["cpu_baseline"] = cpu_baseline_kv(w, inp, min(args.cpu_seconds, 10.0))
+    if args.profile:
+        a = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+    print(json.dumps(out), flush=True)
+
+
 def ingest_pmc(fetch_csv: str, write_csv: str, workload: str):
     """Counter summary -> profiles/traffic_<workload>.json.
 
@@ -148,8 +266,10 @@ def ingest_pmc(fetch_csv: str, write_csv: str, workload: str):
     copy_sym = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
     if not copy_sym:
         raise SystemExit("no copy kernel in the counter file; run bench.py --profile")
-    copy_f = max(sum(fetch[k]) / len(fetch[k]) for k in copy_sym) * 1024
-    copy_w = max(sum(write[k]) / len(write[k]) for k in write if k in copy_sym) * 1024
+    # the largest single copy dispatch is the calibration copy (other, small
+    # copies of the same kernel, such as uploads, would skew an average)
+    copy_f = max(max(fetch[k]) for k in copy_sym) * 1024
+    copy_w = max(max(write[k]) for k in write if k in copy_sym) * 1024
     f_fac, w_fac = COPY_BYTES / copy_f, COPY_BYTES / copy_w
     out = {"workload": workload, "copy_calibration": {"true_bytes": COPY_BYTES,
                                                       "fetch_counted": copy_f,
@@ -196,6 +316,9 @@ def main():
     import seeded_inputs as si
 
     fa.load_library()
+    if args.workload in si.KV_WORKLOADS:
+        bench_kvcache(args, si.KV_WORKLOADS[args.workload])
+        return
     w = si.WORKLOADS[args.workload]
     if w.dtype == "f32":
         raise SystemExit("the fwd+bwd step needs a 16-bit workload")

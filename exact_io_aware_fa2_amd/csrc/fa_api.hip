@@ -219,7 +219,7 @@ int check_kv_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
   if (B > INT32_MAX / H) return FA_ERR_SHAPE;
   const int64_t bh = B * H;
   if (bh * Nq > INT32_MAX) return FA_ERR_SHAPE;
-  const fa::KvPlan p = fa::kv_plan(bh, Nq, Nk);
+  const fa::KvPlan p = fa::kv_plan(bh, Nq, Nk, d);
   if ((bh * p.n_qb * p.n_splits + 3) / 4 > kMaxWorkgroups) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   return FA_OK;

@@ -74,20 +74,23 @@ struct KvArgs {
 
 // How the keys are split: every wavefront takes `kps` keys (a power of two,
 // >= 64) of one head for one block of 32 queries.  kps doubles from 64 until
-// the launch has at most 16384 wavefronts (64 per compute unit), so a decode
-// step over a long cache still spreads over the whole chip while each range
-// stays long enough to amortise its partial result.
+// the launch has at most 8192 wavefronts at d = 128 (16384 at d = 64), i.e.
+// 32 (64) per compute unit: a decode step over a long cache still spreads
+// over the whole chip, while each range moves at least ~128 KB of K and V
+// (measured on a B=4 H=32 32768-row decode step: 2x more, shorter ranges
+// cost 10-18% at d = 128, 2x fewer changed nothing at d = 64).
 struct KvPlan {
   int n_qb;      // 32-query blocks
   int kps;       // keys per range
   int n_splits;  // ranges per head
 };
 
-inline KvPlan kv_plan(int64_t BH, int64_t Nq, int64_t Nk) {
+inline KvPlan kv_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t d) {
   KvPlan p;
   p.n_qb = (int)((Nq + 31) / 32);
+  const int64_t max_waves = d == 128 ? 8192 : 16384;
   int64_t kps = 64;
-  while (kps < Nk && BH * p.n_qb * ((Nk + kps - 1) / kps) > 16384) kps *= 2;
+  while (kps < Nk && BH * p.n_qb * ((Nk + kps - 1) / kps) > max_waves) kps *= 2;
   p.kps = (int)kps;
   p.n_splits = (int)((Nk + kps - 1) / kps);
   return p;
@@ -97,7 +100,7 @@ inline KvPlan kv_plan(int64_t BH, int64_t Nq, int64_t Nk) {
 // partial O then 2 floats of base-2 log-sum-exps.  0 when one range covers
 // the cache (the kernel then writes O and LSE directly).
 inline size_t kv_workspace_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t d) {
-  const KvPlan p = kv_plan(BH, Nq, Nk);
+  const KvPlan p = kv_plan(BH, Nq, Nk, d);
   if (p.n_splits == 1) return 0;
   return (size_t)p.n_splits * (size_t)BH * (size_t)Nq * (size_t)(d + 2) * sizeof(float);
 }

@@ -166,8 +166,10 @@ def test_kvcache_workspace_bytes(lib):
     # a single decode query over a 4096-row cache at B*H = 8 is split into 64 ranges of 64 keys:
     # per range, head and query 128 floats of partial O and 2 log-sum-exps
     assert ws(2, 4, 1, 4096, 128, 2) == 64 * 8 * 1 * 130 * 4
-    # B*H = 256 over 32768 keys: ranges double until at most 16384 wavefronts (512 keys, 64 ranges)
-    assert ws(8, 32, 1, 32768, 128, 1) == 64 * 256 * 130 * 4
+    # B*H = 256 over 32768 keys: ranges double until at most 8192 wavefronts at d = 128
+    # (1024 keys, 32 ranges), 16384 at d = 64 (512 keys, 64 ranges)
+    assert ws(8, 32, 1, 32768, 128, 1) == 32 * 256 * 130 * 4
+    assert ws(8, 32, 1, 32768, 64, 1) == 64 * 256 * 66 * 4
     # one range covers the cache: no workspace (O and LSE are written directly)
     # a 4096-query chunk of one head: 128 query blocks x 64 ranges of 64 keys = 8192 wavefronts
     assert ws(1, 1, 4096, 4096, 64, 2) == 64 * 4096 * 66 * 4
