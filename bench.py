@@ -3,7 +3,9 @@
 
 One step = the whole hot path over one batch of synthetic input: fa_fwd, then
 the three backward stages (fa_bwd_prep, fa_bwd_dkdv, fa_bwd_dq), all through
-the C ABI on the current HIP stream.  The default workload is the
+the C ABI; dQ runs on a second stream beside dK/dV (they are independent),
+--serial keeps every stage on one stream.  Per-kernel durations (roofline)
+come from a separate pass with the stages in order, each between HIP events.  The default workload is the
 fwd+bwd configuration B=8 H=16 N=4096 d=64, bf16, causal, with Q, K, V, dO
 drawn as seeded N(0, 1) values (numpy PCG64, seed 1005) rounded to bf16.
 
@@ -298,6 +300,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--serial", action="store_true",
+                    help="time the step with all stages in order on one stream (dQ not beside dK/dV)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
 
@@ -359,22 +363,44 @@ def main():
         if evs is not None:
             evs[4].record()
 
+    # The two gradient stages after fa_bwd_prep are independent (both read the
+    # prepared D vector): dQ runs on a second stream (default priority) beside
+    # dK/dV, and the main stream joins it before the step ends.
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def step_overlapped():
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+        fa.fa_bwd_prep(o, do, ws)
+        side.wait_stream(main)
+        fa.fa_bwd_dkdv(q, k, v, do, lse, ws, dk, dv, w.scale, w.causal)
+        with torch.cuda.stream(side):
+            fa.fa_bwd_dq(q, k, v, do, lse, ws, dq, w.scale, w.causal)
+        main.wait_stream(side)
+
+    run = step if args.serial else step_overlapped
     for _ in range(args.warmup):
-        step()
+        run()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(args.steps):
-        step(evs[i])
+        run()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-
     ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    # per-kernel durations: the same steps with the stages in order on one
+    # stream, each between its own events (these times feed the roofline)
+    n_k = max(5, min(args.steps, 20))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_k)]
+    for i in range(n_k):
+        step(evs[i])
+    torch.cuda.synchronize()
     kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
     flop_step = w.fwd_flop() + w.bwd_flop()
     value = flop_step / (ms_step * 1e-3) / 1e12
@@ -415,6 +441,8 @@ def main():
         "bwd_tflops": round(w.bwd_flop() / ((kern_ms["prep"] + kern_ms["dkdv"] + kern_ms["dq"]) * 1e-3) / 1e12, 1),
         "kernels": per_kernel,
         "wall_s_timed": round(wall, 3),
+        "schedule": "stages in order on one stream" if args.serial else
+                    "fwd, prep, then dK/dV and dQ on two streams at once",
         "roofline": roof,
     }
     if not args.no_cpu_baseline and not args.profile:
