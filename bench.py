@@ -17,7 +17,8 @@ the same workload.
 Modes
   (default)             the benchmark above
   --workload D1         a decode step against a key/value cache instead (fa_fwd_kvcache,
-                        B=4 H=32, one query, 32768-row cache, d=128): HBM GB/s
+                        B=4 H=32, one query, 32768-row cache, d=128): HBM GB/s;
+                        D1f8: the same with an 8-bit E4M3 cache (fa_fwd_kvcache_fp8)
   --profile             3 warm-up + 20 timed steps, no CPU baseline, for rocprofv3 runs;
                         also runs a plain 1 GiB device copy (the calibration
                         kernel for FETCH_SIZE / WRITE_SIZE counters)
@@ -124,11 +125,12 @@ def cpu_baseline(w, target_s: float):
 
 
 def kv_bytes(w, seqlens) -> float:
-    """Compulsory HBM bytes of one call of fa_fwd_kvcache: read Q and the filled
-    cache rows of K and V once, write O and LSE."""
+    """Compulsory HBM bytes of one call of fa_fwd_kvcache(_fp8): read Q and the
+    filled cache rows of K and V once, write O and LSE."""
     s = {"bf16": 2, "f16": 2}[w.dtype]
+    sc = 1 if w.cache == "e4m3" else s
     qo = 2 * w.B * w.H * w.Nq * w.d * s + 4 * w.B * w.H * w.Nq
-    kv = 2 * w.H * w.d * s * float(sum(int(x) for x in seqlens))
+    kv = 2 * w.H * w.d * sc * float(sum(int(x) for x in seqlens))
     return qo + kv
 
 
@@ -142,14 +144,14 @@ def cpu_baseline_kv(w, inp, target_s: float):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     heads, t_total, nbytes = 0, 0.0, 0.0
-    s = 2
+    s = 1 if w.cache == "e4m3" else 2
     while t_total < target_s and heads < w.B * w.H:
         b, h = heads % w.B, heads // w.B
         L = int(inp["seqlens"][b])
         t0 = time.perf_counter()
         kvcache_fwd_head(inp["q"][0][b, h], inp["k"][0][b, h], inp["v"][0][b, h], w.scale, w.causal, L)
         t_total += time.perf_counter() - t0
-        nbytes += 2 * L * w.d * s + 2 * w.Nq * w.d * s + 4 * w.Nq
+        nbytes += 2 * L * w.d * s + 2 * w.Nq * w.d * 2 + 4 * w.Nq
         heads += 1
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} heads (Nq={w.Nq}, filled lengths of the workload, d={w.d}), "
@@ -174,7 +176,12 @@ def bench_kvcache(args, w):
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    q, k, v = up("q"), up("k"), up("v")
+    fp8 = w.cache == "e4m3"
+    q = up("q")
+    if fp8:
+        k, v = (torch.from_numpy(inp[n][1]).to(dev) for n in ("k", "v"))
+    else:
+        k, v = up("k"), up("v")
     lens = torch.from_numpy(inp["seqlens"]).to(dev)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
@@ -182,7 +189,11 @@ def bench_kvcache(args, w):
     ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
 
     def step():
-        fa.fa_fwd_kvcache(q, k, v, lens, o, lse, ws, w.scale, w.causal)
+        if fp8:
+            fa.fa_fwd_kvcache_fp8(q, k, v, float(inp["k_scale"]), float(inp["v_scale"]), lens, o, lse, ws,
+                                  w.scale, w.causal)
+        else:
+            fa.fa_fwd_kvcache(q, k, v, lens, o, lse, ws, w.scale, w.causal)
 
     for _ in range(args.warmup):
         step()
@@ -214,11 +225,13 @@ def bench_kvcache(args, w):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": f"synthetic: seeded N(0,{w.sigma:g}) Q, K, V (numpy PCG64 seed {w.seed}) rounded to {w.dtype}, "
-                f"filled lengths uniform in [{w.min_fill:g} Nk, Nk]",
+        "dtype": f"{w.dtype}+e4m3" if fp8 else w.dtype,
+        "data": f"synthetic: seeded N(0,{w.sigma:g}) Q, K, V (numpy PCG64 seed {w.seed}) rounded to {w.dtype}"
+                + (", K and V quantised to E4M3 with power-of-two per-tensor scales" if fp8 else "")
+                + f", filled lengths uniform in [{w.min_fill:g} Nk, Nk]",
         "config": {"workload": f"{w.name}: decode B={w.B} H={w.H} Nq={w.Nq} cache Nk={w.Nk} d={w.d} "
-                               f"{w.dtype} {'causal' if w.causal else 'non-causal'}",
+                               f"{w.dtype}{' queries, E4M3 cache' if fp8 else ''} "
+                               f"{'causal' if w.causal else 'non-causal'}",
                    "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "seqlens": [int(x) for x in inp["seqlens"]], "parallelism": "single GPU"},
         "workspace_bytes": nb,

@@ -13,10 +13,12 @@ place of pointers):
     fa_bwd_prep(o, dout, workspace); fa_bwd_dkdv(...); fa_bwd_dq(...)  (fa_bwd's stages)
     fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, workspace, scale, causal)
     fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, dtype)
+    fa_fwd_kvcache_fp8(q, k_cache, v_cache, k_scale, v_scale, seqlens_k, o, lse, workspace, scale, causal)
 Conveniences that allocate their outputs with torch:
     fwd(q, k, v, causal=False, scale=None) -> (o, lse)
     bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
     fwd_kvcache(q, k_cache, v_cache, seqlens_k=None, causal=True, scale=None) -> (o, lse)
+    fwd_kvcache_fp8(q, k8, v8, k_scale, v_scale, seqlens_k=None, causal=True, scale=None) -> (o, lse)
     FlashAttention (torch.autograd.Function) and attention(q, k, v, causal, scale)
 """
 
@@ -74,6 +76,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fa_fwd_kvcache_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
     L.fa_fwd_kvcache.restype = i32
     L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+    L.fa_fwd_kvcache_fp8.restype = i32
+    L.fa_fwd_kvcache_fp8.argtypes = [vp, vp, vp, f32, f32, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, f32, i32,
+                                     i32, vp]
     _lib = L
     return L
 
@@ -219,6 +224,47 @@ def fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, workspace, scale: flo
                             dtype_code(q), _stream(q)))
 
 
+def fa_fwd_kvcache_fp8(q, k_cache, v_cache, k_scale: float, v_scale: float, seqlens_k, o, lse, workspace,
+                       scale: float, causal: bool) -> None:
+    """As fa_fwd_kvcache with an 8-bit cache: k_cache, v_cache are uint8 [B, H, Nk, d]
+    tensors of OCP E4M3 codes, dequantised as k_scale * code and v_scale * code."""
+    L = load_library()
+    torch = _torch()
+    _check_tensors(q, k_cache, v_cache, seqlens_k, o, lse, workspace)
+    B, H, Nq, d = _bhnd(q)
+    Nk = int(k_cache.shape[2]) if k_cache.dim() == 4 else -1
+    if tuple(k_cache.shape) != (B, H, Nk, d) or tuple(v_cache.shape) != (B, H, Nk, d):
+        raise ValueError("k_cache and v_cache must be [B, H, Nk, d] with q's B, H and d")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("an 8-bit cache holds uint8 E4M3 codes")
+    if o.dtype != q.dtype or tuple(o.shape) != (B, H, Nq, d):
+        raise ValueError("o must be [B, H, Nq, d] of q's dtype")
+    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, Nq]")
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or tuple(seqlens_k.shape) != (B,)):
+        raise ValueError("seqlens_k must be int32 [B]")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(L.fa_fwd_kvcache_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale),
+                                _ptr(seqlens_k), _ptr(o), _ptr(lse), _ptr(workspace), nbytes, B, H, Nq, Nk, d,
+                                float(scale), int(bool(causal)), dtype_code(q), _stream(q)))
+
+
+def fwd_kvcache_fp8(q, k_cache, v_cache, k_scale: float, v_scale: float, seqlens_k=None, causal: bool = True,
+                    scale: float | None = None, workspace=None):
+    """Allocate O, LSE (and the workspace unless given) and run the queries
+    against an 8-bit cache. Returns (o, lse)."""
+    torch = _torch()
+    B, H, Nq, d = _bhnd(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nb = fa_fwd_kvcache_workspace_bytes(B, H, Nq, int(k_cache.shape[2]), d, dtype_code(q))
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb > 0 else None
+    fa_fwd_kvcache_fp8(q, k_cache, v_cache, k_scale, v_scale, seqlens_k, o, lse, workspace,
+                       default_scale(d) if scale is None else scale, causal)
+    return o, lse
+
+
 def fwd_kvcache(q, k_cache, v_cache, seqlens_k=None, causal: bool = True, scale: float | None = None,
                 workspace=None):
     """Allocate O, LSE (and the workspace unless given) and run the queries
@@ -293,7 +339,7 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None):
 
 __all__ = [
     "load_library", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_prep", "fa_bwd_dkdv",
-    "fa_bwd_dq", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fwd", "bwd", "fwd_kvcache",
-    "attention",
+    "fa_bwd_dq", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache_fp8", "fwd", "bwd",
+    "fwd_kvcache", "fwd_kvcache_fp8", "attention",
     "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH",
 ]

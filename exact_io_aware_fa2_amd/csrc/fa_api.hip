@@ -267,6 +267,50 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, cons
   a.Nk = (int)Nk;
   a.d = (int)d;
   a.c = exp2_factor(scale);
+  a.v_scale = 1.0f;
+  a.fp8_cache = 0;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.stream = (hipStream_t)stream;
+  return status_of(fa::launch_fwd_kvcache(a));
+}
+
+int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                       float v_scale, const int32_t* seqlens_k, void* o, float* lse, void* workspace,
+                       size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                       float scale, int causal, int dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !lse) return FA_ERR_NULL;
+  int st = check_kv_shape(B, H, Nq, Nk, d);
+  if (st != FA_OK) return st;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0) return FA_ERR_ALIGN;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  if (!isfinite(k_scale) || !isfinite(v_scale) || !(k_scale > 0.0f) || !(v_scale > 0.0f)) return FA_ERR_SCALE;
+  const size_t need = fa::kv_workspace_bytes(B * H, Nq, Nk, d);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  }
+  fa::KvArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seqlens = seqlens_k;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = need > 0 ? workspace : nullptr;
+  a.H = (int)H;
+  a.BH = (int)(B * H);
+  a.Nq = (int)Nq;
+  a.Nk = (int)Nk;
+  a.d = (int)d;
+  // scores are q . (k_scale * code): the K scale joins the exponent factor
+  a.c = exp2_factor(scale * k_scale);
+  a.v_scale = v_scale;
+  a.fp8_cache = 1;
   a.causal = causal != 0;
   a.dtype = dtype;
   a.stream = (hipStream_t)stream;

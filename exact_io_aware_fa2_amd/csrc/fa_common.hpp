@@ -92,6 +92,12 @@ struct BF16 {
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
     return d;
   }
+  // Two OCP E4M3 codes (bytes 0, 1 of x, or 2, 3 with hi) -> packed pair,
+  // exact (v_cvt_scalef32_pk_bf16_fp8 with scale 1).
+  __device__ static inline uint32_t from_e4m3(uint32_t x, bool hi) {
+    return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+  }
 };
 
 struct F16 {
@@ -143,6 +149,11 @@ struct F16 {
     f32x16_t d;
     asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
     return d;
+  }
+  // Two OCP E4M3 codes -> packed fp16 pair, exact (v_cvt_scalef32_pk_f16_fp8, scale 1).
+  __device__ static inline uint32_t from_e4m3(uint32_t x, bool hi) {
+    return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
   }
 };
 

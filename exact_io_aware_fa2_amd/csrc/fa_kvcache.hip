@@ -44,21 +44,29 @@ namespace fa {
 // LDS reads returns for the V^T operand.
 __device__ inline int kv_tile_key(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <class TR, int D, bool CAUSAL, bool DIRECT>
+// F8: the cache holds OCP E4M3 codes (one byte per element) with per-tensor
+// scales; K's scale is folded into c by the launcher, V's multiplies the
+// output (v_scale, 1 for a 16-bit cache).  The codes are converted to the
+// query's 16-bit type (exactly: every E4M3 value is a bf16 and an fp16 value)
+// as they are written to LDS, so the products and everything after them are
+// those of the 16-bit cache.
+template <class TR, int D, bool CAUSAL, bool DIRECT, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kv_split_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ Q, const void* __restrict__ K, const void* __restrict__ V,
     const int32_t* __restrict__ seqlens, uint16_t* __restrict__ O, float* __restrict__ LSE,
     float* __restrict__ part_o, float* __restrict__ part_l, int H, int BH, int Nq, int Nk, int n_qb,
-    int n_splits, int kps, uint32_t n_waves, float c) {
+    int n_splits, int kps, uint32_t n_waves, float c, float v_scale) {
   constexpr int NKS = D / 16;          // k-steps of S^T = K Q^T
   constexpr int NDB = D / 32;          // 32-row blocks of O^T
-  constexpr uint32_t RB = 2 * D;       // global row bytes
+  constexpr uint32_t RB = 2 * D;       // global row bytes of Q
+  constexpr uint32_t RBC = F8 ? D : 2 * D;  // global row bytes of the cache
   constexpr int RS = 2 * D + 64;       // LDS row bytes of the V tile: a stride of 16 (mod 64)
                                        // dwords puts the 4 rows of a transposed read in 4 bank groups
   constexpr int RSK = 2 * D + 16;      // LDS row bytes of the K tile: a stride of 4 (mod 64) dwords
                                        // puts the 16 rows of a row-wise operand read in 16 bank groups
-  constexpr int VCH = D / 8;           // 16-byte chunks per V row
-  constexpr int NVL = 32 * VCH / 64;   // V chunks per lane per tile
+  constexpr int VCH = (int)RBC / 16;   // 16-byte chunks per cache row
+  constexpr int NVL = 32 * VCH / 64;   // chunks per lane per tile and tensor
+  constexpr int EPC = F8 ? 16 : 8;     // elements per chunk
   static_assert(32 * RS >= kTileRowsBytes<D>, "the output tile fits the V rows");
   __shared__ __attribute__((aligned(16))) char smem[4 * 32 * (RS + RSK)];
 
@@ -96,8 +104,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(qres, off + 32 * ks);
   }
   // the cache of this head up to the filled length: rows at and past L read as zeros
-  const rsrc_t kres = make_rsrc(K + (size_t)bh * Nk * D, (uint32_t)L * RB);
-  const rsrc_t vres = make_rsrc(V + (size_t)bh * Nk * D, (uint32_t)L * RB);
+  const size_t cache_head = (size_t)bh * Nk * RBC;  // bytes
+  const rsrc_t kres = make_rsrc((const char*)K + cache_head, (uint32_t)L * RBC);
+  const rsrc_t vres = make_rsrc((const char*)V + cache_head, (uint32_t)L * RBC);
   const int k_row = kv_tile_key(l32) * RSK + 16 * h;  // A operand of K: row read from LDS
   // transposed-read address of this lane: group G = lane / 16 reads columns
   // 16 (G % 2) + 0..15 of rows 8 h + 0..3 (and + 4), lane 4 e + i of the group
@@ -124,14 +133,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int ch = 64 * i + lane;
-      kc[i] = buf_load16(kres, (uint32_t)k0 * RB + (uint32_t)(ch / VCH) * RB + 16 * (ch % VCH));
+      kc[i] = buf_load16(kres, (uint32_t)k0 * RBC + (uint32_t)(ch / VCH) * RBC + 16 * (ch % VCH));
     }
   };
   auto load_v = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int ch = 64 * i + lane;
-      vv[i] = buf_load16(vres, (uint32_t)k0 * RB + (uint32_t)(ch / VCH) * RB + 16 * (ch % VCH));
+      vv[i] = buf_load16(vres, (uint32_t)k0 * RBC + (uint32_t)(ch / VCH) * RBC + 16 * (ch % VCH));
+    }
+  };
+  // chunk x (16 bytes of a cache row) -> its row's LDS position: as is, or
+  // as 16 E4M3 codes converted to 32 bytes of the 16-bit type
+  auto put = [&](char* dst, u32x4_t x) __attribute__((always_inline)) {
+    if constexpr (F8) {
+      u32x4_t a, b;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        a[2 * j] = TR::from_e4m3(x[j], false);
+        a[2 * j + 1] = TR::from_e4m3(x[j], true);
+        b[2 * j] = TR::from_e4m3(x[2 + j], false);
+        b[2 * j + 1] = TR::from_e4m3(x[2 + j], true);
+      }
+      *(u32x4_t*)dst = a;
+      *(u32x4_t*)(dst + 16) = b;
+    } else {
+      *(u32x4_t*)dst = x;
     }
   };
   if (kb < ke) {
@@ -148,7 +175,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int ch = 64 * i + lane;
-      *(u32x4_t*)(ldk + (ch / VCH) * RSK + 16 * (ch % VCH)) = kc[i];
+      put(ldk + (ch / VCH) * RSK + 2 * EPC * (ch % VCH), kc[i]);
     }
     load_k(kn);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
@@ -201,7 +228,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int ch = 64 * i + lane;
-      *(u32x4_t*)(lds + (ch / VCH) * RS + 16 * (ch % VCH)) = vv[i];
+      put(lds + (ch / VCH) * RS + 2 * EPC * (ch % VCH), vv[i]);
     }
     load_v(kn);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
@@ -219,7 +246,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   l += swap_halves(l);
   lt += swap_halves(lt);
   const bool empty = m == -INFINITY;  // no visible key for this query in this range
-  const float inv = empty ? 0.0f : 1.0f / lt;
+  const float inv = empty ? 0.0f : v_scale / lt;
 
   if constexpr (DIRECT) {
     u32x2_t ov[NDB][4];
@@ -333,23 +360,23 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------ launch
 
-template <class TR, int D, bool CAUSAL>
+template <class TR, int D, bool CAUSAL, bool F8>
 static hipError_t launch_kv(const KvArgs& a, const KvPlan& p) {
   const uint32_t n_waves = (uint32_t)((int64_t)a.BH * p.n_qb * p.n_splits);
   const uint32_t n_wg = (n_waves + 3) / 4;
   float* part_o = (float*)a.workspace;
   float* part_l = part_o ? part_o + (size_t)p.n_splits * a.BH * a.Nq * D : nullptr;
   if (p.n_splits == 1) {
-    hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, true>), dim3(n_wg), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.seqlens,
+    hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, true, F8>), dim3(n_wg), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, a.k, a.v, a.seqlens,
                        (uint16_t*)a.o, a.lse, nullptr, nullptr, a.H, a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits,
-                       p.kps, n_waves, a.c);
+                       p.kps, n_waves, a.c, a.v_scale);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, false>), dim3(n_wg), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.seqlens, nullptr,
+  hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, false, F8>), dim3(n_wg), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, a.k, a.v, a.seqlens, nullptr,
                      nullptr, part_o, part_l, a.H, a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits, p.kps, n_waves,
-                     a.c);
+                     a.c, a.v_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = a.BH * a.Nq;
@@ -358,15 +385,16 @@ static hipError_t launch_kv(const KvArgs& a, const KvPlan& p) {
   return hipGetLastError();
 }
 
-template <class TR>
+template <class TR, bool F8>
 static hipError_t dispatch_kv(const KvArgs& a, const KvPlan& p) {
-  if (a.d == 128) return a.causal ? launch_kv<TR, 128, true>(a, p) : launch_kv<TR, 128, false>(a, p);
-  return a.causal ? launch_kv<TR, 64, true>(a, p) : launch_kv<TR, 64, false>(a, p);
+  if (a.d == 128) return a.causal ? launch_kv<TR, 128, true, F8>(a, p) : launch_kv<TR, 128, false, F8>(a, p);
+  return a.causal ? launch_kv<TR, 64, true, F8>(a, p) : launch_kv<TR, 64, false, F8>(a, p);
 }
 
 hipError_t launch_fwd_kvcache(const KvArgs& a) {
   const KvPlan p = kv_plan(a.BH, a.Nq, a.Nk, a.d);
-  return a.dtype == DT_BF16 ? dispatch_kv<BF16>(a, p) : dispatch_kv<F16>(a, p);
+  if (a.fp8_cache) return a.dtype == DT_BF16 ? dispatch_kv<BF16, true>(a, p) : dispatch_kv<F16, true>(a, p);
+  return a.dtype == DT_BF16 ? dispatch_kv<BF16, false>(a, p) : dispatch_kv<F16, false>(a, p);
 }
 
 }  // namespace fa

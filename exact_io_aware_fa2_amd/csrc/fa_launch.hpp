@@ -66,9 +66,11 @@ struct KvArgs {
   int Nq;
   int Nk;
   int d;
-  float c;                 // scale * log2(e)
+  float c;                 // scale * log2(e) (times the K scale of an 8-bit cache)
+  float v_scale;           // multiplies O: the V scale of an 8-bit cache, else 1
+  int fp8_cache;           // k, v hold OCP E4M3 codes (1 byte per element)
   int causal;
-  int dtype;
+  int dtype;               // of q and o (FA_BF16 or FA_F16)
   hipStream_t stream;
 };
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
   FA_OK = 0,
@@ -164,6 +164,26 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, cons
                    void* o, float* lse, void* workspace, size_t workspace_bytes,
                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
                    int dtype, void* stream);
+
+/* fa_fwd_kvcache with the cache stored in 8 bits: k_cache and v_cache hold
+ * OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, largest value 448; one byte per element, layout [B,H,Nk,d])
+ * with one scale per tensor: the cached key row j is k_scale * E4M3(k[j]),
+ * the value row v_scale * E4M3(v[j]).  The pages describe 8-bit floating
+ * point as a later step of the method's line ("FlashAttention-2 (DE)",
+ * "Vergleich mit nachfolgenden Versionen / FlashAttention-3"); here it halves
+ * the bytes a decode step reads.  With those dequantised values the result is
+ * the same attention as fa_fwd_kvcache computes (the codes convert exactly to
+ * the query's 16-bit type); the difference from an unquantised cache is the
+ * quantisation of the cache alone.
+ *   k_scale, v_scale  finite and > 0, else FA_ERR_SCALE.
+ * Every other argument, the workspace size (fa_fwd_kvcache_workspace_bytes
+ * with the query's dtype), alignment and error rule is as for
+ * fa_fwd_kvcache; dtype is that of q and o (FA_BF16 or FA_F16). */
+int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                       float v_scale, const int32_t* seqlens_k, void* o, float* lse, void* workspace,
+                       size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                       float scale, int causal, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

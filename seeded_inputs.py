@@ -138,6 +138,7 @@ class KvWorkload:
     sigma: float
     seed: int
     min_fill: float = 0.5  # filled lengths drawn uniformly in [min_fill * Nk, Nk]
+    cache: str = "same"    # "same": K, V in the query dtype; "e4m3": 8-bit cache
 
     @property
     def scale(self) -> float:
@@ -147,6 +148,8 @@ class KvWorkload:
 KV_WORKLOADS = {
     "D1": KvWorkload("D1", 4, 32, 1, 32768, 128, "bf16", True, 1.0, 1006),
     "D1d64": KvWorkload("D1d64", 4, 32, 1, 32768, 64, "bf16", True, 1.0, 1006),
+    # the same decode step with the cache stored as per-tensor scaled E4M3
+    "D1f8": KvWorkload("D1f8", 4, 32, 1, 32768, 128, "bf16", True, 1.0, 1006, cache="e4m3"),
 }
 
 
@@ -171,4 +174,84 @@ def make_kvcache_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, si
 
 
 def make_kv_workload_inputs(w: KvWorkload):
+    if w.cache == "e4m3":
+        return make_kvcache_fp8_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.sigma, w.seed, w.min_fill)
     return make_kvcache_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.sigma, w.seed, w.min_fill)
+
+
+# ---- 8-bit floating point (OCP E4M3, "fn": no infinities, max 448) for a
+# quantised key/value cache.  Only the rounding of drawn values to the
+# storage format lives here.
+
+def _e4m3_positive_table() -> np.ndarray:
+    """Values of the codes 0x00 .. 0x7E (0x7F is NaN), ascending."""
+    codes = np.arange(0x7F)
+    e, m = codes >> 3, codes & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+E4M3_MAX = 448.0
+
+
+def round_e4m3(x: np.ndarray) -> np.ndarray:
+    """float32 -> E4M3 codes (uint8), round to nearest, ties to even, values
+    beyond +-448 saturate to +-448, NaN -> 0x7F.
+
+    |x| >= 2^-6 (normal): |x| = f 2^e with f in [0.5, 1); the code is
+    8 (e + 6) + rint(16 f) - 8 (3 mantissa bits; a mantissa that rounds up to
+    16 carries into the exponent by the same sum).  |x| < 2^-6 (subnormal,
+    steps of 2^-9): the code is rint(512 |x|).  rint rounds half to even, and
+    the code's last bit is the mantissa's, so ties go to the even code.
+    Works in chunks (the arithmetic is exact in float32)."""
+    x = np.asarray(x, dtype=np.float32)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 1 << 24
+    for i in range(0, flat.size, step):
+        xi = flat[i:i + step]
+        a = np.minimum(np.abs(xi), np.float32(E4M3_MAX))
+        f, e = np.frexp(a)
+        normal = 8 * (e.astype(np.int32) + 6) + np.rint(16 * f).astype(np.int32) - 8
+        sub = np.rint(a * np.float32(512.0)).astype(np.int32)
+        code = np.where(a < np.float32(2.0 ** -6), sub, normal).astype(np.uint8)
+        code = np.where(np.signbit(xi) & (code != 0), code | np.uint8(0x80), code)
+        out[i:i + step] = np.where(np.isnan(xi), np.uint8(0x7F), code)
+    return out.reshape(x.shape)
+
+
+def e4m3_to_f32(code: np.ndarray) -> np.ndarray:
+    """E4M3 codes -> their float32 values (exact)."""
+    code = np.asarray(code, dtype=np.uint8)
+    tab = np.append(_e4m3_positive_table(), np.nan)
+    v = tab[code & 0x7F]
+    return np.where(code & 0x80, -v, v).astype(np.float32)
+
+
+def quantise_e4m3(x: np.ndarray):
+    """Per-tensor scaled E4M3 with a power-of-two scale: scale = 2^ceil(log2(
+    max|x| / 448)) (1 if x is all zero), codes = round_e4m3(x / scale).
+    Returns (codes uint8, scale float32, dequantised float32 values
+    scale * e4m3(codes), exact: the scale only shifts exponents)."""
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    scale = np.float32(2.0 ** np.ceil(np.log2(amax / E4M3_MAX)) if amax > 0 else 1.0)
+    codes = round_e4m3(np.asarray(x, dtype=np.float32) / scale)
+    deq = e4m3_to_f32(codes) * scale
+    return codes, scale, deq
+
+
+def make_kvcache_fp8_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, sigma: float, seed: int,
+                            min_fill: float = 0.5):
+    """As make_kvcache_inputs, with the cache stored as per-tensor scaled E4M3.
+
+    The same draws as make_kvcache_inputs (so the 16-bit and 8-bit caches
+    hold the same underlying values); K and V are then quantised with
+    quantise_e4m3.  Returns the make_kvcache_inputs dict with "k" and "v"
+    replaced by (dequantised float32 values, uint8 codes), the 16-bit cache
+    kept as "k16"/"v16", and "k_scale", "v_scale"."""
+    out = make_kvcache_inputs(B, H, Nq, Nk, d, dtype, sigma, seed, min_fill)
+    out["k16"], out["v16"] = out["k"], out["v"]
+    for nm in ("k", "v"):
+        codes, sc, deq = quantise_e4m3(out[nm + "16"][0])
+        out[nm] = (deq, codes)
+        out[nm + "_scale"] = sc
+    return out

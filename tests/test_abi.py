@@ -35,13 +35,13 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
          "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kvcache_workspace_bytes",
-         "fa_fwd_kvcache"])
+         "fa_fwd_kvcache", "fa_fwd_kvcache_fp8"])
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 2
+    assert lib.fa_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -177,3 +177,23 @@ def test_kvcache_workspace_bytes(lib):
     assert ws(2, 4, 1, 4096, 128, 0) == 0  # fp32 is not taken
     assert ws(0, 4, 1, 4096, 128, 2) == 0
     assert ws(2, 4, 1, 4096, 96, 2) == 0
+
+
+def kv8(lib, q=P[0], k=P[1], v=P[2], ks=0.01, vs=0.02, lens=None, o=P[3], lse=P[4], ws=P[10], wsb=1 << 30,
+        B=2, H=4, Nq=1, Nk=4096, d=128, scale=0.088, causal=1, dtype=2):
+    return lib.fa_fwd_kvcache_fp8(q, k, v, ks, vs, lens, o, lse, ws, wsb, B, H, Nq, Nk, d, scale, causal,
+                                  dtype, None)
+
+
+def test_kvcache_fp8_argument_errors(lib):
+    for name in ("q", "k", "v", "o", "lse"):
+        assert kv8(lib, **{name: None}) == FA_ERR_NULL, name
+    assert kv8(lib, Nk=0) == FA_ERR_SHAPE
+    assert kv8(lib, d=32) == FA_ERR_HEADDIM
+    assert kv8(lib, dtype=0) == FA_ERR_DTYPE
+    assert kv8(lib, k=P[1] + 4) == FA_ERR_ALIGN
+    for bad in (0.0, -1.0, math.inf, math.nan):
+        assert kv8(lib, ks=bad) == FA_ERR_SCALE
+        assert kv8(lib, vs=bad) == FA_ERR_SCALE
+    assert kv8(lib, scale=-0.1) == FA_ERR_SCALE
+    assert kv8(lib, ws=None) == FA_ERR_WORKSPACE

@@ -47,3 +47,59 @@ def test_workload_table():
     assert w.fwd_flop() == 4 * 2 * 32 * 8192 ** 2 * 128 / 2
     assert si.WORKLOADS["C4"].sigma == 0.5
     assert si.WORKLOADS["C5"].backward
+
+
+# ---------------------------------------------------------------- E4M3 (8-bit) cache rounding
+
+def test_e4m3_codes_round_trip_and_known_values():
+    """OCP E4M3 ("fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent
+    field 0 is subnormal (m/8 * 2^-6); 0x7F/0xFF are NaN; the largest value
+    is 1.75 * 2^8 = 448."""
+    import numpy as np
+    import seeded_inputs as si
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = si.e4m3_to_f32(codes)
+    assert np.array_equal(si.round_e4m3(vals)[vals != 0], codes[vals != 0])  # -0 maps to +0
+    known = {0x38: 1.0, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x08: 2.0 ** -6, 0x07: 7 * 2.0 ** -9,
+             0x40: 2.0, 0xC6: -3.5, 0x3F: 1.875, 0x00: 0.0}
+    for c, v in known.items():
+        assert si.e4m3_to_f32(np.array([c], np.uint8))[0] == v
+        assert si.round_e4m3(np.array([v], np.float32))[0] == c
+    assert np.isnan(si.e4m3_to_f32(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def test_e4m3_rounding_ties_to_even_and_saturates():
+    import numpy as np
+    import seeded_inputs as si
+    # midpoints: 1.0625 between 1.0 (0x38, even) and 1.125 (0x39); 1.1875 between 0x39 and 1.25 (0x3A)
+    x = np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -11, 460.0, 1e9, -1e9, 1.06], np.float32)
+    assert si.round_e4m3(x).tolist() == [0x38, 0x3A, 0x00, 0x01, 0x7E, 0x7E, 0xFE, 0x38]
+    # nearest: every finite value rounds to a code no further than any other code
+    rng = np.random.default_rng(3)
+    y = (rng.standard_normal(5000) * 50).astype(np.float32)
+    q = si.e4m3_to_f32(si.round_e4m3(y))
+    tab = si.e4m3_to_f32(np.arange(256, dtype=np.uint8))
+    tab = tab[np.isfinite(tab)]
+    best = np.abs(y[:, None] - tab[None, :]).min(axis=1)
+    assert np.array_equal(np.abs(y - q), np.minimum(best, np.abs(y - q)))
+    assert np.allclose(np.abs(y - q), best, rtol=0, atol=0)
+
+
+def test_fp8_cache_inputs_share_the_16_bit_draws():
+    import numpy as np
+    import seeded_inputs as si
+    a = si.make_kvcache_inputs(2, 3, 2, 50, 64, "bf16", 1.0, 9)
+    b = si.make_kvcache_fp8_inputs(2, 3, 2, 50, 64, "bf16", 1.0, 9)
+    assert np.array_equal(a["q"][1], b["q"][1]) and np.array_equal(a["seqlens"], b["seqlens"])
+    assert np.array_equal(a["k"][1], b["k16"][1])
+    for nm in ("k", "v"):
+        deq, codes = b[nm]
+        assert codes.dtype == np.uint8 and codes.shape == (2, 3, 50, 64)
+        sc = float(b[nm + "_scale"])
+        assert sc == 2.0 ** round(np.log2(sc))  # a power of two: dequantised values are exact
+        assert np.array_equal(deq.astype(np.float64), si.e4m3_to_f32(codes).astype(np.float64) * sc)
+        top = np.abs(si.e4m3_to_f32(codes)).max()
+        assert 224.0 < top <= 448.0  # max|x| / scale lands in (224, 448]
+        # each value is the nearest scaled code to its 16-bit draw
+        x = b[nm + "16"][0] / sc
+        assert np.all(np.abs(x - si.e4m3_to_f32(codes)) <= np.abs(x) * 2.0 ** -4 + 2.0 ** -10)

@@ -137,3 +137,69 @@ def test_decode_workload_full_size_sampled_heads(name):
         o_ref, l_ref = kvcache_fwd_head(inp["q"][0][b, h], inp["k"][0][b, h], inp["v"][0][b, h], w.scale,
                                         w.causal, L)
         _check(o[b, h], lse[b, h], o_ref, l_ref, w.dtype, f"{name} head ({b},{h}) L={L}")
+
+
+# ------------------------------------------------------------ 8-bit (E4M3) cache
+
+def _run8(inp, dtype, causal, scale, k_codes=None, v_codes=None):
+    import torch
+    fa = lib()
+    q = to_device(inp["q"][1], dtype)
+    k = torch.from_numpy(inp["k"][1] if k_codes is None else k_codes).cuda()
+    v = torch.from_numpy(inp["v"][1] if v_codes is None else v_codes).cuda()
+    lens = torch.from_numpy(inp["seqlens"]).cuda()
+    o, lse = fa.fwd_kvcache_fp8(q, k, v, float(inp["k_scale"]), float(inp["v_scale"]), lens, causal, scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Nq,Nk,fill", [SMALL[0], SMALL[1], SMALL[2], SMALL[4], SMALL[6]])
+def test_fp8_cache_small_shapes(B, H, Nq, Nk, fill, causal, d, dtype):
+    """Against the oracle on the dequantised cache (k_scale * E4M3 codes): the
+    same attention as with a 16-bit cache, to the same tolerances."""
+    seed = 8000 + Nq * 13 + Nk
+    inp = si.make_kvcache_fp8_inputs(B, H, Nq, Nk, d, dtype, 1.0, seed, fill)
+    scale = 1.0 / np.sqrt(d)
+    say(f"kvcache fp8 B{B} H{H} Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal} seed={seed} "
+        f"k_scale={inp['k_scale']:.4g} v_scale={inp['v_scale']:.4g}")
+    o, lse = _run8(inp, dtype, causal, scale)
+    o_ref, lse_ref = kvcache_fwd(inp["q"][0], inp["k"][0], inp["v"][0], scale, causal, inp["seqlens"])
+    _check(o, lse, o_ref, lse_ref, dtype, f"fp8 Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal}")
+
+
+def test_fp8_cache_unfilled_rows_are_never_read():
+    inp = si.make_kvcache_fp8_inputs(3, 2, 4, 600, 128, "bf16", 1.0, 81, 0.2)
+    k, v = inp["k"][1].copy(), inp["v"][1].copy()
+    for b, L in enumerate(inp["seqlens"]):
+        k[b, :, L:] = 0x7F  # E4M3 NaN
+        v[b, :, L:] = 0x7F
+    say(f"kvcache fp8 NaN codes past the filled lengths {inp['seqlens'].tolist()}")
+    for causal in (False, True):
+        a = _run8(inp, "bf16", causal, 0.09)
+        b = _run8(inp, "bf16", causal, 0.09, k_codes=k, v_codes=v)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_fp8_decode_workload_full_size_sampled_heads():
+    """The benchmarked 8-bit decode step at full size: parity against the
+    oracle on the dequantised cache, and (reported separately, as the error
+    the quantisation itself adds) the distance to the oracle on the 16-bit
+    cache the codes were quantised from."""
+    w = si.KV_WORKLOADS["D1f8"]
+    say(f"D1f8 full size on GPU: {w}")
+    inp = si.make_kv_workload_inputs(w)
+    o, lse = _run8(inp, w.dtype, w.causal, w.scale)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    for (b, h) in [(0, 0), (1, 17), (2, 5), (3, 31)]:
+        L = int(inp["seqlens"][b])
+        o_ref, l_ref = kvcache_fwd_head(inp["q"][0][b, h], inp["k"][0][b, h], inp["v"][0][b, h], w.scale,
+                                        w.causal, L)
+        _check(o[b, h], lse[b, h], o_ref, l_ref, w.dtype, f"D1f8 head ({b},{h}) L={L}")
+        o16, l16 = kvcache_fwd_head(inp["q"][0][b, h], inp["k16"][0][b, h], inp["v16"][0][b, h], w.scale,
+                                    w.causal, L)
+        qo, ql = float(np.abs(o[b, h] - o16).max()), float(np.abs(lse[b, h] - l16).max())
+        say(f"  quantisation error vs the 16-bit cache: O max-abs {qo:.3e}, LSE max-abs {ql:.3e}")
+        assert qo < 0.05 and ql < 0.5  # sanity only: E4M3 keeps 3 mantissa bits
