@@ -19,7 +19,8 @@ Modes
   --workload D1         a decode step against a key/value cache instead (fa_fwd_kvcache,
                         B=4 H=32, one query, 32768-row cache, d=128): HBM GB/s;
                         D1f8: the same with an 8-bit E4M3 cache (fa_fwd_kvcache_fp8)
-  --profile             3 warm-up + 20 timed steps, no CPU baseline, for rocprofv3 runs;
+  --profile             3 warm-up + 20 timed steps (stages in order on one stream), no CPU
+                        baseline, for rocprofv3 runs;
                         also runs a plain 1 GiB device copy (the calibration
                         kernel for FETCH_SIZE / WRITE_SIZE counters)
   --ingest-pmc F W      turn two rocprofv3 --pmc csv files (FETCH_SIZE, then
@@ -340,7 +341,9 @@ def main():
     if w.dtype == "f32":
         raise SystemExit("the fwd+bwd step needs a 16-bit workload")
     if args.profile:
-        args.steps, args.warmup = min(args.steps, 20), min(args.warmup, 3)
+        # profiled runs keep the stages on one stream, so that each kernel's
+        # traced duration is its own (not shared with a concurrent stage)
+        args.steps, args.warmup, args.serial = min(args.steps, 20), min(args.warmup, 3), True
     dev = torch.device("cuda:0")
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
     inp = si.make_workload_inputs(w, backward=True)
