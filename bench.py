@@ -19,6 +19,8 @@ Modes
   --workload D1         a decode step against a key/value cache instead (fa_fwd_kvcache,
                         B=4 H=32, one query, 32768-row cache, d=128): HBM GB/s;
                         D1f8: the same with an 8-bit E4M3 cache (fa_fwd_kvcache_fp8)
+  --fwd-only            fa_fwd alone: time, TFLOP/s and compulsory GB/s per workload
+                        (--workload C1,C3,...; --workload short: the short-sequence sweep)
   --profile             3 warm-up + 20 timed steps (stages in order on one stream), no CPU
                         baseline, for rocprofv3 runs;
                         also runs a plain 1 GiB device copy (the calibration
@@ -252,6 +254,62 @@ def bench_kvcache(args, w):
     print(json.dumps(out), flush=True)
 
 
+def bench_fwd_only(args, workloads):
+    """fa_fwd alone on each workload: one JSON line each with the median time
+    of --steps calls (HIP events, after --warmup), TFLOP/s against the dense
+    MFMA peak of the dtype and GB/s of compulsory bytes (Q, K, V read once,
+    O and LSE written once) against 8 TB/s."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_fa2_amd as fa
+    import seeded_inputs as si
+
+    dev = torch.device("cuda:0")
+    for w in workloads:
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+        inp = si.make_workload_inputs(w, backward=False)
+
+        def up(name):
+            a = inp[name][1]
+            if w.dtype == "bf16":
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+
+        q, k, v = up("q"), up("k"), up("v")
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1 in evs:
+            e0.record()
+            fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        s = {"bf16": 2, "f16": 2, "f32": 4}[w.dtype]
+        nbytes = 4 * w.B * w.H * w.N * w.d * s + 4 * w.B * w.H * w.N
+        peak = PEAK_MFMA_16BIT if s == 2 else 157.3
+        tf = w.fwd_flop() / (ms * 1e-3) / 1e12
+        print(json.dumps({"mode": "forward only", "workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} "
+                                                              f"{'causal' if w.causal else 'non-causal'}",
+                          "median_us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+                          "frac_mfma_peak": round(tf / peak, 4), "mfma_peak": peak,
+                          "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
+                          "compulsory_bytes": nbytes, "steps": args.steps}), flush=True)
+        del q, k, v, o, lse, inp
+
+
+def short_n_workloads():
+    """Short sequences, small head dimension: B=16 H=16 d=64 bf16 non-causal,
+    N = 128, 256, 512, 1024 (seed 1007); where the forward is closest to the
+    HBM roofline (arithmetic intensity ~N/2 FLOP per byte)."""
+    import seeded_inputs as si
+    return [si.Workload(f"S{n}", 16, 16, n, 64, "bf16", False, 1.0, 1007) for n in (128, 256, 512, 1024)]
+
+
 def ingest_pmc(fetch_csv: str, write_csv: str, workload: str):
     """Counter summary -> profiles/traffic_<workload>.json.
 
@@ -317,6 +375,9 @@ def main():
     ap.add_argument("--serial", action="store_true",
                     help="time the step with all stages in order on one stream (dQ not beside dK/dV)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time fa_fwd alone on --workload (any of C1..C5, C3d64, C5d128; comma-separated), "
+                         "or on the short-sequence sweep with --workload short")
     args = ap.parse_args()
 
     if args.ingest_pmc:
@@ -334,6 +395,10 @@ def main():
     import seeded_inputs as si
 
     fa.load_library()
+    if args.fwd_only:
+        wls = short_n_workloads() if args.workload == "short" else [si.WORKLOADS[n] for n in args.workload.split(",")]
+        bench_fwd_only(args, wls)
+        return
     if args.workload in si.KV_WORKLOADS:
         bench_kvcache(args, si.KV_WORKLOADS[args.workload])
         return
