@@ -127,6 +127,30 @@ def cpu_baseline(w, target_s: float):
                       f"+ backward, {t_total:.1f} s; BLAS threads {threads}, host cpus {os.cpu_count()}"}
 
 
+def measured_mfma_peak() -> dict:
+    """Sustained dense bf16 MFMA rate of this device from the library's probe
+    (fa_probe_mfma_bf16: register-only v_mfma_f32_32x32x16_bf16 chains, two
+    wavefronts per SIMD on 256 compute units), best of 5 timed launches."""
+    import torch
+
+    import exact_io_aware_fa2_amd as fa
+    wgs, iters = 512, 4096
+    fa.fa_probe_mfma_bf16(wgs, iters)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flop = fa.fa_probe_mfma_bf16(wgs, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    # 256 CUs x 4096 FLOP per clock (dense bf16): the clock the rate implies
+    return {"TFLOP/s": round(best, 1), "frac_of_spec": round(best / PEAK_MFMA_16BIT, 4),
+            "implied_clock_GHz": round(best * 1e12 / (256 * 4096) / 1e9, 3),
+            "probe": "fa_probe_mfma_bf16, 512 workgroups x 4 wavefronts x 4096 rounds of 4 MFMAs"}
+
+
 def kv_bytes(w, seqlens) -> float:
     """Compulsory HBM bytes of one call of fa_fwd_kvcache(_fp8): read Q and the
     filled cache rows of K and V once, write O and LSE."""
@@ -478,11 +502,28 @@ def main():
     # per-kernel durations: the same steps with the stages in order on one
     # stream, each between its own events (these times feed the roofline)
     n_k = max(5, min(args.steps, 20))
+    for _ in range(2):
+        step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_k)]
     for i in range(n_k):
         step(evs[i])
     torch.cuda.synchronize()
     kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    # secondary: the same steps with the caches cold, a 512 MiB scrub written
+    # before each step (outside the timed region)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flushed = []
+    for i in range(min(args.steps, 10)):
+        scrub.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        flushed.append(e0.elapsed_time(e1))
+    del scrub
+    ms_flushed = float(np.median(flushed))
+
     flop_step = w.fwd_flop() + w.bwd_flop()
     value = flop_step / (ms_step * 1e-3) / 1e12
     alg = algorithmic(w)
@@ -518,6 +559,9 @@ def main():
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "parallelism": "single GPU"},
         "frac_of_peak": round(value / PEAK_MFMA_16BIT, 4),
+        "flushed": {"ms_per_step": round(ms_flushed, 4),
+                    "value": round(flop_step / (ms_flushed * 1e-3) / 1e12, 2),
+                    "note": "median of 10 steps, each after a 512 MiB scrub of the caches"},
         "fwd_tflops": round(w.fwd_flop() / (kern_ms["fwd"] * 1e-3) / 1e12, 1),
         "bwd_tflops": round(w.bwd_flop() / ((kern_ms["prep"] + kern_ms["dkdv"] + kern_ms["dq"]) * 1e-3) / 1e12, 1),
         "kernels": per_kernel,
@@ -526,6 +570,10 @@ def main():
                     "fwd, prep, then dK/dV and dQ on two streams at once",
         "roofline": roof,
     }
+    if not args.profile:
+        m = measured_mfma_peak()
+        m["frac_of_measured_dominant"] = round(achieved / m["TFLOP/s"], 4)
+        out["mfma_peak_measured"] = m
     if not args.no_cpu_baseline and not args.profile:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     if args.profile:

@@ -76,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fa_fwd_kvcache_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
     L.fa_fwd_kvcache.restype = i32
     L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+    L.fa_probe_mfma_bf16.restype = i64
+    L.fa_probe_mfma_bf16.argtypes = [i64, i64, vp]
     L.fa_fwd_kvcache_fp8.restype = i32
     L.fa_fwd_kvcache_fp8.argtypes = [vp, vp, vp, f32, f32, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, f32, i32,
                                      i32, vp]
@@ -279,6 +281,15 @@ def fwd_kvcache(q, k_cache, v_cache, seqlens_k=None, causal: bool = True, scale:
     fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, workspace,
                    default_scale(d) if scale is None else scale, causal)
     return o, lse
+
+
+def fa_probe_mfma_bf16(workgroups: int, iters: int) -> int:
+    """Enqueue the dense bf16 MFMA probe on the current stream; returns its FLOP count."""
+    torch = _torch()
+    n = int(load_library().fa_probe_mfma_bf16(workgroups, iters, torch.cuda.current_stream().cuda_stream))
+    if n < 0:
+        _check(-n)
+    return n
 
 
 def default_scale(d: int) -> float:

@@ -318,3 +318,13 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, 
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int64_t fa_probe_mfma_bf16(int64_t workgroups, int64_t iters, void* stream) {
+  if (workgroups < 1 || workgroups > kMaxWorkgroups || iters < 1 || iters > INT32_MAX) return -FA_ERR_SHAPE;
+  if (fa::launch_mfma_peak((int)workgroups, (int)iters, (hipStream_t)stream) != hipSuccess) return -FA_ERR_HIP;
+  return workgroups * 4 * iters * 4 * 32768;
+}
+
+}  // extern "C"

@@ -126,8 +126,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // previous one is computed.  The loads are issued on every iteration (the
   // last one reloads its own tile, an L2 hit), so that the wait counts are the
   // same on every path and no wait for the current tile's data also waits for
-  // the next tile's.  Chunk i of a lane is row (64 i + lane) / (D / 8), 16-byte
-  // column chunk (64 i + lane) % (D / 8) of the tile.
+  // the next tile's.  Chunk i of a lane is 16-byte chunk (64 i + lane) % VCH
+  // of row (64 i + lane) / VCH of the tile (VCH chunks per cache row).
   u32x4_t kc[NVL], vv[NVL];
   auto load_k = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll

@@ -109,6 +109,9 @@ inline size_t kv_workspace_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t d) 
 
 hipError_t launch_fwd_kvcache(const KvArgs& a);
 
+// Measurement probe (fa_probe_mfma_bf16): workgroups of 4 wavefronts.
+hipError_t launch_mfma_peak(int workgroups, int iters, hipStream_t stream);
+
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);                 // all three stages in order
 hipError_t launch_bwd_stage(const BwdArgs& a, int stage);  // one stage

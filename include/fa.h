@@ -185,6 +185,18 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, 
                        size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                        float scale, int causal, int dtype, void* stream);
 
+/* Measurement probe, not part of attention: enqueues a kernel of `workgroups`
+ * workgroups (4 wavefronts each) in which every wavefront issues `iters`
+ * rounds of four independent dense bf16 matrix products
+ * (v_mfma_f32_32x32x16_bf16, 32768 FLOP each) on register operands, reading
+ * and writing no memory.  Timed by the caller (events around the call on
+ * `stream`), it gives the sustained dense bf16 MFMA rate the attention
+ * kernels are compared with beside the published peak.  Returns the FLOP
+ * count of the launch (workgroups * 4 * iters * 4 * 32768), or the negated
+ * FA_ERR_SHAPE (workgroups not in [1, 2^24 - 1] or iters not in
+ * [1, 2^31 - 1]) or FA_ERR_HIP (launch refused). */
+int64_t fa_probe_mfma_bf16(int64_t workgroups, int64_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
          "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kvcache_workspace_bytes",
-         "fa_fwd_kvcache", "fa_fwd_kvcache_fp8"])
+         "fa_fwd_kvcache", "fa_fwd_kvcache_fp8", "fa_probe_mfma_bf16"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -197,3 +197,11 @@ def test_kvcache_fp8_argument_errors(lib):
         assert kv8(lib, vs=bad) == FA_ERR_SCALE
     assert kv8(lib, scale=-0.1) == FA_ERR_SCALE
     assert kv8(lib, ws=None) == FA_ERR_WORKSPACE
+
+
+def test_probe_argument_errors(lib):
+    lib.fa_probe_mfma_bf16.restype = ctypes.c_int64
+    lib.fa_probe_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    assert lib.fa_probe_mfma_bf16(0, 10, None) == -FA_ERR_SHAPE
+    assert lib.fa_probe_mfma_bf16(10, 0, None) == -FA_ERR_SHAPE
+    assert lib.fa_probe_mfma_bf16(1 << 24, 10, None) == -FA_ERR_SHAPE
