@@ -120,27 +120,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = zero16();
 
-  // K and V of a tile are loaded one step ahead into the same registers: the
-  // next tile's K as soon as this tile's K is in LDS, the next tile's V as
-  // soon as this tile's V is, so one tile's loads are in flight while the
-  // previous one is computed.  The loads are issued on every iteration (the
-  // last one reloads its own tile, an L2 hit), so that the wait counts are the
-  // same on every path and no wait for the current tile's data also waits for
-  // the next tile's.  Chunk i of a lane is 16-byte chunk (64 i + lane) % VCH
-  // of row (64 i + lane) / VCH of the tile (VCH chunks per cache row).
-  u32x4_t kc[NVL], vv[NVL];
-  auto load_k = [&](int k0) __attribute__((always_inline)) {
+  // K and V are loaded DEPTH tiles ahead: the loads of tile i + DEPTH go into
+  // the registers tile i has just written to LDS (K right after its K rows are
+  // in LDS, V right after its V rows), so DEPTH tiles' loads are in flight
+  // while a tile is computed.  A 16-bit tile is 32 rows x 2 d bytes per
+  // tensor, an 8-bit one half that; the 8-bit cache runs two tiles ahead in
+  // the registers one 16-bit tile takes (measured: the same speed at d = 128,
+  // 3% faster at d = 64; two tiles ahead for the 16-bit cache at d = 64 costs
+  // a wavefront per SIMD and was 2% slower).  The loads are issued for every
+  // tile (past the range a tile reloads itself, an L2 hit, and the extra
+  // tiles of the last group are fully masked), so that the wait counts are
+  // the same on every path and no wait for one tile's data also waits for a
+  // later tile's.  Chunk i of a lane is 16-byte chunk (64 i + lane) % VCH of
+  // row (64 i + lane) / VCH of the tile (VCH chunks per cache row).
+  constexpr int DEPTH = F8 ? 2 : 1;
+  u32x4_t kc[DEPTH][NVL], vv[DEPTH][NVL];
+  auto load_k = [&](u32x4_t (&dst)[NVL], int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int ch = 64 * i + lane;
-      kc[i] = buf_load16(kres, (uint32_t)k0 * RBC + (uint32_t)(ch / VCH) * RBC + 16 * (ch % VCH));
+      dst[i] = buf_load16(kres, (uint32_t)k0 * RBC + (uint32_t)(ch / VCH) * RBC + 16 * (ch % VCH));
     }
   };
-  auto load_v = [&](int k0) __attribute__((always_inline)) {
+  auto load_v = [&](u32x4_t (&dst)[NVL], int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int ch = 64 * i + lane;
-      vv[i] = buf_load16(vres, (uint32_t)k0 * RBC + (uint32_t)(ch / VCH) * RBC + 16 * (ch % VCH));
+      dst[i] = buf_load16(vres, (uint32_t)k0 * RBC + (uint32_t)(ch / VCH) * RBC + 16 * (ch % VCH));
     }
   };
   // chunk x (16 bytes of a cache row) -> its row's LDS position: as is, or
@@ -161,23 +167,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       *(u32x4_t*)dst = x;
     }
   };
+  // keys of this range visible to this lane's query (the last group of DEPTH
+  // tiles may reach past the range: those keys are masked here)
+  const int lim_r = min(lim, ke - 1);
   if (kb < ke) {
-    // K first: the loop's wait for K(i) leaves V(i) in flight, which needs
-    // this issue order on entry as well as on the back edge
-    load_k(kb);
-    __builtin_amdgcn_sched_barrier(0);
-    load_v(kb);
+    // K before V, tile by tile: a wait for one tile's K then leaves its V and
+    // every later tile in flight, on entry as on the back edge
+#pragma unroll
+    for (int t = 0; t < DEPTH; ++t) {
+      const int kt = kb + 32 * t < ke ? kb + 32 * t : kb;
+      load_k(kc[t], kt);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(vv[t], kt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  for (int k0 = kb; k0 < ke; k0 += 32) {
-    const int kn = k0 + 32 < ke ? k0 + 32 : k0;
+
+  // one 32-key tile starting at key k0, its chunks in registers kcs, vvs,
+  // which then receive the tile starting at key kn
+  auto tile = [&](u32x4_t (&kcs)[NVL], u32x4_t (&vvs)[NVL], int k0, int kn) __attribute__((always_inline)) {
     // K tile -> LDS (the previous tile's operand reads are done: they fed
     // its S products, which come before its V writes and their fence)
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int ch = 64 * i + lane;
-      put(ldk + (ch / VCH) * RSK + 2 * EPC * (ch % VCH), kc[i]);
+      put(ldk + (ch / VCH) * RSK + 2 * EPC * (ch % VCH), kcs[i]);
     }
-    load_k(kn);
+    load_k(kcs, kn);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
@@ -194,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = k0 + 16 * (r / 8) + 8 * h + (r % 8);
-      x[r] = key <= lim ? s[r] * c : -INFINITY;
+      x[r] = key <= lim_r ? s[r] * c : -INFINITY;
       mt = fmaxf(mt, x[r]);
     }
     mt = fmaxf(mt, swap_halves(mt));
@@ -228,9 +244,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int ch = 64 * i + lane;
-      put(lds + (ch / VCH) * RS + 2 * EPC * (ch % VCH), vv[i]);
+      put(lds + (ch / VCH) * RS + 2 * EPC * (ch % VCH), vvs[i]);
     }
-    load_v(kn);
+    load_v(vvs, kn);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
@@ -242,6 +258,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const u32x2_t a = lds_read_tr(p), b2 = lds_read_tr(p + 4 * RS);
         acc[db] = TR::mfma(u32x4_t{a[0], a[1], b2[0], b2[1]}, pk[t], acc[db]);
       }
+  };
+  for (int k0 = kb; k0 < ke; k0 += 32 * DEPTH) {
+    static_for<0, DEPTH>([&](auto tc) __attribute__((always_inline)) {
+      constexpr int t = decltype(tc)::value;
+      const int kt = k0 + 32 * t;
+      const int kn = kt + 32 * DEPTH < ke ? kt + 32 * DEPTH : kt;
+      tile(kc[t], vv[t], kt, kn);
+    });
   }
   l += swap_halves(l);
   lt += swap_halves(lt);
