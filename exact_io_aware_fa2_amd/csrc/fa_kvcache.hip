@@ -123,17 +123,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // K and V are loaded DEPTH tiles ahead: the loads of tile i + DEPTH go into
   // the registers tile i has just written to LDS (K right after its K rows are
   // in LDS, V right after its V rows), so DEPTH tiles' loads are in flight
-  // while a tile is computed.  A 16-bit tile is 32 rows x 2 d bytes per
-  // tensor, an 8-bit one half that; the 8-bit cache runs two tiles ahead in
-  // the registers one 16-bit tile takes (measured: the same speed at d = 128,
-  // 3% faster at d = 64; two tiles ahead for the 16-bit cache at d = 64 costs
-  // a wavefront per SIMD and was 2% slower).  The loads are issued for every
-  // tile (past the range a tile reloads itself, an L2 hit, and the extra
-  // tiles of the last group are fully masked), so that the wait counts are
-  // the same on every path and no wait for one tile's data also waits for a
-  // later tile's.  Chunk i of a lane is 16-byte chunk (64 i + lane) % VCH of
-  // row (64 i + lane) / VCH of the tile (VCH chunks per cache row).
-  constexpr int DEPTH = F8 ? 2 : 1;
+  // while a tile is computed.  One tile ahead is used: two (in the registers
+  // of one 16-bit tile for the 8-bit cache, or at a wavefront per SIMD less
+  // for the 16-bit cache at d = 64) measured no faster, and the 8-bit cache
+  // then fetched 5% more than its compulsory bytes.  The loads are issued for
+  // every tile (past the range a tile reloads itself, an L2 hit, and the
+  // extra tiles of a last group of DEPTH are fully masked), so that the wait
+  // counts are the same on every path and no wait for one tile's data also
+  // waits for a later tile's.  Chunk i of a lane is 16-byte chunk
+  // (64 i + lane) % VCH of row (64 i + lane) / VCH of the tile (VCH chunks
+  // per cache row).
+  constexpr int DEPTH = 1;
   u32x4_t kc[DEPTH][NVL], vv[DEPTH][NVL];
   auto load_k = [&](u32x4_t (&dst)[NVL], int k0) __attribute__((always_inline)) {
 #pragma unroll
