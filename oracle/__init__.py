@@ -11,7 +11,8 @@ attention.py  plain float64 numpy definition of attention forward (two-pass
               softmax, never online) and of its gradient (softmax Jacobian).
 kvcache.py    plain float64 definition of a few new queries attending to a
               key/value cache (fewer queries than keys, bottom-right causal
-              mask, per-batch filled lengths).
+              mask, per-batch filled lengths), and variable-length
+              packed batches built from it.
 brute.py      40-digit ``decimal`` brute force of both forwards for tiny
               shapes, used only to pin ``attention.py`` and ``kvcache.py``.
 
@@ -21,7 +22,7 @@ Parity status: every public function here is pinned by ``tests/test_oracle.py``
 
 from .attention import attention_fwd, attention_fwd_head, attention_bwd, attention_bwd_head
 from .brute import brute_fwd_decimal, brute_kvcache_decimal
-from .kvcache import kvcache_fwd, kvcache_fwd_head
+from .kvcache import kvcache_fwd, kvcache_fwd_head, varlen_fwd
 
 __all__ = [
     "attention_fwd",
@@ -32,4 +33,5 @@ __all__ = [
     "brute_kvcache_decimal",
     "kvcache_fwd",
     "kvcache_fwd_head",
+    "varlen_fwd",
 ]

@@ -93,3 +93,25 @@ def kvcache_fwd(q, k, v, scale: float, causal: bool, seqlens=None):
         for hi in range(h):
             o[bi, hi], lse[bi, hi] = kvcache_fwd_head(q[bi, hi], k[bi, hi], v[bi, hi], scale, causal, lens[bi])
     return o, lse
+
+
+def varlen_fwd(q, k, v, cu_q, cu_k, scale: float, causal: bool):
+    """Variable-length packed batch: sequence b owns query rows
+    cu_q[b] .. cu_q[b+1]-1 of q [total_q, H, d] and key/value rows
+    cu_k[b] .. cu_k[b+1]-1 of k, v [total_k, H, d]; within a sequence the
+    rule above applies with Nq = its query count and L = its key count
+    (causal: bottom-right aligned).  Returns (O [total_q, H, d],
+    LSE [H, total_q]) in float64; rows of no sequence stay 0 / -inf."""
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+    tq, h, d = q.shape
+    o = np.zeros((tq, h, v.shape[2]))
+    lse = np.full((h, tq), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 <= q0:
+            continue
+        for hi in range(h):
+            ob, lb = kvcache_fwd_head(q[q0:q1, hi], k[k0:k1, hi], v[k0:k1, hi], scale, causal)
+            o[q0:q1, hi] = ob
+            lse[hi, q0:q1] = lb
+    return o, lse

@@ -183,3 +183,56 @@ def test_kvcache_mutations_are_caught(label, old, new):
     mod = types.ModuleType("kv_mutant")
     exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
     assert not _kv_pins_pass(mod), f"pins did not catch mutation: {label}"
+
+
+# ---------------------------------------------------------------- variable-length packed batches
+
+def _pack(x, lens):
+    """[B, H, n, d] (first lens[b] rows of each b) -> packed [sum lens, H, d]."""
+    return np.concatenate([x[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(lens)], axis=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equal_lengths_is_the_batched_call(causal):
+    rng = np.random.default_rng(60)
+    B, H, nq, nk, d = 3, 2, 5, 9, 4
+    q, k, v = rnd(rng, B, H, nq, d), rnd(rng, B, H, nk, d), rnd(rng, B, H, nk, d)
+    o, lse = kvcache_fwd(q, k, v, 0.5, causal)
+    cu_q, cu_k = np.arange(B + 1) * nq, np.arange(B + 1) * nk
+    ov, lv = varlen_fwd(_pack(q, [nq] * B), _pack(k, [nk] * B), _pack(v, [nk] * B), cu_q, cu_k, 0.5, causal)
+    assert np.array_equal(ov, _pack(o, [nq] * B))
+    assert np.array_equal(lv, np.concatenate([lse[b] for b in range(B)], axis=1))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_matches_decimal_brute_force(causal):
+    rng = np.random.default_rng(61)
+    lq, lk = [2, 0, 3, 1], [3, 2, 2, 0]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    H, d = 2, 3
+    q, k, v = rnd(rng, cu_q[-1], H, d, s=1.5), rnd(rng, cu_k[-1], H, d, s=1.5), rnd(rng, cu_k[-1], H, d)
+    o, lse = varlen_fwd(q, k, v, cu_q, cu_k, 0.7, causal)
+    for b in range(len(lq)):
+        for h in range(H):
+            qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+            if lq[b] == 0:
+                continue
+            ob, lb = _dec(*brute_kvcache_decimal(q[qs, h], k[ks, h], v[ks, h], 0.7, causal, lk[b]))
+            assert np.max(np.abs(o[qs, h] - ob)) <= 1e-12
+            fin = np.isfinite(lb)
+            assert np.array_equal(np.isneginf(lse[h, qs]), np.isneginf(lb))
+            assert np.max(np.abs(lse[h, qs][fin] - lb[fin]), initial=0.0) <= 1e-12
+
+
+def test_varlen_sequences_are_independent():
+    """Changing one sequence's keys changes only that sequence's outputs."""
+    rng = np.random.default_rng(62)
+    lq, lk = [3, 4], [5, 6]
+    cu_q, cu_k = np.array([0, 3, 7]), np.array([0, 5, 11])
+    q, k, v = rnd(rng, 7, 2, 4), rnd(rng, 11, 2, 4), rnd(rng, 11, 2, 4)
+    o1, l1 = varlen_fwd(q, k, v, cu_q, cu_k, 0.5, True)
+    k2 = k.copy()
+    k2[5:] += 1.0
+    o2, l2 = varlen_fwd(q, k2, v, cu_q, cu_k, 0.5, True)
+    assert np.array_equal(o1[:3], o2[:3]) and np.array_equal(l1[:, :3], l2[:, :3])
+    assert not np.allclose(o1[3:], o2[3:])
