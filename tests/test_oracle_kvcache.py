@@ -12,7 +12,7 @@ import types
 import numpy as np
 import pytest
 
-from oracle import attention_fwd_head, brute_kvcache_decimal, kvcache_fwd, kvcache_fwd_head
+from oracle import attention_fwd_head, brute_kvcache_decimal, kvcache_fwd, kvcache_fwd_head, varlen_fwd
 from oracle import kvcache as okv
 
 
