@@ -14,11 +14,13 @@ place of pointers):
     fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, workspace, scale, causal)
     fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, dtype)
     fa_fwd_kvcache_fp8(q, k_cache, v_cache, k_scale, v_scale, seqlens_k, o, lse, workspace, scale, causal)
+    fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, workspace, max_q, max_k, scale, causal)
 Conveniences that allocate their outputs with torch:
     fwd(q, k, v, causal=False, scale=None) -> (o, lse)
     bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
     fwd_kvcache(q, k_cache, v_cache, seqlens_k=None, causal=True, scale=None) -> (o, lse)
     fwd_kvcache_fp8(q, k8, v8, k_scale, v_scale, seqlens_k=None, causal=True, scale=None) -> (o, lse)
+    fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_q, max_k, causal=False, scale=None) -> (o, lse)
     FlashAttention (torch.autograd.Function) and attention(q, k, v, causal, scale)
 """
 
@@ -76,6 +78,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fa_fwd_kvcache_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
     L.fa_fwd_kvcache.restype = i32
     L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+    L.fa_fwd_varlen_workspace_bytes.restype = sz
+    L.fa_fwd_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+    L.fa_fwd_varlen.restype = i32
+    L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, i64, i64, f32, i32,
+                                i32, vp]
     L.fa_probe_mfma_bf16.restype = i64
     L.fa_probe_mfma_bf16.argtypes = [i64, i64, vp]
     L.fa_fwd_kvcache_fp8.restype = i32
@@ -283,6 +290,52 @@ def fwd_kvcache(q, k_cache, v_cache, seqlens_k=None, causal: bool = True, scale:
     return o, lse
 
 
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, workspace, max_q: int, max_k: int,
+                  scale: float, causal: bool) -> None:
+    """Enqueue a variable-length packed batch (see include/fa.h): q, o
+    [total_q, H, d]; k, v [total_k, H, d]; cu_seqlens_q/k int32 [B + 1] on
+    the device; lse float32 [H, total_q]."""
+    L = load_library()
+    torch = _torch()
+    _check_tensors(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, workspace)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("packed tensors are [total, H, d]")
+    tq, H, d = (int(x) for x in q.shape)
+    tk = int(k.shape[0])
+    if tuple(k.shape) != (tk, H, d) or tuple(v.shape) != (tk, H, d) or tuple(o.shape) != (tq, H, d):
+        raise ValueError("k, v must be [total_k, H, d] and o [total_q, H, d]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
+        raise ValueError("q, k, v, o must share dtype")
+    if tuple(lse.shape) != (H, tq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [H, total_q]")
+    B = int(cu_seqlens_q.shape[0]) - 1
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        if cu.dtype != torch.int32 or tuple(cu.shape) != (B + 1,):
+            raise ValueError("cu_seqlens must be int32 [B + 1]")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(L.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(o), _ptr(lse),
+                           _ptr(workspace), nbytes, B, H, tq, tk, int(max_q), int(max_k), d, float(scale),
+                           int(bool(causal)), dtype_code(q), _stream(q)))
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_q: int, max_k: int, causal: bool = False,
+               scale: float | None = None, workspace=None):
+    """Allocate O, LSE (and the workspace unless given) and run a packed
+    variable-length batch. Returns (o [total_q, H, d], lse [H, total_q]).
+    O rows outside every sequence are zero."""
+    torch = _torch()
+    tq, H, d = (int(x) for x in q.shape)
+    B = int(cu_seqlens_q.shape[0]) - 1
+    o = torch.zeros_like(q)
+    lse = torch.empty((H, tq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nb = int(load_library().fa_fwd_varlen_workspace_bytes(B, H, max_q, max_k, d, dtype_code(q)))
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb > 0 else None
+    fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, workspace, max_q, max_k,
+                  default_scale(d) if scale is None else scale, causal)
+    return o, lse
+
+
 def fa_probe_mfma_bf16(workgroups: int, iters: int) -> int:
     """Enqueue the dense bf16 MFMA probe on the current stream; returns its FLOP count."""
     torch = _torch()
@@ -351,6 +404,6 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None):
 __all__ = [
     "load_library", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_prep", "fa_bwd_dkdv",
     "fa_bwd_dq", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache_fp8", "fwd", "bwd",
-    "fwd_kvcache", "fwd_kvcache_fp8", "attention",
+    "fwd_kvcache", "fwd_kvcache_fp8", "fa_fwd_varlen", "fwd_varlen", "fa_probe_mfma_bf16", "attention",
     "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH",
 ]

@@ -225,6 +225,20 @@ int check_kv_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
   return FA_OK;
 }
 
+// [B, H, N, d] queries and outputs, [B, H, Nk, d] caches, [B, H, Nq] LSE.
+fa::KvLayout dense_layout(int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+  fa::KvLayout l{};
+  l.q_sb = H * Nq * d;
+  l.q_sh = Nq * d;
+  l.q_sr = d;
+  l.c_sb = H * Nk * d;
+  l.c_sh = Nk * d;
+  l.c_sr = d;
+  l.l_sb = H * Nq;
+  l.l_sh = Nq;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -261,6 +275,7 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, cons
   a.o = o;
   a.lse = lse;
   a.workspace = need > 0 ? workspace : nullptr;
+  a.lay = dense_layout(H, Nq, Nk, d);
   a.H = (int)H;
   a.BH = (int)(B * H);
   a.Nq = (int)Nq;
@@ -302,6 +317,7 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, 
   a.o = o;
   a.lse = lse;
   a.workspace = need > 0 ? workspace : nullptr;
+  a.lay = dense_layout(H, Nq, Nk, d);
   a.H = (int)H;
   a.BH = (int)(B * H);
   a.Nq = (int)Nq;
@@ -325,6 +341,72 @@ int64_t fa_probe_mfma_bf16(int64_t workgroups, int64_t iters, void* stream) {
   if (workgroups < 1 || workgroups > kMaxWorkgroups || iters < 1 || iters > INT32_MAX) return -FA_ERR_SHAPE;
   if (fa::launch_mfma_peak((int)workgroups, (int)iters, (hipStream_t)stream) != hipSuccess) return -FA_ERR_HIP;
   return workgroups * 4 * iters * 4 * 32768;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t fa_fwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t max_q, int64_t max_k, int64_t d,
+                                     int dtype) {
+  return fa_fwd_kvcache_workspace_bytes(B, H, max_q, max_k, d, dtype);
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                  int64_t B, int64_t H, int64_t total_q, int64_t total_k, int64_t max_q, int64_t max_k,
+                  int64_t d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !o || !lse) return FA_ERR_NULL;
+  int st = check_kv_shape(B, H, max_q, max_k, d);
+  if (st != FA_OK) return st;
+  if (total_q < 1 || total_k < 1 || total_q > INT32_MAX || total_k > INT32_MAX) return FA_ERR_SHAPE;
+  // one sequence's rows must stay within 32-bit byte offsets of its first row
+  if (max_q * H * d * 2 >= (int64_t(1) << 31) || max_k * H * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return FA_ERR_ALIGN;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  const size_t need = fa::kv_workspace_bytes(B * H, max_q, max_k, d);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  }
+  fa::KvArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.seqlens = nullptr;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = need > 0 ? workspace : nullptr;
+  fa::KvLayout l{};
+  l.q_sb = 0;  // packed [total, H, d]: sequence b starts at row cu[b]
+  l.q_sh = d;
+  l.q_sr = H * d;
+  l.c_sb = 0;
+  l.c_sh = d;
+  l.c_sr = H * d;
+  l.l_sb = 0;  // [H, total_q]
+  l.l_sh = total_q;
+  l.cu_q = cu_seqlens_q;
+  l.cu_k = cu_seqlens_k;
+  l.total_q = total_q;
+  l.total_k = total_k;
+  a.lay = l;
+  a.H = (int)H;
+  a.BH = (int)(B * H);
+  a.Nq = (int)max_q;
+  a.Nk = (int)max_k;
+  a.d = (int)d;
+  a.c = exp2_factor(scale);
+  a.v_scale = 1.0f;
+  a.fp8_cache = 0;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.stream = (hipStream_t)stream;
+  return status_of(fa::launch_fwd_kvcache(a));
 }
 
 }  // extern "C"

@@ -337,10 +337,10 @@ __device__ inline bool wave_uniform(bool x) { return __builtin_amdgcn_readfirstl
 // 64 / (D / 8) rows per instruction) instead of 8-byte pieces of 32 rows.
 // lds: this wavefront's scratch, 32 rows of 2 D bytes, 16-byte chunk c of
 // row r at chunk position c ^ (r % (D / 8)); rows at and past nrows are not
-// stored.
+// stored; row r goes to dst + r * row_stride (elements).
 template <int D>
 __device__ inline void store_tile_rows(char* lds, const u32x2_t (&v)[D / 32][4], uint16_t* dst, int nrows,
-                                       int lane) {
+                                       int lane, size_t row_stride = D) {
   constexpr int RS = 2 * D;
   constexpr int CPR = D / 8;     // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;  // rows per store instruction
@@ -358,7 +358,7 @@ __device__ inline void store_tile_rows(char* lds, const u32x2_t (&v)[D / 32][4],
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = RPI * i + lane / CPR, ch = lane % CPR;
     const u32x4_t x = *(const u32x4_t*)(lds + r * RS + (ch ^ (r % CPR)) * 16);
-    if (r < nrows) *(u32x4_t*)(dst + (size_t)r * D + 8 * ch) = x;
+    if (r < nrows) *(u32x4_t*)(dst + (size_t)r * row_stride + 8 * ch) = x;
   }
 }
 // bytes of LDS scratch per wavefront for store_tile_rows

@@ -54,12 +54,11 @@ template <class TR, int D, bool CAUSAL, bool DIRECT, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kv_split_kernel(
     const uint16_t* __restrict__ Q, const void* __restrict__ K, const void* __restrict__ V,
     const int32_t* __restrict__ seqlens, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    float* __restrict__ part_o, float* __restrict__ part_l, int H, int BH, int Nq, int Nk, int n_qb,
-    int n_splits, int kps, uint32_t n_waves, float c, float v_scale) {
+    float* __restrict__ part_o, float* __restrict__ part_l, KvLayout lay, int H, int BH, int Nq, int Nk,
+    int n_qb, int n_splits, int kps, uint32_t n_waves, float c, float v_scale) {
   constexpr int NKS = D / 16;          // k-steps of S^T = K Q^T
   constexpr int NDB = D / 32;          // 32-row blocks of O^T
-  constexpr uint32_t RB = 2 * D;       // global row bytes of Q
-  constexpr uint32_t RBC = F8 ? D : 2 * D;  // global row bytes of the cache
+  constexpr uint32_t RBC = F8 ? D : 2 * D;  // bytes of one cache row's d elements
   constexpr int RS = 2 * D + 64;       // LDS row bytes of the V tile: a stride of 16 (mod 64)
                                        // dwords puts the 4 rows of a transposed read in 4 bank groups
   constexpr int RSK = 2 * D + 16;      // LDS row bytes of the K tile: a stride of 4 (mod 64) dwords
@@ -82,31 +81,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int qb = (int)(wid % (uint32_t)n_qb);
   const int split = (int)((wid / (uint32_t)n_qb) % (uint32_t)n_splits);
   const int bh = (int)(wid / ((uint32_t)n_qb * (uint32_t)n_splits));
-  int L = seqlens ? seqlens[bh / H] : Nk;
-  L = __builtin_amdgcn_readfirstlane(min(max(L, 0), Nk));
+  const int b = bh / H, hd = bh % H;
+  // this sequence's queries (start qs, count Lq) and cache rows (start ks0, count L)
+  int qs = 0, Lq = Nq, ks0 = 0, L;
+  if (lay.cu_q) {
+    qs = (int)min(max((int64_t)lay.cu_q[b], (int64_t)0), lay.total_q);
+    Lq = (int)min(max((int64_t)lay.cu_q[b + 1] - qs, (int64_t)0), min((int64_t)Nq, lay.total_q - qs));
+  }
+  if (lay.cu_k) {
+    ks0 = (int)min(max((int64_t)lay.cu_k[b], (int64_t)0), lay.total_k);
+    L = (int)min(max((int64_t)lay.cu_k[b + 1] - ks0, (int64_t)0), min((int64_t)Nk, lay.total_k - ks0));
+  } else {
+    L = seqlens ? min(max(seqlens[b], 0), Nk) : Nk;
+  }
+  qs = __builtin_amdgcn_readfirstlane(qs);
+  Lq = __builtin_amdgcn_readfirstlane(Lq);
+  ks0 = __builtin_amdgcn_readfirstlane(ks0);
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int q0 = 32 * qb;
+  if (q0 >= Lq) return;  // no query of this sequence in this block
   char* lds = smem + w * 32 * (RS + RSK);  // V rows, then K rows
   char* ldk = lds + 32 * RS;
 
-  const int q0 = 32 * qb;
-  const int qi = q0 + l32;  // this lane's query (rows past Nq read as zeros, never stored)
+  const int qi = q0 + l32;  // this lane's query (rows past Lq read as zeros, never stored)
   // last visible key of this lane's query, and of the block's last real query
-  const int lim = CAUSAL ? min(L - 1, qi + L - Nq) : L - 1;
-  const int lim_blk = CAUSAL ? min(L - 1, min(q0 + 31, Nq - 1) + L - Nq) : L - 1;
+  const int lim = CAUSAL ? min(L - 1, qi + L - Lq) : L - 1;
+  const int lim_blk = CAUSAL ? min(L - 1, min(q0 + 31, Lq - 1) + L - Lq) : L - 1;
   const int kb = split * kps;
   const int ke = min(kb + kps, lim_blk + 1);
 
   // Q rows of this block as B operands (column = query)
+  const uint32_t rsq = (uint32_t)lay.q_sr * 2;             // bytes between query rows
+  const uint32_t rsc = (uint32_t)lay.c_sr * (F8 ? 1 : 2);  // bytes between cache rows
+  const size_t q_head = (size_t)(b * lay.q_sb + hd * lay.q_sh + qs * lay.q_sr);  // elements
   u32x4_t qf[NKS];
   {
-    const rsrc_t qres = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * RB);
-    const uint32_t off = (uint32_t)qi * RB + 16 * h;
+    const rsrc_t qres = make_rsrc(Q + q_head, Lq > 0 ? (uint32_t)(Lq - 1) * rsq + 2 * D : 0u);
+    const uint32_t off = (uint32_t)qi * rsq + 16 * h;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(qres, off + 32 * ks);
   }
   // the cache of this head up to the filled length: rows at and past L read as zeros
-  const size_t cache_head = (size_t)bh * Nk * RBC;  // bytes
-  const rsrc_t kres = make_rsrc((const char*)K + cache_head, (uint32_t)L * RBC);
-  const rsrc_t vres = make_rsrc((const char*)V + cache_head, (uint32_t)L * RBC);
+  const size_t cache_head = (size_t)(b * lay.c_sb + hd * lay.c_sh + ks0 * lay.c_sr) * (F8 ? 1 : 2);  // bytes
+  const uint32_t cache_bytes = L > 0 ? (uint32_t)(L - 1) * rsc + RBC : 0u;
+  const rsrc_t kres = make_rsrc((const char*)K + cache_head, cache_bytes);
+  const rsrc_t vres = make_rsrc((const char*)V + cache_head, cache_bytes);
   const int k_row = kv_tile_key(l32) * RSK + 16 * h;  // A operand of K: row read from LDS
   // transposed-read address of this lane: group G = lane / 16 reads columns
   // 16 (G % 2) + 0..15 of rows 8 h + 0..3 (and + 4), lane 4 e + i of the group
@@ -139,14 +158,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int ch = 64 * i + lane;
-      dst[i] = buf_load16(kres, (uint32_t)k0 * RBC + (uint32_t)(ch / VCH) * RBC + 16 * (ch % VCH));
+      dst[i] = buf_load16(kres, (uint32_t)(k0 + ch / VCH) * rsc + 16 * (ch % VCH));
     }
   };
   auto load_v = [&](u32x4_t (&dst)[NVL], int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int ch = 64 * i + lane;
-      dst[i] = buf_load16(vres, (uint32_t)k0 * RBC + (uint32_t)(ch / VCH) * RBC + 16 * (ch % VCH));
+      dst[i] = buf_load16(vres, (uint32_t)(k0 + ch / VCH) * rsc + 16 * (ch % VCH));
     }
   };
   // chunk x (16 bytes of a cache row) -> its row's LDS position: as is, or
@@ -283,10 +302,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    store_tile_rows<D>(lds, ov, O + ((size_t)bh * Nq + q0) * D, min(32, Nq - q0), lane);
-    if (h == 0 && qi < Nq) LSE[(size_t)bh * Nq + qi] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+    store_tile_rows<D>(lds, ov, O + q_head + (size_t)q0 * lay.q_sr, min(32, Lq - q0), lane, (size_t)lay.q_sr);
+    if (h == 0 && qi < Lq)
+      LSE[b * lay.l_sb + hd * lay.l_sh + qs + qi] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
   } else {
-    if (qi < Nq) {
+    if (qi < Lq) {
       const size_t rec = ((size_t)split * BH + bh) * Nq + qi;
       float* po = part_o + rec * D;
 #pragma unroll
@@ -315,12 +335,21 @@ template <class TR, int D>
 __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__ part_o,
                                                        const float* __restrict__ part_l,
                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
-                                                       int rows, int n_splits) {
+                                                       KvLayout lay, int H, int Nq, int rows, int n_splits) {
   constexpr int PER = D / 64;  // columns per lane
   constexpr int UNR = 16;      // ranges whose rows are loaded before their use
   const int lane = threadIdx.x & 63;
   const int row = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (row >= rows) return;
+  // row = (batch * H + head) * Nq + query; queries past the sequence's own
+  // count have no partial results and no output
+  const int bh = row / Nq, qi = row % Nq, b = bh / H, hd = bh % H;
+  int qs = 0, Lq = Nq;
+  if (lay.cu_q) {
+    qs = (int)min(max((int64_t)lay.cu_q[b], (int64_t)0), lay.total_q);
+    Lq = (int)min(max((int64_t)lay.cu_q[b + 1] - qs, (int64_t)0), min((int64_t)Nq, lay.total_q - qs));
+  }
+  if (qi >= __builtin_amdgcn_readfirstlane(Lq)) return;
   float mt = -INFINITY, ml = -INFINITY;
   for (int s = lane; s < n_splits; s += 64) {
     const float2 v = *(const float2*)(part_l + 2 * ((size_t)s * rows + row));
@@ -373,13 +402,13 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__
     }
   }
   const float inv = empty ? 0.0f : 1.0f / ws;
-  uint16_t* orow = O + (size_t)row * D + PER * lane;
+  uint16_t* orow = O + (size_t)(b * lay.q_sb + hd * lay.q_sh + (qs + qi) * lay.q_sr) + PER * lane;
   if constexpr (PER == 2) {
     *(uint32_t*)orow = TR::pack2(acc[0] * inv, acc[1] * inv);
   } else {
     *orow = (uint16_t)(TR::pack2(acc[0] * inv, 0.0f) & 0xFFFFu);
   }
-  if (lane == 0) LSE[row] = empty ? -INFINITY : (ml + __log2f(ls)) * kLn2;
+  if (lane == 0) LSE[b * lay.l_sb + hd * lay.l_sh + qs + qi] = empty ? -INFINITY : (ml + __log2f(ls)) * kLn2;
 }
 
 // ------------------------------------------------------------------ launch
@@ -393,19 +422,19 @@ static hipError_t launch_kv(const KvArgs& a, const KvPlan& p) {
   if (p.n_splits == 1) {
     hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, true, F8>), dim3(n_wg), dim3(256), 0, a.stream,
                        (const uint16_t*)a.q, a.k, a.v, a.seqlens,
-                       (uint16_t*)a.o, a.lse, nullptr, nullptr, a.H, a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits,
+                       (uint16_t*)a.o, a.lse, nullptr, nullptr, a.lay, a.H, a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits,
                        p.kps, n_waves, a.c, a.v_scale);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, false, F8>), dim3(n_wg), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, a.k, a.v, a.seqlens, nullptr,
-                     nullptr, part_o, part_l, a.H, a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits, p.kps, n_waves,
+                     nullptr, part_o, part_l, a.lay, a.H, a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits, p.kps, n_waves,
                      a.c, a.v_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = a.BH * a.Nq;
   hipLaunchKernelGGL((kv_merge_kernel<TR, D>), dim3((rows + 3) / 4), dim3(256), 0, a.stream, part_o, part_l,
-                     (uint16_t*)a.o, a.lse, rows, p.n_splits);
+                     (uint16_t*)a.o, a.lse, a.lay, a.H, a.Nq, rows, p.n_splits);
   return hipGetLastError();
 }
 

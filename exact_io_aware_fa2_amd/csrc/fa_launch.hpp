@@ -52,7 +52,23 @@ struct BwdArgs {
 
 enum BwdStage { BWD_PREP = 0, BWD_DKDV = 1, BWD_DQ = 2 };
 
-// Queries against a key/value cache (fa_fwd_kvcache).
+// Where the rows of sequence b, head h lie (element offsets): row r of q/o at
+// b q_sb + h q_sh + (start_q(b) + r) q_sr, row j of the cache (k/v) at
+// b c_sb + h c_sh + (start_k(b) + j) c_sr, and the LSE of query r at
+// b l_sb + h l_sh + start_q(b) + r.  Without prefix sums every sequence
+// starts at row 0 and has Nq queries and Nk (or seqlens[b]) cache rows; with
+// them, sequence b has rows cu[b] .. cu[b + 1] - 1 of a packed tensor of
+// total rows (the kernels clamp both into [0, total]).
+struct KvLayout {
+  int64_t q_sb, q_sh, q_sr;
+  int64_t c_sb, c_sh, c_sr;
+  int64_t l_sb, l_sh;
+  const int32_t* cu_q;  // [B + 1] or NULL
+  const int32_t* cu_k;  // [B + 1] or NULL
+  int64_t total_q, total_k;
+};
+
+// Queries against a key/value cache (fa_fwd_kvcache, fa_fwd_varlen).
 struct KvArgs {
   const void* q;           // [BH, Nq, d]
   const void* k;           // [BH, Nk, d] cache (capacity Nk rows)
@@ -61,10 +77,11 @@ struct KvArgs {
   void* o;                 // [BH, Nq, d]
   float* lse;              // [BH, Nq]
   void* workspace;         // kv_workspace_bytes() bytes (NULL when that is 0)
+  KvLayout lay;
   int H;
   int BH;
-  int Nq;
-  int Nk;
+  int Nq;                  // queries per sequence (the largest, with prefix sums)
+  int Nk;                  // cache rows per sequence (the largest, with prefix sums)
   int d;
   float c;                 // scale * log2(e) (times the K scale of an 8-bit cache)
   float v_scale;           // multiplies O: the V scale of an 8-bit cache, else 1

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum {
   FA_OK = 0,
@@ -184,6 +184,37 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, 
                        float v_scale, const int32_t* seqlens_k, void* o, float* lse, void* workspace,
                        size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                        float scale, int causal, int dtype, void* stream);
+
+/* Variable-length packed batch: B sequences of different lengths stored
+ * back to back, as training on packed sequences and serving batches of
+ * prompts lay them out (the pages' drop-in use with the usual attention
+ * interfaces: "FlashAttention-2 (DE)", "Anwendung und Integration in das
+ * Ökosystem").  Sequence b owns rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ * of q and o, and rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v;
+ * within it, attention is that of fa_fwd_kvcache with Nq = its query count
+ * and L = its key count (causal: key j visible to query i iff
+ * j <= i + L - Nq, bottom-right aligned; equal lengths give fa_fwd's mask).
+ *   q, o          [total_q, H, d] of type dtype (FA_BF16 or FA_F16), packed
+ *                 rows; o rows outside every sequence are left unchanged.
+ *   k, v          [total_k, H, d], same type.
+ *   cu_seqlens_q, DEVICE int32 [B + 1] non-decreasing prefix sums (4-byte
+ *   cu_seqlens_k  aligned); entries are clamped to [0, total], a sequence's
+ *                 counts to [0, max_q] and [0, max_k].
+ *   lse           [H, total_q] float32 (natural log; -infinity and o = 0 for
+ *                 a query that sees no key).
+ *   max_q, max_k  the largest query and key count of any sequence, in
+ *                 [1, 2^22]; max * H * d * 2 must stay below 2^31 bytes.
+ *   workspace     fa_fwd_varlen_workspace_bytes(B, H, max_q, max_k, d, dtype)
+ *                 bytes (16-byte aligned, may be NULL when that is 0).
+ * Errors as for fa_fwd_kvcache (FA_ERR_NULL also for NULL prefix sums,
+ * FA_ERR_SHAPE for total_q or total_k < 1 or the offset limit). */
+size_t fa_fwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t max_q, int64_t max_k, int64_t d,
+                                     int dtype);
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                  int64_t B, int64_t H, int64_t total_q, int64_t total_k, int64_t max_q, int64_t max_k,
+                  int64_t d, float scale, int causal, int dtype, void* stream);
 
 /* Measurement probe, not part of attention: enqueues a kernel of `workgroups`
  * workgroups (4 wavefronts each) in which every wavefront issues `iters`

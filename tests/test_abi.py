@@ -35,13 +35,14 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
          "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kvcache_workspace_bytes",
-         "fa_fwd_kvcache", "fa_fwd_kvcache_fp8", "fa_probe_mfma_bf16"])
+         "fa_fwd_kvcache", "fa_fwd_kvcache_fp8", "fa_probe_mfma_bf16", "fa_fwd_varlen_workspace_bytes",
+         "fa_fwd_varlen"])
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 3
+    assert lib.fa_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -205,3 +206,28 @@ def test_probe_argument_errors(lib):
     assert lib.fa_probe_mfma_bf16(0, 10, None) == -FA_ERR_SHAPE
     assert lib.fa_probe_mfma_bf16(10, 0, None) == -FA_ERR_SHAPE
     assert lib.fa_probe_mfma_bf16(1 << 24, 10, None) == -FA_ERR_SHAPE
+
+
+def vl(lib, q=P[0], k=P[1], v=P[2], cq=P[8], ck=P[9], o=P[3], lse=P[4], ws=P[10], wsb=1 << 30, B=3, H=4,
+       tq=300, tk=500, mq=128, mk=256, d=128, scale=0.088, causal=1, dtype=2):
+    return lib.fa_fwd_varlen(q, k, v, cq, ck, o, lse, ws, wsb, B, H, tq, tk, mq, mk, d, scale, causal, dtype, None)
+
+
+def test_varlen_argument_errors(lib):
+    for name in ("q", "k", "v", "cq", "ck", "o", "lse"):
+        assert vl(lib, **{name: None}) == FA_ERR_NULL, name
+    assert vl(lib, B=0) == FA_ERR_SHAPE
+    assert vl(lib, tq=0) == FA_ERR_SHAPE
+    assert vl(lib, tk=0) == FA_ERR_SHAPE
+    assert vl(lib, mq=0) == FA_ERR_SHAPE
+    assert vl(lib, mk=(1 << 22) + 1) == FA_ERR_SHAPE
+    assert vl(lib, H=64, mk=1 << 17) == FA_ERR_SHAPE  # 2^17 * 64 * 128 * 2 = 2^31 bytes
+    assert vl(lib, d=80) == FA_ERR_HEADDIM
+    assert vl(lib, dtype=0) == FA_ERR_DTYPE
+    assert vl(lib, cq=P[8] + 2) == FA_ERR_ALIGN
+    assert vl(lib, o=P[3] + 8) == FA_ERR_ALIGN
+    assert vl(lib, scale=-1.0) == FA_ERR_SCALE
+    need = lib.fa_fwd_varlen_workspace_bytes(3, 4, 128, 256, 128, 2)
+    assert need == lib.fa_fwd_kvcache_workspace_bytes(3, 4, 128, 256, 128, 2) > 0
+    assert vl(lib, ws=None) == FA_ERR_WORKSPACE
+    assert vl(lib, wsb=need - 1) == FA_ERR_WORKSPACE

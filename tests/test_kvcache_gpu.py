@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import seeded_inputs as si
-from oracle import kvcache_fwd, kvcache_fwd_head
+from oracle import kvcache_fwd, kvcache_fwd_head, varlen_fwd
 from parity import TOL, lib, say, to_device
 
 pytestmark = pytest.mark.gpu
@@ -203,3 +203,95 @@ def test_fp8_decode_workload_full_size_sampled_heads():
         qo, ql = float(np.abs(o[b, h] - o16).max()), float(np.abs(lse[b, h] - l16).max())
         say(f"  quantisation error vs the 16-bit cache: O max-abs {qo:.3e}, LSE max-abs {ql:.3e}")
         assert qo < 0.05 and ql < 0.5  # sanity only: E4M3 keeps 3 mantissa bits
+
+
+# ------------------------------------------------------------ variable-length packed batches
+
+def _run_varlen(inp, dtype, causal, scale, max_q=None, max_k=None, o_init=None):
+    import torch
+    fa = lib()
+    q, k, v = (to_device(inp[n][1], dtype) for n in ("q", "k", "v"))
+    cq, ck = (torch.from_numpy(inp[n]).cuda() for n in ("cu_q", "cu_k"))
+    mq = int(np.diff(inp["cu_q"]).max()) if max_q is None else max_q
+    mk = int(np.diff(inp["cu_k"]).max()) if max_k is None else max_k
+    o = torch.zeros_like(q) if o_init is None else to_device(o_init, dtype)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
+    nb = int(fa.load_library().fa_fwd_varlen_workspace_bytes(len(inp["cu_q"]) - 1, q.shape[1], max(mq, 1),
+                                                                max(mk, 1), q.shape[2], fa.dtype_code(q)))
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
+    fa.fa_fwd_varlen(q, k, v, cq, ck, o, lse, ws, max(mq, 1), max(mk, 1), scale, causal)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+VARLEN = [  # query lengths, key lengths
+    ([1, 100, 0, 33, 257], [50, 100, 7, 33, 300]),  # decode row, square, empty, ragged, longer cache
+    ([64, 5, 200], [16, 500, 40]),                   # more queries than keys (empty causal rows)
+    ([1000, 1], [1000, 3000]),                       # one long sequence beside a decode step
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", range(len(VARLEN)))
+def test_varlen_small(case, causal, d, dtype):
+    lq, lk = VARLEN[case]
+    seed = 9000 + 17 * case + d
+    inp = si.make_varlen_inputs(lq, lk, 3, d, dtype, 1.0, seed)
+    scale = 1.0 / np.sqrt(d)
+    say(f"varlen lq={lq} lk={lk} H3 d{d} {dtype} causal={causal} seed={seed}")
+    o, lse = _run_varlen(inp, dtype, causal, scale)
+    o_ref, lse_ref = varlen_fwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["cu_q"], inp["cu_k"], scale, causal)
+    _check(o.transpose(1, 0, 2), lse, o_ref.transpose(1, 0, 2), lse_ref, dtype,
+           f"varlen case {case} d{d} {dtype} causal={causal}")
+
+
+def test_varlen_equal_lengths_equal_the_ordinary_forward():
+    """Equal lengths, packed: the same outputs as fa_fwd on the [B, H, N, d]
+    layout of the same values (different kernels, both against the oracle)."""
+    import torch
+    fa = lib()
+    B, H, N, d = 3, 4, 300, 128
+    inp = si.make_varlen_inputs([N] * B, [N] * B, H, d, "bf16", 1.0, 91)
+    o, lse = _run_varlen(inp, "bf16", True, 1 / np.sqrt(d))
+    dense = lambda x: np.ascontiguousarray(x.reshape(B, N, H, d).transpose(0, 2, 1, 3))
+    q, k, v = (to_device(dense(inp[n][1]), "bf16") for n in ("q", "k", "v"))
+    o2, lse2 = fa.fwd(q, k, v, True, 1 / np.sqrt(d))
+    torch.cuda.synchronize()
+    o2 = o2.float().cpu().numpy().transpose(0, 2, 1, 3).reshape(B * N, H, d)
+    lse2 = lse2.cpu().numpy().transpose(1, 0, 2).reshape(H, B * N)
+    o_ref, lse_ref = varlen_fwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["cu_q"], inp["cu_k"], 1 / np.sqrt(d), True)
+    t = lambda x: x.transpose(1, 0, 2)
+    _check(t(o), lse, t(o_ref), lse_ref, "bf16", "fa_fwd_varlen")
+    _check(t(o2), lse2, t(o_ref), lse_ref, "bf16", "fa_fwd on the same values")
+
+
+def test_varlen_rows_outside_the_sequences_are_left_unchanged():
+    inp = si.make_varlen_inputs([10, 20], [30, 20], 2, 64, "bf16", 1.0, 92)
+    tq = 30
+    inp["cu_q"] = np.array([0, 10, 25], np.int32)  # rows 25..29 belong to no sequence
+    sentinel = si.round_to(np.full((tq, 2, 64), 7.0, np.float32), "bf16")[1]
+    o, lse = _run_varlen(inp, "bf16", False, 0.125, max_q=20, max_k=30, o_init=sentinel)
+    assert np.all(o[25:] == 7.0)
+    o_ref, lse_ref = varlen_fwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["cu_q"], inp["cu_k"], 0.125, False)
+    _check(o[:25].transpose(1, 0, 2), lse[:, :25], o_ref[:25].transpose(1, 0, 2), lse_ref[:, :25], "bf16",
+           "partial cover")
+
+
+def test_varlen_one_range_per_head_direct_path_sampled():
+    """Many long sequences: every head's keys fit one range, so the split
+    kernel writes O and LSE itself (no merge); sampled heads against the oracle."""
+    fa = lib()
+    lq = lk = [4096, 4000, 4096, 3900]
+    H, d = 16, 128
+    assert fa.load_library().fa_fwd_varlen_workspace_bytes(4, H, 4096, 4096, d, fa.FA_BF16) == 0
+    inp = si.make_varlen_inputs(lq, lk, H, d, "bf16", 1.0, 93)
+    say("varlen direct path: 4 sequences of ~4096, H16 d128 causal")
+    o, lse = _run_varlen(inp, "bf16", True, 1 / np.sqrt(d))
+    cu = inp["cu_q"]
+    for b, h in [(0, 0), (1, 7), (3, 15)]:
+        qs = slice(cu[b], cu[b + 1])
+        rows = np.r_[0:256, lq[b] - 128:lq[b]]
+        of, lf = kvcache_fwd_head(inp["q"][0][qs, h], inp["k"][0][qs, h], inp["v"][0][qs, h], 1 / np.sqrt(d), True)
+        _check(o[qs, h][rows], lse[h, qs][rows], of[rows], lf[rows], "bf16", f"direct path seq {b} head {h}")
