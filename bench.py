@@ -19,6 +19,7 @@ Modes
   --workload D1         a decode step against a key/value cache instead (fa_fwd_kvcache,
                         B=4 H=32, one query, 32768-row cache, d=128): HBM GB/s;
                         D1f8: the same with an 8-bit E4M3 cache (fa_fwd_kvcache_fp8)
+  --varlen              fa_fwd_varlen on a packed batch of 16 ragged causal prefill sequences
   --fwd-only            fa_fwd alone: time, TFLOP/s and compulsory GB/s per workload
                         (--workload C1,C3,...; --workload short: the short-sequence sweep)
   --profile             3 warm-up + 20 timed steps (stages in order on one stream), no CPU
@@ -326,6 +327,48 @@ def bench_fwd_only(args, workloads):
         del q, k, v, o, lse, inp
 
 
+def bench_varlen(args):
+    """A packed variable-length prefill batch through fa_fwd_varlen: 16
+    sequences with lengths drawn uniformly in [512, 4096] (seed 1008), H=16,
+    d=128, bf16, causal (queries = keys per sequence).  TFLOP/s of the
+    per-sequence causal work, sum_b 2 H L_b^2 d, median of --steps calls."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_fa2_amd as fa
+    import seeded_inputs as si
+
+    rng = np.random.default_rng(1008)
+    lens = rng.integers(512, 4097, size=16).tolist()
+    H, d = 16, 128
+    inp = si.make_varlen_inputs(lens, lens, H, d, "bf16", 1.0, 1008)
+    dev = torch.device("cuda:0")
+    up = lambda n: torch.from_numpy(inp[n][1].view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = up("q"), up("k"), up("v")
+    cq, ck = (torch.from_numpy(inp[n]).to(dev) for n in ("cu_q", "cu_k"))
+    o = torch.empty_like(q)
+    lse = torch.empty((H, q.shape[0]), dtype=torch.float32, device=dev)
+    mx = max(lens)
+    nb = int(fa.load_library().fa_fwd_varlen_workspace_bytes(len(lens), H, mx, mx, d, fa.FA_BF16))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    call = lambda: fa.fa_fwd_varlen(q, k, v, cq, ck, o, lse, ws, mx, mx, 1 / np.sqrt(d), True)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    flop = sum(2.0 * H * L * L * d for L in lens)
+    print(json.dumps({"mode": "varlen prefill", "workload": f"16 packed sequences, lengths {lens}, H={H} d={d} bf16 causal",
+                      "median_us": round(ms * 1e3, 1), "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
+                      "frac_mfma_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_MFMA_16BIT, 4),
+                      "workspace_bytes": nb}), flush=True)
+
+
 def short_n_workloads():
     """Short sequences, small head dimension: B=16 H=16 d=64 bf16 non-causal,
     N = 128, 256, 512, 1024 (seed 1007); where the forward is closest to the
@@ -399,6 +442,8 @@ def main():
     ap.add_argument("--serial", action="store_true",
                     help="time the step with all stages in order on one stream (dQ not beside dK/dV)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--varlen", action="store_true",
+                    help="time fa_fwd_varlen on a packed batch of 16 ragged causal prefill sequences")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time fa_fwd alone on --workload (any of C1..C5, C3d64, C5d128; comma-separated), "
                          "or on the short-sequence sweep with --workload short")
@@ -419,6 +464,9 @@ def main():
     import seeded_inputs as si
 
     fa.load_library()
+    if args.varlen:
+        bench_varlen(args)
+        return
     if args.fwd_only:
         wls = short_n_workloads() if args.workload == "short" else [si.WORKLOADS[n] for n in args.workload.split(",")]
         bench_fwd_only(args, wls)
