@@ -199,7 +199,9 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, 
  *   k, v          [total_k, H, d], same type.
  *   cu_seqlens_q, DEVICE int32 [B + 1] non-decreasing prefix sums (4-byte
  *   cu_seqlens_k  aligned); entries are clamped to [0, total], a sequence's
- *                 counts to [0, max_q] and [0, max_k].
+ *                 counts to [0, max_q] and [0, max_k], so malformed sums
+ *                 never make an access leave the tensors (rows two
+ *                 sequences claim then hold unspecified values).
  *   lse           [H, total_q] float32 (natural log; -infinity and o = 0 for
  *                 a query that sees no key).
  *   max_q, max_k  the largest query and key count of any sequence, in

@@ -295,3 +295,19 @@ def test_varlen_one_range_per_head_direct_path_sampled():
         rows = np.r_[0:256, lq[b] - 128:lq[b]]
         of, lf = kvcache_fwd_head(inp["q"][0][qs, h], inp["k"][0][qs, h], inp["v"][0][qs, h], 1 / np.sqrt(d), True)
         _check(o[qs, h][rows], lse[h, qs][rows], of[rows], lf[rows], "bf16", f"direct path seq {b} head {h}")
+
+
+def test_varlen_malformed_prefix_sums_stay_in_bounds():
+    """Prefix sums that decrease or pass the end are clamped by the kernels
+    (no access leaves the tensors); rows only a well-formed sequence covers
+    are still exact.  Here sequence 1 has a negative count (skipped) and
+    sequence 2 runs past total_q (cut at the end)."""
+    lq = [50, 0, 70]
+    inp = si.make_varlen_inputs(lq, [60, 10, 80], 2, 128, "bf16", 1.0, 94)
+    inp["cu_q"] = np.array([0, 50, 30, 100000], np.int32)  # total_q = 120
+    say(f"varlen malformed cu_q {inp['cu_q'].tolist()}")
+    o, lse = _run_varlen(inp, "bf16", True, 0.088, max_q=128, max_k=80)
+    assert np.isfinite(o).all()
+    # rows 0..29 belong to sequence 0 only (sequence 2 starts at row 30)
+    of, lf = kvcache_fwd_head(inp["q"][0][0:50, 1], inp["k"][0][0:60, 1], inp["v"][0][0:60, 1], 0.088, True)
+    _check(o[0:30, 1], lse[1, 0:30], of[0:30], lf[0:30], "bf16", "sequence 0 rows")
