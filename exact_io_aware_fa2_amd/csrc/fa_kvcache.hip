@@ -28,9 +28,13 @@
 // computes S^T = K Q^T with the A operands read back row-wise, and
 // O^T += V^T P~^T with V read back transposed (ds_read_b64_tr_b16).  Loading
 // the A operands of K straight from memory (32 rows touched per instruction)
-// measured 5-10% slower.  No workgroup barrier is used: the four wavefronts of
-// a workgroup are independent, and consecutive wavefronts take consecutive
-// ranges (no reuse between them, so no XCD grouping).
+// measured 5-10% slower.  With few query blocks (decoding) the four
+// wavefronts of a workgroup are independent, each staging its own tiles (no
+// workgroup barrier); consecutive wavefronts take consecutive ranges (no
+// reuse between them, so no XCD grouping).  With four or more query blocks
+// per head (prefill, packed batches) a workgroup's wavefronts take four
+// consecutive blocks of one range and stage each tile once for all four
+// (GRP below; 12% faster on a packed prefill batch).
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -50,7 +54,13 @@ __device__ inline int kv_tile_key(int m) { return (m & ~12) | ((m & 4) << 1) | (
 // query's 16-bit type (exactly: every E4M3 value is a bf16 and an fp16 value)
 // as they are written to LDS, so the products and everything after them are
 // those of the 16-bit cache.
-template <class TR, int D, bool CAUSAL, bool DIRECT, bool F8>
+//
+// GRP (many queries, 16-bit cache): a workgroup takes four consecutive query
+// blocks of one (head, key range) instead of four independent ones, and its
+// wavefronts stage each K and V tile once for all four (every thread loads
+// and writes a quarter of it, two LDS buffers, one workgroup barrier per
+// tile), instead of each wavefront staging its own copy.
+template <class TR, int D, bool CAUSAL, bool DIRECT, bool F8, bool GRP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kv_split_kernel(
     const uint16_t* __restrict__ Q, const void* __restrict__ K, const void* __restrict__ V,
     const int32_t* __restrict__ seqlens, uint16_t* __restrict__ O, float* __restrict__ LSE,
@@ -67,7 +77,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   constexpr int NVL = 32 * VCH / 64;   // chunks per lane per tile and tensor
   constexpr int EPC = F8 ? 16 : 8;     // elements per chunk
   static_assert(32 * RS >= kTileRowsBytes<D>, "the output tile fits the V rows");
-  __shared__ __attribute__((aligned(16))) char smem[4 * 32 * (RS + RSK)];
+  static_assert(!(GRP && F8), "shared staging is for the 16-bit cache");
+  constexpr int BUF = 32 * (RS + RSK);  // one tile of V rows, then K rows
+  static_assert(!GRP || 2 * BUF >= 4 * kTileRowsBytes<D>, "four output tiles fit the two buffers");
+  __shared__ __attribute__((aligned(16))) char smem[(GRP ? 2 : 4) * BUF];
 
   const int lane = threadIdx.x & 63;
   // wave-uniform values are made visibly uniform (readfirstlane), so that the
@@ -76,11 +89,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int h = lane >> 5;
   const int l32 = lane & 31;
   // wavefront -> (head, key range, query block), query block fastest
-  const uint32_t wid = 4 * blockIdx.x + (uint32_t)w;
-  if (wid >= n_waves) return;
-  const int qb = (int)(wid % (uint32_t)n_qb);
-  const int split = (int)((wid / (uint32_t)n_qb) % (uint32_t)n_splits);
-  const int bh = (int)(wid / ((uint32_t)n_qb * (uint32_t)n_splits));
+  int qb, split, bh;
+  if constexpr (GRP) {
+    const uint32_t n_qg = ((uint32_t)n_qb + 3) / 4;  // groups of four query blocks
+    const uint32_t g = blockIdx.x;
+    qb = (int)(4 * (g % n_qg)) + w;
+    split = (int)((g / n_qg) % (uint32_t)n_splits);
+    bh = (int)(g / (n_qg * (uint32_t)n_splits));
+  } else {
+    const uint32_t wid = 4 * blockIdx.x + (uint32_t)w;
+    if (wid >= n_waves) return;
+    qb = (int)(wid % (uint32_t)n_qb);
+    split = (int)((wid / (uint32_t)n_qb) % (uint32_t)n_splits);
+    bh = (int)(wid / ((uint32_t)n_qb * (uint32_t)n_splits));
+  }
   const int b = bh / H, hd = bh % H;
   // this sequence's queries (start qs, count Lq) and cache rows (start ks0, count L)
   int qs = 0, Lq = Nq, ks0 = 0, L;
@@ -99,14 +121,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   ks0 = __builtin_amdgcn_readfirstlane(ks0);
   L = __builtin_amdgcn_readfirstlane(L);
   const int q0 = 32 * qb;
-  if (q0 >= Lq) return;  // no query of this sequence in this block
-  char* lds = smem + w * 32 * (RS + RSK);  // V rows, then K rows
+  // no query of this sequence in this block (GRP: in the workgroup's four
+  // blocks; a wavefront of a later, empty block still stages and waits)
+  if ((GRP ? q0 - 32 * w : q0) >= Lq) return;
+  char* lds = smem + w * BUF;  // (per wavefront) V rows, then K rows
   char* ldk = lds + 32 * RS;
 
   const int qi = q0 + l32;  // this lane's query (rows past Lq read as zeros, never stored)
   // last visible key of this lane's query, and of the block's last real query
   const int lim = CAUSAL ? min(L - 1, qi + L - Lq) : L - 1;
-  const int lim_blk = CAUSAL ? min(L - 1, min(q0 + 31, Lq - 1) + L - Lq) : L - 1;
+  const int q_last = GRP ? q0 - 32 * w + 127 : q0 + 31;  // last query of the block (GRP: group)
+  const int lim_blk = CAUSAL ? min(L - 1, min(q_last, Lq - 1) + L - Lq) : L - 1;
   const int kb = split * kps;
   const int ke = min(kb + kps, lim_blk + 1);
 
@@ -139,33 +164,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = zero16();
 
-  // K and V are loaded DEPTH tiles ahead: the loads of tile i + DEPTH go into
-  // the registers tile i has just written to LDS (K right after its K rows are
-  // in LDS, V right after its V rows), so DEPTH tiles' loads are in flight
-  // while a tile is computed.  One tile ahead is used: two (in the registers
-  // of one 16-bit tile for the 8-bit cache, or at a wavefront per SIMD less
-  // for the 16-bit cache at d = 64) measured no faster, and the 8-bit cache
-  // then fetched 5% more than its compulsory bytes.  The loads are issued for
-  // every tile (past the range a tile reloads itself, an L2 hit, and the
-  // extra tiles of a last group of DEPTH are fully masked), so that the wait
-  // counts are the same on every path and no wait for one tile's data also
-  // waits for a later tile's.  Chunk i of a lane is 16-byte chunk
-  // (64 i + lane) % VCH of row (64 i + lane) / VCH of the tile (VCH chunks
-  // per cache row).
-  constexpr int DEPTH = 1;
-  u32x4_t kc[DEPTH][NVL], vv[DEPTH][NVL];
-  auto load_k = [&](u32x4_t (&dst)[NVL], int k0) __attribute__((always_inline)) {
+  // K and V are loaded one tile ahead: the loads of tile i + 1 go into the
+  // registers tile i has just written to LDS (K right after its K rows are in
+  // LDS, V right after its V rows), so one tile's loads are in flight while a
+  // tile is computed.  (Two tiles ahead -- in the registers of one 16-bit
+  // tile for the 8-bit cache, or at a wavefront per SIMD less for the 16-bit
+  // cache at d = 64 -- measured no faster, and the 8-bit cache then fetched
+  // 5% more than its compulsory bytes.)  The loads are issued for every tile
+  // (the last one reloads itself, an L2 hit), so that the wait counts are the
+  // same on every path and no wait for one tile's data also waits for the
+  // next tile's.  Chunk i of a thread is 16-byte chunk x % VCH of row
+  // x / VCH of the tile (VCH chunks per cache row), x = 64 i + lane for a
+  // wavefront's own staging, x = 256 i + thread for the workgroup's (GRP).
+  constexpr int NCH = GRP ? 32 * VCH / 256 : NVL;  // chunks per thread and tensor
+  static_assert(NCH >= 1, "every thread stages at least one chunk");
+  const int tid_s = GRP ? (int)threadIdx.x : lane;
+  constexpr int CST = GRP ? 256 : 64;
+  u32x4_t kc[NCH], vv[NCH];
+  auto load_k = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      const int ch = 64 * i + lane;
-      dst[i] = buf_load16(kres, (uint32_t)(k0 + ch / VCH) * rsc + 16 * (ch % VCH));
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = CST * i + tid_s;
+      kc[i] = buf_load16(kres, (uint32_t)(k0 + ch / VCH) * rsc + 16 * (ch % VCH));
     }
   };
-  auto load_v = [&](u32x4_t (&dst)[NVL], int k0) __attribute__((always_inline)) {
+  auto load_v = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      const int ch = 64 * i + lane;
-      dst[i] = buf_load16(vres, (uint32_t)(k0 + ch / VCH) * rsc + 16 * (ch % VCH));
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = CST * i + tid_s;
+      vv[i] = buf_load16(vres, (uint32_t)(k0 + ch / VCH) * rsc + 16 * (ch % VCH));
     }
   };
   // chunk x (16 bytes of a cache row) -> its row's LDS position: as is, or
@@ -186,39 +213,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       *(u32x4_t*)dst = x;
     }
   };
-  // keys of this range visible to this lane's query (the last group of DEPTH
-  // tiles may reach past the range: those keys are masked here)
+  // keys of this range visible to this lane's query
   const int lim_r = min(lim, ke - 1);
   if (kb < ke) {
-    // K before V, tile by tile: a wait for one tile's K then leaves its V and
-    // every later tile in flight, on entry as on the back edge
-#pragma unroll
-    for (int t = 0; t < DEPTH; ++t) {
-      const int kt = kb + 32 * t < ke ? kb + 32 * t : kb;
-      load_k(kc[t], kt);
-      __builtin_amdgcn_sched_barrier(0);
-      load_v(vv[t], kt);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    // K before V: the wait for a tile's K leaves its V in flight, on entry as
+    // on the back edge
+    load_k(kb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(kb);
   }
-
-  // one 32-key tile starting at key k0, its chunks in registers kcs, vvs,
-  // which then receive the tile starting at key kn
-  auto tile = [&](u32x4_t (&kcs)[NVL], u32x4_t (&vvs)[NVL], int k0, int kn) __attribute__((always_inline)) {
-    // K tile -> LDS (the previous tile's operand reads are done: they fed
-    // its S products, which come before its V writes and their fence)
-#pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      const int ch = 64 * i + lane;
-      put(ldk + (ch / VCH) * RSK + 2 * EPC * (ch % VCH), kcs[i]);
-    }
-    load_k(kcs, kn);
+  auto wave_sync = []() __attribute__((always_inline)) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  };
+
+  // one 32-key tile starting at key k0, staged in bv (V rows) and bk (K rows);
+  // the staging registers then receive the tile starting at key kn
+  auto tile = [&](char* bv, char* bk, int k0, int kn) __attribute__((always_inline)) {
+    // K rows -> LDS.  Own staging: the previous tile's operand reads are done
+    // (they fed its S products, which come before its V writes and their
+    // fence).  GRP: this buffer was last read two tiles ago, before the
+    // previous tile's barrier.
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = CST * i + tid_s;
+      put(bk + (ch / VCH) * RSK + 2 * EPC * (ch % VCH), kc[i]);
+    }
+    load_k(kn);
+    if constexpr (GRP) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int ch = CST * i + tid_s;
+        put(bv + (ch / VCH) * RS + 2 * EPC * (ch % VCH), vv[i]);
+      }
+      load_v(kn);
+      lds_barrier();  // the whole tile is in LDS
+    } else {
+      wave_sync();
+    }
     u32x4_t kf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) kf[ks] = *(const u32x4_t*)(ldk + k_row + 32 * ks);
+    for (int ks = 0; ks < NKS; ++ks) kf[ks] = *(const u32x4_t*)(bk + k_row + 32 * ks);
     f32x16_t s = zero16();
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) s = TR::mfma(kf[ks], qf[ks], s);
@@ -256,35 +292,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         lt = TR::sum2(pk[t][j], lt);
       }
 
-    // V tile -> this wavefront's LDS rows (after the previous tile's reads)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    if constexpr (!GRP) {
+      // V rows -> this wavefront's LDS (after the previous tile's reads)
+      wave_sync();
 #pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      const int ch = 64 * i + lane;
-      put(lds + (ch / VCH) * RS + 2 * EPC * (ch % VCH), vvs[i]);
+      for (int i = 0; i < NCH; ++i) {
+        const int ch = CST * i + tid_s;
+        put(bv + (ch / VCH) * RS + 2 * EPC * (ch % VCH), vv[i]);
+      }
+      load_v(kn);
+      wave_sync();
     }
-    load_v(vvs, kn);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const char* p = lds + tr_base + 16 * t * RS + 64 * db;
+        const char* p = bv + tr_base + 16 * t * RS + 64 * db;
         const u32x2_t a = lds_read_tr(p), b2 = lds_read_tr(p + 4 * RS);
         acc[db] = TR::mfma(u32x4_t{a[0], a[1], b2[0], b2[1]}, pk[t], acc[db]);
       }
   };
-  for (int k0 = kb; k0 < ke; k0 += 32 * DEPTH) {
-    static_for<0, DEPTH>([&](auto tc) __attribute__((always_inline)) {
-      constexpr int t = decltype(tc)::value;
-      const int kt = k0 + 32 * t;
-      const int kn = kt + 32 * DEPTH < ke ? kt + 32 * DEPTH : kt;
-      tile(kc[t], vv[t], kt, kn);
-    });
+  int it = 0;
+  for (int k0 = kb; k0 < ke; k0 += 32, ++it) {
+    const int kn = k0 + 32 < ke ? k0 + 32 : k0;
+    if constexpr (GRP) {
+      char* bv = smem + (it & 1) * BUF;
+      tile(bv, bv + 32 * RS, k0, kn);
+    } else {
+      tile(lds, ldk, k0, kn);
+    }
   }
   l += swap_halves(l);
   lt += swap_halves(lt);
@@ -299,10 +335,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       for (int g = 0; g < 4; ++g)
         ov[db][g] = u32x2_t{TR::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
                             TR::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    store_tile_rows<D>(lds, ov, O + q_head + (size_t)q0 * lay.q_sr, min(32, Lq - q0), lane, (size_t)lay.q_sr);
+    if constexpr (GRP) {
+      lds_barrier();  // every wavefront is done with the tiles; slice w of the buffers is its own
+      store_tile_rows<D>(smem + w * kTileRowsBytes<D>, ov, O + q_head + (size_t)q0 * lay.q_sr, min(32, Lq - q0),
+                         lane, (size_t)lay.q_sr);
+    } else {
+      wave_sync();
+      store_tile_rows<D>(lds, ov, O + q_head + (size_t)q0 * lay.q_sr, min(32, Lq - q0), lane, (size_t)lay.q_sr);
+    }
     if (h == 0 && qi < Lq)
       LSE[b * lay.l_sb + hd * lay.l_sh + qs + qi] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
   } else {
@@ -413,25 +453,37 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------ launch
 
+template <class TR, int D, bool CAUSAL, bool F8, bool GRP>
+static hipError_t launch_split(const KvArgs& a, const KvPlan& p, bool direct, float* part_o, float* part_l) {
+  const uint32_t n_waves = (uint32_t)((int64_t)a.BH * p.n_qb * p.n_splits);
+  const uint32_t n_wg = GRP ? (uint32_t)((int64_t)a.BH * p.n_splits * ((p.n_qb + 3) / 4)) : (n_waves + 3) / 4;
+  if (direct)
+    hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, true, F8, GRP>), dim3(n_wg), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, a.k, a.v, a.seqlens, (uint16_t*)a.o, a.lse, nullptr, nullptr, a.lay,
+                       a.H, a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits, p.kps, n_waves, a.c, a.v_scale);
+  else
+    hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, false, F8, GRP>), dim3(n_wg), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, a.k, a.v, a.seqlens, nullptr, nullptr, part_o, part_l, a.lay, a.H,
+                       a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits, p.kps, n_waves, a.c, a.v_scale);
+  return hipGetLastError();
+}
+
+// Many query blocks per head (prefill, packed batches) and a 16-bit cache:
+// workgroups of four query blocks share each staged tile (GRP); few query
+// blocks (decode) or an 8-bit cache: independent wavefronts.
 template <class TR, int D, bool CAUSAL, bool F8>
 static hipError_t launch_kv(const KvArgs& a, const KvPlan& p) {
-  const uint32_t n_waves = (uint32_t)((int64_t)a.BH * p.n_qb * p.n_splits);
-  const uint32_t n_wg = (n_waves + 3) / 4;
   float* part_o = (float*)a.workspace;
   float* part_l = part_o ? part_o + (size_t)p.n_splits * a.BH * a.Nq * D : nullptr;
-  if (p.n_splits == 1) {
-    hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, true, F8>), dim3(n_wg), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.q, a.k, a.v, a.seqlens,
-                       (uint16_t*)a.o, a.lse, nullptr, nullptr, a.lay, a.H, a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits,
-                       p.kps, n_waves, a.c, a.v_scale);
-    return hipGetLastError();
+  const bool direct = p.n_splits == 1;
+  hipError_t e;
+  if constexpr (!F8) {
+    e = p.n_qb >= 4 ? launch_split<TR, D, CAUSAL, false, true>(a, p, direct, part_o, part_l)
+                    : launch_split<TR, D, CAUSAL, false, false>(a, p, direct, part_o, part_l);
+  } else {
+    e = launch_split<TR, D, CAUSAL, true, false>(a, p, direct, part_o, part_l);
   }
-  hipLaunchKernelGGL((kv_split_kernel<TR, D, CAUSAL, false, F8>), dim3(n_wg), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, a.k, a.v, a.seqlens, nullptr,
-                     nullptr, part_o, part_l, a.lay, a.H, a.BH, a.Nq, a.Nk, p.n_qb, p.n_splits, p.kps, n_waves,
-                     a.c, a.v_scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || direct) return e;
   const int rows = a.BH * a.Nq;
   hipLaunchKernelGGL((kv_merge_kernel<TR, D>), dim3((rows + 3) / 4), dim3(256), 0, a.stream, part_o, part_l,
                      (uint16_t*)a.o, a.lse, a.lay, a.H, a.Nq, rows, p.n_splits);
