@@ -210,9 +210,9 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
 
 namespace {
 
-// Checks of fa_fwd_kvcache's sizes: the query and cache lengths are bounded
-// like N, and the split kernel's workgroup count (four wavefronts each) like
-// every other grid.
+// Checks of the split-key entry points' sizes: the query and cache lengths
+// are bounded like N, the split kernel's workgroup count (four wavefronts
+// each) like every other grid; head dimensions 32, 64 and 128.
 int check_kv_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
   if (Nq > kMaxN || Nk > kMaxN) return FA_ERR_SHAPE;
@@ -221,7 +221,7 @@ int check_kv_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
   if (bh * Nq > INT32_MAX) return FA_ERR_SHAPE;
   const fa::KvPlan p = fa::kv_plan(bh, Nq, Nk, d);
   if ((bh * p.n_qb * p.n_splits + 3) / 4 > kMaxWorkgroups) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_HEADDIM;
   return FA_OK;
 }
 

@@ -376,8 +376,8 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__
                                                        const float* __restrict__ part_l,
                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
                                                        KvLayout lay, int H, int Nq, int rows, int n_splits) {
-  constexpr int PER = D / 64;  // columns per lane
-  constexpr int UNR = 16;      // ranges whose rows are loaded before their use
+  constexpr int PER = D >= 64 ? D / 64 : 1;  // columns per lane
+  constexpr int UNR = 16;                    // ranges whose rows are loaded before their use
   const int lane = threadIdx.x & 63;
   const int row = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (row >= rows) return;
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__
 #pragma unroll
         for (int j = 0; j < UNR; ++j) {
           const int s = s0 + min(j0 + j, ns - 1);  // clamped: a repeated row gets weight 0 below
-          const float* po = part_o + ((size_t)s * rows + row) * D + PER * lane;
+          const float* po = part_o + ((size_t)s * rows + row) * D + min(PER * lane, D - PER);
 #pragma unroll
           for (int p = 0; p < PER; ++p) x[j][p] = po[p];
         }
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__
   uint16_t* orow = O + (size_t)(b * lay.q_sb + hd * lay.q_sh + (qs + qi) * lay.q_sr) + PER * lane;
   if constexpr (PER == 2) {
     *(uint32_t*)orow = TR::pack2(acc[0] * inv, acc[1] * inv);
-  } else {
+  } else if (PER * lane < D) {  // d = 32: lanes 32..63 hold no column
     *orow = (uint16_t)(TR::pack2(acc[0] * inv, 0.0f) & 0xFFFFu);
   }
   if (lane == 0) LSE[b * lay.l_sb + hd * lay.l_sh + qs + qi] = empty ? -INFINITY : (ml + __log2f(ls)) * kLn2;
@@ -477,11 +477,11 @@ static hipError_t launch_kv(const KvArgs& a, const KvPlan& p) {
   float* part_l = part_o ? part_o + (size_t)p.n_splits * a.BH * a.Nq * D : nullptr;
   const bool direct = p.n_splits == 1;
   hipError_t e;
-  if constexpr (!F8) {
+  if constexpr (!F8 && D >= 64) {  // (at d = 32 a tile is fewer chunks than threads)
     e = p.n_qb >= 4 ? launch_split<TR, D, CAUSAL, false, true>(a, p, direct, part_o, part_l)
                     : launch_split<TR, D, CAUSAL, false, false>(a, p, direct, part_o, part_l);
   } else {
-    e = launch_split<TR, D, CAUSAL, true, false>(a, p, direct, part_o, part_l);
+    e = launch_split<TR, D, CAUSAL, F8, false>(a, p, direct, part_o, part_l);
   }
   if (e != hipSuccess || direct) return e;
   const int rows = a.BH * a.Nq;
@@ -493,7 +493,8 @@ static hipError_t launch_kv(const KvArgs& a, const KvPlan& p) {
 template <class TR, bool F8>
 static hipError_t dispatch_kv(const KvArgs& a, const KvPlan& p) {
   if (a.d == 128) return a.causal ? launch_kv<TR, 128, true, F8>(a, p) : launch_kv<TR, 128, false, F8>(a, p);
-  return a.causal ? launch_kv<TR, 64, true, F8>(a, p) : launch_kv<TR, 64, false, F8>(a, p);
+  if (a.d == 64) return a.causal ? launch_kv<TR, 64, true, F8>(a, p) : launch_kv<TR, 64, false, F8>(a, p);
+  return a.causal ? launch_kv<TR, 32, true, F8>(a, p) : launch_kv<TR, 32, false, F8>(a, p);
 }
 
 hipError_t launch_fwd_kvcache(const KvArgs& a) {

@@ -57,7 +57,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL */
   FA_ERR_SHAPE = 2,     /* B, H or N < 1, N > 2^22, or B*H*ceil(N/32) >= 2^24 */
-  FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
+  FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 (32 also for the split-key entry points) */
   FA_ERR_DTYPE = 4,     /* unknown dtype, or a dtype this entry point does not take */
   FA_ERR_ALIGN = 5,     /* a data pointer is not 16-byte aligned */
   FA_ERR_SCALE = 6,     /* scale is negative, NaN or infinite */
@@ -153,6 +153,8 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
  *              initialised; may be NULL when that size is 0.  It holds the
  *              partial results of the key ranges the cache is split into.
  *   scale, causal, dtype, stream: as for fa_fwd.  Nq, Nk in [1, 2^22].
+ *   d          64 or 128 as everywhere, and also 32 (this entry point,
+ *              fa_fwd_kvcache_fp8 and fa_fwd_varlen only).
  * Errors: FA_ERR_NULL (q, k_cache, v_cache, o or lse NULL), FA_ERR_SHAPE,
  * FA_ERR_HEADDIM, FA_ERR_DTYPE (FA_F32 is not taken), FA_ERR_ALIGN,
  * FA_ERR_SCALE, FA_ERR_WORKSPACE (NULL or too small when the size is > 0).

@@ -176,6 +176,7 @@ def test_kvcache_workspace_bytes(lib):
     assert ws(1, 1, 4096, 4096, 64, 2) == 64 * 4096 * 66 * 4
     assert ws(64, 64, 2048, 2048, 128, 2) == 0
     assert ws(2, 4, 1, 4096, 128, 0) == 0  # fp32 is not taken
+    assert ws(2, 4, 1, 4096, 32, 2) == 64 * 8 * 34 * 4  # d = 32 is taken by the split-key path
     assert ws(0, 4, 1, 4096, 128, 2) == 0
     assert ws(2, 4, 1, 4096, 96, 2) == 0
 
@@ -190,7 +191,8 @@ def test_kvcache_fp8_argument_errors(lib):
     for name in ("q", "k", "v", "o", "lse"):
         assert kv8(lib, **{name: None}) == FA_ERR_NULL, name
     assert kv8(lib, Nk=0) == FA_ERR_SHAPE
-    assert kv8(lib, d=32) == FA_ERR_HEADDIM
+    assert kv8(lib, d=96) == FA_ERR_HEADDIM
+    assert kv8(lib, d=256) == FA_ERR_HEADDIM
     assert kv8(lib, dtype=0) == FA_ERR_DTYPE
     assert kv8(lib, k=P[1] + 4) == FA_ERR_ALIGN
     for bad in (0.0, -1.0, math.inf, math.nan):

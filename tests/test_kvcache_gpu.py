@@ -61,7 +61,7 @@ SMALL = [  # B, H, Nq, Nk, min_fill
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,Nq,Nk,fill", SMALL)
 def test_small_shapes(B, H, Nq, Nk, fill, causal, d, dtype):
@@ -154,7 +154,7 @@ def _run8(inp, dtype, causal, scale, k_codes=None, v_codes=None):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,Nq,Nk,fill", [SMALL[0], SMALL[1], SMALL[2], SMALL[4], SMALL[6]])
 def test_fp8_cache_small_shapes(B, H, Nq, Nk, fill, causal, d, dtype):
@@ -232,7 +232,7 @@ VARLEN = [  # query lengths, key lengths
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("case", range(len(VARLEN)))
 def test_varlen_small(case, causal, d, dtype):
