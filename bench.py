@@ -537,15 +537,19 @@ def main():
     torch.cuda.synchronize()
 
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(args.steps):
+        step_evs[i].record()
         run()
+    step_evs[args.steps].record()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    step_ms = [step_evs[i].elapsed_time(step_evs[i + 1]) for i in range(args.steps)]
 
     # per-kernel durations: the same steps with the stages in order on one
     # stream, each between its own events (these times feed the roofline)
@@ -556,7 +560,8 @@ def main():
     for i in range(n_k):
         step(evs[i])
     torch.cuda.synchronize()
-    kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    kern_samples = {n: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, n in enumerate(names)}
+    kern_ms = {n: float(np.mean(v)) for n, v in kern_samples.items()}
     # secondary: the same steps with the caches cold, a 512 MiB scrub written
     # before each step (outside the timed region)
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -577,12 +582,14 @@ def main():
     alg = algorithmic(w)
     per_kernel = {}
     for n in names:
+        spread = {"ms_median": round(float(np.median(kern_samples[n])), 4),
+                  "ms_min": round(float(np.min(kern_samples[n])), 4)}
         if n == "prep":
-            per_kernel[n] = {"ms": round(kern_ms[n], 4), "GB/s": round(alg[n] / kern_ms[n] / 1e6, 1)}
+            per_kernel[n] = {"ms": round(kern_ms[n], 4), "GB/s": round(alg[n] / kern_ms[n] / 1e6, 1), **spread}
         else:
             tf = alg[n] / (kern_ms[n] * 1e-3) / 1e12
             per_kernel[n] = {"ms": round(kern_ms[n], 4), "TFLOP/s": round(tf, 1),
-                             "frac": round(tf / PEAK_MFMA_16BIT, 4)}
+                             "frac": round(tf / PEAK_MFMA_16BIT, 4), **spread}
     dom = max(["fwd", "dkdv", "dq"], key=lambda n: kern_ms[n])
     achieved = alg[dom] / (kern_ms[dom] * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_MFMA_16BIT,
@@ -597,6 +604,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "ms_per_step_min": round(float(np.min(step_ms)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
