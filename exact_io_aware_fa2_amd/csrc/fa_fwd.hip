@@ -874,7 +874,7 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float* __restrict__ Q,
   constexpr int KP = D + 1;  // padded K row (conflict-free column reads)
   constexpr int NDB = D / 32;
   __shared__ float sK[BC * KP];
-  __shared__ float sV[BC * D];
+  __shared__ __attribute__((aligned(16))) float sV[BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -906,15 +906,37 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float* __restrict__ Q,
   const int wave_last = CAUSAL ? min(N, qw + 32) : N;
   const int wave_tiles = (wave_last + BC - 1) / BC;
 
+  // staging: 16-byte chunks x = tid + 256 i of the tile (row x / (D / 4),
+  // columns 4 (x % (D / 4)) + 0..3), loaded one tile ahead into registers so
+  // the next tile's loads are in flight while this one is computed; rows past
+  // the end are zeros
+  constexpr int NST = BC * D / 4 / 256;
+  float4 kst[NST], vst[NST];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const int x = tid + 256 * i, row = x / (D / 4), col = 4 * (x % (D / 4));
+      const bool ok = j0 + row < N;
+      const size_t off = head_off + (size_t)(j0 + row) * D + col;
+      kst[i] = ok ? *(const float4*)(K + off) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+      vst[i] = ok ? *(const float4*)(V + off) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
+  load_tile(0);
   for (int jt = 0; jt < n_tiles; ++jt) {
     const int j0 = jt * BC;
-    __syncthreads();
-    for (int x = tid; x < BC * D; x += 256) {
-      const int row = x / D, col = x % D;
-      const bool ok = j0 + row < N;
-      sK[row * KP + col] = ok ? K[head_off + (size_t)(j0 + row) * D + col] : 0.0f;
-      sV[row * D + col] = ok ? V[head_off + (size_t)(j0 + row) * D + col] : 0.0f;
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const int x = tid + 256 * i, row = x / (D / 4), col = 4 * (x % (D / 4));
+      float* kd = sK + row * KP + col;  // padded rows: not 16-byte aligned
+      kd[0] = kst[i].x;
+      kd[1] = kst[i].y;
+      kd[2] = kst[i].z;
+      kd[3] = kst[i].w;
+      *(float4*)(sV + row * D + col) = vst[i];
     }
+    if (jt + 1 < n_tiles) load_tile(j0 + BC);
     __syncthreads();
     if (jt >= wave_tiles) continue;
 
