@@ -20,13 +20,16 @@
  *     key j is visible to query i iff j <= i (top-left aligned, equal query and
  *     key lengths), and the gradient is the chain rule through the softmax.
  *
- * Conventions shared by every entry point
+ * Conventions shared by every entry point (unless its own comment says
+ * otherwise: the key/value-cache and variable-length entry points take other
+ * layouts and also d = 32, the probe computes nothing)
  *   Layout     q, k, v, o, dout, dq, dk, dv: contiguous row-major [B, H, N, d]
  *              arrays of the element type `dtype`.  lse: contiguous [B, H, N]
  *              float32.  Head dimension d must be 64 or 128.
  *   Memory     All data pointers are DEVICE pointers owned by the caller.  The
  *              library allocates no device memory and keeps no pointer after a
- *              call returns.  Every data pointer must be 16-byte aligned.
+ *              call returns.  Every tensor pointer must be 16-byte aligned
+ *              (int32 length arrays: 4-byte).
  *   Streams    `stream` is a hipStream_t (NULL = the default stream).  Calls
  *              only enqueue work on it and return; they never synchronise and
  *              never copy to the host.  Concurrent calls on different streams
@@ -35,7 +38,8 @@
  *              in float32; outputs have the input type (LSE: float32).  The
  *              probabilities that multiply V are rounded to the input type
  *              (round to nearest even); the float32 path keeps them in float32.
- *   Errors     Return FA_OK (0) or a positive fa_status.  Arguments are checked
+ *   Errors     Return FA_OK (0) or a positive fa_status (the probe: a negated
+ *              one).  Arguments are checked
  *              before any device call; on an argument error nothing is
  *              enqueued.  FA_ERR_HIP means the HIP runtime refused the launch
  *              (no device, invalid stream, ...); hipGetLastError() then holds
