@@ -22,7 +22,7 @@ Parity status: every public function here is pinned by ``tests/test_oracle.py``
 
 from .attention import attention_fwd, attention_fwd_head, attention_bwd, attention_bwd_head
 from .brute import brute_fwd_decimal, brute_kvcache_decimal
-from .kvcache import kvcache_fwd, kvcache_fwd_head, varlen_fwd
+from .kvcache import kvcache_fwd, kvcache_fwd_head, varlen_bwd_causal, varlen_fwd
 
 __all__ = [
     "attention_fwd",
@@ -34,4 +34,5 @@ __all__ = [
     "kvcache_fwd",
     "kvcache_fwd_head",
     "varlen_fwd",
+    "varlen_bwd_causal",
 ]

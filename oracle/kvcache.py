@@ -115,3 +115,23 @@ def varlen_fwd(q, k, v, cu_q, cu_k, scale: float, causal: bool):
             o[q0:q1, hi] = ob
             lse[hi, q0:q1] = lb
     return o, lse
+
+
+def varlen_bwd_causal(q, k, v, do, cu, scale: float):
+    """Gradient of causal self-attention over a packed variable-length batch:
+    sequence b owns rows cu[b] .. cu[b+1]-1 of q, k, v, do (each [total, H, d]),
+    with as many queries as keys.  Per sequence and head this is the pinned
+    ``attention_bwd_head`` of ``attention.py`` (softmax Jacobian, causal).
+    Returns (dQ, dK, dV) [total, H, d] float64; rows of no sequence stay 0."""
+    from .attention import attention_bwd_head
+    q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+    tot, h, d = q.shape
+    dq, dk, dv = (np.zeros((tot, h, d)) for _ in range(3))
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if s1 <= s0:
+            continue
+        for hi in range(h):
+            g = attention_bwd_head(q[s0:s1, hi], k[s0:s1, hi], v[s0:s1, hi], do[s0:s1, hi], scale, True)
+            dq[s0:s1, hi], dk[s0:s1, hi], dv[s0:s1, hi] = g
+    return dq, dk, dv

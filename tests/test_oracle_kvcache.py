@@ -239,3 +239,37 @@ def test_varlen_sequences_are_independent():
     o2, l2 = varlen_fwd(q, k2, v, cu_q, cu_k, 0.5, True)
     assert np.array_equal(o1[:3], o2[:3]) and np.array_equal(l1[:, :3], l2[:, :3])
     assert not np.allclose(o1[3:], o2[3:])
+
+
+def test_varlen_backward_equal_lengths_is_the_batched_gradient():
+    from oracle import attention_bwd, varlen_bwd_causal
+    rng = np.random.default_rng(63)
+    B, H, n, d = 3, 2, 6, 4
+    q, k, v, do = (rnd(rng, B, H, n, d) for _ in range(4))
+    g = attention_bwd(q, k, v, do, 0.5, True)
+    cu = np.arange(B + 1) * n
+    gv = varlen_bwd_causal(*(_pack(x, [n] * B) for x in (q, k, v, do)), cu, 0.5)
+    for a, b in zip(gv, g):
+        assert np.array_equal(a, _pack(b, [n] * B))
+
+
+def test_varlen_backward_matches_finite_differences_of_the_forward():
+    """Central differences of sum(O * dO) through the varlen forward oracle,
+    ragged lengths (including an empty sequence)."""
+    from oracle import varlen_bwd_causal
+    rng = np.random.default_rng(64)
+    lens = [3, 0, 2, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    tot, H, d, sc = int(cu[-1]), 2, 3, 0.6
+    q, k, v, do = (rnd(rng, tot, H, d) for _ in range(4))
+    dq, dk, dv = varlen_bwd_causal(q, k, v, do, cu, sc)
+    f = lambda q_, k_, v_: float(np.sum(varlen_fwd(q_, k_, v_, cu, cu, sc, True)[0] * do))
+    eps = 1e-6
+    for which, g in ((0, dq), (1, dk), (2, dv)):
+        for idx in np.ndindex(tot, H, d):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += eps
+            fp = f(*args)
+            args[which][idx] -= 2 * eps
+            fm = f(*args)
+            assert abs((fp - fm) / (2 * eps) - g[idx]) <= 1e-7
