@@ -19,7 +19,7 @@ Modes
   --workload D1         a decode step against a key/value cache instead (fa_fwd_kvcache,
                         B=4 H=32, one query, 32768-row cache, d=128): HBM GB/s;
                         D1f8: the same with an 8-bit E4M3 cache (fa_fwd_kvcache_fp8)
-  --varlen              fa_fwd_varlen on a packed batch of 16 ragged causal prefill sequences
+  --varlen              fa_fwd_varlen + fa_bwd_varlen on a packed batch of 16 ragged causal sequences
   --fwd-only            fa_fwd alone: time, TFLOP/s and compulsory GB/s per workload
                         (--workload C1,C3,...; --workload short: the short-sequence sweep)
   --profile             3 warm-up + 20 timed steps (stages in order on one stream), no CPU
@@ -328,10 +328,11 @@ def bench_fwd_only(args, workloads):
 
 
 def bench_varlen(args):
-    """A packed variable-length prefill batch through fa_fwd_varlen: 16
-    sequences with lengths drawn uniformly in [512, 4096] (seed 1008), H=16,
-    d=128, bf16, causal (queries = keys per sequence).  TFLOP/s of the
-    per-sequence causal work, sum_b 2 H L_b^2 d, median of --steps calls."""
+    """A packed variable-length training batch: 16 causal sequences with
+    lengths drawn uniformly in [512, 4096] (seed 1008), H=16, d=128, bf16
+    (queries = keys per sequence), through fa_fwd_varlen and fa_bwd_varlen.
+    TFLOP/s of the per-sequence causal work, sum_b 2 H L_b^2 d forward and
+    2.5 times that backward, median of --steps calls of each."""
     import numpy as np
     import torch
 
@@ -341,32 +342,47 @@ def bench_varlen(args):
     rng = np.random.default_rng(1008)
     lens = rng.integers(512, 4097, size=16).tolist()
     H, d = 16, 128
-    inp = si.make_varlen_inputs(lens, lens, H, d, "bf16", 1.0, 1008)
+    scale = 1 / np.sqrt(d)
+    inp = si.make_varlen_inputs(lens, lens, H, d, "bf16", 1.0, 1008, backward=True)
     dev = torch.device("cuda:0")
     up = lambda n: torch.from_numpy(inp[n][1].view(np.int16)).view(torch.bfloat16).to(dev)
-    q, k, v = up("q"), up("k"), up("v")
-    cq, ck = (torch.from_numpy(inp[n]).to(dev) for n in ("cu_q", "cu_k"))
+    q, k, v, do = up("q"), up("k"), up("v"), up("do")
+    del inp
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
     o = torch.empty_like(q)
     lse = torch.empty((H, q.shape[0]), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     mx = max(lens)
-    nb = int(fa.load_library().fa_fwd_varlen_workspace_bytes(len(lens), H, mx, mx, d, fa.FA_BF16))
+    lib = fa.load_library()
+    nb = int(lib.fa_fwd_varlen_workspace_bytes(len(lens), H, mx, mx, d, fa.FA_BF16))
     ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
-    call = lambda: fa.fa_fwd_varlen(q, k, v, cq, ck, o, lse, ws, mx, mx, 1 / np.sqrt(d), True)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for e0, e1 in evs:
-        e0.record()
-        call()
-        e1.record()
-    torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    nbb = int(lib.fa_bwd_varlen_workspace_bytes(len(lens), H, mx, d, fa.FA_BF16))
+    wsb = torch.empty(nbb, dtype=torch.uint8, device=dev)
+    fwd = lambda: fa.fa_fwd_varlen(q, k, v, cu, cu, o, lse, ws, mx, mx, scale, True)
+    bwd = lambda: fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, dq, dk, dv, wsb, mx, scale)
+
+    def timed(call):
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1 in evs:
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    ms_f = timed(fwd)
+    ms_b = timed(bwd)
     flop = sum(2.0 * H * L * L * d for L in lens)
-    print(json.dumps({"mode": "varlen prefill", "workload": f"16 packed sequences, lengths {lens}, H={H} d={d} bf16 causal",
-                      "median_us": round(ms * 1e3, 1), "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
-                      "frac_mfma_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_MFMA_16BIT, 4),
-                      "workspace_bytes": nb}), flush=True)
+    rate = lambda f, ms: f / (ms * 1e-3) / 1e12
+    print(json.dumps({"mode": "varlen training", "workload": f"16 packed sequences, lengths {lens}, H={H} d={d} bf16 causal",
+                      "fwd_median_us": round(ms_f * 1e3, 1), "fwd_TFLOP/s": round(rate(flop, ms_f), 1),
+                      "bwd_median_us": round(ms_b * 1e3, 1), "bwd_TFLOP/s": round(rate(2.5 * flop, ms_b), 1),
+                      "fwd_bwd_TFLOP/s": round(rate(3.5 * flop, ms_f + ms_b), 1),
+                      "frac_mfma_peak_fwd_bwd": round(rate(3.5 * flop, ms_f + ms_b) / PEAK_MFMA_16BIT, 4),
+                      "workspace_bytes": {"fwd": nb, "bwd": nbb}}), flush=True)
 
 
 def short_n_workloads():
@@ -443,7 +459,7 @@ def main():
                     help="time the step with all stages in order on one stream (dQ not beside dK/dV)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--varlen", action="store_true",
-                    help="time fa_fwd_varlen on a packed batch of 16 ragged causal prefill sequences")
+                    help="time fa_fwd_varlen and fa_bwd_varlen on a packed batch of 16 ragged causal sequences")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time fa_fwd alone on --workload (any of C1..C5, C3d64, C5d128; comma-separated), "
                          "or on the short-sequence sweep with --workload short")

@@ -83,6 +83,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fa_fwd_varlen.restype = i32
     L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, i64, i64, f32, i32,
                                 i32, vp]
+    L.fa_bwd_varlen_workspace_bytes.restype = sz
+    L.fa_bwd_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    L.fa_bwd_varlen.restype = i32
+    L.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, f32, i32,
+                                vp]
     L.fa_probe_mfma_bf16.restype = i64
     L.fa_probe_mfma_bf16.argtypes = [i64, i64, vp]
     L.fa_fwd_kvcache_fp8.restype = i32
@@ -334,6 +339,49 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_q: int, max_k: int, caus
     fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, workspace, max_q, max_k,
                   default_scale(d) if scale is None else scale, causal)
     return o, lse
+
+
+def fa_bwd_varlen_workspace_bytes(B: int, H: int, max_len: int, d: int, dtype: int) -> int:
+    return int(load_library().fa_bwd_varlen_workspace_bytes(B, H, max_len, d, dtype))
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, dq, dk, dv, workspace, max_len: int, scale: float) -> None:
+    """Enqueue the causal backward of a packed variable-length batch (see
+    include/fa.h): q, k, v, o, dout, dq, dk, dv [total, H, d]; lse float32
+    [H, total]; cu_seqlens int32 [B + 1] on the device."""
+    L = load_library()
+    torch = _torch()
+    _check_tensors(q, k, v, o, lse, dout, cu_seqlens, dq, dk, dv, workspace)
+    if q.dim() != 3:
+        raise ValueError("packed tensors are [total, H, d]")
+    total, H, d = (int(x) for x in q.shape)
+    for t in (k, v, o, dout, dq, dk, dv):
+        if tuple(t.shape) != (total, H, d) or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dout, dq, dk, dv must all be [total, H, d] of one dtype")
+    if tuple(lse.shape) != (H, total) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [H, total]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be int32 [B + 1]")
+    B = int(cu_seqlens.shape[0]) - 1
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(L.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(cu_seqlens), _ptr(dq),
+                           _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, B, H, total, int(max_len), d, float(scale),
+                           dtype_code(q), _stream(q)))
+
+
+def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_len: int, scale: float | None = None, workspace=None):
+    """Allocate dQ, dK, dV (zero rows outside every sequence) and the
+    workspace unless given, and run the causal packed backward."""
+    torch = _torch()
+    total, H, d = (int(x) for x in q.shape)
+    B = int(cu_seqlens.shape[0]) - 1
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    if workspace is None:
+        nb = fa_bwd_varlen_workspace_bytes(B, H, max_len, d, dtype_code(q))
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, dq, dk, dv, workspace, max_len,
+                  default_scale(d) if scale is None else scale)
+    return dq, dk, dv
 
 
 def fa_probe_mfma_bf16(workgroups: int, iters: int) -> int:

@@ -410,3 +410,66 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t fa_bwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t max_len, int64_t d, int dtype) {
+  if (check_shape(B, H, max_len, d) != FA_OK) return 0;
+  if (dtype != FA_F16 && dtype != FA_BF16) return 0;
+  return fa::varlen_bwd_workspace_bytes(B, H, max_len, d);
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, const int32_t* cu_seqlens, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, int64_t B, int64_t H, int64_t total, int64_t max_len, int64_t d,
+                  float scale, int dtype, void* stream) {
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!p) return FA_ERR_NULL;
+  if (!cu_seqlens) return FA_ERR_NULL;
+  int st = check_shape(B, H, max_len, d);
+  if (st != FA_OK) return st;
+  if (total < 1 || total > INT32_MAX) return FA_ERR_SHAPE;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return FA_ERR_ALIGN;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  const size_t need = fa::varlen_bwd_workspace_bytes(B, H, max_len, d);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+
+  fa::VarlenBwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.cu = cu_seqlens;
+  const size_t rows = (size_t)(B * H * max_len);
+  char* w = (char*)workspace;
+  for (int t = 0; t < 8; ++t) {
+    a.pad[t] = w;
+    w += fa::varlen_piece(rows * (size_t)d * 2);
+  }
+  a.lse_pad = (float*)w;
+  w += fa::varlen_piece(rows * sizeof(float));
+  a.dvec = (float*)w;
+  a.B = (int)B;
+  a.H = (int)H;
+  a.max_len = (int)max_len;
+  a.d = (int)d;
+  a.total = total;
+  a.scale = scale;
+  a.c = exp2_factor(scale);
+  a.dtype = dtype;
+  a.stream = (hipStream_t)stream;
+  return status_of(fa::launch_bwd_varlen(a));
+}
+
+}  // extern "C"

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum {
   FA_OK = 0,
@@ -223,6 +223,44 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
                   const int32_t* cu_seqlens_k, void* o, float* lse, void* workspace, size_t workspace_bytes,
                   int64_t B, int64_t H, int64_t total_q, int64_t total_k, int64_t max_q, int64_t max_k,
                   int64_t d, float scale, int causal, int dtype, void* stream);
+
+/* Backward of causal self-attention over a variable-length packed batch
+ * (the training side of the packed layout of fa_fwd_varlen with equal query
+ * and key prefix sums; the pages' drop-in use with the usual attention
+ * interfaces: "FlashAttention-2 (DE)", "Anwendung und Integration in das
+ * Ökosystem"; the gradient, recomputed as in fa_bwd: "FlashAttention"
+ * lexicon, "Methodische Grundlagen").
+ * Sequence b owns rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of every tensor and
+ * attends causally within itself (key j visible to query i iff j <= i).
+ * Computed exactly by copying the sequences into a padded
+ * [B, H, max_len, d] batch in the workspace (zero rows after each length,
+ * LSE +infinity there, which gives those rows zero probability and zero
+ * gradient), running fa_bwd's kernels on it, and copying the first rows of
+ * each sequence back.
+ *   q, k, v, o,   [total, H, d] of type dtype (FA_BF16 or FA_F16), packed
+ *   dout          rows, 16-byte aligned; o and lse are fa_fwd_varlen's output
+ *                 for these q, k, v with causal = 1.
+ *   lse           [H, total] float32 (natural log).
+ *   cu_seqlens    DEVICE int32 [B + 1] non-decreasing prefix sums (4-byte
+ *                 aligned), clamped like fa_fwd_varlen's.
+ *   dq, dk, dv    [total, H, d] outputs, same type; rows outside every
+ *                 sequence, and rows past max_len of a longer sequence, are
+ *                 left unchanged.
+ *   max_len       the largest sequence length, in [1, 2^22].
+ *   workspace     fa_bwd_varlen_workspace_bytes(B, H, max_len, d, dtype)
+ *                 bytes, 16-byte aligned (8 B H max_len d 2-byte padded
+ *                 tensors and two float vectors; rounded to 256 bytes each).
+ * Deterministic (fixed reduction order).  Errors: FA_ERR_NULL, FA_ERR_SHAPE
+ * (as fa_fwd for B, H, max_len; total < 1 or > 2^31 - 1), FA_ERR_HEADDIM
+ * (d not 64 or 128), FA_ERR_DTYPE (not FA_BF16 / FA_F16), FA_ERR_ALIGN,
+ * FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_HIP.  The workspace size function
+ * returns 0 for arguments the entry point rejects. */
+size_t fa_bwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t max_len, int64_t d, int dtype);
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, const int32_t* cu_seqlens, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, int64_t B, int64_t H, int64_t total, int64_t max_len, int64_t d,
+                  float scale, int dtype, void* stream);
 
 /* Measurement probe, not part of attention: enqueues a kernel of `workgroups`
  * workgroups (4 wavefronts each) in which every wavefront issues `iters`

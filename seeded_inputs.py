@@ -257,14 +257,16 @@ def make_kvcache_fp8_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str
     return out
 
 
-def make_varlen_inputs(lens_q, lens_k, H: int, d: int, dtype: str, sigma: float, seed: int):
+def make_varlen_inputs(lens_q, lens_k, H: int, d: int, dtype: str, sigma: float, seed: int,
+                       backward: bool = False):
     """A packed variable-length batch: Q [sum lens_q, H, d], then K and V
-    [sum lens_k, H, d], drawn and rounded as in make_inputs, and the int32
-    prefix sums cu_q, cu_k [B + 1]."""
+    [sum lens_k, H, d] (and, with backward, dO [sum lens_q, H, d]), drawn and
+    rounded as in make_inputs, and the int32 prefix sums cu_q, cu_k [B + 1]."""
     rng = np.random.default_rng(seed)
     tq, tk = int(sum(lens_q)), int(sum(lens_k))
     out = {}
-    for nm, n in (("q", tq), ("k", tk), ("v", tk)):
+    draws = (("q", tq), ("k", tk), ("v", tk)) + ((("do", tq),) if backward else ())
+    for nm, n in draws:
         x = rng.standard_normal((n, H, d), dtype=np.float32)
         if sigma != 1.0:
             x *= np.float32(sigma)

@@ -36,13 +36,13 @@ def test_header_declares_the_entry_points():
         ["fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
          "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kvcache_workspace_bytes",
          "fa_fwd_kvcache", "fa_fwd_kvcache_fp8", "fa_probe_mfma_bf16", "fa_fwd_varlen_workspace_bytes",
-         "fa_fwd_varlen"])
+         "fa_fwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_bwd_varlen"])
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 4
+    assert lib.fa_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -233,3 +233,41 @@ def test_varlen_argument_errors(lib):
     assert need == lib.fa_fwd_kvcache_workspace_bytes(3, 4, 128, 256, 128, 2) > 0
     assert vl(lib, ws=None) == FA_ERR_WORKSPACE
     assert vl(lib, wsb=need - 1) == FA_ERR_WORKSPACE
+
+
+def bvl(lib, ptrs=None, cu=P[10], ws=P[11], wsb=1 << 40, B=3, H=4, total=300, max_len=128, d=128, scale=0.088,
+        dtype=2):
+    q, k, v, o, lse, do, dq, dk, dv = ptrs if ptrs is not None else P[:9]
+    return lib.fa_bwd_varlen(q, k, v, o, lse, do, cu, dq, dk, dv, ws, wsb, B, H, total, max_len, d, scale, dtype,
+                             None)
+
+
+def test_varlen_bwd_argument_errors(lib):
+    # every case is rejected before any launch (the pointers are never touched)
+    for i in range(9):
+        ptrs = list(P[:9])
+        ptrs[i] = None
+        assert bvl(lib, ptrs) == FA_ERR_NULL, i
+    assert bvl(lib, cu=None) == FA_ERR_NULL
+    assert bvl(lib, B=0) == FA_ERR_SHAPE
+    assert bvl(lib, total=0) == FA_ERR_SHAPE
+    assert bvl(lib, total=1 << 31) == FA_ERR_SHAPE
+    assert bvl(lib, max_len=0) == FA_ERR_SHAPE
+    assert bvl(lib, max_len=(1 << 22) + 1) == FA_ERR_SHAPE
+    assert bvl(lib, d=32) == FA_ERR_HEADDIM
+    assert bvl(lib, dtype=0) == FA_ERR_DTYPE
+    for i in range(9):
+        ptrs = list(P[:9])
+        ptrs[i] += 8
+        assert bvl(lib, ptrs) == FA_ERR_ALIGN, i
+    assert bvl(lib, cu=P[10] + 2) == FA_ERR_ALIGN
+    assert bvl(lib, scale=float("nan")) == FA_ERR_SCALE
+    need = lib.fa_bwd_varlen_workspace_bytes(3, 4, 128, 128, 2)
+    rows = 3 * 4 * 128
+    assert need == 8 * rows * 128 * 2 + 2 * rows * 4
+    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 64, 1) == 8 * 512 + 2 * 256
+    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 64, 0) == 0
+    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 32, 2) == 0
+    assert bvl(lib, ws=None) == FA_ERR_WORKSPACE
+    assert bvl(lib, wsb=need - 1) == FA_ERR_WORKSPACE
+    assert bvl(lib, ws=P[11] + 4, wsb=need) == FA_ERR_ALIGN

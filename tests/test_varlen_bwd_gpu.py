@@ -1,0 +1,164 @@
+"""Backward parity on the GPU for causal self-attention over a packed
+variable-length batch: fa_bwd_varlen (fed the library's own fa_fwd_varlen O
+and LSE, as a training step would) against the float64 oracle's per-sequence
+softmax-Jacobian gradient (oracle.varlen_bwd_causal) on the same seeded Q, K,
+V, dO.  Bound: relative L2 <= 1e-2 for each of dQ, dK, dV per sequence and
+head, as for fa_bwd.  Lengths cover one row, empty sequences, lengths below,
+at and above the 128-row tiles, and ragged tails; the 16-sequence prefill
+batch the benchmark times runs in full and is checked on sampled sequences."""
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from oracle import attention_bwd_head, varlen_bwd_causal
+from parity import BWD_REL_L2, lib, rel_l2, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _upload(inp, dtype):
+    import torch
+    q, k, v, do = (to_device(inp[n][1], dtype) for n in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(inp["cu_q"]).cuda()
+    return q, k, v, do, cu
+
+
+def _run(inp, dtype, scale, max_len=None, init=None):
+    """fa_fwd_varlen (causal) then fa_bwd_varlen; returns dq, dk, dv as float
+    [total, H, d] arrays.  `init` pre-fills the gradient buffers."""
+    import torch
+    fa = lib()
+    q, k, v, do, cu = _upload(inp, dtype)
+    mx = int(np.diff(inp["cu_q"]).max()) if max_len is None else max_len
+    mx = max(mx, 1)
+    o, lse = fa.fwd_varlen(q, k, v, cu, cu, mx, mx, True, scale)
+    if init is None:
+        dq, dk, dv = fa.bwd_varlen(q, k, v, o, lse, do, cu, mx, scale)
+    else:
+        dq, dk, dv = (to_device(init, dtype) for _ in range(3))
+        nb = fa.fa_bwd_varlen_workspace_bytes(len(inp["cu_q"]) - 1, q.shape[1], mx, q.shape[2], fa.dtype_code(q))
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, dq, dk, dv, ws, mx, scale)
+    torch.cuda.synchronize()
+    return tuple(g.float().cpu().numpy() for g in (dq, dk, dv))
+
+
+def _check_seqs(inp, grads, ref, seqs, heads, label):
+    cu = inp["cu_q"]
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b in seqs:
+        rows = slice(int(cu[b]), int(cu[b + 1]))
+        for h in heads:
+            r = ref(b, h) if callable(ref) else tuple(x[rows, h] for x in ref)
+            for name, g, rr in zip(("dq", "dk", "dv"), grads, r):
+                gg = g[rows, h]
+                assert np.isfinite(gg).all(), (label, name, b, h)
+                if gg.size == 0:
+                    continue
+                if np.linalg.norm(rr) == 0.0:
+                    # a one-row sequence: dQ = dK = 0 exactly; only rounding noise may remain
+                    assert np.abs(gg).max() <= 1e-5, (label, name, b, h)
+                    continue
+                worst[name] = max(worst[name], rel_l2(gg, rr))
+    say(f"  {label}: rel-L2 {worst}")
+    for name, e in worst.items():
+        assert e <= BWD_REL_L2, (label, name, e)
+
+
+LENGTHS = [
+    [1, 100, 0, 33, 257],  # one row, one tile, empty, ragged, several tiles
+    [64, 5, 200],           # below and above a tile
+    [1000, 1],              # one long sequence beside a one-row one
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", range(len(LENGTHS)))
+def test_varlen_bwd_small(case, d, dtype):
+    lens = LENGTHS[case]
+    seed = 9300 + 13 * case + d
+    H = 3
+    inp = si.make_varlen_inputs(lens, lens, H, d, dtype, 1.0, seed, backward=True)
+    scale = 1.0 / np.sqrt(d)
+    say(f"varlen bwd lens={lens} H{H} d{d} {dtype} seed={seed}")
+    grads = _run(inp, dtype, scale)
+    ref = varlen_bwd_causal(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], inp["cu_q"], scale)
+    _check_seqs(inp, grads, ref, range(len(lens)), range(H), f"lens {lens} d{d} {dtype}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_bwd_equal_lengths_bitwise_equal_the_ordinary_backward(d):
+    """Equal lengths: the padded batch is the [B, H, N, d] batch itself, so
+    the gradients are those of fa_bwd on the same values, bit for bit."""
+    import torch
+    fa = lib()
+    B, H, N = 3, 4, 300
+    scale = 1 / np.sqrt(d)
+    inp = si.make_varlen_inputs([N] * B, [N] * B, H, d, "bf16", 1.0, 9400 + d, backward=True)
+    q, k, v, do, cu = _upload(inp, "bf16")
+    dense = lambda x: x.reshape(B, N, H, d).permute(0, 2, 1, 3).contiguous()
+    packed = lambda x: x.permute(0, 2, 1, 3).reshape(B * N, H, d).contiguous()
+    qd, kd, vd, dod = (dense(x) for x in (q, k, v, do))
+    od, lsed = fa.fwd(qd, kd, vd, True, scale)
+    g_dense = fa.bwd(qd, kd, vd, od, lsed, dod, True, scale)
+    o = packed(od)
+    lse = lsed.permute(1, 0, 2).reshape(H, B * N).contiguous()
+    g_var = fa.bwd_varlen(q, k, v, o, lse, do, cu, N, scale)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), g_var, g_dense):
+        assert torch.equal(a, packed(b)), name
+    grads = tuple(g.float().cpu().numpy() for g in g_var)
+    ref = varlen_bwd_causal(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], inp["cu_q"], scale)
+    _check_seqs(inp, grads, ref, range(B), range(H), f"equal lengths d{d}")
+
+
+def test_varlen_bwd_rows_outside_the_sequences_are_left_unchanged():
+    lens = [10, 15]
+    inp = si.make_varlen_inputs(lens + [5], lens + [5], 2, 64, "bf16", 1.0, 9410, backward=True)
+    inp["cu_q"] = np.array([0, 10, 25], np.int32)  # rows 25..29 belong to no sequence
+    sentinel = si.round_to(np.full((30, 2, 64), 7.0, np.float32), "bf16")[1]
+    say("varlen bwd partial cover, cu [0, 10, 25] of 30 rows")
+    grads = _run(inp, "bf16", 0.125, init=sentinel)
+    for g in grads:
+        assert np.all(g[25:] == 7.0)
+    ref = varlen_bwd_causal(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], inp["cu_q"], 0.125)
+    _check_seqs(inp, grads, ref, range(2), range(2), "partial cover")
+
+
+def test_varlen_bwd_max_len_above_every_length_and_determinism():
+    """A max_len larger than every sequence only adds padded rows; repeated
+    calls are bitwise identical."""
+    lens = [70, 130]
+    inp = si.make_varlen_inputs(lens, lens, 2, 128, "bf16", 1.0, 9420, backward=True)
+    say("varlen bwd max_len 256 over lengths [70, 130]")
+    g1 = _run(inp, "bf16", 0.088, max_len=256)
+    g2 = _run(inp, "bf16", 0.088, max_len=256)
+    for a, b in zip(g1, g2):
+        assert np.array_equal(a, b)
+    ref = varlen_bwd_causal(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], inp["cu_q"], 0.088)
+    _check_seqs(inp, g1, ref, range(2), range(2), "max_len 256")
+
+
+def test_varlen_bwd_prefill_batch_full_size_sampled():
+    """The 16-sequence packed prefill batch (lengths uniform in [512, 4096],
+    seed 1008, H=16, d=128, bf16) the benchmark times, run in full; sampled
+    (sequence, head) pairs against the oracle in full."""
+    rng = np.random.default_rng(1008)
+    lens = rng.integers(512, 4097, size=16).tolist()
+    H, d = 16, 128
+    scale = 1 / np.sqrt(d)
+    inp = si.make_varlen_inputs(lens, lens, H, d, "bf16", 1.0, 1008, backward=True)
+    say(f"varlen bwd prefill batch lengths {lens}")
+    grads = _run(inp, "bf16", scale)
+    cu = inp["cu_q"]
+
+    def ref(b, h):
+        rows = slice(int(cu[b]), int(cu[b + 1]))
+        return attention_bwd_head(inp["q"][0][rows, h], inp["k"][0][rows, h], inp["v"][0][rows, h],
+                                  inp["do"][0][rows, h], scale, True)
+
+    shortest = int(np.argmin(lens))
+    _check_seqs(inp, grads, ref, [shortest], [0, 15], "prefill shortest sequence")
+    _check_seqs(inp, grads, ref, [5], [7], "prefill sequence 5")
