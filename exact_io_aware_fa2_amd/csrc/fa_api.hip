@@ -460,6 +460,8 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   a.lse_pad = (float*)w;
   w += fa::varlen_piece(rows * sizeof(float));
   a.dvec = (float*)w;
+  w += fa::varlen_piece(rows * sizeof(float));
+  a.lens = (int32_t*)w;
   a.B = (int)B;
   a.H = (int)H;
   a.max_len = (int)max_len;

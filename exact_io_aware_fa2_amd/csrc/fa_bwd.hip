@@ -85,7 +85,8 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dvec,
                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_ktiles,
-                          uint32_t total, float c, float neg_inv_scale, float scale) {
+                          uint32_t total, float c, float neg_inv_scale, float scale,
+                          const int32_t* __restrict__ lens, int H) {
   constexpr int NT = 256;
   constexpr int BKV = 128;                  // keys per workgroup
   constexpr int BQ = 64;                    // query rows per stage
@@ -127,6 +128,11 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int key = kw + l32;
   const size_t head_off = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * RB;
+  // Padded batch (causal only): rows from the sequence's length Nb on are
+  // zero with LSE +inf, so queries past Nb add nothing and keys past Nb are
+  // never wanted; tiles wholly past Nb are skipped.
+  const int Nb = lens ? min(N, lens[bh / H]) : N;
+  if (k0 >= Nb) return;
 
   // K and V rows of this wavefront's keys as B operands (column = key)
   u32x4_t kf[NKS], vf[NKS];
@@ -158,7 +164,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const uint32_t tbase = (uint32_t)((h + 4 * (L16 >> 2)) * RBL + (16 * (G & 1) + 4 * (L16 & 3)) * 2);
 
   const int i_begin = CAUSAL ? k0 : 0;
-  const int n_st = (N - i_begin + BQ - 1) / BQ;
+  const int n_st = (Nb - i_begin + BQ - 1) / BQ;
 
   // ---- staging: chunk i of this thread is row tid / CPR + ROWSTEP i, column
   // chunk tid % CPR, of both Q and dO.  Wave w loads vector w % 2 of the stage
@@ -414,7 +420,7 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ Dvec,
                         uint16_t* __restrict__ dQ, int N, int n_qtiles, uint32_t total, float c,
-                        float scale) {
+                        float scale, const int32_t* __restrict__ lens, int H) {
   constexpr int NT = 256;
   constexpr int BR = 128;                   // query rows per workgroup
   constexpr int BC = 64;                    // keys per stage
@@ -455,6 +461,11 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const int qrow = qw + l32;
   const size_t head_off = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * RB;
+  // Padded batch (causal only, as in the dK/dV kernel): query tiles wholly
+  // past the sequence's length Nb are skipped, and no key from Nb on is read
+  // for the rest (under the causal mask no real query sees one).
+  const int Nb = lens ? min(N, lens[bh / H]) : N;
+  if (q0 >= Nb) return;
 
   // Q and dO rows of this wavefront's queries as B operands (column = query)
   u32x4_t qf[NKS], of[NKS];
@@ -484,7 +495,7 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const int L16 = lane & 15, G = lane >> 4;
   const uint32_t tbase = (uint32_t)((h + 4 * (L16 >> 2)) * RBL + (16 * (G & 1) + 4 * (L16 & 3)) * 2);
 
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int kv_end = CAUSAL ? min(Nb, q0 + BR) : N;
   const int n_st = (kv_end + BC - 1) / BC;
 
   // ---- staging: chunk i of this thread is row tid / CPR + ROWSTEP i, column
@@ -690,7 +701,7 @@ static hipError_t dkdv_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2>), dim3(total), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     a.N, n_ktiles, total, s * kLog2e, -1.0f / s, a.scale);
+                     a.N, n_ktiles, total, s * kLog2e, -1.0f / s, a.scale, a.lens, a.H);
   return hipGetLastError();
 }
 
@@ -702,7 +713,7 @@ static hipError_t dq_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.N, n_qtiles, total,
-                     a.c, a.scale);
+                     a.c, a.scale, a.lens, a.H);
   return hipGetLastError();
 }
 

@@ -48,6 +48,11 @@ struct BwdArgs {
   int causal;
   int dtype;
   hipStream_t stream;
+  // Padded variable-length batch (causal only): lens[b] rows of the N of
+  // sequence b = bh / H are real, the rest zero with LSE +inf; the dK/dV
+  // and dQ kernels skip tiles past lens[b].  NULL: every row is real.
+  const int32_t* lens = nullptr;
+  int H = 1;
 };
 
 enum BwdStage { BWD_PREP = 0, BWD_DKDV = 1, BWD_DQ = 2 };
@@ -143,6 +148,7 @@ struct VarlenBwdArgs {
   void* pad[8];         // padded q, k, v, o, dout, dq, dk, dv
   float* lse_pad;       // [B, H, max_len]
   float* dvec;          // [B, H, max_len]
+  int32_t* lens;        // [B] clamped sequence lengths
   int B, H, max_len, d;
   int64_t total;
   float scale;
@@ -152,12 +158,13 @@ struct VarlenBwdArgs {
 };
 
 // Workspace of fa_bwd_varlen, carved into 256-byte aligned pieces: eight
-// padded 16-bit tensors of B H max_len d elements, then two float vectors of
-// B H max_len (padded LSE, D).
+// padded 16-bit tensors of B H max_len d elements, two float vectors of
+// B H max_len (padded LSE, D), then B int32 sequence lengths.
 inline size_t varlen_piece(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
 inline size_t varlen_bwd_workspace_bytes(int64_t B, int64_t H, int64_t max_len, int64_t d) {
   const size_t rows = (size_t)B * (size_t)H * (size_t)max_len;
-  return 8 * varlen_piece(rows * (size_t)d * 2) + 2 * varlen_piece(rows * sizeof(float));
+  return 8 * varlen_piece(rows * (size_t)d * 2) + 2 * varlen_piece(rows * sizeof(float)) +
+         varlen_piece((size_t)B * sizeof(int32_t));
 }
 
 hipError_t launch_bwd_varlen(const VarlenBwdArgs& a);

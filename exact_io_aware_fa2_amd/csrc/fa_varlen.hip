@@ -13,10 +13,9 @@
 //   - a padded query has dO = 0 and O = 0, so D = dO.O = 0 and dP = 0, and
 //     LSE = +infinity makes its probabilities exp(s - LSE) = 0: dS = P (dP - D)
 //     = 0 and its terms in dV = P^T dO and dK = dS^T Q vanish.
-// The copies are HBM-bound (16 bytes per thread, coalesced rows) and cost
-// far less than the backward itself; the padding costs the work of the
-// padded rows, which the kernels skip only where whole tiles are past the
-// diagonal.
+// The copies are HBM-bound (16 bytes per thread, coalesced rows).  The
+// dK/dV and dQ kernels are given the sequence lengths and skip every tile
+// that lies wholly past one, so padding costs only the ragged last tiles.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -59,8 +58,10 @@ __global__ __launch_bounds__(256) void varlen_copy_kernel(const uint16_t* __rest
 }
 
 // LSE packed [H, total] -> padded [B, H, max_len]; rows past a sequence's
-// length get +infinity (their probabilities are then exactly 0).
+// length get +infinity (their probabilities are then exactly 0).  The thread
+// of row 0 of head 0 also records the sequence's clamped length.
 __global__ __launch_bounds__(256) void varlen_lse_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                         int32_t* __restrict__ lens,
                                                          const int32_t* __restrict__ cu, int H, int max_len,
                                                          int64_t total, int64_t n) {
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -71,6 +72,7 @@ __global__ __launch_bounds__(256) void varlen_lse_kernel(const float* __restrict
   int start, len;
   seq_span(cu, b, total, max_len, start, len);
   dst[x] = r < len ? src[(size_t)h * total + start + r] : INFINITY;
+  if (r == 0 && h == 0) lens[b] = len;
 }
 
 hipError_t launch_bwd_varlen(const VarlenBwdArgs& a) {
@@ -82,8 +84,8 @@ hipError_t launch_bwd_varlen(const VarlenBwdArgs& a) {
     hipLaunchKernelGGL((varlen_copy_kernel<true>), grid_c, dim3(256), 0, a.stream, (const uint16_t*)src_in[t],
                        (uint16_t*)a.pad[t], a.cu, a.H, a.max_len, a.d, a.total, chunks);
   }
-  hipLaunchKernelGGL(varlen_lse_kernel, grid_l, dim3(256), 0, a.stream, a.lse, a.lse_pad, a.cu, a.H, a.max_len,
-                     a.total, rows);
+  hipLaunchKernelGGL(varlen_lse_kernel, grid_l, dim3(256), 0, a.stream, a.lse, a.lse_pad, a.lens, a.cu, a.H,
+                     a.max_len, a.total, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   BwdArgs b{};
@@ -105,6 +107,8 @@ hipError_t launch_bwd_varlen(const VarlenBwdArgs& a) {
   b.causal = 1;
   b.dtype = a.dtype;
   b.stream = a.stream;
+  b.lens = a.lens;  // skip the tiles past each sequence's length
+  b.H = a.H;
   e = launch_bwd(b);
   if (e != hipSuccess) return e;
   void* dst_out[3] = {a.dq, a.dk, a.dv};

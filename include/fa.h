@@ -235,8 +235,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
  * Computed exactly by copying the sequences into a padded
  * [B, H, max_len, d] batch in the workspace (zero rows after each length,
  * LSE +infinity there, which gives those rows zero probability and zero
- * gradient), running fa_bwd's kernels on it, and copying the first rows of
- * each sequence back.
+ * gradient), running fa_bwd's kernels on it (skipping every tile wholly
+ * past a sequence's length), and copying the first rows of each sequence
+ * back.
  *   q, k, v, o,   [total, H, d] of type dtype (FA_BF16 or FA_F16), packed
  *   dout          rows, 16-byte aligned; o and lse are fa_fwd_varlen's output
  *                 for these q, k, v with causal = 1.
@@ -249,7 +250,8 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
  *   max_len       the largest sequence length, in [1, 2^22].
  *   workspace     fa_bwd_varlen_workspace_bytes(B, H, max_len, d, dtype)
  *                 bytes, 16-byte aligned (8 B H max_len d 2-byte padded
- *                 tensors and two float vectors; rounded to 256 bytes each).
+ *                 tensors, two float vectors of B H max_len and B int32
+ *                 lengths, each rounded up to 256 bytes).
  * Deterministic (fixed reduction order).  Errors: FA_ERR_NULL, FA_ERR_SHAPE
  * (as fa_fwd for B, H, max_len; total < 1 or > 2^31 - 1), FA_ERR_HEADDIM
  * (d not 64 or 128), FA_ERR_DTYPE (not FA_BF16 / FA_F16), FA_ERR_ALIGN,

@@ -264,8 +264,8 @@ def test_varlen_bwd_argument_errors(lib):
     assert bvl(lib, scale=float("nan")) == FA_ERR_SCALE
     need = lib.fa_bwd_varlen_workspace_bytes(3, 4, 128, 128, 2)
     rows = 3 * 4 * 128
-    assert need == 8 * rows * 128 * 2 + 2 * rows * 4
-    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 64, 1) == 8 * 512 + 2 * 256
+    assert need == 8 * rows * 128 * 2 + 2 * rows * 4 + 256
+    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 64, 1) == 8 * 512 + 2 * 256 + 256
     assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 64, 0) == 0
     assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 32, 2) == 0
     assert bvl(lib, ws=None) == FA_ERR_WORKSPACE
