@@ -356,7 +356,7 @@ def bench_varlen(args):
     lib = fa.load_library()
     nb = int(lib.fa_fwd_varlen_workspace_bytes(len(lens), H, mx, mx, d, fa.FA_BF16))
     ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
-    nbb = int(lib.fa_bwd_varlen_workspace_bytes(len(lens), H, mx, d, fa.FA_BF16))
+    nbb = int(lib.fa_bwd_varlen_workspace_bytes(len(lens), H, q.shape[0], mx, d, fa.FA_BF16))
     wsb = torch.empty(nbb, dtype=torch.uint8, device=dev)
     fwd = lambda: fa.fa_fwd_varlen(q, k, v, cu, cu, o, lse, ws, mx, mx, scale, True)
     bwd = lambda: fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, dq, dk, dv, wsb, mx, scale)

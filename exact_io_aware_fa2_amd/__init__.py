@@ -84,7 +84,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, i64, i64, f32, i32,
                                 i32, vp]
     L.fa_bwd_varlen_workspace_bytes.restype = sz
-    L.fa_bwd_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    L.fa_bwd_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
     L.fa_bwd_varlen.restype = i32
     L.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, f32, i32,
                                 vp]
@@ -341,8 +341,8 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_q: int, max_k: int, caus
     return o, lse
 
 
-def fa_bwd_varlen_workspace_bytes(B: int, H: int, max_len: int, d: int, dtype: int) -> int:
-    return int(load_library().fa_bwd_varlen_workspace_bytes(B, H, max_len, d, dtype))
+def fa_bwd_varlen_workspace_bytes(B: int, H: int, total: int, max_len: int, d: int, dtype: int) -> int:
+    return int(load_library().fa_bwd_varlen_workspace_bytes(B, H, total, max_len, d, dtype))
 
 
 def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, dq, dk, dv, workspace, max_len: int, scale: float) -> None:
@@ -377,7 +377,7 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_len: int, scale: float | N
     B = int(cu_seqlens.shape[0]) - 1
     dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
     if workspace is None:
-        nb = fa_bwd_varlen_workspace_bytes(B, H, max_len, d, dtype_code(q))
+        nb = fa_bwd_varlen_workspace_bytes(B, H, total, max_len, d, dtype_code(q))
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
     fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, dq, dk, dv, workspace, max_len,
                   default_scale(d) if scale is None else scale)

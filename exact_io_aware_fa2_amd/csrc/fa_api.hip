@@ -413,10 +413,12 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
 
 extern "C" {
 
-size_t fa_bwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t max_len, int64_t d, int dtype) {
+size_t fa_bwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t total, int64_t max_len, int64_t d,
+                                     int dtype) {
   if (check_shape(B, H, max_len, d) != FA_OK) return 0;
+  if (total < 1 || total > INT32_MAX || total * H > INT32_MAX) return 0;
   if (dtype != FA_F16 && dtype != FA_BF16) return 0;
-  return fa::varlen_bwd_workspace_bytes(B, H, max_len, d);
+  return (size_t)(total * H) * sizeof(float);
 }
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -429,18 +431,21 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   if (!cu_seqlens) return FA_ERR_NULL;
   int st = check_shape(B, H, max_len, d);
   if (st != FA_OK) return st;
-  if (total < 1 || total > INT32_MAX) return FA_ERR_SHAPE;
+  if (total < 1 || total > INT32_MAX || total * H > INT32_MAX) return FA_ERR_SHAPE;
+  // one sequence's rows, and the rows past them a 128-row tile and its
+  // prefetch reach, stay within 32-bit byte offsets of its first row
+  if ((max_len + 128) * H * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return FA_ERR_ALIGN;
   st = check_scale(scale);
   if (st != FA_OK) return st;
-  const size_t need = fa::varlen_bwd_workspace_bytes(B, H, max_len, d);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < fa_bwd_varlen_workspace_bytes(B, H, total, max_len, d, dtype))
+    return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
 
-  fa::VarlenBwdArgs a{};
+  fa::BwdArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -450,28 +455,19 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.cu = cu_seqlens;
-  const size_t rows = (size_t)(B * H * max_len);
-  char* w = (char*)workspace;
-  for (int t = 0; t < 8; ++t) {
-    a.pad[t] = w;
-    w += fa::varlen_piece(rows * (size_t)d * 2);
-  }
-  a.lse_pad = (float*)w;
-  w += fa::varlen_piece(rows * sizeof(float));
-  a.dvec = (float*)w;
-  w += fa::varlen_piece(rows * sizeof(float));
-  a.lens = (int32_t*)w;
-  a.B = (int)B;
-  a.H = (int)H;
-  a.max_len = (int)max_len;
+  a.dvec = (float*)workspace;  // D_i, [H, total]
+  a.BH = (int)(B * H);
+  a.N = (int)max_len;
   a.d = (int)d;
-  a.total = total;
   a.scale = scale;
   a.c = exp2_factor(scale);
+  a.causal = 1;
   a.dtype = dtype;
   a.stream = (hipStream_t)stream;
-  return status_of(fa::launch_bwd_varlen(a));
+  a.cu = cu_seqlens;
+  a.H = (int)H;
+  a.total = (int)total;
+  return status_of(fa::launch_bwd(a));
 }
 
 }  // extern "C"

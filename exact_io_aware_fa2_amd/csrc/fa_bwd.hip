@@ -36,10 +36,12 @@ namespace fa {
 
 // ------------------------------------------------------------------ D_i
 
-template <class TR, int D>
+// VL: O and dO are a packed [total, H, D] batch (row = t H + h) and D_i is
+// stored as [H, total], the layout of the packed LSE.
+template <class TR, int D, bool VL>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
                                                       const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ Dv, int rows) {
+                                                      float* __restrict__ Dv, int rows, int H, int total) {
   constexpr int KCH = D / 8;            // lanes per row
   constexpr int RPB = 256 / KCH;        // rows per workgroup
   const int tid = threadIdx.x;
@@ -54,7 +56,45 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   }
 #pragma unroll
   for (int off = KCH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && ch == 0) Dv[row] = acc;
+  if (row < rows && ch == 0) Dv[VL ? (size_t)(row % H) * total + row / H : (size_t)row] = acc;
+}
+
+// ------------------------------------------------------------------ head placement
+
+// Where the rows of head bh lie.  Dense [BH, N, D]: rows of D elements from
+// bh N D, vectors (LSE, D_i) from bh N, all N rows real.  Packed (VL): head
+// h of sequence b = bh / H owns rows cu[b] .. cu[b + 1] - 1 of [total, H, D]
+// (row stride H D, vectors [H, total] from h total + cu[b]), clamped into
+// [0, total] and to N rows, so malformed prefix sums never move an access out
+// of the tensors.  `bytes` ends right after the last real row: buffer loads
+// of rows from Nb on read zeros, as past the end of a dense head.
+struct HeadRows {
+  size_t off;       // element offset of row 0
+  size_t vec;       // element offset of vector entry 0
+  uint32_t rs;      // row stride (bytes)
+  uint32_t bytes;   // buffer range from row 0
+  int Nb;           // real rows
+};
+
+template <int D, bool VL>
+__device__ inline HeadRows head_rows(int bh, int N, const int32_t* __restrict__ cu, int H, int total) {
+  HeadRows r;
+  if constexpr (VL) {
+    const int b = bh / H, hd = bh - b * H;
+    const int64_t s0 = min(max((int64_t)cu[b], (int64_t)0), (int64_t)total);
+    r.Nb = (int)min(max((int64_t)cu[b + 1] - s0, (int64_t)0), min((int64_t)N, (int64_t)total - s0));
+    r.off = ((size_t)s0 * H + hd) * D;
+    r.vec = (size_t)hd * total + s0;
+    r.rs = (uint32_t)H * (2 * D);
+    r.bytes = r.Nb > 0 ? (uint32_t)(r.Nb - 1) * r.rs + 2 * D : 0u;
+  } else {
+    r.Nb = N;
+    r.off = (size_t)bh * N * D;
+    r.vec = (size_t)bh * N;
+    r.rs = 2 * D;
+    r.bytes = (uint32_t)N * (2 * D);
+  }
+  return r;
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -79,14 +119,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // the dV/dK products lie 4 rows apart: with the padded rows, both the row
 // reads (S, dP) and the transposed reads (dV, dK) are free of bank conflicts,
 // and no transposed copy of Q or dO is staged.
-template <class TR, int D, bool CAUSAL, int OCC>
+template <class TR, int D, bool CAUSAL, int OCC, bool VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dvec,
                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_ktiles,
                           uint32_t total, float c, float neg_inv_scale, float scale,
-                          const int32_t* __restrict__ lens, int H) {
+                          const int32_t* __restrict__ cu, int H, int n_rows) {
   constexpr int NT = 256;
   constexpr int BKV = 128;                  // keys per workgroup
   constexpr int BQ = 64;                    // query rows per stage
@@ -126,20 +166,21 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int k0 = kt * BKV;
   const int kw = k0 + 32 * w;               // first key of this wavefront
   const int key = kw + l32;
-  const size_t head_off = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * RB;
-  // Padded batch (causal only): rows from the sequence's length Nb on are
-  // zero with LSE +inf, so queries past Nb add nothing and keys past Nb are
-  // never wanted; tiles wholly past Nb are skipped.
-  const int Nb = lens ? min(N, lens[bh / H]) : N;
+  // Packed batches are causal only: a real query never sees a key past
+  // Nb, and tiles wholly past Nb are skipped.
+  const HeadRows hr = head_rows<D, VL>(bh, N, cu, H, n_rows);
+  const int Nb = hr.Nb;
   if (k0 >= Nb) return;
+  const size_t head_off = hr.off;
+  const uint32_t head_bytes = hr.bytes;
+  const uint32_t rs = VL ? hr.rs : RB;
 
   // K and V rows of this wavefront's keys as B operands (column = key)
   u32x4_t kf[NKS], vf[NKS];
   {
     const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
     const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
-    const uint32_t off = (uint32_t)key * RB + 16 * h;
+    const uint32_t off = (uint32_t)key * rs + 16 * h;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       kf[ks] = buf_load16(kres, off + 32 * ks);
@@ -173,9 +214,9 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const rsrc_t ores = make_rsrc(dO + head_off, head_bytes);
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const bool is_d = (wu & 1) != 0;
-  const rsrc_t vres = make_rsrc(is_d ? (const void*)(Dvec + (size_t)bh * N) : (const void*)(LSE + (size_t)bh * N),
-                                (uint32_t)N * 4);
-  const uint32_t g_off = (uint32_t)(tid / CPR) * RB + (tid % CPR) * 16;
+  const rsrc_t vres = make_rsrc(is_d ? (const void*)(Dvec + hr.vec) : (const void*)(LSE + hr.vec),
+                                (uint32_t)Nb * 4);
+  const uint32_t g_off = (uint32_t)(tid / CPR) * rs + (tid % CPR) * 16;
   const uint32_t s_off = (uint32_t)(tid / CPR) * RBL + (tid % CPR) * 16;
   const int vrow = (lane & 32) + perm(lane & 31);
   const uint32_t v_off = OFF_L + 4 * BQ * wu + 4 * lane;
@@ -189,11 +230,11 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   // staging part j < NCH: Q chunk j; j < 2 NCH: dO chunk j - NCH; j = 2 NCH: the vector
   constexpr int NPART = 2 * NCH + 1;
   auto load_part = [&](int i0, int j, int t = 0) __attribute__((always_inline)) {
-    const uint32_t base = g_off + (uint32_t)i0 * RB;
+    const uint32_t base = g_off + (uint32_t)i0 * rs;
     if (j < NCH) {
-      sq[t][j] = buf_load16(qres, base + ROWSTEP * j * RB);
+      sq[t][j] = buf_load16(qres, base + ROWSTEP * j * rs);
     } else if (j < 2 * NCH) {
-      so[t][j - NCH] = buf_load16(ores, base + ROWSTEP * (j - NCH) * RB);
+      so[t][j - NCH] = buf_load16(ores, base + ROWSTEP * (j - NCH) * rs);
     } else {
       vidx[t] = i0 + vrow;
       vraw[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vres, (uint32_t)vidx[t] * 4, 0, 0));
@@ -206,7 +247,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       *(u32x4_t*)(smem + sb + OFF_O + s_off + ROWSTEP * (j - NCH) * RBL) = so[t][j - NCH];
     } else {
       // rows past the end: -inf initialises their S, so P = 0; D = 0
-      const bool in = vidx[t] < N;
+      const bool in = vidx[t] < Nb;
       *(float*)(smem + sb + v_off) = is_d ? (in ? -vraw[t] : 0.0f) : (in ? vraw[t] * neg_inv_scale : -INFINITY);
     }
   };
@@ -391,11 +432,12 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                           TR::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3])};
     }
   static_assert(4 * kTileRowsBytes<D> <= STG, "four wavefronts' rows fit one stage slot");
-  const int nrows = min(32, N - kw);
-  store_tile_rows<D>(smem + ((n_st + 1) & 3) * STG + w * kTileRowsBytes<D>, ok, dK + head_off + (size_t)kw * D,
-                     nrows, lane);
-  store_tile_rows<D>(smem + ((n_st + 2) & 3) * STG + w * kTileRowsBytes<D>, ov, dV + head_off + (size_t)kw * D,
-                     nrows, lane);
+  const int nrows = min(32, Nb - kw);
+  const size_t ostride = VL ? (size_t)H * D : (size_t)D;
+  store_tile_rows<D>(smem + ((n_st + 1) & 3) * STG + w * kTileRowsBytes<D>, ok,
+                     dK + head_off + (size_t)kw * ostride, nrows, lane, ostride);
+  store_tile_rows<D>(smem + ((n_st + 2) & 3) * STG + w * kTileRowsBytes<D>, ov,
+                     dV + head_off + (size_t)kw * ostride, nrows, lane, ostride);
 }
 
 // ------------------------------------------------------------------ dQ
@@ -414,13 +456,13 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 // are per-lane constants (D enters as the dP accumulators' initial value).
 // Keys past the end need no mask: their K and V rows read as zeros, so their
 // dS multiplies a zero row of K.
-template <class TR, int D, bool CAUSAL, int OCC>
+template <class TR, int D, bool CAUSAL, int OCC, bool VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ Dvec,
                         uint16_t* __restrict__ dQ, int N, int n_qtiles, uint32_t total, float c,
-                        float scale, const int32_t* __restrict__ lens, int H) {
+                        float scale, const int32_t* __restrict__ cu, int H, int n_rows) {
   constexpr int NT = 256;
   constexpr int BR = 128;                   // query rows per workgroup
   constexpr int BC = 64;                    // keys per stage
@@ -459,20 +501,22 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const int q0 = qt * BR;
   const int qw = q0 + 32 * w;               // first query row of this wavefront
   const int qrow = qw + l32;
-  const size_t head_off = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * RB;
-  // Padded batch (causal only, as in the dK/dV kernel): query tiles wholly
-  // past the sequence's length Nb are skipped, and no key from Nb on is read
-  // for the rest (under the causal mask no real query sees one).
-  const int Nb = lens ? min(N, lens[bh / H]) : N;
+  // Packed batches (causal only, as in the dK/dV kernel): query tiles
+  // wholly past the sequence's length Nb are skipped, and no key from Nb on
+  // is read for the rest (under the causal mask no real query sees one).
+  const HeadRows hr = head_rows<D, VL>(bh, N, cu, H, n_rows);
+  const int Nb = hr.Nb;
   if (q0 >= Nb) return;
+  const size_t head_off = hr.off;
+  const uint32_t head_bytes = hr.bytes;
+  const uint32_t rs = VL ? hr.rs : RB;
 
   // Q and dO rows of this wavefront's queries as B operands (column = query)
   u32x4_t qf[NKS], of[NKS];
   {
     const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
     const rsrc_t ores = make_rsrc(dO + head_off, head_bytes);
-    const uint32_t off = (uint32_t)qrow * RB + 16 * h;
+    const uint32_t off = (uint32_t)qrow * rs + 16 * h;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       qf[ks] = buf_load16(qres, off + 32 * ks);
@@ -480,8 +524,8 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     }
   }
   // rows past the end: P = exp2(-inf) = 0, so dS = 0 there
-  const float lq = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dd = qrow < N ? Dvec[(size_t)bh * N + qrow] : 0.0f;
+  const float lq = qrow < Nb ? LSE[hr.vec + qrow] * kLog2e : INFINITY;
+  const float dd = qrow < Nb ? Dvec[hr.vec + qrow] : 0.0f;
   f32x16_t negd;  // initial value of the dP accumulators
 #pragma unroll
   for (int i = 0; i < 16; ++i) negd[i] = -dd;
@@ -495,21 +539,21 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const int L16 = lane & 15, G = lane >> 4;
   const uint32_t tbase = (uint32_t)((h + 4 * (L16 >> 2)) * RBL + (16 * (G & 1) + 4 * (L16 & 3)) * 2);
 
-  const int kv_end = CAUSAL ? min(Nb, q0 + BR) : N;
+  const int kv_end = CAUSAL ? min(Nb, q0 + BR) : Nb;
   const int n_st = (kv_end + BC - 1) / BC;
 
   // ---- staging: chunk i of this thread is row tid / CPR + ROWSTEP i, column
   // chunk tid % CPR, of both K and V (part j < NCH: K chunk j, else V chunk j - NCH)
   const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
   const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
-  const uint32_t g_off = (uint32_t)(tid / CPR) * RB + (tid % CPR) * 16;
+  const uint32_t g_off = (uint32_t)(tid / CPR) * rs + (tid % CPR) * 16;
   const uint32_t s_off = (uint32_t)(tid / CPR) * RBL + (tid % CPR) * 16;
   // (set 1 of the staging registers: prologue only, two stages in flight)
   u32x4_t sk[2][NCH], sv[2][NCH];
   auto load_part = [&](int j0, int j, int t = 0) __attribute__((always_inline)) {
-    const uint32_t base = g_off + (uint32_t)j0 * RB;
-    if (j < NCH) sk[t][j] = buf_load16(kres, base + ROWSTEP * j * RB);
-    else sv[t][j - NCH] = buf_load16(vres, base + ROWSTEP * (j - NCH) * RB);
+    const uint32_t base = g_off + (uint32_t)j0 * rs;
+    if (j < NCH) sk[t][j] = buf_load16(kres, base + ROWSTEP * j * rs);
+    else sv[t][j - NCH] = buf_load16(vres, base + ROWSTEP * (j - NCH) * rs);
   };
   auto store_part = [&](uint32_t sb, int j, int t = 0) __attribute__((always_inline)) {
     if (j < NCH) *(u32x4_t*)(smem + sb + s_off + ROWSTEP * j * RBL) = sk[t][j];
@@ -672,8 +716,9 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   // dQ stored as whole rows through LDS: after the last barrier every stage
   // slot but that of the last block is free
   static_assert(4 * kTileRowsBytes<D> <= STG, "four wavefronts' rows fit one stage slot");
-  store_tile_rows<D>(smem + ((n_st + 1) & 3) * STG + w * kTileRowsBytes<D>, od, dQ + head_off + (size_t)qw * D,
-                     min(32, N - qw), lane);
+  const size_t ostride = VL ? (size_t)H * D : (size_t)D;
+  store_tile_rows<D>(smem + ((n_st + 1) & 3) * STG + w * kTileRowsBytes<D>, od,
+                     dQ + head_off + (size_t)qw * ostride, min(32, Nb - qw), lane, ostride);
 }
 
 // ------------------------------------------------------------------ launch
@@ -681,15 +726,21 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
 template <class TR, int D>
 static hipError_t prep_t(const BwdArgs& a) {
-  const int rows = a.BH * a.N;
   constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<TR, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0,
-                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dvec, rows);
+  if (a.cu) {  // packed: total H rows, D_i stored [H, total]
+    const int rows = a.total * a.H;
+    hipLaunchKernelGGL((bwd_pre_kernel<TR, D, true>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dvec, rows, a.H, a.total);
+  } else {
+    const int rows = a.BH * a.N;
+    hipLaunchKernelGGL((bwd_pre_kernel<TR, D, false>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dvec, rows, 1, 0);
+  }
   return hipGetLastError();
 }
 
-template <class TR, int D, bool CAUSAL>
-static hipError_t dkdv_t(const BwdArgs& a) {
+template <class TR, int D, bool CAUSAL, bool VL>
+static void dkdv_launch(const BwdArgs& a) {
   const int n_ktiles = (a.N + 127) / 128;
   const uint32_t total = (uint32_t)(n_ktiles * a.BH);
   // The kernel forms the exponent as (q.k - LSE / s) * s log2 e with s the
@@ -698,22 +749,44 @@ static hipError_t dkdv_t(const BwdArgs& a) {
   // exponent is -LSE log2 e, its value at scale 0 (dK is still multiplied by
   // the true scale).
   const float s = a.scale >= 0x1p-100f ? a.scale : 0x1p-100f;
-  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2>), dim3(total), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, VL>), dim3(total), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     a.N, n_ktiles, total, s * kLog2e, -1.0f / s, a.scale, a.lens, a.H);
+                     a.N, n_ktiles, total, s * kLog2e, -1.0f / s, a.scale, a.cu, a.H, a.total);
+}
+
+template <class TR, int D, bool CAUSAL>
+static hipError_t dkdv_t(const BwdArgs& a) {
+  if constexpr (CAUSAL) {
+    if (a.cu) dkdv_launch<TR, D, true, true>(a);
+    else dkdv_launch<TR, D, true, false>(a);
+  } else {
+    if (a.cu) return hipErrorInvalidValue;  // packed batches are causal only
+    dkdv_launch<TR, D, false, false>(a);
+  }
   return hipGetLastError();
 }
 
 // dQ: the pipelined kernel, one wavefront per SIMD at d = 128 and two at d = 64
-template <class TR, int D, bool CAUSAL>
-static hipError_t dq_t(const BwdArgs& a) {
+template <class TR, int D, bool CAUSAL, bool VL>
+static void dq_launch(const BwdArgs& a) {
   const int n_qtiles = (a.N + 127) / 128;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2>), dim3(total), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+  hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, VL>), dim3(total), dim3(256), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.N, n_qtiles, total,
-                     a.c, a.scale, a.lens, a.H);
+                     a.c, a.scale, a.cu, a.H, a.total);
+}
+
+template <class TR, int D, bool CAUSAL>
+static hipError_t dq_t(const BwdArgs& a) {
+  if constexpr (CAUSAL) {
+    if (a.cu) dq_launch<TR, D, true, true>(a);
+    else dq_launch<TR, D, true, false>(a);
+  } else {
+    if (a.cu) return hipErrorInvalidValue;
+    dq_launch<TR, D, false, false>(a);
+  }
   return hipGetLastError();
 }
 

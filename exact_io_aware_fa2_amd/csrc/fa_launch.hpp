@@ -48,11 +48,13 @@ struct BwdArgs {
   int causal;
   int dtype;
   hipStream_t stream;
-  // Padded variable-length batch (causal only): lens[b] rows of the N of
-  // sequence b = bh / H are real, the rest zero with LSE +inf; the dK/dV
-  // and dQ kernels skip tiles past lens[b].  NULL: every row is real.
-  const int32_t* lens = nullptr;
+  // Packed variable-length batch (causal only; fa_bwd_varlen): q, k, v, o,
+  // dout, dq, dk, dv are [total, H, d], lse and dvec [H, total], and head h
+  // of sequence b = bh / H owns rows cu[b] .. cu[b + 1] - 1 (at most N of
+  // them; BH = B H).  NULL: the dense [BH, N, d] layout.
+  const int32_t* cu = nullptr;
   int H = 1;
+  int total = 0;
 };
 
 enum BwdStage { BWD_PREP = 0, BWD_DKDV = 1, BWD_DQ = 2 };
@@ -131,43 +133,6 @@ inline size_t kv_workspace_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t d) 
 
 hipError_t launch_fwd_kvcache(const KvArgs& a);
 
-// Backward of causal self-attention over a packed batch (fa_bwd_varlen): the
-// sequences are copied into a padded [B, H, max_len, d] batch in the
-// workspace, the square backward runs on it, and dQ, dK, dV are copied back.
-struct VarlenBwdArgs {
-  const void* q;        // [total, H, d]
-  const void* k;
-  const void* v;
-  const void* o;
-  const float* lse;     // [H, total]
-  const void* dout;
-  void* dq;             // [total, H, d]
-  void* dk;
-  void* dv;
-  const int32_t* cu;    // [B + 1] prefix sums of the sequence lengths
-  void* pad[8];         // padded q, k, v, o, dout, dq, dk, dv
-  float* lse_pad;       // [B, H, max_len]
-  float* dvec;          // [B, H, max_len]
-  int32_t* lens;        // [B] clamped sequence lengths
-  int B, H, max_len, d;
-  int64_t total;
-  float scale;
-  float c;              // scale * log2(e)
-  int dtype;
-  hipStream_t stream;
-};
-
-// Workspace of fa_bwd_varlen, carved into 256-byte aligned pieces: eight
-// padded 16-bit tensors of B H max_len d elements, two float vectors of
-// B H max_len (padded LSE, D), then B int32 sequence lengths.
-inline size_t varlen_piece(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
-inline size_t varlen_bwd_workspace_bytes(int64_t B, int64_t H, int64_t max_len, int64_t d) {
-  const size_t rows = (size_t)B * (size_t)H * (size_t)max_len;
-  return 8 * varlen_piece(rows * (size_t)d * 2) + 2 * varlen_piece(rows * sizeof(float)) +
-         varlen_piece((size_t)B * sizeof(int32_t));
-}
-
-hipError_t launch_bwd_varlen(const VarlenBwdArgs& a);
 
 // Measurement probe (fa_probe_mfma_bf16): workgroups of 4 wavefronts.
 hipError_t launch_mfma_peak(int workgroups, int iters, hipStream_t stream);

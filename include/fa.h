@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum {
   FA_OK = 0,
@@ -229,35 +229,35 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
  * and key prefix sums; the pages' drop-in use with the usual attention
  * interfaces: "FlashAttention-2 (DE)", "Anwendung und Integration in das
  * Ökosystem"; the gradient, recomputed as in fa_bwd: "FlashAttention"
- * lexicon, "Methodische Grundlagen").
- * Sequence b owns rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of every tensor and
- * attends causally within itself (key j visible to query i iff j <= i).
- * Computed exactly by copying the sequences into a padded
- * [B, H, max_len, d] batch in the workspace (zero rows after each length,
- * LSE +infinity there, which gives those rows zero probability and zero
- * gradient), running fa_bwd's kernels on it (skipping every tile wholly
- * past a sequence's length), and copying the first rows of each sequence
- * back.
+ * lexicon, "Methodische Grundlagen").  Sequence b owns rows
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 of every tensor and attends causally
+ * within itself (key j visible to query i iff j <= i).  fa_bwd's kernels
+ * read and write the packed rows in place (row stride H d), one workgroup
+ * per head and 128-row tile of max_len, and skip tiles past a sequence's
+ * length.
  *   q, k, v, o,   [total, H, d] of type dtype (FA_BF16 or FA_F16), packed
  *   dout          rows, 16-byte aligned; o and lse are fa_fwd_varlen's output
  *                 for these q, k, v with causal = 1.
  *   lse           [H, total] float32 (natural log).
  *   cu_seqlens    DEVICE int32 [B + 1] non-decreasing prefix sums (4-byte
- *                 aligned), clamped like fa_fwd_varlen's.
+ *                 aligned), clamped like fa_fwd_varlen's (entries to
+ *                 [0, total], a sequence's length to [0, max_len]).
  *   dq, dk, dv    [total, H, d] outputs, same type; rows outside every
  *                 sequence, and rows past max_len of a longer sequence, are
  *                 left unchanged.
- *   max_len       the largest sequence length, in [1, 2^22].
- *   workspace     fa_bwd_varlen_workspace_bytes(B, H, max_len, d, dtype)
- *                 bytes, 16-byte aligned (8 B H max_len d 2-byte padded
- *                 tensors, two float vectors of B H max_len and B int32
- *                 lengths, each rounded up to 256 bytes).
+ *   max_len       the largest sequence length, in [1, 2^22];
+ *                 (max_len + 128) * H * d * 2 must stay below 2^31 bytes.
+ *   workspace     fa_bwd_varlen_workspace_bytes(B, H, total, max_len, d,
+ *                 dtype) bytes (total * H floats: D_i = dO_i . O_i),
+ *                 16-byte aligned, contents need not be initialised.
  * Deterministic (fixed reduction order).  Errors: FA_ERR_NULL, FA_ERR_SHAPE
- * (as fa_fwd for B, H, max_len; total < 1 or > 2^31 - 1), FA_ERR_HEADDIM
- * (d not 64 or 128), FA_ERR_DTYPE (not FA_BF16 / FA_F16), FA_ERR_ALIGN,
- * FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_HIP.  The workspace size function
- * returns 0 for arguments the entry point rejects. */
-size_t fa_bwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t max_len, int64_t d, int dtype);
+ * (as fa_fwd for B, H, max_len; total < 1, total * H > 2^31 - 1, or the
+ * offset limit), FA_ERR_HEADDIM (d not 64 or 128), FA_ERR_DTYPE (not
+ * FA_BF16 / FA_F16), FA_ERR_ALIGN, FA_ERR_SCALE, FA_ERR_WORKSPACE,
+ * FA_ERR_HIP.  The workspace size function returns 0 for arguments the
+ * entry point rejects. */
+size_t fa_bwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t total, int64_t max_len, int64_t d,
+                                     int dtype);
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   const void* dout, const int32_t* cu_seqlens, void* dq, void* dk, void* dv, void* workspace,

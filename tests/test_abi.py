@@ -42,7 +42,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 5
+    assert lib.fa_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -262,12 +262,13 @@ def test_varlen_bwd_argument_errors(lib):
         assert bvl(lib, ptrs) == FA_ERR_ALIGN, i
     assert bvl(lib, cu=P[10] + 2) == FA_ERR_ALIGN
     assert bvl(lib, scale=float("nan")) == FA_ERR_SCALE
-    need = lib.fa_bwd_varlen_workspace_bytes(3, 4, 128, 128, 2)
-    rows = 3 * 4 * 128
-    assert need == 8 * rows * 128 * 2 + 2 * rows * 4 + 256
-    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 64, 1) == 8 * 512 + 2 * 256 + 256
-    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 64, 0) == 0
-    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 32, 2) == 0
+    assert bvl(lib, total=(1 << 29)) == FA_ERR_SHAPE  # total * H = 2^31
+    assert bvl(lib, H=64, max_len=(1 << 17) - 128) == FA_ERR_SHAPE  # 2^17 * 64 * 128 * 2 = 2^31 bytes
+    need = lib.fa_bwd_varlen_workspace_bytes(3, 4, 300, 128, 128, 2)
+    assert need == 4 * 300 * 4
+    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 3, 64, 0) == 0
+    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 3, 32, 2) == 0
+    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 0, 3, 64, 2) == 0
     assert bvl(lib, ws=None) == FA_ERR_WORKSPACE
     assert bvl(lib, wsb=need - 1) == FA_ERR_WORKSPACE
     assert bvl(lib, ws=P[11] + 4, wsb=need) == FA_ERR_ALIGN

@@ -37,7 +37,8 @@ def _run(inp, dtype, scale, max_len=None, init=None):
         dq, dk, dv = fa.bwd_varlen(q, k, v, o, lse, do, cu, mx, scale)
     else:
         dq, dk, dv = (to_device(init, dtype) for _ in range(3))
-        nb = fa.fa_bwd_varlen_workspace_bytes(len(inp["cu_q"]) - 1, q.shape[1], mx, q.shape[2], fa.dtype_code(q))
+        nb = fa.fa_bwd_varlen_workspace_bytes(len(inp["cu_q"]) - 1, q.shape[1], q.shape[0], mx, q.shape[2],
+                                              fa.dtype_code(q))
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
         fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, dq, dk, dv, ws, mx, scale)
     torch.cuda.synchronize()
@@ -90,8 +91,9 @@ def test_varlen_bwd_small(case, d, dtype):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_varlen_bwd_equal_lengths_bitwise_equal_the_ordinary_backward(d):
-    """Equal lengths: the padded batch is the [B, H, N, d] batch itself, so
-    the gradients are those of fa_bwd on the same values, bit for bit."""
+    """Equal lengths: the packed kernels take the same tiles in the same
+    order as fa_bwd on the [B, H, N, d] layout of the same values (only the
+    row addressing differs), so the gradients agree bit for bit."""
     import torch
     fa = lib()
     B, H, N = 3, 4, 300
@@ -128,8 +130,9 @@ def test_varlen_bwd_rows_outside_the_sequences_are_left_unchanged():
 
 
 def test_varlen_bwd_max_len_above_every_length_and_determinism():
-    """A max_len larger than every sequence only adds padded rows; repeated
-    calls are bitwise identical."""
+    """A max_len larger than every sequence only adds workgroups that find
+    their tiles past the sequence and return; repeated calls are bitwise
+    identical."""
     lens = [70, 130]
     inp = si.make_varlen_inputs(lens, lens, 2, 128, "bf16", 1.0, 9420, backward=True)
     say("varlen bwd max_len 256 over lengths [70, 130]")
@@ -162,3 +165,27 @@ def test_varlen_bwd_prefill_batch_full_size_sampled():
     shortest = int(np.argmin(lens))
     _check_seqs(inp, grads, ref, [shortest], [0, 15], "prefill shortest sequence")
     _check_seqs(inp, grads, ref, [5], [7], "prefill sequence 5")
+
+
+def test_varlen_bwd_malformed_prefix_sums_stay_in_bounds():
+    """Prefix sums that decrease or pass the end are clamped (no access
+    leaves the tensors).  Sequence 1 has a negative length (skipped) and
+    sequence 2 starts at row 30 and is cut at total = 120 rows, so rows
+    30..49 are claimed twice; dQ of rows 0..29 involves sequence 0's rows
+    0..29 only and stays exact."""
+    lens = [50, 0, 70]
+    inp = si.make_varlen_inputs(lens, lens, 2, 128, "bf16", 1.0, 9430, backward=True)
+    inp["cu_q"] = np.array([0, 50, 30, 100000], np.int32)
+    say(f"varlen bwd malformed cu {inp['cu_q'].tolist()}")
+    grads = _run(inp, "bf16", 0.088, max_len=128)
+    for g in grads:
+        assert np.isfinite(g).all()
+
+    def ref(b, h):
+        r = attention_bwd_head(inp["q"][0][0:50, h], inp["k"][0][0:50, h], inp["v"][0][0:50, h],
+                               inp["do"][0][0:50, h], 0.088, True)
+        return tuple(x[:30] for x in r)
+
+    cu_ok = np.array([0, 30], np.int32)
+    _check_seqs({"cu_q": cu_ok}, (grads[0], grads[0], grads[0]),
+                lambda b, h: (ref(b, h)[0],) * 3, [0], [0, 1], "sequence 0 dQ rows 0..29")
