@@ -368,6 +368,30 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
     return FA_ERR_ALIGN;
   st = check_scale(scale);
   if (st != FA_OK) return st;
+  // Self-attention (one prefix-sum array for queries and keys): the square
+  // forward kernels, reading and writing the packed rows in place, when the
+  // head size is theirs and the rows a 256-row tile and its prefetch reach
+  // stay within 32-bit byte offsets of a sequence's first row.
+  if (cu_seqlens_q == cu_seqlens_k && total_q == total_k && max_q == max_k && (d == 64 || d == 128) &&
+      (max_q + 512) * H * d * 2 < (int64_t(1) << 31) && total_q * H <= INT32_MAX) {
+    fa::FwdArgs f;
+    f.q = q;
+    f.k = k;
+    f.v = v;
+    f.o = o;
+    f.lse = lse;
+    f.BH = (int)(B * H);
+    f.N = (int)max_q;
+    f.d = (int)d;
+    f.c = exp2_factor(scale);
+    f.causal = causal != 0;
+    f.dtype = dtype;
+    f.stream = (hipStream_t)stream;
+    f.cu = cu_seqlens_q;
+    f.H = (int)H;
+    f.total = (int)total_q;
+    return status_of(fa::launch_fwd(f));
+  }
   const size_t need = fa::kv_workspace_bytes(B * H, max_q, max_k, d);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;

@@ -59,44 +59,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   if (row < rows && ch == 0) Dv[VL ? (size_t)(row % H) * total + row / H : (size_t)row] = acc;
 }
 
-// ------------------------------------------------------------------ head placement
-
-// Where the rows of head bh lie.  Dense [BH, N, D]: rows of D elements from
-// bh N D, vectors (LSE, D_i) from bh N, all N rows real.  Packed (VL): head
-// h of sequence b = bh / H owns rows cu[b] .. cu[b + 1] - 1 of [total, H, D]
-// (row stride H D, vectors [H, total] from h total + cu[b]), clamped into
-// [0, total] and to N rows, so malformed prefix sums never move an access out
-// of the tensors.  `bytes` ends right after the last real row: buffer loads
-// of rows from Nb on read zeros, as past the end of a dense head.
-struct HeadRows {
-  size_t off;       // element offset of row 0
-  size_t vec;       // element offset of vector entry 0
-  uint32_t rs;      // row stride (bytes)
-  uint32_t bytes;   // buffer range from row 0
-  int Nb;           // real rows
-};
-
-template <int D, bool VL>
-__device__ inline HeadRows head_rows(int bh, int N, const int32_t* __restrict__ cu, int H, int total) {
-  HeadRows r;
-  if constexpr (VL) {
-    const int b = bh / H, hd = bh - b * H;
-    const int64_t s0 = min(max((int64_t)cu[b], (int64_t)0), (int64_t)total);
-    r.Nb = (int)min(max((int64_t)cu[b + 1] - s0, (int64_t)0), min((int64_t)N, (int64_t)total - s0));
-    r.off = ((size_t)s0 * H + hd) * D;
-    r.vec = (size_t)hd * total + s0;
-    r.rs = (uint32_t)H * (2 * D);
-    r.bytes = r.Nb > 0 ? (uint32_t)(r.Nb - 1) * r.rs + 2 * D : 0u;
-  } else {
-    r.Nb = N;
-    r.off = (size_t)bh * N * D;
-    r.vec = (size_t)bh * N;
-    r.rs = 2 * D;
-    r.bytes = (uint32_t)N * (2 * D);
-  }
-  return r;
-}
-
 // ------------------------------------------------------------------ dK, dV
 
 // dK, dV software-pipelined inside each wavefront: one wavefront per SIMD,
@@ -170,7 +132,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   // Nb, and tiles wholly past Nb are skipped.
   const HeadRows hr = head_rows<D, VL>(bh, N, cu, H, n_rows);
   const int Nb = hr.Nb;
-  if (k0 >= Nb) return;
+  if (VL && k0 >= Nb) return;
   const size_t head_off = hr.off;
   const uint32_t head_bytes = hr.bytes;
   const uint32_t rs = VL ? hr.rs : RB;
@@ -506,7 +468,7 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   // is read for the rest (under the causal mask no real query sees one).
   const HeadRows hr = head_rows<D, VL>(bh, N, cu, H, n_rows);
   const int Nb = hr.Nb;
-  if (q0 >= Nb) return;
+  if (VL && q0 >= Nb) return;
   const size_t head_off = hr.off;
   const uint32_t head_bytes = hr.bytes;
   const uint32_t rs = VL ? hr.rs : RB;

@@ -361,6 +361,42 @@ __device__ inline void store_tile_rows(char* lds, const u32x2_t (&v)[D / 32][4],
     if (r < nrows) *(u32x4_t*)(dst + (size_t)r * row_stride + 8 * ch) = x;
   }
 }
+// Where the rows of head bh lie.  Dense [BH, N, D]: rows of D elements from
+// bh N D, vectors (LSE, D_i) from bh N, all N rows real.  Packed (VL): head
+// h of sequence b = bh / H owns rows cu[b] .. cu[b + 1] - 1 of [total, H, D]
+// (row stride H D, vectors [H, total] from h total + cu[b]), clamped into
+// [0, total] and to N rows, so malformed prefix sums never move an access out
+// of the tensors.  `bytes` ends right after the last real row: buffer loads
+// of rows from Nb on read zeros, as past the end of a dense head.
+struct HeadRows {
+  size_t off;       // element offset of row 0
+  size_t vec;       // element offset of vector entry 0
+  uint32_t rs;      // row stride (bytes)
+  uint32_t bytes;   // buffer range from row 0
+  int Nb;           // real rows
+};
+
+template <int D, bool VL>
+__device__ inline HeadRows head_rows(int bh, int N, const int32_t* __restrict__ cu, int H, int total) {
+  HeadRows r;
+  if constexpr (VL) {
+    const int b = bh / H, hd = bh - b * H;
+    const int64_t s0 = min(max((int64_t)cu[b], (int64_t)0), (int64_t)total);
+    r.Nb = (int)min(max((int64_t)cu[b + 1] - s0, (int64_t)0), min((int64_t)N, (int64_t)total - s0));
+    r.off = ((size_t)s0 * H + hd) * D;
+    r.vec = (size_t)hd * total + s0;
+    r.rs = (uint32_t)H * (2 * D);
+    r.bytes = r.Nb > 0 ? (uint32_t)(r.Nb - 1) * r.rs + 2 * D : 0u;
+  } else {
+    r.Nb = N;
+    r.off = (size_t)bh * N * D;
+    r.vec = (size_t)bh * N;
+    r.rs = 2 * D;
+    r.bytes = (uint32_t)N * (2 * D);
+  }
+  return r;
+}
+
 // bytes of LDS scratch per wavefront for store_tile_rows
 template <int D>
 constexpr int kTileRowsBytes = 32 * 2 * D;

@@ -81,11 +81,12 @@ constexpr float kSumMax = 32768.0f;
 //      on consecutive columns) both hit distinct banks.
 //
 // All matrix operands and accumulators live in VGPRs (the MfmaAsm forms).
-template <class TR, int D, int BC, int QB, bool CAUSAL>
+template <class TR, int D, int BC, int QB, bool CAUSAL, bool VL>
 __global__ __launch_bounds__(512 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB, 3 - QB)))
 void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                  float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c) {
+                  float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c,
+                  const int32_t* __restrict__ cu, int H, int n_rows) {
   // QB: 32-row query blocks per wavefront (2: one wavefront per SIMD, 1: two)
   constexpr int NT = 512 / QB;          // threads per workgroup
   constexpr int NW = NT / 64;           // wavefronts per workgroup
@@ -126,8 +127,20 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   int qt = lid % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest tiles first
   const int q0 = qt * BR;
-  const size_t head_off = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * RB;
+  // VL: a packed self-attention batch; head bh's Nb rows (its sequence) at
+  // row stride rs, and tiles wholly past them skipped
+  const HeadRows hr = head_rows<D, VL>(bh, N, cu, H, n_rows);
+  const int Nb = hr.Nb;
+  if (VL && q0 >= Nb) return;
+  const size_t head_off = hr.off;
+  const uint32_t head_bytes = hr.bytes;
+  const uint32_t rs = VL ? hr.rs : RB;
+  // the row stride as the staging loads use it: re-read per use in the packed
+  // variant, so that the per-row offsets are not kept live across the loop
+  auto row_stride = [&]() __attribute__((always_inline)) -> uint32_t {
+    if constexpr (VL) return __builtin_amdgcn_readfirstlane(rs);
+    return RB;
+  };
   const int qw = q0 + 32 * QB * w;  // first query row of this wavefront
 
   // Q rows as the B operand of S^T = K Q^T, loaded once (rows past the end
@@ -139,10 +152,10 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
-        qf[qb][ks] = buf_load16(qres, (uint32_t)(qw + 32 * qb + l32) * RB + 32 * ks + 16 * h);
+        qf[qb][ks] = buf_load16(qres, (uint32_t)(qw + 32 * qb + l32) * rs + 32 * ks + 16 * h);
   }
 
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int kv_end = CAUSAL ? min(Nb, q0 + BR) : Nb;
   const int n_tiles = (kv_end + BC - 1) / BC;
 
   // ---- staging.  Rows past the end of the sequence read zeros (their scores
@@ -152,25 +165,25 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   u32x4_t stk[NKC];
   uint32_t stv[8][CW / 2];
   // K: chunk tid + NT r -> row (tid / KCH) + (NT / KCH) r, 16-byte column tid % KCH
-  const uint32_t koff = (uint32_t)(tid / KCH) * RB + (tid % KCH) * 16;
+  const uint32_t koff = (uint32_t)(tid / KCH) * rs + (tid % KCH) * 16;
   const int kst = (tid / KCH) * KS + (tid % KCH) * 8;
   // V: unit tid -> (16-key step vs, half vh, column group vc); 8 rows x CW columns
   const int vc = tid % NCG;
   const int vh = (tid / NCG) & 1;
   const int vs = tid / (2 * NCG);
-  const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * RB + vc * CW * 2;
+  const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * rs + vc * CW * 2;
   const int vrow = (2 * vs + vh) * D * 8;
   const int vsw = (CW * vc) ^ ((CW * vc >> 3) & 3);  // swizzled slot of column CW vc (+ cc: xor)
 
   auto load_k = [&](int tile) {
 #pragma unroll
     for (int r = 0; r < NKC; ++r)
-      stk[r] = buf_load16(kres, koff + (uint32_t)(tile * BC + (NT / KCH) * r) * RB);
+      stk[r] = buf_load16(kres, koff + (uint32_t)(tile * BC + (NT / KCH) * r) * row_stride());
   };
   auto load_v = [&](int tile) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t off = voff + (uint32_t)(tile * BC + 8 * (k / 4) + (k % 4)) * RB;
+      const uint32_t off = voff + (uint32_t)(tile * BC + 8 * (k / 4) + (k % 4)) * row_stride();
       if constexpr (CW == 4) {
         const u32x2_t x = buf_load8(vres, off);
         stv[k][0] = x[0];
@@ -266,7 +279,7 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
       const float x = s_cur[qb][kb][r];
       if constexpr (MASKED) {
         const int key = j0 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
-        return (key >= N || (CAUSAL && key > qw + 32 * qb + l32)) ? -INFINITY : x;
+        return (key >= Nb || (CAUSAL && key > qw + 32 * qb + l32)) ? -INFINITY : x;
       }
       return x;
     };
@@ -430,7 +443,7 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
     // visible to every row of this wavefront run without masking; the rest
     // (the causal diagonal, the ragged end) mask scores as they are read.
     const int n_iter = (n_tiles + 1) & ~1;
-    int n_open = N / BC;
+    int n_open = Nb / BC;
     if (CAUSAL) n_open = min(n_open, (qw + 1) / BC);
     n_open = __builtin_amdgcn_readfirstlane(min(n_open, n_tiles) & ~1);
     int j = 0;
@@ -470,10 +483,10 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int row = qw + 32 * qb + l32;
-      const int kend = CAUSAL ? min(N, qw + 32 * qb + 32) : N;
+      const int kend = CAUSAL ? min(Nb, qw + 32 * qb + 32) : Nb;
       float mx = -INFINITY;
       for (int k0 = 0; k0 < kend; k0 += 32) {
-        const uint32_t ko = (uint32_t)(k0 + l32) * RB + 16 * h;
+        const uint32_t ko = (uint32_t)(k0 + l32) * rs + 16 * h;
         f32x16_t sc = TR::mma0(buf_load16(kres, ko), qf[qb][0]);
 #pragma unroll
         for (int ks = 1; ks < NKS; ++ks) TR::mma(sc, buf_load16(kres, ko + 32 * ks), qf[qb][ks]);
@@ -482,7 +495,7 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 8 * (r / 4) + 4 * h + (r % 4);
-          if (!(key >= N || (CAUSAL && key > row))) mx = __builtin_elementwise_maximum(mx, sc[r]);
+          if (!(key >= Nb || (CAUSAL && key > row))) mx = __builtin_elementwise_maximum(mx, sc[r]);
         }
       }
       mx = __builtin_elementwise_maximum(mx, swap_halves(mx));
@@ -525,9 +538,11 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
     static_assert(QB == 1 && (NW / 2) * kTileRowsBytes<D> <= (int)sizeof(sK) &&
                       (NW / 2) * kTileRowsBytes<D> <= (int)sizeof(sV), "rows fit the tile buffers");
     if (qb == 0) lds_barrier();
+    const size_t ostride = VL ? (size_t)H * D : (size_t)D;
     store_tile_rows<D>((w < NW / 2 ? (char*)sK : (char*)sV) + (w % (NW / 2)) * kTileRowsBytes<D>, ov,
-                       O + head_off + (size_t)(qw + 32 * qb) * D, min(32, N - (qw + 32 * qb)), lane);
-    if (qrow < N && h == 0) LSE[(size_t)bh * N + qrow] = (m_run[qb] + __log2f(l)) * kLn2;
+                       O + head_off + (size_t)(qw + 32 * qb) * ostride, min(32, Nb - (qw + 32 * qb)), lane,
+                       ostride);
+    if (qrow < Nb && h == 0) LSE[hr.vec + qrow] = (m_run[qb] + __log2f(l)) * kLn2;
   }
 }
 
@@ -555,11 +570,12 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
 //      values lane (c % 32, h) needs for one O^T += V^T P^T instruction.
 //      Column c sits at slot c ^ ((c >> 3) & 3) of its row (bank-conflict-
 //      free staging writes and fragment reads).
-template <class TR, int D, int BC, bool CAUSAL>
+template <class TR, int D, int BC, bool CAUSAL, bool VL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                  float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c) {
+                  float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c,
+                  const int32_t* __restrict__ cu, int H, int n_rows) {
   constexpr int NW = 8;                     // wavefronts per workgroup
   constexpr int BR = 32 * NW;               // query rows per workgroup
   constexpr int KCH = D / 8;                // 16-byte chunks per row
@@ -589,9 +605,15 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   int qt = lid % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest tiles first
   const int q0 = qt * BR;
-  const size_t head_off = (size_t)bh * N * D;
   constexpr uint32_t RB = D * 2;   // bytes per row
-  const uint32_t head_bytes = (uint32_t)N * RB;
+  // VL: a packed self-attention batch; head bh's Nb rows (its sequence) at
+  // row stride rs, and tiles wholly past them skipped
+  const HeadRows hr = head_rows<D, VL>(bh, N, cu, H, n_rows);
+  const int Nb = hr.Nb;
+  if (VL && q0 >= Nb) return;
+  const size_t head_off = hr.off;
+  const uint32_t head_bytes = hr.bytes;
+  const uint32_t rs = VL ? hr.rs : RB;
   const int qw = q0 + 32 * w;      // first query row of this wavefront
   const int qrow = qw + l32;
 
@@ -600,7 +622,7 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   u32x4_t qf[NKS];
   {
     const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
-    const uint32_t qoff = (uint32_t)qrow * RB + 16 * h;
+    const uint32_t qoff = (uint32_t)qrow * rs + 16 * h;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(qres, qoff + 32 * ks);
   }
@@ -612,9 +634,9 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   uint32_t pt[NKB][8];
   float m_run = -INFINITY, l_run = 0.0f, lt_run = 0.0f;
 
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int kv_end = CAUSAL ? min(Nb, q0 + BR) : Nb;
   const int n_tiles = (kv_end + BC - 1) / BC;
-  const int wave_end = CAUSAL ? min(N, qw + 32) : N;
+  const int wave_end = CAUSAL ? min(Nb, qw + 32) : Nb;
   const int wave_tiles = (wave_end + BC - 1) / BC;
 
   // ---- staging: 4 x 16 bytes per thread in both roles.  Rows past the end of
@@ -625,24 +647,24 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
   u32x4_t stg[4];
   // K role: chunk ci = st + 256 r -> row ci / KCH, 16-byte column ci % KCH
-  const uint32_t koff = (uint32_t)(st / KCH) * RB + (st % KCH) * 16;
+  const uint32_t koff = (uint32_t)(st / KCH) * rs + (st % KCH) * 16;
   const int kst = (st / KCH) * KS + (st % KCH) * 8;
   // V role: unit st -> (16-key step vs, half vh, 4-column chunk vc); 8 rows x 8 bytes
   const int vc = st % (D / 4);
   const int vh = (st / (D / 4)) & 1;
   const int vs = st / (D / 2);
-  const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * RB + vc * 8;
+  const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * rs + vc * 8;
   const int vst = ((2 * vs + vh) * D + 4 * vc) * 8;
   const int vsw = (vc >> 1) & 3;  // slot swizzle of this thread's four columns
 
   auto load_tile = [&](int j0) {
     if (grp == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) stg[r] = buf_load16(kres, koff + (uint32_t)(j0 + (256 / KCH) * r) * RB);
+      for (int r = 0; r < 4; ++r) stg[r] = buf_load16(kres, koff + (uint32_t)(j0 + (256 / KCH) * r) * rs);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const u32x2_t x = buf_load8(vres, voff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * RB);
+        const u32x2_t x = buf_load8(vres, voff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * rs);
         stg[k / 2][2 * (k % 2) + 0] = x[0];
         stg[k / 2][2 * (k % 2) + 1] = x[1];
       }
@@ -784,13 +806,13 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       if (j + 2 < n_tiles) load_tile((j + 2) * BC);
       if (j < wave_tiles) {
         const int j0 = j * BC;
-        if (wave_uniform((CAUSAL && j0 + BC - 1 > qw) || j0 + BC > N)) {
+        if (wave_uniform((CAUSAL && j0 + BC - 1 > qw) || j0 + BC > Nb)) {
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = j0 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
-              if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
+              if (key >= Nb || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
             }
         }
         // probabilities against the reference maximum m_run
@@ -857,8 +879,10 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                           TR::pack2(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
   // O stored as whole rows through LDS (the K buffers; the loop ended with a barrier)
   static_assert(8 * kTileRowsBytes<D> <= (int)sizeof(sK), "rows of all wavefronts fit the K buffers");
-  store_tile_rows<D>((char*)sK + w * kTileRowsBytes<D>, ov, O + head_off + (size_t)qw * D, min(32, N - qw), lane);
-  if (qrow < N && h == 0) LSE[(size_t)bh * N + qrow] = (m_run + __log2f(l)) * kLn2;
+  const size_t ostride = VL ? (size_t)H * D : (size_t)D;
+  store_tile_rows<D>((char*)sK + w * kTileRowsBytes<D>, ov, O + head_off + (size_t)qw * ostride, min(32, Nb - qw),
+                     lane, ostride);
+  if (qrow < Nb && h == 0) LSE[hr.vec + qrow] = (m_run + __log2f(l)) * kLn2;
 }
 
 // fp32 inputs: same scheme with v_mfma_f32_32x32x2_f32 and unrounded fp32
@@ -991,25 +1015,37 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float* __restrict__ Q,
 
 // ------------------------------------------------------------------ launch
 
-template <class TR, bool CAUSAL>
-static hipError_t launch_pipe(const FwdArgs& a) {  // d = 128
+template <class TR, bool CAUSAL, bool VL>
+static void launch_pipe_vl(const FwdArgs& a) {  // d = 128
   constexpr int BR = 256;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((fwd16_pipe_kernel<TR, 128, 64, 1, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
+  hipLaunchKernelGGL((fwd16_pipe_kernel<TR, 128, 64, 1, CAUSAL, VL>), dim3(total), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c);
+                     (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c, a.cu, a.H, a.total);
+}
+
+template <class TR, bool CAUSAL, bool VL>
+static void launch_pp_vl(const FwdArgs& a) {  // d = 64
+  constexpr int BR = 256;
+  const int n_qtiles = (a.N + BR - 1) / BR;
+  const uint32_t total = (uint32_t)(n_qtiles * a.BH);
+  hipLaunchKernelGGL((fwd16_pp_kernel<TR, 64, 128, CAUSAL, VL>), dim3(total), dim3(512), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c, a.cu, a.H, a.total);
+}
+
+template <class TR, bool CAUSAL>
+static hipError_t launch_pipe(const FwdArgs& a) {
+  if (a.cu) launch_pipe_vl<TR, CAUSAL, true>(a);
+  else launch_pipe_vl<TR, CAUSAL, false>(a);
   return hipGetLastError();
 }
 
 template <class TR, bool CAUSAL>
-static hipError_t launch_pp(const FwdArgs& a) {  // d = 64
-  constexpr int BR = 256;
-  const int n_qtiles = (a.N + BR - 1) / BR;
-  const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((fwd16_pp_kernel<TR, 64, 128, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c);
+static hipError_t launch_pp(const FwdArgs& a) {
+  if (a.cu) launch_pp_vl<TR, CAUSAL, true>(a);
+  else launch_pp_vl<TR, CAUSAL, false>(a);
   return hipGetLastError();
 }
 
@@ -1030,6 +1066,7 @@ static hipError_t dispatch16(const FwdArgs& a) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
+  if (a.cu && a.dtype != DT_BF16 && a.dtype != DT_F16) return hipErrorInvalidValue;  // packed: 16-bit only
   switch (a.dtype) {
     case DT_BF16: return dispatch16<BF16>(a);
     case DT_F16: return dispatch16<F16>(a);

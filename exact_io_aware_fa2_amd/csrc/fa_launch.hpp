@@ -27,6 +27,13 @@ struct FwdArgs {
   int causal;
   int dtype;
   hipStream_t stream;
+  // Packed variable-length self-attention batch (16-bit types only): q, k,
+  // v, o are [total, H, d], lse [H, total], and head h of sequence
+  // b = bh / H owns rows cu[b] .. cu[b + 1] - 1 (at most N of them;
+  // BH = B H).  NULL: the dense [BH, N, d] layout.
+  const int32_t* cu = nullptr;
+  int H = 1;
+  int total = 0;
 };
 
 struct BwdArgs {

@@ -214,6 +214,11 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, 
  *                 [1, 2^22]; max * H * d * 2 must stay below 2^31 bytes.
  *   workspace     fa_fwd_varlen_workspace_bytes(B, H, max_q, max_k, d, dtype)
  *                 bytes (16-byte aligned, may be NULL when that is 0).
+ * When cu_seqlens_q and cu_seqlens_k are the same pointer (self-attention:
+ * equal query and key counts), total_q = total_k, max_q = max_k, d is 64 or
+ * 128 and (max_q + 512) * H * d * 2 < 2^31, fa_fwd's kernels run on the
+ * packed rows in place and the workspace is not used; otherwise the
+ * split-key kernels of fa_fwd_kvcache do.
  * Errors as for fa_fwd_kvcache (FA_ERR_NULL also for NULL prefix sums,
  * FA_ERR_SHAPE for total_q or total_k < 1 or the offset limit). */
 size_t fa_fwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t max_q, int64_t max_k, int64_t d,
