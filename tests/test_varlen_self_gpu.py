@@ -51,7 +51,7 @@ LENGTHS = [
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])  # 32: the split-key kernel serves it
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("case", range(len(LENGTHS)))
 def test_varlen_self_small(case, causal, d, dtype):
