@@ -469,8 +469,8 @@ def main():
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1 "
-                                   "(heads shard across GPUs with no communication: see DESIGN.md)"}))
+        print(json.dumps({"error": "the library runs on one GPU; use --gpus 1 (on several GPUs, "
+                                   "heads would shard across them with no communication)"}))
         sys.exit(2)
 
     import numpy as np
