@@ -272,3 +272,15 @@ def test_varlen_bwd_argument_errors(lib):
     assert bvl(lib, ws=None) == FA_ERR_WORKSPACE
     assert bvl(lib, wsb=need - 1) == FA_ERR_WORKSPACE
     assert bvl(lib, ws=P[11] + 4, wsb=need) == FA_ERR_ALIGN
+
+
+def test_varlen_self_attention_route_checks_arguments_first(lib):
+    # one prefix-sum array for queries and keys selects the square kernels,
+    # but only after every argument check (each case below returns before any launch)
+    same = dict(cq=P[8], ck=P[8], tq=500, tk=500, mq=256, mk=256)
+    assert vl(lib, **same, d=80) == FA_ERR_HEADDIM
+    assert vl(lib, **same, dtype=0) == FA_ERR_DTYPE
+    assert vl(lib, **same, o=P[3] + 8) == FA_ERR_ALIGN
+    assert vl(lib, **same, scale=-1.0) == FA_ERR_SCALE
+    assert vl(lib, **same, q=None) == FA_ERR_NULL
+    assert vl(lib, **dict(same, tq=0)) == FA_ERR_SHAPE
