@@ -144,6 +144,26 @@ def _check_tensors(*ts):
             raise ValueError("all tensors must be contiguous")
 
 
+def _check_like(ref, names, *ts):
+    """Every tensor of ts has ref's shape and dtype (names: for the message)."""
+    for t in ts:
+        if tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype:
+            raise ValueError(f"{names} must share shape and dtype")
+
+
+def _check_f32(t, shape, what: str):
+    torch = _torch()
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.float32:
+        raise ValueError(f"{what} must be float32 {list(shape)}")
+
+
+def _check_workspace(workspace, B: int, H: int, N: int):
+    """The backward's workspace holds one float32 per query row."""
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < 4 * B * H * N:
+        raise ValueError(f"workspace must hold at least {4 * B * H * N} bytes")
+
+
 def fa_fwd(q, k, v, o, lse, scale: float, causal: bool) -> None:
     """Enqueue the forward on the current stream of q's device (see include/fa.h)."""
     L = load_library()
@@ -166,11 +186,11 @@ def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype: int) -> int:
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale: float, causal: bool) -> None:
     """Enqueue the backward on the current stream of q's device (see include/fa.h)."""
     L = load_library()
-    _check_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace)
     B, H, N, d = _bhnd(q)
-    for t in (k, v, o, dout, dq, dk, dv):
-        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
-            raise ValueError("q, k, v, o, dout, dq, dk, dv must share shape and dtype")
+    _check_like(q, "q, k, v, o, dout, dq, dk, dv", k, v, o, dout, dq, dk, dv)
+    _check_f32(lse, (B, H, N), "lse")
+    _check_workspace(workspace, B, H, N)
+    _check_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace)
     nbytes = workspace.numel() * workspace.element_size()
     _check(L.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
@@ -180,8 +200,10 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale: float, causal: b
 def fa_bwd_prep(o, dout, workspace) -> None:
     """Stage 1 of the backward: workspace[i] = dout_i . o_i (float32)."""
     L = load_library()
-    _check_tensors(o, dout, workspace)
     B, H, N, d = _bhnd(o)
+    _check_like(o, "o, dout", dout)
+    _check_workspace(workspace, B, H, N)
+    _check_tensors(o, dout, workspace)
     _check(L.fa_bwd_prep(_ptr(o), _ptr(dout), _ptr(workspace),
                          workspace.numel() * workspace.element_size(), B, H, N, d,
                          dtype_code(o), _stream(o)))
@@ -190,8 +212,11 @@ def fa_bwd_prep(o, dout, workspace) -> None:
 def fa_bwd_dkdv(q, k, v, dout, lse, workspace, dk, dv, scale: float, causal: bool) -> None:
     """Stage 2 of the backward: dK and dV (needs the prepared workspace)."""
     L = load_library()
-    _check_tensors(q, k, v, dout, lse, workspace, dk, dv)
     B, H, N, d = _bhnd(q)
+    _check_like(q, "q, k, v, dout, dk, dv", k, v, dout, dk, dv)
+    _check_f32(lse, (B, H, N), "lse")
+    _check_workspace(workspace, B, H, N)
+    _check_tensors(q, k, v, dout, lse, workspace, dk, dv)
     _check(L.fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _ptr(dk), _ptr(dv),
                          B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), _stream(q)))
@@ -200,8 +225,11 @@ def fa_bwd_dkdv(q, k, v, dout, lse, workspace, dk, dv, scale: float, causal: boo
 def fa_bwd_dq(q, k, v, dout, lse, workspace, dq, scale: float, causal: bool) -> None:
     """Stage 3 of the backward: dQ (needs the prepared workspace)."""
     L = load_library()
-    _check_tensors(q, k, v, dout, lse, workspace, dq)
     B, H, N, d = _bhnd(q)
+    _check_like(q, "q, k, v, dout, dq", k, v, dout, dq)
+    _check_f32(lse, (B, H, N), "lse")
+    _check_workspace(workspace, B, H, N)
+    _check_tensors(q, k, v, dout, lse, workspace, dq)
     _check(L.fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(workspace),
                        workspace.numel() * workspace.element_size(), _ptr(dq),
                        B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), _stream(q)))

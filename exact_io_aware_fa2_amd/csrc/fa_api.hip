@@ -28,8 +28,11 @@ int check_shape(int64_t B, int64_t H, int64_t N, int64_t d) {
   return FA_OK;
 }
 
+// The scale must be finite and >= 0, and so must the factor the kernels use,
+// scale * log2(e) (it overflows to infinity above about 2.4e38).
 int check_scale(float scale) {
   if (!isfinite(scale) || scale < 0.0f) return FA_ERR_SCALE;
+  if (!isfinite(scale * fa::kLog2eHost)) return FA_ERR_SCALE;
   return FA_OK;
 }
 
@@ -304,6 +307,8 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, 
   st = check_scale(scale);
   if (st != FA_OK) return st;
   if (!isfinite(k_scale) || !isfinite(v_scale) || !(k_scale > 0.0f) || !(v_scale > 0.0f)) return FA_ERR_SCALE;
+  // the K scale joins the exponent factor: the product must stay finite
+  if (!isfinite(scale * k_scale * fa::kLog2eHost)) return FA_ERR_SCALE;
   const size_t need = fa::kv_workspace_bytes(B * H, Nq, Nk, d);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
@@ -339,6 +344,8 @@ extern "C" {
 
 int64_t fa_probe_mfma_bf16(int64_t workgroups, int64_t iters, void* stream) {
   if (workgroups < 1 || workgroups > kMaxWorkgroups || iters < 1 || iters > INT32_MAX) return -FA_ERR_SHAPE;
+  // the FLOP count (workgroups * iters * 2^19) must fit in int64
+  if (workgroups * iters > (INT64_MAX >> 19)) return -FA_ERR_SHAPE;
   if (fa::launch_mfma_peak((int)workgroups, (int)iters, (hipStream_t)stream) != hipSuccess) return -FA_ERR_HIP;
   return workgroups * 4 * iters * 4 * 32768;
 }

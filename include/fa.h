@@ -64,7 +64,7 @@ typedef enum {
   FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 (32 also for the split-key entry points) */
   FA_ERR_DTYPE = 4,     /* unknown dtype, or a dtype this entry point does not take */
   FA_ERR_ALIGN = 5,     /* a data pointer is not 16-byte aligned */
-  FA_ERR_SCALE = 6,     /* scale is negative, NaN or infinite */
+  FA_ERR_SCALE = 6,     /* scale is negative, NaN or infinite, or scale * log2(e) overflows */
   FA_ERR_WORKSPACE = 7, /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_HIP = 8        /* the HIP runtime rejected a launch */
 } fa_status;
@@ -277,8 +277,9 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
  * `stream`), it gives the sustained dense bf16 MFMA rate the attention
  * kernels are compared with beside the published peak.  Returns the FLOP
  * count of the launch (workgroups * 4 * iters * 4 * 32768), or the negated
- * FA_ERR_SHAPE (workgroups not in [1, 2^24 - 1] or iters not in
- * [1, 2^31 - 1]) or FA_ERR_HIP (launch refused). */
+ * FA_ERR_SHAPE (workgroups not in [1, 2^24 - 1], iters not in
+ * [1, 2^31 - 1], or workgroups * iters above 2^44, where the count would
+ * leave int64) or FA_ERR_HIP (launch refused). */
 int64_t fa_probe_mfma_bf16(int64_t workgroups, int64_t iters, void* stream);
 
 #ifdef __cplusplus

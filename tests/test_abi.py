@@ -85,6 +85,9 @@ def test_fwd_argument_errors(lib):
     assert fwd(lib, scale=float("nan")) == FA_ERR_SCALE
     assert fwd(lib, scale=math.inf) == FA_ERR_SCALE
     assert fwd(lib, scale=-0.5) == FA_ERR_SCALE
+    # finite, but scale * log2(e) overflows float32
+    assert fwd(lib, scale=3.0e38) == FA_ERR_SCALE
+    assert bwd(lib, scale=3.0e38) == FA_ERR_SCALE
 
 
 def test_bwd_argument_errors(lib):
@@ -133,6 +136,51 @@ def test_binding_rejects_host_tensors_and_bad_shapes(lib):
         fa.fwd(q, q, q)
     with pytest.raises(TypeError):
         fa.dtype_code(torch.zeros(1, dtype=torch.int32))
+
+
+def test_binding_checks_backward_tensors_before_the_call(lib):
+    """Wrong shapes, dtypes or sizes of lse, gradients and the workspace are
+    named by the wrappers (before any pointer reaches the library)."""
+    torch = pytest.importorskip("torch")
+    import exact_io_aware_fa2_amd as fa
+    B, H, N, d = 1, 2, 16, 64
+    t = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt)  # noqa: E731
+    q = t(B, H, N, d)
+    lse = t(B, H, N, dt=torch.float32)
+    ws = torch.zeros(4 * B * H * N, dtype=torch.uint8)
+    good = dict(q=q, k=q, v=q, o=q, lse=lse, dout=q, dq=q, dk=q, dv=q, workspace=ws)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                  a["workspace"], 0.125, True)
+
+    with pytest.raises(ValueError, match="lse"):
+        call(lse=t(B, H, N))  # bf16, not float32
+    with pytest.raises(ValueError, match="lse"):
+        call(lse=t(B, H, N + 1, dt=torch.float32))
+    with pytest.raises(ValueError, match="share shape"):
+        call(dv=t(B, H, N, d + 64))
+    with pytest.raises(ValueError, match="share shape"):
+        call(dout=t(B, H, N, d, dt=torch.float16))
+    with pytest.raises(ValueError, match="workspace"):
+        call(workspace=torch.zeros(4 * B * H * N - 1, dtype=torch.uint8))
+    # the stage wrappers check the same
+    with pytest.raises(ValueError, match="share shape"):
+        fa.fa_bwd_prep(q, t(B, H, N - 1, d), ws)
+    with pytest.raises(ValueError, match="workspace"):
+        fa.fa_bwd_prep(q, q, torch.zeros(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="lse"):
+        fa.fa_bwd_dkdv(q, q, q, q, t(B, H, N), ws, q, q, 0.125, True)
+    with pytest.raises(ValueError, match="share shape"):
+        fa.fa_bwd_dkdv(q, q, q, q, lse, ws, t(B, H, N, 32), q, 0.125, True)
+    with pytest.raises(ValueError, match="lse"):
+        fa.fa_bwd_dq(q, q, q, q, t(B, 1, N, dt=torch.float32), ws, q, 0.125, True)
+    with pytest.raises(ValueError, match="share shape"):
+        fa.fa_bwd_dq(q, t(B, H, N, d, dt=torch.float16), q, q, lse, ws, q, 0.125, True)
+    # right shapes on the host: refused as host tensors
+    with pytest.raises(ValueError, match="GPU"):
+        call()
 
 
 def kv(lib, q=P[0], k=P[1], v=P[2], lens=None, o=P[3], lse=P[4], ws=P[10], wsb=1 << 30, B=2, H=4,
@@ -199,6 +247,9 @@ def test_kvcache_fp8_argument_errors(lib):
         assert kv8(lib, ks=bad) == FA_ERR_SCALE
         assert kv8(lib, vs=bad) == FA_ERR_SCALE
     assert kv8(lib, scale=-0.1) == FA_ERR_SCALE
+    # each finite, the exponent factor scale * k_scale * log2(e) is not
+    assert kv8(lib, scale=1.0e20, ks=1.0e20) == FA_ERR_SCALE
+    assert kv(lib, scale=3.0e38) == FA_ERR_SCALE
     assert kv8(lib, ws=None) == FA_ERR_WORKSPACE
 
 
@@ -208,6 +259,8 @@ def test_probe_argument_errors(lib):
     assert lib.fa_probe_mfma_bf16(0, 10, None) == -FA_ERR_SHAPE
     assert lib.fa_probe_mfma_bf16(10, 0, None) == -FA_ERR_SHAPE
     assert lib.fa_probe_mfma_bf16(1 << 24, 10, None) == -FA_ERR_SHAPE
+    # the FLOP count would leave int64
+    assert lib.fa_probe_mfma_bf16((1 << 24) - 1, (1 << 31) - 1, None) == -FA_ERR_SHAPE
 
 
 def vl(lib, q=P[0], k=P[1], v=P[2], cq=P[8], ck=P[9], o=P[3], lse=P[4], ws=P[10], wsb=1 << 30, B=3, H=4,
