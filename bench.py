@@ -294,6 +294,11 @@ def bench_fwd_only(args, workloads):
     for w in workloads:
         tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
         inp = si.make_workload_inputs(w, backward=False)
+        if args.growing:
+            # keys scaled up along the sequence (x1 at key 0 to x6 at the last): the row
+            # maxima of later key tiles far exceed the first tile's
+            grow = (1.0 + 5.0 * np.arange(w.N, dtype=np.float32) / w.N)[None, None, :, None]
+            inp["k"] = si.round_to(inp["k"][0] * grow, w.dtype)
 
         def up(name):
             a = inp[name][1]
@@ -319,12 +324,20 @@ def bench_fwd_only(args, workloads):
         peak = PEAK_MFMA_16BIT if s == 2 else 157.3
         tf = w.fwd_flop() / (ms * 1e-3) / 1e12
         print(json.dumps({"mode": "forward only", "workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} "
-                                                              f"{'causal' if w.causal else 'non-causal'}",
+                                                              f"{'causal' if w.causal else 'non-causal'}"
+                                                              + (" keys growing x1..x6" if args.growing else ""),
                           "median_us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
                           "frac_mfma_peak": round(tf / peak, 4), "mfma_peak": peak,
                           "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
                           "compulsory_bytes": nbytes, "steps": args.steps}), flush=True)
         del q, k, v, o, lse, inp
+    if args.profile:
+        # the calibration kernel for FETCH_SIZE / WRITE_SIZE counters
+        a = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
 
 
 def bench_varlen(args):
@@ -463,6 +476,9 @@ def main():
     ap.add_argument("--fwd-only", action="store_true",
                     help="time fa_fwd alone on --workload (any of C1..C5, C3d64, C5d128; comma-separated), "
                          "or on the short-sequence sweep with --workload short")
+    ap.add_argument("--growing", action="store_true",
+                    help="with --fwd-only: keys scaled by 1 + 5 j / N along the sequence (row maxima "
+                         "rise after the first key tile)")
     args = ap.parse_args()
 
     if args.ingest_pmc:

@@ -11,7 +11,7 @@ import pytest
 
 import seeded_inputs as si
 from oracle import kvcache_fwd_head, varlen_fwd
-from parity import TOL, lib, say, to_device
+from parity import TOL, assert_fwd_ok_peaked, lib, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -132,3 +132,23 @@ def test_varlen_self_prefill_batch_full_size_sampled():
         rows = slice(int(cu[b]), int(cu[b + 1]))
         of, lf = kvcache_fwd_head(inp["q"][0][rows, h], inp["k"][0][rows, h], inp["v"][0][rows, h], scale, True)
         _check(o[rows, h], lse[h, rows], of, lf, "bf16", f"sequence {b} head {h}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_self_growing_scores(causal, d):
+    """Keys scaled up along each sequence (x1 to x6): later key tiles hold row
+    maxima far above the first tile's, so the packed kernels must raise their
+    reference maximum (d = 64: the tile is re-based; d = 128: the pass is
+    redone against exact maxima), as the dense kernels do."""
+    lens = [600, 300, 1000, 1]
+    seed = 9800 + d + int(causal)
+    inp = si.make_varlen_inputs(lens, lens, 2, d, "bf16", 1.0, seed)
+    pos = np.concatenate([np.arange(n) / n for n in lens]).astype(np.float32)
+    inp["k"] = si.round_to(inp["k"][0] * (1.0 + 5.0 * pos)[:, None, None], "bf16")
+    scale = 1.0 / np.sqrt(d)
+    say(f"varlen self growing keys lens={lens} H2 d{d} causal={causal} seed={seed}")
+    o, lse = _fwd(inp, "bf16", causal, scale)
+    o_ref, lse_ref = varlen_fwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["cu_q"], inp["cu_k"], scale, causal)
+    # peaked rows: |O| reaches 5.4 here, where bf16 output rounding alone moves an element by up to 0.0156
+    assert_fwd_ok_peaked(o, lse, o_ref, lse_ref, "bf16", f"growing keys lens {lens} d{d} causal={causal}")
