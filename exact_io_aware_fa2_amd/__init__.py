@@ -9,6 +9,7 @@ Raw entry points (same names and argument order as include/fa.h, tensors in
 place of pointers):
     fa_fwd(q, k, v, o, lse, scale, causal)
     fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, causal)
+    fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, scale, causal)  (no workspace)
     fa_bwd_workspace_bytes(B, H, N, d, dtype)
     fa_bwd_prep(o, dout, workspace); fa_bwd_dkdv(...); fa_bwd_dq(...)  (fa_bwd's stages)
     fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, workspace, scale, causal)
@@ -36,7 +37,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_DTYPE",
-    5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_WORKSPACE", 8: "FA_ERR_HIP",
+    5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_WORKSPACE", 8: "FA_ERR_HIP", 9: "FA_ERR_SCRATCH",
 }
 
 _lib = None
@@ -88,6 +89,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fa_bwd_varlen.restype = i32
     L.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, f32, i32,
                                 vp]
+    L.fa_bwd_noalloc_max_rows.restype = sz
+    L.fa_bwd_noalloc_max_rows.argtypes = []
+    L.fa_bwd_noalloc.restype = i32
+    L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
     L.fa_probe_mfma_bf16.restype = i64
     L.fa_probe_mfma_bf16.argtypes = [i64, i64, vp]
     L.fa_fwd_kvcache_fp8.restype = i32
@@ -195,6 +200,24 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale: float, causal: b
     _check(L.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
                     B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), _stream(q)))
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool) -> None:
+    """fa_bwd without a workspace: the library's static per-GPU scratch holds
+    D_i (B * H * N <= fa_bwd_noalloc_max_rows()); allocates nothing.  Calls
+    that overlap in time on one GPU race (see include/fa.h)."""
+    L = load_library()
+    B, H, N, d = _bhnd(q)
+    _check_like(q, "q, k, v, o, dout, dq, dk, dv", k, v, o, dout, dq, dk, dv)
+    _check_f32(lse, (B, H, N), "lse")
+    _check_tensors(q, k, v, o, lse, dout, dq, dk, dv)
+    _check(L.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                            _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                            dtype_code(q), _stream(q)))
+
+
+def fa_bwd_noalloc_max_rows() -> int:
+    return int(load_library().fa_bwd_noalloc_max_rows())
 
 
 def fa_bwd_prep(o, dout, workspace) -> None:

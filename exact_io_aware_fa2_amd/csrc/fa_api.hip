@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_launch.hpp"
 
@@ -63,6 +65,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SCALE: return "scale must be finite and >= 0";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_SCRATCH: return "sizes exceed the static scratch of fa_bwd_noalloc";
     default: return "unknown status";
   }
 }
@@ -499,6 +502,83 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   a.H = (int)H;
   a.total = (int)total;
   return status_of(fa::launch_bwd(a));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ fa_bwd_noalloc
+//
+// fa_bwd without a caller workspace, for callers that cannot allocate.  Its
+// one scratch array (D_i = dO_i . O_i, one float per query row) is this
+// file-scope device array; every GPU holds its own copy at its own address.
+// Host code never passes the array's name to a kernel (on the host it is
+// only a stand-in symbol): the device address is looked up once per device,
+// with that device current, and kept in kScratchPtr.
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;  // 16 MiB: B * H * N <= 4194304 rows
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, NULL until looked up
+
+// Device address of `scratch` on the device the work runs on (the stream's
+// device; the current device for the NULL stream), looked up on the first
+// call on that device with it current (the caller's current device is
+// restored afterwards).
+void* scratch_ptr(hipStream_t stream, int* status) {
+  *status = FA_ERR_HIP;
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return nullptr;
+    if (e != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  *status = FA_OK;
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_bwd_noalloc_max_rows(void) { return kScratchBytes / sizeof(float); }
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                   int64_t d, float scale, int causal, int dtype, void* stream) {
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!p) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  if ((size_t)(B * H * N) * sizeof(float) > kScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = scratch_ptr((hipStream_t)stream, &st);
+  if (st != FA_OK) return st;
+  // the D_i rows are written by the first stage before the others read them:
+  // nothing in the scratch has to start at zero
+  return fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, kScratchBytes, B, H, N, d, scale, causal, dtype,
+                stream);
 }
 
 }  // extern "C"

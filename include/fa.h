@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 typedef enum {
   FA_OK = 0,
@@ -66,7 +66,8 @@ typedef enum {
   FA_ERR_ALIGN = 5,     /* a data pointer is not 16-byte aligned */
   FA_ERR_SCALE = 6,     /* scale is negative, NaN or infinite, or scale * log2(e) overflows */
   FA_ERR_WORKSPACE = 7, /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
-  FA_ERR_HIP = 8        /* the HIP runtime rejected a launch */
+  FA_ERR_HIP = 8,       /* the HIP runtime rejected a launch */
+  FA_ERR_SCRATCH = 9    /* fa_bwd_noalloc: the sizes need more than its static scratch */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
@@ -107,6 +108,27 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* workspace, size_t workspace_bytes,
            int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
            int dtype, void* stream);
+
+/* fa_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same backward, same kernels and bitwise the same results, with no
+ * workspace argument.  Its one scratch array (D_i, one float per query row)
+ * is a static device array of the library, 16 MiB per GPU, held from the
+ * first call on a GPU until the process ends; so B * H * N must be at most
+ * fa_bwd_noalloc_max_rows() = 4194304, else FA_ERR_SCRATCH (checked before
+ * any device call).  The call allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine; its first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress) once.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap in time on one GPU (different streams, or
+ * different threads without ordering) race and may give wrong gradients.
+ * Arguments, layout, errors and determinism otherwise as fa_bwd. */
+size_t fa_bwd_noalloc_max_rows(void);
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                   int dtype, void* stream);
 
 /* The three stages fa_bwd runs, in this order, for callers that schedule or
  * time them separately (same arguments, contract and errors as fa_bwd; each

@@ -36,17 +36,18 @@ def test_header_declares_the_entry_points():
         ["fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
          "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kvcache_workspace_bytes",
          "fa_fwd_kvcache", "fa_fwd_kvcache_fp8", "fa_probe_mfma_bf16", "fa_fwd_varlen_workspace_bytes",
-         "fa_fwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_bwd_varlen"])
+         "fa_fwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_bwd_varlen", "fa_bwd_noalloc_max_rows",
+         "fa_bwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 6
+    assert lib.fa_abi_version() == 7
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = lib.fa_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.fa_status_string(99).decode() == "unknown status"
@@ -101,6 +102,30 @@ def test_bwd_argument_errors(lib):
     assert bwd(lib, ws=None) == FA_ERR_WORKSPACE
     assert bwd(lib, wsb=4 * 2 * 64 - 1) == FA_ERR_WORKSPACE
     assert bwd(lib, ws=P[10] + 4) == FA_ERR_ALIGN
+
+
+def noalloc(lib, B=1, H=2, N=64, d=64, scale=0.125, dtype=2, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], do=P[5], dq=P[6], dk=P[7], dv=P[8])
+    a.update(kw)
+    return lib.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                              B, H, N, d, scale, 1, dtype, None)
+
+
+def test_noalloc_argument_errors(lib):
+    """fa_bwd_noalloc checks like fa_bwd and refuses sizes beyond its static
+    scratch (one float per query row) before any device call."""
+    FA_ERR_SCRATCH = 9
+    rows = lib.fa_bwd_noalloc_max_rows()
+    assert rows == (16 << 20) // 4
+    assert noalloc(lib, dv=None) == FA_ERR_NULL
+    assert noalloc(lib, N=0) == FA_ERR_SHAPE
+    assert noalloc(lib, d=80) == FA_ERR_HEADDIM
+    assert noalloc(lib, dtype=0) == FA_ERR_DTYPE
+    assert noalloc(lib, lse=P[4] + 4) == FA_ERR_ALIGN
+    assert noalloc(lib, scale=math.nan) == FA_ERR_SCALE
+    # one row more than the scratch holds (B * H * N = rows + 64)
+    assert noalloc(lib, B=rows // 64 + 1, H=1, N=64) == FA_ERR_SCRATCH
+    assert noalloc(lib, B=1, H=64, N=rows // 64 + 1) == FA_ERR_SCRATCH
 
 
 def test_stage_argument_errors(lib):
