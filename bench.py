@@ -21,7 +21,8 @@ Modes
                         D1f8: the same with an 8-bit E4M3 cache (fa_fwd_kvcache_fp8)
   --varlen              fa_fwd_varlen + fa_bwd_varlen on a packed batch of 16 ragged causal sequences
   --fwd-only            fa_fwd alone: time, TFLOP/s and compulsory GB/s per workload
-                        (--workload C1,C3,...; --workload short: the short-sequence sweep)
+                        (--workload C1,C3,...; --workload short: the short-sequence sweep;
+                        --workload C3f8 or C2f8: fa_fwd_fp8 on the 8-bit form of C3's / C2's draw)
   --profile             3 warm-up + 20 timed steps (stages in order on one stream), no CPU
                         baseline, for rocprofv3 runs;
                         also runs a plain 1 GiB device copy (the calibration
@@ -53,10 +54,11 @@ KERNEL_SOURCES = {
     "prep": ["fa_bwd.hip", "fa_common.hpp"],
     "dkdv": ["fa_bwd.hip", "fa_common.hpp"],
     "dq": ["fa_bwd.hip", "fa_common.hpp"],
+    "fwd8": ["fa_fwd_fp8.hip", "fa_common.hpp"],
 }
 # substrings of the mangled kernel names, as rocprofv3 reports them
 KERNEL_SYMBOLS = {"fwd": "fwd16_p", "prep": "bwd_pre_kernel", "dkdv": "bwd_dkdv",
-                  "dq": "bwd_dq", "kv": "kv_split"}
+                  "dq": "bwd_dq", "kv": "kv_split", "fwd8": "fwd8_pipe"}
 
 
 def src_hash(kernel: str) -> str:
@@ -292,6 +294,9 @@ def bench_fwd_only(args, workloads):
 
     dev = torch.device("cuda:0")
     for w in workloads:
+        if isinstance(w, si.Fp8Workload):
+            bench_fwd_fp8(args, w)
+            continue
         tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
         inp = si.make_workload_inputs(w, backward=False)
         if args.growing:
@@ -333,6 +338,60 @@ def bench_fwd_only(args, workloads):
         del q, k, v, o, lse, inp
     if args.profile:
         # the calibration kernel for FETCH_SIZE / WRITE_SIZE counters
+        a = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+
+PEAK_MFMA_FP8 = 5033.2  # TFLOP/s, MI355X dense fp8 MFMA (twice the 16-bit rate)
+
+
+def bench_fwd_fp8(args, w):
+    """fa_fwd_fp8 on an 8-bit workload: median of --steps calls.  Half of the
+    forward's FLOP (S = Q K^T) run on the FP8 matrix cores, half (O = P V) on
+    the 16-bit ones, so the peak of the mix is 2 / (1 / fp8 + 1 / bf16)."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_fa2_amd as fa
+    import seeded_inputs as si
+
+    dev = torch.device("cuda:0")
+    inp = si.make_fp8_workload_inputs(w)
+    t = {n: torch.from_numpy(inp[n][1]).to(dev) for n in ("q", "k", "v")}
+    sc = {n: torch.from_numpy(inp[n + "_scale"]).to(dev) for n in ("q", "k", "v")}
+    odt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.out_dtype]
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=odt, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def call():
+        fa.fa_fwd_fp8(t["q"], t["k"], t["v"], sc["q"], sc["k"], sc["v"], w.granularity, o, lse, w.scale, w.causal)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    tf = w.fwd_flop() / (ms * 1e-3) / 1e12
+    mixed = 2.0 / (1.0 / PEAK_MFMA_FP8 + 1.0 / PEAK_MFMA_16BIT)
+    nbytes = 3 * w.B * w.H * w.N * w.d + w.B * w.H * w.N * w.d * 2 + 4 * w.B * w.H * w.N
+    print(json.dumps({"mode": "forward only, 8-bit inputs", "workload":
+                      f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} E4M3 q/k/v, {w.granularity} scales, "
+                      f"{w.out_dtype} out, {'causal' if w.causal else 'non-causal'}",
+                      "median_us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+                      "frac_mixed_peak": round(tf / mixed, 4), "mixed_peak": round(mixed, 1),
+                      "frac_fp8_peak": round(tf / PEAK_MFMA_FP8, 4), "fp8_peak": PEAK_MFMA_FP8,
+                      "frac_bf16_peak": round(tf / PEAK_MFMA_16BIT, 4),
+                      "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "compulsory_bytes": nbytes,
+                      "steps": args.steps}), flush=True)
+    if args.profile:
         a = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
@@ -500,7 +559,8 @@ def main():
         bench_varlen(args)
         return
     if args.fwd_only:
-        wls = short_n_workloads() if args.workload == "short" else [si.WORKLOADS[n] for n in args.workload.split(",")]
+        wls = short_n_workloads() if args.workload == "short" else \
+            [si.WORKLOADS[n] if n in si.WORKLOADS else si.FP8_WORKLOADS[n] for n in args.workload.split(",")]
         bench_fwd_only(args, wls)
         return
     if args.workload in si.KV_WORKLOADS:

@@ -16,12 +16,14 @@ place of pointers):
     fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, dtype)
     fa_fwd_kvcache_fp8(q, k_cache, v_cache, k_scale, v_scale, seqlens_k, o, lse, workspace, scale, causal)
     fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, workspace, max_q, max_k, scale, causal)
+    fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, granularity, o, lse, scale, causal)
 Conveniences that allocate their outputs with torch:
     fwd(q, k, v, causal=False, scale=None) -> (o, lse)
     bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
     fwd_kvcache(q, k_cache, v_cache, seqlens_k=None, causal=True, scale=None) -> (o, lse)
     fwd_kvcache_fp8(q, k8, v8, k_scale, v_scale, seqlens_k=None, causal=True, scale=None) -> (o, lse)
     fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_q, max_k, causal=False, scale=None) -> (o, lse)
+    fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, granularity="block", causal=False, scale=None) -> (o, lse)
     FlashAttention (torch.autograd.Function) and attention(q, k, v, causal, scale)
 """
 
@@ -89,6 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fa_bwd_varlen.restype = i32
     L.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, f32, i32,
                                 vp]
+    L.fa_fwd_fp8.restype = i32
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
     L.fa_bwd_noalloc_max_rows.restype = sz
     L.fa_bwd_noalloc_max_rows.argtypes = []
     L.fa_bwd_noalloc.restype = i32
@@ -200,6 +204,51 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale: float, causal: b
     _check(L.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
                     B, H, N, d, float(scale), int(bool(causal)), dtype_code(q), _stream(q)))
+
+
+FA_SCALE_TENSOR, FA_SCALE_BLOCK = 0, 1
+FP8_BLOCK = 128
+
+
+def fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, granularity: str, o, lse, scale: float,
+               causal: bool) -> None:
+    """Forward on 8-bit inputs (see include/fa.h): q8, k8, v8 uint8 E4M3 codes
+    [B, H, N, d] (d = 128); float32 scales on the device: granularity
+    "tensor" one each, "block" q_scale and k_scale [B, H, ceil(N / 128)] and
+    v_scale [B, H]; o [B, H, N, d] bf16 or fp16; lse float32 [B, H, N]."""
+    L = load_library()
+    torch = _torch()
+    B, H, N, d = _bhnd(q8)
+    for t in (q8, k8, v8):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != torch.uint8:
+            raise ValueError("q8, k8, v8 must be uint8 [B, H, N, d] of one shape")
+    if tuple(o.shape) != (B, H, N, d) or o.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("o must be bf16 or fp16 [B, H, N, d]")
+    _check_f32(lse, (B, H, N), "lse")
+    if granularity == "tensor":
+        shapes, g = ((1,), (1,), (1,)), FA_SCALE_TENSOR
+    elif granularity == "block":
+        nb = (N + FP8_BLOCK - 1) // FP8_BLOCK
+        shapes, g = ((B, H, nb), (B, H, nb), (B, H)), FA_SCALE_BLOCK
+    else:
+        raise ValueError("granularity must be 'tensor' or 'block'")
+    for t, shp, nm in zip((q_scale, k_scale, v_scale), shapes, ("q_scale", "k_scale", "v_scale")):
+        _check_f32(t, shp, nm)
+    _check_tensors(q8, k8, v8, q_scale, k_scale, v_scale, o, lse)
+    _check(L.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), g, _ptr(o),
+                        _ptr(lse), B, H, N, d, float(scale), int(bool(causal)), dtype_code(o), _stream(q8)))
+
+
+def fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, granularity: str = "block", causal: bool = False,
+            scale: float | None = None, out_dtype=None):
+    """Allocate O (bf16 unless out_dtype) and LSE and run the 8-bit forward."""
+    torch = _torch()
+    B, H, N, d = _bhnd(q8)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, granularity, o, lse,
+               default_scale(d) if scale is None else scale, causal)
+    return o, lse
 
 
 def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool) -> None:

@@ -506,6 +506,45 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
 
 }  // extern "C"
 
+extern "C" {
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale, const float* k_scale,
+               const float* v_scale, int scale_granularity, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+               int64_t d, float scale, int causal, int dtype, void* stream) {
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_HEADDIM;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (scale_granularity != FA_SCALE_TENSOR && scale_granularity != FA_SCALE_BLOCK) return FA_ERR_DTYPE;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  const void* sp[] = {q_scale, k_scale, v_scale};
+  for (const void* p : sp)
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return FA_ERR_ALIGN;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  fa::Fp8Args a;
+  a.q = q8;
+  a.k = k8;
+  a.v = v8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.per_block = scale_granularity == FA_SCALE_BLOCK;
+  a.o = o;
+  a.lse = lse;
+  a.BH = (int)(B * H);
+  a.N = (int)N;
+  a.d = (int)d;
+  a.c = exp2_factor(scale);
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.stream = (hipStream_t)stream;
+  return status_of(fa::launch_fwd_fp8(a));
+}
+
+}  // extern "C"
+
 // ------------------------------------------------------------ fa_bwd_noalloc
 //
 // fa_bwd without a caller workspace, for callers that cannot allocate.  Its

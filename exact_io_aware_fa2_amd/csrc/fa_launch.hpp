@@ -141,6 +141,31 @@ inline size_t kv_workspace_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t d) 
 hipError_t launch_fwd_kvcache(const KvArgs& a);
 
 
+// 8-bit (E4M3) Q, K, V with float scales (fa_fwd_fp8): [BH, N, d] codes;
+// per_block: q_scale and k_scale hold one float per 128-row block of each
+// head ([BH, ceil(N / 128)]) and v_scale one per head ([BH]); otherwise each
+// holds one float for the whole tensor.
+struct Fp8Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  int per_block;
+  void* o;      // [BH, N, d] of dtype
+  float* lse;   // [BH, N]
+  int BH;
+  int N;
+  int d;
+  float c;      // scale * log2(e)
+  int causal;
+  int dtype;    // of o and of the probabilities (DT_BF16 or DT_F16)
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd_fp8(const Fp8Args& a);
+
 // Measurement probe (fa_probe_mfma_bf16): workgroups of 4 wavefronts.
 hipError_t launch_mfma_peak(int workgroups, int iters, hipStream_t stream);
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7
+#define FA_ABI_VERSION 8
 
 typedef enum {
   FA_OK = 0,
@@ -290,6 +290,39 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
                   const void* dout, const int32_t* cu_seqlens, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, int64_t B, int64_t H, int64_t total, int64_t max_len, int64_t d,
                   float scale, int dtype, void* stream);
+
+/* Forward attention on 8-bit floating-point inputs.  The pages name 8-bit
+ * floating point as the next step of the method's line ("FlashAttention-2
+ * (DE)", "Vergleich mit nachfolgenden Versionen / FlashAttention-3"); here Q,
+ * K and V are OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, no infinities, largest value 448; one byte per element)
+ * with float scales, and S = Q K^T runs on the FP8 matrix cores.
+ *   q8, k8, v8  [B,H,N,d] uint8 E4M3 codes, 16-byte aligned; d must be 128.
+ *   q_scale,    DEVICE float32 scales (4-byte aligned), all finite and > 0:
+ *   k_scale,    FA_SCALE_TENSOR: one float each, element x of a tensor stands
+ *   v_scale     for scale * E4M3(x);  FA_SCALE_BLOCK: q_scale and k_scale
+ *               [B,H,ceil(N/128)], one per block of 128 rows of a head (row
+ *               i of head (b,h) stands for q_scale[b,h,i/128] * E4M3(q8[..])),
+ *               v_scale [B,H], one per head.  (Scales cannot be checked by
+ *               the host; a non-positive or non-finite one gives unspecified
+ *               results.)
+ *   o           [B,H,N,d] output of type dtype (FA_BF16 or FA_F16): the
+ *               probabilities are rounded to this type and multiply V, whose
+ *               codes convert to it exactly.
+ *   lse         [B,H,N] float32, natural log, as fa_fwd.
+ *   scale, causal, stream, errors: as fa_fwd (FA_ERR_HEADDIM for d != 128,
+ *   FA_ERR_DTYPE also for an unknown scale_granularity).
+ * With the dequantised values (codes times scales) the result is fa_fwd's
+ * exact attention to the 16-bit path's precision: the scores are exact
+ * products of the codes accumulated in float32, the scales multiply them in
+ * float32; only the rounding of the inputs to 8 bits differs from attention
+ * on 16-bit inputs.  Deterministic. */
+enum { FA_SCALE_TENSOR = 0, FA_SCALE_BLOCK = 1 };
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale, const float* k_scale,
+               const float* v_scale, int scale_granularity, void* o, float* lse,
+               int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+               int dtype, void* stream);
 
 /* Measurement probe, not part of attention: enqueues a kernel of `workgroups`
  * workgroups (4 wavefronts each) in which every wavefront issues `iters`

@@ -53,6 +53,31 @@ class Workload:
         return replace(self, **kw)
 
 
+@dataclass(frozen=True)
+class Fp8Workload:
+    """8-bit (E4M3) Q, K, V with float scales: the parent workload's draw
+    (same seed, same 16-bit values), quantised per tensor or per block of
+    FP8_BLOCK rows of a head (V: per head)."""
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    out_dtype: str  # 16-bit type of O and of the probabilities
+    causal: bool
+    sigma: float
+    seed: int
+    granularity: str  # "tensor" | "block"
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+    def fwd_flop(self) -> float:
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+
 WORKLOADS = {
     # tiny forward case: fp32, non-causal
     "C1": Workload("C1", 1, 2, 256, 64, "f32", False, 1.0, 1001),
@@ -66,6 +91,13 @@ WORKLOADS = {
     # backward bf16 causal with recompute (and its d=128 variant)
     "C5": Workload("C5", 8, 16, 4096, 64, "bf16", True, 1.0, 1005, backward=True),
     "C5d128": Workload("C5d128", 8, 16, 4096, 128, "bf16", True, 1.0, 1005, backward=True),
+}
+
+# the forward on 8-bit inputs: C3's and C2's draws quantised to E4M3 with one
+# scale per 128-row block of each head (V: per head), bf16 output
+FP8_WORKLOADS = {
+    "C3f8": Fp8Workload("C3f8", 2, 32, 8192, 128, "bf16", True, 1.0, 1003, "block"),
+    "C2f8": Fp8Workload("C2f8", 4, 16, 2048, 128, "bf16", False, 1.0, 1002, "block"),
 }
 
 
@@ -274,3 +306,60 @@ def make_varlen_inputs(lens_q, lens_k, H: int, d: int, dtype: str, sigma: float,
     out["cu_q"] = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
     out["cu_k"] = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
     return out
+
+
+# ---- 8-bit Q, K, V with float scales (the 8-bit forward)
+
+FP8_BLOCK = 128  # rows of a head sharing one scale (per-block scaling)
+
+
+def quantise_e4m3_scaled(x: np.ndarray, granularity: str, per_head_only: bool = False):
+    """E4M3 codes with float32 scales for a [B, H, N, d] tensor.
+
+    granularity "tensor": one scale, amax / 448 over the whole tensor;
+    "block": one scale per block of FP8_BLOCK rows of each head ([B, H,
+    ceil(N / FP8_BLOCK)]), or per head ([B, H]) with per_head_only.  A block
+    of zeros gets scale 1.  codes = round_e4m3(x / scale) in float32.
+    Returns (codes uint8, scales float32, dequantised float64 values
+    scale * e4m3(codes): exact in float64, and what the codes stand for)."""
+    x = np.asarray(x, dtype=np.float32)
+    B, H, N, d = x.shape
+    if granularity == "tensor":
+        amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+        sc = np.array([amax / np.float32(E4M3_MAX) if amax > 0 else 1.0], dtype=np.float32)
+        rows = np.broadcast_to(sc[0], (B, H, N))
+    elif per_head_only:
+        amax = np.max(np.abs(x), axis=(2, 3))
+        sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), 1.0).astype(np.float32)
+        rows = np.broadcast_to(sc[:, :, None], (B, H, N))
+    else:
+        nb = (N + FP8_BLOCK - 1) // FP8_BLOCK
+        pad = np.zeros((B, H, nb * FP8_BLOCK, d), dtype=np.float32)
+        pad[:, :, :N] = np.abs(x)
+        amax = pad.reshape(B, H, nb, FP8_BLOCK * d).max(axis=3)
+        sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), 1.0).astype(np.float32)
+        rows = np.repeat(sc, FP8_BLOCK, axis=2)[:, :, :N]
+    rows = np.ascontiguousarray(rows, dtype=np.float32)
+    codes = round_e4m3(x / rows[..., None])
+    deq = e4m3_to_f32(codes).astype(np.float64) * rows[..., None].astype(np.float64)
+    return codes, np.ascontiguousarray(sc, dtype=np.float32), deq
+
+
+def make_fp8_inputs(B: int, H: int, N: int, d: int, out_dtype: str, sigma: float, seed: int, granularity: str):
+    """Q, K, V drawn and rounded as make_inputs (the 16-bit inputs, kept as
+    "q16", "k16", "v16"), then quantised with quantise_e4m3_scaled: Q and K
+    per tensor or per block of FP8_BLOCK rows, V per tensor or per head.
+    "q", "k", "v" are (dequantised float64 values, uint8 codes) and
+    "q_scale", "k_scale", "v_scale" the float32 scales."""
+    base = make_inputs(B, H, N, d, out_dtype, sigma, seed)
+    out = {}
+    for nm in ("q", "k", "v"):
+        out[nm + "16"] = base[nm]
+        codes, sc, deq = quantise_e4m3_scaled(base[nm][0], granularity, per_head_only=(nm == "v"))
+        out[nm] = (deq, codes)
+        out[nm + "_scale"] = sc
+    return out
+
+
+def make_fp8_workload_inputs(w: Fp8Workload):
+    return make_fp8_inputs(w.B, w.H, w.N, w.d, w.out_dtype, w.sigma, w.seed, w.granularity)

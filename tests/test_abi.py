@@ -37,13 +37,13 @@ def test_header_declares_the_entry_points():
          "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kvcache_workspace_bytes",
          "fa_fwd_kvcache", "fa_fwd_kvcache_fp8", "fa_probe_mfma_bf16", "fa_fwd_varlen_workspace_bytes",
          "fa_fwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_bwd_varlen", "fa_bwd_noalloc_max_rows",
-         "fa_bwd_noalloc"])
+         "fa_bwd_noalloc", "fa_fwd_fp8"])
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 7
+    assert lib.fa_abi_version() == 8
 
 
 def test_status_strings(lib):
@@ -126,6 +126,25 @@ def test_noalloc_argument_errors(lib):
     # one row more than the scratch holds (B * H * N = rows + 64)
     assert noalloc(lib, B=rows // 64 + 1, H=1, N=64) == FA_ERR_SCRATCH
     assert noalloc(lib, B=1, H=64, N=rows // 64 + 1) == FA_ERR_SCRATCH
+
+
+def f8(lib, q=P[0], k=P[1], v=P[2], qs=P[8], ks=P[9], vs=P[10], g=1, o=P[3], lse=P[4], B=1, H=2, N=300, d=128,
+       scale=0.088, causal=1, dtype=2):
+    return lib.fa_fwd_fp8(q, k, v, qs, ks, vs, g, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+def test_fp8_argument_errors(lib):
+    for name in ("q", "k", "v", "qs", "ks", "vs", "o", "lse"):
+        assert f8(lib, **{name: None}) == FA_ERR_NULL, name
+    assert f8(lib, N=0) == FA_ERR_SHAPE
+    assert f8(lib, d=64) == FA_ERR_HEADDIM
+    assert f8(lib, d=96) == FA_ERR_HEADDIM
+    assert f8(lib, dtype=0) == FA_ERR_DTYPE  # the output is 16-bit
+    assert f8(lib, g=2) == FA_ERR_DTYPE      # unknown scale granularity
+    assert f8(lib, k=P[1] + 8) == FA_ERR_ALIGN
+    assert f8(lib, qs=P[8] + 2) == FA_ERR_ALIGN
+    assert f8(lib, scale=-1.0) == FA_ERR_SCALE
+    assert f8(lib, scale=math.inf) == FA_ERR_SCALE
 
 
 def test_stage_argument_errors(lib):

@@ -103,3 +103,35 @@ def test_fp8_cache_inputs_share_the_16_bit_draws():
         # each value is the nearest scaled code to its 16-bit draw
         x = b[nm + "16"][0] / sc
         assert np.all(np.abs(x - si.e4m3_to_f32(codes)) <= np.abs(x) * 2.0 ** -4 + 2.0 ** -10)
+
+
+def test_scaled_e4m3_blocks():
+    """Per-block quantisation: one scale per 128-row block of a head (V: per
+    head), amax / 448 each, codes whose dequantised values are within E4M3's
+    half step (2^-4 relative for normal values) of the inputs, and blocks
+    independent of each other."""
+    x = si.make_inputs(2, 3, 300, 16, "bf16", 1.0, 31)["q"][0]
+    x[0, 1, 128:256] *= 100.0  # one loud block
+    codes, sc, deq = si.quantise_e4m3_scaled(x, "block")
+    assert codes.dtype == np.uint8 and sc.shape == (2, 3, 3) and sc.dtype == np.float32
+    np.testing.assert_allclose(sc[0, 1, 1], np.abs(x[0, 1, 128:256]).max() / 448.0, rtol=1e-6)
+    np.testing.assert_allclose(sc[0, 1, 0], np.abs(x[0, 1, :128]).max() / 448.0, rtol=1e-6)
+    # the loud block's scale does not touch its neighbours
+    assert sc[0, 1, 1] > 50 * sc[0, 1, 0]
+    assert np.abs(deq).max() <= np.abs(x).max() * (1 + 2.0 ** -4)
+    big = np.abs(x) >= 2.0 ** -6 * np.repeat(sc, 128, axis=2)[:, :, :300, None]
+    rel = np.abs(deq - x) / np.abs(x)
+    assert rel[big].max() <= 2.0 ** -4 + 1e-7
+    # dequantised = code value times the float32 scale, exactly
+    rows = np.repeat(sc, 128, axis=2)[:, :, :300, None].astype(np.float64)
+    np.testing.assert_array_equal(deq, si.e4m3_to_f32(codes).astype(np.float64) * rows)
+    # per head (V) and per tensor
+    _, sh, _ = si.quantise_e4m3_scaled(x, "block", per_head_only=True)
+    assert sh.shape == (2, 3)
+    np.testing.assert_allclose(sh, np.abs(x).max(axis=(2, 3)) / 448.0, rtol=1e-6)
+    _, st, _ = si.quantise_e4m3_scaled(x, "tensor")
+    assert st.shape == (1,)
+    # an all-zero block gets scale 1 (codes 0)
+    z = np.zeros((1, 1, 130, 4), dtype=np.float32)
+    cz, sz, dz = si.quantise_e4m3_scaled(z, "block")
+    assert (sz == 1.0).all() and (cz == 0).all() and (dz == 0).all()
