@@ -11,8 +11,8 @@ attention.py  plain float64 numpy definition of attention forward (two-pass
               softmax, never online) and of its gradient (softmax Jacobian).
 kvcache.py    plain float64 definition of a few new queries attending to a
               key/value cache (fewer queries than keys, bottom-right causal
-              mask, per-batch filled lengths), and variable-length
-              packed batches built from it.
+              mask, per-batch filled lengths), its gradient (softmax
+              Jacobian), and variable-length packed batches built from both.
 brute.py      40-digit ``decimal`` brute force of both forwards for tiny
               shapes, used only to pin ``attention.py`` and ``kvcache.py``.
 
@@ -22,7 +22,7 @@ Parity status: every public function here is pinned by ``tests/test_oracle.py``
 
 from .attention import attention_fwd, attention_fwd_head, attention_bwd, attention_bwd_head
 from .brute import brute_fwd_decimal, brute_kvcache_decimal
-from .kvcache import kvcache_fwd, kvcache_fwd_head, varlen_bwd_causal, varlen_fwd
+from .kvcache import kvcache_bwd_head, kvcache_fwd, kvcache_fwd_head, varlen_bwd, varlen_bwd_causal, varlen_fwd
 
 __all__ = [
     "attention_fwd",
@@ -35,4 +35,6 @@ __all__ = [
     "kvcache_fwd_head",
     "varlen_fwd",
     "varlen_bwd_causal",
+    "kvcache_bwd_head",
+    "varlen_bwd",
 ]

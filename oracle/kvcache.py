@@ -135,3 +135,65 @@ def varlen_bwd_causal(q, k, v, do, cu, scale: float):
             g = attention_bwd_head(q[s0:s1, hi], k[s0:s1, hi], v[s0:s1, hi], do[s0:s1, hi], scale, True)
             dq[s0:s1, hi], dk[s0:s1, hi], dv[s0:s1, hi] = g
     return dq, dk, dv
+
+
+def kvcache_bwd_head(q, k, v, do, scale: float, causal: bool, seqlen: int | None = None):
+    """Gradient of ``kvcache_fwd_head``'s O with respect to q, k, v for the
+    upstream gradient do ([Nq, d]): the chain rule through the softmax over
+    each query's visible keys (the bottom-right mask above), written out as
+    the softmax Jacobian, in float64:
+
+        dV_j  = sum_i p_ij dO_i
+        dP_ij = dO_i . v_j
+        dS_ij = p_ij (dP_ij - sum_j' p_ij' dP_ij')
+        dQ_i  = scale sum_j dS_ij k_j
+        dK_j  = scale sum_i dS_ij q_i
+
+    A query with no visible key has the constant output 0: it adds nothing
+    and its dQ is 0.  Cache rows at and past the filled length get zero
+    gradients.  Returns (dQ [Nq, d], dK [Nk, d], dV [Nk, d])."""
+    q = np.asarray(q, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    nk = np.asarray(k).shape[0]
+    L = nk if seqlen is None else int(seqlen)
+    kk = np.asarray(k, dtype=np.float64)[:L]
+    vv = np.asarray(v, dtype=np.float64)[:L]
+    nq, d = q.shape
+    dq = np.zeros((nq, d))
+    dk = np.zeros((nk, kk.shape[1] if L else d))
+    dv = np.zeros((nk, vv.shape[1] if L else d))
+    if L == 0:
+        return dq, dk, dv
+    vis = _visible(nq, L, causal)
+    s = np.where(vis, scale * (q @ kk.T), -np.inf)
+    rows = vis.any(axis=1)
+    p = np.zeros((nq, L))
+    m = s[rows].max(axis=1, keepdims=True)
+    e = np.exp(s[rows] - m)
+    p[rows] = e / e.sum(axis=1, keepdims=True)  # 0 at masked keys and in empty rows
+    dv[:L] = p.T @ do
+    dp = do @ vv.T
+    ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+    dq[:] = scale * (ds @ kk)
+    dk[:L] = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def varlen_bwd(q, k, v, do, cu_q, cu_k, scale: float, causal: bool):
+    """Gradient of ``varlen_fwd``'s O for the upstream gradient do
+    [total_q, H, d]: per sequence and head ``kvcache_bwd_head`` with that
+    sequence's query and key rows (any counts; causal bottom-right aligned).
+    Returns (dQ [total_q, H, d], dK, dV [total_k, H, d]) in float64; rows of
+    no sequence stay 0."""
+    q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+    tq, h, d = q.shape
+    tk = k.shape[0]
+    dq, dk, dv = np.zeros((tq, h, d)), np.zeros((tk, h, d)), np.zeros((tk, h, v.shape[2]))
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 <= q0 and k1 <= k0:
+            continue
+        for hi in range(h):
+            g = kvcache_bwd_head(q[q0:q1, hi], k[k0:k1, hi], v[k0:k1, hi], do[q0:q1, hi], scale, causal)
+            dq[q0:q1, hi], dk[k0:k1, hi], dv[k0:k1, hi] = g
+    return dq, dk, dv

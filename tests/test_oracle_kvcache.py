@@ -273,3 +273,109 @@ def test_varlen_backward_matches_finite_differences_of_the_forward():
             args[which][idx] -= 2 * eps
             fm = f(*args)
             assert abs((fp - fm) / (2 * eps) - g[idx]) <= 1e-7
+
+
+
+# ---------------------------------------------------------------- gradient with unequal counts
+
+def _kv_grad_fd_ok(mod, nq, nk, L, causal, seed, tol=1e-7):
+    """Central differences of sum(O * dO) through kvcache_fwd_head, every
+    input element, against mod.kvcache_bwd_head."""
+    rng = np.random.default_rng(seed)
+    q, k, v, do = rnd(rng, nq, 3, s=1.2), rnd(rng, nk, 3, s=1.2), rnd(rng, nk, 3), rnd(rng, nq, 3)
+    sc = 0.7
+    dq, dk, dv = mod.kvcache_bwd_head(q, k, v, do, sc, causal, L)
+    f = lambda q_, k_, v_: float(np.sum(okv.kvcache_fwd_head(q_, k_, v_, sc, causal, L)[0] * do))
+    eps = 1e-6
+    for which, g in ((0, dq), (1, dk), (2, dv)):
+        base = (q, k, v)[which]
+        for idx in np.ndindex(*base.shape):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += eps
+            fp = f(*args)
+            args[which][idx] -= 2 * eps
+            fm = f(*args)
+            if not abs((fp - fm) / (2 * eps) - g[idx]) <= tol:
+                return False
+    return True
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk,L", [(3, 7, 5), (5, 4, 4), (6, 6, 2), (1, 4, 4), (4, 4, 4), (2, 3, 0)])
+def test_kvcache_backward_matches_finite_differences(nq, nk, L, causal):
+    """Fewer and more queries than keys, a partly filled cache, empty rows
+    (causal with nq > L), the square case and an empty cache."""
+    assert _kv_grad_fd_ok(okv, nq, nk, L, causal, seed=70 + nq + 3 * L)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kvcache_backward_square_case_is_the_ordinary_gradient(causal):
+    from oracle import attention_bwd_head
+    rng = np.random.default_rng(71)
+    q, k, v, do = (rnd(rng, 9, 4) for _ in range(4))
+    for a, b in zip(okv.kvcache_bwd_head(q, k, v, do, 0.4, causal), attention_bwd_head(q, k, v, do, 0.4, causal)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_kvcache_backward_invariants():
+    """Rows of P sum to 1 over visible keys: sum_j dV_j = sum of dO over rows
+    with a visible key; a common shift of all keys leaves O unchanged, so
+    sum_j dK_j = 0; unfilled cache rows get zero gradients."""
+    rng = np.random.default_rng(72)
+    nq, nk, L = 6, 8, 5
+    q, k, v, do = rnd(rng, nq, 3), rnd(rng, nk, 3), rnd(rng, nk, 3), rnd(rng, nq, 3)
+    dq, dk, dv = okv.kvcache_bwd_head(q, k, v, do, 0.8, True, L)
+    seen = (np.arange(nq)[:, None] + (L - nq) >= 0).ravel()  # rows with a visible key
+    np.testing.assert_allclose(dv.sum(axis=0), do[seen].sum(axis=0), atol=1e-12)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+    assert not dk[L:].any() and not dv[L:].any()
+    assert not dq[~seen].any()
+
+
+def test_varlen_backward_general_is_per_sequence_and_reduces_to_the_causal_one():
+    from oracle import varlen_bwd, varlen_bwd_causal
+    rng = np.random.default_rng(73)
+    lq, lk = [3, 0, 5, 2], [4, 2, 3, 2]
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    H, d = 2, 3
+    q, do = rnd(rng, int(cq[-1]), H, d), rnd(rng, int(cq[-1]), H, d)
+    k, v = rnd(rng, int(ck[-1]), H, d), rnd(rng, int(ck[-1]), H, d)
+    for causal in (False, True):
+        dq, dk, dv = varlen_bwd(q, k, v, do, cq, ck, 0.5, causal)
+        for b in range(4):
+            for h in range(H):
+                g = okv.kvcache_bwd_head(q[cq[b]:cq[b + 1], h], k[ck[b]:ck[b + 1], h], v[ck[b]:ck[b + 1], h],
+                                         do[cq[b]:cq[b + 1], h], 0.5, causal)
+                assert np.array_equal(dq[cq[b]:cq[b + 1], h], g[0])
+                assert np.array_equal(dk[ck[b]:ck[b + 1], h], g[1])
+                assert np.array_equal(dv[ck[b]:ck[b + 1], h], g[2])
+    # equal counts, causal: the self-attention gradient
+    lens = [4, 1, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = [rnd(rng, int(cu[-1]), H, d) for _ in range(4)]
+    for a, b in zip(varlen_bwd(*x, cu, cu, 0.5, True), varlen_bwd_causal(*x, cu, 0.5)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+KV_BWD_MUTATIONS = [
+    ("dV from dO without P", "dv[:L] = p.T @ do", "dv[:L] = np.ones_like(p).T @ do"),
+    ("Jacobian sign", "ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))",
+     "ds = p * (dp + np.sum(p * dp, axis=1, keepdims=True))"),
+    ("Jacobian term missing", "ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))", "ds = p * dp"),
+    ("dQ scale missing", "dq[:] = scale * (ds @ kk)", "dq[:] = (ds @ kk)"),
+    ("dK from the wrong operand", "dk[:L] = scale * (ds.T @ q)", "dk[:L] = scale * (ds.T @ do)"),
+    ("backward mask top-left", "s = np.where(vis, scale * (q @ kk.T), -np.inf)\n    rows = vis.any(axis=1)\n    p = ",
+     "s = np.where(_visible(nq, L, False) if False else (np.arange(L)[None, :] <= np.arange(nq)[:, None]) "
+     "if causal else vis, scale * (q @ kk.T), -np.inf)\n    rows = vis.any(axis=1)\n    p = "),
+]
+
+
+@pytest.mark.parametrize("label,old,new", KV_BWD_MUTATIONS, ids=[m[0] for m in KV_BWD_MUTATIONS])
+def test_kvcache_backward_mutations_are_caught(label, old, new):
+    src = open(okv.__file__).read()
+    assert old in src, f"mutation anchor not found: {label}"
+    mod = types.ModuleType("kv_bwd_mutant")
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
+    ok = all(_kv_grad_fd_ok(mod, nq, nk, L, causal, seed=80 + nq)
+             for causal in (False, True) for nq, nk, L in ((3, 7, 5), (5, 4, 4)))
+    assert not ok, f"finite differences did not catch mutation: {label}"
