@@ -431,7 +431,7 @@ def bench_varlen(args):
     nbb = int(lib.fa_bwd_varlen_workspace_bytes(len(lens), H, q.shape[0], mx, d, fa.FA_BF16))
     wsb = torch.empty(nbb, dtype=torch.uint8, device=dev)
     fwd = lambda: fa.fa_fwd_varlen(q, k, v, cu, cu, o, lse, ws, mx, mx, scale, True)
-    bwd = lambda: fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, dq, dk, dv, wsb, mx, scale)
+    bwd = lambda: fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, cu, dq, dk, dv, wsb, mx, mx, scale, True)
 
     def timed(call):
         for _ in range(args.warmup):

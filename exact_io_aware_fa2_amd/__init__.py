@@ -17,6 +17,10 @@ place of pointers):
     fa_fwd_kvcache_fp8(q, k_cache, v_cache, k_scale, v_scale, seqlens_k, o, lse, workspace, scale, causal)
     fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, workspace, max_q, max_k, scale, causal)
     fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, granularity, o, lse, scale, causal)
+    fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace, max_q, max_k,
+                  scale, causal)
+    fa_fwd_strided(q, k, v, o, lse, scale, causal)   ([B, H, N, d] views with any strides)
+    fa_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, causal)
 Conveniences that allocate their outputs with torch:
     fwd(q, k, v, causal=False, scale=None) -> (o, lse)
     bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
@@ -24,6 +28,7 @@ Conveniences that allocate their outputs with torch:
     fwd_kvcache_fp8(q, k8, v8, k_scale, v_scale, seqlens_k=None, causal=True, scale=None) -> (o, lse)
     fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_q, max_k, causal=False, scale=None) -> (o, lse)
     fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, granularity="block", causal=False, scale=None) -> (o, lse)
+    bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k=None, max_q=None, max_k=None, causal=True)
     FlashAttention (torch.autograd.Function) and attention(q, k, v, causal, scale)
 """
 
@@ -89,8 +94,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fa_bwd_varlen_workspace_bytes.restype = sz
     L.fa_bwd_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
     L.fa_bwd_varlen.restype = i32
-    L.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, f32, i32,
-                                vp]
+    L.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, i64,
+                                i64, f32, i32, i32, vp]
+    L.fa_fwd_strided.restype = i32
+    L.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
+    L.fa_bwd_strided.restype = i32
+    L.fa_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i64, i64, i64, i64, f32, i32, i32, vp]
     L.fa_fwd_fp8.restype = i32
     L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
     L.fa_bwd_noalloc_max_rows.restype = sz
@@ -441,47 +450,110 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_q: int, max_k: int, caus
     return o, lse
 
 
-def fa_bwd_varlen_workspace_bytes(B: int, H: int, total: int, max_len: int, d: int, dtype: int) -> int:
-    return int(load_library().fa_bwd_varlen_workspace_bytes(B, H, total, max_len, d, dtype))
+def fa_bwd_varlen_workspace_bytes(B: int, H: int, total_q: int, max_q: int, d: int, dtype: int) -> int:
+    return int(load_library().fa_bwd_varlen_workspace_bytes(B, H, total_q, max_q, d, dtype))
 
 
-def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, dq, dk, dv, workspace, max_len: int, scale: float) -> None:
-    """Enqueue the causal backward of a packed variable-length batch (see
-    include/fa.h): q, k, v, o, dout, dq, dk, dv [total, H, d]; lse float32
-    [H, total]; cu_seqlens int32 [B + 1] on the device."""
+def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace, max_q: int,
+                  max_k: int, scale: float, causal: bool) -> None:
+    """Enqueue the backward of a packed variable-length batch (see
+    include/fa.h): q, o, dout, dq [total_q, H, d]; k, v, dk, dv [total_k, H,
+    d]; lse float32 [H, total_q]; cu_seqlens_q/k int32 [B + 1] on the device
+    (the same tensor for self-attention)."""
     L = load_library()
     torch = _torch()
-    _check_tensors(q, k, v, o, lse, dout, cu_seqlens, dq, dk, dv, workspace)
-    if q.dim() != 3:
+    if q.dim() != 3 or k.dim() != 3:
         raise ValueError("packed tensors are [total, H, d]")
-    total, H, d = (int(x) for x in q.shape)
-    for t in (k, v, o, dout, dq, dk, dv):
-        if tuple(t.shape) != (total, H, d) or t.dtype != q.dtype:
-            raise ValueError("q, k, v, o, dout, dq, dk, dv must all be [total, H, d] of one dtype")
-    if tuple(lse.shape) != (H, total) or lse.dtype != torch.float32:
-        raise ValueError("lse must be float32 [H, total]")
-    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
-        raise ValueError("cu_seqlens must be int32 [B + 1]")
-    B = int(cu_seqlens.shape[0]) - 1
+    tq, H, d = (int(x) for x in q.shape)
+    tk = int(k.shape[0])
+    for t in (o, dout, dq):
+        if tuple(t.shape) != (tq, H, d) or t.dtype != q.dtype:
+            raise ValueError("q, o, dout, dq must be [total_q, H, d] of one dtype")
+    for t in (k, v, dk, dv):
+        if tuple(t.shape) != (tk, H, d) or t.dtype != q.dtype:
+            raise ValueError("k, v, dk, dv must be [total_k, H, d] of q's dtype")
+    _check_f32(lse, (H, tq), "lse")
+    B = int(cu_seqlens_q.shape[0]) - 1
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        if cu.dtype != torch.int32 or tuple(cu.shape) != (B + 1,):
+            raise ValueError("cu_seqlens must be int32 [B + 1]")
+    _check_tensors(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(L.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(cu_seqlens), _ptr(dq),
-                           _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, B, H, total, int(max_len), d, float(scale),
-                           dtype_code(q), _stream(q)))
+    _check(L.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(cu_seqlens_q),
+                           _ptr(cu_seqlens_k), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, B, H, tq, tk,
+                           int(max_q), int(max_k), d, float(scale), int(bool(causal)), dtype_code(q), _stream(q)))
 
 
-def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_len: int, scale: float | None = None, workspace=None):
+def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k=None, max_q: int | None = None,
+               max_k: int | None = None, causal: bool = True, scale: float | None = None, workspace=None):
     """Allocate dQ, dK, dV (zero rows outside every sequence) and the
-    workspace unless given, and run the causal packed backward."""
+    workspace unless given, and run the packed backward (keys share the
+    query prefix sums unless cu_seqlens_k is given)."""
     torch = _torch()
-    total, H, d = (int(x) for x in q.shape)
-    B = int(cu_seqlens.shape[0]) - 1
+    tq, H, d = (int(x) for x in q.shape)
+    cu_k = cu_seqlens_q if cu_seqlens_k is None else cu_seqlens_k
+    B = int(cu_seqlens_q.shape[0]) - 1
+    if max_q is None:
+        max_q = max(int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()), 1)
+    if max_k is None:
+        max_k = max_q if cu_seqlens_k is None else max(int((cu_k[1:] - cu_k[:-1]).max().item()), 1)
     dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
     if workspace is None:
-        nb = fa_bwd_varlen_workspace_bytes(B, H, total, max_len, d, dtype_code(q))
+        nb = fa_bwd_varlen_workspace_bytes(B, H, tq, max_q, d, dtype_code(q))
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
-    fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, dq, dk, dv, workspace, max_len,
-                  default_scale(d) if scale is None else scale)
+    fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_k, dq, dk, dv, workspace, max_q, max_k,
+                  default_scale(d) if scale is None else scale, causal)
     return dq, dk, dv
+
+
+def _strides_of(*ts):
+    """Element strides (batch, head, row) of [B, H, N, d] views whose d
+    elements are contiguous, as the flat int64 list the strided entry points
+    take."""
+    out = []
+    for t in ts:
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError("strided tensors are [B, H, N, d] views with contiguous d")
+        out += [int(t.stride(0)), int(t.stride(1)), int(t.stride(2))]
+    return (ctypes.c_int64 * len(out))(*out)
+
+
+def fa_fwd_strided(q, k, v, o, lse, scale: float, causal: bool) -> None:
+    """fa_fwd on [B, H, N, d] views with any strides (contiguous d): e.g.
+    [B, N, H, d] tensors transposed, or slices of a packed QKV tensor."""
+    L = load_library()
+    B, H, N, d = _bhnd(q)
+    for t in (k, v, o):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o must share shape and dtype")
+    _check_f32(lse, (B, H, N), "lse")
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous")
+    st = _strides_of(q, k, v, o)
+    if not all(t.is_cuda for t in (q, k, v, o, lse)):
+        raise ValueError("all tensors must be on the GPU")
+    _check(L.fa_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), st, B, H, N, d, float(scale),
+                            int(bool(causal)), dtype_code(q), _stream(q)))
+
+
+def fa_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale: float, causal: bool) -> None:
+    """fa_bwd on [B, H, N, d] views with any strides (contiguous d)."""
+    L = load_library()
+    B, H, N, d = _bhnd(q)
+    for t in (k, v, o, dout, dq, dk, dv):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dout, dq, dk, dv must share shape and dtype")
+    _check_f32(lse, (B, H, N), "lse")
+    _check_workspace(workspace, B, H, N)
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous")
+    st = _strides_of(q, k, v, o, dout, dq, dk, dv)
+    if not all(t.is_cuda for t in (q, k, v, o, lse, dout, dq, dk, dv, workspace)):
+        raise ValueError("all tensors must be on the GPU")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(L.fa_bwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                            _ptr(workspace), nbytes, st, B, H, N, d, float(scale), int(bool(causal)), dtype_code(q),
+                            _stream(q)))
 
 
 def fa_probe_mfma_bf16(workgroups: int, iters: int) -> int:

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_kvcache.hip", "fa_probe.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_bwd_wide.hip", "fa_kvcache.hip",
+           "fa_probe.hip"]
 ARCH = "gfx950"
 
 

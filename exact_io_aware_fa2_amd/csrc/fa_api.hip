@@ -26,7 +26,73 @@ int check_shape(int64_t B, int64_t H, int64_t N, int64_t d) {
   if (B > INT32_MAX / H) return FA_ERR_SHAPE;
   const int64_t bh = B * H;
   if (bh * ((N + 31) / 32) > kMaxWorkgroups) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_HEADDIM;
+  return FA_OK;
+}
+
+// The backward takes the same head dimensions (d = 256 on its own kernels),
+// with the rows a 64-row tile reaches past a head's last row within 32-bit
+// byte offsets.
+int check_shape_bwd(int64_t B, int64_t H, int64_t N, int64_t d) {
+  const int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (d == 256 && (N + 64) * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int fwd_d256(const void* q, const void* k, const void* v, void* o, float* lse, const fa::KvLayout& lay,
+             int64_t B, int64_t H, int64_t N, float scale, int causal, int dtype, void* stream);
+fa::KvLayout dense_layout(int64_t H, int64_t Nq, int64_t Nk, int64_t d);
+
+// Head dimensions the square kernels take through the general layout: 32 and
+// 96 run on the d = 64 and d = 128 kernels with the columns past d read as
+// zeros and never stored.
+bool padded_d(int64_t d) { return d == 32 || d == 96; }
+
+// Contiguous [B, H, N, d] tensors and [B, H, N] LSE as a general layout.
+fa::GenLayout dense_layout_g(int64_t H, int64_t N, int64_t d) {
+  fa::GenLayout g{};
+  const fa::Strides s{H * N * d, N * d, d};
+  g.q = g.k = g.v = g.o = g.dout = g.dq = g.dk = g.dv = s;
+  g.l_sb = H * N;
+  g.l_sh = N;
+  g.H = (int)H;
+  g.dr = (int)d;
+  return g;
+}
+
+// Packed [total, H, d] tensors (sequence b's rows from cu[b]), LSE [H, total_q].
+fa::GenLayout packed_layout_g(int64_t H, int64_t d, const int32_t* cu_q, const int32_t* cu_k, int64_t total_q,
+                              int64_t total_k) {
+  fa::GenLayout g{};
+  const fa::Strides s{0, d, H * d};
+  g.q = g.k = g.v = g.o = g.dout = g.dq = g.dk = g.dv = s;
+  g.cu_q = cu_q;
+  g.cu_k = cu_k;
+  g.total_q = total_q;
+  g.total_k = total_k;
+  g.l_sb = 0;
+  g.l_sh = total_q;
+  g.H = (int)H;
+  g.dr = (int)d;
+  return g;
+}
+
+// Caller strides (elements; batch, head, row per tensor): non-negative, every
+// row start 16-byte aligned (multiples of 8 elements), output rows not
+// overlapping (row stride >= d), and the rows a kernel reaches from a head's
+// first row (N plus a 512-row prefetch margin) within 32-bit byte offsets.
+int check_strides(const int64_t* st, int ntensors, const bool* output, int64_t N, int64_t d) {
+  for (int t = 0; t < ntensors; ++t) {
+    for (int j = 0; j < 3; ++j) {
+      const int64_t x = st[3 * t + j];
+      if (x < 0) return FA_ERR_SHAPE;
+      if (x % 8) return FA_ERR_ALIGN;
+    }
+    const int64_t sr = st[3 * t + 2];
+    if (sr < d && (output[t] || N > 1)) return FA_ERR_SHAPE;
+    if ((N + 512) * sr * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  }
   return FA_OK;
 }
 
@@ -59,7 +125,7 @@ const char* fa_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "null pointer argument";
     case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and within limits)";
-    case FA_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
+    case FA_ERR_HEADDIM: return "unsupported head dimension for this entry point";
     case FA_ERR_DTYPE: return "unsupported dtype";
     case FA_ERR_ALIGN: return "data pointer not 16-byte aligned";
     case FA_ERR_SCALE: return "scale must be finite and >= 0";
@@ -76,12 +142,20 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (dtype == FA_F32 && d != 64 && d != 128) return FA_ERR_HEADDIM;  // float32: d = 64 or 128
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
   st = check_scale(scale);
   if (st != FA_OK) return st;
+  if (d == 256) {
+    // rows a wavefront reaches from a head's first row stay within 32-bit byte offsets
+    if ((N + 64) * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+    return fwd_d256(q, k, v, o, lse, dense_layout(H, N, N, d), B, H, N, scale, causal, dtype, stream);
+  }
 
   fa::FwdArgs a;
+  a.general = padded_d(d);
+  a.g = dense_layout_g(H, N, d);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -98,7 +172,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 }
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
-  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  if (check_shape_bwd(B, H, N, d) != FA_OK) return 0;
   if (dtype != FA_F16 && dtype != FA_BF16) return 0;
   return (size_t)(B * H * N) * sizeof(float);
 }
@@ -114,7 +188,7 @@ int bwd_common(fa::BwdArgs& a, const void* const* ptrs, int nptrs, const void* w
                int causal, int dtype, void* stream) {
   for (int i = 0; i < nptrs; ++i)
     if (!ptrs[i]) return FA_ERR_NULL;
-  int st = check_shape(B, H, N, d);
+  int st = check_shape_bwd(B, H, N, d);
   if (st != FA_OK) return st;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   for (int i = 0; i < nptrs; ++i)
@@ -127,8 +201,10 @@ int bwd_common(fa::BwdArgs& a, const void* const* ptrs, int nptrs, const void* w
   a = fa::BwdArgs{};
   a.dvec = (float*)workspace;
   a.BH = (int)(B * H);
-  a.N = (int)N;
+  a.Nq = a.Nk = (int)N;
   a.d = (int)d;
+  a.general = padded_d(d);
+  a.g = dense_layout_g(H, N, d);
   a.scale = scale;
   a.c = exp2_factor(scale);
   a.causal = causal != 0;
@@ -227,22 +303,50 @@ int check_kv_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
   if (bh * Nq > INT32_MAX) return FA_ERR_SHAPE;
   const fa::KvPlan p = fa::kv_plan(bh, Nq, Nk, d);
   if ((bh * p.n_qb * p.n_splits + 3) / 4 > kMaxWorkgroups) return FA_ERR_SHAPE;
-  if (d != 32 && d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (d != 32 && d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
   return FA_OK;
 }
 
 // [B, H, N, d] queries and outputs, [B, H, Nk, d] caches, [B, H, Nq] LSE.
 fa::KvLayout dense_layout(int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
   fa::KvLayout l{};
-  l.q_sb = H * Nq * d;
-  l.q_sh = Nq * d;
-  l.q_sr = d;
-  l.c_sb = H * Nk * d;
-  l.c_sh = Nk * d;
-  l.c_sr = d;
+  l.q_sb = l.o_sb = H * Nq * d;
+  l.q_sh = l.o_sh = Nq * d;
+  l.q_sr = l.o_sr = d;
+  l.c_sb = l.v_sb = H * Nk * d;
+  l.c_sh = l.v_sh = Nk * d;
+  l.c_sr = l.v_sr = d;
   l.l_sb = H * Nq;
   l.l_sh = Nq;
   return l;
+}
+
+// The square forward at d = 256: the split-key kernel with one key range per
+// head (no workspace), queries = keys, the square causal mask (bottom-right
+// and top-left alignment coincide for equal counts).
+int fwd_d256(const void* q, const void* k, const void* v, void* o, float* lse, const fa::KvLayout& lay,
+             int64_t B, int64_t H, int64_t N, float scale, int causal, int dtype, void* stream) {
+  fa::KvArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.seqlens = nullptr;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = nullptr;
+  a.lay = lay;
+  a.H = (int)H;
+  a.BH = (int)(B * H);
+  a.Nq = a.Nk = (int)N;
+  a.d = 256;
+  a.c = exp2_factor(scale);
+  a.v_scale = 1.0f;
+  a.fp8_cache = 0;
+  a.one_range = 1;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.stream = (hipStream_t)stream;
+  return fa::launch_fwd_kvcache(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // namespace
@@ -303,6 +407,7 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, 
   if (!q || !k_cache || !v_cache || !o || !lse) return FA_ERR_NULL;
   int st = check_kv_shape(B, H, Nq, Nk, d);
   if (st != FA_OK) return st;
+  if (d == 256) return FA_ERR_HEADDIM;  // the 8-bit cache: d = 32, 64, 128
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
@@ -367,7 +472,8 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
                   int64_t B, int64_t H, int64_t total_q, int64_t total_k, int64_t max_q, int64_t max_k,
                   int64_t d, float scale, int causal, int dtype, void* stream) {
   if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !o || !lse) return FA_ERR_NULL;
-  int st = check_kv_shape(B, H, max_q, max_k, d);
+  // d = 96: the square kernels only (self-attention below); the split-key kernel takes 32, 64, 128
+  int st = check_kv_shape(B, H, max_q, max_k, d == 96 ? 128 : d);
   if (st != FA_OK) return st;
   if (total_q < 1 || total_k < 1 || total_q > INT32_MAX || total_k > INT32_MAX) return FA_ERR_SHAPE;
   // one sequence's rows must stay within 32-bit byte offsets of its first row
@@ -382,7 +488,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
   // forward kernels, reading and writing the packed rows in place, when the
   // head size is theirs and the rows a 256-row tile and its prefetch reach
   // stay within 32-bit byte offsets of a sequence's first row.
-  if (cu_seqlens_q == cu_seqlens_k && total_q == total_k && max_q == max_k && (d == 64 || d == 128) &&
+  if (cu_seqlens_q == cu_seqlens_k && total_q == total_k && max_q == max_k && d <= 128 &&
       (max_q + 512) * H * d * 2 < (int64_t(1) << 31) && total_q * H <= INT32_MAX) {
     fa::FwdArgs f;
     f.q = q;
@@ -397,11 +503,11 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
     f.causal = causal != 0;
     f.dtype = dtype;
     f.stream = (hipStream_t)stream;
-    f.cu = cu_seqlens_q;
-    f.H = (int)H;
-    f.total = (int)total_q;
+    f.general = true;
+    f.g = packed_layout_g(H, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k);
     return status_of(fa::launch_fwd(f));
   }
+  if (d == 96) return FA_ERR_HEADDIM;
   const size_t need = fa::kv_workspace_bytes(B * H, max_q, max_k, d);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
@@ -416,12 +522,12 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
   a.lse = lse;
   a.workspace = need > 0 ? workspace : nullptr;
   fa::KvLayout l{};
-  l.q_sb = 0;  // packed [total, H, d]: sequence b starts at row cu[b]
-  l.q_sh = d;
-  l.q_sr = H * d;
-  l.c_sb = 0;
-  l.c_sh = d;
-  l.c_sr = H * d;
+  l.q_sb = l.o_sb = 0;  // packed [total, H, d]: sequence b starts at row cu[b]
+  l.q_sh = l.o_sh = d;
+  l.q_sr = l.o_sr = H * d;
+  l.c_sb = l.v_sb = 0;
+  l.c_sh = l.v_sh = d;
+  l.c_sr = l.v_sr = H * d;
   l.l_sb = 0;  // [H, total_q]
   l.l_sh = total_q;
   l.cu_q = cu_seqlens_q;
@@ -447,35 +553,41 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
 
 extern "C" {
 
-size_t fa_bwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t total, int64_t max_len, int64_t d,
+size_t fa_bwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t total_q, int64_t max_q, int64_t d,
                                      int dtype) {
-  if (check_shape(B, H, max_len, d) != FA_OK) return 0;
-  if (total < 1 || total > INT32_MAX || total * H > INT32_MAX) return 0;
+  if (check_shape_bwd(B, H, max_q, d) != FA_OK) return 0;
+  if (total_q < 1 || total_q > INT32_MAX || total_q * H > INT32_MAX) return 0;
   if (dtype != FA_F16 && dtype != FA_BF16) return 0;
-  return (size_t)(total * H) * sizeof(float);
+  return (size_t)(total_q * H) * sizeof(float);
 }
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                  const void* dout, const int32_t* cu_seqlens, void* dq, void* dk, void* dv, void* workspace,
-                  size_t workspace_bytes, int64_t B, int64_t H, int64_t total, int64_t max_len, int64_t d,
-                  float scale, int dtype, void* stream) {
+                  const void* dout, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq, void* dk,
+                  void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t total_q,
+                  int64_t total_k, int64_t max_q, int64_t max_k, int64_t d, float scale, int causal, int dtype,
+                  void* stream) {
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
   for (const void* p : ptrs)
     if (!p) return FA_ERR_NULL;
-  if (!cu_seqlens) return FA_ERR_NULL;
-  int st = check_shape(B, H, max_len, d);
+  if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, max_q, d);
   if (st != FA_OK) return st;
-  if (total < 1 || total > INT32_MAX || total * H > INT32_MAX) return FA_ERR_SHAPE;
-  // one sequence's rows, and the rows past them a 128-row tile and its
-  // prefetch reach, stay within 32-bit byte offsets of its first row
-  if ((max_len + 128) * H * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  st = check_shape_bwd(B, H, max_k, d);
+  if (st != FA_OK) return st;
+  if (total_q < 1 || total_q > INT32_MAX || total_q * H > INT32_MAX) return FA_ERR_SHAPE;
+  if (total_k < 1 || total_k > INT32_MAX || total_k * H > INT32_MAX) return FA_ERR_SHAPE;
+  // one sequence's rows, and the rows past them a tile and its prefetch
+  // reach, stay within 32-bit byte offsets of its first row
+  if ((max_q + 512) * H * d * 2 >= (int64_t(1) << 31) || (max_k + 512) * H * d * 2 >= (int64_t(1) << 31))
+    return FA_ERR_SHAPE;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
-  if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return FA_ERR_ALIGN;
   st = check_scale(scale);
   if (st != FA_OK) return st;
-  if (!workspace || workspace_bytes < fa_bwd_varlen_workspace_bytes(B, H, total, max_len, d, dtype))
+  if (!workspace || workspace_bytes < fa_bwd_varlen_workspace_bytes(B, H, total_q, max_q, d, dtype))
     return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
 
@@ -489,18 +601,18 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.dvec = (float*)workspace;  // D_i, [H, total]
+  a.dvec = (float*)workspace;  // D_i, [H, total_q] like the LSE
   a.BH = (int)(B * H);
-  a.N = (int)max_len;
+  a.Nq = (int)max_q;
+  a.Nk = (int)max_k;
   a.d = (int)d;
   a.scale = scale;
   a.c = exp2_factor(scale);
-  a.causal = 1;
+  a.causal = causal != 0;
   a.dtype = dtype;
   a.stream = (hipStream_t)stream;
-  a.cu = cu_seqlens;
-  a.H = (int)H;
-  a.total = (int)total;
+  a.general = true;
+  a.g = packed_layout_g(H, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k);
   return status_of(fa::launch_bwd(a));
 }
 
@@ -604,7 +716,7 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
   for (const void* p : ptrs)
     if (!p) return FA_ERR_NULL;
-  int st = check_shape(B, H, N, d);
+  int st = check_shape_bwd(B, H, N, d);
   if (st != FA_OK) return st;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   for (const void* p : ptrs)
@@ -618,6 +730,76 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
   // nothing in the scratch has to start at zero
   return fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, kScratchBytes, B, H, N, d, scale, causal, dtype,
                 stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, const int64_t* strides,
+                   int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !strides) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  const bool out[4] = {false, false, false, true};
+  st = check_strides(strides, 4, out, N, d);
+  if (st != FA_OK) return st;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = (int)(B * H);
+  a.N = (int)N;
+  a.d = (int)d;
+  a.c = exp2_factor(scale);
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.stream = (hipStream_t)stream;
+  a.general = true;
+  a.g = dense_layout_g(H, N, d);
+  fa::Strides* t[4] = {&a.g.q, &a.g.k, &a.g.v, &a.g.o};
+  for (int i = 0; i < 4; ++i) *t[i] = fa::Strides{strides[3 * i], strides[3 * i + 1], strides[3 * i + 2]};
+  if (d == 256) {
+    fa::KvLayout l = dense_layout(H, N, N, d);
+    l.q_sb = strides[0], l.q_sh = strides[1], l.q_sr = strides[2];
+    l.c_sb = strides[3], l.c_sh = strides[4], l.c_sr = strides[5];
+    l.v_sb = strides[6], l.v_sh = strides[7], l.v_sr = strides[8];
+    l.o_sb = strides[9], l.o_sh = strides[10], l.o_sr = strides[11];
+    return fwd_d256(q, k, v, o, lse, l, B, H, N, scale, causal, dtype, stream);
+  }
+  return status_of(fa::launch_fwd(a));
+}
+
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, const int64_t* strides,
+                   int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, void* stream) {
+  if (!strides) return FA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  fa::BwdArgs a;
+  int st = bwd_common(a, ptrs, 9, workspace, workspace_bytes, B, H, N, d, scale, causal, dtype, stream);
+  if (st != FA_OK) return st;
+  const bool out[8] = {false, false, false, false, false, true, true, true};
+  st = check_strides(strides, 8, out, N, d);
+  if (st != FA_OK) return st;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.general = true;
+  fa::Strides* t[8] = {&a.g.q, &a.g.k, &a.g.v, &a.g.o, &a.g.dout, &a.g.dq, &a.g.dk, &a.g.dv};
+  for (int i = 0; i < 8; ++i) *t[i] = fa::Strides{strides[3 * i], strides[3 * i + 1], strides[3 * i + 2]};
+  return status_of(fa::launch_bwd(a));
 }
 
 }  // extern "C"

@@ -36,27 +36,40 @@ namespace fa {
 
 // ------------------------------------------------------------------ D_i
 
-// VL: O and dO are a packed [total, H, D] batch (row = t H + h) and D_i is
-// stored as [H, total], the layout of the packed LSE.
-template <class TR, int D, bool VL>
+// GL: the general layout (strides of O and dO, packed sequences, DR < D
+// columns); rows = BH * Nq, row r is query r % Nq of head r / Nq, skipped
+// past its sequence's count, and D_i goes where the LSE entry of that row is.
+template <class TR, int D, bool GL>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
                                                       const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ Dv, int rows, int H, int total) {
+                                                      float* __restrict__ Dv, int rows, int Nq, GenLayout g) {
   constexpr int KCH = D / 8;            // lanes per row
   constexpr int RPB = 256 / KCH;        // rows per workgroup
   const int tid = threadIdx.x;
   const int row = blockIdx.x * RPB + tid / KCH;
   const int ch = tid % KCH;
   float acc = 0.0f;
-  if (row < rows) {
-    const u32x4_t a = *(const u32x4_t*)(O + (size_t)row * D + ch * 8);
-    const u32x4_t b = *(const u32x4_t*)(dO + (size_t)row * D + ch * 8);
+  bool real = row < rows;
+  size_t o_at = (size_t)row * D, do_at = (size_t)row * D, d_at = (size_t)row;
+  if constexpr (GL) {
+    const int bh = real ? row / Nq : 0, i = real ? row - bh * Nq : 0;
+    const int b = bh / g.H, hd = bh - b * g.H;
+    int sq = 0, lq = 0;
+    if (real) seq_rows(g.cu_q, g.total_q, b, Nq, sq, lq);
+    real = real && i < lq;
+    o_at = (size_t)((int64_t)b * g.o.sb + (int64_t)hd * g.o.sh + (int64_t)(sq + i) * g.o.sr);
+    do_at = (size_t)((int64_t)b * g.dout.sb + (int64_t)hd * g.dout.sh + (int64_t)(sq + i) * g.dout.sr);
+    d_at = (size_t)((int64_t)b * g.l_sb + (int64_t)hd * g.l_sh + sq + i);
+  }
+  if (real && (!GL || ch < g.dr / 8)) {
+    const u32x4_t a = *(const u32x4_t*)(O + o_at + ch * 8);
+    const u32x4_t b = *(const u32x4_t*)(dO + do_at + ch * 8);
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc = TR::dot2(a[p], b[p], acc);
   }
 #pragma unroll
   for (int off = KCH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && ch == 0) Dv[VL ? (size_t)(row % H) * total + row / H : (size_t)row] = acc;
+  if (real && ch == 0) Dv[d_at] = acc;
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -81,14 +94,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // the dV/dK products lie 4 rows apart: with the padded rows, both the row
 // reads (S, dP) and the transposed reads (dV, dK) are free of bank conflicts,
 // and no transposed copy of Q or dO is staged.
-template <class TR, int D, bool CAUSAL, int OCC, bool VL>
+template <class TR, int D, bool CAUSAL, int OCC, bool GL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dvec,
-                          uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_ktiles,
-                          uint32_t total, float c, float neg_inv_scale, float scale,
-                          const int32_t* __restrict__ cu, int H, int n_rows) {
+                          uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Nq, int Nk, int n_ktiles,
+                          uint32_t total, float c, float neg_inv_scale, float scale, GenLayout g) {
   constexpr int NT = 256;
   constexpr int BKV = 128;                  // keys per workgroup
   constexpr int BQ = 64;                    // query rows per stage
@@ -128,25 +140,50 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int k0 = kt * BKV;
   const int kw = k0 + 32 * w;               // first key of this wavefront
   const int key = kw + l32;
-  // Packed batches are causal only: a real query never sees a key past
-  // Nb, and tiles wholly past Nb are skipped.
-  const HeadRows hr = head_rows<D, VL>(bh, N, cu, H, n_rows);
-  const int Nb = hr.Nb;
-  if (VL && k0 >= Nb) return;
-  const size_t head_off = hr.off;
-  const uint32_t head_bytes = hr.bytes;
-  const uint32_t rs = VL ? hr.rs : RB;
+  // Addressing: dense [BH, N, D] (Nq = Nk), or (GL) the general layout:
+  // per-tensor strides, packed sequences with Lq queries and Lk keys (key
+  // tiles wholly past Lk skipped), DR < D data columns.  Causal is aligned
+  // bottom right: key j is visible to query i iff j <= i + delta, delta =
+  // Lk - Lq (0 for equal counts: the square mask).
+  int Lq = Nq, Lk = Nk, DR = D, delta = 0;
+  size_t q_off, do_off, k_off, v_off, dk_off, dv_off, l_off, dks, dvs;
+  uint32_t q_bytes, do_bytes, k_bytes, v_bytes, rsq, rsdo, rsk, rsv;
+  if constexpr (GL) {
+    const int b = bh / g.H, hd = bh - b * g.H;
+    int sq, sk;
+    seq_rows(g.cu_q, g.total_q, b, Nq, sq, Lq);
+    seq_rows(g.cu_k, g.total_k, b, Nk, sk, Lk);
+    DR = g.dr;
+    delta = CAUSAL ? Lk - Lq : 0;
+    const TRows tq = tensor_rows(g.q, b, hd, sq, Lq, DR), tdo = tensor_rows(g.dout, b, hd, sq, Lq, DR);
+    const TRows tk = tensor_rows(g.k, b, hd, sk, Lk, DR), tv = tensor_rows(g.v, b, hd, sk, Lk, DR);
+    q_off = tq.off, do_off = tdo.off, k_off = tk.off, v_off = tv.off;
+    q_bytes = tq.bytes, do_bytes = tdo.bytes, k_bytes = tk.bytes, v_bytes = tv.bytes;
+    rsq = tq.rs, rsdo = tdo.rs, rsk = tk.rs, rsv = tv.rs;
+    dk_off = (size_t)((int64_t)b * g.dk.sb + (int64_t)hd * g.dk.sh + (int64_t)sk * g.dk.sr);
+    dv_off = (size_t)((int64_t)b * g.dv.sb + (int64_t)hd * g.dv.sh + (int64_t)sk * g.dv.sr);
+    dks = (size_t)g.dk.sr, dvs = (size_t)g.dv.sr;
+    l_off = (size_t)((int64_t)b * g.l_sb + (int64_t)hd * g.l_sh + sq);
+  } else {
+    q_off = do_off = k_off = v_off = dk_off = dv_off = (size_t)bh * Nq * D;
+    q_bytes = do_bytes = k_bytes = v_bytes = (uint32_t)Nq * RB;
+    rsq = rsdo = rsk = rsv = RB;
+    dks = dvs = D;
+    l_off = (size_t)bh * Nq;
+  }
+  if (GL && k0 >= Lk) return;
 
   // K and V rows of this wavefront's keys as B operands (column = key)
   u32x4_t kf[NKS], vf[NKS];
   {
-    const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
-    const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
-    const uint32_t off = (uint32_t)key * rs + 16 * h;
+    const rsrc_t kres = make_rsrc(K + k_off, k_bytes);
+    const rsrc_t vres = make_rsrc(V + v_off, v_bytes);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = buf_load16(kres, off + 32 * ks);
-      vf[ks] = buf_load16(vres, off + 32 * ks);
+      const uint32_t pad_k = GL ? col_pad(32 * ks + 16 * h, DR, k_bytes) : 0u;
+      const uint32_t pad_v = GL ? col_pad(32 * ks + 16 * h, DR, v_bytes) : 0u;
+      kf[ks] = buf_load16(kres, (uint32_t)key * rsk + 16 * h + 32 * ks + pad_k);
+      vf[ks] = buf_load16(vres, (uint32_t)key * rsv + 16 * h + 32 * ks + pad_v);
     }
   }
   f32x16_t acc_dk[NDB], acc_dv[NDB];
@@ -166,22 +203,39 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int L16 = lane & 15, G = lane >> 4;
   const uint32_t tbase = (uint32_t)((h + 4 * (L16 >> 2)) * RBL + (16 * (G & 1) + 4 * (L16 & 3)) * 2);
 
-  const int i_begin = CAUSAL ? k0 : 0;
-  const int n_st = (Nb - i_begin + BQ - 1) / BQ;
+  // the first query row that sees a key of this tile (causal), and the stages
+  const int i_begin = CAUSAL ? max(0, k0 - delta) : 0;
+  const int n_st = (Lq - i_begin + BQ - 1) / BQ;
+  const int nrows = min(32, Lk - kw);
+  const int nch = GL ? DR / 8 : D / 8;
+  if (GL && n_st <= 0) {
+    // no query sees these keys (an empty query sequence): dK = dV = 0
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int i = lane; i < 32 * (D / 8); i += 64) {
+      const int r = i / (D / 8), ch = i % (D / 8);
+      if (r < nrows && ch < nch) {
+        *(u32x4_t*)(dK + dk_off + (size_t)(kw + r) * dks + 8 * ch) = z;
+        *(u32x4_t*)(dV + dv_off + (size_t)(kw + r) * dvs + 8 * ch) = z;
+      }
+    }
+    return;
+  }
 
   // ---- staging: chunk i of this thread is row tid / CPR + ROWSTEP i, column
   // chunk tid % CPR, of both Q and dO.  Wave w loads vector w % 2 of the stage
   // (0: -LSE / scale, 1: -D) at positions m = lane: row 32 (m / 32) + perm(m % 32).
-  const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
-  const rsrc_t ores = make_rsrc(dO + head_off, head_bytes);
+  const rsrc_t qres = make_rsrc(Q + q_off, q_bytes);
+  const rsrc_t ores = make_rsrc(dO + do_off, do_bytes);
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const bool is_d = (wu & 1) != 0;
-  const rsrc_t vres = make_rsrc(is_d ? (const void*)(Dvec + hr.vec) : (const void*)(LSE + hr.vec),
-                                (uint32_t)Nb * 4);
-  const uint32_t g_off = (uint32_t)(tid / CPR) * rs + (tid % CPR) * 16;
+  const rsrc_t vres = make_rsrc(is_d ? (const void*)(Dvec + l_off) : (const void*)(LSE + l_off),
+                                (uint32_t)Lq * 4);
+  const uint32_t g_col = (tid % CPR) * 16;
+  const uint32_t gq_off = (uint32_t)(tid / CPR) * rsq + g_col + (GL ? col_pad(g_col, DR, q_bytes) : 0u);
+  const uint32_t go_off = (uint32_t)(tid / CPR) * rsdo + g_col + (GL ? col_pad(g_col, DR, do_bytes) : 0u);
   const uint32_t s_off = (uint32_t)(tid / CPR) * RBL + (tid % CPR) * 16;
   const int vrow = (lane & 32) + perm(lane & 31);
-  const uint32_t v_off = OFF_L + 4 * BQ * wu + 4 * lane;
+  const uint32_t vec_off = OFF_L + 4 * BQ * wu + 4 * lane;
   // The loaded values are only used when they are written to LDS (a whole
   // iteration later), so no wait for the loads stalls the products.  Set 1
   // of the staging registers is used only by the prologue (two stages in
@@ -192,11 +246,12 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   // staging part j < NCH: Q chunk j; j < 2 NCH: dO chunk j - NCH; j = 2 NCH: the vector
   constexpr int NPART = 2 * NCH + 1;
   auto load_part = [&](int i0, int j, int t = 0) __attribute__((always_inline)) {
-    const uint32_t base = g_off + (uint32_t)i0 * rs;
     if (j < NCH) {
-      sq[t][j] = buf_load16(qres, base + ROWSTEP * j * rs);
+      const uint32_t r = GL ? __builtin_amdgcn_readfirstlane(rsq) : RB;
+      sq[t][j] = buf_load16(qres, gq_off + (uint32_t)(i0 + ROWSTEP * j) * r);
     } else if (j < 2 * NCH) {
-      so[t][j - NCH] = buf_load16(ores, base + ROWSTEP * (j - NCH) * rs);
+      const uint32_t r = GL ? __builtin_amdgcn_readfirstlane(rsdo) : RB;
+      so[t][j - NCH] = buf_load16(ores, go_off + (uint32_t)(i0 + ROWSTEP * (j - NCH)) * r);
     } else {
       vidx[t] = i0 + vrow;
       vraw[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vres, (uint32_t)vidx[t] * 4, 0, 0));
@@ -209,8 +264,8 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       *(u32x4_t*)(smem + sb + OFF_O + s_off + ROWSTEP * (j - NCH) * RBL) = so[t][j - NCH];
     } else {
       // rows past the end: -inf initialises their S, so P = 0; D = 0
-      const bool in = vidx[t] < Nb;
-      *(float*)(smem + sb + v_off) = is_d ? (in ? -vraw[t] : 0.0f) : (in ? vraw[t] * neg_inv_scale : -INFINITY);
+      const bool in = vidx[t] < Lq;
+      *(float*)(smem + sb + vec_off) = is_d ? (in ? -vraw[t] : 0.0f) : (in ? vraw[t] * neg_inv_scale : -INFINITY);
     }
   };
 
@@ -269,7 +324,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     load_vecs(sb1, NB, dp[NB], sc[NB]);
 
     // causal: key kw + l32 is visible to the row of score r iff thr <= qoff(r)
-    const int thr = kw - q0 + l32 - h;
+    const int thr = kw - delta - q0 + l32 - h;
     float pe[16], dsv[16];
     auto vwork = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
@@ -348,8 +403,9 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
   for (int x = 0; x < AH; ++x) fr[x] = frag(x, 0u, 3u * STG, 1);
 
-  // ---- pairs of iterations over the stages.  Causal: the blocks of the first
-  // two stages (each wavefront's diagonal block and those above it) are masked.
+  // ---- pairs of iterations over the stages.  Causal: the stages with a
+  // query that does not see every key of the tile are masked (with the square
+  // mask: the first two, each wavefront's diagonal block and those above it).
   auto pair = [&](auto masked_c, int s) __attribute__((always_inline)) {
     const uint32_t b0 = (uint32_t)(s & 3) * STG;
     const uint32_t bp1 = (uint32_t)((s + 1) & 3) * STG;
@@ -360,7 +416,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     iteration(std::integral_constant<int, 1>{}, masked_c, bp1, b0, bp1, b0, q0 + 32, 0, bp2);
     lds_barrier();
   };
-  const int n_masked = CAUSAL ? min(2, n_st) : 0;
+  const int n_masked = CAUSAL ? min((k0 + BKV - delta - i_begin + BQ - 1) / BQ, n_st) : 0;
   int s = 0;
   for (; s < n_masked; ++s) pair(std::true_type{}, s);
   for (; s < n_st; ++s) pair(std::false_type{}, s);
@@ -394,12 +450,10 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                           TR::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3])};
     }
   static_assert(4 * kTileRowsBytes<D> <= STG, "four wavefronts' rows fit one stage slot");
-  const int nrows = min(32, Nb - kw);
-  const size_t ostride = VL ? (size_t)H * D : (size_t)D;
   store_tile_rows<D>(smem + ((n_st + 1) & 3) * STG + w * kTileRowsBytes<D>, ok,
-                     dK + head_off + (size_t)kw * ostride, nrows, lane, ostride);
+                     dK + dk_off + (size_t)kw * dks, nrows, lane, dks, nch);
   store_tile_rows<D>(smem + ((n_st + 2) & 3) * STG + w * kTileRowsBytes<D>, ov,
-                     dV + head_off + (size_t)kw * ostride, nrows, lane, ostride);
+                     dV + dv_off + (size_t)kw * dvs, nrows, lane, dvs, nch);
 }
 
 // ------------------------------------------------------------------ dQ
@@ -418,13 +472,13 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 // are per-lane constants (D enters as the dP accumulators' initial value).
 // Keys past the end need no mask: their K and V rows read as zeros, so their
 // dS multiplies a zero row of K.
-template <class TR, int D, bool CAUSAL, int OCC, bool VL>
+template <class TR, int D, bool CAUSAL, int OCC, bool GL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ Dvec,
-                        uint16_t* __restrict__ dQ, int N, int n_qtiles, uint32_t total, float c,
-                        float scale, const int32_t* __restrict__ cu, int H, int n_rows) {
+                        uint16_t* __restrict__ dQ, int Nq, int Nk, int n_qtiles, uint32_t total, float c,
+                        float scale, GenLayout g) {
   constexpr int NT = 256;
   constexpr int BR = 128;                   // query rows per workgroup
   constexpr int BC = 64;                    // keys per stage
@@ -463,31 +517,53 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const int q0 = qt * BR;
   const int qw = q0 + 32 * w;               // first query row of this wavefront
   const int qrow = qw + l32;
-  // Packed batches (causal only, as in the dK/dV kernel): query tiles
-  // wholly past the sequence's length Nb are skipped, and no key from Nb on
-  // is read for the rest (under the causal mask no real query sees one).
-  const HeadRows hr = head_rows<D, VL>(bh, N, cu, H, n_rows);
-  const int Nb = hr.Nb;
-  if (VL && q0 >= Nb) return;
-  const size_t head_off = hr.off;
-  const uint32_t head_bytes = hr.bytes;
-  const uint32_t rs = VL ? hr.rs : RB;
+  // Addressing as in the dK/dV kernel: dense [BH, N, D], or (GL) per-tensor
+  // strides, packed sequences of Lq queries and Lk keys (query tiles wholly
+  // past Lq skipped), DR < D data columns; causal aligned bottom right (key j
+  // visible to query i iff j <= i + delta, delta = Lk - Lq).
+  int Lq = Nq, Lk = Nk, DR = D, delta = 0;
+  size_t q_off, do_off, k_off, v_off, dq_off, l_off, dqs;
+  uint32_t q_bytes, do_bytes, k_bytes, v_bytes, rsq, rsdo, rsk, rsv;
+  if constexpr (GL) {
+    const int b = bh / g.H, hd = bh - b * g.H;
+    int sq, sk;
+    seq_rows(g.cu_q, g.total_q, b, Nq, sq, Lq);
+    seq_rows(g.cu_k, g.total_k, b, Nk, sk, Lk);
+    DR = g.dr;
+    delta = CAUSAL ? Lk - Lq : 0;
+    const TRows tq = tensor_rows(g.q, b, hd, sq, Lq, DR), tdo = tensor_rows(g.dout, b, hd, sq, Lq, DR);
+    const TRows tk = tensor_rows(g.k, b, hd, sk, Lk, DR), tv = tensor_rows(g.v, b, hd, sk, Lk, DR);
+    q_off = tq.off, do_off = tdo.off, k_off = tk.off, v_off = tv.off;
+    q_bytes = tq.bytes, do_bytes = tdo.bytes, k_bytes = tk.bytes, v_bytes = tv.bytes;
+    rsq = tq.rs, rsdo = tdo.rs, rsk = tk.rs, rsv = tv.rs;
+    dq_off = (size_t)((int64_t)b * g.dq.sb + (int64_t)hd * g.dq.sh + (int64_t)sq * g.dq.sr);
+    dqs = (size_t)g.dq.sr;
+    l_off = (size_t)((int64_t)b * g.l_sb + (int64_t)hd * g.l_sh + sq);
+  } else {
+    q_off = do_off = k_off = v_off = dq_off = (size_t)bh * Nq * D;
+    q_bytes = do_bytes = k_bytes = v_bytes = (uint32_t)Nq * RB;
+    rsq = rsdo = rsk = rsv = RB;
+    dqs = D;
+    l_off = (size_t)bh * Nq;
+  }
+  if (GL && q0 >= Lq) return;
 
   // Q and dO rows of this wavefront's queries as B operands (column = query)
   u32x4_t qf[NKS], of[NKS];
   {
-    const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
-    const rsrc_t ores = make_rsrc(dO + head_off, head_bytes);
-    const uint32_t off = (uint32_t)qrow * rs + 16 * h;
+    const rsrc_t qres = make_rsrc(Q + q_off, q_bytes);
+    const rsrc_t ores = make_rsrc(dO + do_off, do_bytes);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      qf[ks] = buf_load16(qres, off + 32 * ks);
-      of[ks] = buf_load16(ores, off + 32 * ks);
+      const uint32_t pad_q = GL ? col_pad(32 * ks + 16 * h, DR, q_bytes) : 0u;
+      const uint32_t pad_o = GL ? col_pad(32 * ks + 16 * h, DR, do_bytes) : 0u;
+      qf[ks] = buf_load16(qres, (uint32_t)qrow * rsq + 16 * h + 32 * ks + pad_q);
+      of[ks] = buf_load16(ores, (uint32_t)qrow * rsdo + 16 * h + 32 * ks + pad_o);
     }
   }
   // rows past the end: P = exp2(-inf) = 0, so dS = 0 there
-  const float lq = qrow < Nb ? LSE[hr.vec + qrow] * kLog2e : INFINITY;
-  const float dd = qrow < Nb ? Dvec[hr.vec + qrow] : 0.0f;
+  const float lq = qrow < Lq ? LSE[l_off + qrow] * kLog2e : INFINITY;
+  const float dd = qrow < Lq ? Dvec[l_off + qrow] : 0.0f;
   f32x16_t negd;  // initial value of the dP accumulators
 #pragma unroll
   for (int i = 0; i < 16; ++i) negd[i] = -dd;
@@ -501,21 +577,39 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const int L16 = lane & 15, G = lane >> 4;
   const uint32_t tbase = (uint32_t)((h + 4 * (L16 >> 2)) * RBL + (16 * (G & 1) + 4 * (L16 & 3)) * 2);
 
-  const int kv_end = CAUSAL ? min(Nb, q0 + BR) : Nb;
+  // keys visible to the workgroup's last row; none (every row of the tile
+  // sees no key: an empty key sequence, or rows before the bottom-right
+  // diagonal starts): dQ = 0
+  const int kv_end = CAUSAL ? min(Lk, q0 + BR + delta) : Lk;
+  const int nch = GL ? DR / 8 : D / 8;
+  if (GL && kv_end <= 0) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int i = lane; i < 32 * (D / 8); i += 64) {
+      const int r = i / (D / 8), ch = i % (D / 8);
+      if (r < Lq - qw && ch < nch) *(u32x4_t*)(dQ + dq_off + (size_t)(qw + r) * dqs + 8 * ch) = z;
+    }
+    return;
+  }
   const int n_st = (kv_end + BC - 1) / BC;
 
   // ---- staging: chunk i of this thread is row tid / CPR + ROWSTEP i, column
   // chunk tid % CPR, of both K and V (part j < NCH: K chunk j, else V chunk j - NCH)
-  const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
-  const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
-  const uint32_t g_off = (uint32_t)(tid / CPR) * rs + (tid % CPR) * 16;
+  const rsrc_t kres = make_rsrc(K + k_off, k_bytes);
+  const rsrc_t vres = make_rsrc(V + v_off, v_bytes);
+  const uint32_t g_col = (tid % CPR) * 16;
+  const uint32_t gk_off = (uint32_t)(tid / CPR) * rsk + g_col + (GL ? col_pad(g_col, DR, k_bytes) : 0u);
+  const uint32_t gv_off = (uint32_t)(tid / CPR) * rsv + g_col + (GL ? col_pad(g_col, DR, v_bytes) : 0u);
   const uint32_t s_off = (uint32_t)(tid / CPR) * RBL + (tid % CPR) * 16;
   // (set 1 of the staging registers: prologue only, two stages in flight)
   u32x4_t sk[2][NCH], sv[2][NCH];
   auto load_part = [&](int j0, int j, int t = 0) __attribute__((always_inline)) {
-    const uint32_t base = g_off + (uint32_t)j0 * rs;
-    if (j < NCH) sk[t][j] = buf_load16(kres, base + ROWSTEP * j * rs);
-    else sv[t][j - NCH] = buf_load16(vres, base + ROWSTEP * (j - NCH) * rs);
+    if (j < NCH) {
+      const uint32_t r = GL ? __builtin_amdgcn_readfirstlane(rsk) : RB;
+      sk[t][j] = buf_load16(kres, gk_off + (uint32_t)(j0 + ROWSTEP * j) * r);
+    } else {
+      const uint32_t r = GL ? __builtin_amdgcn_readfirstlane(rsv) : RB;
+      sv[t][j - NCH] = buf_load16(vres, gv_off + (uint32_t)(j0 + ROWSTEP * (j - NCH)) * r);
+    }
   };
   auto store_part = [&](uint32_t sb, int j, int t = 0) __attribute__((always_inline)) {
     if (j < NCH) *(u32x4_t*)(smem + sb + s_off + ROWSTEP * j * RBL) = sk[t][j];
@@ -562,7 +656,7 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     asm volatile("" : "+v"(dsk[NB][0]), "+v"(dsk[NB][1]));
 
     // causal: key j0 + koff(r) is visible to this lane's row iff koff(r) <= thr
-    const int thr = qrow - j0 - h;
+    const int thr = qrow + delta - j0 - h;
     float pe[16], dsv[16];
     auto vwork = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
@@ -640,9 +734,10 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
   for (int x = 0; x < AH; ++x) fr[x] = frag(x, 0u, 3u * STG, 1);
 
-  // ---- pairs of iterations over the stages.  Causal: the blocks of the last
-  // two stages (each wavefront's diagonal block and the fully masked blocks
-  // past it) are masked.
+  // ---- pairs of iterations over the stages.  Causal: the stages with a key
+  // that some row of the workgroup does not see are masked (with the square
+  // mask: the last two, each wavefront's diagonal block and the fully masked
+  // blocks past it).
   auto pair = [&](auto masked_c, int s) __attribute__((always_inline)) {
     const uint32_t b0 = (uint32_t)(s & 3) * STG;
     const uint32_t bp1 = (uint32_t)((s + 1) & 3) * STG;
@@ -653,7 +748,7 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     iteration(std::integral_constant<int, 1>{}, masked_c, bp1, b0, bp1, b0, j0 + 32, 0, bp2);
     lds_barrier();
   };
-  const int n_open = CAUSAL ? max(0, n_st - 2) : n_st;
+  const int n_open = CAUSAL ? min(max(q0 + delta + 1, 0) / BC, n_st) : n_st;
   int s = 0;
   for (; s < n_open; ++s) pair(std::false_type{}, s);
   for (; s < n_st; ++s) pair(std::true_type{}, s);
@@ -678,32 +773,28 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   // dQ stored as whole rows through LDS: after the last barrier every stage
   // slot but that of the last block is free
   static_assert(4 * kTileRowsBytes<D> <= STG, "four wavefronts' rows fit one stage slot");
-  const size_t ostride = VL ? (size_t)H * D : (size_t)D;
   store_tile_rows<D>(smem + ((n_st + 1) & 3) * STG + w * kTileRowsBytes<D>, od,
-                     dQ + head_off + (size_t)qw * ostride, min(32, Nb - qw), lane, ostride);
+                     dQ + dq_off + (size_t)qw * dqs, min(32, Lq - qw), lane, dqs, nch);
 }
 
 // ------------------------------------------------------------------ launch
 
-
 template <class TR, int D>
 static hipError_t prep_t(const BwdArgs& a) {
   constexpr int RPB = 256 / (D / 8);
-  if (a.cu) {  // packed: total H rows, D_i stored [H, total]
-    const int rows = a.total * a.H;
+  const int rows = a.BH * a.Nq;
+  if (a.general)
     hipLaunchKernelGGL((bwd_pre_kernel<TR, D, true>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dvec, rows, a.H, a.total);
-  } else {
-    const int rows = a.BH * a.N;
+                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dvec, rows, a.Nq, a.g);
+  else
     hipLaunchKernelGGL((bwd_pre_kernel<TR, D, false>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dvec, rows, 1, 0);
-  }
+                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dvec, rows, a.Nq, a.g);
   return hipGetLastError();
 }
 
-template <class TR, int D, bool CAUSAL, bool VL>
+template <class TR, int D, bool CAUSAL, bool GL>
 static void dkdv_launch(const BwdArgs& a) {
-  const int n_ktiles = (a.N + 127) / 128;
+  const int n_ktiles = (a.Nk + 127) / 128;
   const uint32_t total = (uint32_t)(n_ktiles * a.BH);
   // The kernel forms the exponent as (q.k - LSE / s) * s log2 e with s the
   // scale.  Below 2^-100 (scale 0 included) it takes s = 2^-100 there, so that
@@ -711,50 +802,49 @@ static void dkdv_launch(const BwdArgs& a) {
   // exponent is -LSE log2 e, its value at scale 0 (dK is still multiplied by
   // the true scale).
   const float s = a.scale >= 0x1p-100f ? a.scale : 0x1p-100f;
-  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, VL>), dim3(total), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, GL>), dim3(total), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     a.N, n_ktiles, total, s * kLog2e, -1.0f / s, a.scale, a.cu, a.H, a.total);
+                     a.Nq, a.Nk, n_ktiles, total, s * kLog2e, -1.0f / s, a.scale, a.g);
 }
 
 template <class TR, int D, bool CAUSAL>
 static hipError_t dkdv_t(const BwdArgs& a) {
-  if constexpr (CAUSAL) {
-    if (a.cu) dkdv_launch<TR, D, true, true>(a);
-    else dkdv_launch<TR, D, true, false>(a);
-  } else {
-    if (a.cu) return hipErrorInvalidValue;  // packed batches are causal only
-    dkdv_launch<TR, D, false, false>(a);
-  }
+  if (a.general) dkdv_launch<TR, D, CAUSAL, true>(a);
+  else dkdv_launch<TR, D, CAUSAL, false>(a);
   return hipGetLastError();
 }
 
 // dQ: the pipelined kernel, one wavefront per SIMD at d = 128 and two at d = 64
-template <class TR, int D, bool CAUSAL, bool VL>
+template <class TR, int D, bool CAUSAL, bool GL>
 static void dq_launch(const BwdArgs& a) {
-  const int n_qtiles = (a.N + 127) / 128;
+  const int n_qtiles = (a.Nq + 127) / 128;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, VL>), dim3(total), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, GL>), dim3(total), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.N, n_qtiles, total,
-                     a.c, a.scale, a.cu, a.H, a.total);
+                     (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.Nq, a.Nk, n_qtiles, total,
+                     a.c, a.scale, a.g);
 }
 
 template <class TR, int D, bool CAUSAL>
 static hipError_t dq_t(const BwdArgs& a) {
-  if constexpr (CAUSAL) {
-    if (a.cu) dq_launch<TR, D, true, true>(a);
-    else dq_launch<TR, D, true, false>(a);
-  } else {
-    if (a.cu) return hipErrorInvalidValue;
-    dq_launch<TR, D, false, false>(a);
-  }
+  if (a.general) dq_launch<TR, D, CAUSAL, true>(a);
+  else dq_launch<TR, D, CAUSAL, false>(a);
   return hipGetLastError();
 }
 
+// the kernels' width: d = 128 and 96 (general layout, zero columns) on the
+// d = 128 kernels, d = 64 and 32 on the d = 64 kernels
 template <class TR>
 static hipError_t stage_t(const BwdArgs& a, int stage) {
-  const bool d128 = a.d == 128;
+  if (a.d == 256) {  // the wide kernels (fa_bwd_wide.hip), always in the general layout
+    if (stage != BWD_PREP) return launch_bwd_wide_stage(a, stage);
+    const int rows = a.BH * a.Nq;
+    hipLaunchKernelGGL((bwd_pre_kernel<TR, 256, true>), dim3((rows + 7) / 8), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dvec, rows, a.Nq, a.g);
+    return hipGetLastError();
+  }
+  const bool d128 = a.d > 64;
   switch (stage) {
     case BWD_PREP: return d128 ? prep_t<TR, 128>(a) : prep_t<TR, 64>(a);
     case BWD_DKDV:

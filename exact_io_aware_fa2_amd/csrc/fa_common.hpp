@@ -336,11 +336,12 @@ __device__ inline bool wave_uniform(bool x) { return __builtin_amdgcn_readfirstl
 // that each store instruction writes whole rows (16 bytes per lane,
 // 64 / (D / 8) rows per instruction) instead of 8-byte pieces of 32 rows.
 // lds: this wavefront's scratch, 32 rows of 2 D bytes, 16-byte chunk c of
-// row r at chunk position c ^ (r % (D / 8)); rows at and past nrows are not
-// stored; row r goes to dst + r * row_stride (elements).
+// row r at chunk position c ^ (r % (D / 8)); rows at and past nrows, and
+// 16-byte chunks at and past nch, are not stored; row r goes to dst + r *
+// row_stride (elements).
 template <int D>
 __device__ inline void store_tile_rows(char* lds, const u32x2_t (&v)[D / 32][4], uint16_t* dst, int nrows,
-                                       int lane, size_t row_stride = D) {
+                                       int lane, size_t row_stride = D, int nch = D / 8) {
   constexpr int RS = 2 * D;
   constexpr int CPR = D / 8;     // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;  // rows per store instruction
@@ -358,9 +359,70 @@ __device__ inline void store_tile_rows(char* lds, const u32x2_t (&v)[D / 32][4],
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = RPI * i + lane / CPR, ch = lane % CPR;
     const u32x4_t x = *(const u32x4_t*)(lds + r * RS + (ch ^ (r % CPR)) * 16);
-    if (r < nrows) *(u32x4_t*)(dst + (size_t)r * row_stride + 8 * ch) = x;
+    if (r < nrows && ch < nch) *(u32x4_t*)(dst + (size_t)r * row_stride + 8 * ch) = x;
   }
 }
+// ---- general layouts: any element strides per tensor (batch, head, row;
+// the head dimension contiguous), packed variable-length batches, and head
+// dimensions below the kernel's D.
+//
+// Tensor t's row r of sequence b, head h starts at element
+//   b * t.sb + h * t.sh + (start(b) + r) * t.sr,
+// start(b) = cu[b] for a packed batch (whose tensors have sb = 0), else 0.
+// LSE and D_i entry (b, h, r) is at b * l_sb + h * l_sh + start_q(b) + r.
+// Columns at and past dr (a head dimension below the kernel's D) read as
+// zeros and are not stored, so the kernel's products over D columns are the
+// products over dr.
+struct Strides {
+  int64_t sb, sh, sr;
+};
+struct GenLayout {
+  Strides q, k, v, o, dout, dq, dk, dv;
+  const int32_t* cu_q;  // [B + 1] query-side prefix sums, or NULL
+  const int32_t* cu_k;  // [B + 1] key-side prefix sums, or NULL
+  int64_t total_q, total_k;  // rows of the packed tensors (prefix sums clamped into [0, total])
+  int64_t l_sb, l_sh;
+  int H;
+  int dr;
+};
+
+// First row and row count of sequence b's queries (or keys): prefix sums
+// clamped into [0, total] and the count to [0, nmax]; without prefix sums
+// rows 0 .. nmax - 1.
+__device__ inline void seq_rows(const int32_t* __restrict__ cu, int64_t total, int b, int nmax, int& start,
+                                int& count) {
+  if (cu) {
+    const int64_t s0 = min(max((int64_t)cu[b], (int64_t)0), total);
+    start = (int)s0;
+    count = (int)min(max((int64_t)cu[b + 1] - s0, (int64_t)0), min((int64_t)nmax, total - s0));
+  } else {
+    start = 0;
+    count = nmax;
+  }
+}
+
+// One tensor's rows of one (sequence, head): element offset of row 0, row
+// stride in bytes (16-bit elements), and the buffer range in bytes, which
+// ends right after the last real row's dr columns (rows from `count` on read
+// zeros).
+struct TRows {
+  size_t off;
+  uint32_t rs;
+  uint32_t bytes;
+};
+__device__ inline TRows tensor_rows(const Strides& t, int b, int h, int start, int count, int dr) {
+  TRows r;
+  r.off = (size_t)((int64_t)b * t.sb + (int64_t)h * t.sh + (int64_t)start * t.sr);
+  r.rs = (uint32_t)(t.sr * 2);
+  r.bytes = count > 0 ? (uint32_t)(count - 1) * r.rs + 2u * (uint32_t)dr : 0u;
+  return r;
+}
+
+// Offset added to a load whose 16-bit columns start at byte `cb` of a row:
+// past the data's dr columns it moves the load past the buffer range, so it
+// reads zeros (bytes < 2^31 and row offsets < 2^31 keep the sum in 32 bits).
+__device__ inline uint32_t col_pad(uint32_t cb, int dr, uint32_t bytes) { return cb >= 2u * (uint32_t)dr ? bytes : 0u; }
+
 // Where the rows of head bh lie.  Dense [BH, N, D]: rows of D elements from
 // bh N D, vectors (LSE, D_i) from bh N, all N rows real.  Packed (VL): head
 // h of sequence b = bh / H owns rows cu[b] .. cu[b + 1] - 1 of [total, H, D]

@@ -81,12 +81,11 @@ constexpr float kSumMax = 32768.0f;
 //      on consecutive columns) both hit distinct banks.
 //
 // All matrix operands and accumulators live in VGPRs (the MfmaAsm forms).
-template <class TR, int D, int BC, int QB, bool CAUSAL, bool VL>
+template <class TR, int D, int BC, int QB, bool CAUSAL, bool GL>
 __global__ __launch_bounds__(512 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB, 3 - QB)))
 void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                  float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c,
-                  const int32_t* __restrict__ cu, int H, int n_rows) {
+                  float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c, GenLayout g) {
   // QB: 32-row query blocks per wavefront (2: one wavefront per SIMD, 1: two)
   constexpr int NT = 512 / QB;          // threads per workgroup
   constexpr int NW = NT / 64;           // wavefronts per workgroup
@@ -127,18 +126,43 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   int qt = lid % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest tiles first
   const int q0 = qt * BR;
-  // VL: a packed self-attention batch; head bh's Nb rows (its sequence) at
-  // row stride rs, and tiles wholly past them skipped
-  const HeadRows hr = head_rows<D, VL>(bh, N, cu, H, n_rows);
-  const int Nb = hr.Nb;
-  if (VL && q0 >= Nb) return;
-  const size_t head_off = hr.off;
-  const uint32_t head_bytes = hr.bytes;
-  const uint32_t rs = VL ? hr.rs : RB;
-  // the row stride as the staging loads use it: re-read per use in the packed
-  // variant, so that the per-row offsets are not kept live across the loop
-  auto row_stride = [&]() __attribute__((always_inline)) -> uint32_t {
-    if constexpr (VL) return __builtin_amdgcn_readfirstlane(rs);
+  // Addressing: dense [BH, N, D], or (GL) the general layout: per-tensor
+  // strides, a packed self-attention batch (head bh's Nb rows, its sequence;
+  // tiles wholly past them skipped), and data with DR < D columns (columns
+  // past DR read zeros and are not stored).
+  int Nb = N, DR = D;
+  size_t q_off, k_off, v_off, o_off, l_off, os;
+  uint32_t q_bytes, k_bytes, v_bytes, rsq, rsk, rsv;
+  if constexpr (GL) {
+    const int b = bh / g.H, hd = bh - b * g.H;
+    int sq, sk, nq, nk;
+    seq_rows(g.cu_q, g.total_q, b, N, sq, nq);
+    seq_rows(g.cu_k, g.total_k, b, N, sk, nk);
+    Nb = min(nq, nk);  // self-attention: equal counts (malformed sums: the smaller)
+    DR = g.dr;
+    const TRows tq = tensor_rows(g.q, b, hd, sq, Nb, DR), tk = tensor_rows(g.k, b, hd, sk, Nb, DR);
+    const TRows tv = tensor_rows(g.v, b, hd, sk, Nb, DR), to = tensor_rows(g.o, b, hd, sq, Nb, DR);
+    q_off = tq.off, k_off = tk.off, v_off = tv.off, o_off = to.off;
+    q_bytes = tq.bytes, k_bytes = tk.bytes, v_bytes = tv.bytes;
+    rsq = tq.rs, rsk = tk.rs, rsv = tv.rs;
+    os = (size_t)g.o.sr;
+    l_off = (size_t)((int64_t)b * g.l_sb + (int64_t)hd * g.l_sh + sq);
+  } else {
+    q_off = k_off = v_off = o_off = (size_t)bh * N * D;
+    q_bytes = k_bytes = v_bytes = (uint32_t)N * RB;
+    rsq = rsk = rsv = RB;
+    os = D;
+    l_off = (size_t)bh * N;
+  }
+  if (GL && q0 >= Nb) return;
+  // the row strides as the staging loads use them: re-read per use in the
+  // general layout, so that the per-row offsets are not kept live across the loop
+  auto row_stride_k = [&]() __attribute__((always_inline)) -> uint32_t {
+    if constexpr (GL) return __builtin_amdgcn_readfirstlane(rsk);
+    return RB;
+  };
+  auto row_stride_v = [&]() __attribute__((always_inline)) -> uint32_t {
+    if constexpr (GL) return __builtin_amdgcn_readfirstlane(rsv);
     return RB;
   };
   const int qw = q0 + 32 * QB * w;  // first query row of this wavefront
@@ -147,12 +171,13 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   // read zeros; their results are never stored).
   u32x4_t qf[QB][NKS];
   {
-    const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
+    const rsrc_t qres = make_rsrc(Q + q_off, q_bytes);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
-        qf[qb][ks] = buf_load16(qres, (uint32_t)(qw + 32 * qb + l32) * rs + 32 * ks + 16 * h);
+        qf[qb][ks] = buf_load16(qres, (uint32_t)(qw + 32 * qb + l32) * rsq + 32 * ks + 16 * h +
+                                          (GL ? col_pad(32 * ks + 16 * h, DR, q_bytes) : 0u));
   }
 
   const int kv_end = CAUSAL ? min(Nb, q0 + BR) : Nb;
@@ -160,30 +185,32 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
 
   // ---- staging.  Rows past the end of the sequence read zeros (their scores
   // are masked, their values multiplied by zero probabilities).
-  const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
-  const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
+  const rsrc_t kres = make_rsrc(K + k_off, k_bytes);
+  const rsrc_t vres = make_rsrc(V + v_off, v_bytes);
   u32x4_t stk[NKC];
   uint32_t stv[8][CW / 2];
   // K: chunk tid + NT r -> row (tid / KCH) + (NT / KCH) r, 16-byte column tid % KCH
-  const uint32_t koff = (uint32_t)(tid / KCH) * rs + (tid % KCH) * 16;
+  const uint32_t koff = (uint32_t)(tid / KCH) * rsk + (tid % KCH) * 16 +
+                        (GL ? col_pad((tid % KCH) * 16, DR, k_bytes) : 0u);
   const int kst = (tid / KCH) * KS + (tid % KCH) * 8;
   // V: unit tid -> (16-key step vs, half vh, column group vc); 8 rows x CW columns
   const int vc = tid % NCG;
   const int vh = (tid / NCG) & 1;
   const int vs = tid / (2 * NCG);
-  const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * rs + vc * CW * 2;
+  const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * rsv + vc * CW * 2 +
+                        (GL ? col_pad(vc * CW * 2, DR, v_bytes) : 0u);
   const int vrow = (2 * vs + vh) * D * 8;
   const int vsw = (CW * vc) ^ ((CW * vc >> 3) & 3);  // swizzled slot of column CW vc (+ cc: xor)
 
   auto load_k = [&](int tile) {
 #pragma unroll
     for (int r = 0; r < NKC; ++r)
-      stk[r] = buf_load16(kres, koff + (uint32_t)(tile * BC + (NT / KCH) * r) * row_stride());
+      stk[r] = buf_load16(kres, koff + (uint32_t)(tile * BC + (NT / KCH) * r) * row_stride_k());
   };
   auto load_v = [&](int tile) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t off = voff + (uint32_t)(tile * BC + 8 * (k / 4) + (k % 4)) * row_stride();
+      const uint32_t off = voff + (uint32_t)(tile * BC + 8 * (k / 4) + (k % 4)) * row_stride_v();
       if constexpr (CW == 4) {
         const u32x2_t x = buf_load8(vres, off);
         stv[k][0] = x[0];
@@ -486,10 +513,11 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
       const int kend = CAUSAL ? min(Nb, qw + 32 * qb + 32) : Nb;
       float mx = -INFINITY;
       for (int k0 = 0; k0 < kend; k0 += 32) {
-        const uint32_t ko = (uint32_t)(k0 + l32) * rs + 16 * h;
-        f32x16_t sc = TR::mma0(buf_load16(kres, ko), qf[qb][0]);
+        const uint32_t ko = (uint32_t)(k0 + l32) * rsk + 16 * h;
+        auto kpad = [&](int ks) -> uint32_t { return GL ? col_pad(32 * ks + 16 * h, DR, k_bytes) : 0u; };
+        f32x16_t sc = TR::mma0(buf_load16(kres, ko + kpad(0)), qf[qb][0]);
 #pragma unroll
-        for (int ks = 1; ks < NKS; ++ks) TR::mma(sc, buf_load16(kres, ko + 32 * ks), qf[qb][ks]);
+        for (int ks = 1; ks < NKS; ++ks) TR::mma(sc, buf_load16(kres, ko + 32 * ks + kpad(ks)), qf[qb][ks]);
         f32x16_t sc2 = sc;
         mfma_wait_v(sc, sc2);
 #pragma unroll
@@ -538,11 +566,10 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
     static_assert(QB == 1 && (NW / 2) * kTileRowsBytes<D> <= (int)sizeof(sK) &&
                       (NW / 2) * kTileRowsBytes<D> <= (int)sizeof(sV), "rows fit the tile buffers");
     if (qb == 0) lds_barrier();
-    const size_t ostride = VL ? (size_t)H * D : (size_t)D;
     store_tile_rows<D>((w < NW / 2 ? (char*)sK : (char*)sV) + (w % (NW / 2)) * kTileRowsBytes<D>, ov,
-                       O + head_off + (size_t)(qw + 32 * qb) * ostride, min(32, Nb - (qw + 32 * qb)), lane,
-                       ostride);
-    if (qrow < Nb && h == 0) LSE[hr.vec + qrow] = (m_run[qb] + __log2f(l)) * kLn2;
+                       O + o_off + (size_t)(qw + 32 * qb) * os, min(32, Nb - (qw + 32 * qb)), lane, os,
+                       GL ? DR / 8 : D / 8);
+    if (qrow < Nb && h == 0) LSE[l_off + qrow] = (m_run[qb] + __log2f(l)) * kLn2;
   }
 }
 
@@ -570,12 +597,11 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
 //      values lane (c % 32, h) needs for one O^T += V^T P^T instruction.
 //      Column c sits at slot c ^ ((c >> 3) & 3) of its row (bank-conflict-
 //      free staging writes and fragment reads).
-template <class TR, int D, int BC, bool CAUSAL, bool VL>
+template <class TR, int D, int BC, bool CAUSAL, bool GL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                  float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c,
-                  const int32_t* __restrict__ cu, int H, int n_rows) {
+                  float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c, GenLayout g) {
   constexpr int NW = 8;                     // wavefronts per workgroup
   constexpr int BR = 32 * NW;               // query rows per workgroup
   constexpr int KCH = D / 8;                // 16-byte chunks per row
@@ -606,14 +632,34 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest tiles first
   const int q0 = qt * BR;
   constexpr uint32_t RB = D * 2;   // bytes per row
-  // VL: a packed self-attention batch; head bh's Nb rows (its sequence) at
-  // row stride rs, and tiles wholly past them skipped
-  const HeadRows hr = head_rows<D, VL>(bh, N, cu, H, n_rows);
-  const int Nb = hr.Nb;
-  if (VL && q0 >= Nb) return;
-  const size_t head_off = hr.off;
-  const uint32_t head_bytes = hr.bytes;
-  const uint32_t rs = VL ? hr.rs : RB;
+  // Addressing: dense [BH, N, D], or (GL) the general layout (per-tensor
+  // strides, a packed self-attention batch with tiles wholly past the
+  // sequence skipped, DR < D data columns), as in fwd16_pipe_kernel.
+  int Nb = N, DR = D;
+  size_t q_off, k_off, v_off, o_off, l_off, os;
+  uint32_t q_bytes, k_bytes, v_bytes, rsq, rsk, rsv;
+  if constexpr (GL) {
+    const int b = bh / g.H, hd = bh - b * g.H;
+    int sq, sk, nq, nk;
+    seq_rows(g.cu_q, g.total_q, b, N, sq, nq);
+    seq_rows(g.cu_k, g.total_k, b, N, sk, nk);
+    Nb = min(nq, nk);
+    DR = g.dr;
+    const TRows tq = tensor_rows(g.q, b, hd, sq, Nb, DR), tk = tensor_rows(g.k, b, hd, sk, Nb, DR);
+    const TRows tv = tensor_rows(g.v, b, hd, sk, Nb, DR), to = tensor_rows(g.o, b, hd, sq, Nb, DR);
+    q_off = tq.off, k_off = tk.off, v_off = tv.off, o_off = to.off;
+    q_bytes = tq.bytes, k_bytes = tk.bytes, v_bytes = tv.bytes;
+    rsq = tq.rs, rsk = tk.rs, rsv = tv.rs;
+    os = (size_t)g.o.sr;
+    l_off = (size_t)((int64_t)b * g.l_sb + (int64_t)hd * g.l_sh + sq);
+  } else {
+    q_off = k_off = v_off = o_off = (size_t)bh * N * D;
+    q_bytes = k_bytes = v_bytes = (uint32_t)N * RB;
+    rsq = rsk = rsv = RB;
+    os = D;
+    l_off = (size_t)bh * N;
+  }
+  if (GL && q0 >= Nb) return;
   const int qw = q0 + 32 * w;      // first query row of this wavefront
   const int qrow = qw + l32;
 
@@ -621,10 +667,11 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // read zeros; their results are never stored).
   u32x4_t qf[NKS];
   {
-    const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
-    const uint32_t qoff = (uint32_t)qrow * rs + 16 * h;
+    const rsrc_t qres = make_rsrc(Q + q_off, q_bytes);
+    const uint32_t qoff = (uint32_t)qrow * rsq + 16 * h;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(qres, qoff + 32 * ks);
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[ks] = buf_load16(qres, qoff + 32 * ks + (GL ? col_pad(32 * ks + 16 * h, DR, q_bytes) : 0u));
   }
 
   f32x16_t acc_o[NDB];
@@ -643,28 +690,29 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // the sequence read zeros (their scores are masked to -inf, so they add 0).
   // One resource per tensor: each is uniform across the wave (SGPRs); a
   // resource selected by the (per-lane) group index would not be.
-  const rsrc_t kres = make_rsrc(K + head_off, head_bytes);
-  const rsrc_t vres = make_rsrc(V + head_off, head_bytes);
+  const rsrc_t kres = make_rsrc(K + k_off, k_bytes);
+  const rsrc_t vres = make_rsrc(V + v_off, v_bytes);
   u32x4_t stg[4];
   // K role: chunk ci = st + 256 r -> row ci / KCH, 16-byte column ci % KCH
-  const uint32_t koff = (uint32_t)(st / KCH) * rs + (st % KCH) * 16;
+  const uint32_t koff = (uint32_t)(st / KCH) * rsk + (st % KCH) * 16 +
+                        (GL ? col_pad((st % KCH) * 16, DR, k_bytes) : 0u);
   const int kst = (st / KCH) * KS + (st % KCH) * 8;
   // V role: unit st -> (16-key step vs, half vh, 4-column chunk vc); 8 rows x 8 bytes
   const int vc = st % (D / 4);
   const int vh = (st / (D / 4)) & 1;
   const int vs = st / (D / 2);
-  const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * rs + vc * 8;
+  const uint32_t voff = (uint32_t)(16 * vs + 4 * vh) * rsv + vc * 8 + (GL ? col_pad(vc * 8, DR, v_bytes) : 0u);
   const int vst = ((2 * vs + vh) * D + 4 * vc) * 8;
   const int vsw = (vc >> 1) & 3;  // slot swizzle of this thread's four columns
 
   auto load_tile = [&](int j0) {
     if (grp == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) stg[r] = buf_load16(kres, koff + (uint32_t)(j0 + (256 / KCH) * r) * rs);
+      for (int r = 0; r < 4; ++r) stg[r] = buf_load16(kres, koff + (uint32_t)(j0 + (256 / KCH) * r) * rsk);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const u32x2_t x = buf_load8(vres, voff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * rs);
+        const u32x2_t x = buf_load8(vres, voff + (uint32_t)(j0 + 8 * (k / 4) + (k % 4)) * rsv);
         stg[k / 2][2 * (k % 2) + 0] = x[0];
         stg[k / 2][2 * (k % 2) + 1] = x[1];
       }
@@ -879,10 +927,9 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                           TR::pack2(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
   // O stored as whole rows through LDS (the K buffers; the loop ended with a barrier)
   static_assert(8 * kTileRowsBytes<D> <= (int)sizeof(sK), "rows of all wavefronts fit the K buffers");
-  const size_t ostride = VL ? (size_t)H * D : (size_t)D;
-  store_tile_rows<D>((char*)sK + w * kTileRowsBytes<D>, ov, O + head_off + (size_t)qw * ostride, min(32, Nb - qw),
-                     lane, ostride);
-  if (qrow < Nb && h == 0) LSE[hr.vec + qrow] = (m_run + __log2f(l)) * kLn2;
+  store_tile_rows<D>((char*)sK + w * kTileRowsBytes<D>, ov, O + o_off + (size_t)qw * os, min(32, Nb - qw), lane, os,
+                     GL ? DR / 8 : D / 8);
+  if (qrow < Nb && h == 0) LSE[l_off + qrow] = (m_run + __log2f(l)) * kLn2;
 }
 
 // fp32 inputs: same scheme with v_mfma_f32_32x32x2_f32 and unrounded fp32
@@ -1015,37 +1062,37 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float* __restrict__ Q,
 
 // ------------------------------------------------------------------ launch
 
-template <class TR, bool CAUSAL, bool VL>
-static void launch_pipe_vl(const FwdArgs& a) {  // d = 128
+template <class TR, bool CAUSAL, bool GL>
+static void launch_pipe_gl(const FwdArgs& a) {  // d = 128 (and d = 96 in the general layout)
   constexpr int BR = 256;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((fwd16_pipe_kernel<TR, 128, 64, 1, CAUSAL, VL>), dim3(total), dim3(512), 0, a.stream,
+  hipLaunchKernelGGL((fwd16_pipe_kernel<TR, 128, 64, 1, CAUSAL, GL>), dim3(total), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c, a.cu, a.H, a.total);
+                     (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c, a.g);
 }
 
-template <class TR, bool CAUSAL, bool VL>
-static void launch_pp_vl(const FwdArgs& a) {  // d = 64
+template <class TR, bool CAUSAL, bool GL>
+static void launch_pp_gl(const FwdArgs& a) {  // d = 64 (and d = 32 in the general layout)
   constexpr int BR = 256;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((fwd16_pp_kernel<TR, 64, 128, CAUSAL, VL>), dim3(total), dim3(512), 0, a.stream,
+  hipLaunchKernelGGL((fwd16_pp_kernel<TR, 64, 128, CAUSAL, GL>), dim3(total), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c, a.cu, a.H, a.total);
+                     (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c, a.g);
 }
 
 template <class TR, bool CAUSAL>
 static hipError_t launch_pipe(const FwdArgs& a) {
-  if (a.cu) launch_pipe_vl<TR, CAUSAL, true>(a);
-  else launch_pipe_vl<TR, CAUSAL, false>(a);
+  if (a.general) launch_pipe_gl<TR, CAUSAL, true>(a);
+  else launch_pipe_gl<TR, CAUSAL, false>(a);
   return hipGetLastError();
 }
 
 template <class TR, bool CAUSAL>
 static hipError_t launch_pp(const FwdArgs& a) {
-  if (a.cu) launch_pp_vl<TR, CAUSAL, true>(a);
-  else launch_pp_vl<TR, CAUSAL, false>(a);
+  if (a.general) launch_pp_gl<TR, CAUSAL, true>(a);
+  else launch_pp_gl<TR, CAUSAL, false>(a);
   return hipGetLastError();
 }
 
@@ -1061,12 +1108,14 @@ static hipError_t launch32(const FwdArgs& a) {
 
 template <class TR>
 static hipError_t dispatch16(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_pipe<TR, true>(a) : launch_pipe<TR, false>(a);
+  // the kernel's width: d = 128 and 96 (general layout, zero columns) on the
+  // d = 128 kernel, d = 64 and 32 on the d = 64 kernel
+  if (a.d > 64) return a.causal ? launch_pipe<TR, true>(a) : launch_pipe<TR, false>(a);
   return a.causal ? launch_pp<TR, true>(a) : launch_pp<TR, false>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.cu && a.dtype != DT_BF16 && a.dtype != DT_F16) return hipErrorInvalidValue;  // packed: 16-bit only
+  if (a.general && a.dtype != DT_BF16 && a.dtype != DT_F16) return hipErrorInvalidValue;  // 16-bit only
   switch (a.dtype) {
     case DT_BF16: return dispatch16<BF16>(a);
     case DT_F16: return dispatch16<F16>(a);

@@ -61,7 +61,7 @@ __device__ inline int kv_tile_key(int m) { return (m & ~12) | ((m & 4) << 1) | (
 // and writes a quarter of it, two LDS buffers, one workgroup barrier per
 // tile), instead of each wavefront staging its own copy.
 template <class TR, int D, bool CAUSAL, bool DIRECT, bool F8, bool GRP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kv_split_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2))) void kv_split_kernel(
     const uint16_t* __restrict__ Q, const void* __restrict__ K, const void* __restrict__ V,
     const int32_t* __restrict__ seqlens, uint16_t* __restrict__ O, float* __restrict__ LSE,
     float* __restrict__ part_o, float* __restrict__ part_l, KvLayout lay, int H, int BH, int Nq, int Nk,
@@ -139,6 +139,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const uint32_t rsq = (uint32_t)lay.q_sr * 2;             // bytes between query rows
   const uint32_t rsc = (uint32_t)lay.c_sr * (F8 ? 1 : 2);  // bytes between cache rows
   const size_t q_head = (size_t)(b * lay.q_sb + hd * lay.q_sh + qs * lay.q_sr);  // elements
+  const size_t o_head = (size_t)(b * lay.o_sb + hd * lay.o_sh + qs * lay.o_sr);  // elements
   u32x4_t qf[NKS];
   {
     const rsrc_t qres = make_rsrc(Q + q_head, Lq > 0 ? (uint32_t)(Lq - 1) * rsq + 2 * D : 0u);
@@ -148,9 +149,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
   // the cache of this head up to the filled length: rows at and past L read as zeros
   const size_t cache_head = (size_t)(b * lay.c_sb + hd * lay.c_sh + ks0 * lay.c_sr) * (F8 ? 1 : 2);  // bytes
+  const size_t v_head = (size_t)(b * lay.v_sb + hd * lay.v_sh + ks0 * lay.v_sr) * (F8 ? 1 : 2);     // bytes
+  const uint32_t rsv = (uint32_t)lay.v_sr * (F8 ? 1 : 2);  // bytes between value rows
   const uint32_t cache_bytes = L > 0 ? (uint32_t)(L - 1) * rsc + RBC : 0u;
+  const uint32_t v_bytes = L > 0 ? (uint32_t)(L - 1) * rsv + RBC : 0u;
   const rsrc_t kres = make_rsrc((const char*)K + cache_head, cache_bytes);
-  const rsrc_t vres = make_rsrc((const char*)V + cache_head, cache_bytes);
+  const rsrc_t vres = make_rsrc((const char*)V + v_head, v_bytes);
   const int k_row = kv_tile_key(l32) * RSK + 16 * h;  // A operand of K: row read from LDS
   // transposed-read address of this lane: group G = lane / 16 reads columns
   // 16 (G % 2) + 0..15 of rows 8 h + 0..3 (and + 4), lane 4 e + i of the group
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ch = CST * i + tid_s;
-      vv[i] = buf_load16(vres, (uint32_t)(k0 + ch / VCH) * rsc + 16 * (ch % VCH));
+      vv[i] = buf_load16(vres, (uint32_t)(k0 + ch / VCH) * rsv + 16 * (ch % VCH));
     }
   };
   // chunk x (16 bytes of a cache row) -> its row's LDS position: as is, or
@@ -337,11 +341,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                             TR::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
     if constexpr (GRP) {
       lds_barrier();  // every wavefront is done with the tiles; slice w of the buffers is its own
-      store_tile_rows<D>(smem + w * kTileRowsBytes<D>, ov, O + q_head + (size_t)q0 * lay.q_sr, min(32, Lq - q0),
-                         lane, (size_t)lay.q_sr);
+      store_tile_rows<D>(smem + w * kTileRowsBytes<D>, ov, O + o_head + (size_t)q0 * lay.o_sr, min(32, Lq - q0),
+                         lane, (size_t)lay.o_sr);
     } else {
       wave_sync();
-      store_tile_rows<D>(lds, ov, O + q_head + (size_t)q0 * lay.q_sr, min(32, Lq - q0), lane, (size_t)lay.q_sr);
+      store_tile_rows<D>(lds, ov, O + o_head + (size_t)q0 * lay.o_sr, min(32, Lq - q0), lane, (size_t)lay.o_sr);
     }
     if (h == 0 && qi < Lq)
       LSE[b * lay.l_sb + hd * lay.l_sh + qs + qi] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
@@ -442,8 +446,10 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__
     }
   }
   const float inv = empty ? 0.0f : 1.0f / ws;
-  uint16_t* orow = O + (size_t)(b * lay.q_sb + hd * lay.q_sh + (qs + qi) * lay.q_sr) + PER * lane;
-  if constexpr (PER == 2) {
+  uint16_t* orow = O + (size_t)(b * lay.o_sb + hd * lay.o_sh + (qs + qi) * lay.o_sr) + PER * lane;
+  if constexpr (PER == 4) {
+    *(u32x2_t*)orow = u32x2_t{TR::pack2(acc[0] * inv, acc[1] * inv), TR::pack2(acc[2] * inv, acc[3] * inv)};
+  } else if constexpr (PER == 2) {
     *(uint32_t*)orow = TR::pack2(acc[0] * inv, acc[1] * inv);
   } else if (PER * lane < D) {  // d = 32: lanes 32..63 hold no column
     *orow = (uint16_t)(TR::pack2(acc[0] * inv, 0.0f) & 0xFFFFu);
@@ -492,13 +498,17 @@ static hipError_t launch_kv(const KvArgs& a, const KvPlan& p) {
 
 template <class TR, bool F8>
 static hipError_t dispatch_kv(const KvArgs& a, const KvPlan& p) {
+  if constexpr (!F8) {
+    if (a.d == 256) return a.causal ? launch_kv<TR, 256, true, F8>(a, p) : launch_kv<TR, 256, false, F8>(a, p);
+  }
   if (a.d == 128) return a.causal ? launch_kv<TR, 128, true, F8>(a, p) : launch_kv<TR, 128, false, F8>(a, p);
   if (a.d == 64) return a.causal ? launch_kv<TR, 64, true, F8>(a, p) : launch_kv<TR, 64, false, F8>(a, p);
   return a.causal ? launch_kv<TR, 32, true, F8>(a, p) : launch_kv<TR, 32, false, F8>(a, p);
 }
 
 hipError_t launch_fwd_kvcache(const KvArgs& a) {
-  const KvPlan p = kv_plan(a.BH, a.Nq, a.Nk, a.d);
+  const KvPlan p = a.one_range ? kv_plan_one_range(a.Nq, a.Nk) : kv_plan(a.BH, a.Nq, a.Nk, a.d);
+  if (a.fp8_cache && a.d == 256) return hipErrorInvalidValue;
   if (a.fp8_cache) return a.dtype == DT_BF16 ? dispatch_kv<BF16, true>(a, p) : dispatch_kv<F16, true>(a, p);
   return a.dtype == DT_BF16 ? dispatch_kv<BF16, false>(a, p) : dispatch_kv<F16, false>(a, p);
 }

@@ -8,6 +8,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fa_common.hpp"
+
 namespace fa {
 
 enum Dt { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
@@ -27,13 +29,12 @@ struct FwdArgs {
   int causal;
   int dtype;
   hipStream_t stream;
-  // Packed variable-length self-attention batch (16-bit types only): q, k,
-  // v, o are [total, H, d], lse [H, total], and head h of sequence
-  // b = bh / H owns rows cu[b] .. cu[b + 1] - 1 (at most N of them;
-  // BH = B H).  NULL: the dense [BH, N, d] layout.
-  const int32_t* cu = nullptr;
-  int H = 1;
-  int total = 0;
+  // General layout (16-bit types only): per-tensor strides, packed
+  // self-attention batches (equal query and key counts per sequence, at most
+  // N each), head dimensions 32 and 96 (on the 64 / 128 kernels with zero
+  // columns); g.dr = d.  false: the dense [BH, N, d] layout.
+  bool general = false;
+  GenLayout g{};
 };
 
 struct BwdArgs {
@@ -46,37 +47,39 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dvec;  // workspace: D_i = dO_i . O_i, [B*H*N] fp32
+  float* dvec;  // workspace: D_i = dO_i . O_i, one float per query row, at the LSE entry's place
   int BH;
-  int N;
+  int Nq;       // queries per sequence (the largest, with prefix sums)
+  int Nk;       // keys per sequence (dense: Nk = Nq)
   int d;
   float scale;
   float c;      // scale * log2(e)
   int causal;
   int dtype;
   hipStream_t stream;
-  // Packed variable-length batch (causal only; fa_bwd_varlen): q, k, v, o,
-  // dout, dq, dk, dv are [total, H, d], lse and dvec [H, total], and head h
-  // of sequence b = bh / H owns rows cu[b] .. cu[b + 1] - 1 (at most N of
-  // them; BH = B H).  NULL: the dense [BH, N, d] layout.
-  const int32_t* cu = nullptr;
-  int H = 1;
-  int total = 0;
+  // General layout: per-tensor strides, packed sequences with their own
+  // query and key counts (causal aligned bottom right), head dimensions 32
+  // and 96 (zero columns on the 64 / 128 kernels); g.dr = d.  false: the
+  // dense [BH, N, d] layout.
+  bool general = false;
+  GenLayout g{};
 };
 
 enum BwdStage { BWD_PREP = 0, BWD_DKDV = 1, BWD_DQ = 2 };
 
-// Where the rows of sequence b, head h lie (element offsets): row r of q/o at
-// b q_sb + h q_sh + (start_q(b) + r) q_sr, row j of the cache (k/v) at
-// b c_sb + h c_sh + (start_k(b) + j) c_sr, and the LSE of query r at
-// b l_sb + h l_sh + start_q(b) + r.  Without prefix sums every sequence
+// Where the rows of sequence b, head h lie (element offsets): row r of q at
+// b q_sb + h q_sh + (start_q(b) + r) q_sr (o likewise with the o strides),
+// row j of the keys at b c_sb + h c_sh + (start_k(b) + j) c_sr (values with
+// the v strides), and the LSE of query r at b l_sb + h l_sh + start_q(b) + r.  Without prefix sums every sequence
 // starts at row 0 and has Nq queries and Nk (or seqlens[b]) cache rows; with
 // them, sequence b has rows cu[b] .. cu[b + 1] - 1 of a packed tensor of
 // total rows (the kernels clamp both into [0, total]).
 struct KvLayout {
   int64_t q_sb, q_sh, q_sr;
-  int64_t c_sb, c_sh, c_sr;
+  int64_t c_sb, c_sh, c_sr;  // keys
   int64_t l_sb, l_sh;
+  int64_t v_sb, v_sh, v_sr;  // values (the keys' strides unless set otherwise)
+  int64_t o_sb, o_sh, o_sr;  // output (the queries' strides unless set otherwise)
   const int32_t* cu_q;  // [B + 1] or NULL
   const int32_t* cu_k;  // [B + 1] or NULL
   int64_t total_q, total_k;
@@ -100,6 +103,7 @@ struct KvArgs {
   float c;                 // scale * log2(e) (times the K scale of an 8-bit cache)
   float v_scale;           // multiplies O: the V scale of an 8-bit cache, else 1
   int fp8_cache;           // k, v hold OCP E4M3 codes (1 byte per element)
+  int one_range = 0;       // one key range per head (no workspace): the kernel writes O and LSE itself
   int causal;
   int dtype;               // of q and o (FA_BF16 or FA_F16)
   hipStream_t stream;
@@ -121,11 +125,23 @@ struct KvPlan {
 inline KvPlan kv_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t d) {
   KvPlan p;
   p.n_qb = (int)((Nq + 31) / 32);
-  const int64_t max_waves = d == 128 ? 8192 : 16384;
+  const int64_t max_waves = d >= 256 ? 4096 : d == 128 ? 8192 : 16384;
   int64_t kps = 64;
   while (kps < Nk && BH * p.n_qb * ((Nk + kps - 1) / kps) > max_waves) kps *= 2;
   p.kps = (int)kps;
   p.n_splits = (int)((Nk + kps - 1) / kps);
+  return p;
+}
+
+// One range covering every key of a head (the square forward at d = 256,
+// which takes no workspace).
+inline KvPlan kv_plan_one_range(int64_t Nq, int64_t Nk) {
+  KvPlan p;
+  p.n_qb = (int)((Nq + 31) / 32);
+  int64_t kps = 64;
+  while (kps < Nk) kps *= 2;
+  p.kps = (int)kps;
+  p.n_splits = 1;
   return p;
 }
 
@@ -172,5 +188,6 @@ hipError_t launch_mfma_peak(int workgroups, int iters, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);                 // all three stages in order
 hipError_t launch_bwd_stage(const BwdArgs& a, int stage);  // one stage
+hipError_t launch_bwd_wide_stage(const BwdArgs& a, int stage);  // d = 256: dK/dV or dQ
 
 }  // namespace fa

@@ -24,8 +24,11 @@
  * otherwise: the key/value-cache and variable-length entry points take other
  * layouts and also d = 32, the probe computes nothing)
  *   Layout     q, k, v, o, dout, dq, dk, dv: contiguous row-major [B, H, N, d]
- *              arrays of the element type `dtype`.  lse: contiguous [B, H, N]
- *              float32.  Head dimension d must be 64 or 128.
+ *              arrays of the element type `dtype` (the *_strided entry points:
+ *              any strides).  lse: contiguous [B, H, N] float32.  Head
+ *              dimension d: 32, 64, 96, 128 or 256 for 16-bit types (32 and
+ *              96 run on the 64 / 128 kernels with the missing columns read
+ *              as zeros, 256 on kernels of its own); 64 or 128 for float32.
  *   Memory     All data pointers are DEVICE pointers owned by the caller.  The
  *              library allocates no device memory and keeps no pointer after a
  *              call returns.  Every tensor pointer must be 16-byte aligned
@@ -55,13 +58,13 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 8
+#define FA_ABI_VERSION 9
 
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL */
   FA_ERR_SHAPE = 2,     /* B, H or N < 1, N > 2^22, or B*H*ceil(N/32) >= 2^24 */
-  FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 (32 also for the split-key entry points) */
+  FA_ERR_HEADDIM = 3,   /* d not taken by this entry point (see each one) */
   FA_ERR_DTYPE = 4,     /* unknown dtype, or a dtype this entry point does not take */
   FA_ERR_ALIGN = 5,     /* a data pointer is not 16-byte aligned */
   FA_ERR_SCALE = 6,     /* scale is negative, NaN or infinite, or scale * log2(e) overflows */
@@ -79,7 +82,9 @@ int fa_abi_version(void);
 const char* fa_status_string(int status);
 
 /* Forward attention.
- *   q, k, v  [B,H,N,d] inputs of type dtype (FA_F32, FA_F16 or FA_BF16).
+ *   q, k, v  [B,H,N,d] inputs of type dtype (FA_F32, FA_F16 or FA_BF16);
+ *            d = 32, 64, 96, 128, 256 (FA_F32: 64, 128).  At d = 256 the
+ *            split-key kernel runs with one key range per head.
  *   o        [B,H,N,d] output, same type.  Fully overwritten.
  *   lse      [B,H,N] float32 output: natural-log log-sum-exp of the scaled
  *            scores of each row over its visible keys.  Fully overwritten.
@@ -97,7 +102,8 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dt
 /* Backward attention: gradients of O with respect to Q, K and V, given the
  * upstream gradient dout = dL/dO and the forward's own outputs o and lse.
  * The scores and probabilities are recomputed from q, k and lse.
- *   q, k, v, o, dout  [B,H,N,d] inputs of type dtype (FA_F16 or FA_BF16).
+ *   q, k, v, o, dout  [B,H,N,d] inputs of type dtype (FA_F16 or FA_BF16);
+ *                     d = 32, 64, 96, 128 or 256 (N + 64 <= 2^22 at 256).
  *   lse               [B,H,N] float32 from fa_fwd on the same q, k, v.
  *   dq, dk, dv        [B,H,N,d] outputs, same type.  Fully overwritten.
  *   workspace         device scratch of at least fa_bwd_workspace_bytes(),
@@ -179,8 +185,7 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
  *              initialised; may be NULL when that size is 0.  It holds the
  *              partial results of the key ranges the cache is split into.
  *   scale, causal, dtype, stream: as for fa_fwd.  Nq, Nk in [1, 2^22].
- *   d          64 or 128 as everywhere, and also 32 (this entry point,
- *              fa_fwd_kvcache_fp8 and fa_fwd_varlen only).
+ *   d          32, 64, 128 or 256 (fa_fwd_kvcache_fp8: 32, 64, 128).
  * Errors: FA_ERR_NULL (q, k_cache, v_cache, o or lse NULL), FA_ERR_SHAPE,
  * FA_ERR_HEADDIM, FA_ERR_DTYPE (FA_F32 is not taken), FA_ERR_ALIGN,
  * FA_ERR_SCALE, FA_ERR_WORKSPACE (NULL or too small when the size is > 0).
@@ -237,10 +242,11 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, 
  *   workspace     fa_fwd_varlen_workspace_bytes(B, H, max_q, max_k, d, dtype)
  *                 bytes (16-byte aligned, may be NULL when that is 0).
  * When cu_seqlens_q and cu_seqlens_k are the same pointer (self-attention:
- * equal query and key counts), total_q = total_k, max_q = max_k, d is 64 or
- * 128 and (max_q + 512) * H * d * 2 < 2^31, fa_fwd's kernels run on the
+ * equal query and key counts), total_q = total_k, max_q = max_k, d is at
+ * most 128 and (max_q + 512) * H * d * 2 < 2^31, fa_fwd's kernels run on the
  * packed rows in place and the workspace is not used; otherwise the
- * split-key kernels of fa_fwd_kvcache do.
+ * split-key kernels of fa_fwd_kvcache do.  d: 32, 64, 128, 256, and 96 on the
+ * self-attention route only.
  * Errors as for fa_fwd_kvcache (FA_ERR_NULL also for NULL prefix sums,
  * FA_ERR_SHAPE for total_q or total_k < 1 or the offset limit). */
 size_t fa_fwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t max_q, int64_t max_k, int64_t d,
@@ -251,45 +257,74 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
                   int64_t B, int64_t H, int64_t total_q, int64_t total_k, int64_t max_q, int64_t max_k,
                   int64_t d, float scale, int causal, int dtype, void* stream);
 
-/* Backward of causal self-attention over a variable-length packed batch
- * (the training side of the packed layout of fa_fwd_varlen with equal query
- * and key prefix sums; the pages' drop-in use with the usual attention
- * interfaces: "FlashAttention-2 (DE)", "Anwendung und Integration in das
- * Ökosystem"; the gradient, recomputed as in fa_bwd: "FlashAttention"
- * lexicon, "Methodische Grundlagen").  Sequence b owns rows
- * cu_seqlens[b] .. cu_seqlens[b+1]-1 of every tensor and attends causally
- * within itself (key j visible to query i iff j <= i).  fa_bwd's kernels
- * read and write the packed rows in place (row stride H d), one workgroup
- * per head and 128-row tile of max_len, and skip tiles past a sequence's
- * length.
- *   q, k, v, o,   [total, H, d] of type dtype (FA_BF16 or FA_F16), packed
- *   dout          rows, 16-byte aligned; o and lse are fa_fwd_varlen's output
- *                 for these q, k, v with causal = 1.
- *   lse           [H, total] float32 (natural log).
- *   cu_seqlens    DEVICE int32 [B + 1] non-decreasing prefix sums (4-byte
- *                 aligned), clamped like fa_fwd_varlen's (entries to
- *                 [0, total], a sequence's length to [0, max_len]).
- *   dq, dk, dv    [total, H, d] outputs, same type; rows outside every
- *                 sequence, and rows past max_len of a longer sequence, are
- *                 left unchanged.
- *   max_len       the largest sequence length, in [1, 2^22];
- *                 (max_len + 128) * H * d * 2 must stay below 2^31 bytes.
- *   workspace     fa_bwd_varlen_workspace_bytes(B, H, total, max_len, d,
- *                 dtype) bytes (total * H floats: D_i = dO_i . O_i),
+/* Backward over a variable-length packed batch: the training side of
+ * fa_fwd_varlen's packed layout (the pages' drop-in use with the usual
+ * attention interfaces: "FlashAttention-2 (DE)", "Anwendung und Integration
+ * in das Ökosystem"; the gradient, recomputed as in fa_bwd: "FlashAttention"
+ * lexicon, "Methodische Grundlagen").  Sequence b owns query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q, o, dout, dq and key rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k, v, dk, dv; within it the mask
+ * is fa_fwd_varlen's (causal: key j visible to query i iff j <= i + Lk - Lq,
+ * bottom-right aligned; with equal counts the square mask).  fa_bwd's
+ * kernels read and write the packed rows in place (row stride H d), one
+ * workgroup per head and 128-row tile of max_q (dQ) or max_k (dK, dV), and
+ * skip tiles past a sequence's counts.  A key no query sees gets dk = dv = 0,
+ * a query that sees no key dq = 0.
+ *   q, o, dout    [total_q, H, d] of type dtype (FA_BF16 or FA_F16), packed
+ *   k, v          [total_k, H, d]      rows, 16-byte aligned; o and lse are
+ *                 fa_fwd_varlen's output for these q, k, v and causal.
+ *   lse           [H, total_q] float32 (natural log).
+ *   cu_seqlens_q, DEVICE int32 [B + 1] non-decreasing prefix sums (4-byte
+ *   cu_seqlens_k  aligned; may be the same pointer), clamped like
+ *                 fa_fwd_varlen's (entries to [0, total], counts to
+ *                 [0, max]).
+ *   dq            [total_q, H, d], dk, dv [total_k, H, d] outputs, same type;
+ *                 rows outside every sequence are left unchanged.
+ *   max_q, max_k  the largest query / key count of any sequence, in
+ *                 [1, 2^22]; (max + 512) * H * d * 2 must stay below 2^31.
+ *   d             32, 64, 96 or 128.
+ *   workspace     fa_bwd_varlen_workspace_bytes(B, H, total_q, max_q, d,
+ *                 dtype) bytes (total_q * H floats: D_i = dO_i . O_i),
  *                 16-byte aligned, contents need not be initialised.
  * Deterministic (fixed reduction order).  Errors: FA_ERR_NULL, FA_ERR_SHAPE
- * (as fa_fwd for B, H, max_len; total < 1, total * H > 2^31 - 1, or the
- * offset limit), FA_ERR_HEADDIM (d not 64 or 128), FA_ERR_DTYPE (not
- * FA_BF16 / FA_F16), FA_ERR_ALIGN, FA_ERR_SCALE, FA_ERR_WORKSPACE,
- * FA_ERR_HIP.  The workspace size function returns 0 for arguments the
- * entry point rejects. */
-size_t fa_bwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t total, int64_t max_len, int64_t d,
+ * (as fa_fwd for B, H, max_q, max_k; totals < 1, total * H > 2^31 - 1, or
+ * the offset limit), FA_ERR_HEADDIM, FA_ERR_DTYPE (not FA_BF16 / FA_F16),
+ * FA_ERR_ALIGN, FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_HIP.  The workspace
+ * size function returns 0 for arguments the entry point rejects. */
+size_t fa_bwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t total_q, int64_t max_q, int64_t d,
                                      int dtype);
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                  const void* dout, const int32_t* cu_seqlens, void* dq, void* dk, void* dv, void* workspace,
-                  size_t workspace_bytes, int64_t B, int64_t H, int64_t total, int64_t max_len, int64_t d,
-                  float scale, int dtype, void* stream);
+                  const void* dout, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq, void* dk,
+                  void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t total_q,
+                  int64_t total_k, int64_t max_q, int64_t max_k, int64_t d, float scale, int causal, int dtype,
+                  void* stream);
+
+/* Forward and backward with caller strides: any element strides per tensor
+ * (batch, head, row; the d elements of a row contiguous), so that [B, N, H, d]
+ * tensors, views into a packed QKV tensor [B, N, 3, H, d] and the like are
+ * used in place, with no copies (the pages' drop-in use with the usual
+ * attention interfaces: "FlashAttention-2 (DE)", "Anwendung und Integration in
+ * das Ökosystem").  Same attention, mask, numerics and errors as fa_fwd /
+ * fa_bwd (16-bit types only), with:
+ *   strides  HOST int64 array, 3 entries per tensor in the order of the
+ *            pointers: fa_fwd_strided q, k, v, o (12 entries); fa_bwd_strided
+ *            q, k, v, o, dout, dq, dk, dv (24 entries).  Row r of head h of
+ *            batch b of a tensor starts at element b*s[0] + h*s[1] + r*s[2].
+ *            Every stride must be >= 0 and a multiple of 8 (16-byte aligned
+ *            rows: else FA_ERR_ALIGN); an output's row stride >= d; (N + 512)
+ *            * row stride * 2 below 2^31 (else FA_ERR_SHAPE).  Inputs may
+ *            overlap (a head stride of 0 shares one K/V head among query
+ *            heads); outputs must not overlap each other or the inputs.
+ *   lse      contiguous [B, H, N] float32 as for fa_fwd; the backward's
+ *            workspace as for fa_bwd.
+ *   d        32, 64, 96 or 128. */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, const int64_t* strides,
+                   int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, void* stream);
+
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, const int64_t* strides,
+                   int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, void* stream);
 
 /* Forward attention on 8-bit floating-point inputs.  The pages name 8-bit
  * floating point as the next step of the method's line ("FlashAttention-2

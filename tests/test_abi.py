@@ -37,13 +37,13 @@ def test_header_declares_the_entry_points():
          "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kvcache_workspace_bytes",
          "fa_fwd_kvcache", "fa_fwd_kvcache_fp8", "fa_probe_mfma_bf16", "fa_fwd_varlen_workspace_bytes",
          "fa_fwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_bwd_varlen", "fa_bwd_noalloc_max_rows",
-         "fa_bwd_noalloc", "fa_fwd_fp8"])
+         "fa_bwd_noalloc", "fa_fwd_fp8", "fa_fwd_strided", "fa_bwd_strided"])
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 8
+    assert lib.fa_abi_version() == 9
 
 
 def test_status_strings(lib):
@@ -77,8 +77,10 @@ def test_fwd_argument_errors(lib):
     assert fwd(lib, N=0) == FA_ERR_SHAPE
     assert fwd(lib, N=(1 << 22) + 1) == FA_ERR_SHAPE
     assert fwd(lib, B=1 << 20, H=1 << 12) == FA_ERR_SHAPE
-    assert fwd(lib, d=96) == FA_ERR_HEADDIM
-    assert fwd(lib, d=256) == FA_ERR_HEADDIM
+    assert fwd(lib, d=80) == FA_ERR_HEADDIM
+    assert fwd(lib, d=512) == FA_ERR_HEADDIM
+    assert fwd(lib, d=256, dtype=0) == FA_ERR_HEADDIM  # float32: d = 64 or 128
+    assert fwd(lib, d=256, N=(1 << 22) - 32) == FA_ERR_SHAPE  # d = 256 rows past 32-bit offsets
     assert fwd(lib, dtype=3) == FA_ERR_DTYPE
     assert fwd(lib, dtype=-1) == FA_ERR_DTYPE
     assert fwd(lib, v=P[2] + 8) == FA_ERR_ALIGN
@@ -95,7 +97,7 @@ def test_bwd_argument_errors(lib):
     assert bwd(lib, do=None) == FA_ERR_NULL
     assert bwd(lib, dv=None) == FA_ERR_NULL
     assert bwd(lib, N=0) == FA_ERR_SHAPE
-    assert bwd(lib, d=32) == FA_ERR_HEADDIM
+    assert bwd(lib, d=80) == FA_ERR_HEADDIM
     assert bwd(lib, dtype=0) == FA_ERR_DTYPE  # the backward takes 16-bit inputs only
     assert bwd(lib, dq=P[6] + 2) == FA_ERR_ALIGN
     assert bwd(lib, scale=float("-inf")) == FA_ERR_SCALE
@@ -167,7 +169,7 @@ def test_stage_argument_errors(lib):
 def test_workspace_bytes(lib):
     assert lib.fa_bwd_workspace_bytes(2, 3, 100, 64, 2) == 4 * 2 * 3 * 100
     assert lib.fa_bwd_workspace_bytes(1, 1, 1, 128, 1) == 4
-    assert lib.fa_bwd_workspace_bytes(1, 1, 1, 96, 2) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 1, 80, 2) == 0
     assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64, 2) == 0
     assert lib.fa_bwd_workspace_bytes(1, 1, 8, 64, 0) == 0
 
@@ -285,6 +287,7 @@ def test_kvcache_fp8_argument_errors(lib):
     assert kv8(lib, Nk=0) == FA_ERR_SHAPE
     assert kv8(lib, d=96) == FA_ERR_HEADDIM
     assert kv8(lib, d=256) == FA_ERR_HEADDIM
+    assert kv(lib, d=96) == FA_ERR_HEADDIM
     assert kv8(lib, dtype=0) == FA_ERR_DTYPE
     assert kv8(lib, k=P[1] + 4) == FA_ERR_ALIGN
     for bad in (0.0, -1.0, math.inf, math.nan):
@@ -332,11 +335,11 @@ def test_varlen_argument_errors(lib):
     assert vl(lib, wsb=need - 1) == FA_ERR_WORKSPACE
 
 
-def bvl(lib, ptrs=None, cu=P[10], ws=P[11], wsb=1 << 40, B=3, H=4, total=300, max_len=128, d=128, scale=0.088,
-        dtype=2):
+def bvl(lib, ptrs=None, cq=P[10], ck=P[10], ws=P[11], wsb=1 << 40, B=3, H=4, tq=300, tk=300, mq=128, mk=128, d=128,
+        scale=0.088, causal=1, dtype=2):
     q, k, v, o, lse, do, dq, dk, dv = ptrs if ptrs is not None else P[:9]
-    return lib.fa_bwd_varlen(q, k, v, o, lse, do, cu, dq, dk, dv, ws, wsb, B, H, total, max_len, d, scale, dtype,
-                             None)
+    return lib.fa_bwd_varlen(q, k, v, o, lse, do, cq, ck, dq, dk, dv, ws, wsb, B, H, tq, tk, mq, mk, d, scale, causal,
+                             dtype, None)
 
 
 def test_varlen_bwd_argument_errors(lib):
@@ -345,30 +348,81 @@ def test_varlen_bwd_argument_errors(lib):
         ptrs = list(P[:9])
         ptrs[i] = None
         assert bvl(lib, ptrs) == FA_ERR_NULL, i
-    assert bvl(lib, cu=None) == FA_ERR_NULL
+    assert bvl(lib, cq=None) == FA_ERR_NULL
+    assert bvl(lib, ck=None) == FA_ERR_NULL
     assert bvl(lib, B=0) == FA_ERR_SHAPE
-    assert bvl(lib, total=0) == FA_ERR_SHAPE
-    assert bvl(lib, total=1 << 31) == FA_ERR_SHAPE
-    assert bvl(lib, max_len=0) == FA_ERR_SHAPE
-    assert bvl(lib, max_len=(1 << 22) + 1) == FA_ERR_SHAPE
-    assert bvl(lib, d=32) == FA_ERR_HEADDIM
+    assert bvl(lib, tq=0) == FA_ERR_SHAPE
+    assert bvl(lib, tk=0) == FA_ERR_SHAPE
+    assert bvl(lib, tq=1 << 31) == FA_ERR_SHAPE
+    assert bvl(lib, mq=0) == FA_ERR_SHAPE
+    assert bvl(lib, mk=(1 << 22) + 1) == FA_ERR_SHAPE
+    assert bvl(lib, d=80) == FA_ERR_HEADDIM
+    assert bvl(lib, d=512) == FA_ERR_HEADDIM
     assert bvl(lib, dtype=0) == FA_ERR_DTYPE
     for i in range(9):
         ptrs = list(P[:9])
         ptrs[i] += 8
         assert bvl(lib, ptrs) == FA_ERR_ALIGN, i
-    assert bvl(lib, cu=P[10] + 2) == FA_ERR_ALIGN
+    assert bvl(lib, cq=P[10] + 2) == FA_ERR_ALIGN
+    assert bvl(lib, ck=P[9] + 2) == FA_ERR_ALIGN
     assert bvl(lib, scale=float("nan")) == FA_ERR_SCALE
-    assert bvl(lib, total=(1 << 29)) == FA_ERR_SHAPE  # total * H = 2^31
-    assert bvl(lib, H=64, max_len=(1 << 17) - 128) == FA_ERR_SHAPE  # 2^17 * 64 * 128 * 2 = 2^31 bytes
+    assert bvl(lib, tq=(1 << 29)) == FA_ERR_SHAPE  # total * H = 2^31
+    assert bvl(lib, H=64, mq=(1 << 17) - 512) == FA_ERR_SHAPE  # (2^17) * 64 * 128 * 2 = 2^31 bytes
+    assert bvl(lib, H=64, mk=(1 << 17) - 512) == FA_ERR_SHAPE
     need = lib.fa_bwd_varlen_workspace_bytes(3, 4, 300, 128, 128, 2)
     assert need == 4 * 300 * 4
     assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 3, 64, 0) == 0
-    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 3, 32, 2) == 0
+    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 3, 80, 2) == 0
     assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 0, 3, 64, 2) == 0
+    assert lib.fa_bwd_varlen_workspace_bytes(1, 1, 3, 3, 32, 2) == 4 * 3
     assert bvl(lib, ws=None) == FA_ERR_WORKSPACE
     assert bvl(lib, wsb=need - 1) == FA_ERR_WORKSPACE
     assert bvl(lib, ws=P[11] + 4, wsb=need) == FA_ERR_ALIGN
+
+
+def _st(n, d=64, bad=None):
+    """Strides of n contiguous [1, 2, 64, d] tensors, one entry replaced."""
+    st = [2 * 64 * d, 64 * d, d] * n
+    if bad is not None:
+        st[bad[0]] = bad[1]
+    return (ctypes.c_int64 * len(st))(*st)
+
+
+def test_strided_argument_errors(lib):
+    fs = lambda st, d=64, dtype=2, **kw: lib.fa_fwd_strided(  # noqa: E731
+        kw.get("q", P[0]), P[1], P[2], P[3], P[4], st, 1, 2, 64, d, 0.125, 1, dtype, None)
+    assert fs(None) == FA_ERR_NULL
+    assert fs(_st(4), q=None) == FA_ERR_NULL
+    assert fs(_st(4), d=80) == FA_ERR_HEADDIM
+    assert fs(_st(4), dtype=0) == FA_ERR_DTYPE  # 16-bit only
+    assert fs(_st(4, bad=(1, -64))) == FA_ERR_SHAPE    # negative head stride
+    assert fs(_st(4, bad=(5, 60))) == FA_ERR_ALIGN     # k's row stride: rows not 16-byte aligned
+    assert fs(_st(4, bad=(11, 32))) == FA_ERR_SHAPE    # o's rows overlap (row stride < d)
+    assert fs(_st(4, bad=(2, 1 << 24))) == FA_ERR_SHAPE  # q rows past 32-bit offsets
+    bs = lambda st, **kw: lib.fa_bwd_strided(  # noqa: E731
+        *P[:9], P[10], 1 << 20, st, 1, 2, 64, kw.get("d", 64), 0.125, 1, 2, None)
+    assert bs(None) == FA_ERR_NULL
+    assert bs(_st(8, bad=(23, 8))) == FA_ERR_SHAPE     # dv rows overlap
+    assert bs(_st(8, bad=(14, 4))) == FA_ERR_ALIGN     # dout's row stride
+    assert bs(_st(8), d=80) == FA_ERR_HEADDIM
+
+
+def test_head_dims_taken_by_fwd_and_bwd(lib):
+    """d = 32 and 96 are taken by the 16-bit forward and backward (checked
+    here by the workspace size function, which makes no device call), not by
+    the float32 forward; d = 256 by both 16-bit passes; 80, 16 and 512 by
+    neither."""
+    for d in (32, 64, 96, 128, 256):
+        assert lib.fa_bwd_workspace_bytes(1, 2, 10, d, 2) == 4 * 20, d
+    for d in (80, 512, 16):
+        assert lib.fa_bwd_workspace_bytes(1, 2, 10, d, 2) == 0, d
+        assert bwd(lib, d=d) == FA_ERR_HEADDIM
+    assert bwd(lib, d=256, N=(1 << 22) - 32) == FA_ERR_SHAPE  # d = 256 rows past 32-bit offsets
+    for d in (80, 16):
+        assert fwd(lib, d=d) == FA_ERR_HEADDIM
+    assert fwd(lib, d=96, dtype=0) == FA_ERR_HEADDIM
+    assert fwd(lib, d=32, dtype=0) == FA_ERR_HEADDIM
+    assert kv8(lib, d=256) == FA_ERR_HEADDIM  # the 8-bit cache: d = 32, 64, 128
 
 
 def test_varlen_self_attention_route_checks_arguments_first(lib):

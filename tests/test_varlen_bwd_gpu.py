@@ -34,13 +34,13 @@ def _run(inp, dtype, scale, max_len=None, init=None):
     mx = max(mx, 1)
     o, lse = fa.fwd_varlen(q, k, v, cu, cu, mx, mx, True, scale)
     if init is None:
-        dq, dk, dv = fa.bwd_varlen(q, k, v, o, lse, do, cu, mx, scale)
+        dq, dk, dv = fa.bwd_varlen(q, k, v, o, lse, do, cu, cu, mx, mx, True, scale)
     else:
         dq, dk, dv = (to_device(init, dtype) for _ in range(3))
         nb = fa.fa_bwd_varlen_workspace_bytes(len(inp["cu_q"]) - 1, q.shape[1], q.shape[0], mx, q.shape[2],
                                               fa.dtype_code(q))
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, dq, dk, dv, ws, mx, scale)
+        fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, cu, dq, dk, dv, ws, mx, mx, scale, True)
     torch.cuda.synchronize()
     return tuple(g.float().cpu().numpy() for g in (dq, dk, dv))
 
@@ -107,7 +107,7 @@ def test_varlen_bwd_equal_lengths_bitwise_equal_the_ordinary_backward(d):
     g_dense = fa.bwd(qd, kd, vd, od, lsed, dod, True, scale)
     o = packed(od)
     lse = lsed.permute(1, 0, 2).reshape(H, B * N).contiguous()
-    g_var = fa.bwd_varlen(q, k, v, o, lse, do, cu, N, scale)
+    g_var = fa.bwd_varlen(q, k, v, o, lse, do, cu, cu, N, N, True, scale)
     torch.cuda.synchronize()
     for name, a, b in zip(("dq", "dk", "dv"), g_var, g_dense):
         assert torch.equal(a, packed(b)), name
@@ -189,3 +189,87 @@ def test_varlen_bwd_malformed_prefix_sums_stay_in_bounds():
     cu_ok = np.array([0, 30], np.int32)
     _check_seqs({"cu_q": cu_ok}, (grads[0], grads[0], grads[0]),
                 lambda b, h: (ref(b, h)[0],) * 3, [0], [0, 1], "sequence 0 dQ rows 0..29")
+
+
+# ---------------------------------------------------------------- unequal counts and the non-causal mask
+
+def _run_general(inp, dtype, scale, causal, same):
+    """fa_fwd_varlen then fa_bwd_varlen with query prefix sums cu_q and key
+    prefix sums cu_k (`same`: one tensor for both); returns float dq, dk, dv."""
+    import torch
+    fa = lib()
+    q, k, v, do = (to_device(inp[n][1], dtype) for n in ("q", "k", "v", "do"))
+    cq = torch.from_numpy(inp["cu_q"]).cuda()
+    ck = cq if same else torch.from_numpy(inp["cu_k"]).cuda()
+    mq = max(int(np.diff(inp["cu_q"]).max()), 1)
+    mk = max(int(np.diff(inp["cu_k"]).max()), 1)
+    o, lse = fa.fwd_varlen(q, k, v, cq, ck, mq, mk, causal, scale)
+    dq, dk, dv = fa.bwd_varlen(q, k, v, o, lse, do, cq, ck, mq, mk, causal, scale)
+    torch.cuda.synchronize()
+    return tuple(g.float().cpu().numpy() for g in (dq, dk, dv))
+
+
+def _check_general(inp, grads, ref, H, label):
+    """Per sequence and head, relative L2 of dQ (query rows) and dK, dV (key rows)."""
+    cq, ck = inp["cu_q"], inp["cu_k"]
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b in range(len(cq) - 1):
+        for h in range(H):
+            for name, g, r, cu in zip(("dq", "dk", "dv"), grads, ref, (cq, ck, ck)):
+                rows = slice(int(cu[b]), int(cu[b + 1]))
+                gg, rr = g[rows, h], r[rows, h]
+                assert np.isfinite(gg).all(), (label, name, b, h)
+                if gg.size == 0:
+                    continue
+                if np.linalg.norm(rr) < 1e-6:
+                    # no query sees these keys (or one key only): exact zeros up to rounding noise
+                    assert np.abs(gg).max() <= 1e-5, (label, name, b, h)
+                    continue
+                worst[name] = max(worst[name], rel_l2(gg, rr))
+    say(f"  {label}: rel-L2 {worst}")
+    for name, e in worst.items():
+        assert e <= BWD_REL_L2, (label, name, e)
+
+
+UNEQUAL = [
+    ([5, 300, 1, 200], [40, 100, 7, 200]),    # fewer and more queries than keys, equal counts
+    ([130, 0, 64], [257, 9, 1]),              # an empty query sequence, a single key
+    ([1000, 33], [600, 700]),                 # several tiles each side, ragged
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", range(len(UNEQUAL)))
+def test_varlen_bwd_unequal_counts(case, causal, d, dtype):
+    """Sequences with their own query and key counts (causal: bottom-right
+    aligned, so some queries see no key and some keys no query), against the
+    oracle's varlen_bwd."""
+    from oracle import varlen_bwd
+    lq, lk = UNEQUAL[case]
+    H = 2
+    seed = 9500 + 17 * case + d + int(causal)
+    inp = si.make_varlen_inputs(lq, lk, H, d, dtype, 1.0, seed, backward=True)
+    scale = 1.0 / np.sqrt(d)
+    say(f"varlen bwd unequal lq={lq} lk={lk} H{H} d{d} {dtype} causal={causal} seed={seed}")
+    grads = _run_general(inp, dtype, scale, causal, same=False)
+    ref = varlen_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], inp["cu_q"], inp["cu_k"], scale, causal)
+    _check_general(inp, grads, ref, H, f"lq {lq} lk {lk} d{d} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", range(len(LENGTHS)))
+def test_varlen_bwd_non_causal_self_attention(case, d):
+    """The non-causal mask over packed self-attention sequences (one
+    prefix-sum tensor): every query sees its sequence's keys only."""
+    from oracle import varlen_bwd
+    lens = LENGTHS[case]
+    H = 3
+    seed = 9600 + 13 * case + d
+    inp = si.make_varlen_inputs(lens, lens, H, d, "bf16", 1.0, seed, backward=True)
+    scale = 1.0 / np.sqrt(d)
+    say(f"varlen bwd non-causal lens={lens} H{H} d{d} seed={seed}")
+    grads = _run_general(inp, "bf16", scale, False, same=True)
+    ref = varlen_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], inp["cu_q"], inp["cu_k"], scale, False)
+    _check_general(inp, grads, ref, H, f"non-causal lens {lens} d{d}")
