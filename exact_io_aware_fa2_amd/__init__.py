@@ -63,6 +63,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{LIB_NAME} is not built ({path}); run __graft_entry__.build()")
+    # torch ships its own HIP runtime under the same soname as the system's:
+    # whichever is loaded first serves the whole process.  Import torch first
+    # so that the library's kernels and torch's memory and streams share
+    # torch's runtime (loaded the other way round, launches on torch's
+    # tensors fail).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(path)
     vp, i64, f32, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
     L.fa_abi_version.restype = i32
