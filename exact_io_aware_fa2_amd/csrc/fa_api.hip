@@ -4,10 +4,30 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "fa.h"
 #include "fa_launch.hpp"
+
+namespace fa {
+
+int device_cu_count(hipStream_t stream) {
+  constexpr int kDevices = 64;
+  static std::atomic<int> cached[kDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= kDevices) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) n = 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace fa
 
 namespace {
 

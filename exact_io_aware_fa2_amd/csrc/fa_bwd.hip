@@ -504,13 +504,14 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
   __shared__ __attribute__((aligned(16))) char smem[4 * STG];
 
+  // one tile: the whole pass from the first load to the last store
+  auto run_tile = [&](const uint32_t lid) __attribute__((always_inline)) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const uint32_t lid = xcd_remap(blockIdx.x, total);
   const int bh = lid / n_qtiles;
   int qt = lid % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;       // longest rows first
@@ -775,6 +776,8 @@ void bwd_dq_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   static_assert(4 * kTileRowsBytes<D> <= STG, "four wavefronts' rows fit one stage slot");
   store_tile_rows<D>(smem + ((n_st + 1) & 3) * STG + w * kTileRowsBytes<D>, od,
                      dQ + dq_off + (size_t)qw * dqs, min(32, Lq - qw), lane, dqs, nch);
+  };
+  for_each_tile(total, (uint32_t)n_qtiles, run_tile);
 }
 
 // ------------------------------------------------------------------ launch
@@ -820,7 +823,11 @@ template <class TR, int D, bool CAUSAL, bool GL>
 static void dq_launch(const BwdArgs& a) {
   const int n_qtiles = (a.Nq + 127) / 128;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, GL>), dim3(total), dim3(256), 0,
+  // persistent at d = 64 (two resident workgroups per compute unit); at
+  // d = 128 the hardware's own dispatch of one workgroup per tile balances
+  // the causal tiles better than the static deal
+  const uint32_t grid = D == 64 ? persistent_grid(total, a.BH, 2, a.stream) : total;
+  hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, GL>), dim3(grid), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.Nq, a.Nk, n_qtiles, total,
                      a.c, a.scale, a.g);

@@ -263,6 +263,33 @@ __device__ inline uint32_t xcd_remap(uint32_t pid, uint32_t total) {
   return x * base + (x < rem ? x : rem) + slot;
 }
 
+// Tile of round r for workgroup b of a persistent grid of G workgroups
+// (G < total, G and nbh multiples of 8).  Tiles are numbered head * nt + t.
+// Workgroup b runs on XCD b % 8 and takes tiles of the heads congruent to b
+// modulo 8 only, so a head's K/V stream stays in one XCD's L2.  Within an
+// XCD the tiles are ordered t-major (tile 0 of every head first: with the
+// causal mask the heaviest) and dealt to the XCD's G / 8 workgroups round by
+// round, alternating direction, so early (heavy) and late (light) positions
+// even out.  Every tile is dealt exactly once; returns nbh * nt when round r
+// has none left for b (then none of the later rounds has one either).
+__device__ inline uint32_t persistent_tile(uint32_t b, uint32_t G, uint32_t r, uint32_t nbh, uint32_t nt) {
+  const uint32_t x = b % 8, j = b / 8, gx = G / 8, nhx = nbh / 8;
+  const uint32_t p = r * gx + ((r & 1) ? gx - 1 - j : j);
+  if (p >= nhx * nt) return nbh * nt;
+  const uint32_t t = p / nhx, hi = p - t * nhx;
+  return (x + 8 * hi) * nt + t;
+}
+
+// Runs run_tile(tile) for the tiles of this workgroup: its own (grid =
+// total; XCD-grouped numbering), or, in a persistent grid of fewer
+// workgroups than tiles, its share by persistent_tile, one after another
+// with a barrier between them that hands the LDS buffers on.  The persistent
+// grid spares the launch of a workgroup into a compute unit another has just
+// left, which leaves the unit idle for microseconds.  Tiles are independent:
+// no workgroup waits for another.
+template <class F>
+__device__ inline void for_each_tile(uint32_t total, uint32_t nt, F&& run_tile);
+
 // Raw buffer access: 32-bit byte offsets from a per-head base, with the
 // hardware range check (an access at or past `bytes` reads zeros).  The whole
 // offset goes in the VGPR operand so the range check covers it.
@@ -284,6 +311,19 @@ __device__ inline void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <class F>
+__device__ inline void for_each_tile(uint32_t total, uint32_t nt, F&& run_tile) {
+  const bool pers = gridDim.x < total;
+  const uint32_t nbh = total / nt;
+  const uint32_t rounds = pers ? (nbh / 8 * nt + gridDim.x / 8 - 1) / (gridDim.x / 8) : 1u;
+  for (uint32_t r = 0; r < rounds; ++r) {
+    const uint32_t lid = pers ? persistent_tile(blockIdx.x, gridDim.x, r, nbh, nt) : xcd_remap(blockIdx.x, total);
+    if (lid >= total) break;
+    if (r > 0) lds_barrier();
+    run_tile(lid);
+  }
 }
 
 // A straight-line run of NST matrix products, each taking its A operand from

@@ -618,6 +618,8 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KS];
   __shared__ __attribute__((aligned(16))) uint16_t sV[3][BC * D];
 
+  // one tile: the whole pass from the first load to the last store
+  auto run_tile = [&](const uint32_t lid) __attribute__((always_inline)) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -626,7 +628,6 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const uint32_t lid = xcd_remap(blockIdx.x, total);
   const int bh = lid / n_qtiles;
   int qt = lid % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest tiles first
@@ -930,6 +931,8 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   store_tile_rows<D>((char*)sK + w * kTileRowsBytes<D>, ov, O + o_off + (size_t)qw * os, min(32, Nb - qw), lane, os,
                      GL ? DR / 8 : D / 8);
   if (qrow < Nb && h == 0) LSE[l_off + qrow] = (m_run + __log2f(l)) * kLn2;
+  };
+  for_each_tile(total, (uint32_t)n_qtiles, run_tile);
 }
 
 // fp32 inputs: same scheme with v_mfma_f32_32x32x2_f32 and unrounded fp32
@@ -1077,7 +1080,9 @@ static void launch_pp_gl(const FwdArgs& a) {  // d = 64 (and d = 32 in the gener
   constexpr int BR = 256;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((fwd16_pp_kernel<TR, 64, 128, CAUSAL, GL>), dim3(total), dim3(512), 0, a.stream,
+  // persistent: one resident workgroup per compute unit (86 KB of LDS)
+  const uint32_t grid = persistent_grid(total, a.BH, 1, a.stream);
+  hipLaunchKernelGGL((fwd16_pp_kernel<TR, 64, 128, CAUSAL, GL>), dim3(grid), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c, a.g);
 }

@@ -1,7 +1,7 @@
 // Internal interface between the C-ABI entry points (fa_api.hip) and the
 // kernel launchers (fa_fwd.hip, fa_bwd.hip).  Arguments arrive here already
-// validated: non-null, 16-byte aligned, d in {64, 128}, N >= 1, B*H >= 1,
-// finite non-negative scale.
+// validated: non-null, 16-byte aligned, d one the entry point takes, N >= 1,
+// B*H >= 1, finite non-negative scale.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,6 +15,20 @@ namespace fa {
 enum Dt { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
 constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Compute units of the device that runs `stream` (cached per device; 0 if
+// the query fails).
+int device_cu_count(hipStream_t stream);
+
+// Grid of a kernel that can walk its tiles persistently (persistent_tile):
+// one workgroup per resident slot (per_cu per compute unit) when that is
+// fewer than the tiles and the split by XCD is even (heads and slots
+// multiples of 8); otherwise one workgroup per tile.
+inline uint32_t persistent_grid(uint32_t total, int nbh, int per_cu, hipStream_t stream) {
+  const uint32_t slots = (uint32_t)(device_cu_count(stream) * per_cu);
+  if (slots == 0 || slots % 8 != 0 || nbh % 8 != 0 || total <= slots) return total;
+  return slots;
+}
 
 struct FwdArgs {
   const void* q;
