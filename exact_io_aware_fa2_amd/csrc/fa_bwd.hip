@@ -826,7 +826,7 @@ static void dq_launch(const BwdArgs& a) {
   // persistent at d = 64 (two resident workgroups per compute unit); at
   // d = 128 the hardware's own dispatch of one workgroup per tile balances
   // the causal tiles better than the static deal
-  const uint32_t grid = D == 64 ? persistent_grid(total, a.BH, 2, a.stream) : total;
+  const uint32_t grid = D == 64 ? persistent_grid(a.BH, n_qtiles, 2, a.stream) : total;
   hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, GL>), dim3(grid), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.Nq, a.Nk, n_qtiles, total,

@@ -264,19 +264,22 @@ __device__ inline uint32_t xcd_remap(uint32_t pid, uint32_t total) {
 }
 
 // Tile of round r for workgroup b of a persistent grid of G workgroups
-// (G < total, G and nbh multiples of 8).  Tiles are numbered head * nt + t.
-// Workgroup b runs on XCD b % 8 and takes tiles of the heads congruent to b
-// modulo 8 only, so a head's K/V stream stays in one XCD's L2.  Within an
-// XCD the tiles are ordered t-major (tile 0 of every head first: with the
-// causal mask the heaviest) and dealt to the XCD's G / 8 workgroups round by
-// round, alternating direction, so early (heavy) and late (light) positions
-// even out.  Every tile is dealt exactly once; returns nbh * nt when round r
-// has none left for b (then none of the later rounds has one either).
+// (G < total, G and nbh multiples of 8).  Tiles are numbered head * nt + t,
+// t = 0 the heaviest with the causal mask.  Workgroup b runs on XCD b % 8 and
+// takes tiles of the heads congruent to b modulo 8 only.  Within an XCD the
+// tiles are taken head by head, G / 8 per round, so the workgroups of one
+// XCD work on a few heads at a time and those heads' K/V stay in its L2
+// (dealt in the other order, every tile of a round belongs to another head
+// and K/V is fetched again per tile).  Rounds alternate direction: with
+// whole heads per round, a workgroup's tile t in one round is followed by
+// about nt - 1 - t in the next, which evens out the causal costs.  Every
+// tile is dealt exactly once; returns nbh * nt when round r has none left
+// for b (then none of the later rounds has one either).
 __device__ inline uint32_t persistent_tile(uint32_t b, uint32_t G, uint32_t r, uint32_t nbh, uint32_t nt) {
   const uint32_t x = b % 8, j = b / 8, gx = G / 8, nhx = nbh / 8;
   const uint32_t p = r * gx + ((r & 1) ? gx - 1 - j : j);
   if (p >= nhx * nt) return nbh * nt;
-  const uint32_t t = p / nhx, hi = p - t * nhx;
+  const uint32_t hi = p / nt, t = p - hi * nt;
   return (x + 8 * hi) * nt + t;
 }
 

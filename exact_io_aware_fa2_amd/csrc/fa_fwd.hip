@@ -1081,7 +1081,7 @@ static void launch_pp_gl(const FwdArgs& a) {  // d = 64 (and d = 32 in the gener
   const int n_qtiles = (a.N + BR - 1) / BR;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
   // persistent: one resident workgroup per compute unit (86 KB of LDS)
-  const uint32_t grid = persistent_grid(total, a.BH, 1, a.stream);
+  const uint32_t grid = persistent_grid(a.BH, n_qtiles, 1, a.stream);
   hipLaunchKernelGGL((fwd16_pp_kernel<TR, 64, 128, CAUSAL, GL>), dim3(grid), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c, a.g);

@@ -22,11 +22,14 @@ int device_cu_count(hipStream_t stream);
 
 // Grid of a kernel that can walk its tiles persistently (persistent_tile):
 // one workgroup per resident slot (per_cu per compute unit) when that is
-// fewer than the tiles and the split by XCD is even (heads and slots
-// multiples of 8); otherwise one workgroup per tile.
-inline uint32_t persistent_grid(uint32_t total, int nbh, int per_cu, hipStream_t stream) {
+// fewer than the tiles and the deal comes out even: heads a multiple of 8 and
+// every XCD's tiles (nbh / 8 heads of nt tiles) a whole number of rounds of
+// its slots / 8 workgroups.  Otherwise one workgroup per tile.
+inline uint32_t persistent_grid(int nbh, int nt, int per_cu, hipStream_t stream) {
+  const uint32_t total = (uint32_t)nbh * (uint32_t)nt;
   const uint32_t slots = (uint32_t)(device_cu_count(stream) * per_cu);
   if (slots == 0 || slots % 8 != 0 || nbh % 8 != 0 || total <= slots) return total;
+  if (((uint32_t)(nbh / 8) * (uint32_t)nt) % (slots / 8) != 0) return total;
   return slots;
 }
 
