@@ -128,13 +128,14 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
   __shared__ __attribute__((aligned(16))) char smem[4 * STG];
 
+  // one tile: the whole pass from the first load to the last store
+  auto run_tile = [&](const uint32_t lid) __attribute__((always_inline)) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const uint32_t lid = xcd_remap(blockIdx.x, total);
   const int bh = lid / n_ktiles;
   const int kt = lid % n_ktiles;
   const int k0 = kt * BKV;
@@ -454,6 +455,8 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                      dK + dk_off + (size_t)kw * dks, nrows, lane, dks, nch);
   store_tile_rows<D>(smem + ((n_st + 2) & 3) * STG + w * kTileRowsBytes<D>, ov,
                      dV + dv_off + (size_t)kw * dvs, nrows, lane, dvs, nch);
+  };
+  for_each_tile(total, (uint32_t)n_ktiles, run_tile);
 }
 
 // ------------------------------------------------------------------ dQ
@@ -805,7 +808,9 @@ static void dkdv_launch(const BwdArgs& a) {
   // exponent is -LSE log2 e, its value at scale 0 (dK is still multiplied by
   // the true scale).
   const float s = a.scale >= 0x1p-100f ? a.scale : 0x1p-100f;
-  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, GL>), dim3(total), dim3(256), 0,
+  // persistent (one workgroup per resident slot) when the tiles deal out evenly
+  const uint32_t grid = persistent_grid(a.BH, n_ktiles, D == 128 ? 1 : 2, a.stream);
+  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, GL>), dim3(grid), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
                      a.Nq, a.Nk, n_ktiles, total, s * kLog2e, -1.0f / s, a.scale, a.g);
@@ -823,10 +828,8 @@ template <class TR, int D, bool CAUSAL, bool GL>
 static void dq_launch(const BwdArgs& a) {
   const int n_qtiles = (a.Nq + 127) / 128;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  // persistent at d = 64 (two resident workgroups per compute unit); at
-  // d = 128 the hardware's own dispatch of one workgroup per tile balances
-  // the causal tiles better than the static deal
-  const uint32_t grid = D == 64 ? persistent_grid(a.BH, n_qtiles, 2, a.stream) : total;
+  // persistent (one workgroup per resident slot) when the tiles deal out evenly
+  const uint32_t grid = persistent_grid(a.BH, n_qtiles, D == 128 ? 1 : 2, a.stream);
   hipLaunchKernelGGL((bwd_dq_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, GL>), dim3(grid), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.Nq, a.Nk, n_qtiles, total,

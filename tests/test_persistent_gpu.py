@@ -1,6 +1,6 @@
 """Parity of the persistent grids.  The d = 64 forward (fwd16_pp_kernel) and
-the d = 64 dQ kernel launch one workgroup per resident slot, each walking its
-share of the tiles, when the tiles outnumber the slots and the heads split
+the dK/dV and dQ kernels launch one workgroup per resident slot, each walking
+its share of the tiles, when the tiles outnumber the slots and the heads split
 evenly over the 8 XCDs in whole rounds (the shapes below: more tiles than
 the 256 compute units hold, ragged last tiles).  Every output starts as NaN, so a tile that no
 workgroup takes shows as NaN; sampled heads (the first, and the last, which
@@ -65,13 +65,16 @@ def test_varlen_self_d64_more_tiles_than_slots(causal):
     assert_fwd_ok(fwd_errors(og[:, sel], lg[sel], o_ref, l_ref), "bf16", "heads 0 and 7")
 
 
-def test_backward_d64_dq_more_tiles_than_slots():
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_more_tiles_than_slots(d):
     import torch
     fa = lib()
-    B, H, N, d = 2, 8, 4000, 64  # 16 heads x 32 query tiles of 128 rows for the dQ kernel
+    # 32 heads x 32 tiles of 128 keys (dK/dV) or 128 query rows (dQ), the last ragged:
+    # more than the resident slots (512 at d = 64, 256 at d = 128)
+    B, H, N = 4, 8, 4000
     scale = 1.0 / np.sqrt(d)
-    inp = si.make_inputs(B, H, N, d, "bf16", 1.0, 9920, backward=True)
-    say(f"persistent dQ B{B} H{H} N{N} d{d} causal")
+    inp = si.make_inputs(B, H, N, d, "bf16", 1.0, 9920 + d, backward=True)
+    say(f"persistent backward B{B} H{H} N{N} d{d} causal")
     q, k, v = (to_device(inp[n][1], "bf16") for n in ("q", "k", "v"))
     do = to_device(inp["do"][1], "bf16")
     o, lse = fa.fwd(q, k, v, True, scale)
@@ -83,7 +86,7 @@ def test_backward_d64_dq_more_tiles_than_slots():
     grads = [t.float().cpu().numpy() for t in (dq, dk, dv)]
     for g in grads:
         assert np.isfinite(g).all()
-    for (b, h) in [(0, 0), (1, 7)]:
+    for (b, h) in [(0, 0), (3, 7)]:
         ref = attention_bwd_head(inp["q"][0][b, h], inp["k"][0][b, h], inp["v"][0][b, h], inp["do"][0][b, h],
                                  scale, True)
         errs = [rel_l2(g[b, h], r) for g, r in zip(grads, ref)]
