@@ -101,6 +101,13 @@ def test_c3_d64_bf16_causal_sampled():
     _sampled(w, [(0, 3), (1, 30)], _rows_early_random_late)
 
 
+@pytest.mark.parametrize("name", ["C5", "C5d128"])
+def test_c5_forward_full_size_sampled(name):
+    # the forward half of the timed step (persistent grid at d = 64), on its own outputs
+    w = si.WORKLOADS[name]
+    _sampled(w, [(0, 0), (7, 15), (3, 9)], _rows_early_random_late)
+
+
 def test_c4_fp16_causal_long_context_sampled():
     w = si.WORKLOADS["C4"]
     _sampled(w, [(0, 0), (0, 31)], lambda n: _rows_early_random_late(n, early=256, rand=128, late=32))

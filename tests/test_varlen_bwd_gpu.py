@@ -273,3 +273,38 @@ def test_varlen_bwd_non_causal_self_attention(case, d):
     grads = _run_general(inp, "bf16", scale, False, same=True)
     ref = varlen_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], inp["cu_q"], inp["cu_k"], scale, False)
     _check_general(inp, grads, ref, H, f"non-causal lens {lens} d{d}")
+
+
+@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", range(len(UNEQUAL)))
+def test_varlen_bwd_unequal_counts_other_head_dims(case, causal, d):
+    """d = 32 (the d = 64 kernels with zero columns) and d = 256 (the wide
+    kernels) on sequences with their own query and key counts."""
+    from oracle import varlen_bwd
+    lq, lk = UNEQUAL[case]
+    H = 2
+    seed = 9540 + 17 * case + d + int(causal)
+    inp = si.make_varlen_inputs(lq, lk, H, d, "bf16", 1.0, seed, backward=True)
+    scale = 1.0 / np.sqrt(d)
+    say(f"varlen bwd unequal lq={lq} lk={lk} H{H} d{d} causal={causal} seed={seed}")
+    grads = _run_general(inp, "bf16", scale, causal, same=False)
+    ref = varlen_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], inp["cu_q"], inp["cu_k"], scale, causal)
+    _check_general(inp, grads, ref, H, f"lq {lq} lk {lk} d{d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", range(len(LENGTHS)))
+def test_varlen_bwd_self_attention_d96(case, causal):
+    """d = 96 (the d = 128 kernels with zero columns) on packed self-attention
+    sequences, the route fa_fwd_varlen takes it on."""
+    from oracle import varlen_bwd
+    lens = LENGTHS[case]
+    H = 2
+    seed = 9580 + 13 * case + int(causal)
+    inp = si.make_varlen_inputs(lens, lens, H, 96, "bf16", 1.0, seed, backward=True)
+    scale = 1.0 / np.sqrt(96)
+    say(f"varlen bwd self lens={lens} H{H} d96 causal={causal} seed={seed}")
+    grads = _run_general(inp, "bf16", scale, causal, same=True)
+    ref = varlen_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], inp["cu_q"], inp["cu_k"], scale, causal)
+    _check_general(inp, grads, ref, H, f"self lens {lens} d96 causal={causal}")
