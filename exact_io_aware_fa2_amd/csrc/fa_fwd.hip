@@ -301,13 +301,19 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
     const int j0 = j * BC;
     wait_scores(s_cur);  // S_j was produced by matrix instructions
 
-    // score r of block (qb, kb), -inf where masked
+    // score r of block (qb, kb), -inf where masked: its key j0 + 4h + off(kb, r)
+    // is hidden iff off >= lim[qb], the first hidden key of the row (the end of
+    // the sequence, or causally the key after the row's own) less j0 + 4h --
+    // one compare per score against a value of this iteration
+    int lim[QB];
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        lim[qb] = (CAUSAL ? min(Nb, qw + 32 * qb + l32 + 1) : Nb) - j0 - 4 * h;
+    }
     auto score = [&](int qb, int kb, int r) __attribute__((always_inline)) -> float {
       const float x = s_cur[qb][kb][r];
-      if constexpr (MASKED) {
-        const int key = j0 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
-        return (key >= Nb || (CAUSAL && key > qw + 32 * qb + l32)) ? -INFINITY : x;
-      }
+      if constexpr (MASKED) return 32 * kb + 8 * (r / 4) + (r % 4) >= lim[qb] ? -INFINITY : x;
       return x;
     };
 
@@ -856,13 +862,13 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       if (j < wave_tiles) {
         const int j0 = j * BC;
         if (wave_uniform((CAUSAL && j0 + BC - 1 > qw) || j0 + BC > Nb)) {
+          // key j0 + 4h + off is hidden iff off >= lim (one compare per score)
+          const int lim = (CAUSAL ? min(Nb, qrow + 1) : Nb) - j0 - 4 * h;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = j0 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
-              if (key >= Nb || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+              if (32 * kb + 8 * (r / 4) + (r % 4) >= lim) s[kb][r] = -INFINITY;
         }
         // probabilities against the reference maximum m_run
         float lsum, ltsum;

@@ -92,3 +92,22 @@ def test_backward_more_tiles_than_slots(d):
         errs = [rel_l2(g[b, h], r) for g, r in zip(grads, ref)]
         say(f"  head ({b},{h}): rel-L2 dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}")
         assert max(errs) <= BWD_REL_L2
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_persistent_runs_are_bitwise_repeatable(d):
+    """Two calls on a shape that takes the persistent grids (the d = 64
+    forward, both backward kernels) give the same bits."""
+    import torch
+    fa = lib()
+    B, H, N = 4, 8, 4000
+    inp = si.make_inputs(B, H, N, d, "bf16", 1.0, 9930 + d, backward=True)
+    q, k, v, do = (to_device(inp[n][1], "bf16") for n in ("q", "k", "v", "do"))
+    o1, l1 = fa.fwd(q, k, v, True)
+    o2, l2 = fa.fwd(q, k, v, True)
+    g1 = fa.bwd(q, k, v, o1, l1, do, True)
+    g2 = fa.bwd(q, k, v, o1, l1, do, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    for x, y in zip(g1, g2):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
