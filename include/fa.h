@@ -81,7 +81,12 @@ int fa_abi_version(void);
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* fa_status_string(int status);
 
-/* Forward attention.
+/* Forward attention: O = softmax(scale * Q K^T [causal mask]) V and the
+ * per-row log-sum-exp, computed tile by tile with a running normalisation and
+ * without an N x N array in memory ("FlashAttention" lexicon, "Methodische
+ * Grundlagen": tiling and the running normalisation; "FlashAttention-2 (DE)",
+ * "Technische Architektur und Funktionsprinzipien": one workgroup per query
+ * tile and head, rows split across wavefronts, one normalisation at the end).
  *   q, k, v  [B,H,N,d] inputs of type dtype (FA_F32, FA_F16 or FA_BF16);
  *            d = 32, 64, 96, 128, 256 (FA_F32: 64, 128).  At d = 256 the
  *            split-key kernel runs with one key range per head.
@@ -101,7 +106,10 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dt
 
 /* Backward attention: gradients of O with respect to Q, K and V, given the
  * upstream gradient dout = dL/dO and the forward's own outputs o and lse.
- * The scores and probabilities are recomputed from q, k and lse.
+ * The scores and probabilities are recomputed from q, k and lse instead of
+ * being kept from the forward ("FlashAttention" lexicon, "Methodische
+ * Grundlagen", "Neuberechnung statt Speicherung"); the result is exact and
+ * deterministic ("FlashAttention-2 (DE)", "Leistung und Effizienz").
  *   q, k, v, o, dout  [B,H,N,d] inputs of type dtype (FA_F16 or FA_BF16);
  *                     d = 32, 64, 96, 128 or 256 (N + 64 <= 2^22 at 256).
  *   lse               [B,H,N] float32 from fa_fwd on the same q, k, v.
