@@ -326,7 +326,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
  *            heads); outputs must not overlap each other or the inputs.
  *   lse      contiguous [B, H, N] float32 as for fa_fwd; the backward's
  *            workspace as for fa_bwd.
- *   d        32, 64, 96 or 128. */
+ *   d        32, 64, 96, 128 or 256, as fa_fwd / fa_bwd. */
 int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, const int64_t* strides,
                    int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, void* stream);
 
