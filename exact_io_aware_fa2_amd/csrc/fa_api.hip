@@ -116,22 +116,35 @@ int check_strides(const int64_t* st, int ntensors, const bool* output, int64_t N
   return FA_OK;
 }
 
-// The scale must be finite and >= 0, and so must the factor the kernels use,
-// scale * log2(e) (it overflows to infinity above about 2.4e38).
+// The scale must be finite, and so must the factor the kernels use,
+// |scale| * log2(e) (it overflows to infinity above about 2.4e38).
 int check_scale(float scale) {
-  if (!isfinite(scale) || scale < 0.0f) return FA_ERR_SCALE;
-  if (!isfinite(scale * fa::kLog2eHost)) return FA_ERR_SCALE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (!isfinite(fabsf(scale) * fa::kLog2eHost)) return FA_ERR_SCALE;
   return FA_OK;
 }
 
-// Factor turning a raw score into log2 units, scale * log2(e).  The kernels
+// Factor turning a raw score into log2 units, |scale| * log2(e) (a negative
+// scale negates one operand of the scores instead: neg_mask).  The kernels
 // mask a score by setting it to -inf before this multiplication, so the factor
 // must not be zero: scale = 0 uses the smallest normal float instead, which
 // leaves every finite score's contribution at 2^0 = 1 (uniform weights) and
 // keeps masked scores at -inf.
 float exp2_factor(float scale) {
-  const float c = scale * fa::kLog2eHost;
+  const float c = fabsf(scale) * fa::kLog2eHost;
   return c < FLT_MIN ? FLT_MIN : c;
+}
+
+// Softmax of s q.k with s < 0 is softmax of |s| (-q).k: the forward kernels,
+// which keep a running maximum of the raw scores, flip the sign bits of the
+// queries' 16-bit elements under this mask and use |s| for the exponent.
+uint32_t neg_mask(float scale) { return scale < 0.0f ? 0x80008000u : 0u; }
+
+// The backward forms P = exp2(q.k c - LSE log2 e) with no maximum: it takes
+// the factor with the scale's sign (a negative zero counts as zero).
+float exp2_factor_signed(float scale) {
+  const float c = exp2_factor(scale);
+  return scale < 0.0f ? -c : c;
 }
 
 }  // namespace
@@ -148,7 +161,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_HEADDIM: return "unsupported head dimension for this entry point";
     case FA_ERR_DTYPE: return "unsupported dtype";
     case FA_ERR_ALIGN: return "data pointer not 16-byte aligned";
-    case FA_ERR_SCALE: return "scale must be finite and >= 0";
+    case FA_ERR_SCALE: return "scale must be finite (and an 8-bit cache's scales > 0)";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_SCRATCH: return "sizes exceed the static scratch of fa_bwd_noalloc";
@@ -176,6 +189,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   fa::FwdArgs a;
   a.general = padded_d(d);
   a.g = dense_layout_g(H, N, d);
+  a.g.qneg = neg_mask(scale);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -226,7 +240,7 @@ int bwd_common(fa::BwdArgs& a, const void* const* ptrs, int nptrs, const void* w
   a.general = padded_d(d);
   a.g = dense_layout_g(H, N, d);
   a.scale = scale;
-  a.c = exp2_factor(scale);
+  a.c = exp2_factor_signed(scale);
   a.causal = causal != 0;
   a.dtype = dtype;
   a.stream = (hipStream_t)stream;
@@ -355,6 +369,7 @@ int fwd_d256(const void* q, const void* k, const void* v, void* o, float* lse, c
   a.lse = lse;
   a.workspace = nullptr;
   a.lay = lay;
+  a.lay.qneg = neg_mask(scale);
   a.H = (int)H;
   a.BH = (int)(B * H);
   a.Nq = a.Nk = (int)N;
@@ -406,6 +421,7 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, cons
   a.lse = lse;
   a.workspace = need > 0 ? workspace : nullptr;
   a.lay = dense_layout(H, Nq, Nk, d);
+  a.lay.qneg = neg_mask(scale);
   a.H = (int)H;
   a.BH = (int)(B * H);
   a.Nq = (int)Nq;
@@ -451,6 +467,7 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, 
   a.lse = lse;
   a.workspace = need > 0 ? workspace : nullptr;
   a.lay = dense_layout(H, Nq, Nk, d);
+  a.lay.qneg = neg_mask(scale);
   a.H = (int)H;
   a.BH = (int)(B * H);
   a.Nq = (int)Nq;
@@ -525,6 +542,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
     f.stream = (hipStream_t)stream;
     f.general = true;
     f.g = packed_layout_g(H, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k);
+    f.g.qneg = neg_mask(scale);
     return status_of(fa::launch_fwd(f));
   }
   if (d == 96) return FA_ERR_HEADDIM;
@@ -554,6 +572,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
   l.cu_k = cu_seqlens_k;
   l.total_q = total_q;
   l.total_k = total_k;
+  l.qneg = neg_mask(scale);
   a.lay = l;
   a.H = (int)H;
   a.BH = (int)(B * H);
@@ -627,7 +646,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   a.Nk = (int)max_k;
   a.d = (int)d;
   a.scale = scale;
-  a.c = exp2_factor(scale);
+  a.c = exp2_factor_signed(scale);
   a.causal = causal != 0;
   a.dtype = dtype;
   a.stream = (hipStream_t)stream;
@@ -669,6 +688,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_sc
   a.N = (int)N;
   a.d = (int)d;
   a.c = exp2_factor(scale);
+  a.qneg = scale < 0.0f;
   a.causal = causal != 0;
   a.dtype = dtype;
   a.stream = (hipStream_t)stream;
@@ -783,6 +803,7 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
   a.stream = (hipStream_t)stream;
   a.general = true;
   a.g = dense_layout_g(H, N, d);
+  a.g.qneg = neg_mask(scale);
   fa::Strides* t[4] = {&a.g.q, &a.g.k, &a.g.v, &a.g.o};
   for (int i = 0; i < 4; ++i) *t[i] = fa::Strides{strides[3 * i], strides[3 * i + 1], strides[3 * i + 2]};
   if (d == 256) {

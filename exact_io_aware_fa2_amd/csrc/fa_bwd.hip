@@ -125,6 +125,7 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   static_assert(NSL == 32 || NSL == 16, "vector work schedule below");
   static_assert(OCC * 4 * STG <= 160 * 1024, "four stages per workgroup fit in LDS");
   using PM = PipeMma<TR, OCC == 1>;          // K, V, dK and dV in AGPRs at one wavefront per SIMD
+  const float s_out = neg_inv_scale < 0.0f ? -INFINITY : INFINITY;  // initial S of rows past the end
 
   __shared__ __attribute__((aligned(16))) char smem[4 * STG];
 
@@ -264,9 +265,10 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     } else if (j < 2 * NCH) {
       *(u32x4_t*)(smem + sb + OFF_O + s_off + ROWSTEP * (j - NCH) * RBL) = so[t][j - NCH];
     } else {
-      // rows past the end: -inf initialises their S, so P = 0; D = 0
+      // rows past the end: an infinite S of the sign of -1 / s (-inf for s > 0,
+      // +inf for s < 0) makes S c = -inf, so P = 0; D = 0
       const bool in = vidx[t] < Lq;
-      *(float*)(smem + sb + vec_off) = is_d ? (in ? -vraw[t] : 0.0f) : (in ? vraw[t] * neg_inv_scale : -INFINITY);
+      *(float*)(smem + sb + vec_off) = is_d ? (in ? -vraw[t] : 0.0f) : (in ? vraw[t] * neg_inv_scale : s_out);
     }
   };
 
@@ -426,6 +428,11 @@ void bwd_dkdv_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   {
     const uint32_t sb = (uint32_t)((n_st - 1) & 3) * STG;
     asm volatile("" : "+v"(pk[1][0]), "+v"(pk[1][1]), "+v"(dsk[1][0]), "+v"(dsk[1][1]));
+    // where the loops join, the accumulators may have been copied between registers
+    if constexpr (NDB == 4)
+      PM::copy_wait(acc_dk[0], acc_dk[1], acc_dk[2], acc_dk[3], acc_dv[0], acc_dv[1], acc_dv[2], acc_dv[3]);
+    else
+      PM::copy_wait(acc_dk[0], acc_dk[1], acc_dv[0], acc_dv[1]);
 #pragma unroll
     for (int x = 0; x < NKS; ++x) {
       PM::macc(acc_dv[x % NDB], tr_frag(sb, 1, 1, x / NDB, x % NDB), pk[1][x / NDB]);
@@ -803,11 +810,13 @@ static void dkdv_launch(const BwdArgs& a) {
   const int n_ktiles = (a.Nk + 127) / 128;
   const uint32_t total = (uint32_t)(n_ktiles * a.BH);
   // The kernel forms the exponent as (q.k - LSE / s) * s log2 e with s the
-  // scale.  Below 2^-100 (scale 0 included) it takes s = 2^-100 there, so that
+  // scale (of either sign: no running maximum is taken here).  Below 2^-100
+  // in magnitude (scale 0 included) it takes s = +-2^-100 there, so that
   // -1 / s stays finite: q.k then vanishes beside LSE / s in float and the
   // exponent is -LSE log2 e, its value at scale 0 (dK is still multiplied by
   // the true scale).
-  const float s = a.scale >= 0x1p-100f ? a.scale : 0x1p-100f;
+  const float mag = fmaxf(fabsf(a.scale), 0x1p-100f);
+  const float s = a.scale < 0.0f ? -mag : mag;
   // persistent (one workgroup per resident slot) when the tiles deal out evenly
   const uint32_t grid = persistent_grid(a.BH, n_ktiles, D == 128 ? 1 : 2, a.stream);
   hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<TR, D, CAUSAL, D == 128 ? 1 : 2, GL>), dim3(grid), dim3(256), 0,

@@ -193,6 +193,13 @@ __device__ __forceinline__ void mfma_wait_a(f32x16_t& a, f32x16_t& b, f32x16_t& 
 }
 #undef FA_MFMA_WAIT
 
+// The other direction: a vector-ALU write of a VGPR needs two wait states
+// before a matrix instruction reads it, which the compiler does not count
+// for the inline-assembly products either.  valu_to_mfma_wait follows such a
+// write of an operand (the value as its operand: the write stays above it,
+// every read below).  Operands that arrive by loads need none.
+__device__ __forceinline__ void valu_to_mfma_wait(u32x4_t& x) { asm volatile("s_nop 1" : "+v"(x)); }
+
 // Products of the software-pipelined kernels.  With AG (one wavefront per
 // SIMD, 512 registers) the B operands of mb* and the accumulators of macc
 // stay in AGPRs; without (two wavefronts per SIMD, 256 registers each) every
@@ -221,6 +228,18 @@ struct PipeMma {
   __device__ static inline void wait_acc(f32x16_t& a, f32x16_t& b, f32x16_t& c, f32x16_t& d,
                                          f32x16_t& e, f32x16_t& f, f32x16_t& g, f32x16_t& h) {
     if constexpr (AG) mfma_wait_a(a, b, c, d, e, f, g, h); else mfma_wait_v(a, b, c, d, e, f, g, h);
+  }
+  // Two wait states between vector writes of macc accumulators (register
+  // copies the compiler places where control flow joins) and products that
+  // read them next.
+  __device__ static inline void copy_wait(f32x16_t& a, f32x16_t& b, f32x16_t& c, f32x16_t& d) {
+    if constexpr (AG) asm volatile("s_nop 1" : "+a"(a), "+a"(b), "+a"(c), "+a"(d));
+    else asm volatile("s_nop 1" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+  }
+  __device__ static inline void copy_wait(f32x16_t& a, f32x16_t& b, f32x16_t& c, f32x16_t& d,
+                                          f32x16_t& e, f32x16_t& f, f32x16_t& g, f32x16_t& h) {
+    if constexpr (AG) asm volatile("s_nop 1" : "+a"(a), "+a"(b), "+a"(c), "+a"(d), "+a"(e), "+a"(f), "+a"(g), "+a"(h));
+    else asm volatile("s_nop 1" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
   }
 };
 
@@ -427,6 +446,7 @@ struct GenLayout {
   int64_t l_sb, l_sh;
   int H;
   int dr;
+  uint32_t qneg;  // forward kernels: 0x80008000 for a negative scale (sign_flip of the queries), else 0
 };
 
 // First row and row count of sequence b's queries (or keys): prefix sums
@@ -465,6 +485,12 @@ __device__ inline TRows tensor_rows(const Strides& t, int b, int h, int start, i
 // past the data's dr columns it moves the load past the buffer range, so it
 // reads zeros (bytes < 2^31 and row offsets < 2^31 keep the sum in 32 bits).
 __device__ inline uint32_t col_pad(uint32_t cb, int dr, uint32_t bytes) { return cb >= 2u * (uint32_t)dr ? bytes : 0u; }
+
+// A negative scale s enters the forward kernels as |s| with the queries
+// negated, since s q.k = |s| (-q).k: the query fragments' 16-bit elements
+// have their sign bits flipped (m = 0x80008000), or are left alone (m = 0).
+// The exponent factor and every running maximum then see |s|, as for s >= 0.
+__device__ inline u32x4_t sign_flip(u32x4_t x, uint32_t m) { return x ^ m; }
 
 // Where the rows of head bh lie.  Dense [BH, N, D]: rows of D elements from
 // bh N D, vectors (LSE, D_i) from bh N, all N rows real.  Packed (VL): head

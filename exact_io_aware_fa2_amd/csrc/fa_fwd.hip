@@ -168,7 +168,8 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   const int qw = q0 + 32 * QB * w;  // first query row of this wavefront
 
   // Q rows as the B operand of S^T = K Q^T, loaded once (rows past the end
-  // read zeros; their results are never stored).
+  // read zeros; their results are never stored); their signs are flipped for
+  // a negative scale once they have arrived (first pass's prologue).
   u32x4_t qf[QB][NKS];
   {
     const rsrc_t qres = make_rsrc(Q + q_off, q_bytes);
@@ -448,6 +449,15 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
     for (int i = 0; i < CW; ++i) *(u32x4_t*)(&sV[1][(tid + NT * i) * 8]) = u32x4_t{0u, 0u, 0u, 0u};
     load_k(0);
     wait_vmem();  // Q fragments and K_0
+    if (!exact) {
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+  #pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          qf[qb][ks] = sign_flip(qf[qb][ks], g.qneg);
+          valu_to_mfma_wait(qf[qb][ks]);
+        }
+    }
   #pragma unroll
     for (int i = 0; i < NKC; ++i) store_part(i, 0);
     load_k(1);
@@ -671,14 +681,17 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int qrow = qw + l32;
 
   // Q rows as the B operand of S^T = K Q^T, loaded once (rows past the end
-  // read zeros; their results are never stored).
+  // read zeros; their results are never stored); signs flipped for a negative
+  // scale (the products here are compiler builtins, which keep the wait
+  // states after that vector write themselves).
   u32x4_t qf[NKS];
   {
     const rsrc_t qres = make_rsrc(Q + q_off, q_bytes);
     const uint32_t qoff = (uint32_t)qrow * rsq + 16 * h;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      qf[ks] = buf_load16(qres, qoff + 32 * ks + (GL ? col_pad(32 * ks + 16 * h, DR, q_bytes) : 0u));
+      qf[ks] = sign_flip(buf_load16(qres, qoff + 32 * ks + (GL ? col_pad(32 * ks + 16 * h, DR, q_bytes) : 0u)),
+                         g.qneg);
   }
 
   f32x16_t acc_o[NDB];
@@ -943,12 +956,14 @@ void fwd16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
 // fp32 inputs: same scheme with v_mfma_f32_32x32x2_f32 and unrounded fp32
 // probabilities; one block of 32 query rows per wavefront, 32-key tiles.
+// qsign = -1 for a negative scale (the query rows negated, c = |scale| log2 e).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd32_kernel(const float* __restrict__ Q,
                                                     const float* __restrict__ K,
                                                     const float* __restrict__ V,
                                                     float* __restrict__ O, float* __restrict__ LSE,
-                                                    int N, int n_qtiles, uint32_t total, float c) {
+                                                    int N, int n_qtiles, uint32_t total, float c,
+                                                    float qsign) {
   constexpr int BC = 32;
   constexpr int BR = 128;
   constexpr int KP = D + 1;  // padded K row (conflict-free column reads)
@@ -974,7 +989,7 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float* __restrict__ Q,
   float qf[D / 2];
 #pragma unroll
   for (int ks = 0; ks < D / 2; ++ks)
-    qf[ks] = (qrow < N) ? Q[head_off + (size_t)qrow * D + 2 * ks + h] : 0.0f;
+    qf[ks] = (qrow < N) ? qsign * Q[head_off + (size_t)qrow * D + 2 * ks + h] : 0.0f;
 
   f32x16_t acc_o[NDB];
 #pragma unroll
@@ -1113,7 +1128,7 @@ static hipError_t launch32(const FwdArgs& a) {
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
   hipLaunchKernelGGL((fwd32_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
-                     a.N, n_qtiles, total, a.c);
+                     a.N, n_qtiles, total, a.c, a.g.qneg ? -1.0f : 1.0f);
   return hipGetLastError();
 }
 

@@ -74,7 +74,7 @@ void fwd8_pipe_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
                       const uint8_t* __restrict__ V, const float* __restrict__ q_scale,
                       const float* __restrict__ k_scale, const float* __restrict__ v_scale, int per_block,
                       uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, uint32_t total,
-                      float c) {
+                      float c, uint32_t qneg) {
   constexpr int NT = 512;                // threads per workgroup
   constexpr int NW = NT / 64;            // wavefronts per workgroup
   constexpr int BC = 64;                 // keys per tile
@@ -146,6 +146,9 @@ void fwd8_pipe_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
 
   // Q rows as the B operand of S^T = K Q^T: 32 bytes of d per lane and k-step
   // (bytes 64 ks + 32 h .. +31), loaded once; rows past the end read zeros.
+  // A negative scale flips the codes' sign bits (qneg = 0x80808080) once
+  // they have arrived (first pass's prologue): the scores are |scale| (-q).k,
+  // c = |scale| log2 e.
   i32x8_t qf[NK8];
   {
     const rsrc_t qres = make_rsrc(Q + head_off, head_bytes);
@@ -361,6 +364,13 @@ void fwd8_pipe_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
     for (int i = 0; i < CW; ++i) *(u32x4_t*)(&sV[1][(tid + NT * i) * 8]) = u32x4_t{0u, 0u, 0u, 0u};
     load_k(0);
     wait_vmem();  // Q fragments and K_0
+    if (!exact) {
+#pragma unroll
+      for (int ks = 0; ks < NK8; ++ks) {
+        qf[ks] ^= (int32_t)qneg;
+        asm volatile("s_nop 1" : "+v"(qf[ks]));  // vector write -> inline-asm product read
+      }
+    }
     store_part(0, 0);
     load_k(1);
     wait_vmem();
@@ -471,7 +481,8 @@ static hipError_t launch8(const Fp8Args& a) {
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
   hipLaunchKernelGGL((fwd8_pipe_kernel<TR, 128, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_scale, a.k_scale,
-                     a.v_scale, a.per_block, (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c);
+                     a.v_scale, a.per_block, (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c,
+                     a.qneg ? 0x80808080u : 0u);
   return hipGetLastError();
 }
 

@@ -135,7 +135,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 128 ? 1
   const int kb = split * kps;
   const int ke = min(kb + kps, lim_blk + 1);
 
-  // Q rows of this block as B operands (column = query)
+  // Q rows of this block as B operands (column = query); their signs are
+  // flipped for a negative scale in the first tile, once the K rows (loaded
+  // after them) have arrived
   const uint32_t rsq = (uint32_t)lay.q_sr * 2;             // bytes between query rows
   const uint32_t rsc = (uint32_t)lay.c_sr * (F8 ? 1 : 2);  // bytes between cache rows
   const size_t q_head = (size_t)(b * lay.q_sb + hd * lay.q_sh + qs * lay.q_sr);  // elements
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 128 ? 1
 
   // one 32-key tile starting at key k0, staged in bv (V rows) and bk (K rows);
   // the staging registers then receive the tile starting at key kn
-  auto tile = [&](char* bv, char* bk, int k0, int kn) __attribute__((always_inline)) {
+  auto tile = [&](char* bv, char* bk, int k0, int kn, bool first) __attribute__((always_inline)) {
     // K rows -> LDS.  Own staging: the previous tile's operand reads are done
     // (they fed its S products, which come before its V writes and their
     // fence).  GRP: this buffer was last read two tiles ago, before the
@@ -243,6 +245,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 128 ? 1
     for (int i = 0; i < NCH; ++i) {
       const int ch = CST * i + tid_s;
       put(bk + (ch / VCH) * RSK + 2 * EPC * (ch % VCH), kc[i]);
+    }
+    if (first) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] = sign_flip(qf[ks], lay.qneg);
     }
     load_k(kn);
     if constexpr (GRP) {
@@ -321,9 +327,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 128 ? 1
     const int kn = k0 + 32 < ke ? k0 + 32 : k0;
     if constexpr (GRP) {
       char* bv = smem + (it & 1) * BUF;
-      tile(bv, bv + 32 * RS, k0, kn);
+      tile(bv, bv + 32 * RS, k0, kn, it == 0);
     } else {
-      tile(lds, ldk, k0, kn);
+      tile(lds, ldk, k0, kn, it == 0);
     }
   }
   l += swap_halves(l);

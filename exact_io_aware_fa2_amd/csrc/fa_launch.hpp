@@ -42,7 +42,7 @@ struct FwdArgs {
   int BH;     // batch * heads
   int N;      // sequence length (queries = keys)
   int d;      // head dimension
-  float c;    // scale * log2(e)
+  float c;    // |scale| * log2(e); a negative scale sets g.qneg
   int causal;
   int dtype;
   hipStream_t stream;
@@ -70,7 +70,7 @@ struct BwdArgs {
   int Nk;       // keys per sequence (dense: Nk = Nq)
   int d;
   float scale;
-  float c;      // scale * log2(e)
+  float c;      // scale * log2(e), of the scale's sign (no running maximum in the backward)
   int causal;
   int dtype;
   hipStream_t stream;
@@ -100,6 +100,7 @@ struct KvLayout {
   const int32_t* cu_q;  // [B + 1] or NULL
   const int32_t* cu_k;  // [B + 1] or NULL
   int64_t total_q, total_k;
+  uint32_t qneg = 0;  // 0x80008000: negative scale, the query fragments' signs flipped
 };
 
 // Queries against a key/value cache (fa_fwd_kvcache, fa_fwd_varlen).
@@ -117,7 +118,7 @@ struct KvArgs {
   int Nq;                  // queries per sequence (the largest, with prefix sums)
   int Nk;                  // cache rows per sequence (the largest, with prefix sums)
   int d;
-  float c;                 // scale * log2(e) (times the K scale of an 8-bit cache)
+  float c;                 // |scale| * log2(e) (times the K scale of an 8-bit cache)
   float v_scale;           // multiplies O: the V scale of an 8-bit cache, else 1
   int fp8_cache;           // k, v hold OCP E4M3 codes (1 byte per element)
   int one_range = 0;       // one key range per head (no workspace): the kernel writes O and LSE itself
@@ -191,7 +192,8 @@ struct Fp8Args {
   int BH;
   int N;
   int d;
-  float c;      // scale * log2(e)
+  float c;      // |scale| * log2(e)
+  bool qneg;    // negative scale: the query codes' signs flipped
   int causal;
   int dtype;    // of o and of the probabilities (DT_BF16 or DT_F16)
   hipStream_t stream;

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 9
+#define FA_ABI_VERSION 10
 
 typedef enum {
   FA_OK = 0,
@@ -67,7 +67,7 @@ typedef enum {
   FA_ERR_HEADDIM = 3,   /* d not taken by this entry point (see each one) */
   FA_ERR_DTYPE = 4,     /* unknown dtype, or a dtype this entry point does not take */
   FA_ERR_ALIGN = 5,     /* a data pointer is not 16-byte aligned */
-  FA_ERR_SCALE = 6,     /* scale is negative, NaN or infinite, or scale * log2(e) overflows */
+  FA_ERR_SCALE = 6,     /* scale is NaN or infinite, or |scale| * log2(e) overflows */
   FA_ERR_WORKSPACE = 7, /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_HIP = 8,       /* the HIP runtime rejected a launch */
   FA_ERR_SCRATCH = 9    /* fa_bwd_noalloc: the sizes need more than its static scratch */
@@ -93,7 +93,9 @@ const char* fa_status_string(int status);
  *   o        [B,H,N,d] output, same type.  Fully overwritten.
  *   lse      [B,H,N] float32 output: natural-log log-sum-exp of the scaled
  *            scores of each row over its visible keys.  Fully overwritten.
- *   scale    multiplier of q.k (normally 1/sqrt(d)); finite and >= 0.
+ *   scale    multiplier of q.k (normally 1/sqrt(d)); any finite value with
+ *            |scale| * log2(e) finite (a negative scale weights the keys of
+ *            smallest q.k most; 0 gives uniform weights over the visible keys).
  *   causal   0: every key is visible; nonzero: key j visible to query i iff j <= i.
  * The output buffers must not overlap the inputs. */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

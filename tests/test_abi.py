@@ -43,7 +43,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 9
+    assert lib.fa_abi_version() == 10
 
 
 def test_status_strings(lib):
@@ -87,10 +87,13 @@ def test_fwd_argument_errors(lib):
     assert fwd(lib, lse=P[4] + 4) == FA_ERR_ALIGN
     assert fwd(lib, scale=float("nan")) == FA_ERR_SCALE
     assert fwd(lib, scale=math.inf) == FA_ERR_SCALE
-    assert fwd(lib, scale=-0.5) == FA_ERR_SCALE
-    # finite, but scale * log2(e) overflows float32
+    assert fwd(lib, scale=-math.inf) == FA_ERR_SCALE
+    # finite, but |scale| * log2(e) overflows float32 (a negative scale is
+    # taken: softmax of scale * QK^T is defined for any finite scale)
     assert fwd(lib, scale=3.0e38) == FA_ERR_SCALE
+    assert fwd(lib, scale=-3.0e38) == FA_ERR_SCALE
     assert bwd(lib, scale=3.0e38) == FA_ERR_SCALE
+    assert bwd(lib, scale=-3.0e38) == FA_ERR_SCALE
 
 
 def test_bwd_argument_errors(lib):
@@ -145,7 +148,7 @@ def test_fp8_argument_errors(lib):
     assert f8(lib, g=2) == FA_ERR_DTYPE      # unknown scale granularity
     assert f8(lib, k=P[1] + 8) == FA_ERR_ALIGN
     assert f8(lib, qs=P[8] + 2) == FA_ERR_ALIGN
-    assert f8(lib, scale=-1.0) == FA_ERR_SCALE
+    assert f8(lib, scale=-3.0e38) == FA_ERR_SCALE
     assert f8(lib, scale=math.inf) == FA_ERR_SCALE
 
 
@@ -162,7 +165,7 @@ def test_stage_argument_errors(lib):
     assert lib.fa_bwd_dq(P[0], P[1], P[2], P[3], P[4], ws, wsb, P[5] + 2,
                          1, 2, 64, 64, 0.1, 1, 2, None) == FA_ERR_ALIGN
     assert lib.fa_bwd_dq(P[0], P[1], P[2], P[3], P[4], ws, wsb, P[5],
-                         1, 2, 64, 64, -1.0, 1, 2, None) == FA_ERR_SCALE
+                         1, 2, 64, 64, -math.inf, 1, 2, None) == FA_ERR_SCALE
     assert a
 
 
@@ -247,7 +250,7 @@ def test_kvcache_argument_errors(lib):
     assert kv(lib, dtype=7) == FA_ERR_DTYPE
     assert kv(lib, q=P[0] + 8) == FA_ERR_ALIGN
     assert kv(lib, lens=P[9] + 2) == FA_ERR_ALIGN
-    assert kv(lib, scale=-1.0) == FA_ERR_SCALE
+    assert kv(lib, scale=-3.0e38) == FA_ERR_SCALE
     assert kv(lib, scale=math.nan) == FA_ERR_SCALE
     assert kv(lib, ws=None) == FA_ERR_WORKSPACE
     need = lib.fa_fwd_kvcache_workspace_bytes(2, 4, 1, 4096, 128, 2)
@@ -293,9 +296,10 @@ def test_kvcache_fp8_argument_errors(lib):
     for bad in (0.0, -1.0, math.inf, math.nan):
         assert kv8(lib, ks=bad) == FA_ERR_SCALE
         assert kv8(lib, vs=bad) == FA_ERR_SCALE
-    assert kv8(lib, scale=-0.1) == FA_ERR_SCALE
-    # each finite, the exponent factor scale * k_scale * log2(e) is not
+    assert kv8(lib, scale=-math.inf) == FA_ERR_SCALE
+    # each finite, the exponent factor |scale| * k_scale * log2(e) is not
     assert kv8(lib, scale=1.0e20, ks=1.0e20) == FA_ERR_SCALE
+    assert kv8(lib, scale=-1.0e20, ks=1.0e20) == FA_ERR_SCALE
     assert kv(lib, scale=3.0e38) == FA_ERR_SCALE
     assert kv8(lib, ws=None) == FA_ERR_WORKSPACE
 
@@ -328,7 +332,8 @@ def test_varlen_argument_errors(lib):
     assert vl(lib, dtype=0) == FA_ERR_DTYPE
     assert vl(lib, cq=P[8] + 2) == FA_ERR_ALIGN
     assert vl(lib, o=P[3] + 8) == FA_ERR_ALIGN
-    assert vl(lib, scale=-1.0) == FA_ERR_SCALE
+    assert vl(lib, scale=-math.nan) == FA_ERR_SCALE
+    assert vl(lib, scale=-3.0e38) == FA_ERR_SCALE
     need = lib.fa_fwd_varlen_workspace_bytes(3, 4, 128, 256, 128, 2)
     assert need == lib.fa_fwd_kvcache_workspace_bytes(3, 4, 128, 256, 128, 2) > 0
     assert vl(lib, ws=None) == FA_ERR_WORKSPACE
@@ -432,6 +437,6 @@ def test_varlen_self_attention_route_checks_arguments_first(lib):
     assert vl(lib, **same, d=80) == FA_ERR_HEADDIM
     assert vl(lib, **same, dtype=0) == FA_ERR_DTYPE
     assert vl(lib, **same, o=P[3] + 8) == FA_ERR_ALIGN
-    assert vl(lib, **same, scale=-1.0) == FA_ERR_SCALE
+    assert vl(lib, **same, scale=-math.inf) == FA_ERR_SCALE
     assert vl(lib, **same, q=None) == FA_ERR_NULL
     assert vl(lib, **dict(same, tq=0)) == FA_ERR_SHAPE

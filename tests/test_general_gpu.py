@@ -85,14 +85,16 @@ def _bnhd(t):
 
 @pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_strided_bnhd_bitwise_equal_contiguous(causal, d):
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_strided_bnhd_bitwise_equal_contiguous(sign, causal, d):
     """[B, N, H, d] storage for every tensor: the general layout takes the
     same tiles in the same order as the contiguous call, so O, LSE and the
-    gradients agree bit for bit; both against the oracle."""
+    gradients agree bit for bit; both against the oracle (positive and
+    negative scales)."""
     import torch
     fa = lib()
     B, H, N = 2, 3, 700
-    scale = 1.0 / np.sqrt(d)
+    scale = sign / np.sqrt(d)
     inp = si.make_inputs(B, H, N, d, "bf16", 1.0, 9700 + d + int(causal), backward=True)
     q, k, v, do = (to_device(inp[n][1], "bf16") for n in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, causal, scale)

@@ -32,10 +32,13 @@ def rnd(rng, *shape, s=1.0):
 
 @pytest.mark.parametrize("n,d", SHAPES_TINY)
 @pytest.mark.parametrize("causal", [False, True])
-def test_forward_matches_decimal_brute_force(n, d, causal):
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_forward_matches_decimal_brute_force(n, d, causal, sign):
+    # sign -1: softmax(scale QK^T) for a negative scale, defined like any other
+    # (the weights favour the keys of smallest q.k)
     rng = np.random.default_rng(100 + 7 * n + d)
     q, k, v = rnd(rng, n, d, s=1.5), rnd(rng, n, d, s=1.5), rnd(rng, n, d)
-    scale = 1.0 / math.sqrt(d)
+    scale = sign / math.sqrt(d)
     o, lse = attention_fwd_head(q, k, v, scale, causal)
     ob, lb = brute_fwd_decimal(q, k, v, scale, causal)
     ob = np.array([[float(x) for x in r] for r in ob])
@@ -232,9 +235,10 @@ def _loss(q, k, v, do, scale, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_backward_matches_central_finite_differences(causal):
+@pytest.mark.parametrize("sc", [0.7, -0.45])
+def test_backward_matches_central_finite_differences(causal, sc):
     rng = np.random.default_rng(20 + causal)
-    n, d, sc = 6, 3, 0.7
+    n, d = 6, 3
     q, k, v, do = (rnd(rng, n, d) for _ in range(4))
     dq, dk, dv = attention_bwd_head(q, k, v, do, sc, causal)
     h = 1e-6

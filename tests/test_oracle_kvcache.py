@@ -30,12 +30,13 @@ CASES = [(1, 1, 1), (1, 5, 5), (1, 6, 3), (2, 4, 4), (3, 7, 5), (5, 8, 8), (4, 6
 
 @pytest.mark.parametrize("nq,nk,L", CASES)
 @pytest.mark.parametrize("causal", [False, True])
-def test_kvcache_matches_decimal_brute_force(nq, nk, L, causal):
+@pytest.mark.parametrize("scale", [0.7, -0.55])
+def test_kvcache_matches_decimal_brute_force(nq, nk, L, causal, scale):
     rng = np.random.default_rng(500 + 11 * nq + 3 * nk + L)
     d = 3
     q, k, v = rnd(rng, nq, d, s=1.5), rnd(rng, nk, d, s=1.5), rnd(rng, nk, d)
-    o, lse = kvcache_fwd_head(q, k, v, 0.7, causal, L)
-    ob, lb = _dec(*brute_kvcache_decimal(q, k, v, 0.7, causal, L))
+    o, lse = kvcache_fwd_head(q, k, v, scale, causal, L)
+    ob, lb = _dec(*brute_kvcache_decimal(q, k, v, scale, causal, L))
     assert np.array_equal(np.isneginf(lse), np.isneginf(lb))
     fin = np.isfinite(lb)
     assert np.max(np.abs(o - ob), initial=0.0) <= 1e-12
