@@ -52,8 +52,8 @@ KERNEL_SOURCES = {
     "kv": ["fa_kvcache.hip", "fa_common.hpp"],
     "fwd": ["fa_fwd.hip", "fa_common.hpp"],
     "prep": ["fa_bwd.hip", "fa_common.hpp"],
-    "dkdv": ["fa_bwd.hip", "fa_common.hpp"],
-    "dq": ["fa_bwd.hip", "fa_common.hpp"],
+    "dkdv": ["fa_bwd.hip", "fa_bwd_wide.hip", "fa_common.hpp"],
+    "dq": ["fa_bwd.hip", "fa_bwd_wide.hip", "fa_common.hpp"],
     "fwd8": ["fa_fwd_fp8.hip", "fa_common.hpp"],
 }
 # substrings of the mangled kernel names, as rocprofv3 reports them

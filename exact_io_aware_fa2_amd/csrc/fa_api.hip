@@ -60,8 +60,6 @@ int check_shape_bwd(int64_t B, int64_t H, int64_t N, int64_t d) {
   return FA_OK;
 }
 
-int fwd_d256(const void* q, const void* k, const void* v, void* o, float* lse, const fa::KvLayout& lay,
-             int64_t B, int64_t H, int64_t N, float scale, int causal, int dtype, void* stream);
 fa::KvLayout dense_layout(int64_t H, int64_t Nq, int64_t Nk, int64_t d);
 
 // Head dimensions the square kernels take through the general layout: 32 and
@@ -180,11 +178,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return FA_ERR_ALIGN;
   st = check_scale(scale);
   if (st != FA_OK) return st;
-  if (d == 256) {
-    // rows a wavefront reaches from a head's first row stay within 32-bit byte offsets
-    if ((N + 64) * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
-    return fwd_d256(q, k, v, o, lse, dense_layout(H, N, N, d), B, H, N, scale, causal, dtype, stream);
-  }
+  // d = 256: the rows a workgroup and its prefetch reach from a head's first
+  // row stay within 32-bit byte offsets
+  if (d == 256 && (N + 64) * d * 2 >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
 
   fa::FwdArgs a;
   a.general = padded_d(d);
@@ -355,35 +351,6 @@ fa::KvLayout dense_layout(int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
   return l;
 }
 
-// The square forward at d = 256: the split-key kernel with one key range per
-// head (no workspace), queries = keys, the square causal mask (bottom-right
-// and top-left alignment coincide for equal counts).
-int fwd_d256(const void* q, const void* k, const void* v, void* o, float* lse, const fa::KvLayout& lay,
-             int64_t B, int64_t H, int64_t N, float scale, int causal, int dtype, void* stream) {
-  fa::KvArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.seqlens = nullptr;
-  a.o = o;
-  a.lse = lse;
-  a.workspace = nullptr;
-  a.lay = lay;
-  a.lay.qneg = neg_mask(scale);
-  a.H = (int)H;
-  a.BH = (int)(B * H);
-  a.Nq = a.Nk = (int)N;
-  a.d = 256;
-  a.c = exp2_factor(scale);
-  a.v_scale = 1.0f;
-  a.fp8_cache = 0;
-  a.one_range = 1;
-  a.causal = causal != 0;
-  a.dtype = dtype;
-  a.stream = (hipStream_t)stream;
-  return fa::launch_fwd_kvcache(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
-}
-
 }  // namespace
 
 extern "C" {
@@ -523,9 +490,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu
   if (st != FA_OK) return st;
   // Self-attention (one prefix-sum array for queries and keys): the square
   // forward kernels, reading and writing the packed rows in place, when the
-  // head size is theirs and the rows a 256-row tile and its prefetch reach
-  // stay within 32-bit byte offsets of a sequence's first row.
-  if (cu_seqlens_q == cu_seqlens_k && total_q == total_k && max_q == max_k && d <= 128 &&
+  // rows a 256-row tile and its prefetch reach stay within 32-bit byte offsets
+  // of a sequence's first row.
+  if (cu_seqlens_q == cu_seqlens_k && total_q == total_k && max_q == max_k &&
       (max_q + 512) * H * d * 2 < (int64_t(1) << 31) && total_q * H <= INT32_MAX) {
     fa::FwdArgs f;
     f.q = q;
@@ -806,14 +773,6 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
   a.g.qneg = neg_mask(scale);
   fa::Strides* t[4] = {&a.g.q, &a.g.k, &a.g.v, &a.g.o};
   for (int i = 0; i < 4; ++i) *t[i] = fa::Strides{strides[3 * i], strides[3 * i + 1], strides[3 * i + 2]};
-  if (d == 256) {
-    fa::KvLayout l = dense_layout(H, N, N, d);
-    l.q_sb = strides[0], l.q_sh = strides[1], l.q_sr = strides[2];
-    l.c_sb = strides[3], l.c_sh = strides[4], l.c_sr = strides[5];
-    l.v_sb = strides[6], l.v_sh = strides[7], l.v_sr = strides[8];
-    l.o_sb = strides[9], l.o_sh = strides[10], l.o_sr = strides[11];
-    return fwd_d256(q, k, v, o, lse, l, B, H, N, scale, causal, dtype, stream);
-  }
   return status_of(fa::launch_fwd(a));
 }
 

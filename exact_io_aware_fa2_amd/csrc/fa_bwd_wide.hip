@@ -12,9 +12,10 @@
 // columns (the score products are done twice: 1.5x the algorithmic products
 // of the backward).  No software pipeline: each 32-row stage is staged
 // through LDS (two buffers, one workgroup barrier per stage) and the matrix
-// and vector work of a stage follow each other, the compiler scheduling
-// them; one workgroup of four wavefronts per compute unit (512 registers
-// per wavefront).
+// and vector work of a stage follow each other; one workgroup of four
+// wavefronts per compute unit (512 registers per wavefront, the score
+// operands and the gradient accumulators in AGPRs, the score products'
+// operands read from LDS a few products ahead).
 //
 // Layouts as in fa_bwd.hip: S (or S^T) accumulator row m of a 32-row block
 // holds row perm(m) of the staged tile, so that the transposed LDS reads of
@@ -79,6 +80,7 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const int ch = w & 1;  // gradient column half
+  using PM = PipeMma<TR, true>;  // K, V (score operands) and dK, dV (accumulators) in AGPRs
 
   const int bh = blockIdx.x / n_ktiles;
   const int k0 = (blockIdx.x % n_ktiles) * 64;
@@ -107,6 +109,7 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   f32x16_t acc_dk[4], acc_dv[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc_dk[db] = acc_dv[db] = zero16();
+  PM::copy_wait(acc_dk[0], acc_dk[1], acc_dk[2], acc_dk[3], acc_dv[0], acc_dv[1], acc_dv[2], acc_dv[3]);
 
   const int i_begin = CAUSAL ? max(0, k0 - delta) : 0;
   const int n_st = (Lq - i_begin + 31) / 32;
@@ -144,13 +147,22 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     char* st = smem + (s & 1) * STG;
     const int i0 = i_begin + 32 * s;
     if (s + 1 < n_st) load_stage(i0 + 32);
-    // S = Q K^T, dP = dO V^T (rows: queries perm(m); columns: this wavefront's keys)
-    f32x16_t sc = zero16(), dp = zero16();
-#pragma unroll
-    for (int ks = 0; ks < WKS; ++ks) {
-      sc = TR::mfma(*(const u32x4_t*)(st + rbase + 32 * ks), kf[ks], sc);
-      dp = TR::mfma(*(const u32x4_t*)(st + WBLK + rbase + 32 * ks), vf[ks], dp);
-    }
+    // S = Q K^T, dP = dO V^T (rows: queries perm(m); columns: this wavefront's
+    // keys), alternating, each A operand read from LDS four products ahead
+    f32x16_t sc, dp;
+    mma_pipeline<2 * WKS, 4>([&](int x) { return st + ((x & 1) ? WBLK : 0) + rbase + 32 * (x >> 1); },
+                             [&](int x, u32x4_t a) {
+                               const int ks = x >> 1;
+                               if (x & 1) {
+                                 if (ks == 0) dp = PM::mb0(a, vf[0]);
+                                 else PM::mb(dp, a, vf[ks]);
+                               } else {
+                                 if (ks == 0) sc = PM::mb0(a, kf[0]);
+                                 else PM::mb(sc, a, kf[ks]);
+                               }
+                             },
+                             [](int) {});
+    mfma_wait_v(sc, dp);
     // P = exp2(S c - LSE log2 e), dS = P (dP - D), masked; rounded pairs as B operands
     const float* lvec = (const float*)(st + 2 * WBLK);
     u32x4_t pk[2], dsk[2];
@@ -175,21 +187,34 @@ void bwd_dkdv_wide_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       pk[r / 8][(r / 2) % 4] = TR::pack2(p2[0], p2[1]);
       dsk[r / 8][(r / 2) % 4] = TR::pack2(ds2[0], ds2[1]);
     }
-    // dV^T += dO^T P, dK^T += Q^T dS over this wavefront's 128 columns
+    // P and dS were written by vector instructions: two wait states before
+    // the products read them
+    asm volatile("s_nop 1" : "+v"(pk[0]), "+v"(pk[1]), "+v"(dsk[0]), "+v"(dsk[1]));
+    // dV^T += dO^T P, dK^T += Q^T dS over this wavefront's 128 columns;
+    // product x: k-step t = x / 8, column block db = (x / 2) % 4, dV (x even)
+    // or dK (x odd), its transposed A operand read four products ahead
+    auto tr_a = [&](int x) __attribute__((always_inline)) -> u32x4_t {
+      const char* pq = st + tbase + 16 * (x >> 3) * WRBL + 64 * (4 * ch + ((x >> 1) & 3)) + ((x & 1) ? 0 : WBLK);
+      const u32x2_t a0 = lds_read_tr(pq), a1 = lds_read_tr(pq + 2 * WRBL);
+      return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    };
+    u32x4_t fr[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int x = 0; x < 4; ++x) fr[x] = tr_a(x);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const char* pq = st + tbase + 16 * t * WRBL + 64 * (4 * ch + db);
-        const u32x2_t a0 = lds_read_tr(pq + WBLK), a1 = lds_read_tr(pq + WBLK + 2 * WRBL);
-        acc_dv[db] = TR::mfma(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, pk[t], acc_dv[db]);
-        const u32x2_t b0 = lds_read_tr(pq), b1 = lds_read_tr(pq + 2 * WRBL);
-        acc_dk[db] = TR::mfma(u32x4_t{b0[0], b0[1], b1[0], b1[1]}, dsk[t], acc_dk[db]);
-      }
+    for (int x = 0; x < 16; ++x) {
+      const u32x4_t a = fr[x % 4];
+      if (x + 4 < 16) fr[x % 4] = tr_a(x + 4);
+      const int t = x >> 3, db = (x >> 1) & 3;
+      if (x & 1) PM::macc(acc_dk[db], a, dsk[t]);
+      else PM::macc(acc_dv[db], a, pk[t]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (s + 1 < n_st) store_stage(smem + ((s + 1) & 1) * STG);
     __syncthreads();
   }
 
+  PM::wait_acc(acc_dk[0], acc_dk[1], acc_dk[2], acc_dk[3], acc_dv[0], acc_dv[1], acc_dv[2], acc_dv[3]);
   // dK (times the scale) and dV, this wavefront's 128 columns of its 32 keys,
   // as whole rows through LDS (the stages are free after the last barrier)
   u32x2_t ok[4][4], ov[4][4];
@@ -228,6 +253,7 @@ void bwd_dq_wide_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const int ch = w & 1;
+  using PM = PipeMma<TR, true>;  // Q, dO (score operands) and dQ (accumulators) in AGPRs
 
   const int bh = blockIdx.x / n_qtiles;
   int qt = blockIdx.x % n_qtiles;
@@ -261,6 +287,7 @@ void bwd_dq_wide_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   f32x16_t acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = zero16();
+  PM::copy_wait(acc[0], acc[1], acc[2], acc[3]);
 
   const int kv_end = CAUSAL ? min(Lk, q0 + 64 + delta) : Lk;
   const int n_st = kv_end > 0 ? (kv_end + 31) / 32 : 0;
@@ -284,13 +311,22 @@ void bwd_dq_wide_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       lk_.load(kres, tk.rs, j0 + 32, tid);
       lv_.load(vres, tv.rs, j0 + 32, tid);
     }
-    // S^T = K Q^T, dP^T = V dO^T (rows: keys perm(m); columns: this wavefront's queries)
-    f32x16_t sc = zero16(), dp = zero16();
-#pragma unroll
-    for (int ks = 0; ks < WKS; ++ks) {
-      sc = TR::mfma(*(const u32x4_t*)(st + rbase + 32 * ks), qf[ks], sc);
-      dp = TR::mfma(*(const u32x4_t*)(st + WBLK + rbase + 32 * ks), of[ks], dp);
-    }
+    // S^T = K Q^T, dP^T = V dO^T (rows: keys perm(m); columns: this
+    // wavefront's queries), alternating, A operands read four products ahead
+    f32x16_t sc, dp;
+    mma_pipeline<2 * WKS, 4>([&](int x) { return st + ((x & 1) ? WBLK : 0) + rbase + 32 * (x >> 1); },
+                             [&](int x, u32x4_t a) {
+                               const int ks = x >> 1;
+                               if (x & 1) {
+                                 if (ks == 0) dp = PM::mb0(a, of[0]);
+                                 else PM::mb(dp, a, of[ks]);
+                               } else {
+                                 if (ks == 0) sc = PM::mb0(a, qf[0]);
+                                 else PM::mb(sc, a, qf[ks]);
+                               }
+                             },
+                             [](int) {});
+    mfma_wait_v(sc, dp);
     u32x4_t dsk[2];
     const int thr = qrow + delta - j0 - h;  // causal: key j0 + koff(r) visible iff koff(r) <= thr
 #pragma unroll
@@ -309,16 +345,27 @@ void bwd_dq_wide_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       }
       dsk[r / 8][(r / 2) % 4] = TR::pack2(ds2[0], ds2[1]);
     }
+    // dS was written by vector instructions: two wait states before the
+    // products read it
+    asm volatile("s_nop 1" : "+v"(dsk[0]), "+v"(dsk[1]));
     // dQ^T += K^T dS^T over this wavefront's 128 columns (keys past the end
-    // are zero rows of K: their dS adds nothing)
+    // are zero rows of K: their dS adds nothing); product x: k-step x / 4,
+    // column block x % 4, its transposed A operand read four products ahead
+    auto tr_a = [&](int x) __attribute__((always_inline)) -> u32x4_t {
+      const char* pk = st + tbase + 16 * (x >> 2) * WRBL + 64 * (4 * ch + (x & 3));
+      const u32x2_t a0 = lds_read_tr(pk), a1 = lds_read_tr(pk + 2 * WRBL);
+      return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    };
+    u32x4_t fr[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int x = 0; x < 4; ++x) fr[x] = tr_a(x);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const char* pk = st + tbase + 16 * t * WRBL + 64 * (4 * ch + db);
-        const u32x2_t a0 = lds_read_tr(pk), a1 = lds_read_tr(pk + 2 * WRBL);
-        acc[db] = TR::mfma(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, dsk[t], acc[db]);
-      }
+    for (int x = 0; x < 8; ++x) {
+      const u32x4_t a = fr[x % 4];
+      if (x + 4 < 8) fr[x % 4] = tr_a(x + 4);
+      PM::macc(acc[x & 3], a, dsk[x >> 2]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (s + 1 < n_st) {
       char* nx = smem + ((s + 1) & 1) * STG;
       lk_.store(nx, tid);
@@ -327,6 +374,7 @@ void bwd_dq_wide_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     __syncthreads();
   }
 
+  PM::wait_acc(acc[0], acc[1], acc[2], acc[3]);
   u32x2_t od[4][4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)

@@ -170,6 +170,7 @@ struct F16 {
 // operands so that no access moves above the wait.  Back-to-back
 // accumulation into the same registers needs no wait states.
 #define FA_MFMA_WAIT "s_nop 7\n\ts_nop 7\n\ts_nop 4"
+__device__ __forceinline__ void mfma_wait_v(f32x16_t& a) { asm volatile(FA_MFMA_WAIT : "+v"(a)); }
 __device__ __forceinline__ void mfma_wait_v(f32x16_t& a, f32x16_t& b) {
   asm volatile(FA_MFMA_WAIT : "+v"(a), "+v"(b));
 }
@@ -228,6 +229,12 @@ struct PipeMma {
   __device__ static inline void wait_acc(f32x16_t& a, f32x16_t& b, f32x16_t& c, f32x16_t& d,
                                          f32x16_t& e, f32x16_t& f, f32x16_t& g, f32x16_t& h) {
     if constexpr (AG) mfma_wait_a(a, b, c, d, e, f, g, h); else mfma_wait_v(a, b, c, d, e, f, g, h);
+  }
+  // Two wait states between a vector write of an mb* B operand (in AGPRs
+  // with AG) and the products that read it (see valu_to_mfma_wait).
+  __device__ static inline void operand_wait(u32x4_t& x) {
+    if constexpr (AG) asm volatile("s_nop 1" : "+a"(x));
+    else asm volatile("s_nop 1" : "+v"(x));
   }
   // Two wait states between vector writes of macc accumulators (register
   // copies the compiler places where control flow joins) and products that

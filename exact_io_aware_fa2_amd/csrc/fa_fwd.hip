@@ -66,8 +66,10 @@ constexpr float kSumMax = 32768.0f;
 // probability is then at most 1).  So the steady state never re-bases O.
 //
 // Staging (all threads): iteration j writes K_{j+2} and V_j to LDS from
-// registers loaded during iteration j-1, then requests K_{j+3} and V_{j+1}.
-// Iteration j reads K_{j+1} and V_{j-1}, so two buffers of each suffice.
+// registers loaded during iteration j-1, then requests K_{j+3} and V_{j+1}
+// (d = 256: from registers loaded during iteration j-2, then requests K_{j+4}
+// and V_{j+2} into the same registers).  Iteration j reads K_{j+1} and
+// V_{j-1}, so two buffers of each suffice.
 //
 // LDS layouts (per buffer):
 //   K: row-major, rows padded to D + 8 elements, so 16 consecutive rows read
@@ -80,16 +82,23 @@ constexpr float kSumMax = 32768.0f;
 //      staging writes (lanes CW columns apart) and the fragment reads (lanes
 //      on consecutive columns) both hit distinct banks.
 //
-// All matrix operands and accumulators live in VGPRs (the MfmaAsm forms).
+// d <= 128: all matrix operands and accumulators live in VGPRs (the MfmaAsm
+// forms), two wavefronts per SIMD.  d = 256: one wavefront per SIMD (4 per
+// workgroup, 128 rows), with the Q fragments (B operands of S) and the O
+// accumulators in AGPRs (PipeMma with AG), 32-key tiles.
 template <class TR, int D, int BC, int QB, bool CAUSAL, bool GL>
-__global__ __launch_bounds__(512 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB, 3 - QB)))
+__global__ __launch_bounds__(D > 128 ? 256 : 512 / QB)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 3 - QB, D > 128 ? 1 : 3 - QB)))
 void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                   float* __restrict__ LSE, int N, int n_qtiles, uint32_t total, float c, GenLayout g) {
-  // QB: 32-row query blocks per wavefront (2: one wavefront per SIMD, 1: two)
-  constexpr int NT = 512 / QB;          // threads per workgroup
+  // QB: 32-row query blocks per wavefront (2: one wavefront per SIMD, 1: two;
+  // d = 256: 1 at one wavefront per SIMD)
+  constexpr bool AG = D > 128;          // Q and O in AGPRs
+  using PM = PipeMma<TR, AG>;
+  constexpr int NT = AG ? 256 : 512 / QB;  // threads per workgroup
   constexpr int NW = NT / 64;           // wavefronts per workgroup
-  constexpr int BR = NW * 32 * QB;      // query rows per workgroup (256)
+  constexpr int BR = NW * 32 * QB;      // query rows per workgroup (256; 128 at d = 256)
   constexpr int KS = D + 8;             // padded K row (elements)
   constexpr int NKB = BC / 32;          // 32-key blocks per tile
   constexpr int NDB = D / 32;           // 32-column blocks of the output
@@ -188,8 +197,13 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   // are masked, their values multiplied by zero probabilities).
   const rsrc_t kres = make_rsrc(K + k_off, k_bytes);
   const rsrc_t vres = make_rsrc(V + v_off, v_bytes);
-  u32x4_t stk[NKC];
-  uint32_t stv[8][CW / 2];
+  // Staging register sets.  Two at d = 256, where one wavefront per SIMD
+  // leaves no partner to run while a wavefront waits: each iteration then
+  // writes data loaded two iterations earlier, so a load has two
+  // iterations, not one, to arrive.
+  constexpr int NSET = AG ? 2 : 1;
+  u32x4_t stk[NSET][NKC];
+  uint32_t stv[NSET][8][CW / 2];
   // K: chunk tid + NT r -> row (tid / KCH) + (NT / KCH) r, 16-byte column tid % KCH
   const uint32_t koff = (uint32_t)(tid / KCH) * rsk + (tid % KCH) * 16 +
                         (GL ? col_pad((tid % KCH) * 16, DR, k_bytes) : 0u);
@@ -203,34 +217,34 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   const int vrow = (2 * vs + vh) * D * 8;
   const int vsw = (CW * vc) ^ ((CW * vc >> 3) & 3);  // swizzled slot of column CW vc (+ cc: xor)
 
-  auto load_k = [&](int tile) {
+  auto load_k = [&](int tile, int set = 0) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < NKC; ++r)
-      stk[r] = buf_load16(kres, koff + (uint32_t)(tile * BC + (NT / KCH) * r) * row_stride_k());
+      stk[set][r] = buf_load16(kres, koff + (uint32_t)(tile * BC + (NT / KCH) * r) * row_stride_k());
   };
-  auto load_v = [&](int tile) {
+  auto load_v = [&](int tile, int set = 0) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const uint32_t off = voff + (uint32_t)(tile * BC + 8 * (k / 4) + (k % 4)) * row_stride_v();
       if constexpr (CW == 4) {
         const u32x2_t x = buf_load8(vres, off);
-        stv[k][0] = x[0];
-        stv[k][1] = x[1];
+        stv[set][k][0] = x[0];
+        stv[set][k][1] = x[1];
       } else {
-        stv[k][0] = __builtin_amdgcn_raw_buffer_load_b32(vres, off, 0, 0);
+        stv[set][k][0] = __builtin_amdgcn_raw_buffer_load_b32(vres, off, 0, 0);
       }
     }
   };
-  // staging write number i (0 <= i < NKC + CW) into buffer b
-  auto store_part = [&](int i, int b) __attribute__((always_inline)) {
+  // staging write number i (0 <= i < NKC + CW) into buffer b, from register set `set`
+  auto store_part = [&](int i, int b, int set = 0) __attribute__((always_inline)) {
     if (i < NKC) {
-      *(u32x4_t*)(&sK[b][kst + i * (NT / KCH) * KS]) = stk[i];
+      *(u32x4_t*)(&sK[b][kst + i * (NT / KCH) * KS]) = stk[set][i];
     } else {
       const int cc = i - NKC;  // column within the group
       uint32_t o[4];
 #pragma unroll
       for (int kp = 0; kp < 4; ++kp) {
-        const uint32_t x0 = stv[2 * kp][cc / 2], x1 = stv[2 * kp + 1][cc / 2];
+        const uint32_t x0 = stv[set][2 * kp][cc / 2], x1 = stv[set][2 * kp + 1][cc / 2];
         o[kp] = (cc & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
       }
       *(u32x4_t*)(&sV[b][vrow + 8 * (vsw ^ cc)]) = u32x4_t{o[0], o[1], o[2], o[3]};
@@ -273,16 +287,17 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   // of a hazard wait (matrix result -> vector access).
   auto wait_scores = [&](f32x16_t (&sc)[QB][NKB]) __attribute__((always_inline)) {
     f32x16_t* x = &sc[0][0];  // QB * NKB blocks
-    static_assert(QB * NKB == 2 || QB * NKB == 4, "operand list below");
-    if constexpr (QB * NKB == 2) mfma_wait_v(x[0], x[1]);
+    static_assert(QB * NKB == 1 || QB * NKB == 2 || QB * NKB == 4, "operand list below");
+    if constexpr (QB * NKB == 1) mfma_wait_v(x[0]);
+    else if constexpr (QB * NKB == 2) mfma_wait_v(x[0], x[1]);
     else mfma_wait_v(x[0], x[1], x[2], x[3]);
   };
   auto wait_acc = [&]() __attribute__((always_inline)) {
     f32x16_t* x = &acc[0][0];  // QB * NDB blocks
     static_assert(QB * NDB == 2 || QB * NDB == 4 || QB * NDB == 8, "operand list below");
-    if constexpr (QB * NDB == 2) mfma_wait_v(x[0], x[1]);
-    else if constexpr (QB * NDB == 4) mfma_wait_v(x[0], x[1], x[2], x[3]);
-    else mfma_wait_v(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+    if constexpr (QB * NDB == 2) PM::wait_acc(x[0], x[1]);
+    else if constexpr (QB * NDB == 4) PM::wait_acc(x[0], x[1], x[2], x[3]);
+    else PM::wait_acc(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
   };
 
   bool rerun = false;
@@ -377,17 +392,29 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
         for (int k = 0; k < 4; ++k)
           if (i * NS / NPAIR + k == st) stage(i, k);
       // staging: writes of K_{j+2} and V_j, then requests for K_{j+3}, V_{j+1}
-      if (st == kStg0) wait_vmem();
-      if (st >= kStg0 && st < kLoad && (st - kStg0) % 2 == 0) store_part((st - kStg0) / 2, WR);
-      if (st == kLoad) {
-        load_k(j + 3);
-        load_v(j + 1);
+      if constexpr (NSET == 1) {
+        if (st == kStg0) wait_vmem();
+        if (st >= kStg0 && st < kLoad && (st - kStg0) % 2 == 0) store_part((st - kStg0) / 2, WR);
+        if (st == kLoad) {
+          load_k(j + 3);
+          load_v(j + 1);
+        }
+      } else {
+        // set PAR holds K_{j+2} and V_j (loaded two iterations ago; the
+        // compiler waits for exactly those loads) and then receives K_{j+4},
+        // V_{j+2}
+        if (st >= kStg0 && st < kLoad && (st - kStg0) % 2 == 0) store_part((st - kStg0) / 2, WR, PAR);
+        if (st == kLoad) {
+          load_k(j + 4, PAR);
+          load_v(j + 2, PAR);
+        }
       }
     };
 
     // matrix instructions: fragment f (even: V fragment of O += V^T P, odd:
     // K fragment of S) feeds QB products; operand reads run kAhead fragments
-    // ahead.  Steps past NS only finish the softmax pipeline.
+    // ahead (at d = 256, 8 ahead measured no faster).  Steps past NS only
+    // finish the softmax pipeline.
     constexpr int kAhead = 3;
     constexpr int NF = NQF + NVF;
     auto is_pv = [](int f) { return (f & 1) == 0; };
@@ -407,11 +434,11 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
         constexpr int i = fidx(f);
         if constexpr (is_pv(f)) {
           constexpr int ss = i / NDB, db = i % NDB;
-          TR::mma(acc[qb][db], a, pfrag(p_prev, qb, ss));
+          PM::macc(acc[qb][db], a, pfrag(p_prev, qb, ss));
         } else {
           constexpr int kb = i % NKB, ks = i / NKB;
-          if constexpr (ks == 0) s_next[qb][kb] = TR::mma0(a, qf[qb][ks]);
-          else TR::mma(s_next[qb][kb], a, qf[qb][ks]);
+          if constexpr (ks == 0) s_next[qb][kb] = PM::mb0(a, qf[qb][ks]);
+          else PM::mb(s_next[qb][kb], a, qf[qb][ks]);
         }
       }
       valu(st);
@@ -455,7 +482,7 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           qf[qb][ks] = sign_flip(qf[qb][ks], g.qneg);
-          valu_to_mfma_wait(qf[qb][ks]);
+          PM::operand_wait(qf[qb][ks]);
         }
     }
   #pragma unroll
@@ -470,13 +497,17 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
                            const int kb = i % NKB, ks = i / NKB;
   #pragma unroll
                            for (int qb = 0; qb < QB; ++qb) {
-                             if (ks == 0) sA[qb][kb] = TR::mma0(a, qf[qb][ks]);
-                             else TR::mma(sA[qb][kb], a, qf[qb][ks]);
+                             if (ks == 0) sA[qb][kb] = PM::mb0(a, qf[qb][ks]);
+                             else PM::mb(sA[qb][kb], a, qf[qb][ks]);
                            }
                          },
                          [](int) {});
     load_k(2);
     load_v(0);
+    if constexpr (NSET == 2) {
+      load_k(3, 1);
+      load_v(1, 1);
+    }
     lds_barrier();  // every wave is done with K_0 before iteration 0 overwrites it
 
     // Tiles are processed in pairs (the two register sets), over an even number
@@ -504,7 +535,7 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
                          [&](int i, u32x4_t a) {
                            const int ss = i / NDB, db = i % NDB;
   #pragma unroll
-                           for (int qb = 0; qb < QB; ++qb) TR::mma(acc[qb][db], a, pfrag(pB, qb, ss));
+                           for (int qb = 0; qb < QB; ++qb) PM::macc(acc[qb][db], a, pfrag(pB, qb, ss));
                          },
                          [](int) {});
   };
@@ -531,9 +562,9 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
       for (int k0 = 0; k0 < kend; k0 += 32) {
         const uint32_t ko = (uint32_t)(k0 + l32) * rsk + 16 * h;
         auto kpad = [&](int ks) -> uint32_t { return GL ? col_pad(32 * ks + 16 * h, DR, k_bytes) : 0u; };
-        f32x16_t sc = TR::mma0(buf_load16(kres, ko + kpad(0)), qf[qb][0]);
+        f32x16_t sc = PM::mb0(buf_load16(kres, ko + kpad(0)), qf[qb][0]);
 #pragma unroll
-        for (int ks = 1; ks < NKS; ++ks) TR::mma(sc, buf_load16(kres, ko + 32 * ks + kpad(ks)), qf[qb][ks]);
+        for (int ks = 1; ks < NKS; ++ks) PM::mb(sc, buf_load16(kres, ko + 32 * ks + kpad(ks)), qf[qb][ks]);
         f32x16_t sc2 = sc;
         mfma_wait_v(sc, sc2);
 #pragma unroll
@@ -1086,13 +1117,17 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float* __restrict__ Q,
 
 // ------------------------------------------------------------------ launch
 
-template <class TR, bool CAUSAL, bool GL>
-static void launch_pipe_gl(const FwdArgs& a) {  // d = 128 (and d = 96 in the general layout)
-  constexpr int BR = 256;
+// d = 128 (and d = 96 in the general layout): 256 rows and 64-key tiles per
+// workgroup of 8 wavefronts; d = 256: 128 rows and 32-key tiles per workgroup
+// of 4 (one wavefront per SIMD).
+template <class TR, int D, bool CAUSAL, bool GL>
+static void launch_pipe_gl(const FwdArgs& a) {
+  constexpr int BR = D > 128 ? 128 : 256;
+  constexpr int BC = D > 128 ? 32 : 64;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const uint32_t total = (uint32_t)(n_qtiles * a.BH);
-  hipLaunchKernelGGL((fwd16_pipe_kernel<TR, 128, 64, 1, CAUSAL, GL>), dim3(total), dim3(512), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+  hipLaunchKernelGGL((fwd16_pipe_kernel<TR, D, BC, 1, CAUSAL, GL>), dim3(total), dim3(D > 128 ? 256 : 512), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c, a.g);
 }
 
@@ -1110,8 +1145,13 @@ static void launch_pp_gl(const FwdArgs& a) {  // d = 64 (and d = 32 in the gener
 
 template <class TR, bool CAUSAL>
 static hipError_t launch_pipe(const FwdArgs& a) {
-  if (a.general) launch_pipe_gl<TR, CAUSAL, true>(a);
-  else launch_pipe_gl<TR, CAUSAL, false>(a);
+  if (a.d > 128) {
+    if (a.general) launch_pipe_gl<TR, 256, CAUSAL, true>(a);
+    else launch_pipe_gl<TR, 256, CAUSAL, false>(a);
+  } else {
+    if (a.general) launch_pipe_gl<TR, 128, CAUSAL, true>(a);
+    else launch_pipe_gl<TR, 128, CAUSAL, false>(a);
+  }
   return hipGetLastError();
 }
 
@@ -1134,8 +1174,8 @@ static hipError_t launch32(const FwdArgs& a) {
 
 template <class TR>
 static hipError_t dispatch16(const FwdArgs& a) {
-  // the kernel's width: d = 128 and 96 (general layout, zero columns) on the
-  // d = 128 kernel, d = 64 and 32 on the d = 64 kernel
+  // the kernel's width: d = 256 and 128 (and 96: general layout, zero
+  // columns) on the pipelined kernel, d = 64 and 32 on the d = 64 kernel
   if (a.d > 64) return a.causal ? launch_pipe<TR, true>(a) : launch_pipe<TR, false>(a);
   return a.causal ? launch_pp<TR, true>(a) : launch_pp<TR, false>(a);
 }

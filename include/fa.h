@@ -28,7 +28,8 @@
  *              any strides).  lse: contiguous [B, H, N] float32.  Head
  *              dimension d: 32, 64, 96, 128 or 256 for 16-bit types (32 and
  *              96 run on the 64 / 128 kernels with the missing columns read
- *              as zeros, 256 on kernels of its own); 64 or 128 for float32.
+ *              as zeros; the backward runs 256 on kernels of its own); 64
+ *              or 128 for float32.
  *   Memory     All data pointers are DEVICE pointers owned by the caller.  The
  *              library allocates no device memory and keeps no pointer after a
  *              call returns.  Every tensor pointer must be 16-byte aligned
@@ -88,8 +89,9 @@ const char* fa_status_string(int status);
  * "Technische Architektur und Funktionsprinzipien": one workgroup per query
  * tile and head, rows split across wavefronts, one normalisation at the end).
  *   q, k, v  [B,H,N,d] inputs of type dtype (FA_F32, FA_F16 or FA_BF16);
- *            d = 32, 64, 96, 128, 256 (FA_F32: 64, 128).  At d = 256 the
- *            split-key kernel runs with one key range per head.
+ *            d = 32, 64, 96, 128, 256 (FA_F32: 64, 128; at 256 N + 64 <=
+ *            2^22).  d = 256 runs the pipelined d = 128 scheme at one
+ *            wavefront per SIMD (Q and O in accumulation registers).
  *   o        [B,H,N,d] output, same type.  Fully overwritten.
  *   lse      [B,H,N] float32 output: natural-log log-sum-exp of the scaled
  *            scores of each row over its visible keys.  Fully overwritten.
@@ -252,11 +254,11 @@ int fa_fwd_kvcache_fp8(const void* q, const void* k_cache, const void* v_cache, 
  *   workspace     fa_fwd_varlen_workspace_bytes(B, H, max_q, max_k, d, dtype)
  *                 bytes (16-byte aligned, may be NULL when that is 0).
  * When cu_seqlens_q and cu_seqlens_k are the same pointer (self-attention:
- * equal query and key counts), total_q = total_k, max_q = max_k, d is at
- * most 128 and (max_q + 512) * H * d * 2 < 2^31, fa_fwd's kernels run on the
- * packed rows in place and the workspace is not used; otherwise the
- * split-key kernels of fa_fwd_kvcache do.  d: 32, 64, 128, 256, and 96 on the
- * self-attention route only.
+ * equal query and key counts), total_q = total_k, max_q = max_k and
+ * (max_q + 512) * H * d * 2 < 2^31, fa_fwd's kernels run on the packed rows
+ * in place and the workspace is not used; otherwise the split-key kernels of
+ * fa_fwd_kvcache do.  d: 32, 64, 128, 256, and 96 on the self-attention
+ * route only.
  * Errors as for fa_fwd_kvcache (FA_ERR_NULL also for NULL prefix sums,
  * FA_ERR_SHAPE for total_q or total_k < 1 or the offset limit). */
 size_t fa_fwd_varlen_workspace_bytes(int64_t B, int64_t H, int64_t max_q, int64_t max_k, int64_t d,

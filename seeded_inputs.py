@@ -91,6 +91,7 @@ WORKLOADS = {
     # backward bf16 causal with recompute (and its d=128 variant)
     "C5": Workload("C5", 8, 16, 4096, 64, "bf16", True, 1.0, 1005, backward=True),
     "C5d128": Workload("C5d128", 8, 16, 4096, 128, "bf16", True, 1.0, 1005, backward=True),
+    "C5d256": Workload("C5d256", 8, 16, 4096, 256, "bf16", True, 1.0, 1005, backward=True),
 }
 
 # the forward on 8-bit inputs: C3's and C2's draws quantised to E4M3 with one

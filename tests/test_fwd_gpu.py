@@ -148,13 +148,14 @@ def test_large_scores_stay_finite_and_pick_the_max_key():
     assert_fwd_ok(err, "bf16", "x30 queries")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_growing_scores_update_the_reference_maximum(d, causal):
     """Keys scaled up 6x along the sequence: later key tiles hold row maxima far
     above the first tile's (by more than the kernels' tile-sum bound allows),
     so the reference maximum must be raised (d = 64: the tile is re-based;
-    d = 128: the pass is redone against exact maxima).  Result as the oracle."""
+    d = 128, 256: the pass is redone against exact maxima).  Result as the
+    oracle."""
     N = 600
     inp = si.make_inputs(1, 2, N, d, "bf16", 1.0, 17 + d)
     grow = (1.0 + 5.0 * np.arange(N) / N)[None, None, :, None]

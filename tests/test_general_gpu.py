@@ -177,8 +177,9 @@ def test_strided_shared_kv_heads():
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 17, 255, 257, 1000])
 def test_head_dim_256_fwd(N, causal, dtype):
-    """d = 256 (fa_fwd runs the split-key kernel with one key range per
-    head: no workspace) against the oracle."""
+    """d = 256 (fa_fwd runs the pipelined kernel at one wavefront per
+    SIMD, Q and O in AGPRs, 128-row tiles and 32-key tiles) against the
+    oracle."""
     import torch
     fa = lib()
     d = 256
@@ -230,6 +231,17 @@ def test_head_dim_256_several_tiles_strided_and_varlen():
         assert np.array_equal(np.isneginf(lg), ~fin), "queries that see no key: LSE = -inf"
         err = fwd_errors(vo.float().cpu().numpy(), np.where(fin, lg, 0), o_ref, np.where(fin, l_ref, 0))
         assert_fwd_ok(err, "bf16", f"d256 varlen causal={causal}")
+    # packed self-attention (one prefix-sum array): the square kernel in place
+    ls = [300, 1, 129, 700]
+    sl = si.make_varlen_inputs(ls, ls, 2, d, "bf16", 1.0, 9998)
+    sq, sk, sv = (to_device(sl[n][1], "bf16") for n in ("q", "k", "v"))
+    cs = torch.from_numpy(sl["cu_q"]).cuda()
+    for causal in (False, True):
+        so, slse = fa.fwd_varlen(sq, sk, sv, cs, cs, max(ls), max(ls), causal, scale)
+        torch.cuda.synchronize()
+        o_ref, l_ref = varlen_fwd(sl["q"][0], sl["k"][0], sl["v"][0], sl["cu_q"], sl["cu_k"], scale, causal)
+        assert_fwd_ok(fwd_errors(so.float().cpu().numpy(), slse.cpu().numpy(), o_ref, l_ref), "bf16",
+                      f"d256 packed self-attention causal={causal}")
     # decode against a cache (key ranges + merge)
     kv = si.make_kvcache_inputs(2, 2, 1, 3000, d, "bf16", 1.0, 9997, 0.5)
     kq, kk, kvv = (to_device(kv[n][1], "bf16") for n in ("q", "k", "v"))

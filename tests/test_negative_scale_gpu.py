@@ -234,7 +234,7 @@ def test_fp8_forward_negative_scale(causal, gran):
                          f"fp8 {gran} causal={causal}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_growing_scores_negative_scale(d, causal):
     """Keys scaled up 6x along the sequence: the row maxima of -|s| q.k grow
