@@ -565,8 +565,7 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
         f32x16_t sc = PM::mb0(buf_load16(kres, ko + kpad(0)), qf[qb][0]);
 #pragma unroll
         for (int ks = 1; ks < NKS; ++ks) PM::mb(sc, buf_load16(kres, ko + 32 * ks + kpad(ks)), qf[qb][ks]);
-        f32x16_t sc2 = sc;
-        mfma_wait_v(sc, sc2);
+        mfma_wait_v(sc);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 8 * (r / 4) + 4 * h + (r % 4);

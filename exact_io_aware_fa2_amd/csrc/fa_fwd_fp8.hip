@@ -428,8 +428,7 @@ void fwd8_pipe_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__
 #pragma unroll
       for (int ks = 1; ks < NK8; ++ks)
         mma8(sc, cat8(buf_load16(kres, ko + 64 * ks), buf_load16(kres, ko + 64 * ks + 16)), qf[ks], one);
-      f32x16_t sc2 = sc;
-      mfma_wait_v(sc, sc2);
+      mfma_wait_v(sc);
       const float ck = ctile(k0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {

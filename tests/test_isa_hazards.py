@@ -1,13 +1,17 @@
 """Static checks of the gfx950 assembly the library's sources compile to.
 
 The kernels issue most matrix products through inline assembly, which the
-compiler's hazard tracking does not look into.  Results are guarded in the
-sources (21 wait states before a vector read of a product); this test
-checks the other direction in the built code: no vector-ALU instruction
-writes a register that a matrix instruction then reads within fewer than two
-wait states (each instruction counts one, ``s_nop n`` counts n + 1).  It also
-checks that no packed fp32 vector instruction was emitted (the build turns
-the feature off).
+compiler's hazard tracking does not look into, so the built code is checked
+for both directions:
+- no vector-ALU instruction writes a register that a matrix instruction then
+  reads within fewer than two wait states;
+- no instruction other than a matrix product reads the result of an
+  inline-assembly product within fewer than 18 wait states (the sources
+  place 21; compiler-selected products are left to the compiler's own
+  tracking) before the result is overwritten.
+Each instruction counts one wait state, ``s_nop n`` counts n + 1 and an
+intervening matrix product 8.  It also checks that no packed fp32 vector
+instruction was emitted (the build turns the feature off).
 
 CPU only: compiles every source with the library's own flags and
 ``--cuda-device-only -S`` (about a minute on 8 cores).
@@ -36,14 +40,21 @@ def _regs(tok: str) -> set[str]:
     return {f"{m.group(4)}{m.group(5)}"}
 
 
-def _instructions(body: str):
+def _instructions(body: str, with_asm: bool = False):
+    in_asm = False
     for line in body.split("\n"):
+        if ";;#ASMSTART" in line:
+            in_asm = True
+            continue
+        if ";;#ASMEND" in line:
+            in_asm = False
+            continue
         s = line.split(";")[0].strip()
         if not s or s.startswith(".") or s.endswith(":"):
             continue
         parts = s.split(None, 1)
         ops = [o.strip() for o in parts[1].split(",")] if len(parts) > 1 else []
-        yield parts[0], ops
+        yield (parts[0], ops, in_asm) if with_asm else (parts[0], ops)
 
 
 def _is_vector_write(op: str) -> bool:
@@ -77,6 +88,37 @@ def hazards(asm: str):
     return found
 
 
+def result_hazards(asm: str, need: int = 18):
+    """(kernel, product, reader, wait states) for each read of an inline-assembly
+    product's result by a non-product instruction within `need` wait states."""
+    found = []
+    for m in re.finditer(r"^(_ZN2fa\S+):", asm, re.M):
+        start = m.end()
+        end = asm.find(".Lfunc_end", start)
+        insts = list(_instructions(asm[start:end], with_asm=True))
+        for i, (op, ops, in_asm) in enumerate(insts):
+            if "mfma" not in op or not ops or not in_asm:
+                continue
+            dst = _regs(ops[0])
+            ws = 0
+            for op2, ops2, _ in insts[i + 1:i + 40]:
+                if op2.startswith(("s_cbranch", "s_branch")) or op2 == "s_barrier":
+                    break
+                if "mfma" in op2:
+                    if ops2 and dst & _regs(ops2[0]):
+                        break  # accumulated into or overwritten by a later product
+                    ws += 8
+                else:
+                    src = set().union(*(_regs(t) for t in ops2[1:])) if len(ops2) > 1 else set()
+                    if dst & src:
+                        found.append((m.group(1), op, f"{op2} {','.join(ops2[:2])}", ws))
+                        break
+                    ws += int(ops2[0], 0) + 1 if op2 == "s_nop" else 1
+                if ws >= need:
+                    break
+    return found
+
+
 @pytest.fixture(scope="module")
 def assembly():
     try:
@@ -106,6 +148,21 @@ def test_scan_catches_a_planted_hazard():
     assert hazards(spaced) == []
     one = planted.replace("\tv_mfma", "\ts_waitcnt lgkmcnt(0)\n\tv_mfma")
     assert [h[3] for h in hazards(one)] == [1]
+
+
+def test_scan_catches_an_early_result_read():
+    planted = ("_ZN2fa1xEv:\n\t;;#ASMSTART\n\tv_mfma_f32_32x32x16_bf16 a[16:31], v[0:3], v[4:7], a[16:31]\n"
+               "\t;;#ASMEND\n\ts_nop 6\n\tv_accvgpr_mov_b32 a207, a31\n.Lfunc_end0:\n")
+    assert [h[3] for h in result_hazards(planted)] == [7]
+    assert result_hazards(planted.replace("s_nop 6", "s_nop 7\n\ts_nop 7\n\ts_nop 4")) == []
+    # a compiler-selected product (no asm markers) is the compiler's to guard
+    assert result_hazards(planted.replace(";;#ASMSTART", ";").replace(";;#ASMEND", ";")) == []
+
+
+def test_no_early_read_of_a_product_result(assembly):
+    bad = {src: result_hazards(asm) for src, asm in assembly.items()}
+    bad = {k: v for k, v in bad.items() if v}
+    assert not bad, bad
 
 
 def test_no_vector_write_feeds_a_product_too_early(assembly):
