@@ -68,7 +68,7 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
                            const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                            const float* __restrict__ LSE, const float* __restrict__ Dvec,
                            uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Nq, int Nk, int n_ktiles,
-                           float c, float neg_inv_scale, float scale, GenLayout g) {
+                           uint32_t total,                           float c, float neg_inv_scale, float scale, GenLayout g) {
   constexpr int NT = 256;
   constexpr int OFF_V = 2 * WBLK;            // -LSE / s (32 floats), then -D (32 floats)
   constexpr int STG = OFF_V + 2 * 32 * 4;    // one stage slot
@@ -82,6 +82,8 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
   using PM = PipeMma<TR, true>;  // K, V (score operands) and dK, dV (accumulators) in AGPRs
   __shared__ __attribute__((aligned(16))) char smem[4 * STG];
 
+  // tiles of one head run on one XCD and share its L2
+  const uint32_t lid = xcd_remap(blockIdx.x, total);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -90,8 +92,8 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
   const int ch = w & 1;  // gradient column half
   const float s_out = neg_inv_scale < 0.0f ? -INFINITY : INFINITY;  // initial S of rows past the end
 
-  const int bh = blockIdx.x / n_ktiles;
-  const int k0 = (blockIdx.x % n_ktiles) * 64;
+  const int bh = lid / n_ktiles;
+  const int k0 = (lid % n_ktiles) * 64;
   const int kw = k0 + 32 * (w >> 1);
   const int b = bh / g.H, hd = bh - b * g.H;
   int sq, Lq, sk, Lk;
@@ -247,12 +249,17 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
             x = thr <= qoff ? x : -INFINITY;
           }
           pe[r] = fast_exp2(x);
+          pin(pe[r]);
         }
         if (k == 3 * r + 1) {
           dsv[r] = pe[r] * dp[PAR][r];  // dp holds dP - D
+          pin(dsv[r]);
           if (r & 1) {
-            pk[PAR][r / 8][(r / 2) % 4] = TR::pack2(pe[r - 1], pe[r]);
-            dsk[PAR][r / 8][(r / 2) % 4] = TR::pack2(dsv[r - 1], dsv[r]);
+            uint32_t p2 = TR::pack2(pe[r - 1], pe[r]), d2 = TR::pack2(dsv[r - 1], dsv[r]);
+            pin(p2);
+            pin(d2);
+            pk[PAR][r / 8][(r / 2) % 4] = p2;
+            dsk[PAR][r / 8][(r / 2) % 4] = d2;
           }
         }
       }
@@ -366,7 +373,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_q128_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ Dvec, uint16_t* __restrict__ dQ,
-                        int Nq, int Nk, int n_qtiles, float c, float scale, GenLayout g) {
+                        int Nq, int Nk, int n_qtiles, uint32_t total, float c, float scale,
+                        GenLayout g) {
   constexpr int NT = 256;
   constexpr int STG = 2 * WBLK;              // one stage slot: K, V rows of 32 keys
   constexpr int NCH = 32 * (WD / 8) / NT;    // 16-byte chunks per thread and tensor (4)
@@ -379,14 +387,16 @@ void bwd_dq_q128_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   using PM = PipeMma<TR, true>;  // Q, dO (score operands) and dQ (accumulators) in AGPRs
   __shared__ __attribute__((aligned(16))) char smem[4 * STG];
 
+  // tiles of one head run on one XCD and share its L2
+  const uint32_t lid = xcd_remap(blockIdx.x, total);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const int bh = blockIdx.x / n_qtiles;
-  int qt = blockIdx.x % n_qtiles;
+  const int bh = lid / n_qtiles;
+  int qt = lid % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
   const int q0 = qt * 128;
   const int qw = q0 + 32 * w;
@@ -502,9 +512,13 @@ void bwd_dq_q128_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
               x = koff <= thr ? x : -INFINITY;
             }
             pe[r] = fast_exp2(x) * dp[PAR][r];  // dS (dp holds dP - D)
+            pin(pe[r]);
           }
-          if (k == 2 * r + 1 && (r & 1))
-            dsk[PAR][r / 8][(r / 2) % 4] = TR::pack2(pe[r - 1], pe[r]);
+          if (k == 2 * r + 1 && (r & 1)) {
+            uint32_t d2 = TR::pack2(pe[r - 1], pe[r]);
+            pin(d2);
+            dsk[PAR][r / 8][(r / 2) % 4] = d2;
+          }
         }
         if (k >= kW0 && k < kW0 + NPART) store_part(slot(bb + 2), k - kW0);
         if (k >= kL0 && k < kL0 + NPART) load_part(j0 + 96, k - kL0);
@@ -598,19 +612,21 @@ template <class TR, bool CAUSAL>
 static hipError_t wide_t(const BwdArgs& a, int stage) {
   if (stage == BWD_DKDV) {
     const int n_ktiles = (a.Nk + 63) / 64;
+    const uint32_t total = (uint32_t)(n_ktiles * a.BH);
     // the exponent is (q.k - LSE / s) s log2 e with s the scale, of magnitude
     // at least 2^-100 so that -1 / s stays finite (as fa_bwd.hip's dK/dV)
     const float mag = fmaxf(fabsf(a.scale), 0x1p-100f);
     const float s = a.scale < 0.0f ? -mag : mag;
-    hipLaunchKernelGGL((bwd_dkdv_wpipe_kernel<TR, CAUSAL>), dim3((uint32_t)(n_ktiles * a.BH)), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dkdv_wpipe_kernel<TR, CAUSAL>), dim3(total), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Nq, a.Nk,
-                       n_ktiles, s * kLog2e, -1.0f / s, a.scale, a.g);
+                       n_ktiles, total, s * kLog2e, -1.0f / s, a.scale, a.g);
   } else {
     const int n_qtiles = (a.Nq + 127) / 128;
-    hipLaunchKernelGGL((bwd_dq_q128_kernel<TR, CAUSAL>), dim3((uint32_t)(n_qtiles * a.BH)), dim3(256), 0,
+    const uint32_t total = (uint32_t)(n_qtiles * a.BH);
+    hipLaunchKernelGGL((bwd_dq_q128_kernel<TR, CAUSAL>), dim3(total), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.Nq, a.Nk, n_qtiles, a.c,
+                       (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.Nq, a.Nk, n_qtiles, total, a.c,
                        a.scale, a.g);
   }
   return hipGetLastError();
