@@ -82,8 +82,7 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
   using PM = PipeMma<TR, true>;  // K, V (score operands) and dK, dV (accumulators) in AGPRs
   __shared__ __attribute__((aligned(16))) char smem[4 * STG];
 
-  // tiles of one head run on one XCD and share its L2
-  const uint32_t lid = xcd_remap(blockIdx.x, total);
+  auto run_tile = [&](const uint32_t lid) __attribute__((always_inline)) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -352,6 +351,18 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
   store_tile_rows<128>(smem + w * kTileRowsBytes<128>, ok, dK + dk_off + 128 * ch, nrows, lane, (size_t)g.dk.sr);
   store_tile_rows<128>(smem + (4 + w) * kTileRowsBytes<128>, ov, dV + dv_off + 128 * ch, nrows, lane,
                        (size_t)g.dv.sr);
+  };
+  // a workgroup takes tile t and tile nt - 1 - t of one head (with the causal
+  // mask, equal work; the middle tile of an odd count once), and the
+  // workgroups of one head run on one XCD and share its L2
+  const uint32_t nt = (uint32_t)n_ktiles, npair = (nt + 1) / 2;
+  const uint32_t pid = xcd_remap(blockIdx.x, total);
+  const uint32_t hh = pid / npair, tt = pid % npair;
+  run_tile(hh * nt + tt);
+  if (nt - 1 - tt != tt) {
+    lds_barrier();
+    run_tile(hh * nt + nt - 1 - tt);
+  }
 }
 
 // dQ for d = 256 with one wavefront per 32 queries: a workgroup takes 128
@@ -387,8 +398,7 @@ void bwd_dq_q128_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   using PM = PipeMma<TR, true>;  // Q, dO (score operands) and dQ (accumulators) in AGPRs
   __shared__ __attribute__((aligned(16))) char smem[4 * STG];
 
-  // tiles of one head run on one XCD and share its L2
-  const uint32_t lid = xcd_remap(blockIdx.x, total);
+  auto run_tile = [&](const uint32_t lid) __attribute__((always_inline)) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -606,13 +616,25 @@ void bwd_dq_q128_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const size_t dq_off = (size_t)((int64_t)b * g.dq.sb + (int64_t)hd * g.dq.sh + (int64_t)(sq + qw) * g.dq.sr);
   static_assert(4 * kTileRowsBytes<256> <= 4 * STG, "four 32 x 256 tiles fit the stage slots");
   store_tile_rows<256>(smem + w * kTileRowsBytes<256>, od, dQ + dq_off, min(32, Lq - qw), lane, (size_t)g.dq.sr);
+  };
+  // a workgroup takes tile t and tile nt - 1 - t of one head (with the causal
+  // mask, equal work; the middle tile of an odd count once), and the
+  // workgroups of one head run on one XCD and share its L2
+  const uint32_t nt = (uint32_t)n_qtiles, npair = (nt + 1) / 2;
+  const uint32_t pid = xcd_remap(blockIdx.x, total);
+  const uint32_t hh = pid / npair, tt = pid % npair;
+  run_tile(hh * nt + tt);
+  if (nt - 1 - tt != tt) {
+    lds_barrier();
+    run_tile(hh * nt + nt - 1 - tt);
+  }
 }
 
 template <class TR, bool CAUSAL>
 static hipError_t wide_t(const BwdArgs& a, int stage) {
   if (stage == BWD_DKDV) {
     const int n_ktiles = (a.Nk + 63) / 64;
-    const uint32_t total = (uint32_t)(n_ktiles * a.BH);
+    const uint32_t total = (uint32_t)(((n_ktiles + 1) / 2) * a.BH);  // workgroups
     // the exponent is (q.k - LSE / s) s log2 e with s the scale, of magnitude
     // at least 2^-100 so that -1 / s stays finite (as fa_bwd.hip's dK/dV)
     const float mag = fmaxf(fabsf(a.scale), 0x1p-100f);
@@ -623,7 +645,7 @@ static hipError_t wide_t(const BwdArgs& a, int stage) {
                        n_ktiles, total, s * kLog2e, -1.0f / s, a.scale, a.g);
   } else {
     const int n_qtiles = (a.Nq + 127) / 128;
-    const uint32_t total = (uint32_t)(n_qtiles * a.BH);
+    const uint32_t total = (uint32_t)(((n_qtiles + 1) / 2) * a.BH);  // workgroups
     hipLaunchKernelGGL((bwd_dq_q128_kernel<TR, CAUSAL>), dim3(total), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dq, a.Nq, a.Nk, n_qtiles, total, a.c,

@@ -259,8 +259,10 @@ def test_head_dim_256_several_tiles_strided_and_varlen():
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 17, 255, 257, 1000])
 def test_head_dim_256_bwd(N, causal, dtype):
-    """d = 256 backward (its own kernels: each 32-row block shared by two
-    wavefronts that accumulate one half of the gradient's columns each)."""
+    """d = 256 backward (its own kernels: dK/dV with each 32-key block shared
+    by two wavefronts that accumulate one half of the columns each, dQ with
+    one wavefront per 32 queries; two tiles per workgroup, tile t and
+    nt - 1 - t, so odd tile counts (N = 1, 17, 257) run a middle tile once)."""
     import torch
     fa = lib()
     d = 256
