@@ -85,7 +85,9 @@ constexpr float kSumMax = 32768.0f;
 // d <= 128: all matrix operands and accumulators live in VGPRs (the MfmaAsm
 // forms), two wavefronts per SIMD.  d = 256: one wavefront per SIMD (4 per
 // workgroup, 128 rows), with the Q fragments (B operands of S) and the O
-// accumulators in AGPRs (PipeMma with AG), 32-key tiles.
+// accumulators in AGPRs (PipeMma with AG), 32-key tiles, and two query tiles
+// per workgroup (total = workgroups: one per tile at d <= 128, where the
+// second tile's code spills, one per pair of tiles at d = 256).
 template <class TR, int D, int BC, int QB, bool CAUSAL, bool GL>
 __global__ __launch_bounds__(D > 128 ? 256 : 512 / QB)
 __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 3 - QB, D > 128 ? 1 : 3 - QB)))
@@ -130,7 +132,7 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const uint32_t lid = xcd_remap(blockIdx.x, total);
+  auto run_tile = [&](const uint32_t lid) __attribute__((always_inline)) {
   const int bh = lid / n_qtiles;
   int qt = lid % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest tiles first
@@ -616,6 +618,21 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
                        O + o_off + (size_t)(qw + 32 * qb) * os, min(32, Nb - (qw + 32 * qb)), lane, os,
                        GL ? DR / 8 : D / 8);
     if (qrow < Nb && h == 0) LSE[l_off + qrow] = (m_run[qb] + __log2f(l)) * kLn2;
+  }
+  };
+  // tile t and tile nt - 1 - t of one head (equal work with the causal mask;
+  // the middle tile of an odd count once); one head's workgroups on one XCD
+  if constexpr (D > 128) {
+    const uint32_t nt = (uint32_t)n_qtiles, npair = (nt + 1) / 2;
+    const uint32_t pid = xcd_remap(blockIdx.x, total);
+    const uint32_t hh = pid / npair, tt = pid % npair;
+    run_tile(hh * nt + tt);
+    if (nt - 1 - tt != tt) {
+      lds_barrier();
+      run_tile(hh * nt + nt - 1 - tt);
+    }
+  } else {
+    run_tile(xcd_remap(blockIdx.x, total));
   }
 }
 
@@ -1124,7 +1141,7 @@ static void launch_pipe_gl(const FwdArgs& a) {
   constexpr int BR = D > 128 ? 128 : 256;
   constexpr int BC = D > 128 ? 32 : 64;
   const int n_qtiles = (a.N + BR - 1) / BR;
-  const uint32_t total = (uint32_t)(n_qtiles * a.BH);
+  const uint32_t total = (uint32_t)((D > 128 ? (n_qtiles + 1) / 2 : n_qtiles) * a.BH);  // workgroups
   hipLaunchKernelGGL((fwd16_pipe_kernel<TR, D, BC, 1, CAUSAL, GL>), dim3(total), dim3(D > 128 ? 256 : 512), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, n_qtiles, total, a.c, a.g);
