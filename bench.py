@@ -52,18 +52,32 @@ KERNEL_SOURCES = {
     "kv": ["fa_kvcache.hip", "fa_common.hpp"],
     "fwd": ["fa_fwd.hip", "fa_common.hpp"],
     "prep": ["fa_bwd.hip", "fa_common.hpp"],
-    "dkdv": ["fa_bwd.hip", "fa_bwd_wide.hip", "fa_common.hpp"],
-    "dq": ["fa_bwd.hip", "fa_bwd_wide.hip", "fa_common.hpp"],
+    "dkdv": ["fa_bwd.hip", "fa_common.hpp"],
+    "dq": ["fa_bwd.hip", "fa_common.hpp"],
     "fwd8": ["fa_fwd_fp8.hip", "fa_common.hpp"],
 }
+WIDE_SOURCES = ["fa_bwd_wide.hip"]  # the d = 256 dK/dV and dQ kernels
 # substrings of the mangled kernel names, as rocprofv3 reports them
 KERNEL_SYMBOLS = {"fwd": "fwd16_p", "prep": "bwd_pre_kernel", "dkdv": "bwd_dkdv",
                   "dq": "bwd_dq", "kv": "kv_split", "fwd8": "fwd8_pipe"}
 
 
-def src_hash(kernel: str) -> str:
+def workload_d(workload: str) -> int:
+    """Head dimension of a named workload (0 if it has none by that name)."""
+    import seeded_inputs as si
+    for table in ("WORKLOADS", "FP8_WORKLOADS", "KV_WORKLOADS"):
+        w = getattr(si, table, {}).get(workload)
+        if w is not None:
+            return int(getattr(w, "d", 0))
+    return 0
+
+
+def src_hash(kernel: str, d: int = 0) -> str:
+    """Hash of the sources a kernel is built from (at d = 256 the backward
+    stages run the wide kernels)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
+    srcs = KERNEL_SOURCES[kernel] + (WIDE_SOURCES if d == 256 and kernel in ("dkdv", "dq") else [])
+    for f in srcs:
         with open(os.path.join(ROOT, "exact_io_aware_fa2_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -98,7 +112,7 @@ def load_traffic(workload: str, kernel: str):
     with open(p) as f:
         t = json.load(f)
     k = t.get("kernels", {}).get(kernel)
-    if not k or k.get("src_sha") != src_hash(kernel):
+    if not k or k.get("src_sha") != src_hash(kernel, workload_d(workload)):
         return None
     return k["bytes_per_launch"]
 
@@ -509,7 +523,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str, workload: str):
         fv, wv = find(fetch, sym), find(write, sym)
         if fv is None or wv is None:
             continue
-        out["kernels"][kern] = {"src_sha": src_hash(kern),
+        out["kernels"][kern] = {"src_sha": src_hash(kern, workload_d(workload)),
                                 "fetch_bytes": fv * 1024 * f_fac, "write_bytes": wv * 1024 * w_fac,
                                 "bytes_per_launch": fv * 1024 * f_fac + wv * 1024 * w_fac}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
