@@ -86,8 +86,8 @@ constexpr float kSumMax = 32768.0f;
 // forms), two wavefronts per SIMD.  d = 256: one wavefront per SIMD (4 per
 // workgroup, 128 rows), with the Q fragments (B operands of S) and the O
 // accumulators in AGPRs (PipeMma with AG), 32-key tiles, and two query tiles
-// per workgroup (total = workgroups: one per tile at d <= 128, where the
-// second tile's code spills, one per pair of tiles at d = 256).
+// per workgroup (total = workgroups: one per tile at d <= 128, where a second
+// tile adds spills, one per pair of tiles at d = 256).
 template <class TR, int D, int BC, int QB, bool CAUSAL, bool GL>
 __global__ __launch_bounds__(D > 128 ? 256 : 512 / QB)
 __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 3 - QB, D > 128 ? 1 : 3 - QB)))
@@ -132,7 +132,24 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  auto run_tile = [&](const uint32_t lid) __attribute__((always_inline)) {
+  // d = 256: tile t and tile nt - 1 - t of one head (equal work with the
+  // causal mask; the middle tile of an odd count once); d <= 128: one tile.
+  // The workgroups of one head run on one XCD.
+  constexpr int NTILE = D > 128 ? 2 : 1;
+  for (int it = 0; it < NTILE; ++it) {
+  uint32_t lid;
+  if constexpr (D > 128) {
+    const uint32_t nt = (uint32_t)n_qtiles, npair = (nt + 1) / 2;
+    const uint32_t pid = xcd_remap(blockIdx.x, total);
+    const uint32_t hh = pid / npair, tt = pid % npair;
+    if (it == 1) {
+      if (nt - 1 - tt == tt) break;
+      lds_barrier();
+    }
+    lid = hh * nt + (it == 0 ? tt : nt - 1 - tt);
+  } else {
+    lid = xcd_remap(blockIdx.x, total);
+  }
   const int bh = lid / n_qtiles;
   int qt = lid % n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest tiles first
@@ -165,7 +182,7 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
     os = D;
     l_off = (size_t)bh * N;
   }
-  if (GL && q0 >= Nb) return;
+  if (GL && q0 >= Nb) continue;
   // the row strides as the staging loads use them: re-read per use in the
   // general layout, so that the per-row offsets are not kept live across the loop
   auto row_stride_k = [&]() __attribute__((always_inline)) -> uint32_t {
@@ -619,20 +636,6 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
                        GL ? DR / 8 : D / 8);
     if (qrow < Nb && h == 0) LSE[l_off + qrow] = (m_run[qb] + __log2f(l)) * kLn2;
   }
-  };
-  // tile t and tile nt - 1 - t of one head (equal work with the causal mask;
-  // the middle tile of an odd count once); one head's workgroups on one XCD
-  if constexpr (D > 128) {
-    const uint32_t nt = (uint32_t)n_qtiles, npair = (nt + 1) / 2;
-    const uint32_t pid = xcd_remap(blockIdx.x, total);
-    const uint32_t hh = pid / npair, tt = pid % npair;
-    run_tile(hh * nt + tt);
-    if (nt - 1 - tt != tt) {
-      lds_barrier();
-      run_tile(hh * nt + nt - 1 - tt);
-    }
-  } else {
-    run_tile(xcd_remap(blockIdx.x, total));
   }
 }
 
