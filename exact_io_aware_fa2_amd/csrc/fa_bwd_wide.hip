@@ -8,9 +8,9 @@
 // columns (K and V, or Q and dO: 128 registers) together with the
 // accumulators of both dK and dV (256 registers).
 // - dK, dV: every 32-key block is shared by two wavefronts, each
-//   accumulating one half of the gradients' columns; both compute the
-//   block's scores and dP over all 256 columns (those products are done
-//   twice).
+//   accumulating one half of the gradients' columns and computing the scores
+//   and dP of one half of each 32-query block (16 x 16 x 32 products); the
+//   two exchange their halves of P and dS through LDS.
 // - dQ: one gradient, so a wavefront holds its 32 queries' Q and dO operands
 //   and all 256 columns of dQ (256 AGPRs), and every score and dP product is
 //   done once.
@@ -46,41 +46,62 @@ __device__ inline int wperm(int m) { return (m & 16) | ((m & 3) << 2) | ((m >> 2
 
 }  // namespace
 
-// dK, dV for d = 256, software-pipelined inside each wavefront (the scheme
-// of fa_bwd.hip's dK/dV kernel, with 32-row stages): a workgroup takes 64
-// keys, wavefront w the keys k0 + 32 (w / 2) and the columns 128 (w % 2) ..
-// +127 of dK and dV.  Iteration b (query rows i_begin + 32 b .. +31, stage
+// 16 x 16 x 32 products of the d = 256 dK/dV kernel below (B operand in AGPRs).
+typedef float f32x4w_t __attribute__((ext_vector_type(4)));
+template <class TR>
+__device__ inline void mma16(f32x4w_t& c, u32x4_t a, u32x4_t b) {
+  if constexpr (std::is_same_v<TR, BF16>) asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+  else asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+__device__ inline void mfma_wait4(f32x4w_t& a, f32x4w_t& b, f32x4w_t& c, f32x4w_t& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));  // 21 wait states
+}
+// staged row (0..15 within a half block) of row m of a 16 x 16 score tile:
+// the four rows 4 g + i (i = 0..3) a lane holds land on consecutive positions
+// of the exchange rows below
+__device__ constexpr int half_row(int m) { return ((m >> 2) & 1) + 4 * (m & 3) + 2 * (m >> 3); }
+
+// dK, dV for d = 256 with the scores split between the two wavefronts of a
+// pair: a workgroup takes 64 keys, wavefront w the keys k0 + 32 (w / 2) and
+// the columns 128 (w % 2) .. +127 of dK and dV (its K and V fragments cover
+// all 256 columns, as S and dP need them), and it computes S and dP only for the 16 query rows 16 (w % 2) .. +15 of each
+// 32-row block (16 x 16 x 32 products: 32 per block, half the work of the
+// full 32 x 32 blocks), and the two wavefronts exchange their halves of P and
+// dS (rounded, as the products use them) through LDS.  Iteration b (stage
 // slot b % 4) issues
-//   matrix: dV^T += dO_{b-1}^T P_{b-1}, dK^T += Q_{b-1}^T dS_{b-1} (8 each,
-//           this wavefront's columns), S'_{b+1} = Q_{b+1} K^T - LSE / s and
-//           dP_{b+1} = dO_{b+1} V^T - D (16 each, all 256 columns)
-//   vector: P_b = exp2(S'_b c), dS_b = P_b (dP_b - D), rounded and packed
-// one product after another with the vector work between them (c = s log2 e,
-// s the scale; -LSE / s and -D enter as the accumulators' initial values).
-// The stage of block b+2 is written to LDS during iteration b from
-// registers loaded during iteration b-1; one workgroup barrier per
-// iteration.  The first four products of an iteration are dV/dK products
-// (slot b-1), so the operand reads issued for them at the end of the
-// previous iteration never touch the slot being written.
+//   matrix: dV^T += dO_{b-1}^T P_{b-1}, dK^T += Q_{b-1}^T dS_{b-1}: first the
+//           k-step of the wavefront's own rows (its P, dS read back from the
+//           exchange area before the previous barrier), then, between the
+//           S, dP products of block b+1, the partner's k-step (read after it)
+//   vector: P_b = exp2(S'_b c), dS_b = P_b (dP_b - D) for its 16 rows,
+//           written to the exchange area
+// with one workgroup barrier per iteration.  Exchange row = key, 32
+// positions of 16-bit values (80 bytes with padding), position 16 t + 8 h + j
+// for the query the transposed read of the gradient products gives lane
+// half h as its j-th value of k-step t.
 template <class TR, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                           const float* __restrict__ LSE, const float* __restrict__ Dvec,
-                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Nq, int Nk, int n_ktiles,
-                           uint32_t total,                           float c, float neg_inv_scale, float scale, GenLayout g) {
+void bwd_dkdv_half_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                          const float* __restrict__ LSE, const float* __restrict__ Dvec,
+                          uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Nq, int Nk, int n_ktiles,
+                          uint32_t total, float c, float neg_inv_scale, float scale, GenLayout g) {
   constexpr int NT = 256;
   constexpr int OFF_V = 2 * WBLK;            // -LSE / s (32 floats), then -D (32 floats)
   constexpr int STG = OFF_V + 2 * 32 * 4;    // one stage slot
   constexpr int NCH = 32 * (WD / 8) / NT;    // 16-byte chunks per thread and tensor (4)
   constexpr int NPART = 2 * NCH + 1;         // staging parts: Q chunks, dO chunks, the vectors
   constexpr int NSL = 48;                    // products per iteration
-  constexpr int AH = 4;                      // operand reads issued ahead of their product
-  constexpr int kW0 = 8, kL0 = 20;           // first staging write, first staging load (product index)
+  constexpr int NF = 32;                     // LDS operands per iteration
+  constexpr int AH = 4;                      // operands read ahead of their last use
+  constexpr int kW0 = 10, kL0 = 30;          // first staging write, first staging load (product index)
+  constexpr int XP = 80;                     // exchange row bytes
+  constexpr int XOFF = 4 * STG;              // exchange area: [pair][buffer][P, dS][key][position]
+  constexpr int XBUF = 2 * 32 * XP, XPAIR = 2 * XBUF;
   static_assert(kW0 + NPART <= kL0 && kL0 + NPART <= NSL, "staging fits the iteration");
-  static_assert(4 * STG <= 160 * 1024, "four stage slots fit in LDS");
-  using PM = PipeMma<TR, true>;  // K, V (score operands) and dK, dV (accumulators) in AGPRs
-  __shared__ __attribute__((aligned(16))) char smem[4 * STG];
+  static_assert(XOFF + 2 * XPAIR <= 160 * 1024, "stage slots and exchange area fit in LDS");
+  using PM = PipeMma<TR, true>;  // dK, dV accumulators in AGPRs
+  __shared__ __attribute__((aligned(16))) char smem[XOFF + 2 * XPAIR];
 
   auto run_tile = [&](const uint32_t lid) __attribute__((always_inline)) {
   const int tid = threadIdx.x;
@@ -88,7 +109,8 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int ch = w & 1;  // gradient column half
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int ch = w & 1;  // gradient column half and query half
   const float s_out = neg_inv_scale < 0.0f ? -INFINITY : INFINITY;  // initial S of rows past the end
 
   const int bh = lid / n_ktiles;
@@ -122,16 +144,20 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
     return;
   }
 
-  // K and V rows of this wavefront's keys as B operands (column = key), all 256 columns
-  u32x4_t kf[WKS], vf[WKS];
+  // K and V rows of this wavefront's keys as B operands of the 16 x 16 x 32
+  // score products: [key half nb][k-step ks], lane: key 16 nb + lane % 16,
+  // columns 32 ks + 8 (lane / 16) .. +7
+  u32x4_t kf[2][8], vf[2][8];
   {
     const rsrc_t kres = make_rsrc(K + tk.off, tk.bytes), vres = make_rsrc(V + tv.off, tv.bytes);
-    const int key = kw + l32;
 #pragma unroll
-    for (int ks = 0; ks < WKS; ++ks) {
-      kf[ks] = buf_load16(kres, (uint32_t)key * tk.rs + 32 * ks + 16 * h);
-      vf[ks] = buf_load16(vres, (uint32_t)key * tv.rs + 32 * ks + 16 * h);
-    }
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int key = kw + 16 * nb + l16;
+        kf[nb][ks] = buf_load16(kres, (uint32_t)key * tk.rs + 64 * ks + 16 * g4);
+        vf[nb][ks] = buf_load16(vres, (uint32_t)key * tv.rs + 64 * ks + 16 * g4);
+      }
   }
   f32x16_t acc_dk[4], acc_dv[4];
 #pragma unroll
@@ -139,8 +165,8 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
 
   // ---- staging: part j < NCH: chunk tid + 256 j of the Q tile (row
   // (tid + 256 j) / 32, 16-byte column % 32), then the same of dO, then (wave
-  // 0) the vectors at position m = lane % 32: row perm(m), -LSE / s for lanes
-  // 0..31 and -D for lanes 32..63.
+  // 0) the vectors at position p = lane % 32 (row 16 (p / 16) + half_row(p %
+  // 16)), -LSE / s for lanes 0..31 and -D for lanes 32..63.
   const rsrc_t qres = make_rsrc(Q + tq.off, tq.bytes), ores = make_rsrc(dO + tdo.off, tdo.bytes);
   u32x4_t sgq[NCH], sgo[NCH];
   float vraw = 0.0f;
@@ -153,7 +179,7 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
       const int i = tid + NT * (j - NCH);
       sgo[j - NCH] = buf_load16(ores, (uint32_t)(i0 + i / 32) * tdo.rs + 16 * (i % 32));
     } else if (w == 0) {
-      vrow = i0 + wperm(l32);
+      vrow = i0 + 16 * (l32 >> 4) + half_row(l32 & 15);
       vraw = vrow < Lq ? (h == 0 ? LSE[l_off + vrow] : Dvec[l_off + vrow]) : 0.0f;
     }
   };
@@ -171,14 +197,24 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
     }
   };
   auto slot = [&](int blk) __attribute__((always_inline)) -> char* { return smem + (blk & 3) * STG; };
+  char* const xpair = smem + XOFF + (w >> 1) * XPAIR;
+  // exchange addresses: this lane's write (key half nb, P or dS) and its read
+  // (k-step t, P or dS) in buffer buf
+  auto xw = [&](int buf, int which, int nb) __attribute__((always_inline)) -> char* {
+    return xpair + buf * XBUF + which * 32 * XP + (16 * nb + l16) * XP + 2 * (16 * ch + 8 * (g4 & 1) + 4 * (g4 >> 1));
+  };
+  auto xr = [&](int buf, int which, int t) __attribute__((always_inline)) -> const u32x4_t* {
+    return (const u32x4_t*)(xpair + buf * XBUF + which * 32 * XP + l32 * XP + 2 * (16 * t + 8 * h));
+  };
 
-  // ---- operands.  Row reads (S, dP): row perm(l32), chunk h (+ 2 ks);
-  // transposed reads (dK, dV): as the other backward kernels
-  const uint32_t rbase = (uint32_t)(wperm(l32) * WRBL + 16 * h);
-  const int L16 = lane & 15, G = lane >> 4;
-  const uint32_t tbase = (uint32_t)((h + 4 * (L16 >> 2)) * WRBL + (16 * (G & 1) + 4 * (L16 & 3)) * 2);
+  // ---- operands.  Score rows (16 x 16 x 32 A operand): row 16 ch +
+  // half_row(lane % 16), columns 32 ks + 8 (lane / 16); transposed reads (dK,
+  // dV): as the other backward kernels
+  const uint32_t rbase = (uint32_t)((16 * ch + half_row(l16)) * WRBL + 16 * g4);
+  const int G = lane >> 4;
+  const uint32_t tbase = (uint32_t)((h + 4 * (l16 >> 2)) * WRBL + (16 * (G & 1) + 4 * (l16 & 3)) * 2);
   auto row_frag = [&](const char* st, int tensor, int ks) __attribute__((always_inline)) -> u32x4_t {
-    return *(const u32x4_t*)(st + tensor * WBLK + rbase + 32 * ks);
+    return *(const u32x4_t*)(st + tensor * WBLK + rbase + 64 * ks);
   };
   // tensor 0: Q^T (dK), 1: dO^T (dV); k-step t of 16 rows, column block db of this half
   auto tr_frag = [&](const char* st, int tensor, int t, int db) __attribute__((always_inline)) -> u32x4_t {
@@ -186,40 +222,40 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
     const u32x2_t a0 = lds_read_tr(p), a1 = lds_read_tr(p + 2 * WRBL);
     return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
   };
-  // initial values of the S and dP accumulators of a block: -LSE / s, -D of its rows
-  auto load_vecs = [&](const char* st, f32x16_t& l, f32x16_t& d) __attribute__((always_inline)) {
+  // initial values of this wavefront's S and dP tiles of a block: -LSE / s, -D of its rows
+  auto load_vecs = [&](const char* st, f32x4w_t (&l)[2], f32x4w_t (&d)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      const float4 l4 = *(const float4*)(st + OFF_V + 32 * gg + 16 * h);
-      const float4 d4 = *(const float4*)(st + OFF_V + 128 + 32 * gg + 16 * h);
-      l[4 * gg + 0] = l4.x; l[4 * gg + 1] = l4.y; l[4 * gg + 2] = l4.z; l[4 * gg + 3] = l4.w;
-      d[4 * gg + 0] = d4.x; d[4 * gg + 1] = d4.y; d[4 * gg + 2] = d4.z; d[4 * gg + 3] = d4.w;
+    for (int nb = 0; nb < 2; ++nb) {
+      l[nb] = *(const f32x4w_t*)(st + OFF_V + 4 * (16 * ch + 4 * g4));
+      d[nb] = *(const f32x4w_t*)(st + OFF_V + 128 + 4 * (16 * ch + 4 * g4));
     }
+    // the compiler may load once and copy: two wait states before the
+    // products that accumulate into them
+    asm volatile("s_nop 1" : "+v"(l[0]), "+v"(l[1]), "+v"(d[0]), "+v"(d[1]));
   };
-  // product k of an iteration: kind 0: dV (t, db), 1: dK (t, db), 2: S k-step,
-  // 3: dP k-step.  Products 0..3: dV/dK of (t, db) = (0, 0), (0, 1); then six
-  // groups of [S, dP, S, dP, dV, dK]; then the last four S/dP k-steps.
-  struct Prod { int kind, t, db, ks; };
+  // LDS operand f of an iteration: 0..7 the own k-step's dV (even) / dK (odd)
+  // operands of column block f / 2; then per group gi: Q rows, dO rows (k-step
+  // gi of the scores), the partner k-step's gradient operand number gi.
+  // Product k: 0..7 own gradient products; then eight groups [S nb 0, dP nb 0,
+  // S nb 1, dP nb 1, partner gradient product gi].
+  // kind 0 dV, 1 dK (x: own 0 / partner 1 k-step, column block db), 2 S, 3 dP
+  // (key half nb); last: the operand's last use
+  struct Prod { int kind, f, nb, last, x, db; };
   auto prod = [](int k) constexpr -> Prod {
-    if (k < 4) return Prod{k & 1, 0, k >> 1, 0};
-    if (k < 40) {
-      const int gi = (k - 4) / 6, p = (k - 4) % 6;
-      if (p < 4) return Prod{2 + (p & 1), 0, 0, 2 * gi + (p >> 1)};
-      const int x = 2 + gi;  // dV/dK pair index 2..7
-      return Prod{p - 4, x >> 2, x & 3, 0};
-    }
-    const int x = k - 40;
-    return Prod{2 + (x & 1), 0, 0, 12 + (x >> 1)};
+    if (k < 8) return Prod{k & 1, k, 0, 1, 0, k >> 1};
+    const int gi = (k - 8) / 5, p = (k - 8) % 5;
+    if (p < 4) return Prod{2 + (p & 1), 8 + 3 * gi + (p & 1), p >> 1, p >> 1, 0, 0};
+    return Prod{gi & 1, 8 + 3 * gi + 2, 0, 1, 1, gi >> 1};
   };
-  auto frag = [&](int k, const char* sb1, const char* sb2) __attribute__((always_inline)) -> u32x4_t {
-    const Prod p = prod(k);
-    if (p.kind == 0) return tr_frag(sb2, 1, p.t, p.db);
-    if (p.kind == 1) return tr_frag(sb2, 0, p.t, p.db);
-    return row_frag(sb1, p.kind - 2, p.ks);
+  auto frag = [&](int f, const char* sb1, const char* sb2) __attribute__((always_inline)) -> u32x4_t {
+    if (f < 8) return tr_frag(sb2, (f & 1) ? 0 : 1, ch, f >> 1);
+    const int gi = (f - 8) / 3, r = (f - 8) % 3;
+    if (r < 2) return row_frag(sb1, r, gi);
+    return tr_frag(sb2, (gi & 1) ? 0 : 1, 1 - ch, gi >> 1);
   };
 
-  f32x16_t sc[2], dp[2];
-  u32x4_t pk[2][2], dsk[2][2];  // [set][k-step t]: P and dS rounded, packed in pairs
+  f32x4w_t sc[2][2], dp[2][2];  // [register set][key half]
+  u32x4_t pko, dso, pkp, dsp;   // P, dS B operands: own k-step, partner k-step
   u32x4_t fr[AH];
 
   // ---- one iteration (block bb, PAR = bb % 2)
@@ -228,40 +264,46 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
     constexpr int NB = 1 - PAR;
     const char* sb1 = slot(bb + 1);
     const char* sb2 = slot(bb - 1);
-    // S_b, dP_b were written by matrix instructions, P and dS of block b-1 by
-    // vector instructions: all of them ordered before what reads them next
-    mfma_wait_v(sc[PAR], dp[PAR]);
-    asm volatile("s_nop 1" : "+v"(pk[NB][0]), "+v"(pk[NB][1]), "+v"(dsk[NB][0]), "+v"(dsk[NB][1]));
+    mfma_wait4(sc[PAR][0], sc[PAR][1], dp[PAR][0], dp[PAR][1]);  // S_b, dP_b: matrix results
+    // the partner's P, dS of block b-1 (written before the last barrier)
+    pkp = *xr((bb - 1) & 1, 0, 1 - ch);
+    dsp = *xr((bb - 1) & 1, 1, 1 - ch);
     load_vecs(sb1, sc[NB], dp[NB]);
     const int i0 = i_begin + 32 * bb;
-    // causal: key kw + l32 is visible to the query of score r iff thr <= qoff(r)
-    const int thr = kw - delta - i0 + l32 - h;
-    float pe[16], dsv[16];
+    // causal: key kw + 16 nb + lane % 16 is visible to row 4 g + e of the tile
+    // iff thr + 16 nb <= 4 e
+    const int thr = kw + l16 - delta - i0 - 16 * ch - (g4 & 1) - 2 * (g4 >> 1);
+    float pe[8], dsv[8];
+    uint32_t pp[2][2], dd[2][2];
     auto vwork = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (k == 3 * r) {
-          float x = sc[PAR][r] * c;
-          if constexpr (CAUSAL) {
-            const int gq = r / 4, e = r % 4;
-            const int qoff = 16 * (gq / 2) + 4 * e + 2 * (gq % 2);
-            x = thr <= qoff ? x : -INFINITY;
-          }
-          pe[r] = fast_exp2(x);
-          pin(pe[r]);
+      for (int e = 0; e < 8; ++e) {
+        const int nb = e >> 2, r = e & 3;
+        if (k == 8 + 2 * e) {
+          float x = sc[PAR][nb][r] * c;
+          if constexpr (CAUSAL) x = thr + 16 * nb <= 4 * r ? x : -INFINITY;
+          pe[e] = fast_exp2(x);
+          pin(pe[e]);
         }
-        if (k == 3 * r + 1) {
-          dsv[r] = pe[r] * dp[PAR][r];  // dp holds dP - D
-          pin(dsv[r]);
+        if (k == 9 + 2 * e) {
+          dsv[e] = pe[e] * dp[PAR][nb][r];  // dp holds dP - D
+          pin(dsv[e]);
           if (r & 1) {
-            uint32_t p2 = TR::pack2(pe[r - 1], pe[r]), d2 = TR::pack2(dsv[r - 1], dsv[r]);
-            pin(p2);
-            pin(d2);
-            pk[PAR][r / 8][(r / 2) % 4] = p2;
-            dsk[PAR][r / 8][(r / 2) % 4] = d2;
+            pp[nb][r >> 1] = TR::pack2(pe[e - 1], pe[e]);
+            dd[nb][r >> 1] = TR::pack2(dsv[e - 1], dsv[e]);
+            pin(pp[nb][r >> 1]);
+            pin(dd[nb][r >> 1]);
           }
         }
       }
+      // P_b, dS_b to the exchange area, then this wavefront's own k-step back
+      // (the operands of the next iteration's first products)
+      if (k >= 26 && k < 30) {
+        const int which = (k - 26) >> 1, nb = (k - 26) & 1;
+        *(u32x2_t*)xw(bb & 1, which, nb) = which ? u32x2_t{dd[nb][0], dd[nb][1]} : u32x2_t{pp[nb][0], pp[nb][1]};
+      }
+      if (k == 44) pko = *xr(bb & 1, 0, ch);
+      if (k == 45) dso = *xr(bb & 1, 1, ch);
       // staging: the stage of block b+2 into its slot, then the loads of block b+3
       if (k >= kW0 && k < kW0 + NPART) store_part(slot(bb + 2), k - kW0);
       if (k >= kL0 && k < kL0 + NPART) load_part(i0 + 96, k - kL0);
@@ -269,22 +311,24 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
     static_for<0, NSL>([&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
       constexpr Prod p = prod(k);
-      const u32x4_t a = fr[k % AH];
-      if constexpr (k + AH < NSL) fr[k % AH] = frag(k + AH, sb1, sb2);
-      else fr[k % AH] = frag(k + AH - NSL, slot(bb + 2), slot(bb));  // next iteration's dV/dK operands
-      if constexpr (p.kind == 0) PM::macc(acc_dv[p.db], a, pk[NB][p.t]);
-      else if constexpr (p.kind == 1) PM::macc(acc_dk[p.db], a, dsk[NB][p.t]);
-      else if constexpr (p.kind == 2) PM::mb(sc[NB], a, kf[p.ks]);
-      else PM::mb(dp[NB], a, vf[p.ks]);
+      const u32x4_t a = fr[p.f % AH];
+      if constexpr (p.last) {
+        if constexpr (p.f + AH < NF) fr[p.f % AH] = frag(p.f + AH, sb1, sb2);
+        else fr[p.f % AH] = frag(p.f + AH - NF, slot(bb + 2), slot(bb));  // next iteration's first operands
+      }
+      if constexpr (p.kind == 0) PM::macc(acc_dv[p.db], a, p.x ? pkp : pko);
+      else if constexpr (p.kind == 1) PM::macc(acc_dk[p.db], a, p.x ? dsp : dso);
+      else if constexpr (p.kind == 2) mma16<TR>(sc[NB][p.nb], a, kf[p.nb][(p.f - 8) / 3]);
+      else mma16<TR>(dp[NB][p.nb], a, vf[p.nb][(p.f - 8) / 3]);
       vwork(k);
       __builtin_amdgcn_sched_barrier(0);
     });
     lds_barrier();
   };
 
-  // ---- prologue: stages 0 and 1 in slots 0 and 1, slot 3 zeroed (block -1:
-  // its products multiply it by zero P and dS), block 2 requested; S_0, dP_0;
-  // the first operands
+  // ---- prologue: stages 0 and 1 in slots 0 and 1, slot 3 and exchange
+  // buffer 1 zeroed (block -1: its products multiply zeros), block 2
+  // requested; this wavefront's S_0, dP_0; the first operands
 #pragma unroll
   for (int j = 0; j < NPART; ++j) load_part(i_begin, j);
 #pragma unroll
@@ -294,20 +338,22 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
 #pragma unroll
   for (int j = 0; j < NPART; ++j) store_part(slot(1), j);
   for (int i = tid; i < STG / 16; i += NT) *(u32x4_t*)(slot(3) + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
+  for (int i = tid; i < 2 * XPAIR / 16; i += NT) *(u32x4_t*)(smem + XOFF + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int j = 0; j < NPART; ++j) load_part(i_begin + 64, j);
   lds_barrier();
   PM::copy_wait(acc_dk[0], acc_dk[1], acc_dk[2], acc_dk[3], acc_dv[0], acc_dv[1], acc_dv[2], acc_dv[3]);
   load_vecs(slot(0), sc[0], dp[0]);
-  mma_pipeline<2 * WKS, 3>([&](int x) { return slot(0) + ((x & 1) ? WBLK : 0) + rbase + 32 * (x >> 1); },
-                           [&](int x, u32x4_t a) {
-                             const int ks = x >> 1;
-                             if (x & 1) PM::mb(dp[0], a, vf[ks]);
-                             else PM::mb(sc[0], a, kf[ks]);
-                           },
-                           [](int) {});
 #pragma unroll
-  for (int t = 0; t < 2; ++t) pk[1][t] = dsk[1][t] = u32x4_t{0u, 0u, 0u, 0u};
+  for (int ks = 0; ks < 8; ++ks) {
+    const u32x4_t aq = row_frag(slot(0), 0, ks), ao = row_frag(slot(0), 1, ks);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      mma16<TR>(sc[0][nb], aq, kf[nb][ks]);
+      mma16<TR>(dp[0][nb], ao, vf[nb][ks]);
+    }
+  }
+  pko = dso = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int x = 0; x < AH; ++x) fr[x] = frag(x, slot(1), slot(3));
 
@@ -316,23 +362,22 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
     if (bb + 1 < n_st) iteration(std::integral_constant<int, 1>{}, bb + 1);
   }
 
-  // ---- the last block's dV, dK products (register set (n_st - 1) % 2)
-  auto last = [&](auto par_c) __attribute__((always_inline)) {
-    constexpr int PAR = decltype(par_c)::value;
-    const char* st = slot(n_st - 1);
-    asm volatile("s_nop 1" : "+v"(pk[PAR][0]), "+v"(pk[PAR][1]), "+v"(dsk[PAR][0]), "+v"(dsk[PAR][1]));
+  // ---- the last block's dV, dK products: the own k-step from the read-back
+  // registers, the partner's from the exchange area (after the last barrier)
+  {
+    const int bl = n_st - 1;
+    const char* st = slot(bl);
+    pkp = *xr(bl & 1, 0, 1 - ch);
+    dsp = *xr(bl & 1, 1, 1 - ch);
     PM::copy_wait(acc_dk[0], acc_dk[1], acc_dk[2], acc_dk[3], acc_dv[0], acc_dv[1], acc_dv[2], acc_dv[3]);
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      PM::macc(acc_dv[x & 3], tr_frag(st, 1, x >> 2, x & 3), pk[PAR][x >> 2]);
-      PM::macc(acc_dk[x & 3], tr_frag(st, 0, x >> 2, x & 3), dsk[PAR][x >> 2]);
+      const int t = (x >> 2) ? 1 - ch : ch;
+      PM::macc(acc_dv[x & 3], tr_frag(st, 1, t, x & 3), (x >> 2) ? pkp : pko);
+      PM::macc(acc_dk[x & 3], tr_frag(st, 0, t, x & 3), (x >> 2) ? dsp : dso);
     }
-    // before the two paths join: the compiler may copy the accumulators
-    // between registers there, and a copy reads the products' results
     PM::wait_acc(acc_dk[0], acc_dk[1], acc_dk[2], acc_dk[3], acc_dv[0], acc_dv[1], acc_dv[2], acc_dv[3]);
-  };
-  if (n_st & 1) last(std::integral_constant<int, 0>{});
-  else last(std::integral_constant<int, 1>{});
+  }
 
   // dK (times the scale) and dV, this wavefront's 128 columns of its 32 keys,
   // as whole rows through LDS
@@ -368,7 +413,8 @@ void bwd_dkdv_wpipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
 // dQ for d = 256 with one wavefront per 32 queries: a workgroup takes 128
 // queries, wavefront w the queries q0 + 32 w .. +31 and all 256 columns of
 // dQ (eight 32 x 32 accumulators in AGPRs beside the Q and dO operands), so
-// that every block's scores and dP are computed once.  Iteration b (keys
+// that every block's scores and dP are computed once; the software pipeline
+// of the d = 128 kernels, with 32-row stages in four slots.  Iteration b (keys
 // 32 b .. +31, stage slot b % 4) issues
 //   matrix: dQ^T += K_{b-1}^T dS^T_{b-1} (16), S^T_{b+1} = K_{b+1} Q^T,
 //           dP^T_{b+1} = V_{b+1} dO^T - D (16 each)
@@ -639,7 +685,7 @@ static hipError_t wide_t(const BwdArgs& a, int stage) {
     // at least 2^-100 so that -1 / s stays finite (as fa_bwd.hip's dK/dV)
     const float mag = fmaxf(fabsf(a.scale), 0x1p-100f);
     const float s = a.scale < 0.0f ? -mag : mag;
-    hipLaunchKernelGGL((bwd_dkdv_wpipe_kernel<TR, CAUSAL>), dim3(total), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dkdv_half_kernel<TR, CAUSAL>), dim3(total), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Nq, a.Nk,
                        n_ktiles, total, s * kLog2e, -1.0f / s, a.scale, a.g);
