@@ -21,10 +21,13 @@
 // registers per wavefront, the score operands and the gradient accumulators
 // in AGPRs).
 //
-// Layouts as in fa_bwd.hip: S (or S^T) accumulator row m of a 32-row block
+// Layouts: in dQ, as in fa_bwd.hip, S^T accumulator row m of a 32-row block
 // holds row perm(m) of the staged tile, so that the transposed LDS reads of
-// the gradient products gather rows 4 apart (bank-conflict free), and the
-// per-row LSE and D values are staged in the same permuted order.
+// the gradient products gather rows 4 apart (bank-conflict free); in dK/dV
+// row m of a wavefront's 16 x 16 score tile holds staged row half_row(m) of
+// its half, so that the P and dS values a lane holds go to consecutive
+// positions of the exchange rows.  The per-row LSE and D values are staged
+// in the order the accumulators read them.
 // General layout (strides per tensor, packed sequences with their own query
 // and key counts, bottom-right causal alignment), as the other backward
 // kernels' GL variants.
@@ -64,8 +67,8 @@ __device__ constexpr int half_row(int m) { return ((m >> 2) & 1) + 4 * (m & 3) +
 // dK, dV for d = 256 with the scores split between the two wavefronts of a
 // pair: a workgroup takes 64 keys, wavefront w the keys k0 + 32 (w / 2) and
 // the columns 128 (w % 2) .. +127 of dK and dV (its K and V fragments cover
-// all 256 columns, as S and dP need them), and it computes S and dP only for the 16 query rows 16 (w % 2) .. +15 of each
-// 32-row block (16 x 16 x 32 products: 32 per block, half the work of the
+// all 256 columns, as S and dP need them), and it computes S and dP only
+// for the 16 query rows 16 (w % 2) .. +15 of each 32-row block (16 x 16 x 32 products: 32 per block, half the work of the
 // full 32 x 32 blocks), and the two wavefronts exchange their halves of P and
 // dS (rounded, as the products use them) through LDS.  Iteration b (stage
 // slot b % 4) issues
