@@ -286,6 +286,33 @@ def test_head_dim_256_bwd(N, causal, dtype):
     assert all(e <= BWD_REL_L2 for e in errs.values()), errs
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_256_bwd_deterministic_bitwise(causal):
+    """The d = 256 backward twice on the same inputs gives bit-identical dQ,
+    dK, dV (no atomics; the halves of P and dS that the two wavefronts of a
+    key pair exchange through LDS are written and read in a fixed order), at
+    B=1 H=3 N=1100: 18 key tiles and 9 query tiles (an odd count, so one
+    workgroup runs its middle tile alone)."""
+    import torch
+    fa = lib()
+    B, H, N, d = 1, 3, 1100, 256
+    scale = 1.0 / np.sqrt(d)
+    inp = si.make_inputs(B, H, N, d, "bf16", 1.0, 9987, backward=True)
+    q, k, v, do = (to_device(inp[n][1], "bf16") for n in ("q", "k", "v", "do"))
+    say(f"d256 bwd bitwise repeat N{N} causal={causal}")
+    o, lse = fa.fwd(q, k, v, causal, scale)
+    g1 = [t.clone() for t in fa.bwd(q, k, v, o, lse, do, causal, scale)]
+    g2 = fa.bwd(q, k, v, o, lse, do, causal, scale)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), g1, g2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+    ref = attention_bwd_head(inp["q"][0][0, 1], inp["k"][0][0, 1], inp["v"][0][0, 1], inp["do"][0][0, 1],
+                             scale, causal)
+    errs = {n: rel_l2(g[0, 1].float().cpu().numpy(), r) for n, g, r in zip(("dq", "dk", "dv"), g1, ref)}
+    say(f"  head 1 rel-L2 {errs}")
+    assert all(e <= BWD_REL_L2 for e in errs.values()), errs
+
+
 def test_head_dim_256_bwd_strided_and_varlen():
     """d = 256 backward at B=2 H=4 N=1024 causal through fa_bwd_strided in
     [B, N, H, d] storage (bit for bit against fa_bwd on the same values),
