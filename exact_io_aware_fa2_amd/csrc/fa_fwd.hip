@@ -38,6 +38,12 @@
 
 namespace fa {
 
+// Row of a 32-key block that accumulator row m of S^T reads at d = 256:
+// inside each 16 keys, row 4 (m mod 4) + (m / 4) mod 4, so that the keys of
+// the probabilities one lane holds for a 16-key step are the rows a
+// transposed read of V gives it.
+__device__ constexpr int key_perm(int m) { return (m & 16) | ((m & 3) << 2) | ((m >> 2) & 3); }
+
 // Reference maximum of both 16-bit kernels: fixed by the first tile, and
 // changed only when the sum of a row's probabilities over one key tile
 // exceeds this bound (the pipelined kernel then redoes its pass against exact
@@ -124,7 +130,10 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   static_assert(kLoad < NS, "schedule fits one iteration");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * D];
+  // d = 256: V row-major like K (rows padded to D + 8), its product operands
+  // read transposed; d <= 128: the interleaved layout below
+  constexpr int VSR = AG ? D + 8 : D;
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * VSR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -223,6 +232,9 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   constexpr int NSET = AG ? 2 : 1;
   u32x4_t stk[NSET][NKC];
   uint32_t stv[NSET][8][CW / 2];
+  u32x4_t stvr[AG ? NSET : 1][AG ? NKC : 1];  // d = 256: V chunks as K's
+  const uint32_t voffr = (uint32_t)(tid / KCH) * rsv + (tid % KCH) * 16 +
+                         (GL ? col_pad((tid % KCH) * 16, DR, v_bytes) : 0u);
   // K: chunk tid + NT r -> row (tid / KCH) + (NT / KCH) r, 16-byte column tid % KCH
   const uint32_t koff = (uint32_t)(tid / KCH) * rsk + (tid % KCH) * 16 +
                         (GL ? col_pad((tid % KCH) * 16, DR, k_bytes) : 0u);
@@ -242,6 +254,12 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
       stk[set][r] = buf_load16(kres, koff + (uint32_t)(tile * BC + (NT / KCH) * r) * row_stride_k());
   };
   auto load_v = [&](int tile, int set = 0) __attribute__((always_inline)) {
+    if constexpr (AG) {
+#pragma unroll
+      for (int r = 0; r < NKC; ++r)
+        stvr[set][r] = buf_load16(vres, voffr + (uint32_t)(tile * BC + (NT / KCH) * r) * row_stride_v());
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const uint32_t off = voff + (uint32_t)(tile * BC + 8 * (k / 4) + (k % 4)) * row_stride_v();
@@ -258,6 +276,8 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   auto store_part = [&](int i, int b, int set = 0) __attribute__((always_inline)) {
     if (i < NKC) {
       *(u32x4_t*)(&sK[b][kst + i * (NT / KCH) * KS]) = stk[set][i];
+    } else if constexpr (AG) {
+      *(u32x4_t*)(&sV[b][(tid / KCH + (i - NKC) * (NT / KCH)) * VSR + (tid % KCH) * 8]) = stvr[set][i - NKC];
     } else {
       const int cc = i - NKC;  // column within the group
       uint32_t o[4];
@@ -271,7 +291,10 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   };
 
   // ---- per-lane state
-  const int kfrag = l32 * KS + 8 * h;   // element offset of this lane's K fragment
+  // element offset of this lane's K fragment; d = 256: row key_perm(l32), so
+  // that the keys of the probabilities a lane holds for a 16-key step are
+  // the rows a transposed V read gives it (4 apart: bank-conflict free)
+  const int kfrag = (AG ? key_perm(l32) : l32) * KS + 8 * h;
   const int vfrag = (h * D + (l32 ^ ((l32 >> 3) & 3))) * 8;  // this lane's V fragment
   f32x16_t acc[QB][NDB];
 #pragma unroll
@@ -300,6 +323,16 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   };
   auto vaddr = [&](int b, int i) -> const uint16_t* {
     return sV[b] + vfrag + (2 * (i / NDB) * D + 32 * (i % NDB)) * 8;
+  };
+  // PV operand i of buffer b (k-step i / NDB, column block i % NDB)
+  const int vtr = (h + 4 * ((lane & 15) >> 2)) * VSR + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto vread = [&](int b, int i) __attribute__((always_inline)) -> u32x4_t {
+    if constexpr (AG) {
+      const uint16_t* p = sV[b] + vtr + 16 * (i / NDB) * VSR + 32 * (i % NDB);
+      const u32x2_t a0 = lds_read_tr(p), a1 = lds_read_tr(p + 2 * VSR);
+      return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    }
+    return *(const u32x4_t*)vaddr(b, i);
   };
   auto pfrag = [&](const u32x4_t (&p)[QB][NKB][2], int qb, int ss) -> u32x4_t { return p[qb][ss / 2][ss % 2]; };
   // All score blocks of one register set, or all O accumulators, as operands
@@ -344,11 +377,13 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
     if constexpr (MASKED) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        lim[qb] = (CAUSAL ? min(Nb, qw + 32 * qb + l32 + 1) : Nb) - j0 - 4 * h;
+        lim[qb] = (CAUSAL ? min(Nb, qw + 32 * qb + l32 + 1) : Nb) - j0 - (AG ? h : 4 * h);
     }
     auto score = [&](int qb, int kb, int r) __attribute__((always_inline)) -> float {
       const float x = s_cur[qb][kb][r];
-      if constexpr (MASKED) return 32 * kb + 8 * (r / 4) + (r % 4) >= lim[qb] ? -INFINITY : x;
+      // key of score r less j0 and the lane's part (4 h; d = 256: h)
+      const int koff = AG ? 16 * (r / 8) + 4 * (r % 4) + 2 * ((r / 4) & 1) : 8 * (r / 4) + (r % 4);
+      if constexpr (MASKED) return 32 * kb + koff >= lim[qb] ? -INFINITY : x;
       return x;
     };
 
@@ -441,15 +476,19 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
     auto faddr = [&](int f) -> const uint16_t* {
       return is_pv(f) ? vaddr(RD, fidx(f)) : kaddr(RD, fidx(f));
     };
+    auto fread = [&](int f) __attribute__((always_inline)) -> u32x4_t {
+      if (is_pv(f)) return vread(RD, fidx(f));
+      return *(const u32x4_t*)kaddr(RD, fidx(f));
+    };
     u32x4_t fr[kAhead];
 #pragma unroll
-    for (int x = 0; x < kAhead; ++x) fr[x] = *(const u32x4_t*)faddr(x);
+    for (int x = 0; x < kAhead; ++x) fr[x] = fread(x);
     static_for<0, NS + 3>([&](auto stc) __attribute__((always_inline)) {
       constexpr int st = decltype(stc)::value;
       if constexpr (st < NS) {
         constexpr int f = st / QB, qb = st % QB;
         const u32x4_t a = fr[f % kAhead];
-        if constexpr (qb == QB - 1 && f + kAhead < NF) fr[f % kAhead] = *(const u32x4_t*)faddr(f + kAhead);
+        if constexpr (qb == QB - 1 && f + kAhead < NF) fr[f % kAhead] = fread(f + kAhead);
         constexpr int i = fidx(f);
         if constexpr (is_pv(f)) {
           constexpr int ss = i / NDB, db = i % NDB;
@@ -491,8 +530,12 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
   auto run_pass = [&]() __attribute__((always_inline)) {
     // ---- prologue: K_0, K_1 in LDS, V buffer 1 zeroed (iteration 0 multiplies
     // it by the zero probabilities pB), S_0 computed, K_2 and V_0 requested.
+    if constexpr (AG) {
+      for (int i = tid; i < BC * VSR / 8; i += NT) *(u32x4_t*)(&sV[1][8 * i]) = u32x4_t{0u, 0u, 0u, 0u};
+    } else {
   #pragma unroll
-    for (int i = 0; i < CW; ++i) *(u32x4_t*)(&sV[1][(tid + NT * i) * 8]) = u32x4_t{0u, 0u, 0u, 0u};
+      for (int i = 0; i < CW; ++i) *(u32x4_t*)(&sV[1][(tid + NT * i) * 8]) = u32x4_t{0u, 0u, 0u, 0u};
+    }
     load_k(0);
     wait_vmem();  // Q fragments and K_0
     if (!exact) {
@@ -550,13 +593,23 @@ void fwd16_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restric
     }
 
     // last tile (odd index): O += V^T P from register set B and V buffer 1
-    mma_pipeline<NVF, 3>([&](int i) { return vaddr(1, i); },
-                         [&](int i, u32x4_t a) {
-                           const int ss = i / NDB, db = i % NDB;
-  #pragma unroll
-                           for (int qb = 0; qb < QB; ++qb) PM::macc(acc[qb][db], a, pfrag(pB, qb, ss));
-                         },
-                         [](int) {});
+    if constexpr (AG) {
+#pragma unroll
+      for (int i = 0; i < NVF; ++i) {
+        const u32x4_t a = vread(1, i);
+        const int ss = i / NDB, db = i % NDB;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) PM::macc(acc[qb][db], a, pfrag(pB, qb, ss));
+      }
+    } else {
+      mma_pipeline<NVF, 3>([&](int i) { return vaddr(1, i); },
+                           [&](int i, u32x4_t a) {
+                             const int ss = i / NDB, db = i % NDB;
+    #pragma unroll
+                             for (int qb = 0; qb < QB; ++qb) PM::macc(acc[qb][db], a, pfrag(pB, qb, ss));
+                           },
+                           [](int) {});
+    }
   };
 
   // Did a row of this workgroup need a new reference maximum?  (Rare: only
