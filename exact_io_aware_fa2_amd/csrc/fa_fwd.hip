@@ -88,6 +88,10 @@ constexpr float kSumMax = 32768.0f;
 //      staging writes (lanes CW columns apart) and the fragment reads (lanes
 //      on consecutive columns) both hit distinct banks.
 //
+// d = 256 stages V row-major like K instead (rows padded to D + 8) and reads
+// its product operand with two transposed reads, K operand rows in the order
+// key_perm.
+//
 // d <= 128: all matrix operands and accumulators live in VGPRs (the MfmaAsm
 // forms), two wavefronts per SIMD.  d = 256: one wavefront per SIMD (4 per
 // workgroup, 128 rows), with the Q fragments (B operands of S) and the O
