@@ -70,7 +70,7 @@ def test_degenerate_and_large_scales(scale, causal, d):
     _check_heads(inp, grads, [(0, 0), (0, 1)], scale, causal, f"scale={scale} d{d} causal={causal}")
 
 
-@pytest.mark.parametrize("name", ["C5", "C5d128"])
+@pytest.mark.parametrize("name", ["C5", "C5d128", "C5d256"])
 def test_c5_full_size_sampled_heads(name):
     w = si.WORKLOADS[name]
     say(f"{name} full size on GPU: {w}")

@@ -101,9 +101,10 @@ def test_c3_d64_bf16_causal_sampled():
     _sampled(w, [(0, 3), (1, 30)], _rows_early_random_late)
 
 
-@pytest.mark.parametrize("name", ["C5", "C5d128"])
+@pytest.mark.parametrize("name", ["C5", "C5d128", "C5d256"])
 def test_c5_forward_full_size_sampled(name):
-    # the forward half of the timed step (persistent grid at d = 64), on its own outputs
+    # the forward half of the timed step (persistent grid at d = 64; tile
+    # pairs and row-major V at d = 256), on its own outputs
     w = si.WORKLOADS[name]
     _sampled(w, [(0, 0), (7, 15), (3, 9)], _rows_early_random_late)
 
